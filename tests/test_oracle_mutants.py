@@ -1,0 +1,169 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Every mutant below is a plausible slip (a dropped term, a wrong sign, a
+transposed operand, a wrong constant).  It is patched into the oracle module
+on the CPU for the duration of one pin test, which must then fail.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import gpt_oracle as O
+import tests.test_oracle_pins as pins
+
+
+def _ln_unbiased(x, w, b, eps=O.LN_EPS):
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).sum(axis=-1, keepdims=True) / (x.shape[-1] - 1)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = (x - mean) * rstd
+    return xhat * w + b, (xhat, rstd)
+
+
+def _ln_bwd_no_mean_term(dy, w, cache):
+    xhat, rstd = cache
+    g = dy * w
+    dx = rstd * (g - xhat * (g * xhat).mean(axis=-1, keepdims=True))
+    red = tuple(range(dy.ndim - 1))
+    return dx, (dy * xhat).sum(axis=red), dy.sum(axis=red)
+
+
+def _gelu_exact(u):
+    from scipy.special import erf
+    return 0.5 * u * (1 + erf(u / math.sqrt(2)))
+
+
+def _gelu_bwd_sign(u):
+    t = np.tanh(O.GELU_C * (u + O.GELU_A * u ** 3))
+    return 0.5 * (1.0 + t) - 0.5 * u * (1.0 - t * t) * O.GELU_C * (1.0 + 3.0 * O.GELU_A * u * u)
+
+
+def _attn_no_scale(q, k, v):
+    T = q.shape[-2]
+    s = q @ np.swapaxes(k, -1, -2)
+    s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
+    e = np.exp(s - s.max(-1, keepdims=True))
+    p = e / e.sum(-1, keepdims=True)
+    return p @ v, p
+
+
+def _attn_mask_inclusive(q, k, v):
+    # masks the diagonal too (off-by-one); row 0 then has no visible key, so
+    # give it itself to stay finite
+    T, hs = q.shape[-2], q.shape[-1]
+    s = q @ np.swapaxes(k, -1, -2) / math.sqrt(hs)
+    mask = np.triu(np.ones((T, T), bool), 0)
+    mask[0, 0] = False
+    s = np.where(mask, -np.inf, s)
+    e = np.exp(s - s.max(-1, keepdims=True))
+    p = e / e.sum(-1, keepdims=True)
+    return p @ v, p
+
+
+def _attn_bwd_transposed(dout, q, k, v, p):
+    hs = q.shape[-1]
+    dv = p @ dout
+    dp = dout @ np.swapaxes(v, -1, -2)
+    ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+    return ds @ k / math.sqrt(hs), np.swapaxes(ds, -1, -2) @ q / math.sqrt(hs), dv
+
+
+def _ce_unmasked_pad(logits, targets, vocab_size, loss_scale=1.0):
+    return _orig_ce(logits, targets, logits.shape[1], loss_scale)
+
+
+def _ce_sum_not_mean(logits, targets, vocab_size, loss_scale=1.0):
+    loss, d = _orig_ce(logits, targets, vocab_size, loss_scale)
+    n = int((targets >= 0).sum())
+    return loss * n, d * n
+
+
+def _adamw_coupled(params, grads, m, v, mask, t, lr, beta1=0.9, beta2=0.95, eps=1e-8,
+                   weight_decay=0.1, coef=1.0):
+    g = grads * coef + weight_decay * mask * params  # L2 in the gradient, not decoupled
+    return _orig_adamw(params, g, m, v, mask, t, lr, beta1, beta2, eps, 0.0, 1.0)
+
+
+def _adamw_eps_inside(params, grads, m, v, mask, t, lr, beta1=0.9, beta2=0.95, eps=1e-8,
+                      weight_decay=0.1, coef=1.0):
+    g = grads * coef
+    m = beta1 * m + (1 - beta1) * g
+    v = beta2 * v + (1 - beta2) * g * g
+    p = params * (1 - lr * weight_decay * mask)
+    p = p - lr * (m / (1 - beta1 ** t)) / np.sqrt(v / (1 - beta2 ** t) + eps)
+    return p, m, v
+
+
+def _adamw_no_bias_correction(params, grads, m, v, mask, t, lr, beta1=0.9, beta2=0.95,
+                              eps=1e-8, weight_decay=0.1, coef=1.0):
+    g = grads * coef
+    m = beta1 * m + (1 - beta1) * g
+    v = beta2 * v + (1 - beta2) * g * g
+    p = params * (1 - lr * weight_decay * mask)
+    return p - lr * m / (np.sqrt(v) + eps), m, v
+
+
+def _lr_warmup_from_zero(it, max_lr=6e-4, min_lr=None, warmup=715, decay_end=19073):
+    if it < warmup:
+        return max_lr * it / warmup
+    return _orig_lr(it, max_lr, min_lr, warmup, decay_end)
+
+
+def _clip_always(norm, max_norm):
+    return max_norm / (norm + 1e-6)
+
+
+def _decay_all(cfg, dtype=np.float64):
+    return np.ones(O.num_params(cfg), dtype)
+
+
+_orig_ce, _orig_adamw, _orig_lr = O.cross_entropy, O.adamw, O.get_lr
+
+MUTANTS = [
+    ("layernorm_fwd", _ln_unbiased),
+    ("layernorm_bwd", _ln_bwd_no_mean_term),
+    ("gelu_fwd", _gelu_exact),
+    ("gelu_bwd", _gelu_bwd_sign),
+    ("causal_attention_fwd", _attn_no_scale),
+    ("causal_attention_fwd", _attn_mask_inclusive),
+    ("causal_attention_bwd", _attn_bwd_transposed),
+    ("cross_entropy", _ce_unmasked_pad),
+    ("cross_entropy", _ce_sum_not_mean),
+    ("adamw", _adamw_coupled),
+    ("adamw", _adamw_eps_inside),
+    ("adamw", _adamw_no_bias_correction),
+    ("get_lr", _lr_warmup_from_zero),
+    ("clip_coef", _clip_always),
+    ("decay_mask", _decay_all),
+]
+
+# the pins that should catch mistakes in the model and optimizer
+PIN_TESTS = [
+    lambda: pins.test_layernorm_brute_force_and_invariants(),
+    lambda: pins.test_gelu_tanh_form_and_derivative(),
+    lambda: pins.test_ops_match_pytorch_functional(),
+    lambda: pins.test_attention_brute_force_loops(),
+    lambda: pins.test_cross_entropy_against_logsumexp_and_invariants(),
+    lambda: pins.test_model_matches_pytorch_autograd(pins.micro_cfg()),
+    lambda: pins.test_finite_differences_every_tensor(),
+    lambda: pins.test_adamw_first_step_closed_form(),
+    lambda: pins.test_adamw_matches_torch_optimizer_over_steps(),
+    lambda: pins.test_lr_schedule_matches_page_lab(),
+    lambda: pins.test_lr_schedule_build_nanogpt_shape(),
+    lambda: pins.test_clip_against_pytorch(),
+    lambda: pins.test_decay_mask_groups(),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTANTS, ids=[f"{n}:{f.__name__}" for n, f in MUTANTS])
+def test_mutant_is_caught(name, fn, monkeypatch):
+    monkeypatch.setattr(O, name, fn)
+    caught = []
+    for i, pin in enumerate(PIN_TESTS):
+        try:
+            pin()
+        except AssertionError:
+            caught.append(i)
+            break
+    assert caught, f"no pin fails when {name} is replaced by {fn.__name__}"
