@@ -1,0 +1,183 @@
+"""Throughput of one GPT-2 124M bf16 training step on one MI355X.
+
+A step is forward + loss, backward and one AdamW update (with global-norm
+clipping) on a micro-batch of B=16 sequences of T=1024 tokens: the workload of
+"Let's reproduce GPT-2 (124M)" (Speed Stack chapters; 90 ms per step on one
+A100 after every lever).  Inputs are synthetic: Zipf(1.1) token ids over the
+GPT-2 vocabulary, N(0, 0.02) weights with 0.02/sqrt(24) residual
+projections, all resident in HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "gpt2"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+A100_TOKENS_PER_S = 182000.0  # the pages' number for this workload (A100 SXM, 90 ms)
+
+
+def flops_per_token(dims, T):
+    """6N + 12 L H Q T with N the non-embedding parameters (position table
+    excluded), as the MFU estimator of "nanoGPT" Part IV Stage 6."""
+    from transformer_lm_02_amd import synth
+    N = synth.n_params(dims) - dims["block_size"] * dims["n_embd"]
+    hs = dims["n_embd"] // dims["n_head"]
+    return 6 * N + 12 * dims["n_layer"] * dims["n_head"] * hs * T
+
+
+def time_dominant_kernel(torch, bd, B, T, dims, reps=20):
+    """LM-head forward product (16384 x 768 x 50304, bf16 -> bf16), timed
+    with events on the stream it is launched on."""
+    M, N, K = B * T, dims["padded_vocab"], dims["n_embd"]
+    g = torch.Generator(device="cuda").manual_seed(7)
+    A = (torch.randn((M, K), device="cuda", generator=g) * 1.0).to(torch.bfloat16)
+    W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    import ctypes
+    s = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(s.cuda_stream)
+    args = (1, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(W.data_ptr()), None,
+            ctypes.c_void_p(C.data_ptr()), 0, M, N, K, sp)
+    for _ in range(3):
+        bd.check(bd.lib.gpt_op_linear(*args), "gpt_op_linear")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        bd.lib.gpt_op_linear(*args)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * M * N * K
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "gemm_mfma_kernel<256,128,k-contig,k-contig,bf16 out> (tied LM head forward)",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "ms_per_launch": round(ms, 4), "flops_per_launch": flops, "traffic": None}
+
+
+def cpu_baseline(dims, seed=1338):
+    """The float64 oracle (as it stands) on a bounded sample of the workload:
+    one full step (forward, backward, clip, AdamW) on one sequence of 1024
+    tokens with the full model; tokens/s scales linearly in the batch."""
+    from oracle import gpt_oracle as O
+    from transformer_lm_02_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    cfg = O.Config(**{k: dims[k] for k in synth.MODEL_KEYS})
+    params = synth.init_params(dims, seed=1337).astype(np.float64)
+    idx, tgt = synth.tokens(dims, seed=seed, batch=1)
+    zeros = np.zeros_like(params)
+    t0 = time.perf_counter()
+    O.train_step(params, zeros, zeros, 1, [(idx, tgt)], cfg, lr=6e-4)
+    dt = time.perf_counter() - t0
+    return {"value": round(idx.size / dt, 2), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "sample": f"1 x 1024 tokens, full 124M model, float64 numpy step "
+                                        f"(fwd+bwd+clip+AdamW) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the data-parallel exchange is not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from transformer_lm_02_amd import binding as bd
+    from transformer_lm_02_amd import synth
+
+    dims = synth.WORKLOADS[WORKLOAD]
+    B, T = dims["batch"], dims["block_size"]
+    print(f"[bench] building model {WORKLOAD} B={B} T={T}", file=sys.stderr, flush=True)
+    params = synth.init_params(dims, seed=1337)
+    model = bd.GPT(dims, bd.GPT_BF16, max_batch=B, init_params=params)
+    nb = 4
+    batches = []
+    for i in range(nb):
+        idx, tgt = synth.tokens(dims, seed=1338 + i)
+        batches.append((torch.as_tensor(idx).cuda(), torch.as_tensor(tgt).cuda()))
+    torch.cuda.synchronize()
+
+    def step(i):
+        idx, tgt = batches[i % nb]
+        model.forward(idx, tgt)
+        model.backward(zero_first=True)
+        lr = min(6e-4 * (i + 1) / 715, 6e-4)
+        model.adamw_step(lr=lr, t=i + 1, max_norm=1.0)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(s)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    loss = float(model.scalars[0].item())
+    norm = float(model.scalars[1].item())
+    tokens = B * T
+    value = tokens / (ms * 1e-3)
+    fpt = flops_per_token(dims, T)
+    mfu = fpt * tokens / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    print(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), loss {loss:.4f}, "
+          f"norm {norm:.4f}, MFU {mfu:.4f}", file=sys.stderr, flush=True)
+    roof = None
+    if not args.no_kernel_timing:
+        roof = time_dominant_kernel(torch, bd, B, T, dims)
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(dims)
+    out = {
+        "metric": "train tokens/sec + ms/step + MFU, GPT-2 124M bf16 B=16 T=1024, 1 MI355X",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "mfu": round(mfu, 4),
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": round(value / A100_TOKENS_PER_S, 3),
+        "baseline": "pages' 90 ms/step = ~182,000 tokens/s on one A100 SXM (context)",
+        "dtype": "bf16", "data": "synthetic (Zipf(1.1) token ids; random-init weights)",
+        "config": {"workload": "GPT-2 124M training step (fwd+bwd+clip+AdamW), vocab 50304 "
+                               "(pad masked), B=16, T=1024", "global_batch": B, "seq_len": T,
+                   "flops_per_step": fpt * tokens, "loss": round(loss, 4), "grad_norm": round(norm, 4)},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

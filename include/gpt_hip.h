@@ -1,0 +1,193 @@
+/*
+ * gpt_hip.h - C ABI of libgpt_hip.so: one GPT-2 training step (forward,
+ * backward, fused AdamW) on an MI355X (gfx950), written in HIP.
+ *
+ * The model is the decoder-only pre-norm Transformer of "nanoGPT"
+ * (stanleyjacob.dev), Part IV Stage 4 and Part V Deep dive 1: token plus
+ * learned position embeddings, n_layer blocks of x += attn(ln_1(x)) and
+ * x += mlp(ln_2(x)) with causal multi-head self-attention and a tanh-GELU MLP,
+ * a final LayerNorm and an LM head tied to the token embedding, over a
+ * vocabulary padded to a multiple of 64 ("Let's reproduce GPT-2 (124M)",
+ * chapter "Nice/Ugly Numbers": 50257 -> 50304).
+ *
+ * Conventions shared by every entry point:
+ *   - Device memory is owned by the caller.  The library never allocates or
+ *     frees device memory; the handle holds host metadata only.
+ *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
+ *     work on it; nothing synchronises, except gpt_read_flags.  Scalars that
+ *     the step produces (loss, gradient norm) are written to device memory.
+ *   - Return value: 0 on success, a negative GPT_E* code on failure.  On
+ *     failure nothing has been enqueued.  gpt_strerror names the code.
+ *   - All float arguments and buffers are IEEE fp32 unless stated.
+ *
+ * Canonical flat parameter order (fp32, also used for grads, adam_m, adam_v):
+ *   wte[Vp][d], wpe[block_size][d], then for each layer
+ *   ln1.w[d] ln1.b[d] attn.w[3d][d] attn.b[3d] aproj.w[d][d] aproj.b[d]
+ *   ln2.w[d] ln2.b[d] fc.w[4d][d] fc.b[4d] mproj.w[d][4d] mproj.b[d],
+ *   then lnf.w[d] lnf.b[d].  Linear weights are [out][in].  The tied LM head
+ *   is wte itself ("nanoGPT", Deep dive 1, weight tying).
+ */
+#ifndef GPT_HIP_H
+#define GPT_HIP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GPT_OK = 0,
+  GPT_EINVAL = -1,   /* bad config or argument, null pointer, B > max_batch */
+  GPT_ESEQLEN = -2,  /* T > block_size ("Let's reproduce GPT-2 (124M)",
+                        chapter "Implementing the forward pass to get logits") */
+  GPT_ESTATE = -3,   /* backward without a preceding forward with targets */
+  GPT_EHIP = -4,     /* a HIP call failed; gpt_strerror adds its message */
+  GPT_EUNSUPPORTED = -5 /* shape this build's kernels do not cover */
+};
+
+enum { GPT_FP32 = 0, GPT_BF16 = 1 };
+
+/* Device flag bits reported by gpt_read_flags. */
+enum {
+  GPT_FLAG_BAD_TOKEN = 1  /* an input id was outside [0, padded_vocab); its
+                             embedding row was taken as zero */
+};
+
+typedef struct {
+  int32_t vocab_size;   /* real vocabulary V; logits columns >= V are masked */
+  int32_t padded_vocab; /* Vp >= V: rows of wte */
+  int32_t block_size;   /* maximum T: rows of wpe */
+  int32_t n_layer;
+  int32_t n_head;
+  int32_t n_embd;       /* d; the MLP width is 4*d */
+  int32_t mode;         /* GPT_FP32: fp32 everywhere; GPT_BF16: bf16 matrix
+                           operands and stored activations with fp32
+                           accumulation, fp32 residual stream, LayerNorm,
+                           softmax, loss, master weights and optimizer state
+                           ("Let's reproduce GPT-2 (124M)", chapter "Float16,
+                           Gradient Scalers, BF16") */
+  int32_t max_batch;    /* largest B the workspace is sized for */
+} gpt_config;
+
+typedef struct gpt_model gpt_model;
+
+/* Sizes the caller must allocate: n_params fp32 elements for each of params,
+ * grads, adam_m and adam_v, and workspace_bytes of device memory (256-byte
+ * aligned) for activations, the bf16 weight copy and scratch.
+ * Returns GPT_EINVAL for an invalid config, GPT_EUNSUPPORTED for a valid one
+ * these kernels do not cover (bf16 mode needs n_embd % 64 == 0 and head
+ * width 64). */
+int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace_bytes);
+
+/* Bind caller-owned device buffers and create a handle.
+ * params, grads, adam_m, adam_v: device fp32 [n_params]; workspace: device
+ * memory of workspace_bytes.  init_params: device fp32 [n_params] in the
+ * canonical order, copied into params (NULL keeps params as they are).
+ * adam_m and adam_v are zeroed.  The bf16 weight copy is written.
+ * The buffers must stay valid until gpt_destroy. */
+int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads,
+             float* adam_m, float* adam_v, void* workspace, const float* init_params,
+             void* stream);
+
+/* Forward pass and, when targets != NULL, the loss and its gradient w.r.t.
+ * the logits ("nanoGPT", Part IV Stage 4; loss of "Let's reproduce GPT-2
+ * (124M)", chapter "Cross Entropy Loss").
+ * idx, targets: device int32 [B*T], row-major (b, t).  A target of -1 is
+ * ignored (ignore_index=-1); the loss is the mean over the others.
+ * loss_scale multiplies the gradient only (1/k under accumulation over k
+ * micro-batches, "nanoGPT" Part IV Stage 4).
+ * loss_out: device float, receives the unscaled mean loss (may be NULL).
+ * logits_out: optional device buffer [B*T][Vp] (fp32 in GPT_FP32 mode, bf16
+ * in GPT_BF16 mode) receiving the logits before the loss is taken.
+ * Errors: GPT_EINVAL (B < 1, B > max_batch, null idx), GPT_ESEQLEN. */
+int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets,
+                     int32_t B, int32_t T, float loss_scale, float* loss_out,
+                     void* logits_out, void* stream);
+
+/* Backward pass of the last forward (which must have had targets).
+ * zero_first != 0: grads = new gradient; else grads += new gradient
+ * (accumulation until zero_grad, "nanoGPT" Deep dive 2). */
+int gpt_backward(gpt_model* h, int32_t zero_first, void* stream);
+
+/* Global-norm clipping and one AdamW update of params, adam_m, adam_v
+ * ("andrej-karpathy-lets-reproduce-gpt-2", the optimization recipe: betas
+ * (0.9, 0.95), eps 1e-8, clip 1.0, weight decay 0.1 on 2-D tensors only).
+ *   norm = ||grads||_2 over all elements; coef = min(1, max_norm/(norm+1e-6))
+ *   (max_norm <= 0: coef = 1); g = coef*grad;
+ *   m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+ *   p = p (1 - lr wd [p is in a 2-D tensor]);
+ *   p = p - lr (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps).
+ * t: 1-based optimizer step.  norm_out: device float receiving the pre-clip
+ * norm (may be NULL).  skip_nonfinite != 0: when the norm is not finite,
+ * params, adam_m and adam_v are left untouched.  grads are not modified. */
+int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
+                   float weight_decay, float max_norm, int32_t t,
+                   int32_t skip_nonfinite, float* norm_out, void* stream);
+
+/* Synchronise `stream`, return the device flags (GPT_FLAG_*) raised since the
+ * last call in *flags, and clear them. */
+int gpt_read_flags(gpt_model* h, int32_t* flags, void* stream);
+
+void gpt_destroy(gpt_model* h);
+
+const char* gpt_strerror(int code);
+
+/* ---------------------------------------------------------------------------
+ * Single-operation entry points.  They run one kernel of the step on caller
+ * buffers so each can be checked and timed on its own.  All pointers are
+ * device pointers; matrices are row-major; `act` buffers are fp32 when
+ * bf16 == 0 and bf16 (raw uint16 storage) when bf16 != 0.
+ * ------------------------------------------------------------------------- */
+
+/* C = A B^T over K, plus optional bias[n] ("nanoGPT" Deep dive 1: the Linear
+ * layers).  A: act [M][K], B: act [N][K], bias: fp32 [N] or NULL,
+ * C: act [M][N] (fp32 when out_f32 != 0).  bf16 needs K % 8 == 0. */
+int gpt_op_linear(int32_t bf16, const void* A, const void* B, const float* bias,
+                  void* C, int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* dW (+)= dY^T X: dY act [M][N], X act [M][K], dW fp32 [N][K];
+ * accumulate != 0 adds to dW.  The weight gradient of a Linear layer. */
+int gpt_op_linear_dw(int32_t bf16, const void* dY, const void* X, float* dW,
+                     int32_t accumulate, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* dX = dY W: dY act [M][N], W act [N][K], dX fp32 [M][K].  The input
+ * gradient of a Linear layer. */
+int gpt_op_linear_dx(int32_t bf16, const void* dY, const void* W, float* dX,
+                     int32_t M, int32_t N, int32_t K, void* stream);
+
+/* Causal attention forward over qkv act [B*T][3*C] (q | k | v column blocks,
+ * head h at columns h*hs) -> out act [B*T][C], lse fp32 [B][H][T]
+ * (natural-log row logsumexp of the scaled scores).  "nanoGPT" Deep dive 1,
+ * the manual path: softmax(q k^T / sqrt(hs) with -inf above the diagonal) v. */
+int gpt_op_attention_fwd(int32_t bf16, const void* qkv, void* out, float* lse,
+                         int32_t B, int32_t T, int32_t H, int32_t C, void* stream);
+
+/* Its backward: dout act [B*T][C] -> dqkv act [B*T][3*C] (every element
+ * written).  D: fp32 scratch [B][H][T], receives rowsum(dout * out). */
+int gpt_op_attention_bwd(int32_t bf16, const void* qkv, const void* out,
+                         const float* lse, const void* dout, void* dqkv, float* D,
+                         int32_t B, int32_t T, int32_t H, int32_t C, void* stream);
+
+/* y = LayerNorm(x) w + b per row (biased variance, eps 1e-5):
+ * x fp32 [M][C] -> y act [M][C], mean and rstd fp32 [M]. */
+int gpt_op_layernorm_fwd(int32_t bf16, const float* x, const float* w, const float* b,
+                         void* y, float* mean, float* rstd, int32_t M, int32_t C,
+                         void* stream);
+
+/* Masked softmax cross-entropy, in place: logits act [N][ldv] -> dlogits
+ * (loss_scale * (softmax - onehot) / n_valid over columns < V, zero for
+ * columns in [V, ldv)); loss: device fp32 scalar = mean over targets >= 0.
+ * row_loss: device fp32 [N] receiving each row's loss (0 if ignored);
+ * n_valid: device int32 receiving the count of targets >= 0.
+ * bf16 needs ldv % 8 == 0 and ldv <= 53248. */
+int gpt_op_cross_entropy(int32_t bf16, void* logits, const int32_t* targets,
+                         float* loss, float* row_loss, int32_t* n_valid,
+                         float loss_scale, int32_t N, int32_t V, int32_t ldv,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT_HIP_H */

@@ -1,0 +1,187 @@
+"""Kernel-level parity on the GPU: each single-op entry point of the C-ABI
+against the plain definition (the oracle's functions, or numpy float64 for a
+bare matrix product) on the same seeded inputs.  Shapes span several tiles
+and ragged tails; bf16 inputs are rounded to bf16 before the reference sees
+them, so the tolerances measure only the kernel's own arithmetic."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import gpt_oracle as O
+from tests.helpers import bf16_round, case, cosine, max_rel, rel_err, to_dev, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global bd
+    from transformer_lm_02_amd import binding as bd_mod
+    bd = bd_mod
+    yield
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * np.float32(scale)
+
+
+# ---------------------------------------------------------------- matrix products
+LINEAR_SHAPES = [(256, 2304, 768), (300, 200, 136), (1000, 768, 3072), (64, 128, 64),
+                 (129, 50304, 768), (4100, 4800, 1600)]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
+def test_linear_bf16(M, N, K):
+    case(f"linear bf16 M={M} N={N} K={K}")
+    A, B = bf16_round(rnd((M, K), 1)), bf16_round(rnd((N, K), 2, 0.05))
+    bias = rnd(N, 3)
+    ref = A @ B.T + bias
+    C = bd.op_linear(to_dev(A, torch.bfloat16), to_dev(B, torch.bfloat16),
+                     torch.as_tensor(bias).cuda(), out_f32=True)
+    got = to_np(C)
+    assert rel_err(got, ref) < 1e-5 and max_rel(got, ref) < 1e-4
+    Cb = bd.op_linear(to_dev(A, torch.bfloat16), to_dev(B, torch.bfloat16),
+                      torch.as_tensor(bias).cuda(), out_f32=False)
+    assert max_rel(to_np(Cb), ref) < 8e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(16384, 768, 768), (1000, 384, 1536), (77, 64, 64),
+                                   (2048, 50304, 768), (8192, 1600, 4800)])
+def test_linear_dw_bf16(M, N, K):
+    case(f"linear_dw bf16 M={M} N={N} K={K}")
+    dY, X = bf16_round(rnd((M, N), 4, 0.01)), bf16_round(rnd((M, K), 5))
+    ref = dY.T @ X
+    got = to_np(bd.op_linear_dw(to_dev(dY, torch.bfloat16), to_dev(X, torch.bfloat16)))
+    assert rel_err(got, ref) < 1e-5 and max_rel(got, ref) < 1e-4
+    # accumulate
+    dW = torch.as_tensor(np.ones((N, K), np.float32)).cuda()
+    got2 = to_np(bd.op_linear_dw(to_dev(dY, torch.bfloat16), to_dev(X, torch.bfloat16), dW))
+    assert rel_err(got2, ref + 1.0) < 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(16384, 768, 768), (300, 200, 136), (512, 50304, 768),
+                                   (1000, 3072, 768), (257, 4800, 1600)])
+def test_linear_dx_bf16(M, N, K):
+    case(f"linear_dx bf16 M={M} N={N} K={K}")
+    dY, W = bf16_round(rnd((M, N), 6, 0.01)), bf16_round(rnd((N, K), 7, 0.02))
+    ref = dY @ W
+    got = to_np(bd.op_linear_dx(to_dev(dY, torch.bfloat16), to_dev(W, torch.bfloat16)))
+    assert rel_err(got, ref) < 1e-5 and max_rel(got, ref) < 1e-4
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 192, 64), (70, 33, 17)])
+def test_linear_family_fp32(M, N, K):
+    case(f"linear family fp32 M={M} N={N} K={K}")
+    A, B, bias = rnd((M, K), 8), rnd((N, K), 9), rnd(N, 10)
+    got = to_np(bd.op_linear(to_dev(A, torch.float32), to_dev(B, torch.float32),
+                             torch.as_tensor(bias).cuda(), out_f32=True))
+    assert rel_err(got, A.astype(np.float64) @ B.T + bias) < 1e-6
+    dY = rnd((M, N), 11)
+    got = to_np(bd.op_linear_dw(to_dev(dY, torch.float32), to_dev(A, torch.float32)))
+    assert rel_err(got, dY.astype(np.float64).T @ A) < 1e-6
+    got = to_np(bd.op_linear_dx(to_dev(dY, torch.float32), to_dev(B, torch.float32)))
+    assert rel_err(got, dY.astype(np.float64) @ B) < 1e-6
+
+
+# ---------------------------------------------------------------- attention
+def split_heads(qkv, B, T, H):
+    C = qkv.shape[1] // 3
+    hs = C // H
+    return [qkv[:, i * C:(i + 1) * C].reshape(B, T, H, hs).transpose(0, 2, 1, 3) for i in range(3)]
+
+
+def merge_heads(x):
+    B, H, T, hs = x.shape
+    return x.transpose(0, 2, 1, 3).reshape(B * T, H * hs)
+
+
+ATTN_CASES = [  # (bf16, B, T, H, hs)
+    (True, 2, 256, 3, 64), (True, 1, 200, 2, 64), (True, 1, 1024, 2, 64), (True, 3, 65, 1, 64),
+    (True, 1, 1, 2, 64), (True, 2, 96, 2, 32), (False, 4, 64, 4, 16), (False, 1, 37, 2, 24)]
+
+
+@pytest.mark.parametrize("bf,B,T,H,hs", ATTN_CASES)
+def test_attention_fwd_bwd(bf, B, T, H, hs):
+    case(f"attention bf16={bf} B={B} T={T} H={H} hs={hs}")
+    C = H * hs
+    dt = torch.bfloat16 if bf else torch.float32
+    rd = bf16_round if bf else (lambda a: np.asarray(a, np.float64))
+    qkv = rd(rnd((B * T, 3 * C), 12))
+    q, k, v = split_heads(qkv, B, T, H)
+    ref_o, ref_p = O.causal_attention_fwd(q, k, v)
+    s = (q @ k.transpose(0, 1, 3, 2)) / math.sqrt(hs)
+    s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
+    ref_lse = np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1)) + s.max(-1)
+    dqkv_dev = to_dev(qkv, dt)
+    out, lse = bd.op_attention_fwd(dqkv_dev, B, T, H)
+    got_o = to_np(out)
+    tol = 2e-2 if bf else 1e-5
+    assert max_rel(got_o, merge_heads(ref_o)) < tol
+    assert np.abs(to_np(lse) - ref_lse).max() < (2e-3 if bf else 1e-5)
+
+    dout = rd(rnd((B * T, C), 13))
+    do = dout.reshape(B, T, H, hs).transpose(0, 2, 1, 3)
+    dq, dk, dv = O.causal_attention_bwd(do, q, k, v, ref_p)
+    ref_d = np.concatenate([merge_heads(t) for t in (dq, dk, dv)], axis=1)
+    got_d = to_np(bd.op_attention_bwd(dqkv_dev, out, lse, to_dev(dout, dt), B, T, H))
+    for i, name in enumerate("qkv"):
+        g, r = got_d[:, i * C:(i + 1) * C], ref_d[:, i * C:(i + 1) * C]
+        if bf:
+            assert cosine(g, r) > 0.999, name
+            assert rel_err(g, r) < 3e-2, name
+        else:
+            assert rel_err(g, r) < 1e-5, name
+
+
+def test_attention_forward_is_deterministic_and_causal():
+    case("attention causal bit-identity bf16 B=2 T=512 H=2")
+    B, T, H, hs = 2, 512, 2, 64
+    C = H * hs
+    qkv = bf16_round(rnd((B * T, 3 * C), 14))
+    out0, _ = bd.op_attention_fwd(to_dev(qkv, torch.bfloat16), B, T, H)
+    out1, _ = bd.op_attention_fwd(to_dev(qkv, torch.bfloat16), B, T, H)
+    assert torch.equal(out0, out1)
+    t = 300
+    qkv2 = qkv.reshape(B, T, 3 * C).copy()
+    qkv2[:, t + 1:] = bf16_round(rnd(qkv2[:, t + 1:].shape, 15))
+    out2, _ = bd.op_attention_fwd(to_dev(qkv2.reshape(B * T, 3 * C), torch.bfloat16), B, T, H)
+    a = out0.view(B, T, C)[:, :t + 1]
+    b = out2.view(B, T, C)[:, :t + 1]
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- layernorm
+@pytest.mark.parametrize("bf,M,C", [(True, 1000, 768), (True, 333, 1600), (False, 256, 64),
+                                    (True, 16384, 768), (False, 7, 384)])
+def test_layernorm_fwd(bf, M, C):
+    case(f"layernorm bf16={bf} M={M} C={C}")
+    x = rnd((M, C), 16, 3.0) + 1.0
+    w, b = rnd(C, 17) + 1.0, rnd(C, 18)
+    ref, (xhat, rstd) = O.layernorm_fwd(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+    y, mean, rs = bd.op_layernorm_fwd(torch.as_tensor(x).cuda(), torch.as_tensor(w).cuda(),
+                                      torch.as_tensor(b).cuda(), bf16=bf)
+    assert max_rel(to_np(y), ref) < (8e-3 if bf else 2e-6)
+    assert np.abs(to_np(mean) - x.astype(np.float64).mean(1)).max() < 1e-5
+    assert max_rel(to_np(rs), rstd[:, 0]) < 1e-5
+
+
+# ---------------------------------------------------------------- cross-entropy
+@pytest.mark.parametrize("bf,N,V,ldv", [(True, 512, 50257, 50304), (True, 300, 65, 128),
+                                        (False, 256, 65, 65), (False, 100, 37, 64),
+                                        (True, 2048, 50257, 50304)])
+def test_cross_entropy(bf, N, V, ldv):
+    case(f"cross-entropy bf16={bf} N={N} V={V} ldv={ldv}")
+    rd = bf16_round if bf else (lambda a: np.asarray(a, np.float64))
+    z = rd(rnd((N, ldv), 19, 2.0))
+    tgt = np.random.default_rng(20).integers(0, V, N).astype(np.int32)
+    tgt[::17] = -1
+    loss_ref, dz_ref = O.cross_entropy(z, tgt, V, loss_scale=0.5)
+    zd = to_dev(z, torch.bfloat16 if bf else torch.float32)
+    loss, row, nv = bd.op_cross_entropy(zd, torch.as_tensor(tgt).cuda(), V, loss_scale=0.5)
+    assert int(nv.item()) == int((tgt >= 0).sum())
+    assert abs(float(loss.item()) - loss_ref) < (1e-4 if bf else 1e-5) * max(1.0, loss_ref)
+    got = to_np(zd)
+    assert np.all(got[:, V:] == 0)
+    assert max_rel(got, dz_ref) < (1e-2 if bf else 1e-5)

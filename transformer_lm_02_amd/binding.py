@@ -1,0 +1,239 @@
+"""Thin Python binding over libgpt_hip.so (argument marshalling only).
+
+The C entry points keep their names (gpt_init, gpt_forward_loss,
+gpt_backward, gpt_adamw_step, ...).  PyTorch supplies device memory and the
+current HIP stream; every step of the computation runs in the library's
+kernels.  Importing this module fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgpt_hip.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m transformer_lm_02_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+GPT_OK, GPT_EINVAL, GPT_ESEQLEN, GPT_ESTATE, GPT_EHIP, GPT_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+GPT_FP32, GPT_BF16 = 0, 1
+GPT_FLAG_BAD_TOKEN = 1
+
+
+class gpt_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "vocab_size", "padded_vocab", "block_size", "n_layer", "n_head", "n_embd", "mode",
+        "max_batch")]
+
+
+_p, _i32, _i64, _f = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+_SIGS = {
+    "gpt_query_sizes": [ctypes.POINTER(gpt_config), ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
+    "gpt_init": [ctypes.POINTER(_p), ctypes.POINTER(gpt_config), _p, _p, _p, _p, _p, _p, _p],
+    "gpt_forward_loss": [_p, _p, _p, _i32, _i32, _f, _p, _p, _p],
+    "gpt_backward": [_p, _i32, _p],
+    "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
+    "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
+    "gpt_op_linear": [_i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
+    "gpt_op_linear_dw": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
+    "gpt_op_linear_dx": [_i32, _p, _p, _p, _i32, _i32, _i32, _p],
+    "gpt_op_attention_fwd": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
+    "gpt_op_attention_bwd": [_i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
+    "gpt_op_layernorm_fwd": [_i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _p],
+    "gpt_op_cross_entropy": [_i32, _p, _p, _p, _p, _p, _f, _i32, _i32, _i32, _p],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_int
+lib.gpt_destroy.argtypes = [_p]
+lib.gpt_destroy.restype = None
+lib.gpt_strerror.argtypes = [ctypes.c_int]
+lib.gpt_strerror.restype = ctypes.c_char_p
+
+
+class GptError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {lib.gpt_strerror(code).decode()} (code {code})")
+        self.code = code
+
+
+def check(code: int, where: str) -> None:
+    if code != GPT_OK:
+        raise GptError(code, where)
+
+
+def make_config(vocab_size, padded_vocab, block_size, n_layer, n_head, n_embd, mode, max_batch):
+    return gpt_config(vocab_size, padded_vocab, block_size, n_layer, n_head, n_embd, mode, max_batch)
+
+
+def query_sizes(cfg: gpt_config):
+    n, ws = _i64(), _i64()
+    check(lib.gpt_query_sizes(ctypes.byref(cfg), ctypes.byref(n), ctypes.byref(ws)), "gpt_query_sizes")
+    return n.value, ws.value
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class GPT:
+    """Device buffers (torch tensors) plus the library handle."""
+
+    def __init__(self, dims: dict, mode: int, max_batch: int, init_params=None, device="cuda"):
+        import torch
+        self.dims = dict(dims)
+        self.mode = mode
+        self.cfg = make_config(dims["vocab_size"], dims["padded_vocab"], dims["block_size"],
+                               dims["n_layer"], dims["n_head"], dims["n_embd"], mode, max_batch)
+        self.n_params, ws_bytes = query_sizes(self.cfg)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.params = torch.empty(self.n_params, **f32)
+        self.grads = torch.empty(self.n_params, **f32)
+        self.adam_m = torch.empty(self.n_params, **f32)
+        self.adam_v = torch.empty(self.n_params, **f32)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        self.scalars = torch.zeros(4, **f32)  # loss, norm
+        init = None
+        if init_params is not None:
+            init = torch.as_tensor(np.asarray(init_params, dtype=np.float32)).to(device)
+            assert init.numel() == self.n_params
+        h = ctypes.c_void_p()
+        check(lib.gpt_init(ctypes.byref(h), ctypes.byref(self.cfg), _ptr(self.params),
+                           _ptr(self.grads), _ptr(self.adam_m), _ptr(self.adam_v),
+                           _ptr(self.workspace), _ptr(init), _stream()), "gpt_init")
+        self.handle = h
+        self._init = init
+
+    @property
+    def act_dtype(self):
+        import torch
+        return torch.bfloat16 if self.mode == GPT_BF16 else torch.float32
+
+    def forward(self, idx, targets=None, loss_scale=1.0, logits=False):
+        """idx/targets: int32 cuda tensors [B, T].  Returns (loss tensor [1] or
+        None, logits tensor [B, T, Vp] or None)."""
+        import torch
+        B, T = idx.shape
+        out = None
+        if logits:
+            out = torch.empty((B, T, self.dims["padded_vocab"]), dtype=self.act_dtype, device=idx.device)
+        loss = self.scalars[0:1] if targets is not None else None
+        check(lib.gpt_forward_loss(self.handle, _ptr(idx), _ptr(targets), B, T, loss_scale,
+                                   _ptr(loss), _ptr(out), _stream()), "gpt_forward_loss")
+        return loss, out
+
+    def backward(self, zero_first=True):
+        check(lib.gpt_backward(self.handle, 1 if zero_first else 0, _stream()), "gpt_backward")
+
+    def adamw_step(self, lr, t, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
+                   skip_nonfinite=False):
+        norm = self.scalars[1:2]
+        check(lib.gpt_adamw_step(self.handle, lr, beta1, beta2, eps, weight_decay, max_norm, t,
+                                 1 if skip_nonfinite else 0, _ptr(norm), _stream()), "gpt_adamw_step")
+        return norm
+
+    def read_flags(self) -> int:
+        f = _i32()
+        check(lib.gpt_read_flags(self.handle, ctypes.byref(f), _stream()), "gpt_read_flags")
+        return f.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib.gpt_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# --------------------------------------------------------------------------- single ops
+def _bf(t):
+    import torch
+    return 1 if t.dtype == torch.bfloat16 else 0
+
+
+def op_linear(A, B, bias=None, out_f32=False):
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    C = torch.empty((M, N), dtype=torch.float32 if out_f32 else A.dtype, device=A.device)
+    check(lib.gpt_op_linear(_bf(A), _ptr(A), _ptr(B), _ptr(bias), _ptr(C), int(out_f32), M, N, K,
+                            _stream()), "gpt_op_linear")
+    return C
+
+
+def op_linear_dw(dY, X, dW=None):
+    import torch
+    M, N = dY.shape
+    K = X.shape[1]
+    acc = dW is not None
+    if dW is None:
+        dW = torch.empty((N, K), dtype=torch.float32, device=dY.device)
+    check(lib.gpt_op_linear_dw(_bf(dY), _ptr(dY), _ptr(X), _ptr(dW), int(acc), M, N, K, _stream()),
+          "gpt_op_linear_dw")
+    return dW
+
+
+def op_linear_dx(dY, W):
+    import torch
+    M, N = dY.shape
+    K = W.shape[1]
+    dX = torch.empty((M, K), dtype=torch.float32, device=dY.device)
+    check(lib.gpt_op_linear_dx(_bf(dY), _ptr(dY), _ptr(W), _ptr(dX), M, N, K, _stream()),
+          "gpt_op_linear_dx")
+    return dX
+
+
+def op_attention_fwd(qkv, B, T, H):
+    import torch
+    C = qkv.shape[-1] // 3
+    out = torch.empty((B * T, C), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=qkv.device)
+    check(lib.gpt_op_attention_fwd(_bf(qkv), _ptr(qkv), _ptr(out), _ptr(lse), B, T, H, C, _stream()),
+          "gpt_op_attention_fwd")
+    return out, lse
+
+
+def op_attention_bwd(qkv, out, lse, dout, B, T, H):
+    import torch
+    C = qkv.shape[-1] // 3
+    dqkv = torch.empty_like(qkv)
+    D = torch.empty((B, H, T), dtype=torch.float32, device=qkv.device)
+    check(lib.gpt_op_attention_bwd(_bf(qkv), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dqkv),
+                                   _ptr(D), B, T, H, C, _stream()), "gpt_op_attention_bwd")
+    return dqkv
+
+
+def op_layernorm_fwd(x, w, b, bf16=False):
+    import torch
+    M, C = x.shape
+    y = torch.empty((M, C), dtype=torch.bfloat16 if bf16 else torch.float32, device=x.device)
+    mean = torch.empty(M, dtype=torch.float32, device=x.device)
+    rstd = torch.empty(M, dtype=torch.float32, device=x.device)
+    check(lib.gpt_op_layernorm_fwd(int(bf16), _ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(mean),
+                                   _ptr(rstd), M, C, _stream()), "gpt_op_layernorm_fwd")
+    return y, mean, rstd
+
+
+def op_cross_entropy(logits, targets, V, loss_scale=1.0):
+    """In place on logits [N, ldv]; returns (loss [1], row_loss [N], n_valid [1])."""
+    import torch
+    N, ldv = logits.shape
+    loss = torch.empty(1, dtype=torch.float32, device=logits.device)
+    row = torch.empty(N, dtype=torch.float32, device=logits.device)
+    nv = torch.empty(1, dtype=torch.int32, device=logits.device)
+    check(lib.gpt_op_cross_entropy(_bf(logits), _ptr(logits), _ptr(targets), _ptr(loss), _ptr(row),
+                                   _ptr(nv), loss_scale, N, V, ldv, _stream()), "gpt_op_cross_entropy")
+    return loss, row, nv

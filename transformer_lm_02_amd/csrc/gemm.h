@@ -1,0 +1,32 @@
+// GEMM launchers: C[m][n] = sum_k A(m,k) B(n,k), with fused epilogues.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Epilogues, applied per output element (m, n) to the fp32 accumulator:
+enum GemmEpi {
+  EPI_ACT = 0,      // out_act[m][n] = acc + bias[n]
+  EPI_F32 = 1,      // out_f32[m][n] = acc + bias[n]
+  EPI_RESID = 2,    // out_f32[m][n] = aux_f32[m][n] + acc + bias[n]   (residual add)
+  EPI_GELU = 3,     // u = acc + bias[n]; out_act = u; out2_act = gelu(u)
+  EPI_GELU_BWD = 4, // out_act[m][n] = acc * gelu'(aux_act[m][n])
+  EPI_ACCUM = 5     // out_f32[m][n] = (beta ? out_f32[m][n] : 0) + acc
+};
+
+struct GemmEpiArgs {
+  void* out = nullptr;
+  void* out2 = nullptr;
+  const void* aux = nullptr;
+  const float* bias = nullptr;
+  int ldc = 0;
+  int beta = 0;
+};
+
+// A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]; likewise B(n,k).
+// Loads of a k-contiguous operand require K % 8 == 0 (bf16); an m- or
+// n-contiguous operand reads rows k < ka_rows / kb_rows and columns below its
+// leading dimension.  Outputs are written for m < M, n < N.
+int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi,
+                const void* A, int lda, const void* B, int ldb,
+                int M, int N, int K, int ka_rows, int kb_rows,
+                const GemmEpiArgs& e, hipStream_t stream);

@@ -1,0 +1,576 @@
+// C ABI of libgpt_hip.so: host orchestration of one GPT-2 training step.
+//
+// The step is the training iteration of "nanoGPT" (stanleyjacob.dev), Part IV
+// Stages 4-5: forward (embeddings, n_layer pre-norm blocks, ln_f, tied LM
+// head, cross-entropy), backward (accumulating into grads until the caller
+// asks for a fresh start), then global-norm clipping and AdamW.  Every call
+// only enqueues kernels on the caller's stream; all device memory belongs to
+// the caller (params, grads, Adam moments and one workspace).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "gpt_hip.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* what) {
+  g_err = what;
+  return code;
+}
+int map_rc(int rc) {
+  if (rc == 0) return GPT_OK;
+  if (rc == -5) return GPT_EUNSUPPORTED;
+  hipError_t e = hipGetLastError();
+  g_err = hipGetErrorString(e);
+  return GPT_EHIP;
+}
+#define CK(x)                       \
+  do {                              \
+    int rc_ = (x);                  \
+    if (rc_) return map_rc(rc_);    \
+  } while (0)
+#define CKH(x)                                   \
+  do {                                           \
+    hipError_t e_ = (x);                         \
+    if (e_ != hipSuccess) {                      \
+      g_err = hipGetErrorString(e_);             \
+      return GPT_EHIP;                           \
+    }                                            \
+  } while (0)
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// element offsets of every tensor in the canonical flat parameter vector
+struct LayerOff {
+  int64_t ln1w, ln1b, attnw, attnb, aprojw, aprojb, ln2w, ln2b, fcw, fcb, mprojw, mprojb;
+};
+struct ParamOff {
+  int64_t wte, wpe, lnfw, lnfb, total;
+  std::vector<LayerOff> layer;
+  std::vector<std::pair<int64_t, int64_t>> tensors;  // (offset, count) in order
+  std::vector<int> is2d;
+};
+
+ParamOff param_offsets(const gpt_config& c) {
+  ParamOff p;
+  int64_t off = 0;
+  const int64_t d = c.n_embd;
+  auto take = [&](int64_t n, bool two_d) {
+    int64_t o = off;
+    p.tensors.push_back({o, n});
+    p.is2d.push_back(two_d);
+    off += n;
+    return o;
+  };
+  p.wte = take((int64_t)c.padded_vocab * d, true);
+  p.wpe = take((int64_t)c.block_size * d, true);
+  for (int l = 0; l < c.n_layer; ++l) {
+    LayerOff L;
+    L.ln1w = take(d, false);
+    L.ln1b = take(d, false);
+    L.attnw = take(3 * d * d, true);
+    L.attnb = take(3 * d, false);
+    L.aprojw = take(d * d, true);
+    L.aprojb = take(d, false);
+    L.ln2w = take(d, false);
+    L.ln2b = take(d, false);
+    L.fcw = take(4 * d * d, true);
+    L.fcb = take(4 * d, false);
+    L.mprojw = take(4 * d * d, true);
+    L.mprojb = take(d, false);
+    p.layer.push_back(L);
+  }
+  p.lnfw = take(d, false);
+  p.lnfb = take(d, false);
+  p.total = off;
+  return p;
+}
+
+// byte offsets of every buffer in the workspace
+struct WsLayer {
+  size_t x_in, ln1_mean, ln1_rstd, ln1, qkv, att, lse, x_mid, ln2_mean, ln2_rstd, ln2, u, g;
+};
+struct WsOff {
+  size_t shadow = 0;
+  std::vector<WsLayer> layer;
+  size_t x_final, lnf_mean, lnf_rstd, lnf, logits, row_loss, nvalid, flags, scal;
+  size_t dres, dres_act, dln, dbig, dO, Dbuf, ln_part, cs_part, norm_part, chunks;
+  size_t total;
+  int nchunks;
+  int64_t vi;  // logits row pitch: padded_vocab rounded up to 64
+};
+
+constexpr int64_t kChunk = 8192;
+
+WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
+  WsOff w;
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    size_t o = off;
+    off = (size_t)round_up(off + (size_t)bytes, 256);
+    return o;
+  };
+  const bool bf = c.mode == GPT_BF16;
+  const int64_t es = bf ? 2 : 4;
+  const int64_t M = (int64_t)c.max_batch * c.block_size, d = c.n_embd, H = c.n_head;
+  w.vi = round_up(c.padded_vocab, 64);
+  if (bf) w.shadow = take(p.total * 2);
+  for (int l = 0; l < c.n_layer; ++l) {
+    WsLayer L;
+    L.x_in = take(M * d * 4);
+    L.ln1_mean = take(M * 4);
+    L.ln1_rstd = take(M * 4);
+    L.ln1 = take(M * d * es);
+    L.qkv = take(M * 3 * d * es);
+    L.att = take(M * d * es);
+    L.lse = take(M * H * 4);
+    L.x_mid = take(M * d * 4);
+    L.ln2_mean = take(M * 4);
+    L.ln2_rstd = take(M * 4);
+    L.ln2 = take(M * d * es);
+    L.u = take(M * 4 * d * es);
+    L.g = take(M * 4 * d * es);
+    w.layer.push_back(L);
+  }
+  w.x_final = take(M * d * 4);
+  w.lnf_mean = take(M * 4);
+  w.lnf_rstd = take(M * 4);
+  w.lnf = take(M * d * es);
+  w.logits = take(M * w.vi * es);
+  w.row_loss = take(M * 4);
+  w.nvalid = take(4);
+  w.flags = take(4);
+  w.scal = take(16);
+  w.dres = take(M * d * 4);
+  w.dres_act = take(M * d * es);
+  w.dln = take(M * d * 4);
+  w.dbig = take(M * 4 * d * es);
+  w.dO = take(M * d * es);
+  w.Dbuf = take(M * H * 4);
+  w.ln_part = take((int64_t)layernorm_bwd_part_rows((int)M) * 3 * d * 4);
+  w.cs_part = take((int64_t)colsum_part_rows((int)M) * 4 * d * 4);
+  w.norm_part = take((int64_t)adamw_norm_blocks() * 8);
+  int64_t nch = 0;
+  for (auto& t : p.tensors) nch += (t.second + kChunk - 1) / kChunk;
+  w.nchunks = (int)nch;
+  w.chunks = take(nch * (int64_t)sizeof(AdamChunk));
+  w.total = off;
+  return w;
+}
+
+int validate(const gpt_config* c) {
+  if (!c) return fail(GPT_EINVAL, "null config");
+  if (c->vocab_size < 1 || c->padded_vocab < c->vocab_size || c->block_size < 1 ||
+      c->n_layer < 1 || c->n_head < 1 || c->n_embd < 1 || c->max_batch < 1 ||
+      (c->mode != GPT_FP32 && c->mode != GPT_BF16) || c->n_embd % c->n_head)
+    return fail(GPT_EINVAL, "invalid gpt_config");
+  const int hs = c->n_embd / c->n_head;
+  if (c->n_embd % 4 || c->n_embd > 2048 || hs > 128)
+    return fail(GPT_EUNSUPPORTED, "n_embd must be a multiple of 4, at most 2048; head width <= 128");
+  if (c->mode == GPT_BF16) {
+    if (c->n_embd % 64) return fail(GPT_EUNSUPPORTED, "bf16 mode needs n_embd % 64 == 0");
+    if (round_up(c->padded_vocab, 64) > 53248)
+      return fail(GPT_EUNSUPPORTED, "bf16 cross-entropy covers rows up to 53248 columns");
+  }
+  if ((int64_t)c->max_batch * c->block_size > (1 << 26))
+    return fail(GPT_EUNSUPPORTED, "max_batch * block_size too large");
+  return GPT_OK;
+}
+
+}  // namespace
+
+struct gpt_model {
+  gpt_config cfg;
+  ParamOff po;
+  WsOff wo;
+  float *params, *grads, *m, *v;
+  char* ws;
+  std::vector<AdamChunk> chunks;
+  bool have_fwd = false, have_targets = false;
+  int B = 0, T = 0;
+  const int32_t* idx = nullptr;
+
+  bool bf16() const { return cfg.mode == GPT_BF16; }
+  int64_t es() const { return bf16() ? 2 : 4; }
+  template <typename P = void>
+  P* at(size_t off) const { return (P*)(ws + off); }
+  float* P(int64_t off) const { return params + off; }
+  float* G(int64_t off) const { return grads + off; }
+  // matrix operand copy of a weight: bf16 copy in bf16 mode, fp32 params otherwise
+  const void* W(int64_t off) const {
+    return bf16() ? (const void*)(at<bf16_t>(wo.shadow) + off) : (const void*)(params + off);
+  }
+};
+
+extern "C" {
+
+int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace_bytes) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  ParamOff p = param_offsets(*cfg);
+  WsOff w = ws_offsets(*cfg, p);
+  if (n_params) *n_params = p.total;
+  if (workspace_bytes) *workspace_bytes = (int64_t)w.total;
+  return GPT_OK;
+}
+
+int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads, float* adam_m,
+             float* adam_v, void* workspace, const float* init_params, void* stream) {
+  if (!out) return fail(GPT_EINVAL, "null output handle");
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!params || !grads || !adam_m || !adam_v || !workspace)
+    return fail(GPT_EINVAL, "null device buffer");
+  if ((uintptr_t)workspace & 255) return fail(GPT_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  gpt_model* h = new gpt_model;
+  h->cfg = *cfg;
+  h->po = param_offsets(*cfg);
+  h->wo = ws_offsets(*cfg, h->po);
+  h->params = params;
+  h->grads = grads;
+  h->m = adam_m;
+  h->v = adam_v;
+  h->ws = (char*)workspace;
+  for (size_t i = 0; i < h->po.tensors.size(); ++i) {
+    const int64_t o = h->po.tensors[i].first, n = h->po.tensors[i].second;
+    for (int64_t c = 0; c < n; c += kChunk)
+      h->chunks.push_back({o + c, (int32_t)std::min<int64_t>(kChunk, n - c), h->po.is2d[i]});
+  }
+  const int64_t nb = h->po.total * 4;
+  hipError_t e = hipSuccess;
+  if (init_params && init_params != params)
+    e = hipMemcpyAsync(params, init_params, nb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemsetAsync(adam_m, 0, nb, s);
+  if (e == hipSuccess) e = hipMemsetAsync(adam_v, 0, nb, s);
+  if (e == hipSuccess) e = hipMemsetAsync(grads, 0, nb, s);
+  if (e == hipSuccess) e = hipMemsetAsync(h->ws + h->wo.flags, 0, 4, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->ws + h->wo.chunks, h->chunks.data(), h->chunks.size() * sizeof(AdamChunk),
+                       hipMemcpyHostToDevice, s);
+  // the host table must outlive the copy: wait for it once, at set-up
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    g_err = hipGetErrorString(e);
+    delete h;
+    return GPT_EHIP;
+  }
+  if (h->bf16()) {
+    rc = to_bf16_launch(params, h->at<bf16_t>(h->wo.shadow), h->po.total, s);
+    if (rc) {
+      delete h;
+      return map_rc(rc);
+    }
+  }
+  *out = h;
+  return GPT_OK;
+}
+
+int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
+                     float loss_scale, float* loss_out, void* logits_out, void* stream) {
+  if (!h || !idx) return fail(GPT_EINVAL, "null handle or idx");
+  const gpt_config& c = h->cfg;
+  if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
+  if (T < 1) return fail(GPT_EINVAL, "T < 1");
+  if (T > c.block_size) return fail(GPT_ESEQLEN, "T > block_size");
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = h->bf16();
+  const WsOff& w = h->wo;
+  const ParamOff& p = h->po;
+  const int M = B * T, d = c.n_embd, H = c.n_head;
+  h->have_fwd = false;
+
+  CK(embed_fwd_launch(idx, h->P(p.wte), h->P(p.wpe), h->at<float>(w.layer.empty() ? w.x_final : w.layer[0].x_in),
+                      M, T, d, c.padded_vocab, h->at<int>(w.flags), s));
+  for (int l = 0; l < c.n_layer; ++l) {
+    const WsLayer& L = w.layer[l];
+    const LayerOff& P = p.layer[l];
+    const size_t x_out = (l + 1 < c.n_layer) ? w.layer[l + 1].x_in : w.x_final;
+    CK(layernorm_fwd_launch(bf, h->at<float>(L.x_in), h->P(P.ln1w), h->P(P.ln1b), h->at(L.ln1),
+                            h->at<float>(L.ln1_mean), h->at<float>(L.ln1_rstd), M, d, s));
+    GemmEpiArgs e;
+    e.out = h->at(L.qkv);
+    e.bias = h->P(P.attnb);
+    e.ldc = 3 * d;
+    CK(gemm_launch(bf, true, true, EPI_ACT, h->at(L.ln1), d, h->W(P.attnw), d, M, 3 * d, d, d, d,
+                   e, s));
+    CK(attention_fwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), B, T, H, d, s));
+    e = GemmEpiArgs();
+    e.out = h->at(L.x_mid);
+    e.aux = h->at(L.x_in);
+    e.bias = h->P(P.aprojb);
+    e.ldc = d;
+    CK(gemm_launch(bf, true, true, EPI_RESID, h->at(L.att), d, h->W(P.aprojw), d, M, d, d, d, d, e,
+                   s));
+    CK(layernorm_fwd_launch(bf, h->at<float>(L.x_mid), h->P(P.ln2w), h->P(P.ln2b), h->at(L.ln2),
+                            h->at<float>(L.ln2_mean), h->at<float>(L.ln2_rstd), M, d, s));
+    e = GemmEpiArgs();
+    e.out = h->at(L.u);
+    e.out2 = h->at(L.g);
+    e.bias = h->P(P.fcb);
+    e.ldc = 4 * d;
+    CK(gemm_launch(bf, true, true, EPI_GELU, h->at(L.ln2), d, h->W(P.fcw), d, M, 4 * d, d, d, d,
+                   e, s));
+    e = GemmEpiArgs();
+    e.out = h->at(x_out);
+    e.aux = h->at(L.x_mid);
+    e.bias = h->P(P.mprojb);
+    e.ldc = d;
+    CK(gemm_launch(bf, true, true, EPI_RESID, h->at(L.g), 4 * d, h->W(P.mprojw), 4 * d, M, d, 4 * d,
+                   4 * d, 4 * d, e, s));
+  }
+  CK(layernorm_fwd_launch(bf, h->at<float>(w.x_final), h->P(p.lnfw), h->P(p.lnfb), h->at(w.lnf),
+                          h->at<float>(w.lnf_mean), h->at<float>(w.lnf_rstd), M, d, s));
+  {
+    GemmEpiArgs e;
+    e.out = h->at(w.logits);
+    e.ldc = (int)w.vi;
+    CK(gemm_launch(bf, true, true, EPI_ACT, h->at(w.lnf), d, h->W(p.wte), d, M, c.padded_vocab, d,
+                   d, d, e, s));
+  }
+  if (logits_out)
+    CKH(hipMemcpy2DAsync(logits_out, (size_t)c.padded_vocab * h->es(), h->at(w.logits),
+                         (size_t)w.vi * h->es(), (size_t)c.padded_vocab * h->es(), M,
+                         hipMemcpyDeviceToDevice, s));
+  if (targets) {
+    CK(count_valid_launch(targets, M, h->at<int>(w.nvalid), s));
+    CK(cross_entropy_launch(bf, h->at(w.logits), targets, h->at<float>(w.row_loss),
+                            h->at<int>(w.nvalid), loss_scale, M, c.vocab_size, (int)w.vi, s));
+    if (loss_out) CK(loss_finalize_launch(h->at<float>(w.row_loss), M, h->at<int>(w.nvalid), loss_out, s));
+  }
+  h->have_fwd = true;
+  h->have_targets = targets != nullptr;
+  h->B = B;
+  h->T = T;
+  h->idx = idx;
+  return GPT_OK;
+}
+
+int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
+  if (!h) return fail(GPT_EINVAL, "null handle");
+  if (!h->have_fwd || !h->have_targets)
+    return fail(GPT_ESTATE, "backward needs a preceding forward with targets");
+  hipStream_t s = (hipStream_t)stream;
+  const gpt_config& c = h->cfg;
+  const bool bf = h->bf16();
+  const WsOff& w = h->wo;
+  const ParamOff& p = h->po;
+  const int B = h->B, T = h->T, M = B * T, d = c.n_embd, H = c.n_head;
+  const int beta = zero_first ? 0 : 1;
+  const int vi = (int)w.vi;
+  float* dres = h->at<float>(w.dres);
+  void* dres_act = h->at(w.dres_act);
+  float* dln = h->at<float>(w.dln);
+  void* dbig = h->at(w.dbig);
+  float* ln_part = h->at<float>(w.ln_part);
+  float* cs_part = h->at<float>(w.cs_part);
+
+  // LM head: dwte (+)= dlogits^T lnf ; dlnf = dlogits wte
+  {
+    GemmEpiArgs e;
+    e.out = h->G(p.wte);
+    e.ldc = d;
+    e.beta = beta;
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, h->at(w.logits), vi, h->at(w.lnf), d,
+                   c.padded_vocab, d, M, M, M, e, s));
+    e = GemmEpiArgs();
+    e.out = dln;
+    e.ldc = d;
+    CK(gemm_launch(bf, true, false, EPI_F32, h->at(w.logits), vi, h->W(p.wte), d, M, d, vi, vi,
+                   c.padded_vocab, e, s));
+  }
+  CK(layernorm_bwd_launch(bf, dln, h->at<float>(w.x_final), h->at<float>(w.lnf_mean),
+                          h->at<float>(w.lnf_rstd), h->P(p.lnfw), dres, dres_act, 0, ln_part,
+                          h->G(p.lnfw), h->G(p.lnfb), h->G(p.layer[c.n_layer - 1].mprojb), beta, M,
+                          d, s));
+  for (int l = c.n_layer - 1; l >= 0; --l) {
+    const WsLayer& L = w.layer[l];
+    const LayerOff& P = p.layer[l];
+    // MLP projection: dW (+)= dres^T g ; du = (dres Wm) * gelu'(u)
+    GemmEpiArgs e;
+    e.out = h->G(P.mprojw);
+    e.ldc = 4 * d;
+    e.beta = beta;
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.g), 4 * d, d, 4 * d, M, M, M, e,
+                   s));
+    e = GemmEpiArgs();
+    e.out = dbig;
+    e.aux = h->at(L.u);
+    e.ldc = 4 * d;
+    CK(gemm_launch(bf, true, false, EPI_GELU_BWD, dres_act, d, h->W(P.mprojw), 4 * d, M, 4 * d, d,
+                   d, d, e, s));
+    // MLP expansion: db = colsum(du); dW (+)= du^T ln2 ; dln2 = du Wfc
+    CK(colsum_launch(bf, dbig, M, 4 * d, cs_part, h->G(P.fcb), beta, s));
+    e = GemmEpiArgs();
+    e.out = h->G(P.fcw);
+    e.ldc = d;
+    e.beta = beta;
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 4 * d, h->at(L.ln2), d, 4 * d, d, M, M, M, e,
+                   s));
+    e = GemmEpiArgs();
+    e.out = dln;
+    e.ldc = d;
+    CK(gemm_launch(bf, true, false, EPI_F32, dbig, 4 * d, h->W(P.fcw), d, M, d, 4 * d, 4 * d,
+                   4 * d, e, s));
+    CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_mid), h->at<float>(L.ln2_mean),
+                            h->at<float>(L.ln2_rstd), h->P(P.ln2w), dres, dres_act, 1, ln_part,
+                            h->G(P.ln2w), h->G(P.ln2b), h->G(P.aprojb), beta, M, d, s));
+    // attention projection: dW (+)= dres^T att ; datt = dres Wa
+    e = GemmEpiArgs();
+    e.out = h->G(P.aprojw);
+    e.ldc = d;
+    e.beta = beta;
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.att), d, d, d, M, M, M, e, s));
+    e = GemmEpiArgs();
+    e.out = h->at(w.dO);
+    e.ldc = d;
+    CK(gemm_launch(bf, true, false, EPI_ACT, dres_act, d, h->W(P.aprojw), d, M, d, d, d, d, e, s));
+    CK(attention_bwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), h->at(w.dO), dbig,
+                            h->at<float>(w.Dbuf), B, T, H, d, s));
+    // fused q|k|v projection: db = colsum(dqkv); dW (+)= dqkv^T ln1 ; dln1 = dqkv Wqkv
+    CK(colsum_launch(bf, dbig, M, 3 * d, cs_part, h->G(P.attnb), beta, s));
+    e = GemmEpiArgs();
+    e.out = h->G(P.attnw);
+    e.ldc = d;
+    e.beta = beta;
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 3 * d, h->at(L.ln1), d, 3 * d, d, M, M, M, e,
+                   s));
+    e = GemmEpiArgs();
+    e.out = dln;
+    e.ldc = d;
+    CK(gemm_launch(bf, true, false, EPI_F32, dbig, 3 * d, h->W(P.attnw), d, M, d, 3 * d, 3 * d,
+                   3 * d, e, s));
+    CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_in), h->at<float>(L.ln1_mean),
+                            h->at<float>(L.ln1_rstd), h->P(P.ln1w), dres, dres_act, 1, ln_part,
+                            h->G(P.ln1w), h->G(P.ln1b), l > 0 ? h->G(p.layer[l - 1].mprojb) : nullptr,
+                            beta, M, d, s));
+  }
+  // embeddings: dwte[idx] += dx ; dwpe[t] (+)= sum_b dx
+  CK(embed_bwd_launch(h->idx, dres, h->G(p.wte), h->G(p.wpe), B, T, c.block_size, d,
+                      c.padded_vocab, beta, s));
+  return GPT_OK;
+}
+
+int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay,
+                   float max_norm, int32_t t, int32_t skip_nonfinite, float* norm_out,
+                   void* stream) {
+  if (!h) return fail(GPT_EINVAL, "null handle");
+  if (t < 1) return fail(GPT_EINVAL, "t must be >= 1");
+  hipStream_t s = (hipStream_t)stream;
+  const WsOff& w = h->wo;
+  CK(adamw_launch(h->params, h->grads, h->m, h->v,
+                  h->bf16() ? h->at<bf16_t>(w.shadow) : nullptr, h->po.total,
+                  h->at<AdamChunk>(w.chunks), w.nchunks, h->at<double>(w.norm_part),
+                  h->at<float>(w.scal), norm_out, lr, beta1, beta2, eps, weight_decay, max_norm, t,
+                  skip_nonfinite, s));
+  return GPT_OK;
+}
+
+int gpt_read_flags(gpt_model* h, int32_t* flags, void* stream) {
+  if (!h || !flags) return fail(GPT_EINVAL, "null argument");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t v = 0;
+  CKH(hipMemcpyAsync(&v, h->ws + h->wo.flags, 4, hipMemcpyDeviceToHost, s));
+  CKH(hipStreamSynchronize(s));
+  CKH(hipMemsetAsync(h->ws + h->wo.flags, 0, 4, s));
+  *flags = v;
+  return GPT_OK;
+}
+
+void gpt_destroy(gpt_model* h) { delete h; }
+
+const char* gpt_strerror(int code) {
+  static thread_local std::string msg;
+  const char* base = "unknown error";
+  switch (code) {
+    case GPT_OK: return "ok";
+    case GPT_EINVAL: base = "invalid argument"; break;
+    case GPT_ESEQLEN: base = "sequence longer than block_size"; break;
+    case GPT_ESTATE: base = "invalid call order"; break;
+    case GPT_EHIP: base = "HIP error"; break;
+    case GPT_EUNSUPPORTED: base = "unsupported shape"; break;
+  }
+  msg = std::string(base) + (g_err.empty() ? "" : ": " + g_err);
+  return msg.c_str();
+}
+
+// ----------------------------------------------------------------- single ops
+int gpt_op_linear(int32_t bf16, const void* A, const void* B, const float* bias, void* C,
+                  int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!A || !B || !C || M < 0 || N < 0 || K < 1) return fail(GPT_EINVAL, "bad linear arguments");
+  GemmEpiArgs e;
+  e.out = C;
+  e.bias = bias;
+  e.ldc = N;
+  CK(gemm_launch(bf16 != 0, true, true, out_f32 ? EPI_F32 : EPI_ACT, A, K, B, K, M, N, K, K, K, e,
+                 (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_linear_dw(int32_t bf16, const void* dY, const void* X, float* dW, int32_t accumulate,
+                     int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!dY || !X || !dW || M < 1 || N < 0 || K < 0) return fail(GPT_EINVAL, "bad linear_dw arguments");
+  GemmEpiArgs e;
+  e.out = dW;
+  e.ldc = K;
+  e.beta = accumulate ? 1 : 0;
+  CK(gemm_launch(bf16 != 0, false, false, EPI_ACCUM, dY, N, X, K, N, K, M, M, M, e,
+                 (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_linear_dx(int32_t bf16, const void* dY, const void* W, float* dX, int32_t M, int32_t N,
+                     int32_t K, void* stream) {
+  if (!dY || !W || !dX || M < 0 || N < 1 || K < 0) return fail(GPT_EINVAL, "bad linear_dx arguments");
+  GemmEpiArgs e;
+  e.out = dX;
+  e.ldc = K;
+  CK(gemm_launch(bf16 != 0, true, false, EPI_F32, dY, N, W, K, M, K, N, N, N, e,
+                 (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_attention_fwd(int32_t bf16, const void* qkv, void* out, float* lse, int32_t B, int32_t T,
+                         int32_t H, int32_t C, void* stream) {
+  if (!qkv || !out || !lse || B < 1 || T < 1 || H < 1 || C % H) return fail(GPT_EINVAL, "bad attention arguments");
+  CK(attention_fwd_launch(bf16 != 0, qkv, out, lse, B, T, H, C, (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_attention_bwd(int32_t bf16, const void* qkv, const void* out, const float* lse,
+                         const void* dout, void* dqkv, float* D, int32_t B, int32_t T, int32_t H,
+                         int32_t C, void* stream) {
+  if (!qkv || !out || !lse || !dout || !dqkv || !D || B < 1 || T < 1 || H < 1 || C % H)
+    return fail(GPT_EINVAL, "bad attention arguments");
+  CK(attention_bwd_launch(bf16 != 0, qkv, out, lse, dout, dqkv, D, B, T, H, C, (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_layernorm_fwd(int32_t bf16, const float* x, const float* w, const float* b, void* y,
+                         float* mean, float* rstd, int32_t M, int32_t C, void* stream) {
+  if (!x || !w || !b || !y || !mean || !rstd || M < 0 || C < 1) return fail(GPT_EINVAL, "bad layernorm arguments");
+  CK(layernorm_fwd_launch(bf16 != 0, x, w, b, y, mean, rstd, M, C, (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_cross_entropy(int32_t bf16, void* logits, const int32_t* targets, float* loss,
+                         float* row_loss, int32_t* n_valid, float loss_scale, int32_t N, int32_t V,
+                         int32_t ldv, void* stream) {
+  if (!logits || !targets || !loss || !row_loss || !n_valid || N < 1 || V < 1 || ldv < V)
+    return fail(GPT_EINVAL, "bad cross-entropy arguments");
+  hipStream_t s = (hipStream_t)stream;
+  CK(count_valid_launch(targets, N, n_valid, s));
+  CK(cross_entropy_launch(bf16 != 0, logits, targets, row_loss, n_valid, loss_scale, N, V, ldv, s));
+  CK(loss_finalize_launch(row_loss, N, n_valid, loss, s));
+  return GPT_OK;
+}
+
+}  // extern "C"

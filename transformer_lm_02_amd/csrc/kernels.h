@@ -1,0 +1,50 @@
+// Launchers of the HIP kernels (host side).  Each returns 0, -4 (HIP launch
+// error) or -5 (shape the kernel does not cover).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+
+typedef uint16_t bf16_t;
+
+struct AdamChunk {
+  int64_t offset;
+  int32_t count;
+  int32_t decay;
+};
+
+int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
+                         int C, hipStream_t s);
+int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
+                         const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
+                         hipStream_t s);
+
+int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
+                         float* mean, float* rstd, int M, int C, hipStream_t s);
+int layernorm_bwd_part_rows(int M);
+int layernorm_bwd_launch(bool bf16, const float* dy, const float* x, const float* mean,
+                         const float* rstd, const float* w, float* dres, void* dres_act,
+                         int accumulate, float* part, float* dw, float* db, float* bias_grad,
+                         int beta, int M, int C, hipStream_t s);
+
+int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, float* x, int M,
+                     int Tn, int C, int Vp, int* flags, hipStream_t s);
+int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int Tn,
+                     int block_size, int C, int Vp, int beta_wpe, hipStream_t s);
+int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s);
+int cross_entropy_launch(bool bf16, void* logits, const int32_t* tgt, float* row_loss,
+                         const int* n_valid, float loss_scale, int N, int V, int ldv,
+                         hipStream_t s);
+int loss_finalize_launch(const float* row_loss, int N, const int* n_valid, float* loss,
+                         hipStream_t s);
+int colsum_part_rows(int M);
+int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* out, int beta,
+                  hipStream_t s);
+
+int adamw_norm_blocks();
+int adamw_launch(float* p, const float* g, float* m, float* v, bf16_t* shadow, int64_t n,
+                 const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
+                 float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
+                 float max_norm, int t, int skip_nonfinite, hipStream_t s);
+int to_bf16_launch(const float* p, bf16_t* o, int64_t n, hipStream_t s);

@@ -1,0 +1,263 @@
+// Embedding, fused masked softmax cross-entropy, bias-gradient column sums.
+#include "common.h"
+
+// ---------------------------------------------------------------- embedding
+// x[b*T + t] = wte[idx] + wpe[t] ("nanoGPT" (stanleyjacob.dev), Part IV Stage
+// 4: token embeddings plus learned position embeddings).  An id outside
+// [0, Vp) reads no memory: its token row is taken as zero and flag bit 1 set.
+__global__ void embed_fwd_kernel(const int32_t* __restrict__ idx, const float* __restrict__ wte,
+                                 const float* __restrict__ wpe, float* __restrict__ x, int M,
+                                 int Tn, int C, int Vp, int* __restrict__ flags) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const int id = idx[row], t = row % Tn;
+  const bool ok = id >= 0 && id < Vp;
+  if (!ok && lane == 0) atomicOr(flags, 1);
+  const float4* a = (const float4*)(wte + (int64_t)(ok ? id : 0) * C);
+  const float4* p = (const float4*)(wpe + (int64_t)t * C);
+  float4* o = (float4*)(x + row * C);
+  for (int j = lane; j < C / 4; j += 64) {
+    float4 v = p[j];
+    if (ok) {
+      const float4 w = a[j];
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    o[j] = v;
+  }
+}
+
+// dwte[idx[m]] += dx[m] (fp32 atomics: rows of frequent ids add up in the
+// order the hardware serves them, so the last bits can differ run to run).
+__global__ void embed_bwd_wte_kernel(const int32_t* __restrict__ idx, const float* __restrict__ dx,
+                                     float* __restrict__ dwte, int M, int C, int Vp) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const int id = idx[row];
+  if (id < 0 || id >= Vp) return;
+  const float* src = dx + row * C;
+  float* dst = dwte + (int64_t)id * C;
+  for (int j = lane; j < C; j += 64) unsafeAtomicAdd(dst + j, src[j]);
+}
+
+// dwpe[t] = (beta ? dwpe[t] : 0) + sum_b dx[b*T + t] for t < T; rows
+// T..block_size-1 get (beta ? unchanged : 0).  Deterministic.
+__global__ void embed_bwd_wpe_kernel(const float* __restrict__ dx, float* __restrict__ dwpe,
+                                     int B, int Tn, int block_size, int C, int beta) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)block_size * C) return;
+  const int t = i / C, c = i % C;
+  float s = 0.f;
+  if (t < Tn)
+    for (int b = 0; b < B; ++b) s += dx[((int64_t)b * Tn + t) * C + c];
+  dwpe[i] = (beta ? dwpe[i] : 0.f) + s;
+}
+
+// ---------------------------------------------------------------- cross-entropy
+// count of targets >= 0 (ignore_index = -1, "nanoGPT" Part IV Stage 4)
+__global__ void count_valid_kernel(const int32_t* __restrict__ tgt, int N, int* __restrict__ out) {
+  __shared__ int red[4];
+  int c = 0;
+  for (int i = threadIdx.x; i < N; i += blockDim.x) c += tgt[i] >= 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = red[0] + red[1] + red[2] + red[3];
+}
+
+// One row of logits per workgroup, read once into registers:
+//   lse = log sum_{v < V} exp(z_v)  (padded columns v >= V are excluded),
+//   row_loss = lse - z_y,
+//   dz_v = scale * (exp(z_v - lse) - [v == y]) for v < V, 0 for V <= v < ldv,
+// written over the logits ("Let's reproduce GPT-2 (124M)", chapter "Cross
+// Entropy Loss"; scale = loss_scale / n_valid, zero for an ignored row).
+#define CE_THREADS 512
+#define CE_MAXU 13  // uint4 (8 bf16) per thread: rows up to 53248 columns
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < CE_THREADS / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  return r;
+}
+
+__global__ __launch_bounds__(CE_THREADS) void ce_bf16_kernel(
+    bf16_t* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
+    const int* __restrict__ n_valid, float loss_scale, int V, int ldv) {
+  __shared__ float red[CE_THREADS / 64];
+  const int64_t row = blockIdx.x;
+  bf16_t* z = logits + row * ldv;
+  const int nvec = ldv >> 3;
+  uint4 cache[CE_MAXU];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < CE_MAXU; ++i) {
+    const int vi = threadIdx.x + CE_THREADS * i;
+    cache[i] = vi < nvec ? ((const uint4*)z)[vi] : make_uint4(0, 0, 0, 0);
+    const uint32_t* w = (const uint32_t*)&cache[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 8 * vi + e;
+      const float f = bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
+      if (col < V) mx = fmaxf(mx, f);
+    }
+  }
+  mx = block_reduce(mx, true, red);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < CE_MAXU; ++i) {
+    const int vi = threadIdx.x + CE_THREADS * i;
+    const uint32_t* w = (const uint32_t*)&cache[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 8 * vi + e;
+      const float f = bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
+      if (col < V) s += __expf(f - mx);
+    }
+  }
+  s = block_reduce(s, false, red);
+  const float lse = mx + __logf(s);
+  const int y = tgt[row];
+  const int nv = *n_valid;
+  const float scale = (y >= 0 && nv > 0) ? loss_scale / (float)nv : 0.f;
+  float zy = 0.f;
+  if (y >= 0 && y < V) zy = bf2f(z[y]);
+  __syncthreads();  // every thread has read z[y] before it is overwritten
+#pragma unroll
+  for (int i = 0; i < CE_MAXU; ++i) {
+    const int vi = threadIdx.x + CE_THREADS * i;
+    if (vi >= nvec) break;
+    const uint32_t* w = (const uint32_t*)&cache[i];
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 8 * vi + e;
+      const float f = bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
+      d[e] = col < V ? scale * (__expf(f - lse) - (col == y ? 1.f : 0.f)) : 0.f;
+    }
+    ((uint4*)z)[vi] = make_uint4(pack2bf(d[0], d[1]), pack2bf(d[2], d[3]), pack2bf(d[4], d[5]),
+                                 pack2bf(d[6], d[7]));
+  }
+  if (threadIdx.x == 0) row_loss[row] = (y >= 0 && y < V) ? lse - zy : 0.f;
+}
+
+// fp32 logits (fp32 mode): the same, reading the row from memory per pass.
+__global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
+    float* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
+    const int* __restrict__ n_valid, float loss_scale, int V, int ldv) {
+  __shared__ float red[CE_THREADS / 64];
+  const int64_t row = blockIdx.x;
+  float* z = logits + row * ldv;
+  float mx = -INFINITY;
+  for (int c = threadIdx.x; c < V; c += CE_THREADS) mx = fmaxf(mx, z[c]);
+  mx = block_reduce(mx, true, red);
+  float s = 0.f;
+  for (int c = threadIdx.x; c < V; c += CE_THREADS) s += expf(z[c] - mx);
+  s = block_reduce(s, false, red);
+  const float lse = mx + logf(s);
+  const int y = tgt[row];
+  const int nv = *n_valid;
+  const float scale = (y >= 0 && nv > 0) ? loss_scale / (float)nv : 0.f;
+  const float zy = (y >= 0 && y < V) ? z[y] : 0.f;
+  __syncthreads();
+  for (int c = threadIdx.x; c < ldv; c += CE_THREADS)
+    z[c] = c < V ? scale * (expf(z[c] - lse) - (c == y ? 1.f : 0.f)) : 0.f;
+  if (threadIdx.x == 0) row_loss[row] = (y >= 0 && y < V) ? lse - zy : 0.f;
+}
+
+// loss = sum(row_loss) / n_valid, single workgroup, fixed order.
+__global__ void loss_finalize_kernel(const float* __restrict__ row_loss, int N,
+                                     const int* __restrict__ n_valid, float* __restrict__ loss) {
+  __shared__ double red[4];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < N; i += 256) s += row_loss[i];
+  s = wave_sum_d(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int nv = *n_valid;
+    *loss = nv > 0 ? (float)((red[0] + red[1] + red[2] + red[3]) / nv) : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------- column sums
+// part[rb][n] = sum over rows rb*rows_per..(rb+1)*rows_per of a[row][n]
+// (bias gradients: db = sum over tokens of dy).
+#define CS_ROWS 256
+template <typename T>
+__global__ void colsum_part_kernel(const T* __restrict__ a, int M, int N, float* __restrict__ part) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int rb = blockIdx.y;
+  if (n >= N) return;
+  const int r0 = rb * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
+  float s = 0.f;
+  for (int r = r0; r < r1; ++r) s += ldf(a + (int64_t)r * N + n);
+  part[(int64_t)rb * N + n] = s;
+}
+
+// ---------------------------------------------------------------- launchers
+int colsum_finalize_launch(const float* part, int nblk, int64_t stride, float* out, int n, int beta,
+                           hipStream_t s);
+
+int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, float* x, int M,
+                     int Tn, int C, int Vp, int* flags, hipStream_t s) {
+  hipLaunchKernelGGL(embed_fwd_kernel, dim3(cdiv(M, 4)), dim3(256), 0, s, idx, wte, wpe, x, M, Tn,
+                     C, Vp, flags);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int Tn,
+                     int block_size, int C, int Vp, int beta_wpe, hipStream_t s) {
+  const int M = B * Tn;
+  hipLaunchKernelGGL(embed_bwd_wte_kernel, dim3(cdiv(M, 4)), dim3(256), 0, s, idx, dx, dwte, M, C,
+                     Vp);
+  hipLaunchKernelGGL(embed_bwd_wpe_kernel, dim3(cdiv((int64_t)block_size * C, 256)), dim3(256), 0,
+                     s, dx, dwpe, B, Tn, block_size, C, beta_wpe);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s) {
+  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(256), 0, s, tgt, N, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int cross_entropy_launch(bool bf16, void* logits, const int32_t* tgt, float* row_loss,
+                         const int* n_valid, float loss_scale, int N, int V, int ldv,
+                         hipStream_t s) {
+  if (bf16) {
+    if (ldv % 8 || ldv > CE_MAXU * CE_THREADS * 8) return -5;
+    hipLaunchKernelGGL(ce_bf16_kernel, dim3(N), dim3(CE_THREADS), 0, s, (bf16_t*)logits, tgt,
+                       row_loss, n_valid, loss_scale, V, ldv);
+  } else {
+    hipLaunchKernelGGL(ce_f32_kernel, dim3(N), dim3(CE_THREADS), 0, s, (float*)logits, tgt,
+                       row_loss, n_valid, loss_scale, V, ldv);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int loss_finalize_launch(const float* row_loss, int N, const int* n_valid, float* loss,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, s, row_loss, N, n_valid, loss);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int colsum_part_rows(int M) { return (int)cdiv(M, CS_ROWS); }
+
+// out (+)= column sums of a [M][N]; part: fp32 scratch [colsum_part_rows(M)][N].
+int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* out, int beta,
+                  hipStream_t s) {
+  const int nb = colsum_part_rows(M);
+  if (bf16)
+    hipLaunchKernelGGL(colsum_part_kernel<bf16_t>, dim3(cdiv(N, 256), nb), dim3(256), 0, s,
+                       (const bf16_t*)a, M, N, part);
+  else
+    hipLaunchKernelGGL(colsum_part_kernel<float>, dim3(cdiv(N, 256), nb), dim3(256), 0, s,
+                       (const float*)a, M, N, part);
+  if (hipGetLastError() != hipSuccess) return -4;
+  return colsum_finalize_launch(part, nb, N, out, N, beta, s);
+}
