@@ -147,9 +147,13 @@ int gpt_op_linear(int32_t bf16, const void* A, const void* B, const float* bias,
                   void* C, int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream);
 
 /* dW (+)= dY^T X: dY act [M][N], X act [M][K], dW fp32 [N][K];
- * accumulate != 0 adds to dW.  The weight gradient of a Linear layer. */
+ * accumulate != 0 adds to dW.  The weight gradient of a Linear layer.
+ * workspace: optional device fp32 scratch of workspace_bytes (NULL: none);
+ * with enough of it a long reduction over M is split across workgroups and
+ * the partial sums are added in a fixed order. */
 int gpt_op_linear_dw(int32_t bf16, const void* dY, const void* X, float* dW,
-                     int32_t accumulate, int32_t M, int32_t N, int32_t K, void* stream);
+                     int32_t accumulate, int32_t M, int32_t N, int32_t K,
+                     float* workspace, int64_t workspace_bytes, void* stream);
 
 /* dX = dY W: dY act [M][N], W act [N][K], dX fp32 [M][K].  The input
  * gradient of a Linear layer. */

@@ -29,7 +29,7 @@ def rnd(shape, seed, scale=1.0):
 
 # ---------------------------------------------------------------- matrix products
 LINEAR_SHAPES = [(256, 2304, 768), (300, 200, 136), (1000, 768, 3072), (64, 128, 64),
-                 (129, 50304, 768), (4100, 4800, 1600)]
+                 (129, 50304, 768), (4100, 4800, 1600), (4100, 6400, 768), (256, 65, 64)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
@@ -47,22 +47,26 @@ def test_linear_bf16(M, N, K):
     assert max_rel(to_np(Cb), ref) < 8e-3
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("M,N,K", [(16384, 768, 768), (1000, 384, 1536), (77, 64, 64),
-                                   (2048, 50304, 768), (8192, 1600, 4800)])
-def test_linear_dw_bf16(M, N, K):
-    case(f"linear_dw bf16 M={M} N={N} K={K}")
+                                   (2048, 50304, 768), (8192, 1600, 4800), (16384, 2304, 768),
+                                   (3001, 768, 3072)])
+def test_linear_dw_bf16(M, N, K, split):
+    case(f"linear_dw bf16 M={M} N={N} K={K} split-K workspace={split}")
     dY, X = bf16_round(rnd((M, N), 4, 0.01)), bf16_round(rnd((M, K), 5))
     ref = dY.T @ X
-    got = to_np(bd.op_linear_dw(to_dev(dY, torch.bfloat16), to_dev(X, torch.bfloat16)))
+    ws = torch.empty(16 * N * K, dtype=torch.float32, device="cuda") if split else None
+    got = to_np(bd.op_linear_dw(to_dev(dY, torch.bfloat16), to_dev(X, torch.bfloat16), workspace=ws))
     assert rel_err(got, ref) < 1e-5 and max_rel(got, ref) < 1e-4
     # accumulate
     dW = torch.as_tensor(np.ones((N, K), np.float32)).cuda()
-    got2 = to_np(bd.op_linear_dw(to_dev(dY, torch.bfloat16), to_dev(X, torch.bfloat16), dW))
+    got2 = to_np(bd.op_linear_dw(to_dev(dY, torch.bfloat16), to_dev(X, torch.bfloat16), dW,
+                                 workspace=ws))
     assert rel_err(got2, ref + 1.0) < 1e-5
 
 
 @pytest.mark.parametrize("M,N,K", [(16384, 768, 768), (300, 200, 136), (512, 50304, 768),
-                                   (1000, 3072, 768), (257, 4800, 1600)])
+                                   (1000, 3072, 768), (257, 4800, 1600), (4100, 768, 6400)])
 def test_linear_dx_bf16(M, N, K):
     case(f"linear_dx bf16 M={M} N={N} K={K}")
     dY, W = bf16_round(rnd((M, N), 6, 0.01)), bf16_round(rnd((N, K), 7, 0.02))

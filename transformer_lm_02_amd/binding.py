@@ -38,7 +38,7 @@ _SIGS = {
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
     "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
     "gpt_op_linear": [_i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
-    "gpt_op_linear_dw": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
+    "gpt_op_linear_dw": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
     "gpt_op_linear_dx": [_i32, _p, _p, _p, _i32, _i32, _i32, _p],
     "gpt_op_attention_fwd": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
     "gpt_op_attention_bwd": [_i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
@@ -174,15 +174,16 @@ def op_linear(A, B, bias=None, out_f32=False):
     return C
 
 
-def op_linear_dw(dY, X, dW=None):
+def op_linear_dw(dY, X, dW=None, workspace=None):
     import torch
     M, N = dY.shape
     K = X.shape[1]
     acc = dW is not None
     if dW is None:
         dW = torch.empty((N, K), dtype=torch.float32, device=dY.device)
-    check(lib.gpt_op_linear_dw(_bf(dY), _ptr(dY), _ptr(X), _ptr(dW), int(acc), M, N, K, _stream()),
-          "gpt_op_linear_dw")
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.gpt_op_linear_dw(_bf(dY), _ptr(dY), _ptr(X), _ptr(dW), int(acc), M, N, K,
+                               _ptr(workspace), wsb, _stream()), "gpt_op_linear_dw")
     return dW
 
 

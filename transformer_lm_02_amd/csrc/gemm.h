@@ -26,7 +26,12 @@ struct GemmEpiArgs {
 // Loads of a k-contiguous operand require K % 8 == 0 (bf16); an m- or
 // n-contiguous operand reads rows k < ka_rows / kb_rows and columns below its
 // leading dimension.  Outputs are written for m < M, n < N.
+// ws / ws_bytes: optional fp32 scratch for split-K weight gradients.
 int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi,
                 const void* A, int lda, const void* B, int ldb,
                 int M, int N, int K, int ka_rows, int kb_rows,
-                const GemmEpiArgs& e, hipStream_t stream);
+                const GemmEpiArgs& e, hipStream_t stream,
+                float* ws = nullptr, int64_t ws_bytes = 0);
+
+// split-K scratch the launcher may use for an M x N weight gradient
+inline int64_t gemm_splitk_bytes(int64_t M, int64_t N) { return 16 * M * N * 4; }

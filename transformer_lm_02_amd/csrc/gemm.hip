@@ -324,11 +324,19 @@ static void run_f32(const GemmArgsF& a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? 0 : -4;                                       \
   }
 
+int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda, const void* B,
+                 int ldb, int M, int N, int K, int ka_rows, int kb_rows, const GemmEpiArgs& e,
+                 float* ws, int64_t ws_bytes, hipStream_t s);
+
 int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda,
                 const void* B, int ldb, int M, int N, int K, int ka_rows, int kb_rows,
-                const GemmEpiArgs& e, hipStream_t stream) {
+                const GemmEpiArgs& e, hipStream_t stream, float* ws, int64_t ws_bytes) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   if (bf16) {
+    // the pipelined kernel when the shape allows it, else the plain one below
+    const int rc = gemm2_launch(a_kcontig, b_kcontig, epi, A, lda, B, ldb, M, N, K, ka_rows,
+                                kb_rows, e, ws, ws_bytes, stream);
+    if (rc != -5) return rc == 0 ? (hipGetLastError() == hipSuccess ? 0 : -4) : rc;
     if ((a_kcontig && (K % 8 || lda % 8)) || (b_kcontig && (K % 8 || ldb % 8))) return -5;
     if ((!a_kcontig && lda % 8) || (!b_kcontig && ldb % 8)) return -5;
     if (((uintptr_t)A | (uintptr_t)B) & 15) return -5;

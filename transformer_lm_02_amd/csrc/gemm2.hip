@@ -1,0 +1,380 @@
+// Pipelined bf16 MFMA GEMM for gfx950: C[m][n] = sum_k A(m,k) B(n,k).
+//
+// Same products and epilogues as gemm.hip (the Linear layers of "nanoGPT"
+// (stanleyjacob.dev), Part V Deep dive 1, their input and weight gradients,
+// and the tied LM head), arranged for CDNA4:
+//  * operands go from HBM straight into LDS with buffer loads in LDS mode
+//    (no VGPR staging) through an NS-stage ring, so NS-1 k-tiles are in
+//    flight while one is multiplied; out-of-range reads return zero, which
+//    handles ragged edges;
+//  * a k-contiguous operand is stored [rows][64] with its 16-byte chunks
+//    XOR-swizzled by row and read with ds_read_b128; an m/n-contiguous
+//    operand (a transposed use: weight gradients, input gradients through
+//    W) stays in its memory layout [64][rows] and is read with the gfx950
+//    transposing LDS load ds_read_b64_tr_b16, so no register transpose;
+//  * v_mfma_f32_32x32x16_bf16, 4 waves in a 2x2 grid, fp32 accumulators;
+//  * the epilogue goes through LDS so every lane stores 8 contiguous outputs;
+//  * weight gradients with few output tiles split K over workgroups into an
+//    fp32 partial buffer that a second kernel sums in a fixed order.
+#include "common.h"
+#include "gemm.h"
+
+#define AS3(p) ((__attribute__((address_space(3))) void*)(p))
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr uint32_t kOOB = 0xFFFFFF00u;  // byte offset beyond any buffer: loads return 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// One operand tile of ROWS x 64 (k) bf16 per stage.  Each wave issues
+// ROWS/32 loads of 1 KB (64 lanes x 16 bytes, contiguous in LDS).
+template <int ROWS, bool KC>
+struct Stage {
+  static constexpr int LOADS = ROWS / 32;
+  static constexpr int ELEMS = ROWS * 64;
+  uint32_t voff[LOADS];
+  int kofs[LOADS];
+
+  // k-contiguous: LDS [ROWS][64], chunk c of row r at position c ^ ((r>>1)&7)
+  // m-contiguous: LDS [64][ROWS], chunk c of k-row k at position c ^ (2*(k&3))
+  __device__ __forceinline__ void init(int row0, int ld, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int q = i * 4 + wave;
+      if constexpr (KC) {
+        const int r = 8 * q + (lane >> 3), pc = lane & 7;
+        const int c = pc ^ ((r >> 1) & 7);
+        voff[i] = (uint32_t)(((int64_t)(row0 + r) * ld + 8 * c) * 2);
+        kofs[i] = 8 * c;
+      } else {
+        constexpr int CPR = ROWS / 8;          // 16-byte chunks per k-row
+        constexpr int RPL = 64 / CPR;          // k-rows per 1 KB load
+        const int k = q * RPL + lane / CPR, pos = lane % CPR;
+        const int c = pos ^ (2 * (k & 3));
+        voff[i] = (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2);
+        kofs[i] = 0;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, int kt, int ld,
+                                        int K, int wave) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int q = i * 4 + wave;
+      uint32_t off;
+      if constexpr (KC) {
+        off = (kt * 64 + kofs[i] < K) ? voff[i] + (uint32_t)kt * 128u : kOOB;
+      } else {
+        off = voff[i] + (uint32_t)kt * (uint32_t)(64 * ld * 2);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, AS3(lds + q * 512), 16, off, 0, 0, 0);
+    }
+  }
+  // MFMA 32x32x16 operand: lane holds (row rbase + lane%32, k 16ks + 8(lane/32) + 0..7)
+  __device__ __forceinline__ static bf16x8_t frag(const bf16_t* lds, int rbase, int ks, int lane) {
+    if constexpr (KC) {
+      const int r = rbase + (lane & 31), c = 2 * ks + (lane >> 5);
+      return *(const bf16x8_t*)(lds + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+    } else {
+      const int G = lane >> 4, t = lane & 15;
+      const int m = rbase + 16 * (G & 1) + 4 * (t & 3);
+      const int k0 = 16 * ks + 8 * (G >> 1) + (t >> 2);
+      const int c = m >> 3;
+      const int ka = k0, kb = k0 + 4;
+      const bf16_t* pa = lds + ka * ROWS + ((c ^ (2 * (ka & 3))) << 3) + (m & 7);
+      const bf16_t* pb = lds + kb * ROWS + ((c ^ (2 * (kb & 3))) << 3) + (m & 7);
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4_t*)(pa));
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4_t*)(pb));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+struct Gemm2Args {
+  const bf16_t* A;
+  const bf16_t* B;
+  int lda, ldb, M, N, K, ka_rows, kb_rows, tiles_m, tiles_n;
+  int ksplit, k_tiles_per_split;
+  float* part;  // split-K partials [ksplit][M][N] (EPI_ACCUM with ksplit > 1)
+  GemmEpiArgs e;
+};
+
+__device__ __forceinline__ void tile_coords2(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int n = tiles_m * tiles_n;
+  const int xcd = wg & 7, local = wg >> 3;
+  const int base = n >> 3, rem = n & 7;
+  const int tile = xcd * base + min(xcd, rem) + local;
+  constexpr int GROUP_M = 8;
+  const int per_group = GROUP_M * tiles_n;
+  const int g = tile / per_group;
+  const int first_m = g * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int r = tile - g * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+// 8 consecutive outputs of one row: epilogue and 16/32-byte stores
+template <int EPI>
+__device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int splitk, int m, int n,
+                                     const float* v, const float* bias8) {
+  const int64_t i = (int64_t)m * e.ldc + n;
+  if constexpr (EPI == EPI_ACCUM) {
+    if (splitk) {
+      float4* o = (float4*)(part + i);
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      float4* o = (float4*)((float*)e.out + i);
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (e.beta) { a = o[0]; b = o[1]; }
+      o[0] = make_float4(a.x + v[0], a.y + v[1], a.z + v[2], a.w + v[3]);
+      o[1] = make_float4(b.x + v[4], b.y + v[5], b.z + v[6], b.w + v[7]);
+    }
+  } else if constexpr (EPI == EPI_F32) {
+    float4* o = (float4*)((float*)e.out + i);
+    o[0] = make_float4(v[0] + bias8[0], v[1] + bias8[1], v[2] + bias8[2], v[3] + bias8[3]);
+    o[1] = make_float4(v[4] + bias8[4], v[5] + bias8[5], v[6] + bias8[6], v[7] + bias8[7]);
+  } else if constexpr (EPI == EPI_RESID) {
+    const float4* x = (const float4*)((const float*)e.aux + i);
+    const float4 a = x[0], b = x[1];
+    float4* o = (float4*)((float*)e.out + i);
+    o[0] = make_float4(a.x + v[0] + bias8[0], a.y + v[1] + bias8[1], a.z + v[2] + bias8[2],
+                       a.w + v[3] + bias8[3]);
+    o[1] = make_float4(b.x + v[4] + bias8[4], b.y + v[5] + bias8[5], b.z + v[6] + bias8[6],
+                       b.w + v[7] + bias8[7]);
+  } else if constexpr (EPI == EPI_ACT) {
+    *(uint4*)((bf16_t*)e.out + i) =
+        make_uint4(pack2bf(v[0] + bias8[0], v[1] + bias8[1]), pack2bf(v[2] + bias8[2], v[3] + bias8[3]),
+                   pack2bf(v[4] + bias8[4], v[5] + bias8[5]), pack2bf(v[6] + bias8[6], v[7] + bias8[7]));
+  } else if constexpr (EPI == EPI_GELU) {
+    float u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = v[j] + bias8[j];
+    *(uint4*)((bf16_t*)e.out + i) =
+        make_uint4(pack2bf(u[0], u[1]), pack2bf(u[2], u[3]), pack2bf(u[4], u[5]), pack2bf(u[6], u[7]));
+    *(uint4*)((bf16_t*)e.out2 + i) =
+        make_uint4(pack2bf(gelu_f(u[0]), gelu_f(u[1])), pack2bf(gelu_f(u[2]), gelu_f(u[3])),
+                   pack2bf(gelu_f(u[4]), gelu_f(u[5])), pack2bf(gelu_f(u[6]), gelu_f(u[7])));
+  } else {  // EPI_GELU_BWD
+    const uint4 uu = *(const uint4*)((const bf16_t*)e.aux + i);
+    const uint32_t* w = (const uint32_t*)&uu;
+    float d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = v[j] * gelu_grad_f(bf2f((bf16_t)(w[j >> 1] >> (16 * (j & 1)))));
+    *(uint4*)((bf16_t*)e.out + i) =
+        make_uint4(pack2bf(d[0], d[1]), pack2bf(d[2], d[3]), pack2bf(d[4], d[5]), pack2bf(d[6], d[7]));
+  }
+}
+
+template <int BM, int BN, bool AK, bool BKC, int EPI, int NS>
+__global__ __launch_bounds__(256) void gemm2_kernel(Gemm2Args p) {
+  using SA = Stage<BM, AK>;
+  using SB = Stage<BN, BKC>;
+  constexpr int STAGE_ELEMS = SA::ELEMS + SB::ELEMS;
+  constexpr int WR = BM / 2, WC = BN / 2;   // wave tile
+  constexpr int TM = WR / 32, TN = WC / 32; // 32x32 MFMA tiles per wave
+  constexpr int EP_PITCH = WC + 4;          // fp32 epilogue staging pitch
+  constexpr int LDS_ELEMS_RING = NS * STAGE_ELEMS;
+  constexpr int LDS_ELEMS_EPI = 4 * 32 * EP_PITCH * 2;  // in bf16 units
+  constexpr int LDS_ELEMS = LDS_ELEMS_RING > LDS_ELEMS_EPI ? LDS_ELEMS_RING : LDS_ELEMS_EPI;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[LDS_ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  tile_coords2(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int split = blockIdx.y;
+  const int nk_total = (p.K + 63) / 64;
+  const int kt0 = split * p.k_tiles_per_split;
+  const int nk = min(nk_total - kt0, p.k_tiles_per_split);
+
+  const uint32_t a_bytes = (uint32_t)((int64_t)(AK ? p.M : p.ka_rows) * p.lda * 2);
+  const uint32_t b_bytes = (uint32_t)((int64_t)(BKC ? p.N : p.kb_rows) * p.ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, b_bytes);
+  SA sa;
+  SB sb;
+  sa.init(m0, p.lda, lane, wave);
+  sb.init(n0, p.ldb, lane, wave);
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  constexpr int L = SA::LOADS + SB::LOADS;  // loads per wave per stage
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+    if (s < nk) {
+      sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + s, p.lda, p.K, wave);
+      sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + s, p.ldb, p.K, wave);
+    }
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt landed (the NS-2 younger stages may still be in flight)
+    if (kt + NS - 2 < nk) wait_vm_barrier<(NS - 2) * L>();
+    else wait_vm_barrier<0>();
+    if (kt + NS - 1 < nk) {
+      const int s = (kt + NS - 1) % NS;
+      sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + kt + NS - 1, p.lda, p.K, wave);
+      sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + kt + NS - 1, p.ldb, p.K, wave);
+    }
+    const bf16_t* la = lds + (kt % NS) * STAGE_ELEMS;
+    const bf16_t* lb = la + SA::ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = SA::frag(la, wm * WR + 32 * i, ks, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = SB::frag(lb, wn * WC + 32 * j, ks, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // every wave is done with the ring before it is reused for the epilogue
+  wait_vm_barrier<0>();
+
+  // epilogue: per 32-row slab of the wave tile, stage fp32 in LDS, then each
+  // lane handles 8 consecutive columns of one row
+  float* ep = (float*)lds + wave * 32 * EP_PITCH;
+  constexpr int LPR = WC / 8;        // lanes per row
+  constexpr int RPI = 64 / LPR;      // rows per pass
+  const int my_c = 8 * (lane % LPR), my_r = lane / LPR;
+  const int gcol = n0 + wn * WC + my_c;
+  float bias8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (EPI != EPI_ACCUM && EPI != EPI_GELU_BWD && p.e.bias != nullptr && gcol < p.N) {
+    const float4 b0 = *(const float4*)(p.e.bias + gcol), b1 = *(const float4*)(p.e.bias + gcol + 4);
+    bias8[0] = b0.x; bias8[1] = b0.y; bias8[2] = b0.z; bias8[3] = b0.w;
+    bias8[4] = b1.x; bias8[5] = b1.y; bias8[6] = b1.z; bias8[7] = b1.w;
+  }
+  float* part = p.part ? p.part + (int64_t)split * p.M * p.e.ldc : nullptr;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    // accumulator layout of a 32x32 tile: lane l, register r -> row
+    // 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EP_PITCH + 32 * j + (lane & 31)] = acc[i][j][r];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // rolled: keeps the unrolled slab loop small enough that acc[i] stays
+    // statically indexed (in registers)
+#pragma unroll 1
+    for (int rr = 0; rr < 32; rr += RPI) {
+      const int lr = rr + my_r;
+      const int grow = m0 + wm * WR + 32 * i + lr;
+      const float4 v0 = *(const float4*)(ep + lr * EP_PITCH + my_c);
+      const float4 v1 = *(const float4*)(ep + lr * EP_PITCH + my_c + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, p.ksplit > 1, grow, gcol, v, bias8);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
+// out[i] = (beta ? out[i] : 0) + sum_s part[s][i], fixed order
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit, int64_t n,
+                                     float* __restrict__ out, int beta) {
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i4 * 4 >= n) return;
+  float4 s = beta ? ((const float4*)out)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < ksplit; ++k) {
+    const float4 v = ((const float4*)(part + (int64_t)k * n))[i4];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  ((float4*)out)[i4] = s;
+}
+
+template <int BM, int BN, bool AK, bool BKC, int EPI, int NS>
+void run2(Gemm2Args p, hipStream_t s) {
+  p.tiles_m = (int)cdiv(p.M, BM);
+  p.tiles_n = (int)cdiv(p.N, BN);
+  hipLaunchKernelGGL((gemm2_kernel<BM, BN, AK, BKC, EPI, NS>), dim3(p.tiles_m * p.tiles_n, p.ksplit),
+                     dim3(256), 0, s, p);
+}
+
+template <bool AK, bool BKC, int EPI>
+int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
+  const int64_t t256 = cdiv(p.M, 256) * cdiv(p.N, 256);
+  const int64_t t128 = cdiv(p.M, 128) * cdiv(p.N, 128);
+  const int nk = (int)cdiv(p.K, 64);
+  p.ksplit = 1;
+  p.k_tiles_per_split = nk;
+  p.part = nullptr;
+  if (t256 >= 384) {
+    run2<256, 256, AK, BKC, EPI, 2>(p, s);
+    return 0;
+  }
+  if (EPI == EPI_ACCUM && t128 < 256 && nk >= 16 && ws != nullptr) {
+    // split K so that about 512 workgroups run; partials summed afterwards
+    int ks = (int)std::min<int64_t>(16, cdiv(512, t128));
+    ks = std::min(ks, nk / 4);
+    while (ks > 1 && (int64_t)ks * p.M * p.N * 4 > ws_bytes) --ks;
+    if (ks > 1) {
+      p.k_tiles_per_split = (int)cdiv(nk, ks);
+      ks = (int)cdiv(nk, p.k_tiles_per_split);
+      p.ksplit = ks;
+      p.part = ws;
+      run2<128, 128, AK, BKC, EPI, 4>(p, s);
+      const int64_t n = (int64_t)p.M * p.N;
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, ws, ks, n,
+                         (float*)p.e.out, p.e.beta);
+      return 0;
+    }
+  }
+  run2<128, 128, AK, BKC, EPI, 4>(p, s);
+  return 0;
+}
+
+}  // namespace
+
+// The pipelined kernel covers bf16 with k-contiguous K % 8 == 0, every
+// leading dimension % 8 == 0, N % 8 == 0, ldc % 8 == 0 and operands below
+// 4 GiB; otherwise returns -5 and the caller uses gemm.hip's kernel.
+int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda, const void* B,
+                 int ldb, int M, int N, int K, int ka_rows, int kb_rows, const GemmEpiArgs& e,
+                 float* ws, int64_t ws_bytes, hipStream_t s) {
+  if (K % 8 || lda % 8 || ldb % 8 || N % 8 || e.ldc % 8) return -5;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)e.out) & 15) return -5;
+  if ((e.aux && ((uintptr_t)e.aux & 15)) || (e.out2 && ((uintptr_t)e.out2 & 15))) return -5;
+  if (e.bias && ((uintptr_t)e.bias & 15)) return -5;
+  const int64_t abytes = (int64_t)(a_kcontig ? M : ka_rows) * lda * 2;
+  const int64_t bbytes = (int64_t)(b_kcontig ? N : kb_rows) * ldb * 2;
+  if (abytes >= (1ll << 32) - 4096 || bbytes >= (1ll << 32) - 4096) return -5;
+  Gemm2Args p{(const bf16_t*)A, (const bf16_t*)B, lda, ldb, M, N, K, ka_rows, kb_rows, 0, 0, 1, 0,
+              nullptr, e};
+#define G2(AKV, BKV, EPIV) \
+  if (a_kcontig == AKV && b_kcontig == BKV && epi == EPIV) return dispatch2<AKV, BKV, EPIV>(p, ws, ws_bytes, s);
+  G2(true, true, EPI_ACT)
+  G2(true, true, EPI_F32)
+  G2(true, true, EPI_RESID)
+  G2(true, true, EPI_GELU)
+  G2(true, false, EPI_ACT)
+  G2(true, false, EPI_F32)
+  G2(true, false, EPI_GELU_BWD)
+  G2(false, false, EPI_ACCUM)
+#undef G2
+  return -5;
+}

@@ -101,7 +101,8 @@ struct WsOff {
   size_t shadow = 0;
   std::vector<WsLayer> layer;
   size_t x_final, lnf_mean, lnf_rstd, lnf, logits, row_loss, nvalid, flags, scal;
-  size_t dres, dres_act, dln, dbig, dO, Dbuf, ln_part, cs_part, norm_part, chunks;
+  size_t dres, dres_act, dln, dbig, dO, Dbuf, ln_part, cs_part, norm_part, chunks, splitk;
+  int64_t splitk_bytes;
   size_t total;
   int nchunks;
   int64_t vi;  // logits row pitch: padded_vocab rounded up to 64
@@ -157,6 +158,8 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   w.ln_part = take((int64_t)layernorm_bwd_part_rows((int)M) * 3 * d * 4);
   w.cs_part = take((int64_t)colsum_part_rows((int)M) * 4 * d * 4);
   w.norm_part = take((int64_t)adamw_norm_blocks() * 8);
+  w.splitk_bytes = bf ? gemm_splitk_bytes(4 * d, d) : 0;
+  w.splitk = take(w.splitk_bytes);
   int64_t nch = 0;
   for (auto& t : p.tensors) nch += (t.second + kChunk - 1) / kChunk;
   w.nchunks = (int)nch;
@@ -372,6 +375,8 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
   void* dbig = h->at(w.dbig);
   float* ln_part = h->at<float>(w.ln_part);
   float* cs_part = h->at<float>(w.cs_part);
+  float* sk = w.splitk_bytes ? h->at<float>(w.splitk) : nullptr;
+  const int64_t skb = w.splitk_bytes;
 
   // LM head: dwte (+)= dlogits^T lnf ; dlnf = dlogits wte
   {
@@ -380,7 +385,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.ldc = d;
     e.beta = beta;
     CK(gemm_launch(bf, false, false, EPI_ACCUM, h->at(w.logits), vi, h->at(w.lnf), d,
-                   c.padded_vocab, d, M, M, M, e, s));
+                   c.padded_vocab, d, M, M, M, e, s, sk, skb));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -399,8 +404,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.mprojw);
     e.ldc = 4 * d;
     e.beta = beta;
-    CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.g), 4 * d, d, 4 * d, M, M, M, e,
-                   s));
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.g), 4 * d, d, 4 * d, M, M, M, e, s, sk, skb));
     e = GemmEpiArgs();
     e.out = dbig;
     e.aux = h->at(L.u);
@@ -413,8 +417,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.fcw);
     e.ldc = d;
     e.beta = beta;
-    CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 4 * d, h->at(L.ln2), d, 4 * d, d, M, M, M, e,
-                   s));
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 4 * d, h->at(L.ln2), d, 4 * d, d, M, M, M, e, s, sk, skb));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -428,7 +431,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.aprojw);
     e.ldc = d;
     e.beta = beta;
-    CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.att), d, d, d, M, M, M, e, s));
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.att), d, d, d, M, M, M, e, s, sk, skb));
     e = GemmEpiArgs();
     e.out = h->at(w.dO);
     e.ldc = d;
@@ -441,8 +444,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.attnw);
     e.ldc = d;
     e.beta = beta;
-    CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 3 * d, h->at(L.ln1), d, 3 * d, d, M, M, M, e,
-                   s));
+    CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 3 * d, h->at(L.ln1), d, 3 * d, d, M, M, M, e, s, sk, skb));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -516,14 +518,15 @@ int gpt_op_linear(int32_t bf16, const void* A, const void* B, const float* bias,
 }
 
 int gpt_op_linear_dw(int32_t bf16, const void* dY, const void* X, float* dW, int32_t accumulate,
-                     int32_t M, int32_t N, int32_t K, void* stream) {
+                     int32_t M, int32_t N, int32_t K, float* workspace, int64_t workspace_bytes,
+                     void* stream) {
   if (!dY || !X || !dW || M < 1 || N < 0 || K < 0) return fail(GPT_EINVAL, "bad linear_dw arguments");
   GemmEpiArgs e;
   e.out = dW;
   e.ldc = K;
   e.beta = accumulate ? 1 : 0;
   CK(gemm_launch(bf16 != 0, false, false, EPI_ACCUM, dY, N, X, K, N, K, M, M, M, e,
-                 (hipStream_t)stream));
+                 (hipStream_t)stream, workspace, workspace ? workspace_bytes : 0));
   return GPT_OK;
 }
 

@@ -137,27 +137,57 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
       }
     }
   }
-  // each wave writes its own partial row: part[(blk*4 + wave)][3][C]
-  float* out = part + ((int64_t)blockIdx.x * 4 + wave) * 3 * C;
+  // reduce the 4 waves' partials through LDS (one wave at a time) and write
+  // one partial row per block: part[blk][3][C]
+  __shared__ float red[3 * LN_MAXV * 256];
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    const int j = lane + 64 * i;
-    if (j < nv) {
-      ((float4*)out)[j] = pw[i];
-      ((float4*)(out + C))[j] = pb[i];
-      ((float4*)(out + 2 * C))[j] = pr[i];
+      for (int i = 0; i < LN_MAXV; ++i) {
+        const int j = lane + 64 * i;
+        if (j < nv) {
+          float4* r0 = (float4*)red + j;
+          float4* r1 = (float4*)(red + C) + j;
+          float4* r2 = (float4*)(red + 2 * C) + j;
+          if (w == 0) {
+            *r0 = pw[i]; *r1 = pb[i]; *r2 = pr[i];
+          } else {
+            float4 a = *r0, b = *r1, c = *r2;
+            a.x += pw[i].x; a.y += pw[i].y; a.z += pw[i].z; a.w += pw[i].w;
+            b.x += pb[i].x; b.y += pb[i].y; b.z += pb[i].z; b.w += pb[i].w;
+            c.x += pr[i].x; c.y += pr[i].y; c.z += pr[i].z; c.w += pr[i].w;
+            *r0 = a; *r1 = b; *r2 = c;
+          }
+        }
+      }
     }
+    __syncthreads();
   }
+  float* out = part + (int64_t)blockIdx.x * 3 * C;
+  for (int c = threadIdx.x; c < 3 * C; c += 256) out[c] = red[c];
 }
 
-// out[c] = (beta ? out[c] : 0) + sum_b part[b*stride + c], for c < n.
-__global__ void colsum_finalize_kernel(const float* __restrict__ part, int nblk, int64_t stride,
-                                       float* __restrict__ out, int n, int beta) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= n || out == nullptr) return;
+// Column sums of a partial matrix part[nrow][ncol] into up to three outputs:
+// column j goes to out[j / seg][j % seg] = (beta ? old : 0) + sum over rows.
+// 64 columns per block; the 4 waves split the rows, then combine in LDS in a
+// fixed order.
+__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __restrict__ part,
+                                                              int nrow, int ncol, int seg,
+                                                              float* out0, float* out1,
+                                                              float* out2, int beta) {
+  __shared__ float red[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
   float s = 0.f;
-  for (int b = 0; b < nblk; ++b) s += part[(int64_t)b * stride + c];
-  out[c] = (beta ? out[c] : 0.f) + s;
+  if (c < ncol)
+    for (int r = rg; r < nrow; r += 4) s += part[(int64_t)r * ncol + c];
+  red[rg][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (rg == 0 && c < ncol) {
+    const float t = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+    const int k = c / seg, i = c % seg;
+    float* o = k == 0 ? out0 : (k == 1 ? out1 : out2);
+    if (o) o[i] = (beta ? o[i] : 0.f) + t;
+  }
 }
 
 int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
@@ -173,7 +203,7 @@ int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float*
 }
 
 // partial rows written by one backward call (4 per block)
-int layernorm_bwd_part_rows(int M) { return 4 * (int)cdiv(M, LN_BWD_ROWS); }
+int layernorm_bwd_part_rows(int M) { return (int)cdiv(M, LN_BWD_ROWS); }
 
 // dres = (accumulate ? dres : 0) + LN'(dy); dres_act = copy; then
 // dw, db (beta-accumulated) and bias_grad (+)= column sum of dres, if non-null.
@@ -182,27 +212,21 @@ int layernorm_bwd_launch(bool bf16, const float* dy, const float* x, const float
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
                          int beta, int M, int C, hipStream_t s) {
   if (C % 4 || C > LN_MAXV * 256) return -5;
-  const int nb = (int)cdiv(M, LN_BWD_ROWS), np = 4 * nb;
+  const int nb = (int)cdiv(M, LN_BWD_ROWS);
   if (bf16)
     hipLaunchKernelGGL(ln_bwd_kernel<bf16_t>, dim3(nb), dim3(256), 0, s, dy, x, mean, rstd, w,
                        dres, (bf16_t*)dres_act, accumulate, part, M, C);
   else
     hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nb), dim3(256), 0, s, dy, x, mean, rstd, w, dres,
                        (float*)dres_act, accumulate, part, M, C);
-  const int64_t stride = 3 * (int64_t)C;
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(C, 256)), dim3(256), 0, s, part, np, stride,
-                     dw, C, beta);
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(C, 256)), dim3(256), 0, s, part + C, np,
-                     stride, db, C, beta);
-  if (bias_grad)
-    hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(C, 256)), dim3(256), 0, s, part + 2 * C,
-                       np, stride, bias_grad, C, beta);
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(3 * C, 64)), dim3(256), 0, s, part, nb,
+                     3 * C, C, dw, db, bias_grad, beta);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int colsum_finalize_launch(const float* part, int nblk, int64_t stride, float* out, int n, int beta,
+int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
                            hipStream_t s) {
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, part, nblk,
-                     stride, out, n, beta);
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(ncol, 64)), dim3(256), 0, s, part, nrow,
+                     ncol, ncol, out, nullptr, nullptr, beta);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -186,22 +186,45 @@ __global__ void loss_finalize_kernel(const float* __restrict__ row_loss, int N,
 }
 
 // ---------------------------------------------------------------- column sums
-// part[rb][n] = sum over rows rb*rows_per..(rb+1)*rows_per of a[row][n]
-// (bias gradients: db = sum over tokens of dy).
+// part[rb][n] = sum of a[row][n] over the CS_ROWS rows of block-row rb
+// (bias gradients: db = sum over tokens of dy).  Each thread owns 8
+// consecutive columns (one 16-byte bf16 load per row); the 4 waves split the
+// rows and combine in LDS in a fixed order.
 #define CS_ROWS 256
 template <typename T>
-__global__ void colsum_part_kernel(const T* __restrict__ a, int M, int N, float* __restrict__ part) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int rb = blockIdx.y;
-  if (n >= N) return;
-  const int r0 = rb * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
-  float s = 0.f;
-  for (int r = r0; r < r1; ++r) s += ldf(a + (int64_t)r * N + n);
-  part[(int64_t)rb * N + n] = s;
+__global__ __launch_bounds__(256) void colsum_part_kernel(const T* __restrict__ a, int M, int N,
+                                                          float* __restrict__ part) {
+  __shared__ float red[4][64 * 8];
+  const int lane = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * 64 + lane) * 8;
+  const int r0 = blockIdx.y * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (n0 < N) {
+    for (int r = r0 + rg; r < r1; r += 4) {
+      const T* p = a + (int64_t)r * N + n0;
+      if constexpr (sizeof(T) == 2) {
+        const uint4 v = *(const uint4*)p;
+        const uint32_t* w = (const uint32_t*)&v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
+      } else {
+        const float4 v0 = *(const float4*)p, v1 = *(const float4*)(p + 4);
+        s[0] += v0.x; s[1] += v0.y; s[2] += v0.z; s[3] += v0.w;
+        s[4] += v1.x; s[5] += v1.y; s[6] += v1.z; s[7] += v1.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][lane * 8 + e] = s[e];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int n = blockIdx.x * 512 + i;
+    if (n < N) part[(int64_t)blockIdx.y * N + n] = red[0][i] + red[1][i] + red[2][i] + red[3][i];
+  }
 }
 
 // ---------------------------------------------------------------- launchers
-int colsum_finalize_launch(const float* part, int nblk, int64_t stride, float* out, int n, int beta,
+int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
                            hipStream_t s);
 
 int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, float* x, int M,
@@ -248,16 +271,18 @@ int loss_finalize_launch(const float* row_loss, int N, const int* n_valid, float
 
 int colsum_part_rows(int M) { return (int)cdiv(M, CS_ROWS); }
 
-// out (+)= column sums of a [M][N]; part: fp32 scratch [colsum_part_rows(M)][N].
+// out (+)= column sums of a [M][N] (N % 8 == 0); part: fp32 scratch
+// [colsum_part_rows(M)][N].
 int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* out, int beta,
                   hipStream_t s) {
+  if (N % 8) return -5;
   const int nb = colsum_part_rows(M);
   if (bf16)
-    hipLaunchKernelGGL(colsum_part_kernel<bf16_t>, dim3(cdiv(N, 256), nb), dim3(256), 0, s,
+    hipLaunchKernelGGL(colsum_part_kernel<bf16_t>, dim3(cdiv(N, 512), nb), dim3(256), 0, s,
                        (const bf16_t*)a, M, N, part);
   else
-    hipLaunchKernelGGL(colsum_part_kernel<float>, dim3(cdiv(N, 256), nb), dim3(256), 0, s,
+    hipLaunchKernelGGL(colsum_part_kernel<float>, dim3(cdiv(N, 512), nb), dim3(256), 0, s,
                        (const float*)a, M, N, part);
   if (hipGetLastError() != hipSuccess) return -4;
-  return colsum_finalize_launch(part, nb, N, out, N, beta, s);
+  return colsum_finalize_launch(part, nb, N, out, beta, s);
 }
