@@ -13,7 +13,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgpt_hip.so")
+LIB_PATH = os.environ.get("GPT_HIP_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libgpt_hip.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m transformer_lm_02_amd.build`")
 lib = ctypes.CDLL(LIB_PATH)

@@ -111,3 +111,36 @@ int to_bf16_launch(const float* p, bf16_t* o, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(to_bf16_kernel, dim3(2048), dim3(256), 0, s, p, o, n);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+// Transposed bf16 copies of the weight matrices, so that the input-gradient
+// products dX = dY W read both operands along the reduction dimension.
+// One launch over a table of matrices; 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src,
+                                                             bf16_t* __restrict__ dst,
+                                                             const TransposeJob* __restrict__ jobs,
+                                                             int njobs) {
+  __shared__ bf16_t tile[64][66];
+  int j = 0;
+  while (j + 1 < njobs && (int)blockIdx.x >= jobs[j + 1].tile_begin) ++j;
+  const TransposeJob job = jobs[j];
+  const int t = blockIdx.x - job.tile_begin;
+  const int tiles_c = (job.cols + 63) / 64;
+  const int r0 = (t / tiles_c) * 64, c0 = (t % tiles_c) * 64;
+  const bf16_t* S = src + job.src;
+  bf16_t* D = dst + job.dst;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    if (r0 + r < job.rows && c0 + c < job.cols) tile[r][c] = S[(int64_t)(r0 + r) * job.cols + c0 + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c = i / 64, r = i % 64;  // output row c, column r
+    if (r0 + r < job.rows && c0 + c < job.cols) D[(int64_t)(c0 + c) * job.ld + r0 + r] = tile[r][c];
+  }
+}
+
+int transpose_bf16_launch(const bf16_t* src, bf16_t* dst, const TransposeJob* jobs, int njobs,
+                          int total_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(total_tiles), dim3(256), 0, s, src, dst, jobs, njobs);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}

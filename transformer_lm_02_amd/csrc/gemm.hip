@@ -348,6 +348,7 @@ int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* 
   GEMM_CASE(true, true, EPI_F32)
   GEMM_CASE(true, true, EPI_RESID)
   GEMM_CASE(true, true, EPI_GELU)
+  GEMM_CASE(true, true, EPI_GELU_BWD)
   // input gradients: dx = dy W
   GEMM_CASE(true, false, EPI_ACT)
   GEMM_CASE(true, false, EPI_F32)

@@ -16,6 +16,8 @@
 //  * the epilogue goes through LDS so every lane stores 8 contiguous outputs;
 //  * weight gradients with few output tiles split K over workgroups into an
 //    fp32 partial buffer that a second kernel sums in a fixed order.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -30,32 +32,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// One operand tile of ROWS x 64 (k) bf16 per stage.  Each wave issues
-// ROWS/32 loads of 1 KB (64 lanes x 16 bytes, contiguous in LDS).
-template <int ROWS, bool KC>
+// One operand tile of ROWS x BK (k) bf16 per stage.  Each wave issues
+// ROWS*BK/2048 loads of 1 KB (64 lanes x 16 bytes, contiguous in LDS).
+template <int ROWS, bool KC, int BK>
 struct Stage {
-  static constexpr int LOADS = ROWS / 32;
-  static constexpr int ELEMS = ROWS * 64;
+  static constexpr int ELEMS = ROWS * BK;
+  static constexpr int NLOAD = ELEMS / 512;  // 1 KB loads per stage
+  static constexpr int LOADS = NLOAD / 4;    // per wave
+  static_assert(NLOAD % 4 == 0, "tile must split into 4 waves of 1 KB loads");
+  static constexpr int CPR = KC ? BK / 8 : ROWS / 8;  // 16-byte chunks per LDS row
+  static constexpr int RPL = 64 / CPR;                // LDS rows per 1 KB load
+  static_assert(64 % CPR == 0, "1 KB load must cover whole LDS rows");
+  static_assert(KC || CPR % 16 == 0, "transposed tile needs whole 16-chunk bank groups");
   uint32_t voff[LOADS];
   int kofs[LOADS];
 
-  // k-contiguous: LDS [ROWS][64], chunk c of row r at position c ^ ((r>>1)&7)
-  // m-contiguous: LDS [64][ROWS], chunk c of k-row k at position c ^ (2*(k&3))
+  // k-contiguous: LDS [ROWS][BK]; chunk c of row r at position c ^ sw(r)
+  //   with sw(r) = (r>>1)&7 for BK 64, (r>>2)&3 for BK 32 (conflict-free
+  //   16-byte reads of 16 consecutive rows)
+  // m-contiguous: LDS [BK][ROWS]; chunk c of k-row k at position c ^ 4(k&3)
+  //   (conflict-free transposing reads of 4 k-rows x 32 columns: two
+  //   16-lane groups side by side)
+  __device__ __forceinline__ static int swz(int r) {
+    return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  }
   __device__ __forceinline__ void init(int row0, int ld, int lane, int wave) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int q = i * 4 + wave;
+      const int r = q * RPL + lane / CPR, pos = lane % CPR;
       if constexpr (KC) {
-        const int r = 8 * q + (lane >> 3), pc = lane & 7;
-        const int c = pc ^ ((r >> 1) & 7);
+        const int c = pos ^ swz(r);
         voff[i] = (uint32_t)(((int64_t)(row0 + r) * ld + 8 * c) * 2);
         kofs[i] = 8 * c;
       } else {
-        constexpr int CPR = ROWS / 8;          // 16-byte chunks per k-row
-        constexpr int RPL = 64 / CPR;          // k-rows per 1 KB load
-        const int k = q * RPL + lane / CPR, pos = lane % CPR;
-        const int c = pos ^ (2 * (k & 3));
-        voff[i] = (uint32_t)(((int64_t)k * ld + row0 + 8 * c) * 2);
+        const int c = pos ^ (4 * (r & 3));
+        voff[i] = (uint32_t)(((int64_t)r * ld + row0 + 8 * c) * 2);
         kofs[i] = 0;
       }
     }
@@ -67,9 +79,9 @@ struct Stage {
       const int q = i * 4 + wave;
       uint32_t off;
       if constexpr (KC) {
-        off = (kt * 64 + kofs[i] < K) ? voff[i] + (uint32_t)kt * 128u : kOOB;
+        off = (kt * BK + kofs[i] < K) ? voff[i] + (uint32_t)kt * (uint32_t)(BK * 2) : kOOB;
       } else {
-        off = voff[i] + (uint32_t)kt * (uint32_t)(64 * ld * 2);
+        off = voff[i] + (uint32_t)kt * (uint32_t)(BK * ld * 2);
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, AS3(lds + q * 512), 16, off, 0, 0, 0);
     }
@@ -78,15 +90,15 @@ struct Stage {
   __device__ __forceinline__ static bf16x8_t frag(const bf16_t* lds, int rbase, int ks, int lane) {
     if constexpr (KC) {
       const int r = rbase + (lane & 31), c = 2 * ks + (lane >> 5);
-      return *(const bf16x8_t*)(lds + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+      return *(const bf16x8_t*)(lds + r * BK + ((c ^ swz(r)) << 3));
     } else {
       const int G = lane >> 4, t = lane & 15;
       const int m = rbase + 16 * (G & 1) + 4 * (t & 3);
       const int k0 = 16 * ks + 8 * (G >> 1) + (t >> 2);
       const int c = m >> 3;
       const int ka = k0, kb = k0 + 4;
-      const bf16_t* pa = lds + ka * ROWS + ((c ^ (2 * (ka & 3))) << 3) + (m & 7);
-      const bf16_t* pb = lds + kb * ROWS + ((c ^ (2 * (kb & 3))) << 3) + (m & 7);
+      const bf16_t* pa = lds + ka * ROWS + ((c ^ (4 * (ka & 3))) << 3) + (m & 7);
+      const bf16_t* pb = lds + kb * ROWS + ((c ^ (4 * (kb & 3))) << 3) + (m & 7);
       const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (__attribute__((address_space(3))) bf16x4_t*)(pa));
       const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -179,14 +191,15 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
   }
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int NS>
-__global__ __launch_bounds__(256) void gemm2_kernel(Gemm2Args p) {
-  using SA = Stage<BM, AK>;
-  using SB = Stage<BN, BKC>;
+template <int BM, int BN, bool AK, bool BKC, int EPI, int NS, int BK, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
+  using SA = Stage<BM, AK, BK>;
+  using SB = Stage<BN, BKC, BK>;
   constexpr int STAGE_ELEMS = SA::ELEMS + SB::ELEMS;
   constexpr int WR = BM / 2, WC = BN / 2;   // wave tile
   constexpr int TM = WR / 32, TN = WC / 32; // 32x32 MFMA tiles per wave
-  constexpr int EP_PITCH = WC + 4;          // fp32 epilogue staging pitch
+  constexpr int KS = BK / 16;               // MFMA k-steps per k-tile
+  constexpr int EP_PITCH = WC + 8;          // fp32 staging pitch: rows r, r+4 32 banks apart
   constexpr int LDS_ELEMS_RING = NS * STAGE_ELEMS;
   constexpr int LDS_ELEMS_EPI = 4 * 32 * EP_PITCH * 2;  // in bf16 units
   constexpr int LDS_ELEMS = LDS_ELEMS_RING > LDS_ELEMS_EPI ? LDS_ELEMS_RING : LDS_ELEMS_EPI;
@@ -198,7 +211,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(Gemm2Args p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm = wave >> 1, wn = wave & 1;
   const int split = blockIdx.y;
-  const int nk_total = (p.K + 63) / 64;
+  const int nk_total = (p.K + BK - 1) / BK;
   const int kt0 = split * p.k_tiles_per_split;
   const int nk = min(nk_total - kt0, p.k_tiles_per_split);
 
@@ -220,6 +233,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(Gemm2Args p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   constexpr int L = SA::LOADS + SB::LOADS;  // loads per wave per stage
+  constexpr int NF = (TM + TN) * (AK ? 1 : 2) / 1;  // LDS reads per k-step (tr reads count 2)
+  (void)NF;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
     if (s < nk) {
@@ -227,30 +242,102 @@ __global__ __launch_bounds__(256) void gemm2_kernel(Gemm2Args p) {
       sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + s, p.ldb, p.K, wave);
     }
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt landed (the NS-2 younger stages may still be in flight)
-    if (kt + NS - 2 < nk) wait_vm_barrier<(NS - 2) * L>();
-    else wait_vm_barrier<0>();
-    if (kt + NS - 1 < nk) {
-      const int s = (kt + NS - 1) % NS;
-      sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + kt + NS - 1, p.lda, p.K, wave);
-      sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + kt + NS - 1, p.ldb, p.K, wave);
+  if constexpr (OCC > 1) {
+    // Two workgroups share the CU: the other one's MFMAs hide this one's
+    // latencies, so fragments are single-buffered (registers stay within the
+    // 256 per wave that two waves per SIMD allow).
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + NS - 2 < nk) wait_vm_barrier<(NS - 2) * L>();
+      else wait_vm_barrier<0>();
+      if (kt + NS - 1 < nk) {
+        const int s = (kt + NS - 1) % NS;
+        sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + kt + NS - 1, p.lda, p.K, wave);
+        sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + kt + NS - 1, p.ldb, p.K, wave);
+      }
+      const bf16_t* la = lds + (kt % NS) * STAGE_ELEMS;
+      const bf16_t* lb = la + SA::ELEMS;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = SA::frag(la, wm * WR + 32 * i, ks, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = SB::frag(lb, wn * WC + 32 * j, ks, lane);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
     }
-    const bf16_t* la = lds + (kt % NS) * STAGE_ELEMS;
-    const bf16_t* lb = la + SA::ELEMS;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = SA::frag(la, wm * WR + 32 * i, ks, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = SB::frag(lb, wn * WC + 32 * j, ks, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  } else {
+    // Software pipeline.  Stage kt is known resident after a wait (own DMA
+    // count) and a barrier (everyone's); that barrier sits before the last
+    // k-step of tile kt-1, so the first fragments of tile kt are read while the
+    // last MFMAs of tile kt-1 run, and fragments of k-step ks+1 while ks runs.
+    // Before each such barrier the wave's LDS reads of the older stage have
+    // completed (lgkmcnt 0), so the DMA that refills that slot cannot overtake
+    // them.
+    bf16x8_t fa[2][TM], fb[2][TN];
+    if (nk > 0) {
+      if (NS - 2 < nk) wait_vm_barrier<(NS - 2) * L>();
+      else wait_vm_barrier<0>();
+      const bf16_t* la = lds;
+      const bf16_t* lb = la + SA::ELEMS;
+  #pragma unroll
+      for (int i = 0; i < TM; ++i) fa[0][i] = SA::frag(la, wm * WR + 32 * i, 0, lane);
+  #pragma unroll
+      for (int j = 0; j < TN; ++j) fb[0][j] = SB::frag(lb, wn * WC + 32 * j, 0, lane);
     }
+    // one k-tile; HAS_NEXT: another tile follows (the last one is peeled so
+    // the pipelined body has no data-dependent branch around its waits)
+    auto tile = [&](int kt, auto has_next) {
+      constexpr bool HAS_NEXT = decltype(has_next)::value;
+      if (kt + NS - 1 < nk) {
+        const int s = (kt + NS - 1) % NS;
+        sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + kt + NS - 1, p.lda, p.K, wave);
+        sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + kt + NS - 1, p.ldb, p.K, wave);
+      }
+      const bf16_t* la = lds + (kt % NS) * STAGE_ELEMS;
+      const bf16_t* lb = la + SA::ELEMS;
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;  // KS is even: k-step 0 of every tile uses buffer 0
+        if (ks + 1 < KS) {
+  #pragma unroll
+          for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = SA::frag(la, wm * WR + 32 * i, ks + 1, lane);
+  #pragma unroll
+          for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = SB::frag(lb, wn * WC + 32 * j, ks + 1, lane);
+        } else if constexpr (HAS_NEXT) {
+          // next stage: wait for it, then read its first fragments.  The
+          // lgkmcnt(0) wait is the compiler-visible builtin (vmcnt 63, expcnt
+          // 7, lgkmcnt 0) so its own wait accounting knows the older reads
+          // have landed.
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          if (kt + NS - 1 < nk) wait_vm_barrier<(NS - 2) * L>();
+          else wait_vm_barrier<0>();
+          const bf16_t* na = lds + ((kt + 1) % NS) * STAGE_ELEMS;
+          const bf16_t* nb = na + SA::ELEMS;
+  #pragma unroll
+          for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = SA::frag(na, wm * WR + 32 * i, 0, lane);
+  #pragma unroll
+          for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = SB::frag(nb, wn * WC + 32 * j, 0, lane);
+        }
+  #pragma unroll
+        for (int i = 0; i < TM; ++i)
+  #pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        // interleave: LDS reads between MFMAs
+  #pragma unroll
+        for (int g = 0; g < TM + TN; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x100, AK && BKC ? 1 : 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN + TM + TN - 1) / (TM + TN), 0);
+        }
+      }
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::true_type());
+    if (nk > 0) tile(nk - 1, std::false_type());
   }
   // every wave is done with the ring before it is reused for the epilogue
   wait_vm_barrier<0>();
@@ -259,8 +346,9 @@ __global__ __launch_bounds__(256) void gemm2_kernel(Gemm2Args p) {
   // lane handles 8 consecutive columns of one row
   float* ep = (float*)lds + wave * 32 * EP_PITCH;
   constexpr int LPR = WC / 8;        // lanes per row
-  constexpr int RPI = 64 / LPR;      // rows per pass
+  constexpr int RPI = 64 / LPR;      // rows per pass (lanes >= RPI*LPR idle)
   const int my_c = 8 * (lane % LPR), my_r = lane / LPR;
+  const bool lane_on = my_r < RPI;
   const int gcol = n0 + wn * WC + my_c;
   float bias8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (EPI != EPI_ACCUM && EPI != EPI_GELU_BWD && p.e.bias != nullptr && gcol < p.N) {
@@ -285,10 +373,12 @@ __global__ __launch_bounds__(256) void gemm2_kernel(Gemm2Args p) {
     for (int rr = 0; rr < 32; rr += RPI) {
       const int lr = rr + my_r;
       const int grow = m0 + wm * WR + 32 * i + lr;
-      const float4 v0 = *(const float4*)(ep + lr * EP_PITCH + my_c);
-      const float4 v1 = *(const float4*)(ep + lr * EP_PITCH + my_c + 4);
-      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, p.ksplit > 1, grow, gcol, v, bias8);
+      if (lane_on && lr < 32) {
+        const float4 v0 = *(const float4*)(ep + lr * EP_PITCH + my_c);
+        const float4 v1 = *(const float4*)(ep + lr * EP_PITCH + my_c + 4);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, p.ksplit > 1, grow, gcol, v, bias8);
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
@@ -307,45 +397,70 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
   ((float4*)out)[i4] = s;
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int NS>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int NS, int BK, int OCC = 1>
 void run2(Gemm2Args p, hipStream_t s) {
   p.tiles_m = (int)cdiv(p.M, BM);
   p.tiles_n = (int)cdiv(p.N, BN);
-  hipLaunchKernelGGL((gemm2_kernel<BM, BN, AK, BKC, EPI, NS>), dim3(p.tiles_m * p.tiles_n, p.ksplit),
-                     dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm2_kernel<BM, BN, AK, BKC, EPI, NS, BK, OCC>),
+                     dim3(p.tiles_m * p.tiles_n, p.ksplit), dim3(256), 0, s, p);
 }
 
+// rounds of 256 workgroups (one per CU) times the work of one tile
+inline int64_t tile_cost(int64_t M, int64_t N, int BM, int BN) {
+  const int64_t t = cdiv(M, BM) * cdiv(N, BN);
+  return cdiv(t, 256) * BM * BN;
+}
+
+// Tile choice (measured on MI355X for the step's shapes):
+//  * weight gradients (both operands m/n-contiguous): 128x256 tiles, two
+//    workgroups per CU, the token reduction split so that about 400
+//    workgroups run (partials summed in order afterwards);
+//  * k-contiguous products: 256x192 tiles; with many tiles, 2 stages and two
+//    workgroups per CU (one's epilogue hides behind the other's MFMAs),
+//    otherwise 4 stages and one workgroup per CU;
+//  * small problems: 128x128 tiles.
 template <bool AK, bool BKC, int EPI>
 int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
-  const int64_t t256 = cdiv(p.M, 256) * cdiv(p.N, 256);
-  const int64_t t128 = cdiv(p.M, 128) * cdiv(p.N, 128);
-  const int nk = (int)cdiv(p.K, 64);
+  constexpr int BK = 32;
+  const int nk = (int)cdiv(p.K, BK);
   p.ksplit = 1;
   p.k_tiles_per_split = nk;
   p.part = nullptr;
-  if (t256 >= 384) {
-    run2<256, 256, AK, BKC, EPI, 2>(p, s);
-    return 0;
-  }
-  if (EPI == EPI_ACCUM && t128 < 256 && nk >= 16 && ws != nullptr) {
-    // split K so that about 512 workgroups run; partials summed afterwards
-    int ks = (int)std::min<int64_t>(16, cdiv(512, t128));
-    ks = std::min(ks, nk / 4);
-    while (ks > 1 && (int64_t)ks * p.M * p.N * 4 > ws_bytes) --ks;
+  if constexpr (EPI == EPI_ACCUM && !AK && !BKC) {
+    const int64_t tiles = cdiv(p.M, 128) * cdiv(p.N, 256);
+    int ks = 1;
+    if (ws != nullptr && nk >= 16) {
+      ks = (int)std::max<int64_t>(1, std::min<int64_t>(16, (400 + tiles / 2) / tiles));
+      ks = std::min(ks, std::max(1, nk / 8));
+      while (ks > 1 && (int64_t)ks * p.M * p.N * 4 > ws_bytes) --ks;
+    }
     if (ks > 1) {
       p.k_tiles_per_split = (int)cdiv(nk, ks);
       ks = (int)cdiv(nk, p.k_tiles_per_split);
       p.ksplit = ks;
       p.part = ws;
-      run2<128, 128, AK, BKC, EPI, 4>(p, s);
+    }
+    run2<128, 256, AK, BKC, EPI, 2, BK, 2>(p, s);
+    if (p.ksplit > 1) {
       const int64_t n = (int64_t)p.M * p.N;
-      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, ws, ks, n,
-                         (float*)p.e.out, p.e.beta);
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, ws, p.ksplit,
+                         n, (float*)p.e.out, p.e.beta);
+    }
+    return 0;
+  } else {
+    const int64_t t256 = cdiv(p.M, 256) * cdiv(p.N, 256);
+    if (t256 < 64) {  // small problem: smaller tiles keep more CUs busy
+      run2<128, 128, AK, BKC, EPI, 4, 64>(p, s);
       return 0;
     }
+    if constexpr (BKC) {
+      if (cdiv(p.M, 256) * cdiv(p.N, 192) >= 512) run2<256, 192, AK, BKC, EPI, 2, BK, 2>(p, s);
+      else run2<256, 192, AK, BKC, EPI, 4, BK, 1>(p, s);
+    } else {
+      run2<256, 256, AK, BKC, EPI, 4, BK, 1>(p, s);
+    }
+    return 0;
   }
-  run2<128, 128, AK, BKC, EPI, 4>(p, s);
-  return 0;
 }
 
 }  // namespace
@@ -371,6 +486,7 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
   G2(true, true, EPI_F32)
   G2(true, true, EPI_RESID)
   G2(true, true, EPI_GELU)
+  G2(true, true, EPI_GELU_BWD)
   G2(true, false, EPI_ACT)
   G2(true, false, EPI_F32)
   G2(true, false, EPI_GELU_BWD)

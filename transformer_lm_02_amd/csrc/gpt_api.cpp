@@ -16,6 +16,8 @@
 #include "gpt_hip.h"
 #include "kernels.h"
 
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 namespace {
 
 thread_local std::string g_err;
@@ -95,6 +97,7 @@ ParamOff param_offsets(const gpt_config& c) {
 
 // byte offsets of every buffer in the workspace
 struct WsLayer {
+  int64_t attnT, aprojT, fcT, mprojT;  // element offsets in the transposed copy
   size_t x_in, ln1_mean, ln1_rstd, ln1, qkv, att, lse, x_mid, ln2_mean, ln2_rstd, ln2, u, g;
 };
 struct WsOff {
@@ -106,6 +109,9 @@ struct WsOff {
   size_t total;
   int nchunks;
   int64_t vi;  // logits row pitch: padded_vocab rounded up to 64
+  size_t wT = 0, tjobs = 0;  // transposed bf16 weights; their job table
+  int64_t wteT = 0, wT_elems = 0;
+  int njobs = 0, ttiles = 0;
 };
 
 constexpr int64_t kChunk = 8192;
@@ -123,8 +129,28 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   const int64_t M = (int64_t)c.max_batch * c.block_size, d = c.n_embd, H = c.n_head;
   w.vi = round_up(c.padded_vocab, 64);
   if (bf) w.shadow = take(p.total * 2);
+  // transposed copies (bf16 mode): wte^T [d][vi] (columns >= Vp zero), then
+  // per layer attn^T [d][3d], aproj^T [d][d], fc^T [d][4d], mproj^T [4d][d]
+  int64_t te = 0;
+  w.wteT = te;
+  te += d * w.vi;
+  std::vector<int64_t> lt;
+  for (int l = 0; l < c.n_layer; ++l) {
+    lt.push_back(te);
+    te += 12 * d * d;
+  }
+  w.wT_elems = bf ? te : 0;
+  if (bf) {
+    w.wT = take(te * 2);
+    w.njobs = 1 + 4 * c.n_layer;
+    w.tjobs = take((int64_t)w.njobs * (int64_t)sizeof(TransposeJob));
+  }
   for (int l = 0; l < c.n_layer; ++l) {
     WsLayer L;
+    L.attnT = lt[l];
+    L.aprojT = L.attnT + 3 * d * d;
+    L.fcT = L.aprojT + d * d;
+    L.mprojT = L.fcT + 4 * d * d;
     L.x_in = take(M * d * 4);
     L.ln1_mean = take(M * 4);
     L.ln1_rstd = take(M * 4);
@@ -196,6 +222,7 @@ struct gpt_model {
   float *params, *grads, *m, *v;
   char* ws;
   std::vector<AdamChunk> chunks;
+  std::vector<TransposeJob> tjobs;
   bool have_fwd = false, have_targets = false;
   int B = 0, T = 0;
   const int32_t* idx = nullptr;
@@ -209,6 +236,12 @@ struct gpt_model {
   // matrix operand copy of a weight: bf16 copy in bf16 mode, fp32 params otherwise
   const void* W(int64_t off) const {
     return bf16() ? (const void*)(at<bf16_t>(wo.shadow) + off) : (const void*)(params + off);
+  }
+  const bf16_t* WT(int64_t off) const { return at<bf16_t>(wo.wT) + off; }
+  int refresh_transposes(hipStream_t s) const {
+    if (!bf16()) return 0;
+    return transpose_bf16_launch(at<bf16_t>(wo.shadow), at<bf16_t>(wo.wT),
+                                 at<TransposeJob>(wo.tjobs), wo.njobs, wo.ttiles, s);
   }
 };
 
@@ -248,6 +281,24 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
     for (int64_t c = 0; c < n; c += kChunk)
       h->chunks.push_back({o + c, (int32_t)std::min<int64_t>(kChunk, n - c), h->po.is2d[i]});
   }
+  if (h->bf16()) {
+    const int64_t d = cfg->n_embd;
+    int tiles = 0;
+    auto job = [&](int64_t src, int64_t dst, int64_t rows, int64_t cols, int64_t ld) {
+      h->tjobs.push_back({src, dst, (int32_t)rows, (int32_t)cols, (int32_t)ld, tiles});
+      tiles += (int)(cdiv(rows, 64) * cdiv(cols, 64));
+    };
+    job(h->po.wte, h->wo.wteT, cfg->padded_vocab, d, h->wo.vi);
+    for (int l = 0; l < cfg->n_layer; ++l) {
+      const LayerOff& P = h->po.layer[l];
+      const WsLayer& L = h->wo.layer[l];
+      job(P.attnw, L.attnT, 3 * d, d, 3 * d);
+      job(P.aprojw, L.aprojT, d, d, d);
+      job(P.fcw, L.fcT, 4 * d, d, 4 * d);
+      job(P.mprojw, L.mprojT, d, 4 * d, d);
+    }
+    h->wo.ttiles = tiles;
+  }
   const int64_t nb = h->po.total * 4;
   hipError_t e = hipSuccess;
   if (init_params && init_params != params)
@@ -259,6 +310,12 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->ws + h->wo.chunks, h->chunks.data(), h->chunks.size() * sizeof(AdamChunk),
                        hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && h->bf16()) {
+    e = hipMemcpyAsync(h->ws + h->wo.tjobs, h->tjobs.data(), h->tjobs.size() * sizeof(TransposeJob),
+                       hipMemcpyHostToDevice, s);
+    // columns Vp..vi of wte^T stay zero
+    if (e == hipSuccess) e = hipMemsetAsync(h->ws + h->wo.wT, 0, h->wo.wT_elems * 2, s);
+  }
   // the host table must outlive the copy: wait for it once, at set-up
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
@@ -268,6 +325,7 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
   }
   if (h->bf16()) {
     rc = to_bf16_launch(params, h->at<bf16_t>(h->wo.shadow), h->po.total, s);
+    if (!rc) rc = h->refresh_transposes(s);
     if (rc) {
       delete h;
       return map_rc(rc);
@@ -389,8 +447,12 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
-    CK(gemm_launch(bf, true, false, EPI_F32, h->at(w.logits), vi, h->W(p.wte), d, M, d, vi, vi,
-                   c.padded_vocab, e, s));
+    if (bf)
+      CK(gemm_launch(bf, true, true, EPI_F32, h->at(w.logits), vi, h->WT(w.wteT), vi, M, d, vi, vi,
+                     vi, e, s));
+    else
+      CK(gemm_launch(bf, true, false, EPI_F32, h->at(w.logits), vi, h->W(p.wte), d, M, d, vi, vi,
+                     c.padded_vocab, e, s));
   }
   CK(layernorm_bwd_launch(bf, dln, h->at<float>(w.x_final), h->at<float>(w.lnf_mean),
                           h->at<float>(w.lnf_rstd), h->P(p.lnfw), dres, dres_act, 0, ln_part,
@@ -409,8 +471,12 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = dbig;
     e.aux = h->at(L.u);
     e.ldc = 4 * d;
-    CK(gemm_launch(bf, true, false, EPI_GELU_BWD, dres_act, d, h->W(P.mprojw), 4 * d, M, 4 * d, d,
-                   d, d, e, s));
+    if (bf)
+      CK(gemm_launch(bf, true, true, EPI_GELU_BWD, dres_act, d, h->WT(L.mprojT), d, M, 4 * d, d, d,
+                     d, e, s));
+    else
+      CK(gemm_launch(bf, true, false, EPI_GELU_BWD, dres_act, d, h->W(P.mprojw), 4 * d, M, 4 * d, d,
+                     d, d, e, s));
     // MLP expansion: db = colsum(du); dW (+)= du^T ln2 ; dln2 = du Wfc
     CK(colsum_launch(bf, dbig, M, 4 * d, cs_part, h->G(P.fcb), beta, s));
     e = GemmEpiArgs();
@@ -421,8 +487,12 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
-    CK(gemm_launch(bf, true, false, EPI_F32, dbig, 4 * d, h->W(P.fcw), d, M, d, 4 * d, 4 * d,
-                   4 * d, e, s));
+    if (bf)
+      CK(gemm_launch(bf, true, true, EPI_F32, dbig, 4 * d, h->WT(L.fcT), 4 * d, M, d, 4 * d, 4 * d,
+                     4 * d, e, s));
+    else
+      CK(gemm_launch(bf, true, false, EPI_F32, dbig, 4 * d, h->W(P.fcw), d, M, d, 4 * d, 4 * d,
+                     4 * d, e, s));
     CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_mid), h->at<float>(L.ln2_mean),
                             h->at<float>(L.ln2_rstd), h->P(P.ln2w), dres, dres_act, 1, ln_part,
                             h->G(P.ln2w), h->G(P.ln2b), h->G(P.aprojb), beta, M, d, s));
@@ -435,7 +505,10 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e = GemmEpiArgs();
     e.out = h->at(w.dO);
     e.ldc = d;
-    CK(gemm_launch(bf, true, false, EPI_ACT, dres_act, d, h->W(P.aprojw), d, M, d, d, d, d, e, s));
+    if (bf)
+      CK(gemm_launch(bf, true, true, EPI_ACT, dres_act, d, h->WT(L.aprojT), d, M, d, d, d, d, e, s));
+    else
+      CK(gemm_launch(bf, true, false, EPI_ACT, dres_act, d, h->W(P.aprojw), d, M, d, d, d, d, e, s));
     CK(attention_bwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), h->at(w.dO), dbig,
                             h->at<float>(w.Dbuf), B, T, H, d, s));
     // fused q|k|v projection: db = colsum(dqkv); dW (+)= dqkv^T ln1 ; dln1 = dqkv Wqkv
@@ -448,8 +521,12 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
-    CK(gemm_launch(bf, true, false, EPI_F32, dbig, 3 * d, h->W(P.attnw), d, M, d, 3 * d, 3 * d,
-                   3 * d, e, s));
+    if (bf)
+      CK(gemm_launch(bf, true, true, EPI_F32, dbig, 3 * d, h->WT(L.attnT), 3 * d, M, d, 3 * d, 3 * d,
+                     3 * d, e, s));
+    else
+      CK(gemm_launch(bf, true, false, EPI_F32, dbig, 3 * d, h->W(P.attnw), d, M, d, 3 * d, 3 * d,
+                     3 * d, e, s));
     CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_in), h->at<float>(L.ln1_mean),
                             h->at<float>(L.ln1_rstd), h->P(P.ln1w), dres, dres_act, 1, ln_part,
                             h->G(P.ln1w), h->G(P.ln1b), l > 0 ? h->G(p.layer[l - 1].mprojb) : nullptr,
@@ -473,6 +550,7 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, 
                   h->at<AdamChunk>(w.chunks), w.nchunks, h->at<double>(w.norm_part),
                   h->at<float>(w.scal), norm_out, lr, beta1, beta2, eps, weight_decay, max_norm, t,
                   skip_nonfinite, s));
+  CK(h->refresh_transposes(s));
   return GPT_OK;
 }
 

@@ -14,6 +14,15 @@ struct AdamChunk {
   int32_t decay;
 };
 
+// one matrix of the transposed weight copy: src [rows][cols] (elements from
+// the start of the bf16 weights) -> dst [cols][ld] (ld >= rows)
+struct TransposeJob {
+  int64_t src, dst;
+  int32_t rows, cols, ld, tile_begin;
+};
+int transpose_bf16_launch(const bf16_t* src, bf16_t* dst, const TransposeJob* jobs, int njobs,
+                          int total_tiles, hipStream_t s);
+
 int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
                          int C, hipStream_t s);
 int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
