@@ -168,7 +168,8 @@ int gpt_op_attention_fwd(int32_t bf16, const void* qkv, void* out, float* lse,
                          int32_t B, int32_t T, int32_t H, int32_t C, void* stream);
 
 /* Its backward: dout act [B*T][C] -> dqkv act [B*T][3*C] (every element
- * written).  D: fp32 scratch [B][H][T], receives rowsum(dout * out). */
+ * written).  D: fp32 scratch [2][B][H][T]; D[0] receives rowsum(dout * out),
+ * D[1] the row logsumexp times log2(e). */
 int gpt_op_attention_bwd(int32_t bf16, const void* qkv, const void* out,
                          const float* lse, const void* dout, void* dqkv, float* D,
                          int32_t B, int32_t T, int32_t H, int32_t C, void* stream);

@@ -212,7 +212,7 @@ def op_attention_bwd(qkv, out, lse, dout, B, T, H):
     import torch
     C = qkv.shape[-1] // 3
     dqkv = torch.empty_like(qkv)
-    D = torch.empty((B, H, T), dtype=torch.float32, device=qkv.device)
+    D = torch.empty((2, B, H, T), dtype=torch.float32, device=qkv.device)
     check(lib.gpt_op_attention_bwd(_bf(qkv), _ptr(qkv), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dqkv),
                                    _ptr(D), B, T, H, C, _stream()), "gpt_op_attention_bwd")
     return dqkv

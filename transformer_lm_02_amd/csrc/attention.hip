@@ -15,6 +15,8 @@
 // registers are directly the B operand of O^T = V^T P^T.  The backward is two
 // kernels: dK/dV per key block (iterating over query blocks) and dQ per
 // query block (iterating over key blocks), so no atomics are needed.
+#include <type_traits>
+
 #include "common.h"
 
 #define LOG2E 1.4426950408889634f
@@ -51,10 +53,13 @@ __global__ void attn_fwd_generic(const T* __restrict__ qkv, T* __restrict__ out,
   lse[(int64_t)bh * Tn + q] = m + logf(l);
 }
 
-// D[bh][q] = sum_c dO[q][c] * O[q][c]  (= rowsum(P * dP))
+// D[bh][q] = sum_c dO[q][c] * O[q][c]  (= rowsum(P * dP)); with L2 given,
+// also L2[bh][q] = lse[bh][q] * log2(e) (the exponent offset of the bf16
+// backward kernels)
 template <typename T>
 __global__ void attn_bwd_dot(const T* __restrict__ out, const T* __restrict__ dout,
-                             float* __restrict__ D, int B, int Tn, int H, int C) {
+                             const float* __restrict__ lse, float* __restrict__ D,
+                             float* __restrict__ L2, int B, int Tn, int H, int C) {
   const int hs = C / H;
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -65,7 +70,43 @@ __global__ void attn_bwd_dot(const T* __restrict__ out, const T* __restrict__ do
   float s = 0.f;
   for (int c = lane; c < hs; c += 64) s += ldf(O + c) * ldf(dO + c);
   s = wave_sum(s);
-  if (lane == 0) D[row] = s;
+  if (lane == 0) {
+    D[row] = s;
+    if (L2) L2[row] = lse[row] * LOG2E;
+  }
+}
+
+// The same for head width 64 in bf16: one thread per 8 columns (16 bytes of
+// out and of dout), the 8 threads of a (row, head) pair combine by shuffles.
+__global__ __launch_bounds__(256) void attn_bwd_dot64_kernel(const bf16_t* __restrict__ out,
+                                                             const bf16_t* __restrict__ dout,
+                                                             const float* __restrict__ lse,
+                                                             float* __restrict__ D,
+                                                             float* __restrict__ L2, int Tn, int H,
+                                                             int64_t nchunk) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float s = 0.f;
+  if (i < nchunk) {
+    const uint4 a = *(const uint4*)(out + 8 * i);
+    const uint4 g = *(const uint4*)(dout + 8 * i);
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s = fmaf(__uint_as_float(av[j] << 16), __uint_as_float(gv[j] << 16), s);
+      s = fmaf(__uint_as_float(av[j] & 0xffff0000u), __uint_as_float(gv[j] & 0xffff0000u), s);
+    }
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  if (i < nchunk && (i & 7) == 0) {
+    const int64_t row = i / (8 * H);  // b * Tn + t
+    const int hh = (int)((i / 8) % H);
+    const int64_t bb = row / Tn, t = row % Tn;
+    const int64_t o = (bb * H + hh) * Tn + t;
+    D[o] = s;
+    L2[o] = lse[o] * LOG2E;
+  }
 }
 
 template <typename T>
@@ -137,68 +178,61 @@ __global__ void attn_bwd_dkdv_generic(const T* __restrict__ qkv, const float* __
 }
 
 // ================================================================ bf16 flash kernels (hs = 64)
-// LDS tiles of 64 rows x 64 bf16:
-//  "row" layout  [row][64], 16-byte chunk c of row r at chunk position c ^ (r & 7);
-//  "tr" layout   [col][64] holding the transpose (element (row, col) at
-//                [col][row]), 8-byte unit u (4 rows) of line col at u ^ (col & 15).
-__device__ __forceinline__ int row_off(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
-__device__ __forceinline__ int tr_off(int col, int u) { return col * 64 + ((u ^ (col & 15)) << 2); }
+// Tiles of 64 rows x 64 bf16 (one row per key or query, head dims
+// contiguous) go from HBM into LDS with buffer loads in LDS mode, through a
+// ring of NS stages.  A tile keeps its memory layout; the 16-byte chunk c of
+// row r is stored at position c ^ f(r), f(r) = 4*((r>>1)&1) + ((r>>2)&3),
+// which makes both access patterns conflict-free: plain 16-byte reads of 16
+// consecutive rows (an MFMA operand whose k index is the head dimension) and
+// the gfx950 transposing read ds_read_b64_tr_b16 of 4 rows x 32 columns (an
+// operand whose k index is the key or query).
+#define AS3(p) ((__attribute__((address_space(3))) void*)(p))
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-// Stage a 64 x 64 bf16 tile (global rows r0.., row pitch ld, columns at col0)
-// into LDS in "row" layout; rows >= nrows are zero.  256 threads, 2 chunks each.
-__device__ __forceinline__ void stage_row(bf16_t* lds, const bf16_t* __restrict__ g, int64_t ld,
-                                          int r0, int nrows, int tid) {
+__device__ __forceinline__ int tsw(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// This wave's share (2 of 8 loads of 1 KB) of a 64 x 64 tile whose row 0 is
+// global row `row0` of a buffer with row pitch `ld` elements (rows past the
+// buffer's end read as zero).
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, int row0, int ld,
+                                         int col0, int lane, int wave) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, r = idx >> 3, c = idx & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < nrows) v = *(const uint4*)(g + (int64_t)(r0 + r) * ld + 8 * c);
-    *(uint4*)(lds + row_off(r, c)) = v;
+    const int q = 2 * wave + i;
+    const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ tsw(r);
+    const uint32_t off = (uint32_t)(((int64_t)(row0 + r) * ld + col0 + 8 * c) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, AS3(lds + q * 512), 16, off, 0, 0, 0);
   }
 }
-// Same tile into the "tr" layout (transposed).  Each thread reads 2 rows x 8
-// columns and writes 8 packed pairs.
-__device__ __forceinline__ void stage_tr(bf16_t* lds, const bf16_t* __restrict__ g, int64_t ld,
-                                         int r0, int nrows, int tid) {
-  const int cc = tid & 7, rp = tid >> 3;  // column chunk, row pair (0..31)
-  const int r = 2 * rp;
-  uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-  if (r0 + r < nrows) a = *(const uint4*)(g + (int64_t)(r0 + r) * ld + 8 * cc);
-  if (r0 + r + 1 < nrows) b = *(const uint4*)(g + (int64_t)(r0 + r + 1) * ld + 8 * cc);
-  const uint32_t* pa = (const uint32_t*)&a;
-  const uint32_t* pb = (const uint32_t*)&b;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int w = j >> 1;
-    const uint32_t v = (j & 1) ? ((pa[w] >> 16) | (pb[w] & 0xffff0000u))
-                               : ((pa[w] & 0xffffu) | (pb[w] << 16));
-    const int col = 8 * cc + j;
-    // rows r, r+1 live in unit r/4 at half (r % 4) / 2
-    *(uint32_t*)(lds + tr_off(col, r >> 2) + (r & 3)) = v;
-  }
+// 32x32x16 MFMA operand with rows = tile rows base..base+31 and k = head dims
+// 16ks + 8(lane/32) + 0..7 (plain read)
+__device__ __forceinline__ bf16x8_t frag_hd(const bf16_t* t, int base, int ks, int lane) {
+  const int r = base + (lane & 31), c = 2 * ks + (lane >> 5);
+  return *(const bf16x8_t*)(t + r * 64 + ((c ^ tsw(r)) << 3));
 }
-
-// A/B operand of a 32x32x16 MFMA from the "row" layout: row base+lane%32,
-// k-chunk (2*ks + lane/32).
-__device__ __forceinline__ bf16x8_t frag_row(const bf16_t* lds, int base, int ks, int lane) {
-  return *(const bf16x8_t*)(lds + row_off(base + (lane & 31), 2 * ks + (lane >> 5)));
+// 32x32x16 MFMA operand with rows = head dims col0..col0+31 and k = tile rows
+// 16ks + 8(j/4) + 4(lane/32) + j%4 (j = 0..7), the order in which a 32x32
+// accumulator holds its rows (transposing read)
+__device__ __forceinline__ bf16x8_t frag_rows(const bf16_t* __restrict__ t, int col0, int ks, int lane) {
+  const int G = lane >> 4, u = lane & 15;
+  const int col = col0 + 16 * (G & 1) + 4 * (u & 3);
+  const int r0 = 16 * ks + 4 * (G >> 1) + (u >> 2);
+  const int c = col >> 3;
+  const bf16_t* pa = t + r0 * 64 + ((c ^ tsw(r0)) << 3) + (col & 7);
+  const bf16_t* pb = t + (r0 + 8) * 64 + ((c ^ tsw(r0 + 8)) << 3) + (col & 7);
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)pa);
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)pb);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-// Operand whose k index runs over the rows of a "tr" tile, in the order of
-// the 32x32 accumulator layout: line `col`, rows 16*ks + 8*(j/4) + 4*g + j%4.
-__device__ __forceinline__ bf16x8_t frag_tr(const bf16_t* lds, int col, int ks, int lane) {
-  const int g = lane >> 5;
-  const uint2 lo = *(const uint2*)(lds + tr_off(col, 4 * ks + g));
-  const uint2 hi = *(const uint2*)(lds + tr_off(col, 4 * ks + 2 + g));
-  uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  return *(bf16x8_t*)&v;
-}
-// 8 accumulator values (registers 8s..8s+7 of a 32x32 tile) -> bf16 operand.
-__device__ __forceinline__ bf16x8_t pack_acc(const f32x16_t& a, int s, float mul) {
+// 8 accumulator values (registers 8s..8s+7 of a 32x32 tile) -> bf16 operand
+__device__ __forceinline__ bf16x8_t pack_acc(const f32x16_t& a, int s) {
   uint4 v;
-  v.x = pack2bf(a[8 * s + 0] * mul, a[8 * s + 1] * mul);
-  v.y = pack2bf(a[8 * s + 2] * mul, a[8 * s + 3] * mul);
-  v.z = pack2bf(a[8 * s + 4] * mul, a[8 * s + 5] * mul);
-  v.w = pack2bf(a[8 * s + 6] * mul, a[8 * s + 7] * mul);
+  v.x = pack2bf(a[8 * s + 0], a[8 * s + 1]);
+  v.y = pack2bf(a[8 * s + 2], a[8 * s + 3]);
+  v.z = pack2bf(a[8 * s + 4], a[8 * s + 5]);
+  v.w = pack2bf(a[8 * s + 6], a[8 * s + 7]);
   return *(bf16x8_t*)&v;
 }
 __device__ __forceinline__ f32x16_t zero16() {
@@ -207,105 +241,133 @@ __device__ __forceinline__ f32x16_t zero16() {
   for (int r = 0; r < 16; ++r) z[r] = 0.f;
   return z;
 }
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// 2^x by the hardware instruction; every argument here is <= 0 or -inf, so
+// no range reduction is needed (results below 2^-126 flush to zero)
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 #define MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 // row offset inside a 32x32 accumulator tile for register r of this lane
 #define ACC_ROW(r, lane) (8 * ((r) >> 2) + 4 * ((lane) >> 5) + ((r) & 3))
+#define FLASH_NS 3  // the key / query loops below are unrolled by exactly 3
+#define TILE_ELEMS 4096
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int N>
+using Slot = std::integral_constant<int, N>;
 
 // ---------------------------------------------------------------- forward
-// grid: (T/128 query blocks, heaviest first) x (B*H); 4 waves x 32 query rows.
-__global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
-                                                        bf16_t* __restrict__ out,
-                                                        float* __restrict__ lse, int B, int Tn,
-                                                        int H, int C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[2][64 * 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// grid: (T/128 query blocks, heaviest first) x (B*H); 4 waves x 32 query
+// rows.  S^T = K Q^T puts one query per lane, so the running max and sum are
+// the lane's own; P^T in the accumulator registers is directly the B operand
+// of O^T = V^T P^T.  The key loop is unrolled by the ring depth so that every
+// LDS address is a per-lane base plus an immediate offset.
+__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
+                                                           bf16_t* __restrict__ out,
+                                                           float* __restrict__ lse, int B, int Tn,
+                                                           int H, int C) {
+  __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2][TILE_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int nqb = (Tn + 127) / 128;
   const int qb = nqb - 1 - (int)(blockIdx.x / (B * H));
   const int bh = blockIdx.x % (B * H), b = bh / H, h = bh % H;
   const int q0 = qb * 128, qw = q0 + 32 * wave;
-  const int64_t ld = 3 * (int64_t)C;
+  const int ld = 3 * C;
   const bf16_t* base = qkv + (int64_t)b * Tn * ld;
-  const bf16_t* Kg = base + C + h * 64;
-  const bf16_t* Vg = base + 2 * C + h * 64;
-
-  // Q^T operand (B of S^T = K Q^T): lane holds Q[qw + lane%32][16ks + 8g + j]
-  bf16x8_t fq[4];
-  {
-    const int q = qw + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (q < Tn) v = *(const uint4*)(base + (int64_t)q * ld + h * 64 + 16 * ks + 8 * (lane >> 5));
-      fq[ks] = *(bf16x8_t*)&v;
-    }
-  }
-  const float sc = LOG2E * 0.125f;  // log2(e) / sqrt(64)
-  float m = -INFINITY, l = 0.f;
-  f32x16_t o[2] = {zero16(), zero16()};
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(base, (uint32_t)((int64_t)Tn * ld * 2));
   const int my_q = qw + (lane & 31);
 
-  const int kv_end = min(Tn, q0 + 128);
-  const int nkv = (kv_end + 63) / 64;
-  stage_row(sK[0], Kg, ld, 0, Tn, tid);
-  stage_tr(sVt[0], Vg, ld, 0, Tn, tid);
-  __syncthreads();
-  for (int kb = 0; kb < nkv; ++kb) {
-    const int cur = kb & 1, kv0 = kb * 64;
-    if (kb + 1 < nkv) {
-      stage_row(sK[cur ^ 1], Kg, ld, kv0 + 64, Tn, tid);
-      stage_tr(sVt[cur ^ 1], Vg, ld, kv0 + 64, Tn, tid);
+  bf16x8_t fq[4];  // Q^T operand: lane holds Q[my_q][16ks + 8(lane/32) + 0..7]
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (my_q < Tn) v = *(const uint4*)(base + (int64_t)my_q * ld + h * 64 + 16 * ks + 8 * (lane >> 5));
+    fq[ks] = *(bf16x8_t*)&v;
+  }
+  const float sc = LOG2E * 0.125f;  // log2(e) / sqrt(64)
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float m = -INFINITY, l = 0.f;     // m in log2 units of the scaled scores
+  f32x16_t o[2] = {zero16(), zero16()};
+  const int nkv = (min(Tn, q0 + 128) + 63) / 64;
+#pragma unroll
+  for (int st = 0; st < FLASH_NS - 1; ++st)
+    if (st < nkv) {
+      tile_dma(rs, ring[st][0], 64 * st, ld, C + h * 64, lane, wave);
+      tile_dma(rs, ring[st][1], 64 * st, ld, 2 * C + h * 64, lane, wave);
     }
-    if (kv0 <= qw + 31) {  // some key of this block is visible to this wave
-      f32x16_t s[2] = {zero16(), zero16()};
+  auto step = [&](int kb, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    if (kb + FLASH_NS - 2 < nkv) vm_wait_barrier<(FLASH_NS - 2) * 4>();
+    else vm_wait_barrier<0>();
+    if (kb + FLASH_NS - 1 < nkv) {
+      constexpr int NX = (SL + FLASH_NS - 1) % FLASH_NS;
+      const int r0 = 64 * (kb + FLASH_NS - 1);
+      tile_dma(rs, ring[NX][0], r0, ld, C + h * 64, lane, wave);
+      tile_dma(rs, ring[NX][1], r0, ld, 2 * C + h * 64, lane, wave);
+    }
+    const bf16_t* tK = ring[SL][0];
+    const bf16_t* tV = ring[SL][1];
+    const int kv0 = kb * 64;
+    if (kv0 > qw + 31) return;  // every key of the block is after this wave's queries
+    f32x16_t s[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[t] = MFMA32(frag_hd(tK, 32 * t, ks, lane), fq[ks], s[t]);
+    if (kv0 + 63 > qw || kv0 + 64 > Tn) {
+      // keys kv0 + 32t + ACC_ROW(r) past the lane's query or the sequence end
+      const int lim = min(my_q, Tn - 1) - kv0 - 4 * (lane >> 5);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) s[t] = MFMA32(frag_row(sK[cur], 32 * t, ks, lane), fq[ks], s[t]);
-      const bool diag = kv0 + 63 > qw || kv0 + 64 > Tn;
-      float mb = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          s[t][r] = (32 * t + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[t][r];
+    }
+    float mb = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[t][r] * sc;
-          if (diag) {
-            const int kv = kv0 + 32 * t + ACC_ROW(r, lane);
-            if (kv > my_q || kv >= Tn) v = -INFINITY;
-          }
-          s[t][r] = v;
-          mb = fmaxf(mb, v);
-        }
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, fmaxf(s[0][r], s[1][r]));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64)) * sc;
+    // The reference point m of the exponentials moves only when some
+    // query's block maximum exceeds it by more than 8 (log2 units): the
+    // probabilities then stay below 2^8 and the accumulator is rescaled
+    // rarely.  Every lane that moves takes its exact new maximum.
+    if (__builtin_amdgcn_ballot_w64(mb > m + 8.0f)) {
       const float mn = fmaxf(m, mb);
-      const float alpha = exp2f(m - mn);
-      float ls = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[t][r] - mn);
-          s[t][r] = p;
-          ls += p;
-        }
-      l = l * alpha + ls;
-      m = mn;
+      const float alpha = fexp2(m - mn);
+      l *= alpha;
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[ht][r] *= alpha;
-      // O^T += V^T P^T over the 64 keys (4 steps of 16)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const bf16x8_t pb = pack_acc(s[t], ss, 1.0f);
-#pragma unroll
-          for (int ht = 0; ht < 2; ++ht)
-            o[ht] = MFMA32(frag_tr(sVt[cur], 32 * ht + (lane & 31), 2 * t + ss, lane), pb, o[ht]);
-        }
+      m = mn;
     }
-    __syncthreads();
+    const float nm = -m;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w[j] = pack2bf(fexp2(fmaf(s[t][8 * ss + 2 * j], sc, nm)),
+                         fexp2(fmaf(s[t][8 * ss + 2 * j + 1], sc, nm)));
+          // the row sum adds the probabilities as rounded for the product
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[j]), ones, l, false);
+        }
+        const uint4 wv = make_uint4(w[0], w[1], w[2], w[3]);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, wv);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          o[ht] = MFMA32(frag_rows(tV, 32 * ht, 2 * t + ss, lane), pb, o[ht]);
+      }
+  };
+  for (int kb = 0; kb < nkv; kb += FLASH_NS) {
+    step(kb, Slot<0>());
+    if (kb + 1 < nkv) step(kb + 1, Slot<1>());
+    if (kb + 2 < nkv) step(kb + 2, Slot<2>());
   }
   const float lt = l + __shfl_xor(l, 32, 64);
   const float inv = 1.0f / lt;
@@ -326,101 +388,121 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16_t* __restrict
 }
 
 // ---------------------------------------------------------------- backward: dK, dV
-// grid: (T/128 key blocks) x (B*H); 4 waves x 32 key rows; query blocks of 64.
-__global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(
-    const bf16_t* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dg,
-    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dqkv, int B, int Tn, int H, int C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sQt[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sdO[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sdOt[2][64 * 64];
-  __shared__ float sL[2][64], sD[2][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// grid: (T/128 key blocks) x (B*H); 4 waves x 32 keys; query blocks of 64 from
+// the diagonal on.  S = Q K^T and dP = dO V^T put one key per lane; P^T and
+// dS^T are then the A operands of dV += P^T dO and dK += dS^T Q, whose B
+// operands are transposing reads of the dO and Q tiles.  Dg holds
+// rowsum(dO * O) at [0, B*H*T) and the row logsumexp times log2(e) at
+// [B*H*T, 2*B*H*T).
+__global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
+    const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ dqkv, int B, int Tn, int H, int C) {
+  // per stage: Q tile, dO tile, 4 small slots (wave 0: scaled logsumexp, wave 1: D)
+  __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2 * TILE_ELEMS + 4 * 512];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int bh = blockIdx.x % (B * H), b = bh / H, h = bh % H;
-  const int kb = blockIdx.x / (B * H);
-  const int k0 = kb * 128, kw = k0 + 32 * wave;
-  const int64_t ld = 3 * (int64_t)C;
+  const int kblk = blockIdx.x / (B * H);
+  const int k0 = kblk * 128, kw = k0 + 32 * wave;
+  const int ld = 3 * C;
+  const int64_t bht = (int64_t)B * H * Tn;
   const bf16_t* base = qkv + (int64_t)b * Tn * ld;
-  const bf16_t* Qg = base + h * 64;
-  const bf16_t* dOg = dout + (int64_t)b * Tn * C + h * 64;
-  const float* Lg = lse + (int64_t)bh * Tn;
-  const float* DDg = Dg + (int64_t)bh * Tn;
+  const __amdgpu_buffer_rsrc_t rq = rsrc_of(base, (uint32_t)((int64_t)Tn * ld * 2));
+  const __amdgpu_buffer_rsrc_t rdo = rsrc_of(dout + (int64_t)b * Tn * C, (uint32_t)((int64_t)Tn * C * 2));
+  const float* small_src = Dg + (wave == 0 ? bht : 0) + (int64_t)bh * Tn;
+  const __amdgpu_buffer_rsrc_t rsm = rsrc_of(small_src, (uint32_t)(Tn * 4));
 
-  // K and V rows of this wave as B operands (K^T, V^T): lane holds row kw+lane%32
-  bf16x8_t fk[4], fv[4];
-  {
-    const int kv = kw + (lane & 31);
+  const int my_kv = kw + (lane & 31);
+  bf16x8_t fk[4], fv[4];  // K^T, V^T operands: lane holds row my_kv
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
-      if (kv < Tn) {
-        a = *(const uint4*)(base + (int64_t)kv * ld + C + h * 64 + 16 * ks + 8 * (lane >> 5));
-        c = *(const uint4*)(base + (int64_t)kv * ld + 2 * C + h * 64 + 16 * ks + 8 * (lane >> 5));
-      }
-      fk[ks] = *(bf16x8_t*)&a;
-      fv[ks] = *(bf16x8_t*)&c;
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+    if (my_kv < Tn) {
+      a = *(const uint4*)(base + (int64_t)my_kv * ld + C + h * 64 + 16 * ks + 8 * (lane >> 5));
+      c = *(const uint4*)(base + (int64_t)my_kv * ld + 2 * C + h * 64 + 16 * ks + 8 * (lane >> 5));
     }
+    fk[ks] = *(bf16x8_t*)&a;
+    fv[ks] = *(bf16x8_t*)&c;
   }
   const float sc = LOG2E * 0.125f;
-  const int my_kv = kw + (lane & 31);
   f32x16_t dv[2] = {zero16(), zero16()}, dk[2] = {zero16(), zero16()};
-
-  const int qstart = (k0 / 64) * 64;
+  const int qstart = k0;
   const int nq = (Tn - qstart + 63) / 64;
-  auto stage = [&](int buf, int qs) {
-    stage_row(sQ[buf], Qg, ld, qs, Tn, tid);
-    stage_tr(sQt[buf], Qg, ld, qs, Tn, tid);
-    stage_row(sdO[buf], dOg, C, qs, Tn, tid);
-    stage_tr(sdOt[buf], dOg, C, qs, Tn, tid);
-    if (tid < 64) {
-      const int q = qs + tid;
-      sL[buf][tid] = q < Tn ? Lg[q] * LOG2E : 0.f;
-      sD[buf][tid] = q < Tn ? DDg[q] : 0.f;
-    }
+  // 5 loads per wave per stage: 2 + 2 tile loads and one small load
+  auto stage = [&](bf16_t* dst, int qs) {
+    tile_dma(rq, dst, qs, ld, h * 64, lane, wave);
+    tile_dma(rdo, dst + TILE_ELEMS, qs, C, h * 64, lane, wave);
+    // wave 0 fetches the 64 scaled logsumexp values of the block, wave 1
+    // the 64 D values (rows past the end read as zero); waves 2 and 3 issue
+    // a load that reads nothing so that every wave counts the same loads
+    const uint32_t off = wave < 2 ? (uint32_t)((qs + lane) * 4) : 0xFFFFFF00u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsm, AS3(dst + 2 * TILE_ELEMS + wave * 512), 4, off,
+                                             0, 0, 0);
   };
-  if (nq > 0) stage(0, qstart);
-  __syncthreads();
-  for (int qi = 0; qi < nq; ++qi) {
-    const int cur = qi & 1, qs = qstart + 64 * qi;
-    if (qi + 1 < nq) stage(cur ^ 1, qs + 64);
-    if (qs + 63 >= kw && kw < Tn) {  // some query of this block sees these keys
-      // S = Q K^T and dP = dO V^T for 2 query tiles of 32: rows q, columns kv
-      f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+  for (int st = 0; st < FLASH_NS - 1; ++st)
+    if (st < nq) stage(ring[st], qstart + 64 * st);
+  auto step = [&](int qi, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    if (qi + FLASH_NS - 2 < nq) vm_wait_barrier<(FLASH_NS - 2) * 5>();
+    else vm_wait_barrier<0>();
+    if (qi + FLASH_NS - 1 < nq)
+      stage(ring[(SL + FLASH_NS - 1) % FLASH_NS], qstart + 64 * (qi + FLASH_NS - 1));
+    const bf16_t* tQ = ring[SL];
+    const bf16_t* tdO = tQ + TILE_ELEMS;
+    const float* sL = (const float*)(tQ + 2 * TILE_ELEMS);
+    const float* sD = (const float*)(tQ + 2 * TILE_ELEMS + 512);
+    const int qs = qstart + 64 * qi;
+    if (qs + 63 < kw || kw >= Tn) return;  // no query of this block sees these keys
+    // query qs + 32t + ACC_ROW(r) is kept when it lies in [my_kv, Tn);
+    // c = 32t + 8(r/4) + r%4 is kept when (unsigned)(c - lo) < span
+    const bool diag = qs < kw + 31 || qs + 64 > Tn;
+    const int lo = my_kv - qs - 4 * (lane >> 5);
+    const unsigned span = (unsigned)(Tn - my_kv);
+    // the two 32-query halves of the block one after the other keeps the
+    // live accumulators (S, dP, dK, dV) within 256 registers
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          s[t] = MFMA32(frag_row(sQ[cur], 32 * t, ks, lane), fk[ks], s[t]);
-          dp[t] = MFMA32(frag_row(sdO[cur], 32 * t, ks, lane), fv[ks], dp[t]);
-        }
-      const bool diag = qs < kw + 31 || qs + 64 > Tn;
+    for (int t = 0; t < 2; ++t) {
+      f32x16_t sa = zero16(), dpa = zero16();
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int ks = 0; ks < 4; ++ks) {
+        sa = MFMA32(frag_hd(tQ, 32 * t, ks, lane), fk[ks], sa);
+        dpa = MFMA32(frag_hd(tdO, 32 * t, ks, lane), fv[ks], dpa);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = 32 * t + ACC_ROW(r, lane);
+        sa[r] = fexp2(fmaf(sa[r], sc, -sL[qq]));
+      }
+      if (diag) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qq = 32 * t + ACC_ROW(r, lane);
-          float p = exp2f(s[t][r] * sc - sL[cur][qq]);
-          if (diag && (qs + qq < my_kv || qs + qq >= Tn)) p = 0.f;
-          s[t][r] = p;
-          dp[t][r] = p * (dp[t][r] - sD[cur][qq]);
+          const int c = 32 * t + 8 * (r >> 2) + (r & 3);
+          sa[r] = (unsigned)(c - lo) < span ? sa[r] : 0.f;
         }
-      // dV += P^T dO, dK += dS^T Q (k index = query, 4 steps of 16)
+      }
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int r = 0; r < 16; ++r) {
+        const int qq = 32 * t + ACC_ROW(r, lane);
+        dpa[r] = sa[r] * (dpa[r] - sD[qq]);
+      }
 #pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const bf16x8_t pa = pack_acc(s[t], ss, 1.0f);
-          const bf16x8_t da = pack_acc(dp[t], ss, 1.0f);
+      for (int ss = 0; ss < 2; ++ss) {
+        const bf16x8_t pa = pack_acc(sa, ss);
+        const bf16x8_t da = pack_acc(dpa, ss);
 #pragma unroll
-          for (int ht = 0; ht < 2; ++ht) {
-            dv[ht] = MFMA32(pa, frag_tr(sdOt[cur], 32 * ht + (lane & 31), 2 * t + ss, lane), dv[ht]);
-            dk[ht] = MFMA32(da, frag_tr(sQt[cur], 32 * ht + (lane & 31), 2 * t + ss, lane), dk[ht]);
-          }
+        for (int ht = 0; ht < 2; ++ht) {
+          dv[ht] = MFMA32(pa, frag_rows(tdO, 32 * ht, 2 * t + ss, lane), dv[ht]);
+          dk[ht] = MFMA32(da, frag_rows(tQ, 32 * ht, 2 * t + ss, lane), dk[ht]);
         }
+      }
     }
-    __syncthreads();
+  };
+  for (int qi = 0; qi < nq; qi += FLASH_NS) {
+    step(qi, Slot<0>());
+    if (qi + 1 < nq) step(qi + 1, Slot<1>());
+    if (qi + 2 < nq) step(qi + 2, Slot<2>());
   }
-  // dk/dv tiles: rows = key (ACC_ROW), columns = head dim lane%32
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
@@ -435,87 +517,99 @@ __global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------- backward: dQ
-// grid: (T/128 query blocks, heaviest first) x (B*H); 4 waves x 32 query rows.
-__global__ __launch_bounds__(256) void flash_bwd_dq_kernel(
-    const bf16_t* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dg,
-    const bf16_t* __restrict__ dout, bf16_t* __restrict__ dqkv, int B, int Tn, int H, int C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sKt[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// grid: (T/128 query blocks, heaviest first) x (B*H); 4 waves x 32 queries.
+// S^T = K Q^T and dP^T = V dO^T put one query per lane; dS^T is the B
+// operand of dQ^T += K^T dS^T, whose A operand is a transposing read of K.
+__global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
+    const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
+    bf16_t* __restrict__ dqkv, int B, int Tn, int H, int C) {
+  __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2][TILE_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int nqb = (Tn + 127) / 128;
   const int qb = nqb - 1 - (int)(blockIdx.x / (B * H));
   const int bh = blockIdx.x % (B * H), b = bh / H, h = bh % H;
   const int q0 = qb * 128, qw = q0 + 32 * wave;
-  const int64_t ld = 3 * (int64_t)C;
+  const int ld = 3 * C;
+  const int64_t bht = (int64_t)B * H * Tn;
   const bf16_t* base = qkv + (int64_t)b * Tn * ld;
-  const bf16_t* Kg = base + C + h * 64;
-  const bf16_t* Vg = base + 2 * C + h * 64;
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(base, (uint32_t)((int64_t)Tn * ld * 2));
   const int my_q = qw + (lane & 31);
 
   bf16x8_t fq[4], fdo[4];
-  {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
-      if (my_q < Tn) {
-        a = *(const uint4*)(base + (int64_t)my_q * ld + h * 64 + 16 * ks + 8 * (lane >> 5));
-        c = *(const uint4*)(dout + ((int64_t)b * Tn + my_q) * C + h * 64 + 16 * ks + 8 * (lane >> 5));
-      }
-      fq[ks] = *(bf16x8_t*)&a;
-      fdo[ks] = *(bf16x8_t*)&c;
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+    if (my_q < Tn) {
+      a = *(const uint4*)(base + (int64_t)my_q * ld + h * 64 + 16 * ks + 8 * (lane >> 5));
+      c = *(const uint4*)(dout + ((int64_t)b * Tn + my_q) * C + h * 64 + 16 * ks + 8 * (lane >> 5));
     }
+    fq[ks] = *(bf16x8_t*)&a;
+    fdo[ks] = *(bf16x8_t*)&c;
   }
   const float sc = LOG2E * 0.125f;
-  const float L2 = my_q < Tn ? lse[(int64_t)bh * Tn + my_q] * LOG2E : 0.f;
+  const float nL2 = my_q < Tn ? -Dg[bht + (int64_t)bh * Tn + my_q] : 0.f;
   const float Dq = my_q < Tn ? Dg[(int64_t)bh * Tn + my_q] : 0.f;
   f32x16_t dq[2] = {zero16(), zero16()};
-
-  const int kv_end = min(Tn, q0 + 128);
-  const int nkv = (kv_end + 63) / 64;
-  stage_row(sK[0], Kg, ld, 0, Tn, tid);
-  stage_tr(sKt[0], Kg, ld, 0, Tn, tid);
-  stage_row(sV[0], Vg, ld, 0, Tn, tid);
-  __syncthreads();
-  for (int kb = 0; kb < nkv; ++kb) {
-    const int cur = kb & 1, kv0 = kb * 64;
-    if (kb + 1 < nkv) {
-      stage_row(sK[cur ^ 1], Kg, ld, kv0 + 64, Tn, tid);
-      stage_tr(sKt[cur ^ 1], Kg, ld, kv0 + 64, Tn, tid);
-      stage_row(sV[cur ^ 1], Vg, ld, kv0 + 64, Tn, tid);
+  const int nkv = (min(Tn, q0 + 128) + 63) / 64;
+#pragma unroll
+  for (int st = 0; st < FLASH_NS - 1; ++st)
+    if (st < nkv) {
+      tile_dma(rs, ring[st][0], 64 * st, ld, C + h * 64, lane, wave);
+      tile_dma(rs, ring[st][1], 64 * st, ld, 2 * C + h * 64, lane, wave);
     }
-    if (kv0 <= qw + 31) {
-      // S^T = K Q^T, dP^T = V dO^T: rows kv, columns q (= this lane's query)
-      f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          s[t] = MFMA32(frag_row(sK[cur], 32 * t, ks, lane), fq[ks], s[t]);
-          dp[t] = MFMA32(frag_row(sV[cur], 32 * t, ks, lane), fdo[ks], dp[t]);
-        }
-      const bool diag = kv0 + 63 > qw || kv0 + 64 > Tn;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kv0 + 32 * t + ACC_ROW(r, lane);
-          float p = exp2f(s[t][r] * sc - L2);
-          if (diag && (kv > my_q || kv >= Tn)) p = 0.f;
-          dp[t][r] = p * (dp[t][r] - Dq);
-        }
-      // dQ^T += K^T dS^T (k index = key)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const bf16x8_t db = pack_acc(dp[t], ss, 1.0f);
-#pragma unroll
-          for (int ht = 0; ht < 2; ++ht)
-            dq[ht] = MFMA32(frag_tr(sKt[cur], 32 * ht + (lane & 31), 2 * t + ss, lane), db, dq[ht]);
-        }
+  auto step = [&](int kb, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    if (kb + FLASH_NS - 2 < nkv) vm_wait_barrier<(FLASH_NS - 2) * 4>();
+    else vm_wait_barrier<0>();
+    if (kb + FLASH_NS - 1 < nkv) {
+      constexpr int NX = (SL + FLASH_NS - 1) % FLASH_NS;
+      const int r0 = 64 * (kb + FLASH_NS - 1);
+      tile_dma(rs, ring[NX][0], r0, ld, C + h * 64, lane, wave);
+      tile_dma(rs, ring[NX][1], r0, ld, 2 * C + h * 64, lane, wave);
     }
-    __syncthreads();
+    const bf16_t* tK = ring[SL][0];
+    const bf16_t* tV = ring[SL][1];
+    const int kv0 = kb * 64;
+    if (kv0 > qw + 31) return;
+    f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = MFMA32(frag_hd(tK, 32 * t, ks, lane), fq[ks], s[t]);
+        dp[t] = MFMA32(frag_hd(tV, 32 * t, ks, lane), fdo[ks], dp[t]);
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = fexp2(fmaf(s[t][r], sc, nL2));
+    if (kv0 + 63 > qw || kv0 + 64 > Tn) {
+      const int lim = min(my_q, Tn - 1) - kv0 - 4 * (lane >> 5);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[t][r] = (32 * t + 8 * (r >> 2) + (r & 3)) > lim ? 0.f : s[t][r];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[t][r] = s[t][r] * (dp[t][r] - Dq);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const bf16x8_t db = pack_acc(dp[t], ss);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          dq[ht] = MFMA32(frag_rows(tK, 32 * ht, 2 * t + ss, lane), db, dq[ht]);
+      }
+  };
+  for (int kb = 0; kb < nkv; kb += FLASH_NS) {
+    step(kb, Slot<0>());
+    if (kb + 1 < nkv) step(kb + 1, Slot<1>());
+    if (kb + 2 < nkv) step(kb + 2, Slot<2>());
   }
   if (my_q < Tn) {
     bf16_t* dQ = dqkv + ((int64_t)b * Tn + my_q) * ld + h * 64;
@@ -551,7 +645,8 @@ int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int 
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// D: fp32 scratch of B*H*T elements.
+// D: fp32 scratch of 2*B*H*T elements (rowsum(dout * out), then the row
+// logsumexp times log2(e) for the bf16 head-width-64 kernels).
 int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
                          hipStream_t s) {
@@ -559,14 +654,21 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
   if (hs * H != C || hs > 128) return -5;
   const int64_t rows = (int64_t)B * H * Tn;
   if (bf16) {
-    hipLaunchKernelGGL(attn_bwd_dot<bf16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
-                       (const bf16_t*)out, (const bf16_t*)dout, D, B, Tn, H, C);
-    if (hs == 64) {
+    const bool flash = hs == 64;
+    if (flash) {
+      const int64_t nchunk = (int64_t)B * Tn * C / 8;
+      hipLaunchKernelGGL(attn_bwd_dot64_kernel, dim3((unsigned)cdiv(nchunk, 256)), dim3(256), 0, s,
+                         (const bf16_t*)out, (const bf16_t*)dout, lse, D, D + rows, Tn, H, nchunk);
+    } else {
+      hipLaunchKernelGGL(attn_bwd_dot<bf16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
+                         (const bf16_t*)out, (const bf16_t*)dout, lse, D, nullptr, B, Tn, H, C);
+    }
+    if (flash) {
       const int nb = (Tn + 127) / 128;
       hipLaunchKernelGGL(flash_bwd_dkdv_kernel, dim3(nb * B * H), dim3(256), 0, s,
-                         (const bf16_t*)qkv, lse, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
+                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
       hipLaunchKernelGGL(flash_bwd_dq_kernel, dim3(nb * B * H), dim3(256), 0, s,
-                         (const bf16_t*)qkv, lse, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
+                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
     } else {
       hipLaunchKernelGGL(attn_bwd_dq_generic<bf16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
                          (const bf16_t*)qkv, lse, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
@@ -575,7 +677,7 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
     }
   } else {
     hipLaunchKernelGGL(attn_bwd_dot<float>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
-                       (const float*)out, (const float*)dout, D, B, Tn, H, C);
+                       (const float*)out, (const float*)dout, lse, D, nullptr, B, Tn, H, C);
     hipLaunchKernelGGL(attn_bwd_dq_generic<float>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
                        (const float*)qkv, lse, D, (const float*)dout, (float*)dqkv, B, Tn, H, C);
     hipLaunchKernelGGL(attn_bwd_dkdv_generic<float>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,

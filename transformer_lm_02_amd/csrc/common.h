@@ -9,17 +9,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- bf16 <-> fp32
-// Round-to-nearest-even fp32 -> bf16; NaN stays NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN): the gfx950
+// conversion instruction v_cvt_pk_bf16_f32
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 // two floats -> packed pair (lo in bits 0..15)
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_convertvector((f32x2_cvt_t){lo, hi}, bf16x2_cvt_t));
 }
 
 // Activation storage: float (fp32 mode) or bf16_t (bf16 mode).

@@ -87,7 +87,8 @@ struct Stage {
     }
   }
   // MFMA 32x32x16 operand: lane holds (row rbase + lane%32, k 16ks + 8(lane/32) + 0..7)
-  __device__ __forceinline__ static bf16x8_t frag(const bf16_t* lds, int rbase, int ks, int lane) {
+  __device__ __forceinline__ static bf16x8_t frag(const bf16_t* __restrict__ lds, int rbase, int ks,
+                                                  int lane) {
     if constexpr (KC) {
       const int r = rbase + (lane & 31), c = 2 * ks + (lane >> 5);
       return *(const bf16x8_t*)(lds + r * BK + ((c ^ swz(r)) << 3));

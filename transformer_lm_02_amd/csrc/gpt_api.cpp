@@ -180,7 +180,7 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   w.dln = take(M * d * 4);
   w.dbig = take(M * 4 * d * es);
   w.dO = take(M * d * es);
-  w.Dbuf = take(M * H * 4);
+  w.Dbuf = take(2 * M * H * 4);
   w.ln_part = take((int64_t)layernorm_bwd_part_rows((int)M) * 3 * d * 4);
   w.cs_part = take((int64_t)colsum_part_rows((int)M) * 4 * d * 4);
   w.norm_part = take((int64_t)adamw_norm_blocks() * 8);

@@ -13,7 +13,7 @@
 #include "common.h"
 
 #define LN_EPS 1e-5f
-#define LN_MAXV 8  // float4 per lane: C <= 2048
+#define LN_MAXV_MAX 8  // float4 per lane: C <= 2048
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float4 v);
@@ -24,7 +24,7 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
   *(uint2*)p = make_uint2(pack2bf(v.x, v.y), pack2bf(v.z, v.w));
 }
 
-template <typename T>
+template <typename T, int LN_MAXV>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x,
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ b, T* __restrict__ y,
@@ -76,9 +76,11 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 }
 
 // Rows are split into blocks of LN_BWD_ROWS; each block writes partial column
-// sums part[blk][3][C] (dw, db, residual-gradient column sum).
-#define LN_BWD_ROWS 64
-template <typename T>
+// sums part[blk][3][C] (dw, db, residual-gradient column sum).  Each wave
+// takes every 4th row of its block and loads its next row (dy, x and, when
+// accumulating, the old residual gradient) while it works on the current one.
+#define LN_BWD_ROWS 16
+template <typename T, int LN_MAXV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
     const float* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres,
@@ -93,27 +95,44 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
     ww[i] = j < nv ? ((const float4*)w)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const int64_t r0 = (int64_t)blockIdx.x * LN_BWD_ROWS;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 dc[LN_MAXV], xc[LN_MAXV];  // current row: dy, x
+  {
+    const int64_t row = r0 + wave;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int j = lane + 64 * i;
+      const bool ok = j < nv && row < M;
+      dc[i] = ok ? ((const float4*)(dy + row * C))[j] : z4;
+      xc[i] = ok ? ((const float4*)(x + row * C))[j] : z4;
+    }
+  }
   for (int rr = wave; rr < LN_BWD_ROWS; rr += 4) {
     const int64_t row = r0 + rr;
     if (row >= M) break;
+    float4 pc[LN_MAXV], dn[LN_MAXV], xn[LN_MAXV];
+    const int64_t nrow = row + 4;
+    const bool more = rr + 4 < LN_BWD_ROWS && nrow < M;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int j = lane + 64 * i;
+      pc[i] = j < nv && accumulate ? ((const float4*)(dres + row * C))[j] : z4;
+      dn[i] = j < nv && more ? ((const float4*)(dy + nrow * C))[j] : z4;
+      xn[i] = j < nv && more ? ((const float4*)(x + nrow * C))[j] : z4;
+    }
     const float mu = mean[row], rs = rstd[row];
-    const float4* dyr = (const float4*)(dy + row * C);
-    const float4* xr = (const float4*)(x + row * C);
     float4 xh[LN_MAXV], g[LN_MAXV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < LN_MAXV; ++i) {
-      const int j = lane + 64 * i;
-      if (j < nv) {
-        const float4 d = dyr[j], xv = xr[j];
-        xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
-        g[i] = make_float4(d.x * ww[i].x, d.y * ww[i].y, d.z * ww[i].z, d.w * ww[i].w);
-        s1 += g[i].x + g[i].y + g[i].z + g[i].w;
-        s2 += g[i].x * xh[i].x + g[i].y * xh[i].y + g[i].z * xh[i].z + g[i].w * xh[i].w;
-        pw[i].x += d.x * xh[i].x; pw[i].y += d.y * xh[i].y;
-        pw[i].z += d.z * xh[i].z; pw[i].w += d.w * xh[i].w;
-        pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
-      }
+      const float4 d = dc[i], xv = xc[i];
+      xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
+      g[i] = make_float4(d.x * ww[i].x, d.y * ww[i].y, d.z * ww[i].z, d.w * ww[i].w);
+      s1 += g[i].x + g[i].y + g[i].z + g[i].w;
+      s2 += g[i].x * xh[i].x + g[i].y * xh[i].y + g[i].z * xh[i].z + g[i].w * xh[i].w;
+      pw[i].x += d.x * xh[i].x; pw[i].y += d.y * xh[i].y;
+      pw[i].z += d.z * xh[i].z; pw[i].w += d.w * xh[i].w;
+      pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
     }
     const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
     float4* dr = (float4*)(dres + row * C);
@@ -123,23 +142,24 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
       const int j = lane + 64 * i;
       if (j < nv) {
         float4 o;
-        o.x = rs * (g[i].x - m1 - xh[i].x * m2);
-        o.y = rs * (g[i].y - m1 - xh[i].y * m2);
-        o.z = rs * (g[i].z - m1 - xh[i].z * m2);
-        o.w = rs * (g[i].w - m1 - xh[i].w * m2);
-        if (accumulate) {
-          const float4 p = dr[j];
-          o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
-        }
+        o.x = rs * (g[i].x - m1 - xh[i].x * m2) + pc[i].x;
+        o.y = rs * (g[i].y - m1 - xh[i].y * m2) + pc[i].y;
+        o.z = rs * (g[i].z - m1 - xh[i].z * m2) + pc[i].z;
+        o.w = rs * (g[i].w - m1 - xh[i].w * m2) + pc[i].w;
         dr[j] = o;
         store4<T>(da + 4 * j, o);
         pr[i].x += o.x; pr[i].y += o.y; pr[i].z += o.z; pr[i].w += o.w;
       }
     }
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      dc[i] = dn[i];
+      xc[i] = xn[i];
+    }
   }
   // reduce the 4 waves' partials through LDS (one wave at a time) and write
   // one partial row per block: part[blk][3][C]
-  __shared__ float red[3 * LN_MAXV * 256];
+  __shared__ float red[3 * LN_MAXV * 256];  // 3 x C floats
   for (int w = 0; w < 4; ++w) {
     if (wave == w) {
 #pragma unroll
@@ -167,42 +187,86 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
   for (int c = threadIdx.x; c < 3 * C; c += 256) out[c] = red[c];
 }
 
-// Column sums of a partial matrix part[nrow][ncol] into up to three outputs:
-// column j goes to out[j / seg][j % seg] = (beta ? old : 0) + sum over rows.
-// 64 columns per block; the 4 waves split the rows, then combine in LDS in a
-// fixed order.
+// Column sums of part [nrow][ncol] (ncol % 4 == 0, 16-byte aligned rows):
+// each block takes 32 columns; its 256 threads are 8 float4 columns x 32 row
+// groups, each with 4 independent loads in flight, then an LDS reduction.
+// Column c goes to out_k[c % seg] with k = c / seg (seg % 4 == 0); with beta
+// the sum is added to the output, else it replaces it.
 __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __restrict__ part,
                                                               int nrow, int ncol, int seg,
                                                               float* out0, float* out1,
                                                               float* out2, int beta) {
-  __shared__ float red[4][64];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
-  float s = 0.f;
-  if (c < ncol)
-    for (int r = rg; r < nrow; r += 4) s += part[(int64_t)r * ncol + c];
-  red[rg][threadIdx.x & 63] = s;
+  __shared__ float4 red[32][8];
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
+  const int c = blockIdx.x * 32 + 4 * tx;
+  float4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < ncol) {
+    int r = ty;
+    for (; r + 96 < nrow; r += 128) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = *(const float4*)(part + (int64_t)(r + 32 * u) * ncol + c);
+        acc[u].x += v.x; acc[u].y += v.y; acc[u].z += v.z; acc[u].w += v.w;
+      }
+    }
+    for (; r < nrow; r += 32) {
+      const float4 v = *(const float4*)(part + (int64_t)r * ncol + c);
+      acc[0].x += v.x; acc[0].y += v.y; acc[0].z += v.z; acc[0].w += v.w;
+    }
+  }
+  float4 t;
+  t.x = (acc[0].x + acc[1].x) + (acc[2].x + acc[3].x);
+  t.y = (acc[0].y + acc[1].y) + (acc[2].y + acc[3].y);
+  t.z = (acc[0].z + acc[1].z) + (acc[2].z + acc[3].z);
+  t.w = (acc[0].w + acc[1].w) + (acc[2].w + acc[3].w);
+  red[ty][tx] = t;
   __syncthreads();
-  if (rg == 0 && c < ncol) {
-    const float t = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
-    const int k = c / seg, i = c % seg;
-    float* o = k == 0 ? out0 : (k == 1 ? out1 : out2);
-    if (o) o[i] = (beta ? o[i] : 0.f) + t;
+  if (threadIdx.x < 32) {
+    // thread j sums column blockIdx.x * 32 + j over the 32 row groups
+    const int j = threadIdx.x, cc = blockIdx.x * 32 + j;
+    const float* rf = (const float*)red;
+    float v = 0.f;
+#pragma unroll 8
+    for (int g = 0; g < 32; ++g) v += rf[g * 32 + j];
+    if (cc < ncol) {
+      const int k = cc / seg, i = cc % seg;
+      float* o = k == 0 ? out0 : (k == 1 ? out1 : out2);
+      if (o) o[i] = (beta ? o[i] : 0.f) + v;
+    }
   }
 }
 
+// per-lane float4 count: C / 4 / 64 rounded up, so registers track the width
+#define LN_DISPATCH(MACRO) \
+  switch ((C / 4 + 63) / 64) {  \
+    case 1: MACRO(1); break;    \
+    case 2: MACRO(2); break;    \
+    case 3: MACRO(3); break;    \
+    case 4: MACRO(4); break;    \
+    case 5: MACRO(5); break;    \
+    case 6: MACRO(6); break;    \
+    case 7: MACRO(7); break;    \
+    default: MACRO(8); break;   \
+  }
+
 int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s) {
-  if (C % 4 || C > LN_MAXV * 256) return -5;
-  if (bf16)
-    hipLaunchKernelGGL(ln_fwd_kernel<bf16_t>, dim3(cdiv(M, 4)), dim3(256), 0, s, x, w, b,
-                       (bf16_t*)y, mean, rstd, M, C);
-  else
-    hipLaunchKernelGGL(ln_fwd_kernel<float>, dim3(cdiv(M, 4)), dim3(256), 0, s, x, w, b,
+  if (C % 4 || C > LN_MAXV_MAX * 256) return -5;
+#define LNF(V)                                                                                  \
+  if (bf16)                                                                                      \
+    hipLaunchKernelGGL((ln_fwd_kernel<bf16_t, V>), dim3(cdiv(M, 4)), dim3(256), 0, s, x, w, b,  \
+                       (bf16_t*)y, mean, rstd, M, C);                                            \
+  else                                                                                           \
+    hipLaunchKernelGGL((ln_fwd_kernel<float, V>), dim3(cdiv(M, 4)), dim3(256), 0, s, x, w, b,   \
                        (float*)y, mean, rstd, M, C);
+  LN_DISPATCH(LNF)
+#undef LNF
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// partial rows written by one backward call (4 per block)
+// partial rows written by one backward call (one per block)
 int layernorm_bwd_part_rows(int M) { return (int)cdiv(M, LN_BWD_ROWS); }
 
 // dres = (accumulate ? dres : 0) + LN'(dy); dres_act = copy; then
@@ -211,22 +275,26 @@ int layernorm_bwd_launch(bool bf16, const float* dy, const float* x, const float
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
                          int beta, int M, int C, hipStream_t s) {
-  if (C % 4 || C > LN_MAXV * 256) return -5;
+  if (C % 4 || C > LN_MAXV_MAX * 256) return -5;
   const int nb = (int)cdiv(M, LN_BWD_ROWS);
-  if (bf16)
-    hipLaunchKernelGGL(ln_bwd_kernel<bf16_t>, dim3(nb), dim3(256), 0, s, dy, x, mean, rstd, w,
-                       dres, (bf16_t*)dres_act, accumulate, part, M, C);
-  else
-    hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nb), dim3(256), 0, s, dy, x, mean, rstd, w, dres,
-                       (float*)dres_act, accumulate, part, M, C);
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(3 * C, 64)), dim3(256), 0, s, part, nb,
+#define LNB(V)                                                                                   \
+  if (bf16)                                                                                       \
+    hipLaunchKernelGGL((ln_bwd_kernel<bf16_t, V>), dim3(nb), dim3(256), 0, s, dy, x, mean, rstd, \
+                       w, dres, (bf16_t*)dres_act, accumulate, part, M, C);                      \
+  else                                                                                            \
+    hipLaunchKernelGGL((ln_bwd_kernel<float, V>), dim3(nb), dim3(256), 0, s, dy, x, mean, rstd,  \
+                       w, dres, (float*)dres_act, accumulate, part, M, C);
+  LN_DISPATCH(LNB)
+#undef LNB
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(3 * C, 32)), dim3(256), 0, s, part, nb,
                      3 * C, C, dw, db, bias_grad, beta);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
                            hipStream_t s) {
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(ncol, 64)), dim3(256), 0, s, part, nrow,
+  if (ncol % 4) return -5;
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(ncol, 32)), dim3(256), 0, s, part, nrow,
                      ncol, ncol, out, nullptr, nullptr, beta);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -73,8 +73,10 @@ __global__ void count_valid_kernel(const int32_t* __restrict__ tgt, int N, int* 
 //   dz_v = scale * (exp(z_v - lse) - [v == y]) for v < V, 0 for V <= v < ldv,
 // written over the logits ("Let's reproduce GPT-2 (124M)", chapter "Cross
 // Entropy Loss"; scale = loss_scale / n_valid, zero for an ignored row).
-#define CE_THREADS 512
-#define CE_MAXU 13  // uint4 (8 bf16) per thread: rows up to 53248 columns
+#define CE_THREADS 1024    // fp32 kernel
+#define CE_BF_THREADS 512  // bf16 kernel: two rows in flight per compute unit
+#define CE_BF_MAXU 13      // uint4 (8 bf16) per thread: rows up to 53248 columns
+template <int NT>
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
   v = is_max ? wave_max(v) : wave_sum(v);
   const int w = threadIdx.x >> 6;
@@ -82,68 +84,102 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) 
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   float r = red[0];
-  for (int i = 1; i < CE_THREADS / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  for (int i = 1; i < NT / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
   return r;
 }
 
-__global__ __launch_bounds__(CE_THREADS) void ce_bf16_kernel(
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// One block per row; the row stays in registers.  Each thread takes the max
+// m_t of its own columns and replaces every cached logit z by
+// p = exp(z - m_t) (bf16), adding the fp32 values into s_t.  The block then
+// forms lse = M + log(sum_t s_t exp(m_t - M)) with M the row max, and the
+// gradient is p * exp(m_t - lse) * scale; the thread holding the target
+// column rewrites that one element as scale * (exp(z_y - lse) - 1).
+// Columns >= V (padding) are cached as -inf, so every pass is branch-free.
+__global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_bf16_kernel(
     bf16_t* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
     const int* __restrict__ n_valid, float loss_scale, int V, int ldv) {
-  __shared__ float red[CE_THREADS / 64];
+  __shared__ float red[CE_BF_THREADS / 64];
   const int64_t row = blockIdx.x;
   bf16_t* z = logits + row * ldv;
   const int nvec = ldv >> 3;
-  uint4 cache[CE_MAXU];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < CE_MAXU; ++i) {
-    const int vi = threadIdx.x + CE_THREADS * i;
-    cache[i] = vi < nvec ? ((const uint4*)z)[vi] : make_uint4(0, 0, 0, 0);
-    const uint32_t* w = (const uint32_t*)&cache[i];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = 8 * vi + e;
-      const float f = bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
-      if (col < V) mx = fmaxf(mx, f);
-    }
-  }
-  mx = block_reduce(mx, true, red);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < CE_MAXU; ++i) {
-    const int vi = threadIdx.x + CE_THREADS * i;
-    const uint32_t* w = (const uint32_t*)&cache[i];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = 8 * vi + e;
-      const float f = bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
-      if (col < V) s += __expf(f - mx);
-    }
-  }
-  s = block_reduce(s, false, red);
-  const float lse = mx + __logf(s);
   const int y = tgt[row];
+  const bool has_y = y >= 0 && y < V;
+  const float zy = has_y ? bf2f(z[y]) : 0.f;
+  const uint32_t NEG2 = 0xff80ff80u;  // two bf16 -inf
+  // the row through one buffer descriptor (32-bit per-lane offsets, bounds
+  // checked against the row length), so no per-slot 64-bit addresses
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(z, (short)0, ldv * 2, 0x00020000);
+  const uint32_t voff = threadIdx.x * 16;
+  uint4 cache[CE_BF_MAXU];
+#pragma unroll
+  for (int i = 0; i < CE_BF_MAXU; ++i) {
+    const int vi = threadIdx.x + CE_BF_THREADS * i;
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + i * CE_BF_THREADS * 16, 0, 0);
+    cache[i] = 8 * vi < V ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(NEG2, NEG2, NEG2, NEG2);
+  }
+  // when V % 8 != 0 one vector straddles V: its owner masks the columns >= V
+  // (the slot index ip is the same for the whole block)
+  const int vp = V >> 3, ip = vp / CE_BF_THREADS;
+  if ((V & 7) && (int)threadIdx.x == vp % CE_BF_THREADS) {
+#pragma unroll
+    for (int k = 0; k < CE_BF_MAXU; ++k)
+      if (k == ip) {
+        uint32_t w[4] = {cache[k].x, cache[k].y, cache[k].z, cache[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = 8 * vp + 2 * j;
+          if (col >= V) w[j] = (w[j] & 0xffff0000u) | 0xff80u;
+          if (col + 1 >= V) w[j] = (w[j] & 0x0000ffffu) | 0xff800000u;
+        }
+        cache[k] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < CE_BF_MAXU; ++i) {
+    mt = fmaxf(mt, fmaxf(fmaxf(bf_lo(cache[i].x), bf_hi(cache[i].x)), fmaxf(bf_lo(cache[i].y), bf_hi(cache[i].y))));
+    mt = fmaxf(mt, fmaxf(fmaxf(bf_lo(cache[i].z), bf_hi(cache[i].z)), fmaxf(bf_lo(cache[i].w), bf_hi(cache[i].w))));
+  }
+  // a thread without columns keeps mt = -inf and s_t = 0
+  const float mref = mt == -INFINITY ? 0.f : mt;
+  float st = 0.f;
+#pragma unroll
+  for (int i = 0; i < CE_BF_MAXU; ++i) {
+    uint32_t w[4] = {cache[i].x, cache[i].y, cache[i].z, cache[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = __expf(bf_lo(w[j]) - mref), b = __expf(bf_hi(w[j]) - mref);
+      st += a + b;
+      w[j] = pack2bf(a, b);
+    }
+    cache[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  const float M = block_reduce<CE_BF_THREADS>(mt, true, red);
+  const float S = block_reduce<CE_BF_THREADS>(mt == -INFINITY ? 0.f : st * __expf(mt - M), false, red);
+  const float lse = M + __logf(S);
   const int nv = *n_valid;
   const float scale = (y >= 0 && nv > 0) ? loss_scale / (float)nv : 0.f;
-  float zy = 0.f;
-  if (y >= 0 && y < V) zy = bf2f(z[y]);
-  __syncthreads();  // every thread has read z[y] before it is overwritten
+  const float c = scale * __expf(mref - lse);
 #pragma unroll
-  for (int i = 0; i < CE_MAXU; ++i) {
-    const int vi = threadIdx.x + CE_THREADS * i;
-    if (vi >= nvec) break;
-    const uint32_t* w = (const uint32_t*)&cache[i];
-    float d[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = 8 * vi + e;
-      const float f = bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
-      d[e] = col < V ? scale * (__expf(f - lse) - (col == y ? 1.f : 0.f)) : 0.f;
-    }
-    ((uint4*)z)[vi] = make_uint4(pack2bf(d[0], d[1]), pack2bf(d[2], d[3]), pack2bf(d[4], d[5]),
-                                 pack2bf(d[6], d[7]));
+  for (int i = 0; i < CE_BF_MAXU; ++i) {
+    // slots past the row end lie outside the descriptor: the store is dropped
+    const uint32_t w[4] = {cache[i].x, cache[i].y, cache[i].z, cache[i].w};
+    const u32x4_t d = {pack2bf(bf_lo(w[0]) * c, bf_hi(w[0]) * c),
+                       pack2bf(bf_lo(w[1]) * c, bf_hi(w[1]) * c),
+                       pack2bf(bf_lo(w[2]) * c, bf_hi(w[2]) * c),
+                       pack2bf(bf_lo(w[3]) * c, bf_hi(w[3]) * c)};
+    __builtin_amdgcn_raw_buffer_store_b128(d, rs, voff + i * CE_BF_THREADS * 16, 0, 0);
   }
-  if (threadIdx.x == 0) row_loss[row] = (y >= 0 && y < V) ? lse - zy : 0.f;
+  // the same thread wrote the vector holding y just above, so this store
+  // lands after it
+  if (has_y && (int)threadIdx.x == (y >> 3) % CE_BF_THREADS)
+    z[y] = f2bf(scale * (__expf(zy - lse) - 1.0f));
+  if (threadIdx.x == 0) row_loss[row] = has_y ? lse - zy : 0.f;
 }
 
 // fp32 logits (fp32 mode): the same, reading the row from memory per pass.
@@ -155,10 +191,10 @@ __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
   float* z = logits + row * ldv;
   float mx = -INFINITY;
   for (int c = threadIdx.x; c < V; c += CE_THREADS) mx = fmaxf(mx, z[c]);
-  mx = block_reduce(mx, true, red);
+  mx = block_reduce<CE_THREADS>(mx, true, red);
   float s = 0.f;
   for (int c = threadIdx.x; c < V; c += CE_THREADS) s += expf(z[c] - mx);
-  s = block_reduce(s, false, red);
+  s = block_reduce<CE_THREADS>(s, false, red);
   const float lse = mx + logf(s);
   const int y = tgt[row];
   const int nv = *n_valid;
@@ -253,8 +289,8 @@ int cross_entropy_launch(bool bf16, void* logits, const int32_t* tgt, float* row
                          const int* n_valid, float loss_scale, int N, int V, int ldv,
                          hipStream_t s) {
   if (bf16) {
-    if (ldv % 8 || ldv > CE_MAXU * CE_THREADS * 8) return -5;
-    hipLaunchKernelGGL(ce_bf16_kernel, dim3(N), dim3(CE_THREADS), 0, s, (bf16_t*)logits, tgt,
+    if (ldv % 8 || ldv > CE_BF_MAXU * CE_BF_THREADS * 8) return -5;
+    hipLaunchKernelGGL(ce_bf16_kernel, dim3(N), dim3(CE_BF_THREADS), 0, s, (bf16_t*)logits, tgt,
                        row_loss, n_valid, loss_scale, V, ldv);
   } else {
     hipLaunchKernelGGL(ce_f32_kernel, dim3(N), dim3(CE_THREADS), 0, s, (float*)logits, tgt,
