@@ -40,39 +40,109 @@ def flops_per_token(dims, T):
     return 6 * N + 12 * dims["n_layer"] * dims["n_head"] * hs * T
 
 
-def time_dominant_kernel(torch, bd, B, T, dims, reps=20):
-    """LM-head forward product (16384 x 768 x 50304, bf16 -> bf16), timed
-    with events on the stream it is launched on."""
-    M, N, K = B * T, dims["padded_vocab"], dims["n_embd"]
+# The kernel with the largest share of the step: the bf16 GEMM with fp32
+# output and 256x192 tiles that forms the input gradients through the
+# transposed weight copies (fc and qkv per layer, and the tied LM head once).
+DOMINANT_KERNEL = "gemm2_kernel<256, 192, true, true, 1, 4, 32, 1>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_f32_dx.json")
+TRAFFIC_SOURCES = ["transformer_lm_02_amd/csrc/gemm2.hip", "transformer_lm_02_amd/csrc/gemm.h",
+                   "transformer_lm_02_amd/csrc/common.h"]
+
+
+def dominant_launches(B, T, dims):
+    """(M, N, K, count) of the launches one step makes of the dominant kernel."""
+    M, d, L = B * T, dims["n_embd"], dims["n_layer"]
+    vi = -(-dims["padded_vocab"] // 64) * 64
+    return [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, vi, 1)]
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    runs, or None when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_hash") != sources_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def dominant_operands(torch, B, T, dims):
     g = torch.Generator(device="cuda").manual_seed(7)
-    A = (torch.randn((M, K), device="cuda", generator=g) * 1.0).to(torch.bfloat16)
-    W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops = []
+    for (M, N, K, n) in dominant_launches(B, T, dims):
+        A = (torch.randn((M, K), device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
+        W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ops.append((A, W, C, M, N, K, n))
+    return ops
+
+
+def launch_dominant(bd, ops, stream_ptr, reps=1):
     import ctypes
+    for _ in range(reps):
+        for (A, W, C, M, N, K, n) in ops:
+            for _ in range(n):
+                bd.check(bd.lib.gpt_op_linear(1, ctypes.c_void_p(A.data_ptr()),
+                                              ctypes.c_void_p(W.data_ptr()), None,
+                                              ctypes.c_void_p(C.data_ptr()), 1, M, N, K,
+                                              stream_ptr), "gpt_op_linear")
+
+
+def time_dominant_kernel(torch, bd, B, T, dims, reps=5):
+    """The step's launches of the dominant kernel (same shapes, same entry
+    into the library), timed with events on the stream they run on."""
+    import ctypes
+    ops = dominant_operands(torch, B, T, dims)
     s = torch.cuda.current_stream()
     sp = ctypes.c_void_p(s.cuda_stream)
-    args = (1, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(W.data_ptr()), None,
-            ctypes.c_void_p(C.data_ptr()), 0, M, N, K, sp)
-    for _ in range(3):
-        bd.check(bd.lib.gpt_op_linear(*args), "gpt_op_linear")
+    launch_dominant(bd, ops, sp, 1)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
-    for _ in range(reps):
-        bd.lib.gpt_op_linear(*args)
+    launch_dominant(bd, ops, sp, reps)
     e1.record(s)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    flops = 2.0 * M * N * K
-    achieved = flops / (ms * 1e-3) / 1e12
-    return {"kernel": "gemm_mfma_kernel<256,128,k-contig,k-contig,bf16 out> (tied LM head forward)",
+    n_launch = sum(o[-1] for o in ops)
+    ms_total = e0.elapsed_time(e1) / reps
+    flops = sum(2.0 * M * N * K * n for (_, _, _, M, N, K, n) in ops)
+    achieved = flops / (ms_total * 1e-3) / 1e12
+    return {"kernel": DOMINANT_KERNEL + " (fp32-output input gradients: fc, qkv, LM head)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "ms_per_launch": round(ms, 4), "flops_per_launch": flops, "traffic": None}
+            "traffic": measured_traffic(), "launches_per_step": n_launch,
+            "ms_per_launch": round(ms_total / n_launch, 4),
+            "flops_per_launch": flops / n_launch}
+
+
+def probe(torch, bd, B, T, dims):
+    """For counter runs: one step's launches of the dominant kernel, then a
+    plain 1 GiB device copy (the calibration of FETCH_SIZE / WRITE_SIZE)."""
+    import ctypes
+    ops = dominant_operands(torch, B, T, dims)
+    s = torch.cuda.current_stream()
+    launch_dominant(bd, ops, ctypes.c_void_p(s.cuda_stream), 1)
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": DOMINANT_KERNEL, "launches": dominant_launches(B, T, dims),
+                      "copy_bytes": src.numel() * 4, "sources_hash": sources_hash()}), flush=True)
 
 
 def cpu_baseline(dims, seed=1338):
     """The float64 oracle (as it stands) on a bounded sample of the workload:
-    one full step (forward, backward, clip, AdamW) on one sequence of 1024
+    one full step (forward, backward, clip, AdamW) on two sequences of 1024
     tokens with the full model; tokens/s scales linearly in the batch."""
     from oracle import gpt_oracle as O
     from transformer_lm_02_amd import synth
@@ -83,13 +153,13 @@ def cpu_baseline(dims, seed=1338):
         cores = os.cpu_count()
     cfg = O.Config(**{k: dims[k] for k in synth.MODEL_KEYS})
     params = synth.init_params(dims, seed=1337).astype(np.float64)
-    idx, tgt = synth.tokens(dims, seed=seed, batch=1)
+    idx, tgt = synth.tokens(dims, seed=seed, batch=2)
     zeros = np.zeros_like(params)
     t0 = time.perf_counter()
     O.train_step(params, zeros, zeros, 1, [(idx, tgt)], cfg, lr=6e-4)
     dt = time.perf_counter() - t0
     return {"value": round(idx.size / dt, 2), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle", "sample": f"1 x 1024 tokens, full 124M model, float64 numpy step "
+            "kind": "oracle", "sample": f"2 x 1024 tokens, full 124M model, float64 numpy step "
                                         f"(fwd+bwd+clip+AdamW) in {dt:.1f} s"}
 
 
@@ -100,10 +170,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="only launch the dominant kernel and a calibration copy (counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the data-parallel exchange is not implemented)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library "
+              f"runs one GPU per process and has no data-parallel gradient exchange)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -112,6 +185,9 @@ def main():
 
     dims = synth.WORKLOADS[WORKLOAD]
     B, T = dims["batch"], dims["block_size"]
+    if args.probe:
+        probe(torch, bd, B, T, dims)
+        return
     print(f"[bench] building model {WORKLOAD} B={B} T={T}", file=sys.stderr, flush=True)
     params = synth.init_params(dims, seed=1337)
     model = bd.GPT(dims, bd.GPT_BF16, max_batch=B, init_params=params)
