@@ -14,8 +14,9 @@
  *   - Device memory is owned by the caller.  The library never allocates or
  *     frees device memory; the handle holds host metadata only.
  *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
- *     work on it; nothing synchronises, except gpt_read_flags.  Scalars that
- *     the step produces (loss, gradient norm) are written to device memory.
+ *     work on it, except gpt_init (which waits once for its set-up work) and
+ *     gpt_read_flags.  Scalars that the step produces (loss, gradient norm)
+ *     are written to device memory.
  *   - Return value: 0 on success, a negative GPT_E* code on failure.  On
  *     failure nothing has been enqueued.  gpt_strerror names the code.
  *   - All float arguments and buffers are IEEE fp32 unless stated.
@@ -76,8 +77,10 @@ typedef struct gpt_model gpt_model;
  * grads, adam_m and adam_v, and workspace_bytes of device memory (256-byte
  * aligned) for activations, the bf16 weight copy and scratch.
  * Returns GPT_EINVAL for an invalid config, GPT_EUNSUPPORTED for a valid one
- * these kernels do not cover (bf16 mode needs n_embd % 64 == 0 and head
- * width 64). */
+ * these kernels do not cover (n_embd a multiple of 4 up to 2048 and head width
+ * up to 128; bf16 mode also needs n_embd % 64 == 0 and the padded vocabulary,
+ * rounded up to 64, at most 53248).  Head width 64 takes the flash-attention
+ * kernels; other widths a slower per-query kernel. */
 int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace_bytes);
 
 /* Bind caller-owned device buffers and create a handle.
