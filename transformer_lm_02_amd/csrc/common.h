@@ -52,21 +52,26 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 // tanh-approximate GELU and its derivative ("Let's Reproduce GPT-2 in One
-// Read", the GELU check: GPT-2 uses the tanh form).  tanh(y) is evaluated as
-// 1 - 2/(exp(2y)+1), which is exact at both tails.
+// Read", the GELU check: GPT-2 uses the tanh form), c = sqrt(2/pi), a = 0.044715.
 #define GELU_C 0.7978845608028654f
 #define GELU_A 0.044715f
-__device__ __forceinline__ float tanh_fast(float y) {
-  float e = __expf(2.0f * y);
-  return 1.0f - 2.0f / (e + 1.0f);
+// Evaluated through the identity 0.5 (1 + tanh z) = 1 / (1 + e^(-2z)):
+// gelu(u) = u s with s = 1 / (1 + 2^(-2 z log2 e)), z = c (u + a u^3), and
+// gelu'(u) = s + 2 u s (1 - s) c (1 + 3 a u^2).  One hardware exponential and
+// one hardware reciprocal (v_exp_f32, v_rcp_f32) per element; for u far
+// below zero e^(-2z) overflows to inf and s to 0, the limits of both.
+#define GELU_K0 (-2.0f * GELU_C * 1.4426950408889634f)
+#define GELU_K1 (-2.0f * GELU_C * GELU_A * 1.4426950408889634f)
+__device__ __forceinline__ float gelu_sig(float u, float u2) {
+  const float e = __builtin_amdgcn_exp2f(u * fmaf(u2, GELU_K1, GELU_K0));
+  return __builtin_amdgcn_rcpf(1.0f + e);
 }
-__device__ __forceinline__ float gelu_f(float u) {
-  float t = tanh_fast(GELU_C * (u + GELU_A * u * u * u));
-  return 0.5f * u * (1.0f + t);
-}
+__device__ __forceinline__ float gelu_f(float u) { return u * gelu_sig(u, u * u); }
 __device__ __forceinline__ float gelu_grad_f(float u) {
-  float t = tanh_fast(GELU_C * (u + GELU_A * u * u * u));
-  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * GELU_C * (1.0f + 3.0f * GELU_A * u * u);
+  const float u2 = u * u;
+  const float s = gelu_sig(u, u2);
+  const float q = fmaf(u2, 6.0f * GELU_C * GELU_A, 2.0f * GELU_C);  // 2c (1 + 3 a u^2)
+  return fmaf(u * s * (1.0f - s), q, s);
 }
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -139,10 +139,44 @@ __device__ __forceinline__ void tile_coords2(int wg, int tiles_m, int tiles_n, i
   tn = r / gsize;
 }
 
+// Operand an epilogue reads besides the accumulators (8 consecutive outputs
+// of one row): the residual (fp32), the GELU pre-activation (bf16) or the
+// gradient being accumulated into (fp32).  Loaded for a whole slab of rows
+// before any of them is stored, so the loads overlap.
+struct Aux8 {
+  float4 a, b;
+};
+template <int EPI>
+__device__ __forceinline__ Aux8 aux8(const GemmEpiArgs& e, int splitk, int m, int n) {
+  const int64_t i = (int64_t)m * e.ldc + n;
+  Aux8 x;
+  x.a = x.b = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (EPI == EPI_RESID) {
+    const float4* s = (const float4*)((const float*)e.aux + i);
+    x.a = s[0];
+    x.b = s[1];
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    const uint4 u = *(const uint4*)((const bf16_t*)e.aux + i);
+    x.a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                      __uint_as_float(u.w));
+  } else if constexpr (EPI == EPI_ACCUM) {
+    if (!splitk && e.beta) {
+      const float4* s = (const float4*)((const float*)e.out + i);
+      x.a = s[0];
+      x.b = s[1];
+    }
+  }
+  return x;
+}
+template <int EPI>
+constexpr bool epi_reads_aux() {
+  return EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_ACCUM;
+}
+
 // 8 consecutive outputs of one row: epilogue and 16/32-byte stores
 template <int EPI>
 __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int splitk, int m, int n,
-                                     const float* v, const float* bias8) {
+                                     const float* v, const float* bias8, const Aux8& x) {
   const int64_t i = (int64_t)m * e.ldc + n;
   if constexpr (EPI == EPI_ACCUM) {
     if (splitk) {
@@ -151,23 +185,19 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
       o[1] = make_float4(v[4], v[5], v[6], v[7]);
     } else {
       float4* o = (float4*)((float*)e.out + i);
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (e.beta) { a = o[0]; b = o[1]; }
-      o[0] = make_float4(a.x + v[0], a.y + v[1], a.z + v[2], a.w + v[3]);
-      o[1] = make_float4(b.x + v[4], b.y + v[5], b.z + v[6], b.w + v[7]);
+      o[0] = make_float4(x.a.x + v[0], x.a.y + v[1], x.a.z + v[2], x.a.w + v[3]);
+      o[1] = make_float4(x.b.x + v[4], x.b.y + v[5], x.b.z + v[6], x.b.w + v[7]);
     }
   } else if constexpr (EPI == EPI_F32) {
     float4* o = (float4*)((float*)e.out + i);
     o[0] = make_float4(v[0] + bias8[0], v[1] + bias8[1], v[2] + bias8[2], v[3] + bias8[3]);
     o[1] = make_float4(v[4] + bias8[4], v[5] + bias8[5], v[6] + bias8[6], v[7] + bias8[7]);
   } else if constexpr (EPI == EPI_RESID) {
-    const float4* x = (const float4*)((const float*)e.aux + i);
-    const float4 a = x[0], b = x[1];
     float4* o = (float4*)((float*)e.out + i);
-    o[0] = make_float4(a.x + v[0] + bias8[0], a.y + v[1] + bias8[1], a.z + v[2] + bias8[2],
-                       a.w + v[3] + bias8[3]);
-    o[1] = make_float4(b.x + v[4] + bias8[4], b.y + v[5] + bias8[5], b.z + v[6] + bias8[6],
-                       b.w + v[7] + bias8[7]);
+    o[0] = make_float4(x.a.x + v[0] + bias8[0], x.a.y + v[1] + bias8[1], x.a.z + v[2] + bias8[2],
+                       x.a.w + v[3] + bias8[3]);
+    o[1] = make_float4(x.b.x + v[4] + bias8[4], x.b.y + v[5] + bias8[5], x.b.z + v[6] + bias8[6],
+                       x.b.w + v[7] + bias8[7]);
   } else if constexpr (EPI == EPI_ACT) {
     *(uint4*)((bf16_t*)e.out + i) =
         make_uint4(pack2bf(v[0] + bias8[0], v[1] + bias8[1]), pack2bf(v[2] + bias8[2], v[3] + bias8[3]),
@@ -181,9 +211,9 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
     *(uint4*)((bf16_t*)e.out2 + i) =
         make_uint4(pack2bf(gelu_f(u[0]), gelu_f(u[1])), pack2bf(gelu_f(u[2]), gelu_f(u[3])),
                    pack2bf(gelu_f(u[4]), gelu_f(u[5])), pack2bf(gelu_f(u[6]), gelu_f(u[7])));
-  } else {  // EPI_GELU_BWD
-    const uint4 uu = *(const uint4*)((const bf16_t*)e.aux + i);
-    const uint32_t* w = (const uint32_t*)&uu;
+  } else {  // EPI_GELU_BWD: the bf16 pre-activations travel in x.a's bits
+    const uint32_t w[4] = {__float_as_uint(x.a.x), __float_as_uint(x.a.y), __float_as_uint(x.a.z),
+                           __float_as_uint(x.a.w)};
     float d[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) d[j] = v[j] * gelu_grad_f(bf2f((bf16_t)(w[j >> 1] >> (16 * (j & 1)))));
@@ -358,8 +388,12 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
     bias8[4] = b1.x; bias8[5] = b1.y; bias8[6] = b1.z; bias8[7] = b1.w;
   }
   float* part = p.part ? p.part + (int64_t)split * p.M * p.e.ldc : nullptr;
+  const int splitk = p.ksplit > 1;
+  constexpr int NIT = (32 + RPI - 1) / RPI;  // row passes per 32-row slab
+  constexpr int PG = (OCC > 1 || TN > 3) ? 2 : NIT;  // prefetch group (register budget)
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int grow0 = m0 + wm * WR + 32 * i + my_r;
     // accumulator layout of a 32x32 tile: lane l, register r -> row
     // 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
@@ -368,18 +402,37 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
       for (int r = 0; r < 16; ++r)
         ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EP_PITCH + 32 * j + (lane & 31)] = acc[i][j][r];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // rolled: keeps the unrolled slab loop small enough that acc[i] stays
-    // statically indexed (in registers)
-#pragma unroll 1
-    for (int rr = 0; rr < 32; rr += RPI) {
-      const int lr = rr + my_r;
-      const int grow = m0 + wm * WR + 32 * i + lr;
+    auto row_pass = [&](int it, const Aux8& x) {
+      const int lr = it * RPI + my_r;
+      const int grow = grow0 + it * RPI;
       if (lane_on && lr < 32) {
         const float4 v0 = *(const float4*)(ep + lr * EP_PITCH + my_c);
         const float4 v1 = *(const float4*)(ep + lr * EP_PITCH + my_c + 4);
         const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, p.ksplit > 1, grow, gcol, v, bias8);
+        if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, splitk, grow, gcol, v, bias8, x);
       }
+    };
+    if constexpr (epi_reads_aux<EPI>()) {
+      // the auxiliary operands of PG row passes are loaded together, then
+      // those passes run (PG = the whole slab where registers allow)
+#pragma unroll
+      for (int g0 = 0; g0 < NIT; g0 += PG) {
+        Aux8 ax[PG];
+#pragma unroll
+        for (int k = 0; k < PG; ++k) {
+          const int it = g0 + k;
+          const int lr = it * RPI + my_r;
+          if (it < NIT && lane_on && lr < 32 && grow0 + it * RPI < p.M && gcol < p.N)
+            ax[k] = aux8<EPI>(p.e, splitk, grow0 + it * RPI, gcol);
+        }
+#pragma unroll
+        for (int k = 0; k < PG; ++k)
+          if (g0 + k < NIT) row_pass(g0 + k, ax[k]);
+      }
+    } else {
+      // nothing to prefetch: a rolled loop keeps the code (and registers) small
+#pragma unroll 1
+      for (int it = 0; it < NIT; ++it) row_pass(it, Aux8{});
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
@@ -418,7 +471,8 @@ inline int64_t tile_cost(int64_t M, int64_t N, int BM, int BN) {
 //    workgroups run (partials summed in order afterwards);
 //  * k-contiguous products: 256x192 tiles; with many tiles, 2 stages and two
 //    workgroups per CU (one's epilogue hides behind the other's MFMAs),
-//    otherwise 4 stages and one workgroup per CU;
+//    otherwise one workgroup per CU with 2 stages of 64 k (fewer barriers
+//    per k than 4 stages of 32; a deeper ring measured no faster);
 //  * small problems: 128x128 tiles.
 template <bool AK, bool BKC, int EPI>
 int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
@@ -456,7 +510,7 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
     }
     if constexpr (BKC) {
       if (cdiv(p.M, 256) * cdiv(p.N, 192) >= 512) run2<256, 192, AK, BKC, EPI, 2, BK, 2>(p, s);
-      else run2<256, 192, AK, BKC, EPI, 4, BK, 1>(p, s);
+      else run2<256, 192, AK, BKC, EPI, 2, 64, 1>(p, s);  // k-tiles of 64: half the barriers
     } else {
       run2<256, 256, AK, BKC, EPI, 4, BK, 1>(p, s);
     }
