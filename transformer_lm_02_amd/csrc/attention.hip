@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "kernels.h"
 
 #define LOG2E 1.4426950408889634f
 #define LN2 0.6931471805599453f
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
 // [B*H*T, 2*B*H*T).
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dqkv, int B, int Tn, int H, int C) {
+    bf16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
   // per stage: Q tile, dO tile, 4 small slots (wave 0: scaled logsumexp, wave 1: D)
   __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2 * TILE_ELEMS + 4 * 512];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -514,6 +515,40 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
         row[2 * C] = f2bf(dv[ht][r]);
       }
     }
+  if (cs_part) {
+    // column sums of this block's dK and dV over its valid keys (the bias
+    // gradient of the fused projection): per wave over its 32 keys, then the
+    // 4 waves in a fixed order; one partial row per (batch, key block)
+    __shared__ float red[4][128];
+    float sk[2] = {0.f, 0.f}, sv[2] = {0.f, 0.f};
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kw + ACC_ROW(r, lane) < Tn) {
+          sk[ht] += dk[ht][r];
+          sv[ht] += dv[ht][r];
+        }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      sk[ht] += __shfl_xor(sk[ht], 32, 64);
+      sv[ht] += __shfl_xor(sv[ht], 32, 64);
+    }
+    if (lane < 32) {
+      red[wave][32 * 0 + lane] = sk[0];
+      red[wave][32 * 1 + lane] = sk[1];
+      red[wave][64 + lane] = sv[0];
+      red[wave][96 + lane] = sv[1];
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      const int kind = tid >> 6, c = tid & 63;  // kind 0: k, 1: v
+      const int nblk = (Tn + 127) / 128;
+      cs_part[((int64_t)b * nblk + kblk) * 3 * C + (1 + kind) * C + h * 64 + c] =
+          kind == 0 ? v * 0.125f : v;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- backward: dQ
@@ -522,7 +557,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
 // operand of dQ^T += K^T dS^T, whose A operand is a transposing read of K.
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dqkv, int B, int Tn, int H, int C) {
+    bf16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
   __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
@@ -624,6 +659,33 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
         *(uint2*)(dQ + hd) = v;
       }
   }
+  if (cs_part) {
+    // column sums of this block's dQ over its valid queries: the tile goes
+    // to LDS as [head dim][query] (the ring is free once every wave is past
+    // its last key block), then each head dimension is summed in a fixed order
+    __syncthreads();
+    constexpr int TP = 129;  // pitch: rows of consecutive dims fall in distinct banks
+    float* tq = (float*)&ring[0][0][0];  // 64 x TP floats
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tq[(32 * ht + ACC_ROW(r, lane)) * TP + 32 * wave + (lane & 31)] =
+            my_q < Tn ? dq[ht][r] : 0.f;
+    __syncthreads();
+    float* part4 = tq + 64 * TP;  // [4][64]
+    {
+      const int dcol = tid & 63, quarter = tid >> 6;
+      float v = 0.f;
+      for (int q = 0; q < 32; ++q) v += tq[dcol * TP + 32 * quarter + q];
+      part4[quarter * 64 + dcol] = v;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const float v = ((part4[tid] + part4[64 + tid]) + part4[128 + tid]) + part4[192 + tid];
+      cs_part[((int64_t)b * nqb + qb) * 3 * C + h * 64 + tid] = v * 0.125f;
+    }
+  }
 }
 
 // ================================================================ launchers
@@ -647,9 +709,12 @@ int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int 
 
 // D: fp32 scratch of 2*B*H*T elements (rowsum(dout * out), then the row
 // logsumexp times log2(e) for the bf16 head-width-64 kernels).
+// cs_part / cs_out (optional): cs_out[n] (+)= column sums of dqkv (the bias
+// gradient of the fused q|k|v projection); cs_part is fp32 scratch of at
+// least max(B * cdiv(Tn, 128), colsum_part_rows(B * Tn)) x 3C elements.
 int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
-                         hipStream_t s) {
+                         float* cs_part, float* cs_out, int cs_beta, hipStream_t s) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
   const int64_t rows = (int64_t)B * H * Tn;
@@ -665,15 +730,24 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
     }
     if (flash) {
       const int nb = (Tn + 127) / 128;
+      float* cp = cs_out ? cs_part : nullptr;
       hipLaunchKernelGGL(flash_bwd_dkdv_kernel, dim3(nb * B * H), dim3(256), 0, s,
-                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
+                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
       hipLaunchKernelGGL(flash_bwd_dq_kernel, dim3(nb * B * H), dim3(256), 0, s,
-                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
+                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
+      if (cs_out) {
+        if (hipGetLastError() != hipSuccess) return -4;
+        return colsum_finalize_launch(cs_part, B * nb, 3 * C, cs_out, cs_beta, s);
+      }
     } else {
       hipLaunchKernelGGL(attn_bwd_dq_generic<bf16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
                          (const bf16_t*)qkv, lse, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
       hipLaunchKernelGGL(attn_bwd_dkdv_generic<bf16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
                          (const bf16_t*)qkv, lse, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
+    }
+    if (cs_out && !flash) {
+      if (hipGetLastError() != hipSuccess) return -4;
+      return colsum_launch(true, dqkv, B * Tn, 3 * C, cs_part, cs_out, cs_beta, s);
     }
   } else {
     hipLaunchKernelGGL(attn_bwd_dot<float>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
@@ -682,6 +756,10 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
                        (const float*)qkv, lse, D, (const float*)dout, (float*)dqkv, B, Tn, H, C);
     hipLaunchKernelGGL(attn_bwd_dkdv_generic<float>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
                        (const float*)qkv, lse, D, (const float*)dout, (float*)dqkv, B, Tn, H, C);
+    if (cs_out) {
+      if (hipGetLastError() != hipSuccess) return -4;
+      return colsum_launch(false, dqkv, B * Tn, 3 * C, cs_part, cs_out, cs_beta, s);
+    }
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -20,6 +20,14 @@ struct GemmEpiArgs {
   const float* bias = nullptr;
   int ldc = 0;
   int beta = 0;
+  // Optional column sums of the output (a bias gradient):
+  // cs_out[n] = (cs_beta ? cs_out[n] : 0) + sum_m out[m][n].  cs_part is fp32
+  // scratch of at least cdiv(M, 128) * N elements.  The GELU-derivative
+  // epilogue of the pipelined kernel forms them from its fp32 values before
+  // rounding; every other case sums the stored output afterwards.
+  float* cs_part = nullptr;
+  float* cs_out = nullptr;
+  int cs_beta = 0;
 };
 
 // A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]; likewise B(n,k).

@@ -11,6 +11,7 @@
 // epilogues, used in the fp32 correctness mode.
 #include "common.h"
 #include "gemm.h"
+#include "kernels.h"
 
 // ---------------------------------------------------------------- epilogue
 template <int EPI, typename T>
@@ -328,15 +329,35 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
                  int ldb, int M, int N, int K, int ka_rows, int kb_rows, const GemmEpiArgs& e,
                  float* ws, int64_t ws_bytes, hipStream_t s);
 
+static int gemm_launch_plain(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* A,
+                             int lda, const void* B, int ldb, int M, int N, int K, int ka_rows,
+                             int kb_rows, const GemmEpiArgs& e, hipStream_t stream, float* ws,
+                             int64_t ws_bytes);
+
 int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda,
                 const void* B, int ldb, int M, int N, int K, int ka_rows, int kb_rows,
                 const GemmEpiArgs& e, hipStream_t stream, float* ws, int64_t ws_bytes) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   if (bf16) {
-    // the pipelined kernel when the shape allows it, else the plain one below
+    // the pipelined kernel when the shape allows it (column sums included)
     const int rc = gemm2_launch(a_kcontig, b_kcontig, epi, A, lda, B, ldb, M, N, K, ka_rows,
                                 kb_rows, e, ws, ws_bytes, stream);
     if (rc != -5) return rc == 0 ? (hipGetLastError() == hipSuccess ? 0 : -4) : rc;
+  }
+  const int rc = gemm_launch_plain(bf16, a_kcontig, b_kcontig, epi, A, lda, B, ldb, M, N, K,
+                                   ka_rows, kb_rows, e, stream, ws, ws_bytes);
+  if (rc != 0 || !e.cs_out) return rc;
+  if (e.ldc != N) return -5;
+  return colsum_launch(bf16, e.out, M, N, e.cs_part, e.cs_out, e.cs_beta, stream);
+}
+
+static int gemm_launch_plain(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* A,
+                             int lda, const void* B, int ldb, int M, int N, int K, int ka_rows,
+                             int kb_rows, const GemmEpiArgs& e, hipStream_t stream, float* ws,
+                             int64_t ws_bytes) {
+  (void)ws;
+  (void)ws_bytes;
+  if (bf16) {
     if ((a_kcontig && (K % 8 || lda % 8)) || (b_kcontig && (K % 8 || ldb % 8))) return -5;
     if ((!a_kcontig && lda % 8) || (!b_kcontig && ldb % 8)) return -5;
     if (((uintptr_t)A | (uintptr_t)B) & 15) return -5;

@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "kernels.h"
 
 #define AS3(p) ((__attribute__((address_space(3))) void*)(p))
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -176,7 +177,8 @@ constexpr bool epi_reads_aux() {
 // 8 consecutive outputs of one row: epilogue and 16/32-byte stores
 template <int EPI>
 __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int splitk, int m, int n,
-                                     const float* v, const float* bias8, const Aux8& x) {
+                                     const float* v, const float* bias8, const Aux8& x,
+                                     float* csum) {
   const int64_t i = (int64_t)m * e.ldc + n;
   if constexpr (EPI == EPI_ACCUM) {
     if (splitk) {
@@ -217,6 +219,8 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
     float d[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) d[j] = v[j] * gelu_grad_f(bf2f((bf16_t)(w[j >> 1] >> (16 * (j & 1)))));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) csum[j] += d[j];
     *(uint4*)((bf16_t*)e.out + i) =
         make_uint4(pack2bf(d[0], d[1]), pack2bf(d[2], d[3]), pack2bf(d[4], d[5]), pack2bf(d[6], d[7]));
   }
@@ -389,6 +393,9 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   }
   float* part = p.part ? p.part + (int64_t)split * p.M * p.e.ldc : nullptr;
   const int splitk = p.ksplit > 1;
+  // column sums of this lane's 8 columns over its rows (GELU-derivative
+  // epilogue with cs_part set); zeros otherwise
+  float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr int NIT = (32 + RPI - 1) / RPI;  // row passes per 32-row slab
   constexpr int PG = (OCC > 1 || TN > 3) ? 2 : NIT;  // prefetch group (register budget)
 #pragma unroll
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
         const float4 v0 = *(const float4*)(ep + lr * EP_PITCH + my_c);
         const float4 v1 = *(const float4*)(ep + lr * EP_PITCH + my_c + 4);
         const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, splitk, grow, gcol, v, bias8, x);
+        if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, splitk, grow, gcol, v, bias8, x, csum);
       }
     };
     if constexpr (epi_reads_aux<EPI>()) {
@@ -436,6 +443,31 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
+  if constexpr (EPI == EPI_GELU_BWD) {
+    if (p.e.cs_part) {
+      // this wave's staging area is free again (its last reads completed
+      // above): lanes of one row pass put their sums side by side, then the
+      // two waves sharing these columns are added in a fixed order, giving
+      // one partial row per row tile: cs_part[tm][n]
+      float* cw = (float*)lds + wave * 32 * EP_PITCH;
+      if (lane_on) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cw[my_r * WC + my_c + j] = csum[j];
+      }
+      __syncthreads();
+      for (int t = tid; t < 2 * WC; t += 256) {
+        const int wnn = t / WC, c = t % WC;
+        float v = 0.f;
+#pragma unroll
+        for (int wmm = 0; wmm < 2; ++wmm) {
+          const float* src = (const float*)lds + (wmm * 2 + wnn) * 32 * EP_PITCH;
+          for (int r = 0; r < RPI; ++r) v += src[r * WC + c];
+        }
+        const int n = n0 + wnn * WC + c;
+        if (n < p.N) p.e.cs_part[(int64_t)tm * p.N + n] = v;
+      }
+    }
+  }
 }
 
 // out[i] = (beta ? out[i] : 0) + sum_s part[s][i], fixed order
@@ -451,12 +483,16 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
   ((float4*)out)[i4] = s;
 }
 
+// launches one configuration; then, when column sums were asked for, adds
+// the per-row-tile partials into cs_out
 template <int BM, int BN, bool AK, bool BKC, int EPI, int NS, int BK, int OCC = 1>
-void run2(Gemm2Args p, hipStream_t s) {
+int run2(Gemm2Args p, hipStream_t s) {
   p.tiles_m = (int)cdiv(p.M, BM);
   p.tiles_n = (int)cdiv(p.N, BN);
   hipLaunchKernelGGL((gemm2_kernel<BM, BN, AK, BKC, EPI, NS, BK, OCC>),
                      dim3(p.tiles_m * p.tiles_n, p.ksplit), dim3(256), 0, s, p);
+  if (p.e.cs_part) return colsum_finalize_launch(p.e.cs_part, p.tiles_m, p.N, p.e.cs_out, p.e.cs_beta, s);
+  return 0;
 }
 
 // rounds of 256 workgroups (one per CU) times the work of one tile
@@ -495,7 +531,7 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
       p.ksplit = ks;
       p.part = ws;
     }
-    run2<128, 256, AK, BKC, EPI, 2, BK, 2>(p, s);
+    if (const int rc = run2<128, 256, AK, BKC, EPI, 2, BK, 2>(p, s)) return rc;
     if (p.ksplit > 1) {
       const int64_t n = (int64_t)p.M * p.N;
       hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, ws, p.ksplit,
@@ -505,16 +541,14 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
   } else {
     const int64_t t256 = cdiv(p.M, 256) * cdiv(p.N, 256);
     if (t256 < 64) {  // small problem: smaller tiles keep more CUs busy
-      run2<128, 128, AK, BKC, EPI, 4, 64>(p, s);
-      return 0;
+      return run2<128, 128, AK, BKC, EPI, 4, 64>(p, s);
     }
     if constexpr (BKC) {
-      if (cdiv(p.M, 256) * cdiv(p.N, 192) >= 512) run2<256, 192, AK, BKC, EPI, 2, BK, 2>(p, s);
-      else run2<256, 192, AK, BKC, EPI, 2, 64, 1>(p, s);  // k-tiles of 64: half the barriers
+      if (cdiv(p.M, 256) * cdiv(p.N, 192) >= 512) return run2<256, 192, AK, BKC, EPI, 2, BK, 2>(p, s);
+      return run2<256, 192, AK, BKC, EPI, 2, 64, 1>(p, s);  // k-tiles of 64: half the barriers
     } else {
-      run2<256, 256, AK, BKC, EPI, 4, BK, 1>(p, s);
+      return run2<256, 256, AK, BKC, EPI, 4, BK, 1>(p, s);
     }
-    return 0;
   }
 }
 
@@ -527,6 +561,7 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
                  int ldb, int M, int N, int K, int ka_rows, int kb_rows, const GemmEpiArgs& e,
                  float* ws, int64_t ws_bytes, hipStream_t s) {
   if (K % 8 || lda % 8 || ldb % 8 || N % 8 || e.ldc % 8) return -5;
+  if (e.cs_out && (epi != EPI_GELU_BWD || e.ldc != N || N % 4)) return -5;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)e.out) & 15) return -5;
   if ((e.aux && ((uintptr_t)e.aux & 15)) || (e.out2 && ((uintptr_t)e.out2 & 15))) return -5;
   if (e.bias && ((uintptr_t)e.bias & 15)) return -5;

@@ -7,6 +7,8 @@
 // only enqueues kernels on the caller's stream; all device memory belongs to
 // the caller (params, grads, Adam moments and one workspace).
 #include <math.h>
+
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -182,7 +184,9 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   w.dO = take(M * d * es);
   w.Dbuf = take(2 * M * H * 4);
   w.ln_part = take((int64_t)layernorm_bwd_part_rows((int)M) * 3 * d * 4);
-  w.cs_part = take((int64_t)colsum_part_rows((int)M) * 4 * d * 4);
+  // column-sum partials: at most one row per 128 tokens (GEMM row tiles,
+  // attention blocks) or per colsum_part_rows block
+  w.cs_part = take(std::max<int64_t>(cdiv(M, 128), colsum_part_rows((int)M)) * 4 * d * 4);
   w.norm_part = take((int64_t)adamw_norm_blocks() * 8);
   w.splitk_bytes = bf ? gemm_splitk_bytes(4 * d, d) : 0;
   w.splitk = take(w.splitk_bytes);
@@ -471,14 +475,16 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = dbig;
     e.aux = h->at(L.u);
     e.ldc = 4 * d;
+    e.cs_part = cs_part;  // MLP expansion bias: db = colsum(du), formed alongside
+    e.cs_out = h->G(P.fcb);
+    e.cs_beta = beta;
     if (bf)
       CK(gemm_launch(bf, true, true, EPI_GELU_BWD, dres_act, d, h->WT(L.mprojT), d, M, 4 * d, d, d,
                      d, e, s));
     else
       CK(gemm_launch(bf, true, false, EPI_GELU_BWD, dres_act, d, h->W(P.mprojw), 4 * d, M, 4 * d, d,
                      d, d, e, s));
-    // MLP expansion: db = colsum(du); dW (+)= du^T ln2 ; dln2 = du Wfc
-    CK(colsum_launch(bf, dbig, M, 4 * d, cs_part, h->G(P.fcb), beta, s));
+    // MLP expansion: dW (+)= du^T ln2 ; dln2 = du Wfc
     e = GemmEpiArgs();
     e.out = h->G(P.fcw);
     e.ldc = d;
@@ -509,10 +515,11 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
       CK(gemm_launch(bf, true, true, EPI_ACT, dres_act, d, h->WT(L.aprojT), d, M, d, d, d, d, e, s));
     else
       CK(gemm_launch(bf, true, false, EPI_ACT, dres_act, d, h->W(P.aprojw), d, M, d, d, d, d, e, s));
+    // attention; the fused projection's bias gradient db = colsum(dqkv) is
+    // formed by the attention backward
     CK(attention_bwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), h->at(w.dO), dbig,
-                            h->at<float>(w.Dbuf), B, T, H, d, s));
-    // fused q|k|v projection: db = colsum(dqkv); dW (+)= dqkv^T ln1 ; dln1 = dqkv Wqkv
-    CK(colsum_launch(bf, dbig, M, 3 * d, cs_part, h->G(P.attnb), beta, s));
+                            h->at<float>(w.Dbuf), B, T, H, d, cs_part, h->G(P.attnb), beta, s));
+    // fused q|k|v projection: dW (+)= dqkv^T ln1 ; dln1 = dqkv Wqkv
     e = GemmEpiArgs();
     e.out = h->G(P.attnw);
     e.ldc = d;
@@ -631,7 +638,8 @@ int gpt_op_attention_bwd(int32_t bf16, const void* qkv, const void* out, const f
                          int32_t C, void* stream) {
   if (!qkv || !out || !lse || !dout || !dqkv || !D || B < 1 || T < 1 || H < 1 || C % H)
     return fail(GPT_EINVAL, "bad attention arguments");
-  CK(attention_bwd_launch(bf16 != 0, qkv, out, lse, dout, dqkv, D, B, T, H, C, (hipStream_t)stream));
+  CK(attention_bwd_launch(bf16 != 0, qkv, out, lse, dout, dqkv, D, B, T, H, C, nullptr, nullptr, 0,
+                          (hipStream_t)stream));
   return GPT_OK;
 }
 

@@ -27,7 +27,7 @@ int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int 
                          int C, hipStream_t s);
 int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
-                         hipStream_t s);
+                         float* cs_part, float* cs_out, int cs_beta, hipStream_t s);
 
 int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s);
@@ -48,6 +48,9 @@ int cross_entropy_launch(bool bf16, void* logits, const int32_t* tgt, float* row
 int loss_finalize_launch(const float* row_loss, int N, const int* n_valid, float* loss,
                          hipStream_t s);
 int colsum_part_rows(int M);
+// out (+)= column sums of part [nrow][ncol] (ncol % 4 == 0)
+int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
+                           hipStream_t s);
 int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* out, int beta,
                   hipStream_t s);
 
