@@ -41,9 +41,10 @@ def flops_per_token(dims, T):
 
 
 # The kernel with the largest share of the step: the bf16 GEMM with fp32
-# output and 256x192 tiles that forms the input gradients through the
-# transposed weight copies (fc and qkv per layer, and the tied LM head once).
-DOMINANT_KERNEL = "gemm2_kernel<256, 192, true, true, 1, 2, 64, 1>"
+# output (128x192 tiles, two workgroups per CU) that forms the input gradients
+# through the transposed weight copies (fc and qkv per layer, and the tied LM
+# head once).
+DOMINANT_KERNEL = "gemm2_kernel<128, 192, true, true, 1, 2, 64, 2>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_f32_dx.json")
 TRAFFIC_SOURCES = ["transformer_lm_02_amd/csrc/gemm2.hip", "transformer_lm_02_amd/csrc/gemm.h",
                    "transformer_lm_02_amd/csrc/common.h"]

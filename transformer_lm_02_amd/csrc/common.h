@@ -73,5 +73,13 @@ __device__ __forceinline__ float gelu_grad_f(float u) {
   const float q = fmaf(u2, 6.0f * GELU_C * GELU_A, 2.0f * GELU_C);  // 2c (1 + 3 a u^2)
   return fmaf(u * s * (1.0f - s), q, s);
 }
+// both at once from one exponential: g = gelu(u), gp = gelu'(u)
+__device__ __forceinline__ void gelu_both(float u, float& g, float& gp) {
+  const float u2 = u * u;
+  const float s = gelu_sig(u, u2);
+  const float q = fmaf(u2, 6.0f * GELU_C * GELU_A, 2.0f * GELU_C);
+  g = u * s;
+  gp = fmaf(g * (1.0f - s), q, s);
+}
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -8,8 +8,8 @@ enum GemmEpi {
   EPI_ACT = 0,      // out_act[m][n] = acc + bias[n]
   EPI_F32 = 1,      // out_f32[m][n] = acc + bias[n]
   EPI_RESID = 2,    // out_f32[m][n] = aux_f32[m][n] + acc + bias[n]   (residual add)
-  EPI_GELU = 3,     // u = acc + bias[n]; out_act = u; out2_act = gelu(u)
-  EPI_GELU_BWD = 4, // out_act[m][n] = acc * gelu'(aux_act[m][n])
+  EPI_GELU = 3,     // u = acc + bias[n]; out_act = gelu'(u); out2_act = gelu(u)
+  EPI_GELU_BWD = 4, // out_act[m][n] = acc * aux_act[m][n]  (aux: the stored gelu'(u))
   EPI_ACCUM = 5     // out_f32[m][n] = (beta ? out_f32[m][n] : 0) + acc
 };
 

@@ -24,12 +24,12 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& e, int m, int n, fl
   } else if constexpr (EPI == EPI_RESID) {
     ((float*)e.out)[i] = ((const float*)e.aux)[i] + acc + (e.bias ? e.bias[n] : 0.f);
   } else if constexpr (EPI == EPI_GELU) {
-    float u = acc + (e.bias ? e.bias[n] : 0.f);
-    stf((T*)e.out + i, u);
-    stf((T*)e.out2 + i, gelu_f(u));
+    float g, gp;
+    gelu_both(acc + (e.bias ? e.bias[n] : 0.f), g, gp);
+    stf((T*)e.out + i, gp);
+    stf((T*)e.out2 + i, g);
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    float u = ldf((const T*)e.aux + i);
-    stf((T*)e.out + i, acc * gelu_grad_f(u));
+    stf((T*)e.out + i, acc * ldf((const T*)e.aux + i));
   } else {  // EPI_ACCUM
     float* o = (float*)e.out + i;
     *o = (e.beta ? *o : 0.f) + acc;

@@ -205,20 +205,20 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
         make_uint4(pack2bf(v[0] + bias8[0], v[1] + bias8[1]), pack2bf(v[2] + bias8[2], v[3] + bias8[3]),
                    pack2bf(v[4] + bias8[4], v[5] + bias8[5]), pack2bf(v[6] + bias8[6], v[7] + bias8[7]));
   } else if constexpr (EPI == EPI_GELU) {
-    float u[8];
+    // the backward needs only gelu'(u): it is stored in place of u
+    float g[8], gp[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = v[j] + bias8[j];
-    *(uint4*)((bf16_t*)e.out + i) =
-        make_uint4(pack2bf(u[0], u[1]), pack2bf(u[2], u[3]), pack2bf(u[4], u[5]), pack2bf(u[6], u[7]));
+    for (int j = 0; j < 8; ++j) gelu_both(v[j] + bias8[j], g[j], gp[j]);
+    *(uint4*)((bf16_t*)e.out + i) = make_uint4(pack2bf(gp[0], gp[1]), pack2bf(gp[2], gp[3]),
+                                               pack2bf(gp[4], gp[5]), pack2bf(gp[6], gp[7]));
     *(uint4*)((bf16_t*)e.out2 + i) =
-        make_uint4(pack2bf(gelu_f(u[0]), gelu_f(u[1])), pack2bf(gelu_f(u[2]), gelu_f(u[3])),
-                   pack2bf(gelu_f(u[4]), gelu_f(u[5])), pack2bf(gelu_f(u[6]), gelu_f(u[7])));
-  } else {  // EPI_GELU_BWD: the bf16 pre-activations travel in x.a's bits
+        make_uint4(pack2bf(g[0], g[1]), pack2bf(g[2], g[3]), pack2bf(g[4], g[5]), pack2bf(g[6], g[7]));
+  } else {  // EPI_GELU_BWD: the bf16 gelu'(u) values travel in x.a's bits
     const uint32_t w[4] = {__float_as_uint(x.a.x), __float_as_uint(x.a.y), __float_as_uint(x.a.z),
                            __float_as_uint(x.a.w)};
     float d[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) d[j] = v[j] * gelu_grad_f(bf2f((bf16_t)(w[j >> 1] >> (16 * (j & 1)))));
+    for (int j = 0; j < 8; ++j) d[j] = v[j] * bf2f((bf16_t)(w[j >> 1] >> (16 * (j & 1))));
 #pragma unroll
     for (int j = 0; j < 8; ++j) csum[j] += d[j];
     *(uint4*)((bf16_t*)e.out + i) =
@@ -397,7 +397,10 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   // epilogue with cs_part set); zeros otherwise
   float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr int NIT = (32 + RPI - 1) / RPI;  // row passes per 32-row slab
-  constexpr int PG = (OCC > 1 || TN > 3) ? 2 : NIT;  // prefetch group (register budget)
+  // prefetch group (register budget): a whole slab when the accumulators
+  // leave room (or the operand is 16 bytes per pass), else two passes
+  constexpr int PG =
+      ((EPI == EPI_GELU_BWD && TM * TN <= 12) || TM * TN <= 6 || (OCC == 1 && TN <= 3)) ? NIT : 2;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int grow0 = m0 + wm * WR + 32 * i + my_r;
@@ -502,27 +505,31 @@ inline int64_t tile_cost(int64_t M, int64_t N, int BM, int BN) {
 }
 
 // Tile choice (measured on MI355X for the step's shapes):
-//  * weight gradients (both operands m/n-contiguous): 128x256 tiles, two
-//    workgroups per CU, the token reduction split so that about 400
-//    workgroups run (partials summed in order afterwards);
-//  * k-contiguous products: 256x192 tiles; with many tiles, 2 stages and two
-//    workgroups per CU (one's epilogue hides behind the other's MFMAs),
-//    otherwise one workgroup per CU with 2 stages of 64 k (fewer barriers
-//    per k than 4 stages of 32; a deeper ring measured no faster);
+//  * weight gradients (both operands m/n-contiguous): 128x128 tiles with
+//    k-tiles of 64, two workgroups per CU, the token reduction split so that
+//    about 400 workgroups run (partials summed in order afterwards);
+//  * k-contiguous products, two workgroups per CU (one's epilogue and waits
+//    hide behind the other's MFMAs): with at least 1024 tiles of 256x192,
+//    those tiles with 2 stages of 32 k; otherwise 128x192 tiles with 2 stages
+//    of 64 k (half the barriers per k; deeper rings measured no faster);
 //  * small problems: 128x128 tiles.
 template <bool AK, bool BKC, int EPI>
 int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
   constexpr int BK = 32;
-  const int nk = (int)cdiv(p.K, BK);
   p.ksplit = 1;
-  p.k_tiles_per_split = nk;
+  p.k_tiles_per_split = (int)cdiv(p.K, BK);
   p.part = nullptr;
   if constexpr (EPI == EPI_ACCUM && !AK && !BKC) {
-    const int64_t tiles = cdiv(p.M, 128) * cdiv(p.N, 256);
+    // 128x128 tiles, k-tiles of 64, two workgroups per CU; the token
+    // reduction split so that about 400 workgroups run
+    constexpr int BKW = 64;
+    const int nk = (int)cdiv(p.K, BKW);
+    p.k_tiles_per_split = nk;
+    const int64_t tiles = cdiv(p.M, 128) * cdiv(p.N, 128);
     int ks = 1;
-    if (ws != nullptr && nk >= 16) {
+    if (ws != nullptr && nk >= 8) {
       ks = (int)std::max<int64_t>(1, std::min<int64_t>(16, (400 + tiles / 2) / tiles));
-      ks = std::min(ks, std::max(1, nk / 8));
+      ks = std::min(ks, std::max(1, nk / 4));
       while (ks > 1 && (int64_t)ks * p.M * p.N * 4 > ws_bytes) --ks;
     }
     if (ks > 1) {
@@ -531,7 +538,7 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
       p.ksplit = ks;
       p.part = ws;
     }
-    if (const int rc = run2<128, 256, AK, BKC, EPI, 2, BK, 2>(p, s)) return rc;
+    if (const int rc = run2<128, 128, AK, BKC, EPI, 2, BKW, 2>(p, s)) return rc;
     if (p.ksplit > 1) {
       const int64_t n = (int64_t)p.M * p.N;
       hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, ws, p.ksplit,
@@ -544,8 +551,8 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
       return run2<128, 128, AK, BKC, EPI, 4, 64>(p, s);
     }
     if constexpr (BKC) {
-      if (cdiv(p.M, 256) * cdiv(p.N, 192) >= 512) return run2<256, 192, AK, BKC, EPI, 2, BK, 2>(p, s);
-      return run2<256, 192, AK, BKC, EPI, 2, 64, 1>(p, s);  // k-tiles of 64: half the barriers
+      if (cdiv(p.M, 256) * cdiv(p.N, 192) >= 1024) return run2<256, 192, AK, BKC, EPI, 2, BK, 2>(p, s);
+      return run2<128, 192, AK, BKC, EPI, 2, 64, 2>(p, s);  // k-tiles of 64: half the barriers
     } else {
       return run2<256, 256, AK, BKC, EPI, 4, BK, 1>(p, s);
     }

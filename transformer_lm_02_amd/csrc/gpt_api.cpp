@@ -100,7 +100,7 @@ ParamOff param_offsets(const gpt_config& c) {
 // byte offsets of every buffer in the workspace
 struct WsLayer {
   int64_t attnT, aprojT, fcT, mprojT;  // element offsets in the transposed copy
-  size_t x_in, ln1_mean, ln1_rstd, ln1, qkv, att, lse, x_mid, ln2_mean, ln2_rstd, ln2, u, g;
+  size_t x_in, ln1_mean, ln1_rstd, ln1, qkv, att, lse, x_mid, ln2_mean, ln2_rstd, ln2, dgelu, g;
 };
 struct WsOff {
   size_t shadow = 0;
@@ -164,7 +164,7 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
     L.ln2_mean = take(M * 4);
     L.ln2_rstd = take(M * 4);
     L.ln2 = take(M * d * es);
-    L.u = take(M * 4 * d * es);
+    L.dgelu = take(M * 4 * d * es);  // gelu'(u), kept for the backward
     L.g = take(M * 4 * d * es);
     w.layer.push_back(L);
   }
@@ -378,7 +378,7 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, i
     CK(layernorm_fwd_launch(bf, h->at<float>(L.x_mid), h->P(P.ln2w), h->P(P.ln2b), h->at(L.ln2),
                             h->at<float>(L.ln2_mean), h->at<float>(L.ln2_rstd), M, d, s));
     e = GemmEpiArgs();
-    e.out = h->at(L.u);
+    e.out = h->at(L.dgelu);
     e.out2 = h->at(L.g);
     e.bias = h->P(P.fcb);
     e.ldc = 4 * d;
@@ -473,7 +473,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.g), 4 * d, d, 4 * d, M, M, M, e, s, sk, skb));
     e = GemmEpiArgs();
     e.out = dbig;
-    e.aux = h->at(L.u);
+    e.aux = h->at(L.dgelu);
     e.ldc = 4 * d;
     e.cs_part = cs_part;  // MLP expansion bias: db = colsum(du), formed alongside
     e.cs_out = h->G(P.fcb);
