@@ -40,12 +40,13 @@ def flops_per_token(dims, T):
     return 6 * N + 12 * dims["n_layer"] * dims["n_head"] * hs * T
 
 
-# The kernel with the largest share of the step: the bf16 GEMM with fp32
-# output (128x192 tiles, two workgroups per CU) that forms the input gradients
-# through the transposed weight copies (fc and qkv per layer, and the tied LM
-# head once).
-DOMINANT_KERNEL = "gemm2_kernel<128, 192, true, true, 1, 2, 64, 2>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_f32_dx.json")
+# The kernel with the largest share of the step: the bf16 GEMM with bf16
+# output on 128x192 tiles (two workgroups per CU, k-tiles of 64).  A step
+# launches it for the input gradients through the transposed weight copies
+# (fc and qkv per layer, the tied LM head once, the attention projection per
+# layer) and for the forward q|k|v projection.
+DOMINANT_KERNEL = "gemm2_kernel<128, 192, true, true, 0, 2, 64, 2>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_act_128x192.json")
 TRAFFIC_SOURCES = ["transformer_lm_02_amd/csrc/gemm2.hip", "transformer_lm_02_amd/csrc/gemm.h",
                    "transformer_lm_02_amd/csrc/common.h"]
 
@@ -54,7 +55,7 @@ def dominant_launches(B, T, dims):
     """(M, N, K, count) of the launches one step makes of the dominant kernel."""
     M, d, L = B * T, dims["n_embd"], dims["n_layer"]
     vi = -(-dims["padded_vocab"] // 64) * 64
-    return [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, vi, 1)]
+    return [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, vi, 1), (M, d, d, L), (M, 3 * d, d, L)]
 
 
 def sources_hash():
@@ -85,7 +86,7 @@ def dominant_operands(torch, B, T, dims):
     for (M, N, K, n) in dominant_launches(B, T, dims):
         A = (torch.randn((M, K), device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
         W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         ops.append((A, W, C, M, N, K, n))
     return ops
 
@@ -97,7 +98,7 @@ def launch_dominant(bd, ops, stream_ptr, reps=1):
             for _ in range(n):
                 bd.check(bd.lib.gpt_op_linear(1, ctypes.c_void_p(A.data_ptr()),
                                               ctypes.c_void_p(W.data_ptr()), None,
-                                              ctypes.c_void_p(C.data_ptr()), 1, M, N, K,
+                                              ctypes.c_void_p(C.data_ptr()), 0, M, N, K,
                                               stream_ptr), "gpt_op_linear")
 
 
@@ -118,7 +119,8 @@ def time_dominant_kernel(torch, bd, B, T, dims, reps=5):
     ms_total = e0.elapsed_time(e1) / reps
     flops = sum(2.0 * M * N * K * n for (_, _, _, M, N, K, n) in ops)
     achieved = flops / (ms_total * 1e-3) / 1e12
-    return {"kernel": DOMINANT_KERNEL + " (fp32-output input gradients: fc, qkv, LM head)",
+    return {"kernel": DOMINANT_KERNEL + " (input gradients of fc, qkv, attention projection and LM "
+                                        "head; forward q|k|v projection)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(), "launches_per_step": n_launch,

@@ -433,14 +433,17 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
   const int vi = (int)w.vi;
   float* dres = h->at<float>(w.dres);
   void* dres_act = h->at(w.dres_act);
-  float* dln = h->at<float>(w.dln);
+  void* dln = h->at(w.dln);  // input gradients of the LayerNorms, in the activation type
   void* dbig = h->at(w.dbig);
   float* ln_part = h->at<float>(w.ln_part);
   float* cs_part = h->at<float>(w.cs_part);
   float* sk = w.splitk_bytes ? h->at<float>(w.splitk) : nullptr;
   const int64_t skb = w.splitk_bytes;
 
-  // LM head: dwte (+)= dlogits^T lnf ; dlnf = dlogits wte
+  // LM head: dwte (+)= dlogits^T lnf ; dlnf = dlogits wte.  The input
+  // gradients of the LayerNorms (dlnf, dln2, dln1) are stored in the
+  // activation type, as the matrix products' outputs are under bf16 mixed
+  // precision; the LayerNorm backward reads them into fp32.
   {
     GemmEpiArgs e;
     e.out = h->G(p.wte);
@@ -452,10 +455,10 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = dln;
     e.ldc = d;
     if (bf)
-      CK(gemm_launch(bf, true, true, EPI_F32, h->at(w.logits), vi, h->WT(w.wteT), vi, M, d, vi, vi,
+      CK(gemm_launch(bf, true, true, EPI_ACT, h->at(w.logits), vi, h->WT(w.wteT), vi, M, d, vi, vi,
                      vi, e, s));
     else
-      CK(gemm_launch(bf, true, false, EPI_F32, h->at(w.logits), vi, h->W(p.wte), d, M, d, vi, vi,
+      CK(gemm_launch(bf, true, false, EPI_ACT, h->at(w.logits), vi, h->W(p.wte), d, M, d, vi, vi,
                      c.padded_vocab, e, s));
   }
   CK(layernorm_bwd_launch(bf, dln, h->at<float>(w.x_final), h->at<float>(w.lnf_mean),
@@ -494,10 +497,10 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = dln;
     e.ldc = d;
     if (bf)
-      CK(gemm_launch(bf, true, true, EPI_F32, dbig, 4 * d, h->WT(L.fcT), 4 * d, M, d, 4 * d, 4 * d,
+      CK(gemm_launch(bf, true, true, EPI_ACT, dbig, 4 * d, h->WT(L.fcT), 4 * d, M, d, 4 * d, 4 * d,
                      4 * d, e, s));
     else
-      CK(gemm_launch(bf, true, false, EPI_F32, dbig, 4 * d, h->W(P.fcw), d, M, d, 4 * d, 4 * d,
+      CK(gemm_launch(bf, true, false, EPI_ACT, dbig, 4 * d, h->W(P.fcw), d, M, d, 4 * d, 4 * d,
                      4 * d, e, s));
     CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_mid), h->at<float>(L.ln2_mean),
                             h->at<float>(L.ln2_rstd), h->P(P.ln2w), dres, dres_act, 1, ln_part,
@@ -529,10 +532,10 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = dln;
     e.ldc = d;
     if (bf)
-      CK(gemm_launch(bf, true, true, EPI_F32, dbig, 3 * d, h->WT(L.attnT), 3 * d, M, d, 3 * d, 3 * d,
+      CK(gemm_launch(bf, true, true, EPI_ACT, dbig, 3 * d, h->WT(L.attnT), 3 * d, M, d, 3 * d, 3 * d,
                      3 * d, e, s));
     else
-      CK(gemm_launch(bf, true, false, EPI_F32, dbig, 3 * d, h->W(P.attnw), d, M, d, 3 * d, 3 * d,
+      CK(gemm_launch(bf, true, false, EPI_ACT, dbig, 3 * d, h->W(P.attnw), d, M, d, 3 * d, 3 * d,
                      3 * d, e, s));
     CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_in), h->at<float>(L.ln1_mean),
                             h->at<float>(L.ln1_rstd), h->P(P.ln1w), dres, dres_act, 1, ln_part,

@@ -32,7 +32,8 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
 int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s);
 int layernorm_bwd_part_rows(int M);
-int layernorm_bwd_launch(bool bf16, const float* dy, const float* x, const float* mean,
+// dy: the mode's activation type (bf16 or fp32) [M][C]
+int layernorm_bwd_launch(bool bf16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
                          int beta, int M, int C, hipStream_t s);

@@ -15,6 +15,23 @@
 #define LN_EPS 1e-5f
 #define LN_MAXV_MAX 8  // float4 per lane: C <= 2048
 
+// 4 consecutive values of T as loaded (raw) and as fp32
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+  typedef float4 type;
+  __device__ __forceinline__ static float4 load(const float* p) { return *(const float4*)p; }
+  __device__ __forceinline__ static float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ static float4 f32(float4 v) { return v; }
+};
+template <> struct Raw4<bf16_t> {
+  typedef uint2 type;
+  __device__ __forceinline__ static uint2 load(const bf16_t* p) { return *(const uint2*)p; }
+  __device__ __forceinline__ static uint2 zero() { return make_uint2(0u, 0u); }
+  __device__ __forceinline__ static float4 f32(uint2 u) {
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+};
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float4 v);
 template <>
@@ -82,7 +99,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 #define LN_BWD_ROWS 16
 template <typename T, int LN_MAXV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
-    const float* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
+    const T* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres,
     T* __restrict__ dres_act, int accumulate, float* __restrict__ part, int M, int C) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,28 +113,31 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
   }
   const int64_t r0 = (int64_t)blockIdx.x * LN_BWD_ROWS;
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 dc[LN_MAXV], xc[LN_MAXV];  // current row: dy, x
+  typedef typename Raw4<T>::type RawT;
+  RawT dc[LN_MAXV];  // current row: dy (as stored), x
+  float4 xc[LN_MAXV];
   {
     const int64_t row = r0 + wave;
 #pragma unroll
     for (int i = 0; i < LN_MAXV; ++i) {
       const int j = lane + 64 * i;
       const bool ok = j < nv && row < M;
-      dc[i] = ok ? ((const float4*)(dy + row * C))[j] : z4;
+      dc[i] = ok ? Raw4<T>::load(dy + row * C + 4 * j) : Raw4<T>::zero();
       xc[i] = ok ? ((const float4*)(x + row * C))[j] : z4;
     }
   }
   for (int rr = wave; rr < LN_BWD_ROWS; rr += 4) {
     const int64_t row = r0 + rr;
     if (row >= M) break;
-    float4 pc[LN_MAXV], dn[LN_MAXV], xn[LN_MAXV];
+    float4 pc[LN_MAXV], xn[LN_MAXV];
+    RawT dn[LN_MAXV];
     const int64_t nrow = row + 4;
     const bool more = rr + 4 < LN_BWD_ROWS && nrow < M;
 #pragma unroll
     for (int i = 0; i < LN_MAXV; ++i) {
       const int j = lane + 64 * i;
       pc[i] = j < nv && accumulate ? ((const float4*)(dres + row * C))[j] : z4;
-      dn[i] = j < nv && more ? ((const float4*)(dy + nrow * C))[j] : z4;
+      dn[i] = j < nv && more ? Raw4<T>::load(dy + nrow * C + 4 * j) : Raw4<T>::zero();
       xn[i] = j < nv && more ? ((const float4*)(x + nrow * C))[j] : z4;
     }
     const float mu = mean[row], rs = rstd[row];
@@ -125,7 +145,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < LN_MAXV; ++i) {
-      const float4 d = dc[i], xv = xc[i];
+      const float4 d = Raw4<T>::f32(dc[i]), xv = xc[i];
       xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
       g[i] = make_float4(d.x * ww[i].x, d.y * ww[i].y, d.z * ww[i].z, d.w * ww[i].w);
       s1 += g[i].x + g[i].y + g[i].z + g[i].w;
@@ -271,7 +291,7 @@ int layernorm_bwd_part_rows(int M) { return (int)cdiv(M, LN_BWD_ROWS); }
 
 // dres = (accumulate ? dres : 0) + LN'(dy); dres_act = copy; then
 // dw, db (beta-accumulated) and bias_grad (+)= column sum of dres, if non-null.
-int layernorm_bwd_launch(bool bf16, const float* dy, const float* x, const float* mean,
+int layernorm_bwd_launch(bool bf16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
                          int beta, int M, int C, hipStream_t s) {
@@ -279,11 +299,11 @@ int layernorm_bwd_launch(bool bf16, const float* dy, const float* x, const float
   const int nb = (int)cdiv(M, LN_BWD_ROWS);
 #define LNB(V)                                                                                   \
   if (bf16)                                                                                       \
-    hipLaunchKernelGGL((ln_bwd_kernel<bf16_t, V>), dim3(nb), dim3(256), 0, s, dy, x, mean, rstd, \
-                       w, dres, (bf16_t*)dres_act, accumulate, part, M, C);                      \
+    hipLaunchKernelGGL((ln_bwd_kernel<bf16_t, V>), dim3(nb), dim3(256), 0, s, (const bf16_t*)dy, \
+                       x, mean, rstd, w, dres, (bf16_t*)dres_act, accumulate, part, M, C);       \
   else                                                                                            \
-    hipLaunchKernelGGL((ln_bwd_kernel<float, V>), dim3(nb), dim3(256), 0, s, dy, x, mean, rstd,  \
-                       w, dres, (float*)dres_act, accumulate, part, M, C);
+    hipLaunchKernelGGL((ln_bwd_kernel<float, V>), dim3(nb), dim3(256), 0, s, (const float*)dy, x, \
+                       mean, rstd, w, dres, (float*)dres_act, accumulate, part, M, C);
   LN_DISPATCH(LNB)
 #undef LNB
   hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(3 * C, 32)), dim3(256), 0, s, part, nb,
