@@ -114,12 +114,14 @@ int to_bf16_launch(const float* p, bf16_t* o, int64_t n, hipStream_t s) {
 
 // Transposed bf16 copies of the weight matrices, so that the input-gradient
 // products dX = dY W read both operands along the reduction dimension.
-// One launch over a table of matrices; 64 x 64 tiles through LDS.
+// One launch over a table of matrices; 64 x 64 tiles through LDS, moved with
+// 16-byte loads and stores (a tile that is partial or not 8-aligned goes
+// element by element).
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src,
                                                              bf16_t* __restrict__ dst,
                                                              const TransposeJob* __restrict__ jobs,
                                                              int njobs) {
-  __shared__ bf16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
   int j = 0;
   while (j + 1 < njobs && (int)blockIdx.x >= jobs[j + 1].tile_begin) ++j;
   const TransposeJob job = jobs[j];
@@ -128,14 +130,35 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __res
   const int r0 = (t / tiles_c) * 64, c0 = (t % tiles_c) * 64;
   const bf16_t* S = src + job.src;
   bf16_t* D = dst + job.dst;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i / 64, c = i % 64;
-    if (r0 + r < job.rows && c0 + c < job.cols) tile[r][c] = S[(int64_t)(r0 + r) * job.cols + c0 + c];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int c = i / 64, r = i % 64;  // output row c, column r
-    if (r0 + r < job.rows && c0 + c < job.cols) D[(int64_t)(c0 + c) * job.ld + r0 + r] = tile[r][c];
+  const bool full = r0 + 64 <= job.rows && c0 + 64 <= job.cols && job.cols % 8 == 0 &&
+                    job.ld % 8 == 0 && job.src % 8 == 0 && job.dst % 8 == 0;
+  if (full) {
+    // 256 threads x 16 bytes cover 32 rows: two passes in, two passes out
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int r = (threadIdx.x >> 3) + 32 * pass, c8 = 8 * (threadIdx.x & 7);
+      *(uint4*)&tile[r][c8] = *(const uint4*)(S + (int64_t)(r0 + r) * job.cols + c0 + c8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int oc = (threadIdx.x >> 3) + 32 * pass, r8 = 8 * (threadIdx.x & 7);
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)tile[r8 + 2 * k][oc] | ((uint32_t)tile[r8 + 2 * k + 1][oc] << 16);
+      *(uint4*)(D + (int64_t)(c0 + oc) * job.ld + r0 + r8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int r = i / 64, c = i % 64;
+      if (r0 + r < job.rows && c0 + c < job.cols) tile[r][c] = S[(int64_t)(r0 + r) * job.cols + c0 + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int c = i / 64, r = i % 64;  // output row c, column r
+      if (r0 + r < job.rows && c0 + c < job.cols) D[(int64_t)(c0 + c) * job.ld + r0 + r] = tile[r][c];
+    }
   }
 }
 
