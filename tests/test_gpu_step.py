@@ -146,8 +146,8 @@ def test_tiny_fp32_ignored_targets_and_short_sequence():
 
 
 # ---------------------------------------------------------------- bf16 mode
-def bf16_step_parity(name, batch, T=None, seed=0):
-    dims = synth.WORKLOADS[name]
+def bf16_step_parity(name, batch, T=None, seed=0, **override):
+    dims = dict(synth.WORKLOADS[name], **override)
     T = T or dims["block_size"]
     case(f"{name} bf16 step B={batch} T={T}")
     params = synth.init_params(dims, seed=1337 + seed)
@@ -174,6 +174,35 @@ def test_gpt2_bf16_step_parity_two_sequences():
 
 def test_gpt2_bf16_ragged_short_batch():
     bf16_step_parity("gpt2", batch=3, T=200, seed=4)
+
+
+def test_gpt2_1p5b_width_two_layers_bf16_parity():
+    """The 1.5B shape's layer width (d 1600, 25 heads of 64, MLP 6400, padded
+    vocabulary) with two layers: every per-layer kernel at that shape; depth
+    only repeats them."""
+    bf16_step_parity("gpt2_1p5b", batch=1, T=256, seed=6, n_layer=2)
+
+
+def test_gpt2_bf16_gradient_accumulation():
+    """Two micro-batches with loss scale 1/2, the second accumulating into
+    the first's gradients, against the oracle on the two sequences as one
+    batch ("Let's reproduce GPT-2 (124M)", chapter "Gradient Accumulation")."""
+    dims = synth.WORKLOADS["gpt2"]
+    case("gpt2 bf16 accumulation 2 x B=1 T=128")
+    params = synth.init_params(dims, seed=1341)
+    idx, tgt = synth.tokens(dims, seed=1342, batch=2, T=128)
+    ref_loss, ref_g, _ = O.loss_and_grads(params, idx, tgt, ocfg(dims))
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=1, init_params=params)
+    losses = []
+    for i in range(2):
+        loss, _ = m.forward(*dev_tokens(idx[i:i + 1], tgt[i:i + 1]), loss_scale=0.5)
+        losses.append(float(loss.item()))
+        m.backward(zero_first=(i == 0))
+    torch.cuda.synchronize()
+    assert abs(0.5 * sum(losses) - ref_loss) <= 2e-2, (losses, ref_loss)
+    worst = check_grads(dims, to_np(m.grads), ref_g, min_cos=0.995)
+    print(f"lowest cosines {worst}", flush=True)
+    m.close()
 
 
 def test_gpt2_full_batch_sampled_logits_and_properties():

@@ -252,12 +252,32 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 #define MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 // row offset inside a 32x32 accumulator tile for register r of this lane
 #define ACC_ROW(r, lane) (8 * ((r) >> 2) + 4 * ((lane) >> 5) + ((r) & 3))
-#define FLASH_NS 3  // the key / query loops below are unrolled by exactly 3
+// ring depths (stages of 64 rows in LDS) of the three kernels
+#ifndef FLASH_FWD_NS
+#define FLASH_FWD_NS 3
+#endif
+#ifndef FLASH_DKDV_NS
+#define FLASH_DKDV_NS 3
+#endif
+#ifndef FLASH_DQ_NS
+#define FLASH_DQ_NS 3
+#endif
 #define TILE_ELEMS 4096
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <int N>
 using Slot = std::integral_constant<int, N>;
+// f(i + S, Slot<S>) for S = S0 .. NS-1 while i + S < n: the ring loop
+// unrolled by its depth, so every slot index is a compile-time constant
+template <int S, int NS, typename F>
+__device__ __forceinline__ void slot_steps(int i, int n, F& f) {
+  if constexpr (S < NS) {
+    if (i + S < n) {
+      f(i + S, Slot<S>());
+      slot_steps<S + 1, NS>(i, n, f);
+    }
+  }
+}
 
 // ---------------------------------------------------------------- forward
 // grid: (T/128 query blocks, heaviest first) x (B*H); 4 waves x 32 query
@@ -265,6 +285,7 @@ using Slot = std::integral_constant<int, N>;
 // the lane's own; P^T in the accumulator registers is directly the B operand
 // of O^T = V^T P^T.  The key loop is unrolled by the ring depth so that every
 // LDS address is a per-lane base plus an immediate offset.
+template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                            bf16_t* __restrict__ out,
                                                            float* __restrict__ lse, int B, int Tn,
@@ -327,10 +348,10 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
         for (int r = 0; r < 16; ++r)
           s[t][r] = (32 * t + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[t][r];
     }
-    float mb = fmaxf(s[0][0], s[1][0]);
+    float mb = fmax_fast(s[0][0], s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, fmaxf(s[0][r], s[1][r]));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64)) * sc;
+    for (int r = 1; r < 16; ++r) mb = fmax_fast(fmax_fast(mb, s[0][r]), s[1][r]);
+    mb = fmax_fast(mb, __shfl_xor(mb, 32, 64)) * sc;
     // The reference point m of the exponentials moves only when some
     // query's block maximum exceeds it by more than 8 (log2 units): the
     // probabilities then stay below 2^8 and the accumulator is rescaled
@@ -365,11 +386,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
           o[ht] = MFMA32(frag_rows(tV, 32 * ht, 2 * t + ss, lane), pb, o[ht]);
       }
   };
-  for (int kb = 0; kb < nkv; kb += FLASH_NS) {
-    step(kb, Slot<0>());
-    if (kb + 1 < nkv) step(kb + 1, Slot<1>());
-    if (kb + 2 < nkv) step(kb + 2, Slot<2>());
-  }
+  for (int kb = 0; kb < nkv; kb += FLASH_NS) slot_steps<0, FLASH_NS>(kb, nkv, step);
   const float lt = l + __shfl_xor(l, 32, 64);
   const float inv = 1.0f / lt;
   if (my_q < Tn) {
@@ -395,6 +412,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
 // operands are transposing reads of the dO and Q tiles.  Dg holds
 // rowsum(dO * O) at [0, B*H*T) and the row logsumexp times log2(e) at
 // [B*H*T, 2*B*H*T).
+template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
     bf16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
@@ -499,11 +517,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
       }
     }
   };
-  for (int qi = 0; qi < nq; qi += FLASH_NS) {
-    step(qi, Slot<0>());
-    if (qi + 1 < nq) step(qi + 1, Slot<1>());
-    if (qi + 2 < nq) step(qi + 2, Slot<2>());
-  }
+  for (int qi = 0; qi < nq; qi += FLASH_NS) slot_steps<0, FLASH_NS>(qi, nq, step);
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
@@ -555,6 +569,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
 // grid: (T/128 query blocks, heaviest first) x (B*H); 4 waves x 32 queries.
 // S^T = K Q^T and dP^T = V dO^T put one query per lane; dS^T is the B
 // operand of dQ^T += K^T dS^T, whose A operand is a transposing read of K.
+template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
     bf16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
@@ -641,11 +656,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
           dq[ht] = MFMA32(frag_rows(tK, 32 * ht, 2 * t + ss, lane), db, dq[ht]);
       }
   };
-  for (int kb = 0; kb < nkv; kb += FLASH_NS) {
-    step(kb, Slot<0>());
-    if (kb + 1 < nkv) step(kb + 1, Slot<1>());
-    if (kb + 2 < nkv) step(kb + 2, Slot<2>());
-  }
+  for (int kb = 0; kb < nkv; kb += FLASH_NS) slot_steps<0, FLASH_NS>(kb, nkv, step);
   if (my_q < Tn) {
     bf16_t* dQ = dqkv + ((int64_t)b * Tn + my_q) * ld + h * 64;
 #pragma unroll
@@ -695,7 +706,7 @@ int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int 
   if (hs * H != C || hs > 128) return -5;
   if (bf16 && hs == 64) {
     const int nqb = (Tn + 127) / 128;
-    hipLaunchKernelGGL(flash_fwd_kernel, dim3(nqb * B * H), dim3(256), 0, s,
+    hipLaunchKernelGGL(flash_fwd_kernel<FLASH_FWD_NS>, dim3(nqb * B * H), dim3(256), 0, s,
                        (const bf16_t*)qkv, (bf16_t*)out, lse, B, Tn, H, C);
   } else if (bf16) {
     hipLaunchKernelGGL(attn_fwd_generic<bf16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
@@ -731,9 +742,9 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
     if (flash) {
       const int nb = (Tn + 127) / 128;
       float* cp = cs_out ? cs_part : nullptr;
-      hipLaunchKernelGGL(flash_bwd_dkdv_kernel, dim3(nb * B * H), dim3(256), 0, s,
+      hipLaunchKernelGGL(flash_bwd_dkdv_kernel<FLASH_DKDV_NS>, dim3(nb * B * H), dim3(256), 0, s,
                          (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
-      hipLaunchKernelGGL(flash_bwd_dq_kernel, dim3(nb * B * H), dim3(256), 0, s,
+      hipLaunchKernelGGL(flash_bwd_dq_kernel<FLASH_DQ_NS>, dim3(nb * B * H), dim3(256), 0, s,
                          (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
       if (cs_out) {
         if (hipGetLastError() != hipSuccess) return -4;

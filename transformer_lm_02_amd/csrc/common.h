@@ -34,6 +34,13 @@ template <> struct Act<bf16_t> {
 template <typename T> __device__ __forceinline__ float ldf(const T* p) { return Act<T>::ld(p); }
 template <typename T> __device__ __forceinline__ void stf(T* p, float v) { Act<T>::st(p, v); }
 
+// max that propagates NaN (IEEE maximum; v_maximum3_f32 on gfx950).  Unlike
+// fmaxf it needs no canonicalisation of its inputs; for the finite and -inf
+// values it is used on, both agree.
+__device__ __forceinline__ float fmax_fast(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

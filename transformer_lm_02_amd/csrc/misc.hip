@@ -142,8 +142,9 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_bf16_kernel(
   float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < CE_BF_MAXU; ++i) {
-    mt = fmaxf(mt, fmaxf(fmaxf(bf_lo(cache[i].x), bf_hi(cache[i].x)), fmaxf(bf_lo(cache[i].y), bf_hi(cache[i].y))));
-    mt = fmaxf(mt, fmaxf(fmaxf(bf_lo(cache[i].z), bf_hi(cache[i].z)), fmaxf(bf_lo(cache[i].w), bf_hi(cache[i].w))));
+    mt = fmax_fast(fmax_fast(fmax_fast(mt, bf_lo(cache[i].x)), bf_hi(cache[i].x)), bf_lo(cache[i].y));
+    mt = fmax_fast(fmax_fast(fmax_fast(mt, bf_hi(cache[i].y)), bf_lo(cache[i].z)), bf_hi(cache[i].z));
+    mt = fmax_fast(fmax_fast(mt, bf_lo(cache[i].w)), bf_hi(cache[i].w));
   }
   // a thread without columns keeps mt = -inf and s_t = 0
   const float mref = mt == -INFINITY ? 0.f : mt;
