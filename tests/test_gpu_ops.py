@@ -130,9 +130,14 @@ def test_attention_fwd_bwd(bf, B, T, H, hs):
     dq, dk, dv = O.causal_attention_bwd(do, q, k, v, ref_p)
     ref_d = np.concatenate([merge_heads(t) for t in (dq, dk, dv)], axis=1)
     got_d = to_np(bd.op_attention_bwd(dqkv_dev, out, lse, to_dev(dout, dt), B, T, H))
+    scale = np.linalg.norm(ref_d)
     for i, name in enumerate("qkv"):
         g, r = got_d[:, i * C:(i + 1) * C], ref_d[:, i * C:(i + 1) * C]
-        if bf:
+        if np.linalg.norm(r) < 1e-9 * scale:
+            # a single key (T = 1): the softmax is constant, so the query
+            # gradient is zero up to rounding; its direction is noise
+            assert np.linalg.norm(g) < (1e-4 if bf else 1e-9) * scale, name
+        elif bf:
             assert cosine(g, r) > 0.999, name
             assert rel_err(g, r) < 3e-2, name
         else:

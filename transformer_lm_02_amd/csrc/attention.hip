@@ -77,39 +77,6 @@ __global__ void attn_bwd_dot(const T* __restrict__ out, const T* __restrict__ do
   }
 }
 
-// The same for head width 64 in bf16: one thread per 8 columns (16 bytes of
-// out and of dout), the 8 threads of a (row, head) pair combine by shuffles.
-__global__ __launch_bounds__(256) void attn_bwd_dot64_kernel(const bf16_t* __restrict__ out,
-                                                             const bf16_t* __restrict__ dout,
-                                                             const float* __restrict__ lse,
-                                                             float* __restrict__ D,
-                                                             float* __restrict__ L2, int Tn, int H,
-                                                             int64_t nchunk) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  float s = 0.f;
-  if (i < nchunk) {
-    const uint4 a = *(const uint4*)(out + 8 * i);
-    const uint4 g = *(const uint4*)(dout + 8 * i);
-    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, gv[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s = fmaf(__uint_as_float(av[j] << 16), __uint_as_float(gv[j] << 16), s);
-      s = fmaf(__uint_as_float(av[j] & 0xffff0000u), __uint_as_float(gv[j] & 0xffff0000u), s);
-    }
-  }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 4, 64);
-  if (i < nchunk && (i & 7) == 0) {
-    const int64_t row = i / (8 * H);  // b * Tn + t
-    const int hh = (int)((i / 8) % H);
-    const int64_t bb = row / Tn, t = row % Tn;
-    const int64_t o = (bb * H + hh) * Tn + t;
-    D[o] = s;
-    L2[o] = lse[o] * LOG2E;
-  }
-}
-
 template <typename T>
 __global__ void attn_bwd_dq_generic(const T* __restrict__ qkv, const float* __restrict__ lse,
                                     const float* __restrict__ D, const T* __restrict__ dout,
@@ -571,8 +538,9 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
 // operand of dQ^T += K^T dS^T, whose A operand is a transposing read of K.
 template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
-    const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
+    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ outp, const float* __restrict__ lse,
+    float* __restrict__ Dg, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dqkv,
+    float* __restrict__ cs_part, int B, int Tn, int H, int C) {
   __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
@@ -586,20 +554,38 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(base, (uint32_t)((int64_t)Tn * ld * 2));
   const int my_q = qw + (lane & 31);
 
+  // lanes l and l+32 hold the two halves of query row my_q: Q and dO as MFMA
+  // operands, and the attention output O to form D = rowsum(dO * O)
   bf16x8_t fq[4], fdo[4];
+  float dsum = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0), o = make_uint4(0, 0, 0, 0);
     if (my_q < Tn) {
+      const int64_t ro = ((int64_t)b * Tn + my_q) * C + h * 64 + 16 * ks + 8 * (lane >> 5);
       a = *(const uint4*)(base + (int64_t)my_q * ld + h * 64 + 16 * ks + 8 * (lane >> 5));
-      c = *(const uint4*)(dout + ((int64_t)b * Tn + my_q) * C + h * 64 + 16 * ks + 8 * (lane >> 5));
+      c = *(const uint4*)(dout + ro);
+      o = *(const uint4*)(outp + ro);
     }
     fq[ks] = *(bf16x8_t*)&a;
     fdo[ks] = *(bf16x8_t*)&c;
+    const uint32_t ov[4] = {o.x, o.y, o.z, o.w}, gv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dsum = fmaf(__uint_as_float(ov[j] << 16), __uint_as_float(gv[j] << 16), dsum);
+      dsum = fmaf(__uint_as_float(ov[j] & 0xffff0000u), __uint_as_float(gv[j] & 0xffff0000u), dsum);
+    }
   }
+  const float Dq = dsum + __shfl_xor(dsum, 32, 64);
   const float sc = LOG2E * 0.125f;
-  const float nL2 = my_q < Tn ? -Dg[bht + (int64_t)bh * Tn + my_q] : 0.f;
-  const float Dq = my_q < Tn ? Dg[(int64_t)bh * Tn + my_q] : 0.f;
+  const float L2q = my_q < Tn ? lse[(int64_t)bh * Tn + my_q] * LOG2E : 0.f;
+  const float nL2 = -L2q;
+  // D and the scaled logsumexp of every query row, for the key-side kernel
+  // that runs next
+  if (lane < 32 && my_q < Tn) {
+    Dg[(int64_t)bh * Tn + my_q] = Dq;
+    Dg[bht + (int64_t)bh * Tn + my_q] = L2q;
+  }
   f32x16_t dq[2] = {zero16(), zero16()};
   const int nkv = (min(Tn, q0 + 128) + 63) / 64;
 #pragma unroll
@@ -731,20 +717,18 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
   const int64_t rows = (int64_t)B * H * Tn;
   if (bf16) {
     const bool flash = hs == 64;
-    if (flash) {
-      const int64_t nchunk = (int64_t)B * Tn * C / 8;
-      hipLaunchKernelGGL(attn_bwd_dot64_kernel, dim3((unsigned)cdiv(nchunk, 256)), dim3(256), 0, s,
-                         (const bf16_t*)out, (const bf16_t*)dout, lse, D, D + rows, Tn, H, nchunk);
-    } else {
+    if (!flash)
       hipLaunchKernelGGL(attn_bwd_dot<bf16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
                          (const bf16_t*)out, (const bf16_t*)dout, lse, D, nullptr, B, Tn, H, C);
-    }
     if (flash) {
+      // the query-side kernel forms D and the scaled logsumexp of its rows,
+      // so it runs first
       const int nb = (Tn + 127) / 128;
       float* cp = cs_out ? cs_part : nullptr;
-      hipLaunchKernelGGL(flash_bwd_dkdv_kernel<FLASH_DKDV_NS>, dim3(nb * B * H), dim3(256), 0, s,
-                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
       hipLaunchKernelGGL(flash_bwd_dq_kernel<FLASH_DQ_NS>, dim3(nb * B * H), dim3(256), 0, s,
+                         (const bf16_t*)qkv, (const bf16_t*)out, lse, D, (const bf16_t*)dout,
+                         (bf16_t*)dqkv, cp, B, Tn, H, C);
+      hipLaunchKernelGGL(flash_bwd_dkdv_kernel<FLASH_DKDV_NS>, dim3(nb * B * H), dim3(256), 0, s,
                          (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
       if (cs_out) {
         if (hipGetLastError() != hipSuccess) return -4;

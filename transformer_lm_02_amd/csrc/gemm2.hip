@@ -47,6 +47,7 @@ struct Stage {
   static_assert(KC || CPR % 16 == 0, "transposed tile needs whole 16-chunk bank groups");
   uint32_t voff[LOADS];
   int kofs[LOADS];
+  int kfast;  // k-tiles ending at or before this k take the scalar-offset path
 
   // k-contiguous: LDS [ROWS][BK]; chunk c of row r at position c ^ sw(r)
   //   with sw(r) = (r>>1)&7 for BK 64, (r>>2)&3 for BK 32 (conflict-free
@@ -57,7 +58,13 @@ struct Stage {
   __device__ __forceinline__ static int swz(int r) {
     return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
   }
-  __device__ __forceinline__ void init(int row0, int ld, int lane, int wave) {
+  // krows: rows of an m/n-contiguous operand (reads at or past it return 0)
+  __device__ __forceinline__ void init(int row0, int ld, int lane, int wave, int K, int krows) {
+    // A k-contiguous tile's rows past the operand start beyond its buffer, so
+    // their loads are out of range whatever k offset is added.  An
+    // m/n-contiguous tile needs every column inside the row pitch for that.
+    if constexpr (KC) kfast = K;
+    else kfast = row0 + ROWS <= ld ? (K < krows ? K : krows) : 0;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int q = i * 4 + wave;
@@ -73,8 +80,21 @@ struct Stage {
       }
     }
   }
+  // lds and wave are wave-uniform.  A k-tile wholly in range carries its k
+  // offset in the scalar offset operand, so a load needs no vector ALU work;
+  // a k-tile that crosses K (or the rows of an m/n-contiguous operand) sends
+  // each lane's chunks past the end to an offset beyond the buffer instead.
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, int kt, int ld,
                                         int K, int wave) const {
+    if ((kt + 1) * BK <= kfast) {
+      const uint32_t soff =
+          KC ? (uint32_t)kt * (uint32_t)(BK * 2) : (uint32_t)kt * (uint32_t)(BK * ld) * 2u;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, AS3(lds + (i * 4 + wave) * 512), 16,
+                                                 (int)voff[i], (int)soff, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int q = i * 4 + wave;
@@ -240,7 +260,8 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   constexpr int LDS_ELEMS = LDS_ELEMS_RING > LDS_ELEMS_EPI ? LDS_ELEMS_RING : LDS_ELEMS_EPI;
   __shared__ __attribute__((aligned(1024))) bf16_t lds[LDS_ELEMS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   tile_coords2(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -256,8 +277,8 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, b_bytes);
   SA sa;
   SB sb;
-  sa.init(m0, p.lda, lane, wave);
-  sb.init(n0, p.ldb, lane, wave);
+  sa.init(m0, p.lda, lane, wave, p.K, p.ka_rows);
+  sb.init(n0, p.ldb, lane, wave, p.K, p.kb_rows);
 
   f32x16_t acc[TM][TN];
 #pragma unroll

@@ -56,15 +56,34 @@ __global__ void embed_bwd_wpe_kernel(const float* __restrict__ dx, float* __rest
 
 // ---------------------------------------------------------------- cross-entropy
 // count of targets >= 0 (ignore_index = -1, "nanoGPT" Part IV Stage 4)
-__global__ void count_valid_kernel(const int32_t* __restrict__ tgt, int N, int* __restrict__ out) {
-  __shared__ int red[4];
+// One workgroup of 1024 threads: 16-byte loads where the targets are 16-byte
+// aligned, so each thread has only a few loads in flight instead of a long
+// chain of dependent round trips.
+#define RED_THREADS 1024
+__global__ __launch_bounds__(RED_THREADS) void count_valid_kernel(const int32_t* __restrict__ tgt, int N,
+                                                                  int* __restrict__ out) {
+  __shared__ int red[RED_THREADS / 64];
   int c = 0;
-  for (int i = threadIdx.x; i < N; i += blockDim.x) c += tgt[i] >= 0;
+  int done = 0;
+  if (((uintptr_t)tgt & 15) == 0) {
+    const int n4 = N >> 2;
+#pragma unroll 4
+    for (int i = threadIdx.x; i < n4; i += RED_THREADS) {
+      const int4 v = ((const int4*)tgt)[i];
+      c += (v.x >= 0) + (v.y >= 0) + (v.z >= 0) + (v.w >= 0);
+    }
+    done = n4 << 2;
+  }
+  for (int i = done + threadIdx.x; i < N; i += RED_THREADS) c += tgt[i] >= 0;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
   __syncthreads();
-  if (threadIdx.x == 0) *out = red[0] + red[1] + red[2] + red[3];
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int w = 0; w < RED_THREADS / 64; ++w) t += red[w];
+    *out = t;
+  }
 }
 
 // One row of logits per workgroup, read once into registers:
@@ -208,17 +227,32 @@ __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
 }
 
 // loss = sum(row_loss) / n_valid, single workgroup, fixed order.
-__global__ void loss_finalize_kernel(const float* __restrict__ row_loss, int N,
-                                     const int* __restrict__ n_valid, float* __restrict__ loss) {
-  __shared__ double red[4];
+// mean of the row losses over the valid rows, summed in fp64 in a fixed
+// order (thread strides, then waves in order)
+__global__ __launch_bounds__(RED_THREADS) void loss_finalize_kernel(const float* __restrict__ row_loss, int N,
+                                                                    const int* __restrict__ n_valid,
+                                                                    float* __restrict__ loss) {
+  __shared__ double red[RED_THREADS / 64];
   double s = 0.0;
-  for (int i = threadIdx.x; i < N; i += 256) s += row_loss[i];
+  int done = 0;
+  if (((uintptr_t)row_loss & 15) == 0) {
+    const int n4 = N >> 2;
+#pragma unroll 4
+    for (int i = threadIdx.x; i < n4; i += RED_THREADS) {
+      const float4 v = ((const float4*)row_loss)[i];
+      s += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+    }
+    done = n4 << 2;
+  }
+  for (int i = done + threadIdx.x; i < N; i += RED_THREADS) s += row_loss[i];
   s = wave_sum_d(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < RED_THREADS / 64; ++w) t += red[w];
     const int nv = *n_valid;
-    *loss = nv > 0 ? (float)((red[0] + red[1] + red[2] + red[3]) / nv) : 0.f;
+    *loss = nv > 0 ? (float)(t / nv) : 0.f;
   }
 }
 
@@ -282,7 +316,7 @@ int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dw
 }
 
 int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s) {
-  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(256), 0, s, tgt, N, out);
+  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(RED_THREADS), 0, s, tgt, N, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -302,7 +336,7 @@ int cross_entropy_launch(bool bf16, void* logits, const int32_t* tgt, float* row
 
 int loss_finalize_launch(const float* row_loss, int N, const int* n_valid, float* loss,
                          hipStream_t s) {
-  hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, s, row_loss, N, n_valid, loss);
+  hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(RED_THREADS), 0, s, row_loss, N, n_valid, loss);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
