@@ -711,7 +711,8 @@ int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int 
 // least max(B * cdiv(Tn, 128), colsum_part_rows(B * Tn)) x 3C elements.
 int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
-                         float* cs_part, float* cs_out, int cs_beta, hipStream_t s) {
+                         float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
+                         ColsumJob* defer) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
   const int64_t rows = (int64_t)B * H * Tn;
@@ -732,6 +733,14 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
                          (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
       if (cs_out) {
         if (hipGetLastError() != hipSuccess) return -4;
+        if (defer) {
+          *defer = ColsumJob();
+          defer->part = cs_part;
+          defer->out[0] = cs_out;
+          defer->nrow = B * nb;
+          defer->ncol = defer->seg = 3 * C;
+          return 0;
+        }
         return colsum_finalize_launch(cs_part, B * nb, 3 * C, cs_out, cs_beta, s);
       }
     } else {

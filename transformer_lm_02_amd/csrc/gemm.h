@@ -13,6 +13,16 @@ enum GemmEpi {
   EPI_ACCUM = 5     // out_f32[m][n] = (beta ? out_f32[m][n] : 0) + acc
 };
 
+// A column-sum finalize left for later: out[k][i] = (beta ? out[k][i] : 0)
+// + sum over the nrow rows of part [nrow][ncol] at column k * seg + i
+// (k = 0, 1, 2; a null out[k] skips its columns).  Producers fill one when
+// handed a non-null ColsumJob*, so that one launch can finish many.
+struct ColsumJob {
+  const float* part = nullptr;
+  float* out[3] = {nullptr, nullptr, nullptr};
+  int nrow = 0, ncol = 0, seg = 0;
+};
+
 struct GemmEpiArgs {
   void* out = nullptr;
   void* out2 = nullptr;
@@ -28,6 +38,9 @@ struct GemmEpiArgs {
   float* cs_part = nullptr;
   float* cs_out = nullptr;
   int cs_beta = 0;
+  // non-null: the pipelined kernel's column sums are left in cs_part and
+  // described here instead of finalized (part = nullptr if it finalized)
+  ColsumJob* cs_defer = nullptr;
 };
 
 // A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]; likewise B(n,k).

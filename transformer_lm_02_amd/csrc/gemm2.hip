@@ -515,7 +515,17 @@ int run2(Gemm2Args p, hipStream_t s) {
   p.tiles_n = (int)cdiv(p.N, BN);
   hipLaunchKernelGGL((gemm2_kernel<BM, BN, AK, BKC, EPI, NS, BK, OCC>),
                      dim3(p.tiles_m * p.tiles_n, p.ksplit), dim3(256), 0, s, p);
-  if (p.e.cs_part) return colsum_finalize_launch(p.e.cs_part, p.tiles_m, p.N, p.e.cs_out, p.e.cs_beta, s);
+  if (p.e.cs_part) {
+    if (ColsumJob* d = p.e.cs_defer) {
+      *d = ColsumJob();
+      d->part = p.e.cs_part;
+      d->out[0] = p.e.cs_out;
+      d->nrow = p.tiles_m;
+      d->ncol = d->seg = p.N;
+      return hipGetLastError() == hipSuccess ? 0 : -4;
+    }
+    return colsum_finalize_launch(p.e.cs_part, p.tiles_m, p.N, p.e.cs_out, p.e.cs_beta, s);
+  }
   return 0;
 }
 

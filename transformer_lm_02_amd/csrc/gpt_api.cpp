@@ -108,6 +108,7 @@ struct WsOff {
   size_t x_final, lnf_mean, lnf_rstd, lnf, logits, row_loss, nvalid, flags, scal;
   size_t dres, dres_act, dln, dbig, dO, Dbuf, ln_part, cs_part, norm_part, chunks, splitk;
   int64_t splitk_bytes;
+  int64_t ln_part_elems, cs_part_elems;  // one slice of each (several slices kept)
   size_t total;
   int nchunks;
   int64_t vi;  // logits row pitch: padded_vocab rounded up to 64
@@ -183,10 +184,16 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   w.dbig = take(M * 4 * d * es);
   w.dO = take(M * d * es);
   w.Dbuf = take(2 * M * H * 4);
-  w.ln_part = take((int64_t)layernorm_bwd_part_rows((int)M) * 3 * d * 4);
-  // column-sum partials: at most one row per 128 tokens (GEMM row tiles,
-  // attention blocks) or per colsum_part_rows block
-  w.cs_part = take(std::max<int64_t>(cdiv(M, 128), colsum_part_rows((int)M)) * 4 * d * 4);
+  // Column-sum partials of the backward, one slice per producer so that all
+  // of them are finished by one launch at its end: a LayerNorm slice per
+  // LayerNorm (2 per layer + the final one); a column-sum slice (at most one
+  // row per 128 tokens, GEMM row tiles or attention blocks, or per
+  // colsum_part_rows block) for the MLP expansion bias and the q|k|v bias of
+  // every layer.
+  w.ln_part_elems = (int64_t)layernorm_bwd_part_rows((int)M) * 3 * d;
+  w.ln_part = take((2 * c.n_layer + 1) * w.ln_part_elems * 4);
+  w.cs_part_elems = std::max<int64_t>(cdiv(M, 128), colsum_part_rows((int)M)) * 4 * d;
+  w.cs_part = take(2 * c.n_layer * w.cs_part_elems * 4);
   w.norm_part = take((int64_t)adamw_norm_blocks() * 8);
   w.splitk_bytes = bf ? gemm_splitk_bytes(4 * d, d) : 0;
   w.splitk = take(w.splitk_bytes);
@@ -435,8 +442,17 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
   void* dres_act = h->at(w.dres_act);
   void* dln = h->at(w.dln);  // input gradients of the LayerNorms, in the activation type
   void* dbig = h->at(w.dbig);
-  float* ln_part = h->at<float>(w.ln_part);
-  float* cs_part = h->at<float>(w.cs_part);
+  // the column-sum partials each producer leaves (bias and LayerNorm weight
+  // gradients), finished together at the end
+  std::vector<ColsumJob> jobs;
+  jobs.reserve(4 * c.n_layer + 1);
+  int n_ln = 0, n_cs = 0;
+  auto ln_slice = [&]() { return h->at<float>(w.ln_part) + (n_ln++) * w.ln_part_elems; };
+  auto cs_slice = [&]() { return h->at<float>(w.cs_part) + (n_cs++) * w.cs_part_elems; };
+  auto keep = [&](const ColsumJob& j) {
+    if (j.part) jobs.push_back(j);
+  };
+  ColsumJob job;
   float* sk = w.splitk_bytes ? h->at<float>(w.splitk) : nullptr;
   const int64_t skb = w.splitk_bytes;
 
@@ -462,9 +478,10 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
                      c.padded_vocab, e, s));
   }
   CK(layernorm_bwd_launch(bf, dln, h->at<float>(w.x_final), h->at<float>(w.lnf_mean),
-                          h->at<float>(w.lnf_rstd), h->P(p.lnfw), dres, dres_act, 0, ln_part,
+                          h->at<float>(w.lnf_rstd), h->P(p.lnfw), dres, dres_act, 0, ln_slice(),
                           h->G(p.lnfw), h->G(p.lnfb), h->G(p.layer[c.n_layer - 1].mprojb), beta, M,
-                          d, s));
+                          d, s, &(job = ColsumJob())));
+  keep(job);
   for (int l = c.n_layer - 1; l >= 0; --l) {
     const WsLayer& L = w.layer[l];
     const LayerOff& P = p.layer[l];
@@ -478,15 +495,17 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     e.out = dbig;
     e.aux = h->at(L.dgelu);
     e.ldc = 4 * d;
-    e.cs_part = cs_part;  // MLP expansion bias: db = colsum(du), formed alongside
+    e.cs_part = cs_slice();  // MLP expansion bias: db = colsum(du), formed alongside
     e.cs_out = h->G(P.fcb);
     e.cs_beta = beta;
+    e.cs_defer = &(job = ColsumJob());
     if (bf)
       CK(gemm_launch(bf, true, true, EPI_GELU_BWD, dres_act, d, h->WT(L.mprojT), d, M, 4 * d, d, d,
                      d, e, s));
     else
       CK(gemm_launch(bf, true, false, EPI_GELU_BWD, dres_act, d, h->W(P.mprojw), 4 * d, M, 4 * d, d,
                      d, d, e, s));
+    keep(job);
     // MLP expansion: dW (+)= du^T ln2 ; dln2 = du Wfc
     e = GemmEpiArgs();
     e.out = h->G(P.fcw);
@@ -503,8 +522,10 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
       CK(gemm_launch(bf, true, false, EPI_ACT, dbig, 4 * d, h->W(P.fcw), d, M, d, 4 * d, 4 * d,
                      4 * d, e, s));
     CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_mid), h->at<float>(L.ln2_mean),
-                            h->at<float>(L.ln2_rstd), h->P(P.ln2w), dres, dres_act, 1, ln_part,
-                            h->G(P.ln2w), h->G(P.ln2b), h->G(P.aprojb), beta, M, d, s));
+                            h->at<float>(L.ln2_rstd), h->P(P.ln2w), dres, dres_act, 1, ln_slice(),
+                            h->G(P.ln2w), h->G(P.ln2b), h->G(P.aprojb), beta, M, d, s,
+                            &(job = ColsumJob())));
+    keep(job);
     // attention projection: dW (+)= dres^T att ; datt = dres Wa
     e = GemmEpiArgs();
     e.out = h->G(P.aprojw);
@@ -521,7 +542,9 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
     // attention; the fused projection's bias gradient db = colsum(dqkv) is
     // formed by the attention backward
     CK(attention_bwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), h->at(w.dO), dbig,
-                            h->at<float>(w.Dbuf), B, T, H, d, cs_part, h->G(P.attnb), beta, s));
+                            h->at<float>(w.Dbuf), B, T, H, d, cs_slice(), h->G(P.attnb), beta, s,
+                            &(job = ColsumJob())));
+    keep(job);
     // fused q|k|v projection: dW (+)= dqkv^T ln1 ; dln1 = dqkv Wqkv
     e = GemmEpiArgs();
     e.out = h->G(P.attnw);
@@ -538,10 +561,12 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
       CK(gemm_launch(bf, true, false, EPI_ACT, dbig, 3 * d, h->W(P.attnw), d, M, d, 3 * d, 3 * d,
                      3 * d, e, s));
     CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_in), h->at<float>(L.ln1_mean),
-                            h->at<float>(L.ln1_rstd), h->P(P.ln1w), dres, dres_act, 1, ln_part,
+                            h->at<float>(L.ln1_rstd), h->P(P.ln1w), dres, dres_act, 1, ln_slice(),
                             h->G(P.ln1w), h->G(P.ln1b), l > 0 ? h->G(p.layer[l - 1].mprojb) : nullptr,
-                            beta, M, d, s));
+                            beta, M, d, s, &(job = ColsumJob())));
+    keep(job);
   }
+  CK(colsum_finalize_group_launch(jobs.data(), (int)jobs.size(), beta, s));
   // embeddings: dwte[idx] += dx ; dwpe[t] (+)= sum_b dx
   CK(embed_bwd_launch(h->idx, dres, h->G(p.wte), h->G(p.wpe), B, T, c.block_size, d,
                       c.padded_vocab, beta, s));

@@ -25,9 +25,11 @@ int transpose_bf16_launch(const bf16_t* src, bf16_t* dst, const TransposeJob* jo
 
 int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
                          int C, hipStream_t s);
+// defer (optional): see ColsumJob; honoured by the head-width-64 bf16 path
 int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
-                         float* cs_part, float* cs_out, int cs_beta, hipStream_t s);
+                         float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
+                         ColsumJob* defer = nullptr);
 
 int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s);
@@ -36,7 +38,7 @@ int layernorm_bwd_part_rows(int M);
 int layernorm_bwd_launch(bool bf16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
-                         int beta, int M, int C, hipStream_t s);
+                         int beta, int M, int C, hipStream_t s, ColsumJob* defer = nullptr);
 
 int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, float* x, int M,
                      int Tn, int C, int Vp, int* flags, hipStream_t s);
@@ -54,6 +56,10 @@ int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, in
                            hipStream_t s);
 int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* out, int beta,
                   hipStream_t s);
+// finishes n ColsumJobs (each ncol % 4 == 0) in one launch per
+// COLSUM_GROUP_MAX jobs
+#define COLSUM_GROUP_MAX 56
+int colsum_finalize_group_launch(const ColsumJob* jobs, int n, int beta, hipStream_t s);
 
 int adamw_norm_blocks();
 int adamw_launch(float* p, const float* g, float* m, float* v, bf16_t* shadow, int64_t n,

@@ -10,7 +10,10 @@
 // bf16/fp32 copy for the next matrix product, and produces per-block column
 // partial sums of dy*xhat (dw), dy (db) and of the updated residual gradient
 // (the bias gradient of the projection whose output is that residual).
+#include <algorithm>
+
 #include "common.h"
+#include "kernels.h"
 
 #define LN_EPS 1e-5f
 #define LN_MAXV_MAX 8  // float4 per lane: C <= 2048
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
 // sums part[blk][3][C] (dw, db, residual-gradient column sum).  Each wave
 // takes every 4th row of its block and loads its next row (dy, x and, when
 // accumulating, the old residual gradient) while it works on the current one.
-#define LN_BWD_ROWS 16
+#define LN_BWD_ROWS 32
 template <typename T, int LN_MAXV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
     const T* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
@@ -212,13 +215,12 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
 // groups, each with 4 independent loads in flight, then an LDS reduction.
 // Column c goes to out_k[c % seg] with k = c / seg (seg % 4 == 0); with beta
 // the sum is added to the output, else it replaces it.
-__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __restrict__ part,
-                                                              int nrow, int ncol, int seg,
-                                                              float* out0, float* out1,
-                                                              float* out2, int beta) {
-  __shared__ float4 red[32][8];
+__device__ __forceinline__ void colsum_finalize_block(const float* __restrict__ part, int nrow,
+                                                      int ncol, int seg, float* out0, float* out1,
+                                                      float* out2, int beta, int bx,
+                                                      float4 (*red)[8]) {
   const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
-  const int c = blockIdx.x * 32 + 4 * tx;
+  const int c = bx * 32 + 4 * tx;
   float4 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __res
   red[ty][tx] = t;
   __syncthreads();
   if (threadIdx.x < 32) {
-    // thread j sums column blockIdx.x * 32 + j over the 32 row groups
-    const int j = threadIdx.x, cc = blockIdx.x * 32 + j;
+    // thread j sums column bx * 32 + j over the 32 row groups
+    const int j = threadIdx.x, cc = bx * 32 + j;
     const float* rf = (const float*)red;
     float v = 0.f;
 #pragma unroll 8
@@ -256,6 +258,31 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __res
       if (o) o[i] = (beta ? o[i] : 0.f) + v;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __restrict__ part,
+                                                              int nrow, int ncol, int seg,
+                                                              float* out0, float* out1,
+                                                              float* out2, int beta) {
+  __shared__ float4 red[32][8];
+  colsum_finalize_block(part, nrow, ncol, seg, out0, out1, out2, beta, blockIdx.x, red);
+}
+
+// Several finalizes in one launch: job j owns blocks [blk0[j], blk0[j+1]).
+// The table travels in the kernel arguments.
+struct ColsumGroupArgs {
+  ColsumJob job[COLSUM_GROUP_MAX];
+  int blk0[COLSUM_GROUP_MAX + 1];
+  int n, beta;
+};
+__global__ __launch_bounds__(256) void colsum_finalize_group_kernel(ColsumGroupArgs a) {
+  __shared__ float4 red[32][8];
+  const int bx = blockIdx.x;
+  int j = 0;
+  while (j + 1 < a.n && a.blk0[j + 1] <= bx) ++j;
+  const ColsumJob& jb = a.job[j];
+  colsum_finalize_block(jb.part, jb.nrow, jb.ncol, jb.seg, jb.out[0], jb.out[1], jb.out[2], a.beta,
+                        bx - a.blk0[j], red);
 }
 
 // per-lane float4 count: C / 4 / 64 rounded up, so registers track the width
@@ -294,7 +321,7 @@ int layernorm_bwd_part_rows(int M) { return (int)cdiv(M, LN_BWD_ROWS); }
 int layernorm_bwd_launch(bool bf16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
-                         int beta, int M, int C, hipStream_t s) {
+                         int beta, int M, int C, hipStream_t s, ColsumJob* defer) {
   if (C % 4 || C > LN_MAXV_MAX * 256) return -5;
   const int nb = (int)cdiv(M, LN_BWD_ROWS);
 #define LNB(V)                                                                                   \
@@ -306,9 +333,40 @@ int layernorm_bwd_launch(bool bf16, const void* dy, const float* x, const float*
                        mean, rstd, w, dres, (float*)dres_act, accumulate, part, M, C);
   LN_DISPATCH(LNB)
 #undef LNB
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(3 * C, 32)), dim3(256), 0, s, part, nb,
-                     3 * C, C, dw, db, bias_grad, beta);
+  if (defer) {
+    defer->part = part;
+    defer->out[0] = dw;
+    defer->out[1] = db;
+    defer->out[2] = bias_grad;
+    defer->nrow = nb;
+    defer->ncol = 3 * C;
+    defer->seg = C;
+  } else {
+    hipLaunchKernelGGL(colsum_finalize_kernel, dim3(cdiv(3 * C, 32)), dim3(256), 0, s, part, nb,
+                       3 * C, C, dw, db, bias_grad, beta);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int colsum_finalize_group_launch(const ColsumJob* jobs, int n, int beta, hipStream_t s) {
+  for (int j0 = 0; j0 < n; j0 += COLSUM_GROUP_MAX) {
+    ColsumGroupArgs a;
+    a.n = std::min(n - j0, COLSUM_GROUP_MAX);
+    a.beta = beta;
+    int nblk = 0;
+    for (int j = 0; j < a.n; ++j) {
+      const ColsumJob& jb = jobs[j0 + j];
+      if (!jb.part || jb.ncol % 4 || jb.seg < 1) return -5;
+      a.job[j] = jb;
+      a.blk0[j] = nblk;
+      nblk += (int)cdiv(jb.ncol, 32);
+    }
+    a.blk0[a.n] = nblk;
+    if (nblk > 0)
+      hipLaunchKernelGGL(colsum_finalize_group_kernel, dim3(nblk), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return -4;
+  }
+  return 0;
 }
 
 int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
