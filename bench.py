@@ -169,7 +169,7 @@ def cpu_baseline(dims, seed=1338):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -213,17 +213,21 @@ def main():
         step(i)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event per step boundary on the library's stream: no host sync inside
+    # the timed window; per-step times give the spread
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(s)
+    ev[0].record(s)
     for i in range(args.steps):
         step(args.warmup + i)
-    e1.record(s)
+        ev[i + 1].record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     loss = float(model.scalars[0].item())
     norm = float(model.scalars[1].item())
     tokens = B * T
@@ -245,7 +249,9 @@ def main():
     out = {
         "metric": "train tokens/sec + ms/step + MFU, GPT-2 124M bf16 B=16 T=1024, 1 MI355X",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "mfu": round(mfu, 4),
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_per_step_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
+        "mfu": round(mfu, 4),
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": round(value / A100_TOKENS_PER_S, 3),
         "baseline": "pages' 90 ms/step = ~182,000 tokens/s on one A100 SXM (context)",
