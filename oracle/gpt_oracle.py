@@ -1,4 +1,4 @@
-"""Plain CPU oracle for one GPT-2 training step.
+"""Plain CPU oracle for one GPT-2 training step, and for sampling from the model.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this module: only the test suite, the smoke check of the build entry
@@ -38,6 +38,9 @@ Readings taken where the pages are silent (each repeated where it is used):
     with eps added outside the square root; bias correction uses the 1-based
     optimizer step t.
   * Clipping: coef = min(1, max_norm / (norm + 1e-6)), applied always.
+  * Sampling: the top-k cutoff keeps values equal to the k-th largest;
+    top_k <= 0 keeps all; the multinomial draw is by inverse CDF in token-id
+    order with a uniform supplied by the caller.
 """
 from __future__ import annotations
 
@@ -439,3 +442,51 @@ def flops_per_token(cfg: Config, T: int) -> int:
     6N + 12*L*H*Q*T, N the non-embedding parameter count, Q the head width."""
     N = num_params(cfg, non_embedding=True)
     return 6 * N + 12 * cfg.n_layer * cfg.n_head * cfg.head_dim * T
+
+
+# --------------------------------------------------------------------------
+# generation
+# --------------------------------------------------------------------------
+def topk_sample(logits_row, vocab_size, temperature, top_k, u, dtype=np.float64):
+    """One draw of GPT.generate ([NG] Part IV, "one generation (sample.py +
+    model.py, generate)"): the last position's logits over the real
+    vocabulary divided by the temperature; every logit below the top-k
+    cutoff (the k-th largest value) removed, values equal to it kept;
+    softmax; one multinomial draw.
+
+    Readings: top_k <= 0 keeps every id (the pages' cutoff is optional);
+    the draw is by inverse CDF in token-id order with the uniform u in
+    [0, 1) supplied by the caller, i.e. the first id whose cumulative
+    probability exceeds u (the pages name torch.multinomial, whose internal
+    algorithm they do not give; every exact sampler has this distribution).
+    Returns (token, probs over the first vocab_size ids).
+    """
+    z = np.asarray(logits_row, dtype=dtype)[:vocab_size] / dtype(temperature)
+    if 0 < top_k < vocab_size:
+        cutoff = np.sort(z)[vocab_size - top_k]  # the k-th largest
+        z = np.where(z < cutoff, -np.inf, z)
+    p = np.exp(z - z.max())
+    p = p / p.sum()
+    c = np.cumsum(p)
+    tok = int(np.searchsorted(c, u, side="right"))
+    return min(tok, vocab_size - 1), p
+
+
+def generate(flat_params, idx, cfg: Config, n_new, temperature, top_k, us,
+             dtype=np.float64):
+    """GPT.generate of [NG] Part IV ("one generation"): per new token, crop
+    the context to its last block_size tokens, run the whole forward (no
+    cache), take the last position's logits and draw with topk_sample;
+    append and repeat.  us: uniforms (B, n_new).  Returns (tokens (B,
+    T0 + n_new), last-position logits (n_new, B, Vp))."""
+    idx = np.asarray(idx)
+    steps = []
+    for i in range(n_new):
+        ctx = idx[:, -cfg.block_size:]
+        logits, _, _ = forward(flat_params, ctx, None, cfg, dtype=dtype)
+        last = logits[:, -1, :]
+        steps.append(last)
+        nxt = [topk_sample(last[b], cfg.vocab_size, temperature, top_k, us[b, i], dtype)[0]
+               for b in range(idx.shape[0])]
+        idx = np.concatenate([idx, np.asarray(nxt, dtype=idx.dtype)[:, None]], axis=1)
+    return idx, np.stack(steps)

@@ -120,6 +120,53 @@ def _decay_all(cfg, dtype=np.float64):
 
 _orig_ce, _orig_adamw, _orig_lr = O.cross_entropy, O.adamw, O.get_lr
 
+
+def _sample_drops_ties(logits_row, vocab_size, temperature, top_k, u, dtype=np.float64):
+    z = np.asarray(logits_row, dtype=dtype)[:vocab_size] / temperature
+    if 0 < top_k < vocab_size:
+        cutoff = np.sort(z)[vocab_size - top_k]
+        z = np.where(z <= cutoff, -np.inf, z)  # also removes the k-th largest
+        if np.isinf(z).all():
+            z[np.argmax(np.asarray(logits_row)[:vocab_size])] = 0.0
+    p = np.exp(z - z.max())
+    p = p / p.sum()
+    return min(int(np.searchsorted(np.cumsum(p), u, side="right")), vocab_size - 1), p
+
+
+def _sample_times_temperature(logits_row, vocab_size, temperature, top_k, u, dtype=np.float64):
+    return _orig_sample(np.asarray(logits_row, dtype) * temperature * temperature, vocab_size,
+                        temperature, top_k, u, dtype)
+
+
+def _sample_left_boundary(logits_row, vocab_size, temperature, top_k, u, dtype=np.float64):
+    z = np.asarray(logits_row, dtype=dtype)[:vocab_size] / temperature
+    if 0 < top_k < vocab_size:
+        z = np.where(z < np.sort(z)[vocab_size - top_k], -np.inf, z)
+    p = np.exp(z - z.max())
+    p = p / p.sum()
+    return min(int(np.searchsorted(np.cumsum(p), u, side="left")), vocab_size - 1), p
+
+
+def _sample_padded_vocab(logits_row, vocab_size, temperature, top_k, u, dtype=np.float64):
+    return _orig_sample(logits_row, len(logits_row), temperature, top_k, u, dtype)
+
+
+def _generate_first_position(flat_params, idx, cfg, n_new, temperature, top_k, us,
+                             dtype=np.float64):
+    idx = np.asarray(idx)
+    steps = []
+    for i in range(n_new):
+        logits, _, _ = O.forward(flat_params, idx[:, -cfg.block_size:], None, cfg, dtype=dtype)
+        last = logits[:, 0, :]
+        steps.append(last)
+        nxt = [_orig_sample(last[b], cfg.vocab_size, temperature, top_k, us[b, i], dtype)[0]
+               for b in range(idx.shape[0])]
+        idx = np.concatenate([idx, np.asarray(nxt, dtype=idx.dtype)[:, None]], axis=1)
+    return idx, np.stack(steps)
+
+
+_orig_sample = O.topk_sample
+
 MUTANTS = [
     ("layernorm_fwd", _ln_unbiased),
     ("layernorm_bwd", _ln_bwd_no_mean_term),
@@ -136,6 +183,11 @@ MUTANTS = [
     ("get_lr", _lr_warmup_from_zero),
     ("clip_coef", _clip_always),
     ("decay_mask", _decay_all),
+    ("topk_sample", _sample_drops_ties),
+    ("topk_sample", _sample_times_temperature),
+    ("topk_sample", _sample_left_boundary),
+    ("topk_sample", _sample_padded_vocab),
+    ("generate", _generate_first_position),
 ]
 
 # the pins that should catch mistakes in the model and optimizer
@@ -153,6 +205,8 @@ PIN_TESTS = [
     lambda: pins.test_lr_schedule_build_nanogpt_shape(),
     lambda: pins.test_clip_against_pytorch(),
     lambda: pins.test_decay_mask_groups(),
+    lambda: pins.test_topk_sample_closed_forms(),
+    lambda: pins.test_generate_repeats_last_token_in_an_identity_model(),
 ]
 
 

@@ -455,3 +455,70 @@ def test_zipf_generator_law():
     n = idx.size
     for i in (0, 1, 9):
         assert abs(counts[i] / n - p[i]) < 4 * math.sqrt(p[i] / n)
+
+
+# ---------------------------------------------------------------- generation
+def test_topk_sample_closed_forms():
+    # softmax over [0, ln2, ln3] is [1/6, 2/6, 3/6]; the padded id 3 never wins
+    z = np.array([0.0, math.log(2), math.log(3), 50.0])
+    for u, want in [(0.0, 0), (0.1, 0), (0.2, 1), (0.49, 1), (0.51, 2), (0.999, 2)]:
+        tok, p = O.topk_sample(z, 3, 1.0, 0, u)
+        assert tok == want, (u, tok)
+        np.testing.assert_allclose(p, [1 / 6, 2 / 6, 3 / 6], rtol=1e-12)
+    # a cumulative probability equal to u moves to the next id (first id whose
+    # cumulative probability exceeds u)
+    assert O.topk_sample(np.array([0.0, 0.0]), 2, 1.0, 0, 0.5)[0] == 1
+    # temperature divides: logits [0, ln4] at T=2 -> [1/3, 2/3]
+    np.testing.assert_allclose(O.topk_sample(np.array([0.0, math.log(4)]), 2, 2.0, 0, 0.0)[1],
+                               [1 / 3, 2 / 3], rtol=1e-12)
+    # the cutoff keeps values equal to the k-th largest
+    np.testing.assert_allclose(O.topk_sample(np.array([1.0, 1.0, 1.0, 0.0]), 4, 1.0, 2, 0.0)[1],
+                               [1 / 3, 1 / 3, 1 / 3, 0.0], rtol=1e-12)
+    # top-k removes the rest: k=2 of [0, ln2, ln3, ln4] -> [0, 0, 3/7, 4/7]
+    np.testing.assert_allclose(
+        O.topk_sample(np.log(np.array([1.0, 2.0, 3.0, 4.0])), 4, 1.0, 2, 0.0)[1],
+        [0, 0, 3 / 7, 4 / 7], rtol=1e-12, atol=1e-15)
+    # k = 1 is greedy whatever u is
+    rng = np.random.default_rng(5)
+    z = rng.normal(size=100)
+    for u in (0.0, 0.3, 0.999999):
+        assert O.topk_sample(z, 100, 0.8, 1, u)[0] == int(np.argmax(z))
+
+
+def test_topk_sample_frequencies_follow_probabilities():
+    # an even grid of uniforms lands on each id in proportion to its probability
+    rng = np.random.default_rng(6)
+    z = rng.normal(size=20) * 2.0
+    n = 20000
+    counts = np.zeros(20)
+    for j in range(n):
+        counts[O.topk_sample(z, 20, 0.8, 5, (j + 0.5) / n)[0]] += 1
+    e = np.exp(z / 0.8 - (z / 0.8).max())
+    e[np.argsort(z)[:15]] = 0.0  # the 15 smallest are below the top-5 cutoff
+    np.testing.assert_allclose(counts / n, e / e.sum(), atol=2.0 / n)
+
+
+def test_generate_repeats_last_token_in_an_identity_model():
+    # every block projection and bias zero, wpe zero, LayerNorms identity:
+    # blocks add nothing, the logits of a position are LN(wte[tok]) . wte^T,
+    # largest for tok itself, so greedy decoding repeats the last token; going
+    # past block_size exercises the cropping of the context
+    cfg = micro_cfg(vocab_size=11, padded_vocab=16, block_size=8)
+    P = {name: np.zeros(shape) for name, shape in O.param_shapes(cfg)}
+    # token rows: orthonormal and orthogonal to the all-ones vector, so the
+    # LayerNorm only rescales them and distinct rows have zero dot product
+    rng = np.random.default_rng(7)
+    basis = np.linalg.qr(np.column_stack([np.ones(cfg.n_embd),
+                                          rng.normal(size=(cfg.n_embd, cfg.n_embd - 1))]))[0]
+    P["wte"][:cfg.vocab_size] = 3.0 * basis[:, 1:cfg.vocab_size + 1].T
+    for name in P:
+        if name.endswith("ln1.w") or name.endswith("ln2.w") or name == "lnf.w":
+            P[name] = np.ones(P[name].shape)
+    flat = np.concatenate([P[name].ravel() for name, _ in O.param_shapes(cfg)])
+    idx = np.array([[3, 1, 4, 1, 5, 9], [2, 6, 5, 3, 5, 8]])
+    hf = O.layernorm_fwd(P["wte"], np.ones(cfg.n_embd), np.zeros(cfg.n_embd))[0]
+    assert all(np.argmax(hf[t] @ P["wte"][:cfg.vocab_size].T) == t for t in range(cfg.vocab_size))
+    out, logits = O.generate(flat, idx, cfg, 7, 0.8, 1, np.full((2, 7), 0.5))
+    assert out.shape == (2, 13)
+    assert (out[:, 6:] == idx[:, -1:]).all()
+    assert logits.shape == (7, 2, cfg.padded_vocab)
