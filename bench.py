@@ -166,6 +166,70 @@ def cpu_baseline(dims, seed=1338):
                                         f"(fwd+bwd+clip+AdamW) in {dt:.1f} s"}
 
 
+def decode_bench(torch, bd, synth, dims, B, prompt, n_new, temperature=0.8, top_k=200):
+    """Sampling with the key/value cache ("nanoGPT" Part IV, one generation;
+    "Build GPT from scratch", exercise "Add a KV cache"): one prefill of the
+    prompt, then n_new draws, each a decode step and a sample, timed with one
+    event per token.  Prints one JSON line."""
+    params = synth.init_params(dims, seed=1337)
+    model = bd.GPT(dims, bd.GPT_BF16, max_batch=B, init_params=params)
+    idx = torch.as_tensor(synth.tokens(synth.WORKLOADS[WORKLOAD], seed=1338, batch=B, T=prompt)[0]).cuda()
+    g = torch.Generator(device="cuda").manual_seed(1339)
+    u = torch.rand((n_new, B), generator=g, dtype=torch.float32, device="cuda")
+    kv, L = model.kv_cache(B, dims["block_size"])
+    V = dims["vocab_size"]
+    s = torch.cuda.current_stream()
+
+    def run(timed):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_new + 2)]
+        ev[0].record(s)
+        logits = model.prefill(idx, kv, L)
+        ev[1].record(s)
+        for i in range(n_new):
+            tok = bd.sample(logits, V, temperature, top_k, u[i])
+            if i + 1 < n_new:
+                model.decode_step(tok, prompt + i, kv, L, logits)
+            ev[i + 2].record(s)
+        torch.cuda.synchronize()
+        return ev
+
+    run(False)  # warm-up: the same work once
+    ev = run(True)
+    prefill_ms = ev[0].elapsed_time(ev[1])
+    per_tok = [ev[i + 1].elapsed_time(ev[i + 2]) for i in range(1, n_new)]
+    total_ms = ev[1].elapsed_time(ev[-1])
+    srt = sorted(per_tok)
+    pct = lambda q: srt[min(len(srt) - 1, int(round(q * (len(srt) - 1))))]
+    early = sum(per_tok[:64]) / 64
+    late = sum(per_tok[-64:]) / 64
+    # bytes one decode step must read: every bf16 matrix (the tied embedding
+    # once) and the cache of the positions it attends to (mean position)
+    d, Lyr, Vp = dims["n_embd"], dims["n_layer"], dims["padded_vocab"]
+    w_bytes = 2 * (Lyr * 12 * d * d + Vp * d)
+    kv_bytes = 2 * Lyr * 2 * B * d * (prompt + n_new / 2)
+    step_ms = total_ms / n_new
+    achieved = (w_bytes + kv_bytes) / (step_ms * 1e-3) / 1e9
+    out = {
+        "metric": f"decode tokens/s with a KV cache (temperature {temperature}, top-k {top_k}), "
+                  f"GPT-2 124M bf16, B={B}, 1 MI355X",
+        "value": round(B * n_new / (total_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": n_new, "warmup": 1, "ms_per_token": round(step_ms, 4),
+        "ms_per_token_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
+        "ms_per_token_first64_last64": [round(early, 4), round(late, 4)],
+        "prefill_ms": round(prefill_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (Zipf(1.1) prompt; random-init weights)",
+        "config": {"workload": f"GPT-2 124M sampling, prompt {prompt}, {n_new} new tokens, "
+                               f"positions {prompt}..{prompt + n_new - 1}", "batch": B},
+        "roofline": {"kernel": "whole decode step (weights + cache read once per token)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_step": int(w_bytes + kv_bytes)},
+        "cpu_baseline": None,
+    }
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +237,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--decode", type=int, default=0, metavar="B",
+                    help="instead of training, time sampling with the KV cache for B sequences")
     ap.add_argument("--probe", action="store_true",
                     help="only launch the dominant kernel and a calibration copy (counter runs)")
     args = ap.parse_args()
@@ -188,6 +254,9 @@ def main():
 
     dims = synth.WORKLOADS[WORKLOAD]
     B, T = dims["batch"], dims["block_size"]
+    if args.decode:
+        decode_bench(torch, bd, synth, synth.model_dims(dims), args.decode, 64, 448)
+        return
     if args.probe:
         probe(torch, bd, B, T, dims)
         return

@@ -128,6 +128,48 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
                    float weight_decay, float max_norm, int32_t t,
                    int32_t skip_nonfinite, float* norm_out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Sampling from the model ("nanoGPT", Part IV, one generation: sample.py +
+ * model.py, generate), with a cache of keys and values ("Build GPT from
+ * scratch", exercise "Add a KV cache") so that a step feeds one new token per
+ * sequence.  Learned positions make a cache valid only while a sequence fits
+ * in block_size; past it the caller runs gpt_prefill on the last block_size
+ * tokens (the pages' cropping).  These calls overwrite the activations of the
+ * last forward, so gpt_backward afterwards fails with GPT_ESTATE.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of a cache for B sequences of up to max_len positions:
+ * kv[layer][k|v][b][head][t][head_width] in the mode's activation type
+ * (bf16 in GPT_BF16 mode, fp32 in GPT_FP32 mode).  -1 for an invalid config
+ * or size.  The caller allocates it on the device and owns it. */
+int64_t gpt_kv_cache_bytes(const gpt_config* cfg, int32_t B, int32_t max_len);
+
+/* Forward over prompts idx (device int32 [B*T0], row-major (b, t)), storing
+ * every layer's keys and values of positions [0, T0) in kv (sized for exactly
+ * B sequences and max_len positions, 1 <= T0 <= max_len <= block_size), and
+ * the logits of each sequence's last position in logits_out (device fp32
+ * [B][padded_vocab]).  Errors: GPT_EINVAL (null pointer, B outside
+ * [1, max_batch]), GPT_ESEQLEN. */
+int gpt_prefill(gpt_model* h, const int32_t* idx, int32_t B, int32_t T0, void* kv,
+                int32_t max_len, float* logits_out, void* stream);
+
+/* One new token per sequence, tok (device int32 [B]), all at position pos
+ * (0 <= pos < max_len): its keys and values go to cache position pos,
+ * attention covers positions [0, pos], and logits_out (device fp32
+ * [B][padded_vocab]) receives the next-token logits.  kv, B and max_len as in
+ * the gpt_prefill that filled positions [0, pos).  Errors as gpt_prefill. */
+int gpt_decode_step(gpt_model* h, const int32_t* tok, int32_t B, int32_t pos, void* kv,
+                    int32_t max_len, float* logits_out, void* stream);
+
+/* One draw per row of logits (device fp32 [B][ldv], ids [0, V) used):
+ * z = logits / temperature; when 0 < top_k < V, ids with z below the k-th
+ * largest z are removed (ids equal to it stay); p = softmax(z); the token is
+ * the first id whose cumulative p exceeds u[b] (device fp32 [B], uniforms in
+ * [0, 1) that the caller draws).  tok_out: device int32 [B].
+ * Errors: GPT_EINVAL (null pointer, B < 1, ldv < V, temperature <= 0). */
+int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float temperature,
+               int32_t top_k, const float* u, int32_t* tok_out, void* stream);
+
 /* Synchronise `stream`, return the device flags (GPT_FLAG_*) raised since the
  * last call in *flags, and clear them. */
 int gpt_read_flags(gpt_model* h, int32_t* flags, void* stream);

@@ -45,11 +45,16 @@ _SIGS = {
     "gpt_op_attention_bwd": [_i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
     "gpt_op_layernorm_fwd": [_i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _p],
     "gpt_op_cross_entropy": [_i32, _p, _p, _p, _p, _p, _f, _i32, _i32, _i32, _p],
+    "gpt_prefill": [_p, _p, _i32, _i32, _p, _i32, _p, _p],
+    "gpt_decode_step": [_p, _p, _i32, _i32, _p, _i32, _p, _p],
+    "gpt_sample": [_p, _i32, _i32, _i32, _f, _i32, _p, _p, _p],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = ctypes.c_int
+lib.gpt_kv_cache_bytes.argtypes = [ctypes.POINTER(gpt_config), _i32, _i32]
+lib.gpt_kv_cache_bytes.restype = ctypes.c_int64
 lib.gpt_destroy.argtypes = [_p]
 lib.gpt_destroy.restype = None
 lib.gpt_strerror.argtypes = [ctypes.c_int]
@@ -142,6 +147,67 @@ class GPT:
                                  1 if skip_nonfinite else 0, _ptr(norm), _stream()), "gpt_adamw_step")
         return norm
 
+    # ------------------------------------------------------------ sampling
+    def kv_cache(self, B, max_len=None):
+        """Device cache for B sequences of up to max_len (default block_size)
+        positions; returns (buffer, max_len)."""
+        import torch
+        max_len = max_len or self.dims["block_size"]
+        n = lib.gpt_kv_cache_bytes(ctypes.byref(self.cfg), B, max_len)
+        if n < 0:
+            raise GptError(GPT_EINVAL, "gpt_kv_cache_bytes")
+        return torch.empty(n, dtype=torch.uint8, device=self.params.device), max_len
+
+    def prefill(self, idx, kv, max_len, logits=None):
+        """idx: int32 cuda [B, T0].  Returns fp32 logits [B, Vp] of the last position."""
+        import torch
+        B, T0 = idx.shape
+        if logits is None:
+            logits = torch.empty((B, self.dims["padded_vocab"]), dtype=torch.float32, device=idx.device)
+        check(lib.gpt_prefill(self.handle, _ptr(idx), B, T0, _ptr(kv), max_len, _ptr(logits),
+                              _stream()), "gpt_prefill")
+        return logits
+
+    def decode_step(self, tok, pos, kv, max_len, logits=None):
+        """tok: int32 cuda [B] at position pos.  Returns fp32 logits [B, Vp]."""
+        import torch
+        B = tok.shape[0]
+        if logits is None:
+            logits = torch.empty((B, self.dims["padded_vocab"]), dtype=torch.float32, device=tok.device)
+        check(lib.gpt_decode_step(self.handle, _ptr(tok), B, pos, _ptr(kv), max_len, _ptr(logits),
+                                  _stream()), "gpt_decode_step")
+        return logits
+
+    def generate(self, idx, n_new, temperature=0.8, top_k=200, u=None, keep_logits=False):
+        """GPT.generate with the cache: idx int32 cuda [B, T0]; u fp32 cuda
+        [B, n_new] uniforms in [0, 1) (drawn here from torch when None).
+        While a sequence fits in block_size each step feeds one token; past it
+        the last block_size tokens are prefilled again (the pages' cropping).
+        Returns (tokens [B, T0 + n_new], list of the fp32 logits each draw used
+        when keep_logits)."""
+        import torch
+        bs = self.dims["block_size"]
+        B = idx.shape[0]
+        if u is None:
+            u = torch.rand((B, n_new), dtype=torch.float32, device=idx.device)
+        kv, max_len = self.kv_cache(B, bs)
+        seq = idx.to(torch.int32).contiguous()
+        logits = self.prefill(seq[:, -bs:].contiguous(), kv, max_len)
+        kept = []
+        for i in range(n_new):
+            if keep_logits:
+                kept.append(logits.clone())
+            tok = sample(logits, self.dims["vocab_size"], temperature, top_k, u[:, i].contiguous())
+            seq = torch.cat([seq, tok[:, None]], dim=1)
+            if i + 1 == n_new:
+                break
+            n = seq.shape[1]
+            if n <= bs:
+                logits = self.decode_step(tok, n - 1, kv, max_len, logits)
+            else:
+                logits = self.prefill(seq[:, -bs:].contiguous(), kv, max_len, logits)
+        return seq, kept
+
     def read_flags(self) -> int:
         f = _i32()
         check(lib.gpt_read_flags(self.handle, ctypes.byref(f), _stream()), "gpt_read_flags")
@@ -157,6 +223,17 @@ class GPT:
             self.close()
         except Exception:
             pass
+
+
+def sample(logits, vocab_size, temperature, top_k, u):
+    """One draw per row of fp32 logits [B, ldv] over ids [0, vocab_size):
+    gpt_sample.  u: fp32 cuda [B].  Returns int32 tokens [B]."""
+    import torch
+    B, ldv = logits.shape
+    tok = torch.empty(B, dtype=torch.int32, device=logits.device)
+    check(lib.gpt_sample(_ptr(logits), B, vocab_size, ldv, temperature, top_k, _ptr(u), _ptr(tok),
+                         _stream()), "gpt_sample")
+    return tok
 
 
 # --------------------------------------------------------------------------- single ops

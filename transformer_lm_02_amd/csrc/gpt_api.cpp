@@ -346,20 +346,18 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
   return GPT_OK;
 }
 
-int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
-                     float loss_scale, float* loss_out, void* logits_out, void* stream) {
-  if (!h || !idx) return fail(GPT_EINVAL, "null handle or idx");
+// Embedding, the L blocks and the final LayerNorm over B sequences of T
+// tokens ([NG] Part IV Stage 4: GPT.forward up to ln_f).  With kv set, each
+// block's keys and values are also stored in the cache kv (sized for B
+// sequences of max_len positions) at positions [0, T).
+static int forward_stack(gpt_model* h, const int32_t* idx, int B, int T, void* kv, int max_len,
+                         hipStream_t s) {
   const gpt_config& c = h->cfg;
-  if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
-  if (T < 1) return fail(GPT_EINVAL, "T < 1");
-  if (T > c.block_size) return fail(GPT_ESEQLEN, "T > block_size");
-  hipStream_t s = (hipStream_t)stream;
   const bool bf = h->bf16();
   const WsOff& w = h->wo;
   const ParamOff& p = h->po;
   const int M = B * T, d = c.n_embd, H = c.n_head;
-  h->have_fwd = false;
-
+  const int64_t kv_layer = 2ll * B * H * max_len * (d / H);
   CK(embed_fwd_launch(idx, h->P(p.wte), h->P(p.wpe), h->at<float>(w.layer.empty() ? w.x_final : w.layer[0].x_in),
                       M, T, d, c.padded_vocab, h->at<int>(w.flags), s));
   for (int l = 0; l < c.n_layer; ++l) {
@@ -374,6 +372,9 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, i
     e.ldc = 3 * d;
     CK(gemm_launch(bf, true, true, EPI_ACT, h->at(L.ln1), d, h->W(P.attnw), d, M, 3 * d, d, d, d,
                    e, s));
+    if (kv)
+      CK(kv_store_launch(bf, h->at(L.qkv), (char*)kv + l * kv_layer * h->es(), B, T, H, d / H,
+                         max_len, 0, s));
     CK(attention_fwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), B, T, H, d, s));
     e = GemmEpiArgs();
     e.out = h->at(L.x_mid);
@@ -401,6 +402,24 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, i
   }
   CK(layernorm_fwd_launch(bf, h->at<float>(w.x_final), h->P(p.lnfw), h->P(p.lnfb), h->at(w.lnf),
                           h->at<float>(w.lnf_mean), h->at<float>(w.lnf_rstd), M, d, s));
+  return GPT_OK;
+}
+
+int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
+                     float loss_scale, float* loss_out, void* logits_out, void* stream) {
+  if (!h || !idx) return fail(GPT_EINVAL, "null handle or idx");
+  const gpt_config& c = h->cfg;
+  if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
+  if (T < 1) return fail(GPT_EINVAL, "T < 1");
+  if (T > c.block_size) return fail(GPT_ESEQLEN, "T > block_size");
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = h->bf16();
+  const WsOff& w = h->wo;
+  const ParamOff& p = h->po;
+  const int M = B * T, d = c.n_embd;
+  h->have_fwd = false;
+
+  CK(forward_stack(h, idx, B, T, nullptr, 1, s));
   {
     GemmEpiArgs e;
     e.out = h->at(w.logits);
@@ -423,6 +442,163 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, i
   h->B = B;
   h->T = T;
   h->idx = idx;
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------- sampling
+int64_t gpt_kv_cache_bytes(const gpt_config* c, int32_t B, int32_t max_len) {
+  if (validate(c) != GPT_OK || B < 1 || max_len < 1) return -1;
+  const int64_t es = c->mode == GPT_BF16 ? 2 : 4;
+  return (int64_t)c->n_layer * 2 * B * c->n_embd * (int64_t)max_len * es;
+}
+
+static int check_decode_args(gpt_model* h, int B, int max_len, const void* kv, const float* logits_out) {
+  const gpt_config& c = h->cfg;
+  if (!kv || !logits_out) return fail(GPT_EINVAL, "null cache or logits buffer");
+  if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
+  if (max_len < 1 || max_len > c.block_size) return fail(GPT_ESEQLEN, "max_len outside [1, block_size]");
+  return GPT_OK;
+}
+
+// head over one row per sequence: logits [B][padded_vocab] fp32 = rows of
+// lnf (row pitch lda elements) times wte^T
+static int head_rows(gpt_model* h, const void* rows, int lda, int B, float* logits_out, hipStream_t s) {
+  const gpt_config& c = h->cfg;
+  GemmEpiArgs e;
+  e.out = logits_out;
+  e.ldc = c.padded_vocab;
+  CK(gemm_launch(h->bf16(), true, true, EPI_F32, rows, lda, h->W(h->po.wte), c.n_embd, B,
+                 c.padded_vocab, c.n_embd, c.n_embd, c.n_embd, e, s));
+  return GPT_OK;
+}
+
+int gpt_prefill(gpt_model* h, const int32_t* idx, int32_t B, int32_t T0, void* kv, int32_t max_len,
+                float* logits_out, void* stream) {
+  if (!h || !idx) return fail(GPT_EINVAL, "null handle or idx");
+  CK(check_decode_args(h, B, max_len, kv, logits_out));
+  if (T0 < 1 || T0 > max_len) return fail(GPT_ESEQLEN, "prompt length outside [1, max_len]");
+  hipStream_t s = (hipStream_t)stream;
+  h->have_fwd = false;
+  const int d = h->cfg.n_embd;
+  CK(forward_stack(h, idx, B, T0, kv, max_len, s));
+  // the last position of every sequence: row b*T0 + T0-1 of lnf
+  CK(head_rows(h, (const char*)h->at(h->wo.lnf) + (size_t)(T0 - 1) * d * h->es(), T0 * d, B,
+               logits_out, s));
+  return GPT_OK;
+}
+
+int gpt_decode_step(gpt_model* h, const int32_t* tok, int32_t B, int32_t pos, void* kv,
+                    int32_t max_len, float* logits_out, void* stream) {
+  if (!h || !tok) return fail(GPT_EINVAL, "null handle or tokens");
+  CK(check_decode_args(h, B, max_len, kv, logits_out));
+  if (pos < 0 || pos >= max_len) return fail(GPT_ESEQLEN, "position outside [0, max_len)");
+  hipStream_t s = (hipStream_t)stream;
+  h->have_fwd = false;
+  const gpt_config& c = h->cfg;
+  const bool bf = h->bf16();
+  const WsOff& w = h->wo;
+  const ParamOff& p = h->po;
+  const int d = c.n_embd, H = c.n_head, hs = d / H;
+  const int64_t kv_layer = 2ll * B * H * max_len * hs;
+  // B rows, one per sequence, through the layer-0 activation buffers: x
+  // alternates between x_in and x_mid
+  const WsLayer& L = w.layer[0];
+  float* xa = h->at<float>(L.x_in);
+  float* xb = h->at<float>(L.x_mid);
+  CK(embed_fwd_launch(tok, h->P(p.wte), h->P(p.wpe) + (size_t)pos * d, xa, B, 1, d, c.padded_vocab,
+                      h->at<int>(w.flags), s));
+  // few-row products (gemv_launch) where the rows fit; the tiled GEMM
+  // path otherwise (it returns -5 when a shape or alignment does not suit)
+  auto gemv = [&](int epi, const void* A, const float* lnw, const float* lnb, const void* W,
+                  const float* bias, const float* aux, void* out, int N, int K, int ldo, void* kvc)
+      -> int {
+    return gemv_launch(bf, epi, A, lnw, lnb, W, bias, aux, out, B, N, K, ldo, kvc, H, hs, max_len,
+                       pos, s);
+  };
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& P = p.layer[l];
+    void* kvl = (char*)kv + l * kv_layer * h->es();
+    // LayerNorm 1 + q|k|v projection + cache store
+    int rc = gemv(0, xa, h->P(P.ln1w), h->P(P.ln1b), h->W(P.attnw), h->P(P.attnb), nullptr,
+                  h->at(L.qkv), 3 * d, d, 3 * d, kvl);
+    if (rc == -5) {
+      CK(layernorm_fwd_launch(bf, xa, h->P(P.ln1w), h->P(P.ln1b), h->at(L.ln1),
+                              h->at<float>(L.ln1_mean), h->at<float>(L.ln1_rstd), B, d, s));
+      GemmEpiArgs e;
+      e.out = h->at(L.qkv);
+      e.bias = h->P(P.attnb);
+      e.ldc = 3 * d;
+      CK(gemm_launch(bf, true, true, EPI_ACT, h->at(L.ln1), d, h->W(P.attnw), d, B, 3 * d, d, d, d,
+                     e, s));
+      CK(kv_store_launch(bf, h->at(L.qkv), kvl, B, 1, H, hs, max_len, pos, s));
+    } else {
+      CK(rc);
+    }
+    CK(decode_attn_launch(bf, h->at(L.qkv), kvl, h->at(L.att), B, H, hs, max_len, pos + 1, s));
+    // attention projection + residual
+    rc = gemv(2, h->at(L.att), nullptr, nullptr, h->W(P.aprojw), h->P(P.aprojb), xa, xb, d, d, d,
+              nullptr);
+    if (rc == -5) {
+      GemmEpiArgs e;
+      e.out = xb;
+      e.aux = xa;
+      e.bias = h->P(P.aprojb);
+      e.ldc = d;
+      CK(gemm_launch(bf, true, true, EPI_RESID, h->at(L.att), d, h->W(P.aprojw), d, B, d, d, d, d,
+                     e, s));
+    } else {
+      CK(rc);
+    }
+    // LayerNorm 2 + MLP expansion + GELU
+    rc = gemv(3, xb, h->P(P.ln2w), h->P(P.ln2b), h->W(P.fcw), h->P(P.fcb), nullptr, h->at(L.g),
+              4 * d, d, 4 * d, nullptr);
+    if (rc == -5) {
+      CK(layernorm_fwd_launch(bf, xb, h->P(P.ln2w), h->P(P.ln2b), h->at(L.ln2),
+                              h->at<float>(L.ln2_mean), h->at<float>(L.ln2_rstd), B, d, s));
+      GemmEpiArgs e;
+      e.out = h->at(L.dgelu);
+      e.out2 = h->at(L.g);
+      e.bias = h->P(P.fcb);
+      e.ldc = 4 * d;
+      CK(gemm_launch(bf, true, true, EPI_GELU, h->at(L.ln2), d, h->W(P.fcw), d, B, 4 * d, d, d, d,
+                     e, s));
+    } else {
+      CK(rc);
+    }
+    // MLP projection + residual
+    rc = gemv(2, h->at(L.g), nullptr, nullptr, h->W(P.mprojw), h->P(P.mprojb), xb, xa, d, 4 * d, d,
+              nullptr);
+    if (rc == -5) {
+      GemmEpiArgs e;
+      e.out = xa;
+      e.aux = xb;
+      e.bias = h->P(P.mprojb);
+      e.ldc = d;
+      CK(gemm_launch(bf, true, true, EPI_RESID, h->at(L.g), 4 * d, h->W(P.mprojw), 4 * d, B, d,
+                     4 * d, 4 * d, 4 * d, e, s));
+    } else {
+      CK(rc);
+    }
+  }
+  // final LayerNorm + head over every padded column
+  int rc = gemv(1, xa, h->P(p.lnfw), h->P(p.lnfb), h->W(p.wte), nullptr, nullptr, logits_out,
+                c.padded_vocab, d, c.padded_vocab, nullptr);
+  if (rc == -5) {
+    CK(layernorm_fwd_launch(bf, xa, h->P(p.lnfw), h->P(p.lnfb), h->at(w.lnf),
+                            h->at<float>(w.lnf_mean), h->at<float>(w.lnf_rstd), B, d, s));
+    CK(head_rows(h, h->at(w.lnf), d, B, logits_out, s));
+  } else {
+    CK(rc);
+  }
+  return GPT_OK;
+}
+
+int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float temperature,
+               int32_t top_k, const float* u, int32_t* tok_out, void* stream) {
+  if (!logits || !u || !tok_out) return fail(GPT_EINVAL, "null sampling buffer");
+  if (B < 1 || V < 1 || ldv < V) return fail(GPT_EINVAL, "bad sampling shape");
+  if (!(temperature > 0.f)) return fail(GPT_EINVAL, "temperature must be > 0");
+  CK(sample_launch(logits, B, V, ldv, temperature, top_k, u, tok_out, (hipStream_t)stream));
   return GPT_OK;
 }
 

@@ -61,6 +61,20 @@ int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* ou
 #define COLSUM_GROUP_MAX 56
 int colsum_finalize_group_launch(const ColsumJob* jobs, int n, int beta, hipStream_t s);
 
+// sampling with a key/value cache: cache kv[k|v][b][h][t][hs] of one layer
+// (t < max_len), in the mode's activation type
+int kv_store_launch(bool bf16, const void* qkv, void* kv, int B, int Tn, int H, int hs,
+                    int max_len, int pos0, hipStream_t s);
+int decode_attn_launch(bool bf16, const void* qkv, const void* kv, void* out, int B, int H, int hs,
+                       int max_len, int len, hipStream_t s);
+int sample_launch(const float* logits, int B, int V, int ldv, float temperature, int top_k,
+                  const float* u, int32_t* tok, hipStream_t s);
+// products of the few rows of a decode step: see decode.hip
+bool gemv_fits(bool bf16, bool ln, int M, int K);
+int gemv_launch(bool bf16, int epi, const void* A, const float* ln_w, const float* ln_b,
+                const void* W, const float* bias, const float* aux, void* out, int M, int N, int K,
+                int ldo, void* kv, int H, int hs, int max_len, int pos, hipStream_t s);
+
 int adamw_norm_blocks();
 int adamw_launch(float* p, const float* g, float* m, float* v, bf16_t* shadow, int64_t n,
                  const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
