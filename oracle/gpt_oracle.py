@@ -41,6 +41,11 @@ Readings taken where the pages are silent (each repeated where it is used):
   * Sampling: the top-k cutoff keeps values equal to the k-th largest;
     top_k <= 0 keeps all; the multinomial draw is by inverse CDF in token-id
     order with a uniform supplied by the caller.
+  * Dynamic loss scaling (float16): initial scale 2^16, growth factor 2
+    after 2000 consecutive clean steps, backoff factor 0.5 on a step with an
+    inf or NaN gradient (the defaults of the GradScaler the pages construct;
+    no value is printed); a grown scale is kept only if it is finite; a
+    skipped step leaves params, m, v and the optimizer step count unchanged.
 """
 from __future__ import annotations
 
@@ -435,6 +440,84 @@ def train_step(params, m, v, t, micro_batches, cfg: Config, lr, beta1=0.9,
                       beta2, eps, weight_decay, coef)
     return dict(params=p, m=m2, v=v2, loss=float(np.mean(losses)), norm=norm,
                 grads=grads)
+
+
+# --------------------------------------------------------------------------
+# float16 training: dynamic loss scaling
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class LossScaler:
+    """State of the dynamic loss scale of float16 training ([NG] Part IV
+    Stage 4 and Stage 5; Part V Deep dive 2; [RC] "Float16, Gradient Scalers,
+    BF16").  scale multiplies the loss before the backward pass; growth_tracker
+    counts clean steps since the scale last changed; steps counts the AdamW
+    updates actually applied (a skipped step does not advance the bias
+    correction, since the optimizer is not called)."""
+    scale: float = 65536.0
+    growth_tracker: int = 0
+    steps: int = 0
+
+
+def scaler_update(state: LossScaler, found_inf: bool, growth_factor=2.0,
+                  backoff_factor=0.5, growth_interval=2000) -> LossScaler:
+    """The scale after one step ([NG] Part IV Stage 5: an overflow shrinks the
+    scale; the scale is adjusted for the next iteration).  Readings: the
+    library defaults the pages' GradScaler is built with (growth 2, backoff
+    0.5, growth every 2000 clean steps); a step with an overflow multiplies
+    the scale by the backoff factor and restarts the count; the count reaching
+    the interval multiplies it by the growth factor (kept only if finite) and
+    restarts the count."""
+    if found_inf:
+        return LossScaler(state.scale * backoff_factor, 0, state.steps)
+    clean = state.growth_tracker + 1
+    if clean == growth_interval:
+        grown = state.scale * growth_factor
+        return LossScaler(grown if math.isfinite(grown) else state.scale, 0, state.steps + 1)
+    return LossScaler(state.scale, clean, state.steps + 1)
+
+
+def amp_step(params, scaled_grads, m, v, mask, state: LossScaler, lr, beta1=0.9,
+             beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0, growth_factor=2.0,
+             backoff_factor=0.5, growth_interval=2000):
+    """The float16 optimizer step in the pages' order ([NG] Part IV Stage 5;
+    Part VIII checks 6 and 7): unscale the gradients (multiply by 1/scale),
+    clip against the norm of the unscaled gradients, apply AdamW unless an
+    element is inf or NaN (then leave params, m and v as they are), update
+    the scale.  Returns dict(params, m, v, norm (of the unscaled gradients),
+    found_inf, state (the updated LossScaler))."""
+    grads = np.asarray(scaled_grads) * (1.0 / state.scale)
+    found_inf = not bool(np.all(np.isfinite(grads)))
+    norm = grad_norm(grads)
+    if found_inf:
+        p, m2, v2 = params.copy(), m.copy(), v.copy()
+    else:
+        p, m2, v2 = adamw(params, grads, m, v, mask, state.steps + 1, lr, beta1, beta2, eps,
+                          weight_decay, clip_coef(norm, max_norm))
+    new = scaler_update(state, found_inf, growth_factor, backoff_factor, growth_interval)
+    return dict(params=p, m=m2, v=v2, norm=norm, found_inf=found_inf, state=new)
+
+
+def train_step_amp(params, m, v, state: LossScaler, micro_batches, cfg: Config, lr,
+                   beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
+                   growth_factor=2.0, backoff_factor=0.5, growth_interval=2000,
+                   dtype=np.float64):
+    """One float16-style iteration ([NG] Part IV Stages 4-5): every micro-loss
+    is multiplied by scale / k before its backward pass (the scaled backward),
+    the gradients accumulate, then amp_step.  Returns amp_step's dict plus
+    loss (the mean of the unscaled micro-losses) and grads (the accumulated,
+    still scaled gradient)."""
+    k = len(micro_batches)
+    grads = np.zeros(num_params(cfg), dtype=dtype)
+    losses = []
+    for idx, tgt in micro_batches:
+        loss, g, _ = loss_and_grads(params, idx, tgt, cfg, state.scale / k, dtype)
+        grads += g
+        losses.append(loss)
+    out = amp_step(np.asarray(params, dtype), grads, np.asarray(m, dtype), np.asarray(v, dtype),
+                   decay_mask(cfg, dtype), state, lr, beta1, beta2, eps, weight_decay, max_norm,
+                   growth_factor, backoff_factor, growth_interval)
+    out.update(loss=float(np.mean(losses)), grads=grads)
+    return out
 
 
 def flops_per_token(cfg: Config, T: int) -> int:

@@ -167,6 +167,66 @@ def _generate_first_position(flat_params, idx, cfg, n_new, temperature, top_k, u
 
 _orig_sample = O.topk_sample
 
+
+def _amp_no_unscale(params, scaled_grads, m, v, mask, state, lr, beta1=0.9, beta2=0.95,
+                    eps=1e-8, weight_decay=0.1, max_norm=1.0, growth_factor=2.0,
+                    backoff_factor=0.5, growth_interval=2000):
+    return _orig_amp(params, scaled_grads, m, v, mask, O.LossScaler(1.0, state.growth_tracker,
+                                                                     state.steps), lr, beta1,
+                     beta2, eps, weight_decay, max_norm, growth_factor, backoff_factor,
+                     growth_interval) | {"state": O.scaler_update(
+                         state, not np.all(np.isfinite(scaled_grads)), growth_factor,
+                         backoff_factor, growth_interval)}
+
+
+def _amp_clip_before_unscale(params, scaled_grads, m, v, mask, state, lr, beta1=0.9, beta2=0.95,
+                             eps=1e-8, weight_decay=0.1, max_norm=1.0, growth_factor=2.0,
+                             backoff_factor=0.5, growth_interval=2000):
+    norm = O.grad_norm(scaled_grads)
+    g = scaled_grads * O.clip_coef(norm, max_norm) / state.scale
+    return _orig_amp(params, g * state.scale, m, v, mask, state, lr, beta1, beta2, eps,
+                     weight_decay, 0.0, growth_factor, backoff_factor, growth_interval)
+
+
+def _scaler_counts_skips(state, found_inf, growth_factor=2.0, backoff_factor=0.5,
+                         growth_interval=2000):
+    out = _orig_update(state, found_inf, growth_factor, backoff_factor, growth_interval)
+    return O.LossScaler(out.scale, out.growth_tracker, state.steps + 1)
+
+
+def _scaler_grows_early(state, found_inf, growth_factor=2.0, backoff_factor=0.5,
+                        growth_interval=2000):
+    return _orig_update(state, found_inf, growth_factor, backoff_factor, growth_interval - 1)
+
+
+def _scaler_backoff_keeps_count(state, found_inf, growth_factor=2.0, backoff_factor=0.5,
+                                growth_interval=2000):
+    if found_inf:
+        return O.LossScaler(state.scale * backoff_factor, state.growth_tracker, state.steps)
+    return _orig_update(state, found_inf, growth_factor, backoff_factor, growth_interval)
+
+
+def _train_amp_unscaled_backward(params, m, v, state, micro_batches, cfg, lr, beta1=0.9,
+                                 beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
+                                 growth_factor=2.0, backoff_factor=0.5, growth_interval=2000,
+                                 dtype=np.float64):
+    # the loss is not multiplied by the scale before the backward pass
+    k = len(micro_batches)
+    grads = np.zeros(O.num_params(cfg), dtype=dtype)
+    losses = []
+    for idx, tgt in micro_batches:
+        loss, g, _ = O.loss_and_grads(params, idx, tgt, cfg, 1.0 / k, dtype)
+        grads += g
+        losses.append(loss)
+    out = O.amp_step(np.asarray(params, dtype), grads, np.asarray(m, dtype), np.asarray(v, dtype),
+                     O.decay_mask(cfg, dtype), state, lr, beta1, beta2, eps, weight_decay,
+                     max_norm, growth_factor, backoff_factor, growth_interval)
+    out.update(loss=float(np.mean(losses)), grads=grads)
+    return out
+
+
+_orig_amp, _orig_update, _orig_train_amp = O.amp_step, O.scaler_update, O.train_step_amp
+
 MUTANTS = [
     ("layernorm_fwd", _ln_unbiased),
     ("layernorm_bwd", _ln_bwd_no_mean_term),
@@ -188,6 +248,12 @@ MUTANTS = [
     ("topk_sample", _sample_left_boundary),
     ("topk_sample", _sample_padded_vocab),
     ("generate", _generate_first_position),
+    ("amp_step", _amp_no_unscale),
+    ("amp_step", _amp_clip_before_unscale),
+    ("scaler_update", _scaler_counts_skips),
+    ("scaler_update", _scaler_grows_early),
+    ("scaler_update", _scaler_backoff_keeps_count),
+    ("train_step_amp", _train_amp_unscaled_backward),
 ]
 
 # the pins that should catch mistakes in the model and optimizer
@@ -207,6 +273,10 @@ PIN_TESTS = [
     lambda: pins.test_decay_mask_groups(),
     lambda: pins.test_topk_sample_closed_forms(),
     lambda: pins.test_generate_repeats_last_token_in_an_identity_model(),
+    lambda: pins.test_amp_step_matches_torch_grad_scaler(),
+    lambda: pins.test_amp_scale_sequence_closed_form(),
+    lambda: pins.test_amp_skipped_step_changes_nothing_and_keeps_the_step_count(),
+    lambda: pins.test_train_step_amp_equals_unscaled_step(),
 ]
 
 

@@ -522,3 +522,155 @@ def test_generate_repeats_last_token_in_an_identity_model():
     assert out.shape == (2, 13)
     assert (out[:, 6:] == idx[:, -1:]).all()
     assert logits.shape == (7, 2, cfg.padded_vocab)
+
+
+# ---------------------------------------------------------------- float16 loss scaling
+def _torch_scaler_run(steps, growth_interval):
+    """The pages' float16 loop ([NG] Part IV Stage 5) on the CPU in float64:
+    the gradients that scaler.scale(loss).backward() would leave (the true
+    gradient times the current scale, or a planted inf/NaN), then
+    unscale_, clip_grad_norm_(1.0), step, update."""
+    import torch
+    n = len(steps[0][0])
+    p0 = steps[0][1]
+    tp = [torch.tensor(p0[:n // 2].copy(), requires_grad=True),
+          torch.tensor(p0[n // 2:].copy(), requires_grad=True)]
+    opt = torch.optim.AdamW([{"params": [tp[0]], "weight_decay": 0.1},
+                             {"params": [tp[1]], "weight_decay": 0.0}],
+                            lr=1e-3, betas=(0.9, 0.95), eps=1e-8, foreach=False, fused=False)
+    sc = torch.amp.GradScaler("cpu", growth_interval=growth_interval)
+    rows = []
+    for g, _, plant in steps:
+        s = sc.get_scale()
+        opt.zero_grad()
+        # a loss whose gradient is g, through the scaled backward
+        loss = (torch.tensor(g[:n // 2]) * tp[0]).sum() + (torch.tensor(g[n // 2:]) * tp[1]).sum()
+        sc.scale(loss).backward()
+        if plant is not None:
+            i = plant[0]
+            (tp[0].grad if i < n // 2 else tp[1].grad)[i % (n // 2)] = plant[1]
+        sc.unscale_(opt)
+        norm = float(torch.nn.utils.clip_grad_norm_(tp, 1.0))
+        sc.step(opt)
+        sc.update()
+        rows.append(dict(scale_used=s, norm=norm, scale_after=sc.get_scale(),
+                         params=np.concatenate([t.detach().numpy() for t in tp])))
+    return rows
+
+
+def test_amp_step_matches_torch_grad_scaler():
+    """Seven steps with growth every 2 clean steps, one inf and one NaN
+    planted, gradients both below and above the clip threshold: the scale,
+    the reported norm and the parameters follow PyTorch's GradScaler with
+    clip_grad_norm_ and AdamW."""
+    rng = np.random.default_rng(71)
+    n = 40
+    p = rng.standard_normal(n) * 0.02
+    mask = np.zeros(n)
+    mask[:n // 2] = 1.0
+    sizes = [0.3, 3.0, 0.5, 0.2, 4.0, 0.7, 0.1]
+    plants = [None, None, (3, np.inf), None, None, (30, np.nan), None]
+    steps = [(rng.standard_normal(n) * sz / math.sqrt(n), p, pl) for sz, pl in zip(sizes, plants)]
+    ref = _torch_scaler_run(steps, growth_interval=2)
+    st = O.LossScaler()
+    m = np.zeros(n)
+    v = np.zeros(n)
+    for (g, _, plant), r in zip(steps, ref):
+        assert st.scale == r["scale_used"]
+        gs = g * st.scale
+        if plant is not None:
+            gs[plant[0]] = plant[1]
+        out = O.amp_step(p, gs, m, v, mask, st, 1e-3, growth_interval=2)
+        assert out["found_inf"] == (plant is not None)
+        if plant is None:
+            assert abs(out["norm"] - r["norm"]) <= 1e-12 * r["norm"]
+        else:
+            assert not math.isfinite(out["norm"]) and not math.isfinite(r["norm"])
+        p, m, v, st = out["params"], out["m"], out["v"], out["state"]
+        assert st.scale == r["scale_after"]
+        assert np.allclose(p, r["params"], rtol=1e-12, atol=1e-16)
+
+
+def test_amp_scale_sequence_closed_form():
+    """Growth every 2 clean steps, backoff on an overflow: clean, clean,
+    inf, clean, clean, clean, NaN gives scales 2^16, 2^17, 2^16, 2^16, 2^17,
+    2^17, 2^16 after each step and 5 applied updates."""
+    st = O.LossScaler()
+    seen = []
+    for bad in [False, False, True, False, False, False, True]:
+        st = O.scaler_update(st, bad, growth_interval=2)
+        seen.append(st.scale)
+    assert seen == [2.0 ** e for e in (16, 17, 16, 16, 17, 17, 16)]
+    assert st.steps == 5 and st.growth_tracker == 0
+
+
+def test_amp_step_is_invariant_to_a_power_of_two_scale():
+    """Unscaling by an exact power of two: the update, the norm and the
+    clip are those of the unscaled gradient, bit for bit."""
+    rng = np.random.default_rng(72)
+    n = 64
+    p = rng.standard_normal(n) * 0.02
+    mask = (np.arange(n) % 3 != 0).astype(np.float64)
+    g = rng.standard_normal(n) * 1e-9  # eps-sized: scaling errors would show
+    m0 = rng.standard_normal(n) * 1e-9
+    v0 = rng.random(n) * 1e-18
+    ref = O.adamw(p, g, m0, v0, mask, 4, 1e-3, coef=O.clip_coef(O.grad_norm(g), 1.0))
+    for e in (0, 10, 24):
+        st = O.LossScaler(2.0 ** e, 0, 3)
+        out = O.amp_step(p, g * 2.0 ** e, m0, v0, mask, st, 1e-3)
+        assert out["norm"] == O.grad_norm(g) and not out["found_inf"]
+        for a, b in zip((out["params"], out["m"], out["v"]), ref):
+            assert np.array_equal(a, b)
+
+
+def test_amp_clips_the_unscaled_norm():
+    """True norm 0.5 under a scale of 2^20: below the threshold of 1, so
+    no clipping: after the first step m = (1 - beta1) g exactly; true norm 4:
+    clipped to 1."""
+    g = np.zeros(8)
+    g[0], g[5] = 0.3, 0.4
+    zeros = np.zeros(8)
+    out = O.amp_step(zeros, g * 2.0 ** 20, zeros, zeros, zeros, O.LossScaler(2.0 ** 20), 1e-3)
+    assert out["norm"] == 0.5
+    assert np.array_equal(out["m"], (1 - 0.9) * g)
+    out = O.amp_step(zeros, 8 * g * 2.0 ** 20, zeros, zeros, zeros, O.LossScaler(2.0 ** 20), 1e-3)
+    assert abs(np.linalg.norm(out["m"] / (1 - 0.9)) - 1.0 / (1 + 1e-6 / 4)) < 1e-12
+
+
+def test_amp_skipped_step_changes_nothing_and_keeps_the_step_count():
+    """An overflow: params, m and v unchanged, the scale halved, no update
+    counted; the next clean step is AdamW's first step in closed form,
+    p1 = p0 (1 - lr wd) - lr g / (|g| + eps)."""
+    rng = np.random.default_rng(73)
+    n = 16
+    p = rng.standard_normal(n)
+    mask = np.ones(n)
+    g = rng.standard_normal(n)
+    bad = g * 65536.0
+    bad[2] = -np.inf
+    zeros = np.zeros(n)
+    out = O.amp_step(p, bad, zeros, zeros, mask, O.LossScaler(), 1e-2)
+    assert out["found_inf"] and np.array_equal(out["params"], p)
+    assert np.all(out["m"] == 0) and np.all(out["v"] == 0)
+    assert out["state"] == O.LossScaler(32768.0, 0, 0)
+    out = O.amp_step(p, g * 32768.0, zeros, zeros, mask, out["state"], 1e-2, max_norm=0.0)
+    want = p * (1 - 1e-2 * 0.1) - 1e-2 * g / (np.abs(g) + 1e-8)
+    assert np.allclose(out["params"], want, rtol=1e-14, atol=0)
+    assert out["state"] == O.LossScaler(32768.0, 1, 1)
+
+
+def test_train_step_amp_equals_unscaled_step():
+    """The scaled backward and the unscale cancel exactly for a power-of-two
+    scale: two micro-batches under scale 2^16 give the unscaled step's
+    parameters bit for bit, gradients exactly 2^16 times larger, the same
+    loss."""
+    w = synth.WORKLOADS["tiny"]
+    cfg = cfg_of(w)
+    params = synth.init_params(w, seed=3).astype(np.float64)
+    mb = [synth.tokens(w, seed=4 + i) for i in range(2)]
+    zeros = np.zeros_like(params)
+    plain = O.train_step(params, zeros, zeros, 1, mb, cfg, lr=1e-3)
+    amp = O.train_step_amp(params, zeros, zeros, O.LossScaler(), mb, cfg, lr=1e-3)
+    assert np.array_equal(amp["grads"], plain["grads"] * 65536.0)
+    assert amp["loss"] == plain["loss"] and amp["norm"] == plain["norm"]
+    assert np.array_equal(amp["params"], plain["params"])
