@@ -7,9 +7,11 @@ A100 after every lever).  Inputs are synthetic: Zipf(1.1) token ids over the
 GPT-2 vocabulary, N(0, 0.02) weights with 0.02/sqrt(24) residual
 projections, all resident in HBM before the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--fp16]
 
-Prints one JSON line.
+Prints one JSON line.  --fp16 times the same step in IEEE half precision
+with dynamic loss scaling (scaled forward, backward, then unscale, clip,
+AdamW or skip and scale update on the device).
 """
 from __future__ import annotations
 
@@ -80,13 +82,14 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def dominant_operands(torch, B, T, dims):
+def dominant_operands(torch, B, T, dims, dt=None):
+    dt = dt or torch.bfloat16
     g = torch.Generator(device="cuda").manual_seed(7)
     ops = []
     for (M, N, K, n) in dominant_launches(B, T, dims):
-        A = (torch.randn((M, K), device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
-        W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        A = (torch.randn((M, K), device="cuda", generator=g) * 1e-3).to(dt)
+        W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(dt)
+        C = torch.empty((M, N), dtype=dt, device="cuda")
         ops.append((A, W, C, M, N, K, n))
     return ops
 
@@ -96,17 +99,17 @@ def launch_dominant(bd, ops, stream_ptr, reps=1):
     for _ in range(reps):
         for (A, W, C, M, N, K, n) in ops:
             for _ in range(n):
-                bd.check(bd.lib.gpt_op_linear(1, ctypes.c_void_p(A.data_ptr()),
+                bd.check(bd.lib.gpt_op_linear(bd._bf(A), ctypes.c_void_p(A.data_ptr()),
                                               ctypes.c_void_p(W.data_ptr()), None,
                                               ctypes.c_void_p(C.data_ptr()), 0, M, N, K,
                                               stream_ptr), "gpt_op_linear")
 
 
-def time_dominant_kernel(torch, bd, B, T, dims, reps=5):
+def time_dominant_kernel(torch, bd, B, T, dims, reps=5, fp16=False):
     """The step's launches of the dominant kernel (same shapes, same entry
     into the library), timed with events on the stream they run on."""
     import ctypes
-    ops = dominant_operands(torch, B, T, dims)
+    ops = dominant_operands(torch, B, T, dims, torch.float16 if fp16 else torch.bfloat16)
     s = torch.cuda.current_stream()
     sp = ctypes.c_void_p(s.cuda_stream)
     launch_dominant(bd, ops, sp, 1)
@@ -119,11 +122,12 @@ def time_dominant_kernel(torch, bd, B, T, dims, reps=5):
     ms_total = e0.elapsed_time(e1) / reps
     flops = sum(2.0 * M * N * K * n for (_, _, _, M, N, K, n) in ops)
     achieved = flops / (ms_total * 1e-3) / 1e12
-    return {"kernel": DOMINANT_KERNEL + " (input gradients of fc, qkv, attention projection and LM "
-                                        "head; forward q|k|v projection)",
+    name = DOMINANT_KERNEL + (" in binary16" if fp16 else "")
+    return {"kernel": name + " (input gradients of fc, qkv, attention projection and LM "
+                             "head; forward q|k|v projection)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(), "launches_per_step": n_launch,
+            "traffic": None if fp16 else measured_traffic(), "launches_per_step": n_launch,
             "ms_per_launch": round(ms_total / n_launch, 4),
             "flops_per_launch": flops / n_launch}
 
@@ -239,6 +243,8 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="instead of training, time sampling with the KV cache for B sequences")
+    ap.add_argument("--fp16", action="store_true",
+                    help="IEEE half precision with dynamic loss scaling instead of bf16")
     ap.add_argument("--probe", action="store_true",
                     help="only launch the dominant kernel and a calibration copy (counter runs)")
     args = ap.parse_args()
@@ -262,7 +268,8 @@ def main():
         return
     print(f"[bench] building model {WORKLOAD} B={B} T={T}", file=sys.stderr, flush=True)
     params = synth.init_params(dims, seed=1337)
-    model = bd.GPT(dims, bd.GPT_BF16, max_batch=B, init_params=params)
+    model = bd.GPT(dims, bd.GPT_FP16 if args.fp16 else bd.GPT_BF16, max_batch=B,
+                   init_params=params)
     nb = 4
     batches = []
     for i in range(nb):
@@ -272,10 +279,16 @@ def main():
 
     def step(i):
         idx, tgt = batches[i % nb]
-        model.forward(idx, tgt)
-        model.backward(zero_first=True)
         lr = min(6e-4 * (i + 1) / 715, 6e-4)
-        model.adamw_step(lr=lr, t=i + 1, max_norm=1.0)
+        if args.fp16:
+            # scale, backward, unscale, clip, step or skip, update
+            model.forward(idx, tgt, scaled=True)
+            model.backward(zero_first=True)
+            model.amp_step(lr=lr, max_norm=1.0)
+        else:
+            model.forward(idx, tgt)
+            model.backward(zero_first=True)
+            model.adamw_step(lr=lr, t=i + 1, max_norm=1.0)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -305,9 +318,10 @@ def main():
     mfu = fpt * tokens / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
     print(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), loss {loss:.4f}, "
           f"norm {norm:.4f}, MFU {mfu:.4f}", file=sys.stderr, flush=True)
+    scaler = model.scaler_state() if args.fp16 else None
     roof = None
     if not args.no_kernel_timing:
-        roof = time_dominant_kernel(torch, bd, B, T, dims)
+        roof = time_dominant_kernel(torch, bd, B, T, dims, fp16=args.fp16)
     model.close()
     del model
     torch.cuda.empty_cache()
@@ -315,19 +329,23 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(dims)
+    prec = "fp16 (dynamic loss scaling)" if args.fp16 else "bf16"
     out = {
-        "metric": "train tokens/sec + ms/step + MFU, GPT-2 124M bf16 B=16 T=1024, 1 MI355X",
+        "metric": f"train tokens/sec + ms/step + MFU, GPT-2 124M {prec} B=16 T=1024, 1 MI355X",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "ms_per_step_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "mfu": round(mfu, 4),
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": round(value / A100_TOKENS_PER_S, 3),
+        "vs_baseline": None if args.fp16 else round(value / A100_TOKENS_PER_S, 3),
         "baseline": "pages' 90 ms/step = ~182,000 tokens/s on one A100 SXM (context)",
-        "dtype": "bf16", "data": "synthetic (Zipf(1.1) token ids; random-init weights)",
+        "dtype": "fp16" if args.fp16 else "bf16",
+        "data": "synthetic (Zipf(1.1) token ids; random-init weights)",
         "config": {"workload": "GPT-2 124M training step (fwd+bwd+clip+AdamW), vocab 50304 "
                                "(pad masked), B=16, T=1024", "global_batch": B, "seq_len": T,
                    "flops_per_step": fpt * tokens, "loss": round(loss, 4), "grad_norm": round(norm, 4)},
+        **({"loss_scaler": dict(zip(("scale", "growth_tracker", "updates", "last_skipped"), scaler)),
+            "optimizer_steps_run": args.warmup + args.steps} if scaler else {}),
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -47,7 +47,7 @@ enum {
   GPT_EUNSUPPORTED = -5 /* shape this build's kernels do not cover */
 };
 
-enum { GPT_FP32 = 0, GPT_BF16 = 1 };
+enum { GPT_FP32 = 0, GPT_BF16 = 1, GPT_FP16 = 2 };
 
 /* Device flag bits reported by gpt_read_flags. */
 enum {
@@ -67,7 +67,10 @@ typedef struct {
                            accumulation, fp32 residual stream, LayerNorm,
                            softmax, loss, master weights and optimizer state
                            ("Let's reproduce GPT-2 (124M)", chapter "Float16,
-                           Gradient Scalers, BF16") */
+                           Gradient Scalers, BF16"); GPT_FP16: the same with
+                           IEEE binary16 in place of bf16, trained with
+                           dynamic loss scaling (gpt_forward_loss_scaled,
+                           gpt_amp_step) */
   int32_t max_batch;    /* largest B the workspace is sized for */
 } gpt_config;
 
@@ -75,10 +78,10 @@ typedef struct gpt_model gpt_model;
 
 /* Sizes the caller must allocate: n_params fp32 elements for each of params,
  * grads, adam_m and adam_v, and workspace_bytes of device memory (256-byte
- * aligned) for activations, the bf16 weight copy and scratch.
+ * aligned) for activations, the 16-bit weight copy and scratch.
  * Returns GPT_EINVAL for an invalid config, GPT_EUNSUPPORTED for a valid one
  * these kernels do not cover (n_embd a multiple of 4 up to 2048 and head width
- * up to 128; bf16 mode also needs n_embd % 64 == 0 and the padded vocabulary,
+ * up to 128; the 16-bit modes also need n_embd % 64 == 0 and the padded vocabulary,
  * rounded up to 64, at most 53248).  Head width 64 takes the flash-attention
  * kernels; other widths a slower per-query kernel. */
 int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace_bytes);
@@ -87,7 +90,7 @@ int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace
  * params, grads, adam_m, adam_v: device fp32 [n_params]; workspace: device
  * memory of workspace_bytes.  init_params: device fp32 [n_params] in the
  * canonical order, copied into params (NULL keeps params as they are).
- * adam_m and adam_v are zeroed.  The bf16 weight copy is written.
+ * adam_m and adam_v are zeroed.  The 16-bit weight copy (16-bit modes) is written.
  * The buffers must stay valid until gpt_destroy. */
 int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads,
              float* adam_m, float* adam_v, void* workspace, const float* init_params,
@@ -101,8 +104,8 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
  * loss_scale multiplies the gradient only (1/k under accumulation over k
  * micro-batches, "nanoGPT" Part IV Stage 4).
  * loss_out: device float, receives the unscaled mean loss (may be NULL).
- * logits_out: optional device buffer [B*T][Vp] (fp32 in GPT_FP32 mode, bf16
- * in GPT_BF16 mode) receiving the logits before the loss is taken.
+ * logits_out: optional device buffer [B*T][Vp] (fp32 in GPT_FP32 mode, the
+ * 16-bit format in GPT_BF16 and GPT_FP16 modes) receiving the logits before the loss is taken.
  * Errors: GPT_EINVAL (B < 1, B > max_batch, null idx), GPT_ESEQLEN. */
 int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets,
                      int32_t B, int32_t T, float loss_scale, float* loss_out,
@@ -129,6 +132,58 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
                    int32_t skip_nonfinite, float* norm_out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Dynamic loss scaling for float16 training ("nanoGPT", Part IV Stages 4-5,
+ * Part V Deep dive 2 and Part VIII checks 6-7; "Let's reproduce GPT-2
+ * (124M)", chapter "Float16, Gradient Scalers, BF16"): binary16 has a narrow
+ * exponent range, so the loss is multiplied by a scale before the backward
+ * pass, and the optimizer step unscales, clips, then steps or skips, and
+ * adapts the scale.  The order of one iteration is
+ *   gpt_forward_loss_scaled + gpt_backward (per micro-batch), gpt_amp_step.
+ * Usable in every mode; needed in GPT_FP16.
+ * ------------------------------------------------------------------------- */
+
+/* Scaler state, in DEVICE memory, owned by the caller; the library reads and
+ * updates it in stream order, so no host synchronisation is needed per step.
+ * Initialise it once (e.g. {65536.f, 0, 0, 0}). */
+typedef struct {
+  float scale;            /* S: multiplies the loss before the backward pass */
+  int32_t growth_tracker; /* clean steps since S last changed */
+  int32_t steps;          /* AdamW updates applied; skipped steps are not
+                             counted (the bias corrections use steps + 1) */
+  int32_t found_inf;      /* 1 if the last gpt_amp_step skipped its update */
+} gpt_loss_scaler;
+
+/* gpt_forward_loss, with the gradient w.r.t. the logits further multiplied by
+ * scaler->scale (read on the device when the kernel runs).  loss_out is still
+ * the unscaled mean loss.  Errors: as gpt_forward_loss, GPT_EINVAL for a null
+ * scaler. */
+int gpt_forward_loss_scaled(gpt_model* h, const int32_t* idx, const int32_t* targets,
+                            int32_t B, int32_t T, float loss_scale,
+                            const gpt_loss_scaler* scaler, float* loss_out,
+                            void* logits_out, void* stream);
+
+/* The optimizer step of a loss-scaled iteration, in the pages' order, with
+ * S = scaler->scale:
+ *   unscale:  the update uses grads / S (grads themselves are not modified);
+ *   clip:     norm = ||grads / S||_2, coef = min(1, max_norm/(norm+1e-6))
+ *             (max_norm <= 0: coef = 1);
+ *   step:     AdamW exactly as gpt_adamw_step at t = scaler->steps + 1 on
+ *             g = coef grads / S, unless norm is not finite (an inf or NaN
+ *             gradient element): then params, adam_m, adam_v stay untouched;
+ *   update:   not finite: S *= backoff_factor, growth_tracker = 0,
+ *             found_inf = 1; finite: steps += 1, found_inf = 0, and
+ *             growth_tracker += 1, which on reaching growth_interval becomes
+ *             0 with S *= growth_factor (kept only if finite).
+ * Readings (the pages give no values): the library defaults 2.0, 0.5, 2000.
+ * norm_out: device float receiving norm (may be NULL).  Errors: GPT_EINVAL
+ * (null handle or scaler, growth_interval < 1, growth_factor < 1,
+ * backoff_factor outside (0, 1]). */
+int gpt_amp_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
+                 float weight_decay, float max_norm, gpt_loss_scaler* scaler,
+                 float growth_factor, float backoff_factor, int32_t growth_interval,
+                 float* norm_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sampling from the model ("nanoGPT", Part IV, one generation: sample.py +
  * model.py, generate), with a cache of keys and values ("Build GPT from
  * scratch", exercise "Add a KV cache") so that a step feeds one new token per
@@ -140,7 +195,7 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
 
 /* Bytes of a cache for B sequences of up to max_len positions:
  * kv[layer][k|v][b][head][t][head_width] in the mode's activation type
- * (bf16 in GPT_BF16 mode, fp32 in GPT_FP32 mode).  -1 for an invalid config
+ * (bf16 in GPT_BF16 mode, binary16 in GPT_FP16 mode, fp32 in GPT_FP32 mode).  -1 for an invalid config
  * or size.  The caller allocates it on the device and owns it. */
 int64_t gpt_kv_cache_bytes(const gpt_config* cfg, int32_t B, int32_t max_len);
 
@@ -182,13 +237,15 @@ const char* gpt_strerror(int code);
  * Single-operation entry points.  They run one kernel of the step on caller
  * buffers so each can be checked and timed on its own.  All pointers are
  * device pointers; matrices are row-major; `act` buffers are fp32 when
- * bf16 == 0 and bf16 (raw uint16 storage) when bf16 != 0.
+ * dtype == GPT_FP32, bf16 when dtype == GPT_BF16 and binary16 when
+ * dtype == GPT_FP16 (both 16-bit formats as raw uint16 storage).  Another
+ * dtype value returns GPT_EINVAL.
  * ------------------------------------------------------------------------- */
 
 /* C = A B^T over K, plus optional bias[n] ("nanoGPT" Deep dive 1: the Linear
  * layers).  A: act [M][K], B: act [N][K], bias: fp32 [N] or NULL,
- * C: act [M][N] (fp32 when out_f32 != 0).  bf16 needs K % 8 == 0. */
-int gpt_op_linear(int32_t bf16, const void* A, const void* B, const float* bias,
+ * C: act [M][N] (fp32 when out_f32 != 0).  16-bit dtypes need K % 8 == 0. */
+int gpt_op_linear(int32_t dtype, const void* A, const void* B, const float* bias,
                   void* C, int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream);
 
 /* dW (+)= dY^T X: dY act [M][N], X act [M][K], dW fp32 [N][K];
@@ -196,32 +253,32 @@ int gpt_op_linear(int32_t bf16, const void* A, const void* B, const float* bias,
  * workspace: optional device fp32 scratch of workspace_bytes (NULL: none);
  * with enough of it a long reduction over M is split across workgroups and
  * the partial sums are added in a fixed order. */
-int gpt_op_linear_dw(int32_t bf16, const void* dY, const void* X, float* dW,
+int gpt_op_linear_dw(int32_t dtype, const void* dY, const void* X, float* dW,
                      int32_t accumulate, int32_t M, int32_t N, int32_t K,
                      float* workspace, int64_t workspace_bytes, void* stream);
 
 /* dX = dY W: dY act [M][N], W act [N][K], dX fp32 [M][K].  The input
  * gradient of a Linear layer. */
-int gpt_op_linear_dx(int32_t bf16, const void* dY, const void* W, float* dX,
+int gpt_op_linear_dx(int32_t dtype, const void* dY, const void* W, float* dX,
                      int32_t M, int32_t N, int32_t K, void* stream);
 
 /* Causal attention forward over qkv act [B*T][3*C] (q | k | v column blocks,
  * head h at columns h*hs) -> out act [B*T][C], lse fp32 [B][H][T]
  * (natural-log row logsumexp of the scaled scores).  "nanoGPT" Deep dive 1,
  * the manual path: softmax(q k^T / sqrt(hs) with -inf above the diagonal) v. */
-int gpt_op_attention_fwd(int32_t bf16, const void* qkv, void* out, float* lse,
+int gpt_op_attention_fwd(int32_t dtype, const void* qkv, void* out, float* lse,
                          int32_t B, int32_t T, int32_t H, int32_t C, void* stream);
 
 /* Its backward: dout act [B*T][C] -> dqkv act [B*T][3*C] (every element
  * written).  D: fp32 scratch [2][B][H][T]; D[0] receives rowsum(dout * out),
  * D[1] the row logsumexp times log2(e). */
-int gpt_op_attention_bwd(int32_t bf16, const void* qkv, const void* out,
+int gpt_op_attention_bwd(int32_t dtype, const void* qkv, const void* out,
                          const float* lse, const void* dout, void* dqkv, float* D,
                          int32_t B, int32_t T, int32_t H, int32_t C, void* stream);
 
 /* y = LayerNorm(x) w + b per row (biased variance, eps 1e-5):
  * x fp32 [M][C] -> y act [M][C], mean and rstd fp32 [M]. */
-int gpt_op_layernorm_fwd(int32_t bf16, const float* x, const float* w, const float* b,
+int gpt_op_layernorm_fwd(int32_t dtype, const float* x, const float* w, const float* b,
                          void* y, float* mean, float* rstd, int32_t M, int32_t C,
                          void* stream);
 
@@ -230,8 +287,8 @@ int gpt_op_layernorm_fwd(int32_t bf16, const float* x, const float* w, const flo
  * columns in [V, ldv)); loss: device fp32 scalar = mean over targets >= 0.
  * row_loss: device fp32 [N] receiving each row's loss (0 if ignored);
  * n_valid: device int32 receiving the count of targets >= 0.
- * bf16 needs ldv % 8 == 0 and ldv <= 53248. */
-int gpt_op_cross_entropy(int32_t bf16, void* logits, const int32_t* targets,
+ * 16-bit dtypes need ldv % 8 == 0 and ldv <= 53248. */
+int gpt_op_cross_entropy(int32_t dtype, void* logits, const int32_t* targets,
                          float* loss, float* row_loss, int32_t* n_valid,
                          float loss_scale, int32_t N, int32_t V, int32_t ldv,
                          void* stream);

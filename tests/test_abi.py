@@ -94,3 +94,33 @@ def test_null_arguments_are_rejected_without_a_device():
                         None) == bd.GPT_EINVAL
     assert b"invalid argument" in lib.gpt_strerror(bd.GPT_EINVAL)
     lib.gpt_destroy(None)
+
+
+def test_fp16_mode_sizes_match_bf16_and_share_its_limits():
+    for name in ("char", "gpt2"):
+        assert bd.query_sizes(dims_cfg(name, bd.GPT_FP16)) == bd.query_sizes(dims_cfg(name, bd.GPT_BF16))
+    cfg = dims_cfg("tiny", bd.GPT_FP16)
+    cfg.n_embd, cfg.n_head = 96, 3
+    with pytest.raises(bd.GptError) as e:
+        bd.query_sizes(cfg)
+    assert e.value.code == bd.GPT_EUNSUPPORTED
+    c = dims_cfg("gpt2", bd.GPT_FP16)
+    assert bd.lib.gpt_kv_cache_bytes(ctypes.byref(c), 2, 64) == \
+        bd.lib.gpt_kv_cache_bytes(ctypes.byref(dims_cfg("gpt2", bd.GPT_BF16)), 2, 64)
+
+
+def test_loss_scaling_and_dtype_arguments_are_checked_without_a_device():
+    lib = bd.lib
+    assert lib.gpt_forward_loss_scaled(None, None, None, 1, 1, 1.0, None, None, None,
+                                       None) == bd.GPT_EINVAL
+    assert lib.gpt_amp_step(None, 1e-3, .9, .95, 1e-8, .1, 1.0, None, 2.0, 0.5, 2000, None,
+                            None) == bd.GPT_EINVAL
+    # an unknown dtype of a single-op entry point fails before any HIP call
+    assert lib.gpt_op_linear(7, None, None, None, None, 0, 1, 1, 1, None) == bd.GPT_EINVAL
+    assert b"dtype" in lib.gpt_strerror(bd.GPT_EINVAL)
+    h = ctypes.c_void_p()
+    cfg = dims_cfg("tiny", bd.GPT_FP16)
+    cfg.n_head = 5
+    assert lib.gpt_init(ctypes.byref(h), ctypes.byref(cfg), None, None, None, None, None, None,
+                        None) == bd.GPT_EINVAL
+    assert not h.value

@@ -13,6 +13,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
+# PyTorch ships its own HIP runtime.  Loading it first makes the library bind to
+# that same runtime (it is already loaded under the name the library needs);
+# loading the library first would put a second HIP runtime in the process,
+# and whichever starts second finds no device.
+import torch  # noqa: F401  (imported for its side effect on the loader)
+
 LIB_PATH = os.environ.get("GPT_HIP_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libgpt_hip.so")
 if not os.path.exists(LIB_PATH):
@@ -20,7 +26,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 GPT_OK, GPT_EINVAL, GPT_ESEQLEN, GPT_ESTATE, GPT_EHIP, GPT_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
-GPT_FP32, GPT_BF16 = 0, 1
+GPT_FP32, GPT_BF16, GPT_FP16 = 0, 1, 2
 GPT_FLAG_BAD_TOKEN = 1
 
 
@@ -35,6 +41,8 @@ _SIGS = {
     "gpt_query_sizes": [ctypes.POINTER(gpt_config), ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
     "gpt_init": [ctypes.POINTER(_p), ctypes.POINTER(gpt_config), _p, _p, _p, _p, _p, _p, _p],
     "gpt_forward_loss": [_p, _p, _p, _i32, _i32, _f, _p, _p, _p],
+    "gpt_forward_loss_scaled": [_p, _p, _p, _i32, _i32, _f, _p, _p, _p, _p],
+    "gpt_amp_step": [_p, _f, _f, _f, _f, _f, _f, _p, _f, _f, _i32, _p, _p],
     "gpt_backward": [_p, _i32, _p],
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
     "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
@@ -108,6 +116,9 @@ class GPT:
         self.adam_v = torch.empty(self.n_params, **f32)
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         self.scalars = torch.zeros(4, **f32)  # loss, norm
+        # gpt_loss_scaler {float scale; int32 growth_tracker, steps, found_inf}
+        self.scaler = torch.zeros(4, dtype=torch.int32, device=device)
+        self.init_scaler()
         init = None
         if init_params is not None:
             init = torch.as_tensor(np.asarray(init_params, dtype=np.float32)).to(device)
@@ -122,20 +133,49 @@ class GPT:
     @property
     def act_dtype(self):
         import torch
-        return torch.bfloat16 if self.mode == GPT_BF16 else torch.float32
+        return {GPT_BF16: torch.bfloat16, GPT_FP16: torch.float16}.get(self.mode, torch.float32)
 
-    def forward(self, idx, targets=None, loss_scale=1.0, logits=False):
+    def forward(self, idx, targets=None, loss_scale=1.0, logits=False, scaled=False):
         """idx/targets: int32 cuda tensors [B, T].  Returns (loss tensor [1] or
-        None, logits tensor [B, T, Vp] or None)."""
+        None, logits tensor [B, T, Vp] or None).  scaled: the logits gradient
+        is further multiplied by the device loss scale (gpt_forward_loss_scaled)."""
         import torch
         B, T = idx.shape
         out = None
         if logits:
             out = torch.empty((B, T, self.dims["padded_vocab"]), dtype=self.act_dtype, device=idx.device)
         loss = self.scalars[0:1] if targets is not None else None
-        check(lib.gpt_forward_loss(self.handle, _ptr(idx), _ptr(targets), B, T, loss_scale,
-                                   _ptr(loss), _ptr(out), _stream()), "gpt_forward_loss")
+        if scaled:
+            check(lib.gpt_forward_loss_scaled(self.handle, _ptr(idx), _ptr(targets), B, T,
+                                              loss_scale, _ptr(self.scaler), _ptr(loss), _ptr(out),
+                                              _stream()), "gpt_forward_loss_scaled")
+        else:
+            check(lib.gpt_forward_loss(self.handle, _ptr(idx), _ptr(targets), B, T, loss_scale,
+                                       _ptr(loss), _ptr(out), _stream()), "gpt_forward_loss")
         return loss, out
+
+    # ------------------------------------------------------------ loss scaling
+    def init_scaler(self, scale=65536.0, growth_tracker=0, steps=0):
+        """Write the device gpt_loss_scaler state."""
+        import torch
+        st = np.array([0, growth_tracker, steps, 0], np.int32)
+        st[0] = np.array([scale], np.float32).view(np.int32)[0]
+        self.scaler.copy_(torch.from_numpy(st))
+
+    def scaler_state(self):
+        """(scale, growth_tracker, steps, found_inf) read back (synchronises)."""
+        st = self.scaler.cpu().numpy()
+        return float(st[:1].view(np.float32)[0]), int(st[1]), int(st[2]), int(st[3])
+
+    def amp_step(self, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0,
+                 growth_factor=2.0, backoff_factor=0.5, growth_interval=2000):
+        """Unscale, clip, AdamW or skip, scale update: gpt_amp_step.  Returns
+        the device norm of the unscaled gradients."""
+        norm = self.scalars[1:2]
+        check(lib.gpt_amp_step(self.handle, lr, beta1, beta2, eps, weight_decay, max_norm,
+                               _ptr(self.scaler), growth_factor, backoff_factor, growth_interval,
+                               _ptr(norm), _stream()), "gpt_amp_step")
+        return norm
 
     def backward(self, zero_first=True):
         check(lib.gpt_backward(self.handle, 1 if zero_first else 0, _stream()), "gpt_backward")
@@ -238,8 +278,9 @@ def sample(logits, vocab_size, temperature, top_k, u):
 
 # --------------------------------------------------------------------------- single ops
 def _bf(t):
+    """GPT_FP32 / GPT_BF16 / GPT_FP16 from a tensor's dtype."""
     import torch
-    return 1 if t.dtype == torch.bfloat16 else 0
+    return {torch.bfloat16: GPT_BF16, torch.float16: GPT_FP16}.get(t.dtype, GPT_FP32)
 
 
 def op_linear(A, B, bias=None, out_f32=False):
@@ -295,13 +336,14 @@ def op_attention_bwd(qkv, out, lse, dout, B, T, H):
     return dqkv
 
 
-def op_layernorm_fwd(x, w, b, bf16=False):
+def op_layernorm_fwd(x, w, b, bf16=False, fp16=False):
     import torch
     M, C = x.shape
-    y = torch.empty((M, C), dtype=torch.bfloat16 if bf16 else torch.float32, device=x.device)
+    dt = torch.bfloat16 if bf16 else torch.float16 if fp16 else torch.float32
+    y = torch.empty((M, C), dtype=dt, device=x.device)
     mean = torch.empty(M, dtype=torch.float32, device=x.device)
     rstd = torch.empty(M, dtype=torch.float32, device=x.device)
-    check(lib.gpt_op_layernorm_fwd(int(bf16), _ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(mean),
+    check(lib.gpt_op_layernorm_fwd(_bf(y), _ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(mean),
                                    _ptr(rstd), M, C, _stream()), "gpt_op_layernorm_fwd")
     return y, mean, rstd
 

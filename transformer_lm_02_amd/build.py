@@ -2,8 +2,11 @@
 
     python -m transformer_lm_02_amd.build        # or build() from Python
 
-Every source under csrc/ is compiled to an object in _build/ (in parallel),
-then linked into transformer_lm_02_amd/libgpt_hip.so.  Always recompiles.
+Every source under csrc/ is compiled to objects in _build/ (in parallel), then
+linked into transformer_lm_02_amd/libgpt_hip.so.  Always recompiles.  The
+kernels and the host orchestration are compiled twice, once per 16-bit
+activation format (bfloat16, and IEEE binary16 with GPT_HALF_FP16 defined);
+api.cpp, the C ABI that picks between the two, once.
 """
 from __future__ import annotations
 
@@ -29,9 +32,15 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+ONCE = ("api.cpp",)
+
+
+def _compile(job) -> str:
+    src, fp16 = job
+    obj = os.path.join(BUILD, os.path.basename(src) + (".f16.o" if fp16 else ".o"))
     cmd = [HIPCC, *FLAGS]
+    if fp16:
+        cmd += ["-DGPT_HALF_FP16"]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", src, "-o", obj]
@@ -45,8 +54,10 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+    jobs = [(f, False) for f in srcs] + [(f, True) for f in srcs
+                                          if os.path.basename(f) not in ONCE]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

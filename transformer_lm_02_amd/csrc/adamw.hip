@@ -10,6 +10,8 @@
 #include "common.h"
 #include "kernels.h"  // AdamChunk: {first element, count (multiple of 4), decay flag}
 
+namespace HALF_NS {
+
 // sum of squares, fp64 partial per block
 __global__ __launch_bounds__(256) void sumsq_kernel(const float* __restrict__ g, int64_t n,
                                                     double* __restrict__ part) {
@@ -48,14 +50,74 @@ __global__ void norm_finalize_kernel(const double* __restrict__ part, int nblk, 
   }
 }
 
-// One chunk per workgroup.  bf16 copy of the updated weights written when
-// shadow != nullptr.
+// Dynamic loss scaling ("nanoGPT", Part IV Stage 5 and Part V Deep dive 2;
+// "Let's reproduce GPT-2 (124M)", chapter "Float16, Gradient Scalers, BF16"):
+// the gradients hold the true gradient times the scale S.  From the norm of
+// the scaled gradients: norm = norm_s / S (the norm of the unscaled ones),
+// found_inf = norm_s not finite (an inf or NaN element; a sum of squares of
+// finite fp32 values cannot overflow fp64), coef = min(1, max_norm /
+// (norm + 1e-6)); scal[0] = coef / S (the factor the update applies to the
+// stored gradient), scal[1] = found_inf, scal[2..3] = the bias corrections
+// 1 - beta^t at t = steps + 1.  Then the scale update: an overflow multiplies
+// S by the backoff factor and restarts the count of clean steps; a clean step
+// counts an update and, when the count reaches the interval, multiplies S by
+// the growth factor (kept only if finite) and restarts the count.
+struct ScalerState {
+  float scale;
+  int32_t growth_tracker, steps, found_inf;
+};
+__global__ void amp_finalize_kernel(const double* __restrict__ part, int nblk, float max_norm,
+                                    float beta1, float beta2, ScalerState* __restrict__ st,
+                                    float growth, float backoff, int interval,
+                                    float* __restrict__ norm_out, float* __restrict__ scal) {
+  __shared__ double red[4];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nblk; i += 256) s += part[i];
+  s = wave_sum_d(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ScalerState q = *st;
+    const double inv = 1.0 / (double)q.scale;
+    const double norm = sqrt(red[0] + red[1] + red[2] + red[3]) * inv;
+    const bool found_inf = !isfinite(norm);
+    double coef = 1.0;
+    if (max_norm > 0.f && !found_inf) coef = fmin(1.0, (double)max_norm / (norm + 1e-6));
+    const double t = (double)(q.steps + 1);
+    scal[0] = (float)(coef * inv);
+    scal[1] = found_inf ? 1.f : 0.f;
+    scal[2] = (float)(1.0 - pow((double)beta1, t));
+    scal[3] = (float)(1.0 - pow((double)beta2, t));
+    if (norm_out) *norm_out = (float)norm;
+    if (found_inf) {
+      q.scale *= backoff;
+      q.growth_tracker = 0;
+    } else {
+      q.steps += 1;
+      if (++q.growth_tracker == interval) {
+        const float grown = q.scale * growth;
+        if (isfinite(grown)) q.scale = grown;
+        q.growth_tracker = 0;
+      }
+    }
+    q.found_inf = found_inf ? 1 : 0;
+    *st = q;
+  }
+}
+
+// One chunk per workgroup.  16-bit copy of the updated weights written when
+// shadow != nullptr.  bc_in_scal: the bias corrections come from scal[2..3]
+// (the loss-scaled step, whose step count lives on the device).
 __global__ __launch_bounds__(256) void adamw_kernel(
     float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
-    float* __restrict__ v, bf16_t* __restrict__ shadow, const AdamChunk* __restrict__ chunks,
+    float* __restrict__ v, h16_t* __restrict__ shadow, const AdamChunk* __restrict__ chunks,
     const float* __restrict__ scal, float lr, float beta1, float beta2, float eps, float wd,
-    float bc1, float bc2, int skip_nonfinite) {
+    float bc1, float bc2, int skip_nonfinite, int bc_in_scal) {
   if (skip_nonfinite && scal[1] != 0.f) return;
+  if (bc_in_scal) {
+    bc1 = scal[2];
+    bc2 = scal[3];
+  }
   const AdamChunk ch = chunks[blockIdx.x];
   const float coef = scal[0];
   const float decay = ch.decay ? 1.0f - lr * wd : 1.0f;
@@ -80,20 +142,20 @@ __global__ __launch_bounds__(256) void adamw_kernel(
     ((float4*)p)[e] = pp;
     ((float4*)m)[e] = mm;
     ((float4*)v)[e] = vv;
-    if (shadow) *(uint2*)(shadow + 4 * e) = make_uint2(pack2bf(pp.x, pp.y), pack2bf(pp.z, pp.w));
+    if (shadow) *(uint2*)(shadow + 4 * e) = make_uint2(pack2h(pp.x, pp.y), pack2h(pp.z, pp.w));
   }
 }
 
-// fp32 -> bf16 copy of the weights
-__global__ void to_bf16_kernel(const float* __restrict__ p, bf16_t* __restrict__ o, int64_t n) {
+// fp32 -> 16-bit copy of the weights
+__global__ void to_h16_kernel(const float* __restrict__ p, h16_t* __restrict__ o, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    o[i] = f2bf(p[i]);
+    o[i] = f2h(p[i]);
 }
 
 #define NORM_BLOCKS 1024
 int adamw_norm_blocks() { return NORM_BLOCKS; }
 
-int adamw_launch(float* p, const float* g, float* m, float* v, bf16_t* shadow, int64_t n,
+int adamw_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
                  const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
                  float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
                  float max_norm, int t, int skip_nonfinite, hipStream_t s) {
@@ -103,33 +165,47 @@ int adamw_launch(float* p, const float* g, float* m, float* v, bf16_t* shadow, i
   const float bc1 = (float)(1.0 - pow((double)beta1, (double)t));
   const float bc2 = (float)(1.0 - pow((double)beta2, (double)t));
   hipLaunchKernelGGL(adamw_kernel, dim3(nchunks), dim3(256), 0, s, p, g, m, v, shadow, chunks,
-                     scal, lr, beta1, beta2, eps, wd, bc1, bc2, skip_nonfinite);
+                     scal, lr, beta1, beta2, eps, wd, bc1, bc2, skip_nonfinite, 0);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int to_bf16_launch(const float* p, bf16_t* o, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(to_bf16_kernel, dim3(2048), dim3(256), 0, s, p, o, n);
+int adamw_amp_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
+                     const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
+                     float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
+                     float max_norm, float* scaler, float growth, float backoff, int interval,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(sumsq_kernel, dim3(NORM_BLOCKS), dim3(256), 0, s, g, n, norm_part);
+  hipLaunchKernelGGL(amp_finalize_kernel, dim3(1), dim3(256), 0, s, norm_part, NORM_BLOCKS,
+                     max_norm, beta1, beta2, (ScalerState*)scaler, growth, backoff, interval,
+                     norm_out, scal);
+  hipLaunchKernelGGL(adamw_kernel, dim3(nchunks), dim3(256), 0, s, p, g, m, v, shadow, chunks,
+                     scal, lr, beta1, beta2, eps, wd, 1.f, 1.f, 1, 1);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// Transposed bf16 copies of the weight matrices, so that the input-gradient
+int to_h16_launch(const float* p, h16_t* o, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(to_h16_kernel, dim3(2048), dim3(256), 0, s, p, o, n);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Transposed 16-bit copies of the weight matrices, so that the input-gradient
 // products dX = dY W read both operands along the reduction dimension.
 // One launch over a table of matrices; 64 x 64 tiles through LDS, moved with
 // 16-byte loads and stores (a tile that is partial or not 8-aligned goes
 // element by element).
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src,
-                                                             bf16_t* __restrict__ dst,
+__global__ __launch_bounds__(256) void transpose_h16_kernel(const h16_t* __restrict__ src,
+                                                             h16_t* __restrict__ dst,
                                                              const TransposeJob* __restrict__ jobs,
                                                              int njobs) {
-  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
+  __shared__ __attribute__((aligned(16))) h16_t tile[64][72];
   int j = 0;
   while (j + 1 < njobs && (int)blockIdx.x >= jobs[j + 1].tile_begin) ++j;
   const TransposeJob job = jobs[j];
   const int t = blockIdx.x - job.tile_begin;
   const int tiles_c = (job.cols + 63) / 64;
   const int r0 = (t / tiles_c) * 64, c0 = (t % tiles_c) * 64;
-  const bf16_t* S = src + job.src;
-  bf16_t* D = dst + job.dst;
+  const h16_t* S = src + job.src;
+  h16_t* D = dst + job.dst;
   const bool full = r0 + 64 <= job.rows && c0 + 64 <= job.cols && job.cols % 8 == 0 &&
                     job.ld % 8 == 0 && job.src % 8 == 0 && job.dst % 8 == 0;
   if (full) {
@@ -162,8 +238,10 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __res
   }
 }
 
-int transpose_bf16_launch(const bf16_t* src, bf16_t* dst, const TransposeJob* jobs, int njobs,
+int transpose_h16_launch(const h16_t* src, h16_t* dst, const TransposeJob* jobs, int njobs,
                           int total_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(total_tiles), dim3(256), 0, s, src, dst, jobs, njobs);
+  hipLaunchKernelGGL(transpose_h16_kernel, dim3(total_tiles), dim3(256), 0, s, src, dst, jobs, njobs);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+}  // namespace HALF_NS

@@ -3,13 +3,13 @@
 // What is computed is the manual path of "nanoGPT" (stanleyjacob.dev), Part V
 // Deep dive 1: per head, softmax(q k^T / sqrt(hs)) with the entries above the
 // diagonal at -inf, times v; q, k, v are the column blocks of the fused
-// c_attn output, head h at columns h*hs.  The bf16 kernels reach the same
+// c_attn output, head h at columns h*hs.  The 16-bit kernels reach the same
 // result tile by tile with an online softmax and never store the T x T
 // matrix ("Let's reproduce GPT-2 (124M)", chapter "Flash Attention, 96ms"):
 // the forward keeps the row logsumexp, the backward recomputes the
 // probabilities from it.
 //
-// bf16 kernels (head width 64) use v_mfma_f32_32x32x16_bf16.  The forward
+// 16-bit kernels (head width 64) use v_mfma_f32_32x32x16_bf16 (_f16 for binary16).  The forward
 // computes S^T = K Q^T so that one lane owns one query row: its running max
 // and sum stay in the lane, and the probabilities in the accumulator
 // registers are directly the B operand of O^T = V^T P^T.  The backward is two
@@ -19,6 +19,8 @@
 
 #include "common.h"
 #include "kernels.h"
+
+namespace HALF_NS {
 
 #define LOG2E 1.4426950408889634f
 #define LN2 0.6931471805599453f
@@ -55,7 +57,7 @@ __global__ void attn_fwd_generic(const T* __restrict__ qkv, T* __restrict__ out,
 }
 
 // D[bh][q] = sum_c dO[q][c] * O[q][c]  (= rowsum(P * dP)); with L2 given,
-// also L2[bh][q] = lse[bh][q] * log2(e) (the exponent offset of the bf16
+// also L2[bh][q] = lse[bh][q] * log2(e) (the exponent offset of the 16-bit
 // backward kernels)
 template <typename T>
 __global__ void attn_bwd_dot(const T* __restrict__ out, const T* __restrict__ dout,
@@ -145,8 +147,8 @@ __global__ void attn_bwd_dkdv_generic(const T* __restrict__ qkv, const float* __
   }
 }
 
-// ================================================================ bf16 flash kernels (hs = 64)
-// Tiles of 64 rows x 64 bf16 (one row per key or query, head dims
+// ================================================================ 16-bit flash kernels (hs = 64)
+// Tiles of 64 rows x 64 16-bit (one row per key or query, head dims
 // contiguous) go from HBM into LDS with buffer loads in LDS mode, through a
 // ring of NS stages.  A tile keeps its memory layout; the 16-byte chunk c of
 // row r is stored at position c ^ f(r), f(r) = 4*((r>>1)&1) + ((r>>2)&3),
@@ -155,7 +157,6 @@ __global__ void attn_bwd_dkdv_generic(const T* __restrict__ qkv, const float* __
 // the gfx950 transposing read ds_read_b64_tr_b16 of 4 rows x 32 columns (an
 // operand whose k index is the key or query).
 #define AS3(p) ((__attribute__((address_space(3))) void*)(p))
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int tsw(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
@@ -164,7 +165,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_
 // This wave's share (2 of 8 loads of 1 KB) of a 64 x 64 tile whose row 0 is
 // global row `row0` of a buffer with row pitch `ld` elements (rows past the
 // buffer's end read as zero).
-__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, int row0, int ld,
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, h16_t* lds, int row0, int ld,
                                          int col0, int lane, int wave) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -176,32 +177,32 @@ __device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, bf16_t* lds,
 }
 // 32x32x16 MFMA operand with rows = tile rows base..base+31 and k = head dims
 // 16ks + 8(lane/32) + 0..7 (plain read)
-__device__ __forceinline__ bf16x8_t frag_hd(const bf16_t* t, int base, int ks, int lane) {
+__device__ __forceinline__ h16x8_t frag_hd(const h16_t* t, int base, int ks, int lane) {
   const int r = base + (lane & 31), c = 2 * ks + (lane >> 5);
-  return *(const bf16x8_t*)(t + r * 64 + ((c ^ tsw(r)) << 3));
+  return *(const h16x8_t*)(t + r * 64 + ((c ^ tsw(r)) << 3));
 }
 // 32x32x16 MFMA operand with rows = head dims col0..col0+31 and k = tile rows
 // 16ks + 8(j/4) + 4(lane/32) + j%4 (j = 0..7), the order in which a 32x32
 // accumulator holds its rows (transposing read)
-__device__ __forceinline__ bf16x8_t frag_rows(const bf16_t* __restrict__ t, int col0, int ks, int lane) {
+__device__ __forceinline__ h16x8_t frag_rows(const h16_t* __restrict__ t, int col0, int ks, int lane) {
   const int G = lane >> 4, u = lane & 15;
   const int col = col0 + 16 * (G & 1) + 4 * (u & 3);
   const int r0 = 16 * ks + 4 * (G >> 1) + (u >> 2);
   const int c = col >> 3;
-  const bf16_t* pa = t + r0 * 64 + ((c ^ tsw(r0)) << 3) + (col & 7);
-  const bf16_t* pb = t + (r0 + 8) * 64 + ((c ^ tsw(r0 + 8)) << 3) + (col & 7);
-  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)pa);
-  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)pb);
+  const h16_t* pa = t + r0 * 64 + ((c ^ tsw(r0)) << 3) + (col & 7);
+  const h16_t* pb = t + (r0 + 8) * 64 + ((c ^ tsw(r0 + 8)) << 3) + (col & 7);
+  const h16x4_t lo = DS_READ_TR16_B64((__attribute__((address_space(3))) h16x4_t*)pa);
+  const h16x4_t hi = DS_READ_TR16_B64((__attribute__((address_space(3))) h16x4_t*)pb);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-// 8 accumulator values (registers 8s..8s+7 of a 32x32 tile) -> bf16 operand
-__device__ __forceinline__ bf16x8_t pack_acc(const f32x16_t& a, int s) {
+// 8 accumulator values (registers 8s..8s+7 of a 32x32 tile) -> 16-bit operand
+__device__ __forceinline__ h16x8_t pack_acc(const f32x16_t& a, int s) {
   uint4 v;
-  v.x = pack2bf(a[8 * s + 0], a[8 * s + 1]);
-  v.y = pack2bf(a[8 * s + 2], a[8 * s + 3]);
-  v.z = pack2bf(a[8 * s + 4], a[8 * s + 5]);
-  v.w = pack2bf(a[8 * s + 6], a[8 * s + 7]);
-  return *(bf16x8_t*)&v;
+  v.x = pack2h(a[8 * s + 0], a[8 * s + 1]);
+  v.y = pack2h(a[8 * s + 2], a[8 * s + 3]);
+  v.z = pack2h(a[8 * s + 4], a[8 * s + 5]);
+  v.w = pack2h(a[8 * s + 6], a[8 * s + 7]);
+  return *(h16x8_t*)&v;
 }
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
@@ -216,7 +217,7 @@ __device__ __forceinline__ void vm_wait_barrier() {
 // 2^x by the hardware instruction; every argument here is <= 0 or -inf, so
 // no range reduction is needed (results below 2^-126 flush to zero)
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-#define MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+#define MFMA32(a, b, c) MFMA_32X32X16(a, b, c)
 // row offset inside a 32x32 accumulator tile for register r of this lane
 #define ACC_ROW(r, lane) (8 * ((r) >> 2) + 4 * ((lane) >> 5) + ((r) & 3))
 // ring depths (stages of 64 rows in LDS) of the three kernels
@@ -231,7 +232,6 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 #endif
 #define TILE_ELEMS 4096
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <int N>
 using Slot = std::integral_constant<int, N>;
 // f(i + S, Slot<S>) for S = S0 .. NS-1 while i + S < n: the ring loop
@@ -253,11 +253,11 @@ __device__ __forceinline__ void slot_steps(int i, int n, F& f) {
 // of O^T = V^T P^T.  The key loop is unrolled by the ring depth so that every
 // LDS address is a per-lane base plus an immediate offset.
 template <int FLASH_NS>
-__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
-                                                           bf16_t* __restrict__ out,
+__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restrict__ qkv,
+                                                           h16_t* __restrict__ out,
                                                            float* __restrict__ lse, int B, int Tn,
                                                            int H, int C) {
-  __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int nqb = (Tn + 127) / 128;
@@ -265,19 +265,19 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
   const int bh = blockIdx.x % (B * H), b = bh / H, h = bh % H;
   const int q0 = qb * 128, qw = q0 + 32 * wave;
   const int ld = 3 * C;
-  const bf16_t* base = qkv + (int64_t)b * Tn * ld;
+  const h16_t* base = qkv + (int64_t)b * Tn * ld;
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(base, (uint32_t)((int64_t)Tn * ld * 2));
   const int my_q = qw + (lane & 31);
 
-  bf16x8_t fq[4];  // Q^T operand: lane holds Q[my_q][16ks + 8(lane/32) + 0..7]
+  h16x8_t fq[4];  // Q^T operand: lane holds Q[my_q][16ks + 8(lane/32) + 0..7]
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     uint4 v = make_uint4(0, 0, 0, 0);
     if (my_q < Tn) v = *(const uint4*)(base + (int64_t)my_q * ld + h * 64 + 16 * ks + 8 * (lane >> 5));
-    fq[ks] = *(bf16x8_t*)&v;
+    fq[ks] = *(h16x8_t*)&v;
   }
   const float sc = LOG2E * 0.125f;  // log2(e) / sqrt(64)
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const h16x2_t ones = {(h16_el)1.0f, (h16_el)1.0f};
   float m = -INFINITY, l = 0.f;     // m in log2 units of the scaled scores
   f32x16_t o[2] = {zero16(), zero16()};
   const int nkv = (min(Tn, q0 + 128) + 63) / 64;
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
       tile_dma(rs, ring[NX][0], r0, ld, C + h * 64, lane, wave);
       tile_dma(rs, ring[NX][1], r0, ld, 2 * C + h * 64, lane, wave);
     }
-    const bf16_t* tK = ring[SL][0];
-    const bf16_t* tV = ring[SL][1];
+    const h16_t* tK = ring[SL][0];
+    const h16_t* tV = ring[SL][1];
     const int kv0 = kb * 64;
     if (kv0 > qw + 31) return;  // every key of the block is after this wave's queries
     f32x16_t s[2] = {zero16(), zero16()};
@@ -341,13 +341,13 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          w[j] = pack2bf(fexp2(fmaf(s[t][8 * ss + 2 * j], sc, nm)),
+          w[j] = pack2h(fexp2(fmaf(s[t][8 * ss + 2 * j], sc, nm)),
                          fexp2(fmaf(s[t][8 * ss + 2 * j + 1], sc, nm)));
           // the row sum adds the probabilities as rounded for the product
-          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[j]), ones, l, false);
+          l = FDOT2(__builtin_bit_cast(h16x2_t, w[j]), ones, l);
         }
         const uint4 wv = make_uint4(w[0], w[1], w[2], w[3]);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, wv);
+        const h16x8_t pb = __builtin_bit_cast(h16x8_t, wv);
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
           o[ht] = MFMA32(frag_rows(tV, 32 * ht, 2 * t + ss, lane), pb, o[ht]);
@@ -357,15 +357,15 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
   const float lt = l + __shfl_xor(l, 32, 64);
   const float inv = 1.0f / lt;
   if (my_q < Tn) {
-    bf16_t* O = out + ((int64_t)b * Tn + my_q) * C + h * 64;
+    h16_t* O = out + ((int64_t)b * Tn + my_q) * C + h * 64;
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int hd = 32 * ht + 8 * rg + 4 * (lane >> 5);
         uint2 v;
-        v.x = pack2bf(o[ht][4 * rg + 0] * inv, o[ht][4 * rg + 1] * inv);
-        v.y = pack2bf(o[ht][4 * rg + 2] * inv, o[ht][4 * rg + 3] * inv);
+        v.x = pack2h(o[ht][4 * rg + 0] * inv, o[ht][4 * rg + 1] * inv);
+        v.y = pack2h(o[ht][4 * rg + 2] * inv, o[ht][4 * rg + 3] * inv);
         *(uint2*)(O + hd) = v;
       }
     if (lane < 32) lse[(int64_t)bh * Tn + my_q] = (m + __log2f(lt)) * LN2;
@@ -381,10 +381,10 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const bf16_t* __restr
 // [B*H*T, 2*B*H*T).
 template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
-    const bf16_t* __restrict__ qkv, const float* __restrict__ Dg, const bf16_t* __restrict__ dout,
-    bf16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
+    const h16_t* __restrict__ qkv, const float* __restrict__ Dg, const h16_t* __restrict__ dout,
+    h16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
   // per stage: Q tile, dO tile, 4 small slots (wave 0: scaled logsumexp, wave 1: D)
-  __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2 * TILE_ELEMS + 4 * 512];
+  __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2 * TILE_ELEMS + 4 * 512];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int bh = blockIdx.x % (B * H), b = bh / H, h = bh % H;
@@ -392,14 +392,14 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
   const int k0 = kblk * 128, kw = k0 + 32 * wave;
   const int ld = 3 * C;
   const int64_t bht = (int64_t)B * H * Tn;
-  const bf16_t* base = qkv + (int64_t)b * Tn * ld;
+  const h16_t* base = qkv + (int64_t)b * Tn * ld;
   const __amdgpu_buffer_rsrc_t rq = rsrc_of(base, (uint32_t)((int64_t)Tn * ld * 2));
   const __amdgpu_buffer_rsrc_t rdo = rsrc_of(dout + (int64_t)b * Tn * C, (uint32_t)((int64_t)Tn * C * 2));
   const float* small_src = Dg + (wave == 0 ? bht : 0) + (int64_t)bh * Tn;
   const __amdgpu_buffer_rsrc_t rsm = rsrc_of(small_src, (uint32_t)(Tn * 4));
 
   const int my_kv = kw + (lane & 31);
-  bf16x8_t fk[4], fv[4];  // K^T, V^T operands: lane holds row my_kv
+  h16x8_t fk[4], fv[4];  // K^T, V^T operands: lane holds row my_kv
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
@@ -407,15 +407,15 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
       a = *(const uint4*)(base + (int64_t)my_kv * ld + C + h * 64 + 16 * ks + 8 * (lane >> 5));
       c = *(const uint4*)(base + (int64_t)my_kv * ld + 2 * C + h * 64 + 16 * ks + 8 * (lane >> 5));
     }
-    fk[ks] = *(bf16x8_t*)&a;
-    fv[ks] = *(bf16x8_t*)&c;
+    fk[ks] = *(h16x8_t*)&a;
+    fv[ks] = *(h16x8_t*)&c;
   }
   const float sc = LOG2E * 0.125f;
   f32x16_t dv[2] = {zero16(), zero16()}, dk[2] = {zero16(), zero16()};
   const int qstart = k0;
   const int nq = (Tn - qstart + 63) / 64;
   // 5 loads per wave per stage: 2 + 2 tile loads and one small load
-  auto stage = [&](bf16_t* dst, int qs) {
+  auto stage = [&](h16_t* dst, int qs) {
     tile_dma(rq, dst, qs, ld, h * 64, lane, wave);
     tile_dma(rdo, dst + TILE_ELEMS, qs, C, h * 64, lane, wave);
     // wave 0 fetches the 64 scaled logsumexp values of the block, wave 1
@@ -434,8 +434,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     else vm_wait_barrier<0>();
     if (qi + FLASH_NS - 1 < nq)
       stage(ring[(SL + FLASH_NS - 1) % FLASH_NS], qstart + 64 * (qi + FLASH_NS - 1));
-    const bf16_t* tQ = ring[SL];
-    const bf16_t* tdO = tQ + TILE_ELEMS;
+    const h16_t* tQ = ring[SL];
+    const h16_t* tdO = tQ + TILE_ELEMS;
     const float* sL = (const float*)(tQ + 2 * TILE_ELEMS);
     const float* sD = (const float*)(tQ + 2 * TILE_ELEMS + 512);
     const int qs = qstart + 64 * qi;
@@ -474,8 +474,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
       }
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
-        const bf16x8_t pa = pack_acc(sa, ss);
-        const bf16x8_t da = pack_acc(dpa, ss);
+        const h16x8_t pa = pack_acc(sa, ss);
+        const h16x8_t da = pack_acc(dpa, ss);
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
           dv[ht] = MFMA32(pa, frag_rows(tdO, 32 * ht, 2 * t + ss, lane), dv[ht]);
@@ -491,9 +491,9 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) {
       const int kv = kw + ACC_ROW(r, lane);
       if (kv < Tn) {
-        bf16_t* row = dqkv + ((int64_t)b * Tn + kv) * ld + h * 64 + 32 * ht + (lane & 31);
-        row[C] = f2bf(dk[ht][r] * 0.125f);
-        row[2 * C] = f2bf(dv[ht][r]);
+        h16_t* row = dqkv + ((int64_t)b * Tn + kv) * ld + h * 64 + 32 * ht + (lane & 31);
+        row[C] = f2h(dk[ht][r] * 0.125f);
+        row[2 * C] = f2h(dv[ht][r]);
       }
     }
   if (cs_part) {
@@ -538,10 +538,10 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
 // operand of dQ^T += K^T dS^T, whose A operand is a transposing read of K.
 template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
-    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ outp, const float* __restrict__ lse,
-    float* __restrict__ Dg, const bf16_t* __restrict__ dout, bf16_t* __restrict__ dqkv,
+    const h16_t* __restrict__ qkv, const h16_t* __restrict__ outp, const float* __restrict__ lse,
+    float* __restrict__ Dg, const h16_t* __restrict__ dout, h16_t* __restrict__ dqkv,
     float* __restrict__ cs_part, int B, int Tn, int H, int C) {
-  __shared__ __attribute__((aligned(1024))) bf16_t ring[FLASH_NS][2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int nqb = (Tn + 127) / 128;
@@ -550,13 +550,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
   const int q0 = qb * 128, qw = q0 + 32 * wave;
   const int ld = 3 * C;
   const int64_t bht = (int64_t)B * H * Tn;
-  const bf16_t* base = qkv + (int64_t)b * Tn * ld;
+  const h16_t* base = qkv + (int64_t)b * Tn * ld;
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(base, (uint32_t)((int64_t)Tn * ld * 2));
   const int my_q = qw + (lane & 31);
 
   // lanes l and l+32 hold the two halves of query row my_q: Q and dO as MFMA
   // operands, and the attention output O to form D = rowsum(dO * O)
-  bf16x8_t fq[4], fdo[4];
+  h16x8_t fq[4], fdo[4];
   float dsum = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -567,13 +567,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
       c = *(const uint4*)(dout + ro);
       o = *(const uint4*)(outp + ro);
     }
-    fq[ks] = *(bf16x8_t*)&a;
-    fdo[ks] = *(bf16x8_t*)&c;
+    fq[ks] = *(h16x8_t*)&a;
+    fdo[ks] = *(h16x8_t*)&c;
     const uint32_t ov[4] = {o.x, o.y, o.z, o.w}, gv[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      dsum = fmaf(__uint_as_float(ov[j] << 16), __uint_as_float(gv[j] << 16), dsum);
-      dsum = fmaf(__uint_as_float(ov[j] & 0xffff0000u), __uint_as_float(gv[j] & 0xffff0000u), dsum);
+      dsum = fmaf(h_lo(ov[j]), h_lo(gv[j]), dsum);
+      dsum = fmaf(h_hi(ov[j]), h_hi(gv[j]), dsum);
     }
   }
   const float Dq = dsum + __shfl_xor(dsum, 32, 64);
@@ -604,8 +604,8 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
       tile_dma(rs, ring[NX][0], r0, ld, C + h * 64, lane, wave);
       tile_dma(rs, ring[NX][1], r0, ld, 2 * C + h * 64, lane, wave);
     }
-    const bf16_t* tK = ring[SL][0];
-    const bf16_t* tV = ring[SL][1];
+    const h16_t* tK = ring[SL][0];
+    const h16_t* tV = ring[SL][1];
     const int kv0 = kb * 64;
     if (kv0 > qw + 31) return;
     f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
-        const bf16x8_t db = pack_acc(dp[t], ss);
+        const h16x8_t db = pack_acc(dp[t], ss);
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
           dq[ht] = MFMA32(frag_rows(tK, 32 * ht, 2 * t + ss, lane), db, dq[ht]);
@@ -644,15 +644,15 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
   };
   for (int kb = 0; kb < nkv; kb += FLASH_NS) slot_steps<0, FLASH_NS>(kb, nkv, step);
   if (my_q < Tn) {
-    bf16_t* dQ = dqkv + ((int64_t)b * Tn + my_q) * ld + h * 64;
+    h16_t* dQ = dqkv + ((int64_t)b * Tn + my_q) * ld + h * 64;
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int hd = 32 * ht + 8 * rg + 4 * (lane >> 5);
         uint2 v;
-        v.x = pack2bf(dq[ht][4 * rg + 0] * 0.125f, dq[ht][4 * rg + 1] * 0.125f);
-        v.y = pack2bf(dq[ht][4 * rg + 2] * 0.125f, dq[ht][4 * rg + 3] * 0.125f);
+        v.x = pack2h(dq[ht][4 * rg + 0] * 0.125f, dq[ht][4 * rg + 1] * 0.125f);
+        v.y = pack2h(dq[ht][4 * rg + 2] * 0.125f, dq[ht][4 * rg + 3] * 0.125f);
         *(uint2*)(dQ + hd) = v;
       }
   }
@@ -686,17 +686,17 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
 }
 
 // ================================================================ launchers
-int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
+int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
                          int C, hipStream_t s) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
-  if (bf16 && hs == 64) {
+  if (h16 && hs == 64) {
     const int nqb = (Tn + 127) / 128;
     hipLaunchKernelGGL(flash_fwd_kernel<FLASH_FWD_NS>, dim3(nqb * B * H), dim3(256), 0, s,
-                       (const bf16_t*)qkv, (bf16_t*)out, lse, B, Tn, H, C);
-  } else if (bf16) {
-    hipLaunchKernelGGL(attn_fwd_generic<bf16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                       (const bf16_t*)qkv, (bf16_t*)out, lse, B, Tn, H, C);
+                       (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C);
+  } else if (h16) {
+    hipLaunchKernelGGL(attn_fwd_generic<h16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
+                       (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C);
   } else {
     hipLaunchKernelGGL(attn_fwd_generic<float>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
                        (const float*)qkv, (float*)out, lse, B, Tn, H, C);
@@ -705,32 +705,32 @@ int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int 
 }
 
 // D: fp32 scratch of 2*B*H*T elements (rowsum(dout * out), then the row
-// logsumexp times log2(e) for the bf16 head-width-64 kernels).
+// logsumexp times log2(e) for the 16-bit head-width-64 kernels).
 // cs_part / cs_out (optional): cs_out[n] (+)= column sums of dqkv (the bias
 // gradient of the fused q|k|v projection); cs_part is fp32 scratch of at
 // least max(B * cdiv(Tn, 128), colsum_part_rows(B * Tn)) x 3C elements.
-int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
+int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
                          float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
                          ColsumJob* defer) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
   const int64_t rows = (int64_t)B * H * Tn;
-  if (bf16) {
+  if (h16) {
     const bool flash = hs == 64;
     if (!flash)
-      hipLaunchKernelGGL(attn_bwd_dot<bf16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
-                         (const bf16_t*)out, (const bf16_t*)dout, lse, D, nullptr, B, Tn, H, C);
+      hipLaunchKernelGGL(attn_bwd_dot<h16_t>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
+                         (const h16_t*)out, (const h16_t*)dout, lse, D, nullptr, B, Tn, H, C);
     if (flash) {
       // the query-side kernel forms D and the scaled logsumexp of its rows,
       // so it runs first
       const int nb = (Tn + 127) / 128;
       float* cp = cs_out ? cs_part : nullptr;
       hipLaunchKernelGGL(flash_bwd_dq_kernel<FLASH_DQ_NS>, dim3(nb * B * H), dim3(256), 0, s,
-                         (const bf16_t*)qkv, (const bf16_t*)out, lse, D, (const bf16_t*)dout,
-                         (bf16_t*)dqkv, cp, B, Tn, H, C);
+                         (const h16_t*)qkv, (const h16_t*)out, lse, D, (const h16_t*)dout,
+                         (h16_t*)dqkv, cp, B, Tn, H, C);
       hipLaunchKernelGGL(flash_bwd_dkdv_kernel<FLASH_DKDV_NS>, dim3(nb * B * H), dim3(256), 0, s,
-                         (const bf16_t*)qkv, D, (const bf16_t*)dout, (bf16_t*)dqkv, cp, B, Tn, H, C);
+                         (const h16_t*)qkv, D, (const h16_t*)dout, (h16_t*)dqkv, cp, B, Tn, H, C);
       if (cs_out) {
         if (hipGetLastError() != hipSuccess) return -4;
         if (defer) {
@@ -744,10 +744,10 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
         return colsum_finalize_launch(cs_part, B * nb, 3 * C, cs_out, cs_beta, s);
       }
     } else {
-      hipLaunchKernelGGL(attn_bwd_dq_generic<bf16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                         (const bf16_t*)qkv, lse, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
-      hipLaunchKernelGGL(attn_bwd_dkdv_generic<bf16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                         (const bf16_t*)qkv, lse, D, (const bf16_t*)dout, (bf16_t*)dqkv, B, Tn, H, C);
+      hipLaunchKernelGGL(attn_bwd_dq_generic<h16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
+                         (const h16_t*)qkv, lse, D, (const h16_t*)dout, (h16_t*)dqkv, B, Tn, H, C);
+      hipLaunchKernelGGL(attn_bwd_dkdv_generic<h16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
+                         (const h16_t*)qkv, lse, D, (const h16_t*)dout, (h16_t*)dqkv, B, Tn, H, C);
     }
     if (cs_out && !flash) {
       if (hipGetLastError() != hipSuccess) return -4;
@@ -767,3 +767,5 @@ int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const floa
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+}  // namespace HALF_NS

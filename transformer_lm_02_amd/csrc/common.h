@@ -3,33 +3,75 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-typedef uint16_t bf16_t;  // raw bfloat16 storage
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// The 16-bit activation format is fixed per compilation: every kernel source
+// and the host orchestration are compiled twice, once for bfloat16 (namespace
+// b16) and once, with GPT_HALF_FP16 defined, for IEEE binary16 (namespace
+// f16).  Kernels name the format only through h16_t and the helpers below.
+#ifdef GPT_HALF_FP16
+#define HALF_NS f16
+typedef _Float16 h16_el;
+#define H16_NEG_INF 0xfc00u  // binary16 -inf
+#else
+#define HALF_NS b16
+typedef __bf16 h16_el;
+#define H16_NEG_INF 0xff80u  // bfloat16 -inf
+#endif
+
+namespace HALF_NS {
+
+typedef uint16_t h16_t;  // raw 16-bit storage of the build's format
+typedef h16_el h16x8_t __attribute__((ext_vector_type(8)));
+typedef h16_el h16x4_t __attribute__((ext_vector_type(4)));
+typedef h16_el h16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// ---------------------------------------------------------------- bf16 <-> fp32
-// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN): the gfx950
-// conversion instruction v_cvt_pk_bf16_f32
+// ---------------------------------------------------------------- 16-bit <-> fp32
+// fp32 -> 16-bit with round-to-nearest-even; NaN stays NaN, and in binary16 a
+// value beyond the largest finite one becomes inf (so that an overflow shows
+// up in the gradient norm instead of saturating silently).
 typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
-__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ h16_t f2h(float f) { return __builtin_bit_cast(h16_t, (h16_el)f); }
 // two floats -> packed pair (lo in bits 0..15)
-__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t,
-                            __builtin_convertvector((f32x2_cvt_t){lo, hi}, bf16x2_cvt_t));
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_cvt_t){lo, hi}, h16x2_t));
 }
+#ifdef GPT_HALF_FP16
+__device__ __forceinline__ float h2f(h16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ float h_lo(uint32_t w) { return h2f((h16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return h2f((h16_t)(w >> 16)); }
+// the binary16 builtins take __fp16 vectors
+typedef __fp16 fp16v8_t __attribute__((__vector_size__(8 * sizeof(__fp16))));
+typedef __fp16 fp16v4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __fp16 fp16v2_t __attribute__((__vector_size__(2 * sizeof(__fp16))));
+#define MFMA_32X32X16(a, b, c)                                                          \
+  __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(fp16v8_t, (a)),             \
+                                         __builtin_bit_cast(fp16v8_t, (b)), (c), 0, 0, 0)
+#define DS_READ_TR16_B64(p)                                                             \
+  __builtin_bit_cast(h16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16(                  \
+                                  (__attribute__((address_space(3))) fp16v4_t*)(p)))
+#define FDOT2(a, b, c)                                                                  \
+  __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16v2_t, (a)), __builtin_bit_cast(fp16v2_t, (b)), \
+                         (c), false)
+#else
+// a bfloat16 is the top half of an fp32
+__device__ __forceinline__ float h2f(h16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ float h_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+#define MFMA_32X32X16(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+#define DS_READ_TR16_B64(p) __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p)
+#define FDOT2(a, b, c) __builtin_amdgcn_fdot2_f32_bf16((a), (b), (c), false)
+#endif
 
-// Activation storage: float (fp32 mode) or bf16_t (bf16 mode).
+// Activation storage: float (fp32 mode) or h16_t (16-bit modes).
 template <typename T> struct Act;
 template <> struct Act<float> {
   __device__ __forceinline__ static float ld(const float* p) { return *p; }
   __device__ __forceinline__ static void st(float* p, float v) { *p = v; }
 };
-template <> struct Act<bf16_t> {
-  __device__ __forceinline__ static float ld(const bf16_t* p) { return bf2f(*p); }
-  __device__ __forceinline__ static void st(bf16_t* p, float v) { *p = f2bf(v); }
+template <> struct Act<h16_t> {
+  __device__ __forceinline__ static float ld(const h16_t* p) { return h2f(*p); }
+  __device__ __forceinline__ static void st(h16_t* p, float v) { *p = f2h(v); }
 };
 template <typename T> __device__ __forceinline__ float ldf(const T* p) { return Act<T>::ld(p); }
 template <typename T> __device__ __forceinline__ void stf(T* p, float v) { Act<T>::st(p, v); }
@@ -90,3 +132,5 @@ __device__ __forceinline__ void gelu_both(float u, float& g, float& gp) {
 }
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace HALF_NS

@@ -16,6 +16,8 @@
 #include "common.h"
 #include "kernels.h"
 
+namespace HALF_NS {
+
 namespace {
 
 // keys and values of rows [0, T) of every sequence (qkv [B*T][3C], head h at
@@ -52,8 +54,8 @@ __device__ __forceinline__ float dot_row(const float* __restrict__ q, const T* _
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          s = fmaf(q[e + 2 * j], __uint_as_float(w[j] << 16), s);
-          s = fmaf(q[e + 2 * j + 1], __uint_as_float(w[j] & 0xffff0000u), s);
+          s = fmaf(q[e + 2 * j], h_lo(w[j]), s);
+          s = fmaf(q[e + 2 * j + 1], h_hi(w[j]), s);
         }
       }
       return s;
@@ -179,8 +181,8 @@ __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(w[j] << 16);
-      v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      v[2 * j] = h_lo(w[j]);
+      v[2 * j + 1] = h_hi(w[j]);
     }
   } else {
     const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
@@ -491,26 +493,26 @@ __global__ __launch_bounds__(SAMP_THREADS) void sample_kernel(const float* __res
 
 }  // namespace
 
-int kv_store_launch(bool bf16, const void* qkv, void* kv, int B, int Tn, int H, int hs,
+int kv_store_launch(bool h16, const void* qkv, void* kv, int B, int Tn, int H, int hs,
                     int max_len, int pos0, hipStream_t s) {
   if (pos0 < 0 || pos0 + Tn > max_len) return -5;
   const int64_t n = (int64_t)B * Tn * 2 * H * hs;
   const unsigned grid = (unsigned)cdiv(n, 256);
-  if (bf16)
-    hipLaunchKernelGGL(kv_store_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, (const bf16_t*)qkv,
-                       (bf16_t*)kv, B, Tn, H, hs, max_len, pos0);
+  if (h16)
+    hipLaunchKernelGGL(kv_store_kernel<h16_t>, dim3(grid), dim3(256), 0, s, (const h16_t*)qkv,
+                       (h16_t*)kv, B, Tn, H, hs, max_len, pos0);
   else
     hipLaunchKernelGGL(kv_store_kernel<float>, dim3(grid), dim3(256), 0, s, (const float*)qkv,
                        (float*)kv, B, Tn, H, hs, max_len, pos0);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int decode_attn_launch(bool bf16, const void* qkv, const void* kv, void* out, int B, int H, int hs,
+int decode_attn_launch(bool h16, const void* qkv, const void* kv, void* out, int B, int H, int hs,
                        int max_len, int len, hipStream_t s) {
   if (hs < 1 || hs > 128 || len < 1 || len > max_len) return -5;
-  if (bf16)
-    hipLaunchKernelGGL(decode_attn_kernel<bf16_t>, dim3(B * H), dim3(64 * DEC_WAVES), 0, s,
-                       (const bf16_t*)qkv, (const bf16_t*)kv, (bf16_t*)out, B, H, hs, max_len, len);
+  if (h16)
+    hipLaunchKernelGGL(decode_attn_kernel<h16_t>, dim3(B * H), dim3(64 * DEC_WAVES), 0, s,
+                       (const h16_t*)qkv, (const h16_t*)kv, (h16_t*)out, B, H, hs, max_len, len);
   else
     hipLaunchKernelGGL(decode_attn_kernel<float>, dim3(B * H), dim3(64 * DEC_WAVES), 0, s,
                        (const float*)qkv, (const float*)kv, (float*)out, B, H, hs, max_len, len);
@@ -527,23 +529,23 @@ int sample_launch(const float* logits, int B, int V, int ldv, float temperature,
 }
 
 // ln: the rows are normalised in LDS, which bounds M * K
-bool gemv_fits(bool bf16, bool ln, int M, int K) {
-  const int es = bf16 ? 2 : 4;
+bool gemv_fits(bool h16, bool ln, int M, int K) {
+  const int es = h16 ? 2 : 4;
   return M >= 1 && M <= GEMV_MAX_M && K % 8 == 0 &&
          (!ln || (K <= GEMV_MAX_K_LN && (int64_t)M * K * es <= GEMV_LDS_BYTES));
 }
 
 // epi: 0 act, 1 fp32, 2 fp32 residual add, 3 gelu (act); ln_w set: A is fp32
 // and is normalised first; kv set (act epilogue): cache store of columns [C, 3C)
-int gemv_launch(bool bf16, int epi, const void* A, const float* ln_w, const float* ln_b,
+int gemv_launch(bool h16, int epi, const void* A, const float* ln_w, const float* ln_b,
                 const void* W, const float* bias, const float* aux, void* out, int M, int N, int K,
                 int ldo, void* kv, int H, int hs, int max_len, int pos, hipStream_t s) {
   const bool ln = ln_w != nullptr;
-  if (!gemv_fits(bf16, ln, M, K) || N < 1 || epi < 0 || epi > 3) return -5;
+  if (!gemv_fits(h16, ln, M, K) || N < 1 || epi < 0 || epi > 3) return -5;
   if (kv && epi != GV_ACT) return -5;
   if (((uintptr_t)A | (uintptr_t)W) & 15) return -5;
   GemvArgs a{A, ln_w, ln_b, W, bias, aux, out, M, N, K, ldo, kv, H, hs, max_len, pos, H * hs};
-  const size_t lds = ln ? (size_t)M * K * (bf16 ? 2 : 4) : 0;
+  const size_t lds = ln ? (size_t)M * K * (h16 ? 2 : 4) : 0;
   const int nc = N >= 8192 ? 4 : 2;
   const unsigned grid = (unsigned)cdiv(N, 4 * nc);
 #define GV(T, E, L, NCV) hipLaunchKernelGGL((gemv_kernel<T, E, L, NCV>), dim3(grid), dim3(256), lds, s, a)
@@ -554,11 +556,11 @@ int gemv_launch(bool bf16, int epi, const void* A, const float* ln_w, const floa
     case GV_RESID: GV(T, GV_RESID, L, NCV); break;   \
     default: GV(T, GV_GELU, L, NCV); break;          \
   }
-  if (bf16) {
+  if (h16) {
     if (ln) {
-      if (nc == 4) { GV_EPI(bf16_t, true, 4) } else { GV_EPI(bf16_t, true, 2) }
+      if (nc == 4) { GV_EPI(h16_t, true, 4) } else { GV_EPI(h16_t, true, 2) }
     } else {
-      if (nc == 4) { GV_EPI(bf16_t, false, 4) } else { GV_EPI(bf16_t, false, 2) }
+      if (nc == 4) { GV_EPI(h16_t, false, 4) } else { GV_EPI(h16_t, false, 2) }
     }
   } else {
     if (ln) {
@@ -571,3 +573,5 @@ int gemv_launch(bool bf16, int epi, const void* A, const float* ln_w, const floa
 #undef GV
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+}  // namespace HALF_NS

@@ -3,6 +3,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
+namespace HALF_NS {
+
 // Epilogues, applied per output element (m, n) to the fp32 accumulator:
 enum GemmEpi {
   EPI_ACT = 0,      // out_act[m][n] = acc + bias[n]
@@ -44,11 +48,11 @@ struct GemmEpiArgs {
 };
 
 // A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]; likewise B(n,k).
-// Loads of a k-contiguous operand require K % 8 == 0 (bf16); an m- or
+// Loads of a k-contiguous operand require K % 8 == 0 (16-bit); an m- or
 // n-contiguous operand reads rows k < ka_rows / kb_rows and columns below its
 // leading dimension.  Outputs are written for m < M, n < N.
 // ws / ws_bytes: optional fp32 scratch for split-K weight gradients.
-int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi,
+int gemm_launch(bool h16, bool a_kcontig, bool b_kcontig, int epi,
                 const void* A, int lda, const void* B, int ldb,
                 int M, int N, int K, int ka_rows, int kb_rows,
                 const GemmEpiArgs& e, hipStream_t stream,
@@ -56,3 +60,5 @@ int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi,
 
 // split-K scratch the launcher may use for an M x N weight gradient
 inline int64_t gemm_splitk_bytes(int64_t M, int64_t N) { return 16 * M * N * 4; }
+
+}  // namespace HALF_NS

@@ -3,7 +3,7 @@
 // ("nanoGPT" (stanleyjacob.dev), Part V Deep dive 1: c_attn, c_proj, c_fc,
 // the MLP projection and lm_head; their gradients are those of y = x W^T + b).
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950, 4 waves per workgroup in a
+// 16-bit path: v_mfma_f32_32x32x16_bf16 (or _f16) on gfx950, 4 waves per workgroup in a
 // 2x2 grid, BM x BN x 64 block tiles double-buffered in LDS, fp32
 // accumulation, and the elementwise work of the step fused into the
 // epilogue (bias, residual add, tanh-GELU and its derivative, fp32 gradient
@@ -12,6 +12,8 @@
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
+
+namespace HALF_NS {
 
 // ---------------------------------------------------------------- epilogue
 template <int EPI, typename T>
@@ -57,14 +59,14 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 }
 
 struct GemmArgs {
-  const bf16_t* A;
-  const bf16_t* B;
+  const h16_t* A;
+  const h16_t* B;
   int lda, ldb, M, N, K, ka_rows, kb_rows, tiles_m, tiles_n;
   GemmEpiArgs e;
 };
 
-// ---------------------------------------------------------------- bf16 MFMA kernel
-// LDS layouts (bf16 elements, one k-tile of 64):
+// ---------------------------------------------------------------- 16-bit MFMA kernel
+// LDS layouts (16-bit elements, one k-tile of 64):
 //  k-contiguous operand: [rows][64], the 16-byte chunk c of row r stored at
 //    chunk position c ^ (r & 7);
 //  m/n-contiguous operand (transposed while staging): [8 k-chunks][rows][8],
@@ -82,7 +84,7 @@ struct OperandTile {
   static constexpr int NREG = ROWS / 32;
 
   // global -> registers for k-tile starting at k0
-  __device__ __forceinline__ static void load(uint4 (&reg)[NREG], const bf16_t* __restrict__ P,
+  __device__ __forceinline__ static void load(uint4 (&reg)[NREG], const h16_t* __restrict__ P,
                                               int ld, int row0, int nrows, int k0, int K,
                                               int krows, int tid) {
     if constexpr (KC) {
@@ -114,7 +116,7 @@ struct OperandTile {
     }
   }
 
-  __device__ __forceinline__ static void store(const uint4 (&reg)[NREG], bf16_t* lds, int tid) {
+  __device__ __forceinline__ static void store(const uint4 (&reg)[NREG], h16_t* lds, int tid) {
     if constexpr (KC) {
 #pragma unroll
       for (int i = 0; i < NREG; ++i) {
@@ -153,8 +155,8 @@ template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
   using TA = OperandTile<BM, AK>;
   using TB = OperandTile<BN, BKC>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][TA::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][TB::ELEMS];
+  __shared__ __attribute__((aligned(16))) h16_t lds_a[2][TA::ELEMS];
+  __shared__ __attribute__((aligned(16))) h16_t lds_b[2][TB::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tm, tn;
@@ -188,23 +190,23 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
       TA::load(ra, p.A, p.lda, m0, a_rows, (kt + 1) * 64, p.K, p.ka_rows, tid);
       TB::load(rb, p.B, p.ldb, n0, b_rows, (kt + 1) * 64, p.K, p.kb_rows, tid);
     }
-    const bf16_t* la = lds_a[cur];
-    const bf16_t* lb = lds_b[cur];
+    const h16_t* la = lds_a[cur];
+    const h16_t* lb = lds_b[cur];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = 2 * ks + (lane >> 5);
-      bf16x8_t fa[TM], fb[TN];
+      h16x8_t fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        fa[i] = *(const bf16x8_t*)(la + TA::off(wm * (BM / 2) + 32 * i + (lane & 31), c));
+        fa[i] = *(const h16x8_t*)(la + TA::off(wm * (BM / 2) + 32 * i + (lane & 31), c));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        fb[j] = *(const bf16x8_t*)(lb + TB::off(wn * (BN / 2) + 32 * j + (lane & 31), c));
+        fb[j] = *(const h16x8_t*)(lb + TB::off(wn * (BN / 2) + 32 * j + (lane & 31), c));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = MFMA_32X32X16(fa[i], fb[j], acc[i][j]);
     }
     if (kt + 1 < nk) {
       TA::store(ra, lds_a[cur ^ 1], tid);
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < p.M) epi_apply<EPI, bf16_t>(p.e, row, col, acc[i][j][r]);
+        if (row < p.M) epi_apply<EPI, h16_t>(p.e, row, col, acc[i][j][r]);
       }
     }
 }
@@ -320,7 +322,7 @@ static void run_f32(const GemmArgsF& a, hipStream_t s) {
 
 #define GEMM_CASE(AKV, BKV, EPIV)                                                          \
   if (a_kcontig == AKV && b_kcontig == BKV && epi == EPIV) {                              \
-    if (bf16) run_mfma_shape<AKV, BKV, EPIV>(pa, stream);                                  \
+    if (h16) run_mfma_shape<AKV, BKV, EPIV>(pa, stream);                                  \
     else run_f32<AKV, BKV, EPIV>(pf, stream);                                              \
     return hipGetLastError() == hipSuccess ? 0 : -4;                                       \
   }
@@ -329,40 +331,40 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
                  int ldb, int M, int N, int K, int ka_rows, int kb_rows, const GemmEpiArgs& e,
                  float* ws, int64_t ws_bytes, hipStream_t s);
 
-static int gemm_launch_plain(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* A,
+static int gemm_launch_plain(bool h16, bool a_kcontig, bool b_kcontig, int epi, const void* A,
                              int lda, const void* B, int ldb, int M, int N, int K, int ka_rows,
                              int kb_rows, const GemmEpiArgs& e, hipStream_t stream, float* ws,
                              int64_t ws_bytes);
 
-int gemm_launch(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda,
+int gemm_launch(bool h16, bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda,
                 const void* B, int ldb, int M, int N, int K, int ka_rows, int kb_rows,
                 const GemmEpiArgs& e, hipStream_t stream, float* ws, int64_t ws_bytes) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  if (bf16) {
+  if (h16) {
     // the pipelined kernel when the shape allows it (column sums included)
     const int rc = gemm2_launch(a_kcontig, b_kcontig, epi, A, lda, B, ldb, M, N, K, ka_rows,
                                 kb_rows, e, ws, ws_bytes, stream);
     if (rc != -5) return rc == 0 ? (hipGetLastError() == hipSuccess ? 0 : -4) : rc;
   }
-  const int rc = gemm_launch_plain(bf16, a_kcontig, b_kcontig, epi, A, lda, B, ldb, M, N, K,
+  const int rc = gemm_launch_plain(h16, a_kcontig, b_kcontig, epi, A, lda, B, ldb, M, N, K,
                                    ka_rows, kb_rows, e, stream, ws, ws_bytes);
   if (rc != 0 || !e.cs_out) return rc;
   if (e.ldc != N) return -5;
-  return colsum_launch(bf16, e.out, M, N, e.cs_part, e.cs_out, e.cs_beta, stream);
+  return colsum_launch(h16, e.out, M, N, e.cs_part, e.cs_out, e.cs_beta, stream);
 }
 
-static int gemm_launch_plain(bool bf16, bool a_kcontig, bool b_kcontig, int epi, const void* A,
+static int gemm_launch_plain(bool h16, bool a_kcontig, bool b_kcontig, int epi, const void* A,
                              int lda, const void* B, int ldb, int M, int N, int K, int ka_rows,
                              int kb_rows, const GemmEpiArgs& e, hipStream_t stream, float* ws,
                              int64_t ws_bytes) {
   (void)ws;
   (void)ws_bytes;
-  if (bf16) {
+  if (h16) {
     if ((a_kcontig && (K % 8 || lda % 8)) || (b_kcontig && (K % 8 || ldb % 8))) return -5;
     if ((!a_kcontig && lda % 8) || (!b_kcontig && ldb % 8)) return -5;
     if (((uintptr_t)A | (uintptr_t)B) & 15) return -5;
   }
-  GemmArgs pa{(const bf16_t*)A, (const bf16_t*)B, lda, ldb, M, N, K, ka_rows, kb_rows, 0, 0, e};
+  GemmArgs pa{(const h16_t*)A, (const h16_t*)B, lda, ldb, M, N, K, ka_rows, kb_rows, 0, 0, e};
   GemmArgsF pf{(const float*)A, (const float*)B, lda, ldb, M, N, K, ka_rows, kb_rows, 0, 0, e};
   // forward: y = x W^T (+ bias / residual / GELU)
   GEMM_CASE(true, true, EPI_ACT)
@@ -378,3 +380,5 @@ static int gemm_launch_plain(bool bf16, bool a_kcontig, bool b_kcontig, int epi,
   GEMM_CASE(false, false, EPI_ACCUM)
   return -5;
 }
+
+}  // namespace HALF_NS

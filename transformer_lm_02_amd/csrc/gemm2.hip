@@ -1,4 +1,4 @@
-// Pipelined bf16 MFMA GEMM for gfx950: C[m][n] = sum_k A(m,k) B(n,k).
+// Pipelined 16-bit MFMA GEMM for gfx950: C[m][n] = sum_k A(m,k) B(n,k).
 //
 // Same products and epilogues as gemm.hip (the Linear layers of "nanoGPT"
 // (stanleyjacob.dev), Part V Deep dive 1, their input and weight gradients,
@@ -12,7 +12,7 @@
 //    operand (a transposed use: weight gradients, input gradients through
 //    W) stays in its memory layout [64][rows] and is read with the gfx950
 //    transposing LDS load ds_read_b64_tr_b16, so no register transpose;
-//  * v_mfma_f32_32x32x16_bf16, 4 waves in a 2x2 grid, fp32 accumulators;
+//  * v_mfma_f32_32x32x16_bf16 (or _f16), 4 waves in a 2x2 grid, fp32 accumulators;
 //  * the epilogue goes through LDS so every lane stores 8 contiguous outputs;
 //  * weight gradients with few output tiles split K over workgroups into an
 //    fp32 partial buffer that a second kernel sums in a fixed order.
@@ -22,8 +22,9 @@
 #include "gemm.h"
 #include "kernels.h"
 
+namespace HALF_NS {
+
 #define AS3(p) ((__attribute__((address_space(3))) void*)(p))
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -33,7 +34,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// One operand tile of ROWS x BK (k) bf16 per stage.  Each wave issues
+// One operand tile of ROWS x BK (k) 16-bit per stage.  Each wave issues
 // ROWS*BK/2048 loads of 1 KB (64 lanes x 16 bytes, contiguous in LDS).
 template <int ROWS, bool KC, int BK>
 struct Stage {
@@ -84,7 +85,7 @@ struct Stage {
   // offset in the scalar offset operand, so a load needs no vector ALU work;
   // a k-tile that crosses K (or the rows of an m/n-contiguous operand) sends
   // each lane's chunks past the end to an offset beyond the buffer instead.
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, int kt, int ld,
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, h16_t* lds, int kt, int ld,
                                         int K, int wave) const {
     if ((kt + 1) * BK <= kfast) {
       const uint32_t soff =
@@ -108,23 +109,23 @@ struct Stage {
     }
   }
   // MFMA 32x32x16 operand: lane holds (row rbase + lane%32, k 16ks + 8(lane/32) + 0..7)
-  __device__ __forceinline__ static bf16x8_t frag(const bf16_t* __restrict__ lds, int rbase, int ks,
+  __device__ __forceinline__ static h16x8_t frag(const h16_t* __restrict__ lds, int rbase, int ks,
                                                   int lane) {
     if constexpr (KC) {
       const int r = rbase + (lane & 31), c = 2 * ks + (lane >> 5);
-      return *(const bf16x8_t*)(lds + r * BK + ((c ^ swz(r)) << 3));
+      return *(const h16x8_t*)(lds + r * BK + ((c ^ swz(r)) << 3));
     } else {
       const int G = lane >> 4, t = lane & 15;
       const int m = rbase + 16 * (G & 1) + 4 * (t & 3);
       const int k0 = 16 * ks + 8 * (G >> 1) + (t >> 2);
       const int c = m >> 3;
       const int ka = k0, kb = k0 + 4;
-      const bf16_t* pa = lds + ka * ROWS + ((c ^ (4 * (ka & 3))) << 3) + (m & 7);
-      const bf16_t* pb = lds + kb * ROWS + ((c ^ (4 * (kb & 3))) << 3) + (m & 7);
-      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4_t*)(pa));
-      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4_t*)(pb));
+      const h16_t* pa = lds + ka * ROWS + ((c ^ (4 * (ka & 3))) << 3) + (m & 7);
+      const h16_t* pb = lds + kb * ROWS + ((c ^ (4 * (kb & 3))) << 3) + (m & 7);
+      const h16x4_t lo = DS_READ_TR16_B64(
+          (__attribute__((address_space(3))) h16x4_t*)(pa));
+      const h16x4_t hi = DS_READ_TR16_B64(
+          (__attribute__((address_space(3))) h16x4_t*)(pb));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
@@ -137,8 +138,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 struct Gemm2Args {
-  const bf16_t* A;
-  const bf16_t* B;
+  const h16_t* A;
+  const h16_t* B;
   int lda, ldb, M, N, K, ka_rows, kb_rows, tiles_m, tiles_n;
   int ksplit, k_tiles_per_split;
   float* part;  // split-K partials [ksplit][M][N] (EPI_ACCUM with ksplit > 1)
@@ -161,7 +162,7 @@ __device__ __forceinline__ void tile_coords2(int wg, int tiles_m, int tiles_n, i
 }
 
 // Operand an epilogue reads besides the accumulators (8 consecutive outputs
-// of one row): the residual (fp32), the GELU pre-activation (bf16) or the
+// of one row): the residual (fp32), the GELU pre-activation (16-bit) or the
 // gradient being accumulated into (fp32).  Loaded for a whole slab of rows
 // before any of them is stored, so the loads overlap.
 struct Aux8 {
@@ -177,7 +178,7 @@ __device__ __forceinline__ Aux8 aux8(const GemmEpiArgs& e, int splitk, int m, in
     x.a = s[0];
     x.b = s[1];
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    const uint4 u = *(const uint4*)((const bf16_t*)e.aux + i);
+    const uint4 u = *(const uint4*)((const h16_t*)e.aux + i);
     x.a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
                       __uint_as_float(u.w));
   } else if constexpr (EPI == EPI_ACCUM) {
@@ -221,28 +222,28 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
     o[1] = make_float4(x.b.x + v[4] + bias8[4], x.b.y + v[5] + bias8[5], x.b.z + v[6] + bias8[6],
                        x.b.w + v[7] + bias8[7]);
   } else if constexpr (EPI == EPI_ACT) {
-    *(uint4*)((bf16_t*)e.out + i) =
-        make_uint4(pack2bf(v[0] + bias8[0], v[1] + bias8[1]), pack2bf(v[2] + bias8[2], v[3] + bias8[3]),
-                   pack2bf(v[4] + bias8[4], v[5] + bias8[5]), pack2bf(v[6] + bias8[6], v[7] + bias8[7]));
+    *(uint4*)((h16_t*)e.out + i) =
+        make_uint4(pack2h(v[0] + bias8[0], v[1] + bias8[1]), pack2h(v[2] + bias8[2], v[3] + bias8[3]),
+                   pack2h(v[4] + bias8[4], v[5] + bias8[5]), pack2h(v[6] + bias8[6], v[7] + bias8[7]));
   } else if constexpr (EPI == EPI_GELU) {
     // the backward needs only gelu'(u): it is stored in place of u
     float g[8], gp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) gelu_both(v[j] + bias8[j], g[j], gp[j]);
-    *(uint4*)((bf16_t*)e.out + i) = make_uint4(pack2bf(gp[0], gp[1]), pack2bf(gp[2], gp[3]),
-                                               pack2bf(gp[4], gp[5]), pack2bf(gp[6], gp[7]));
-    *(uint4*)((bf16_t*)e.out2 + i) =
-        make_uint4(pack2bf(g[0], g[1]), pack2bf(g[2], g[3]), pack2bf(g[4], g[5]), pack2bf(g[6], g[7]));
-  } else {  // EPI_GELU_BWD: the bf16 gelu'(u) values travel in x.a's bits
+    *(uint4*)((h16_t*)e.out + i) = make_uint4(pack2h(gp[0], gp[1]), pack2h(gp[2], gp[3]),
+                                               pack2h(gp[4], gp[5]), pack2h(gp[6], gp[7]));
+    *(uint4*)((h16_t*)e.out2 + i) =
+        make_uint4(pack2h(g[0], g[1]), pack2h(g[2], g[3]), pack2h(g[4], g[5]), pack2h(g[6], g[7]));
+  } else {  // EPI_GELU_BWD: the 16-bit gelu'(u) values travel in x.a's bits
     const uint32_t w[4] = {__float_as_uint(x.a.x), __float_as_uint(x.a.y), __float_as_uint(x.a.z),
                            __float_as_uint(x.a.w)};
     float d[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) d[j] = v[j] * bf2f((bf16_t)(w[j >> 1] >> (16 * (j & 1))));
+    for (int j = 0; j < 8; ++j) d[j] = v[j] * h2f((h16_t)(w[j >> 1] >> (16 * (j & 1))));
 #pragma unroll
     for (int j = 0; j < 8; ++j) csum[j] += d[j];
-    *(uint4*)((bf16_t*)e.out + i) =
-        make_uint4(pack2bf(d[0], d[1]), pack2bf(d[2], d[3]), pack2bf(d[4], d[5]), pack2bf(d[6], d[7]));
+    *(uint4*)((h16_t*)e.out + i) =
+        make_uint4(pack2h(d[0], d[1]), pack2h(d[2], d[3]), pack2h(d[4], d[5]), pack2h(d[6], d[7]));
   }
 }
 
@@ -256,9 +257,9 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   constexpr int KS = BK / 16;               // MFMA k-steps per k-tile
   constexpr int EP_PITCH = WC + 8;          // fp32 staging pitch: rows r, r+4 32 banks apart
   constexpr int LDS_ELEMS_RING = NS * STAGE_ELEMS;
-  constexpr int LDS_ELEMS_EPI = 4 * 32 * EP_PITCH * 2;  // in bf16 units
+  constexpr int LDS_ELEMS_EPI = 4 * 32 * EP_PITCH * 2;  // in 16-bit units
   constexpr int LDS_ELEMS = LDS_ELEMS_RING > LDS_ELEMS_EPI ? LDS_ELEMS_RING : LDS_ELEMS_EPI;
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[LDS_ELEMS];
+  __shared__ __attribute__((aligned(1024))) h16_t lds[LDS_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -310,11 +311,11 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
         sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + kt + NS - 1, p.lda, p.K, wave);
         sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + kt + NS - 1, p.ldb, p.K, wave);
       }
-      const bf16_t* la = lds + (kt % NS) * STAGE_ELEMS;
-      const bf16_t* lb = la + SA::ELEMS;
+      const h16_t* la = lds + (kt % NS) * STAGE_ELEMS;
+      const h16_t* lb = la + SA::ELEMS;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8_t fa[TM], fb[TN];
+        h16x8_t fa[TM], fb[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i) fa[i] = SA::frag(la, wm * WR + 32 * i, ks, lane);
 #pragma unroll
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = MFMA_32X32X16(fa[i], fb[j], acc[i][j]);
       }
     }
   } else {
@@ -334,12 +335,12 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
     // Before each such barrier the wave's LDS reads of the older stage have
     // completed (lgkmcnt 0), so the DMA that refills that slot cannot overtake
     // them.
-    bf16x8_t fa[2][TM], fb[2][TN];
+    h16x8_t fa[2][TM], fb[2][TN];
     if (nk > 0) {
       if (NS - 2 < nk) wait_vm_barrier<(NS - 2) * L>();
       else wait_vm_barrier<0>();
-      const bf16_t* la = lds;
-      const bf16_t* lb = la + SA::ELEMS;
+      const h16_t* la = lds;
+      const h16_t* lb = la + SA::ELEMS;
   #pragma unroll
       for (int i = 0; i < TM; ++i) fa[0][i] = SA::frag(la, wm * WR + 32 * i, 0, lane);
   #pragma unroll
@@ -354,8 +355,8 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
         sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + kt + NS - 1, p.lda, p.K, wave);
         sb.issue(rb, lds + s * STAGE_ELEMS + SA::ELEMS, kt0 + kt + NS - 1, p.ldb, p.K, wave);
       }
-      const bf16_t* la = lds + (kt % NS) * STAGE_ELEMS;
-      const bf16_t* lb = la + SA::ELEMS;
+      const h16_t* la = lds + (kt % NS) * STAGE_ELEMS;
+      const h16_t* lb = la + SA::ELEMS;
   #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int cur = ks & 1;  // KS is even: k-step 0 of every tile uses buffer 0
@@ -372,8 +373,8 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
           __builtin_amdgcn_s_waitcnt(0xC07F);
           if (kt + NS - 1 < nk) wait_vm_barrier<(NS - 2) * L>();
           else wait_vm_barrier<0>();
-          const bf16_t* na = lds + ((kt + 1) % NS) * STAGE_ELEMS;
-          const bf16_t* nb = na + SA::ELEMS;
+          const h16_t* na = lds + ((kt + 1) % NS) * STAGE_ELEMS;
+          const h16_t* nb = na + SA::ELEMS;
   #pragma unroll
           for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = SA::frag(na, wm * WR + 32 * i, 0, lane);
   #pragma unroll
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
         for (int i = 0; i < TM; ++i)
   #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = MFMA_32X32X16(fa[cur][i], fb[cur][j], acc[i][j]);
         // interleave: LDS reads between MFMAs
   #pragma unroll
         for (int g = 0; g < TM + TN; ++g) {
@@ -592,7 +593,7 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
 
 }  // namespace
 
-// The pipelined kernel covers bf16 with k-contiguous K % 8 == 0, every
+// The pipelined kernel covers 16-bit with k-contiguous K % 8 == 0, every
 // leading dimension % 8 == 0, N % 8 == 0, ldc % 8 == 0 and operands below
 // 4 GiB; otherwise returns -5 and the caller uses gemm.hip's kernel.
 int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda, const void* B,
@@ -606,7 +607,7 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
   const int64_t abytes = (int64_t)(a_kcontig ? M : ka_rows) * lda * 2;
   const int64_t bbytes = (int64_t)(b_kcontig ? N : kb_rows) * ldb * 2;
   if (abytes >= (1ll << 32) - 4096 || bbytes >= (1ll << 32) - 4096) return -5;
-  Gemm2Args p{(const bf16_t*)A, (const bf16_t*)B, lda, ldb, M, N, K, ka_rows, kb_rows, 0, 0, 1, 0,
+  Gemm2Args p{(const h16_t*)A, (const h16_t*)B, lda, ldb, M, N, K, ka_rows, kb_rows, 0, 0, 1, 0,
               nullptr, e};
 #define G2(AKV, BKV, EPIV) \
   if (a_kcontig == AKV && b_kcontig == BKV && epi == EPIV) return dispatch2<AKV, BKV, EPIV>(p, ws, ws_bytes, s);
@@ -622,3 +623,5 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
 #undef G2
   return -5;
 }
+
+}  // namespace HALF_NS

@@ -16,23 +16,22 @@
 #include <vector>
 
 #include "gpt_hip.h"
+#include "api_impl.h"
 #include "kernels.h"
 
-static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
+namespace HALF_NS {
 namespace {
 
-thread_local std::string g_err;
 
 int fail(int code, const char* what) {
-  g_err = what;
+  gpt_error_text() = what;
   return code;
 }
 int map_rc(int rc) {
   if (rc == 0) return GPT_OK;
   if (rc == -5) return GPT_EUNSUPPORTED;
   hipError_t e = hipGetLastError();
-  g_err = hipGetErrorString(e);
+  gpt_error_text() = hipGetErrorString(e);
   return GPT_EHIP;
 }
 #define CK(x)                       \
@@ -44,7 +43,7 @@ int map_rc(int rc) {
   do {                                           \
     hipError_t e_ = (x);                         \
     if (e_ != hipSuccess) {                      \
-      g_err = hipGetErrorString(e_);             \
+      gpt_error_text() = hipGetErrorString(e_);             \
       return GPT_EHIP;                           \
     }                                            \
   } while (0)
@@ -112,7 +111,7 @@ struct WsOff {
   size_t total;
   int nchunks;
   int64_t vi;  // logits row pitch: padded_vocab rounded up to 64
-  size_t wT = 0, tjobs = 0;  // transposed bf16 weights; their job table
+  size_t wT = 0, tjobs = 0;  // transposed 16-bit weights; their job table
   int64_t wteT = 0, wT_elems = 0;
   int njobs = 0, ttiles = 0;
 };
@@ -127,12 +126,12 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
     off = (size_t)round_up(off + (size_t)bytes, 256);
     return o;
   };
-  const bool bf = c.mode == GPT_BF16;
+  const bool bf = c.mode != GPT_FP32;
   const int64_t es = bf ? 2 : 4;
   const int64_t M = (int64_t)c.max_batch * c.block_size, d = c.n_embd, H = c.n_head;
   w.vi = round_up(c.padded_vocab, 64);
   if (bf) w.shadow = take(p.total * 2);
-  // transposed copies (bf16 mode): wte^T [d][vi] (columns >= Vp zero), then
+  // transposed copies (16-bit mode): wte^T [d][vi] (columns >= Vp zero), then
   // per layer attn^T [d][3d], aproj^T [d][d], fc^T [d][4d], mproj^T [4d][d]
   int64_t te = 0;
   w.wteT = te;
@@ -209,15 +208,15 @@ int validate(const gpt_config* c) {
   if (!c) return fail(GPT_EINVAL, "null config");
   if (c->vocab_size < 1 || c->padded_vocab < c->vocab_size || c->block_size < 1 ||
       c->n_layer < 1 || c->n_head < 1 || c->n_embd < 1 || c->max_batch < 1 ||
-      (c->mode != GPT_FP32 && c->mode != GPT_BF16) || c->n_embd % c->n_head)
+      (c->mode != GPT_FP32 && c->mode != GPT_BF16 && c->mode != GPT_FP16) || c->n_embd % c->n_head)
     return fail(GPT_EINVAL, "invalid gpt_config");
   const int hs = c->n_embd / c->n_head;
   if (c->n_embd % 4 || c->n_embd > 2048 || hs > 128)
     return fail(GPT_EUNSUPPORTED, "n_embd must be a multiple of 4, at most 2048; head width <= 128");
-  if (c->mode == GPT_BF16) {
-    if (c->n_embd % 64) return fail(GPT_EUNSUPPORTED, "bf16 mode needs n_embd % 64 == 0");
+  if (c->mode != GPT_FP32) {
+    if (c->n_embd % 64) return fail(GPT_EUNSUPPORTED, "h16 mode needs n_embd % 64 == 0");
     if (round_up(c->padded_vocab, 64) > 53248)
-      return fail(GPT_EUNSUPPORTED, "bf16 cross-entropy covers rows up to 53248 columns");
+      return fail(GPT_EUNSUPPORTED, "h16 cross-entropy covers rows up to 53248 columns");
   }
   if ((int64_t)c->max_batch * c->block_size > (1 << 26))
     return fail(GPT_EUNSUPPORTED, "max_batch * block_size too large");
@@ -226,7 +225,7 @@ int validate(const gpt_config* c) {
 
 }  // namespace
 
-struct gpt_model {
+struct Model {
   gpt_config cfg;
   ParamOff po;
   WsOff wo;
@@ -238,25 +237,24 @@ struct gpt_model {
   int B = 0, T = 0;
   const int32_t* idx = nullptr;
 
-  bool bf16() const { return cfg.mode == GPT_BF16; }
-  int64_t es() const { return bf16() ? 2 : 4; }
+  bool h16() const { return cfg.mode != GPT_FP32; }
+  int64_t es() const { return h16() ? 2 : 4; }
   template <typename P = void>
   P* at(size_t off) const { return (P*)(ws + off); }
   float* P(int64_t off) const { return params + off; }
   float* G(int64_t off) const { return grads + off; }
-  // matrix operand copy of a weight: bf16 copy in bf16 mode, fp32 params otherwise
+  // matrix operand copy of a weight: 16-bit copy in 16-bit mode, fp32 params otherwise
   const void* W(int64_t off) const {
-    return bf16() ? (const void*)(at<bf16_t>(wo.shadow) + off) : (const void*)(params + off);
+    return h16() ? (const void*)(at<h16_t>(wo.shadow) + off) : (const void*)(params + off);
   }
-  const bf16_t* WT(int64_t off) const { return at<bf16_t>(wo.wT) + off; }
+  const h16_t* WT(int64_t off) const { return at<h16_t>(wo.wT) + off; }
   int refresh_transposes(hipStream_t s) const {
-    if (!bf16()) return 0;
-    return transpose_bf16_launch(at<bf16_t>(wo.shadow), at<bf16_t>(wo.wT),
+    if (!h16()) return 0;
+    return transpose_h16_launch(at<h16_t>(wo.shadow), at<h16_t>(wo.wT),
                                  at<TransposeJob>(wo.tjobs), wo.njobs, wo.ttiles, s);
   }
 };
 
-extern "C" {
 
 int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace_bytes) {
   int rc = validate(cfg);
@@ -268,7 +266,7 @@ int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace
   return GPT_OK;
 }
 
-int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads, float* adam_m,
+int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, float* adam_m,
              float* adam_v, void* workspace, const float* init_params, void* stream) {
   if (!out) return fail(GPT_EINVAL, "null output handle");
   *out = nullptr;
@@ -278,7 +276,7 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
     return fail(GPT_EINVAL, "null device buffer");
   if ((uintptr_t)workspace & 255) return fail(GPT_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  gpt_model* h = new gpt_model;
+  Model* h = new Model;
   h->cfg = *cfg;
   h->po = param_offsets(*cfg);
   h->wo = ws_offsets(*cfg, h->po);
@@ -292,7 +290,7 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
     for (int64_t c = 0; c < n; c += kChunk)
       h->chunks.push_back({o + c, (int32_t)std::min<int64_t>(kChunk, n - c), h->po.is2d[i]});
   }
-  if (h->bf16()) {
+  if (h->h16()) {
     const int64_t d = cfg->n_embd;
     int tiles = 0;
     auto job = [&](int64_t src, int64_t dst, int64_t rows, int64_t cols, int64_t ld) {
@@ -321,7 +319,7 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->ws + h->wo.chunks, h->chunks.data(), h->chunks.size() * sizeof(AdamChunk),
                        hipMemcpyHostToDevice, s);
-  if (e == hipSuccess && h->bf16()) {
+  if (e == hipSuccess && h->h16()) {
     e = hipMemcpyAsync(h->ws + h->wo.tjobs, h->tjobs.data(), h->tjobs.size() * sizeof(TransposeJob),
                        hipMemcpyHostToDevice, s);
     // columns Vp..vi of wte^T stay zero
@@ -330,12 +328,12 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
   // the host table must outlive the copy: wait for it once, at set-up
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
-    g_err = hipGetErrorString(e);
+    gpt_error_text() = hipGetErrorString(e);
     delete h;
     return GPT_EHIP;
   }
-  if (h->bf16()) {
-    rc = to_bf16_launch(params, h->at<bf16_t>(h->wo.shadow), h->po.total, s);
+  if (h->h16()) {
+    rc = to_h16_launch(params, h->at<h16_t>(h->wo.shadow), h->po.total, s);
     if (!rc) rc = h->refresh_transposes(s);
     if (rc) {
       delete h;
@@ -350,10 +348,10 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
 // tokens ([NG] Part IV Stage 4: GPT.forward up to ln_f).  With kv set, each
 // block's keys and values are also stored in the cache kv (sized for B
 // sequences of max_len positions) at positions [0, T).
-static int forward_stack(gpt_model* h, const int32_t* idx, int B, int T, void* kv, int max_len,
+static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, int max_len,
                          hipStream_t s) {
   const gpt_config& c = h->cfg;
-  const bool bf = h->bf16();
+  const bool bf = h->h16();
   const WsOff& w = h->wo;
   const ParamOff& p = h->po;
   const int M = B * T, d = c.n_embd, H = c.n_head;
@@ -405,15 +403,16 @@ static int forward_stack(gpt_model* h, const int32_t* idx, int B, int T, void* k
   return GPT_OK;
 }
 
-int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
-                     float loss_scale, float* loss_out, void* logits_out, void* stream) {
+int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
+                     float loss_scale, const float* dscale, float* loss_out, void* logits_out,
+                     void* stream) {
   if (!h || !idx) return fail(GPT_EINVAL, "null handle or idx");
   const gpt_config& c = h->cfg;
   if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
   if (T < 1) return fail(GPT_EINVAL, "T < 1");
   if (T > c.block_size) return fail(GPT_ESEQLEN, "T > block_size");
   hipStream_t s = (hipStream_t)stream;
-  const bool bf = h->bf16();
+  const bool bf = h->h16();
   const WsOff& w = h->wo;
   const ParamOff& p = h->po;
   const int M = B * T, d = c.n_embd;
@@ -434,7 +433,8 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, i
   if (targets) {
     CK(count_valid_launch(targets, M, h->at<int>(w.nvalid), s));
     CK(cross_entropy_launch(bf, h->at(w.logits), targets, h->at<float>(w.row_loss),
-                            h->at<int>(w.nvalid), loss_scale, M, c.vocab_size, (int)w.vi, s));
+                            h->at<int>(w.nvalid), loss_scale, dscale, M, c.vocab_size, (int)w.vi,
+                            s));
     if (loss_out) CK(loss_finalize_launch(h->at<float>(w.row_loss), M, h->at<int>(w.nvalid), loss_out, s));
   }
   h->have_fwd = true;
@@ -448,11 +448,11 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, i
 // ---------------------------------------------------------------- sampling
 int64_t gpt_kv_cache_bytes(const gpt_config* c, int32_t B, int32_t max_len) {
   if (validate(c) != GPT_OK || B < 1 || max_len < 1) return -1;
-  const int64_t es = c->mode == GPT_BF16 ? 2 : 4;
+  const int64_t es = c->mode != GPT_FP32 ? 2 : 4;
   return (int64_t)c->n_layer * 2 * B * c->n_embd * (int64_t)max_len * es;
 }
 
-static int check_decode_args(gpt_model* h, int B, int max_len, const void* kv, const float* logits_out) {
+static int check_decode_args(Model* h, int B, int max_len, const void* kv, const float* logits_out) {
   const gpt_config& c = h->cfg;
   if (!kv || !logits_out) return fail(GPT_EINVAL, "null cache or logits buffer");
   if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
@@ -462,17 +462,17 @@ static int check_decode_args(gpt_model* h, int B, int max_len, const void* kv, c
 
 // head over one row per sequence: logits [B][padded_vocab] fp32 = rows of
 // lnf (row pitch lda elements) times wte^T
-static int head_rows(gpt_model* h, const void* rows, int lda, int B, float* logits_out, hipStream_t s) {
+static int head_rows(Model* h, const void* rows, int lda, int B, float* logits_out, hipStream_t s) {
   const gpt_config& c = h->cfg;
   GemmEpiArgs e;
   e.out = logits_out;
   e.ldc = c.padded_vocab;
-  CK(gemm_launch(h->bf16(), true, true, EPI_F32, rows, lda, h->W(h->po.wte), c.n_embd, B,
+  CK(gemm_launch(h->h16(), true, true, EPI_F32, rows, lda, h->W(h->po.wte), c.n_embd, B,
                  c.padded_vocab, c.n_embd, c.n_embd, c.n_embd, e, s));
   return GPT_OK;
 }
 
-int gpt_prefill(gpt_model* h, const int32_t* idx, int32_t B, int32_t T0, void* kv, int32_t max_len,
+int gpt_prefill(Model* h, const int32_t* idx, int32_t B, int32_t T0, void* kv, int32_t max_len,
                 float* logits_out, void* stream) {
   if (!h || !idx) return fail(GPT_EINVAL, "null handle or idx");
   CK(check_decode_args(h, B, max_len, kv, logits_out));
@@ -487,7 +487,7 @@ int gpt_prefill(gpt_model* h, const int32_t* idx, int32_t B, int32_t T0, void* k
   return GPT_OK;
 }
 
-int gpt_decode_step(gpt_model* h, const int32_t* tok, int32_t B, int32_t pos, void* kv,
+int gpt_decode_step(Model* h, const int32_t* tok, int32_t B, int32_t pos, void* kv,
                     int32_t max_len, float* logits_out, void* stream) {
   if (!h || !tok) return fail(GPT_EINVAL, "null handle or tokens");
   CK(check_decode_args(h, B, max_len, kv, logits_out));
@@ -495,7 +495,7 @@ int gpt_decode_step(gpt_model* h, const int32_t* tok, int32_t B, int32_t pos, vo
   hipStream_t s = (hipStream_t)stream;
   h->have_fwd = false;
   const gpt_config& c = h->cfg;
-  const bool bf = h->bf16();
+  const bool bf = h->h16();
   const WsOff& w = h->wo;
   const ParamOff& p = h->po;
   const int d = c.n_embd, H = c.n_head, hs = d / H;
@@ -602,13 +602,13 @@ int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float tem
   return GPT_OK;
 }
 
-int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
+int gpt_backward(Model* h, int32_t zero_first, void* stream) {
   if (!h) return fail(GPT_EINVAL, "null handle");
   if (!h->have_fwd || !h->have_targets)
     return fail(GPT_ESTATE, "backward needs a preceding forward with targets");
   hipStream_t s = (hipStream_t)stream;
   const gpt_config& c = h->cfg;
-  const bool bf = h->bf16();
+  const bool bf = h->h16();
   const WsOff& w = h->wo;
   const ParamOff& p = h->po;
   const int B = h->B, T = h->T, M = B * T, d = c.n_embd, H = c.n_head;
@@ -634,7 +634,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
 
   // LM head: dwte (+)= dlogits^T lnf ; dlnf = dlogits wte.  The input
   // gradients of the LayerNorms (dlnf, dln2, dln1) are stored in the
-  // activation type, as the matrix products' outputs are under bf16 mixed
+  // activation type, as the matrix products' outputs are under 16-bit mixed
   // precision; the LayerNorm backward reads them into fp32.
   {
     GemmEpiArgs e;
@@ -749,7 +749,7 @@ int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
   return GPT_OK;
 }
 
-int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, float weight_decay,
+int gpt_adamw_step(Model* h, float lr, float beta1, float beta2, float eps, float weight_decay,
                    float max_norm, int32_t t, int32_t skip_nonfinite, float* norm_out,
                    void* stream) {
   if (!h) return fail(GPT_EINVAL, "null handle");
@@ -757,7 +757,7 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, 
   hipStream_t s = (hipStream_t)stream;
   const WsOff& w = h->wo;
   CK(adamw_launch(h->params, h->grads, h->m, h->v,
-                  h->bf16() ? h->at<bf16_t>(w.shadow) : nullptr, h->po.total,
+                  h->h16() ? h->at<h16_t>(w.shadow) : nullptr, h->po.total,
                   h->at<AdamChunk>(w.chunks), w.nchunks, h->at<double>(w.norm_part),
                   h->at<float>(w.scal), norm_out, lr, beta1, beta2, eps, weight_decay, max_norm, t,
                   skip_nonfinite, s));
@@ -765,7 +765,28 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps, 
   return GPT_OK;
 }
 
-int gpt_read_flags(gpt_model* h, int32_t* flags, void* stream) {
+// Dynamic loss scaling: unscale (multiply by 1/scale), clip against the norm of
+// the unscaled gradients, AdamW at step steps+1 unless the norm is not finite,
+// then the scale update, all on the device.
+int gpt_amp_step(Model* h, float lr, float beta1, float beta2, float eps, float weight_decay,
+                 float max_norm, gpt_loss_scaler* scaler, float growth_factor, float backoff_factor,
+                 int32_t growth_interval, float* norm_out, void* stream) {
+  if (!h || !scaler) return fail(GPT_EINVAL, "null handle or scaler");
+  if (growth_interval < 1 || !(growth_factor >= 1.f) || !(backoff_factor > 0.f) ||
+      !(backoff_factor <= 1.f))
+    return fail(GPT_EINVAL, "bad loss-scaler constants");
+  hipStream_t s = (hipStream_t)stream;
+  const WsOff& w = h->wo;
+  CK(adamw_amp_launch(h->params, h->grads, h->m, h->v, h->h16() ? h->at<h16_t>(w.shadow) : nullptr,
+                      h->po.total, h->at<AdamChunk>(w.chunks), w.nchunks,
+                      h->at<double>(w.norm_part), h->at<float>(w.scal), norm_out, lr, beta1, beta2,
+                      eps, weight_decay, max_norm, (float*)scaler, growth_factor, backoff_factor,
+                      growth_interval, s));
+  CK(h->refresh_transposes(s));
+  return GPT_OK;
+}
+
+int gpt_read_flags(Model* h, int32_t* flags, void* stream) {
   if (!h || !flags) return fail(GPT_EINVAL, "null argument");
   hipStream_t s = (hipStream_t)stream;
   int32_t v = 0;
@@ -776,37 +797,23 @@ int gpt_read_flags(gpt_model* h, int32_t* flags, void* stream) {
   return GPT_OK;
 }
 
-void gpt_destroy(gpt_model* h) { delete h; }
+void gpt_destroy(Model* h) { delete h; }
 
-const char* gpt_strerror(int code) {
-  static thread_local std::string msg;
-  const char* base = "unknown error";
-  switch (code) {
-    case GPT_OK: return "ok";
-    case GPT_EINVAL: base = "invalid argument"; break;
-    case GPT_ESEQLEN: base = "sequence longer than block_size"; break;
-    case GPT_ESTATE: base = "invalid call order"; break;
-    case GPT_EHIP: base = "HIP error"; break;
-    case GPT_EUNSUPPORTED: base = "unsupported shape"; break;
-  }
-  msg = std::string(base) + (g_err.empty() ? "" : ": " + g_err);
-  return msg.c_str();
-}
 
 // ----------------------------------------------------------------- single ops
-int gpt_op_linear(int32_t bf16, const void* A, const void* B, const float* bias, void* C,
+int gpt_op_linear(int32_t h16, const void* A, const void* B, const float* bias, void* C,
                   int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream) {
   if (!A || !B || !C || M < 0 || N < 0 || K < 1) return fail(GPT_EINVAL, "bad linear arguments");
   GemmEpiArgs e;
   e.out = C;
   e.bias = bias;
   e.ldc = N;
-  CK(gemm_launch(bf16 != 0, true, true, out_f32 ? EPI_F32 : EPI_ACT, A, K, B, K, M, N, K, K, K, e,
+  CK(gemm_launch(h16 != 0, true, true, out_f32 ? EPI_F32 : EPI_ACT, A, K, B, K, M, N, K, K, K, e,
                  (hipStream_t)stream));
   return GPT_OK;
 }
 
-int gpt_op_linear_dw(int32_t bf16, const void* dY, const void* X, float* dW, int32_t accumulate,
+int gpt_op_linear_dw(int32_t h16, const void* dY, const void* X, float* dW, int32_t accumulate,
                      int32_t M, int32_t N, int32_t K, float* workspace, int64_t workspace_bytes,
                      void* stream) {
   if (!dY || !X || !dW || M < 1 || N < 0 || K < 0) return fail(GPT_EINVAL, "bad linear_dw arguments");
@@ -814,56 +821,57 @@ int gpt_op_linear_dw(int32_t bf16, const void* dY, const void* X, float* dW, int
   e.out = dW;
   e.ldc = K;
   e.beta = accumulate ? 1 : 0;
-  CK(gemm_launch(bf16 != 0, false, false, EPI_ACCUM, dY, N, X, K, N, K, M, M, M, e,
+  CK(gemm_launch(h16 != 0, false, false, EPI_ACCUM, dY, N, X, K, N, K, M, M, M, e,
                  (hipStream_t)stream, workspace, workspace ? workspace_bytes : 0));
   return GPT_OK;
 }
 
-int gpt_op_linear_dx(int32_t bf16, const void* dY, const void* W, float* dX, int32_t M, int32_t N,
+int gpt_op_linear_dx(int32_t h16, const void* dY, const void* W, float* dX, int32_t M, int32_t N,
                      int32_t K, void* stream) {
   if (!dY || !W || !dX || M < 0 || N < 1 || K < 0) return fail(GPT_EINVAL, "bad linear_dx arguments");
   GemmEpiArgs e;
   e.out = dX;
   e.ldc = K;
-  CK(gemm_launch(bf16 != 0, true, false, EPI_F32, dY, N, W, K, M, K, N, N, N, e,
+  CK(gemm_launch(h16 != 0, true, false, EPI_F32, dY, N, W, K, M, K, N, N, N, e,
                  (hipStream_t)stream));
   return GPT_OK;
 }
 
-int gpt_op_attention_fwd(int32_t bf16, const void* qkv, void* out, float* lse, int32_t B, int32_t T,
+int gpt_op_attention_fwd(int32_t h16, const void* qkv, void* out, float* lse, int32_t B, int32_t T,
                          int32_t H, int32_t C, void* stream) {
   if (!qkv || !out || !lse || B < 1 || T < 1 || H < 1 || C % H) return fail(GPT_EINVAL, "bad attention arguments");
-  CK(attention_fwd_launch(bf16 != 0, qkv, out, lse, B, T, H, C, (hipStream_t)stream));
+  CK(attention_fwd_launch(h16 != 0, qkv, out, lse, B, T, H, C, (hipStream_t)stream));
   return GPT_OK;
 }
 
-int gpt_op_attention_bwd(int32_t bf16, const void* qkv, const void* out, const float* lse,
+int gpt_op_attention_bwd(int32_t h16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int32_t B, int32_t T, int32_t H,
                          int32_t C, void* stream) {
   if (!qkv || !out || !lse || !dout || !dqkv || !D || B < 1 || T < 1 || H < 1 || C % H)
     return fail(GPT_EINVAL, "bad attention arguments");
-  CK(attention_bwd_launch(bf16 != 0, qkv, out, lse, dout, dqkv, D, B, T, H, C, nullptr, nullptr, 0,
+  CK(attention_bwd_launch(h16 != 0, qkv, out, lse, dout, dqkv, D, B, T, H, C, nullptr, nullptr, 0,
                           (hipStream_t)stream));
   return GPT_OK;
 }
 
-int gpt_op_layernorm_fwd(int32_t bf16, const float* x, const float* w, const float* b, void* y,
+int gpt_op_layernorm_fwd(int32_t h16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int32_t M, int32_t C, void* stream) {
   if (!x || !w || !b || !y || !mean || !rstd || M < 0 || C < 1) return fail(GPT_EINVAL, "bad layernorm arguments");
-  CK(layernorm_fwd_launch(bf16 != 0, x, w, b, y, mean, rstd, M, C, (hipStream_t)stream));
+  CK(layernorm_fwd_launch(h16 != 0, x, w, b, y, mean, rstd, M, C, (hipStream_t)stream));
   return GPT_OK;
 }
 
-int gpt_op_cross_entropy(int32_t bf16, void* logits, const int32_t* targets, float* loss,
+int gpt_op_cross_entropy(int32_t h16, void* logits, const int32_t* targets, float* loss,
                          float* row_loss, int32_t* n_valid, float loss_scale, int32_t N, int32_t V,
                          int32_t ldv, void* stream) {
   if (!logits || !targets || !loss || !row_loss || !n_valid || N < 1 || V < 1 || ldv < V)
     return fail(GPT_EINVAL, "bad cross-entropy arguments");
   hipStream_t s = (hipStream_t)stream;
   CK(count_valid_launch(targets, N, n_valid, s));
-  CK(cross_entropy_launch(bf16 != 0, logits, targets, row_loss, n_valid, loss_scale, N, V, ldv, s));
+  CK(cross_entropy_launch(h16 != 0, logits, targets, row_loss, n_valid, loss_scale, nullptr, N, V,
+                          ldv, s));
   CK(loss_finalize_launch(row_loss, N, n_valid, loss, s));
   return GPT_OK;
 }
 
-}  // extern "C"
+}  // namespace HALF_NS

@@ -4,9 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
 #include "gemm.h"
 
-typedef uint16_t bf16_t;
+namespace HALF_NS {
+
 
 struct AdamChunk {
   int64_t offset;
@@ -15,27 +17,27 @@ struct AdamChunk {
 };
 
 // one matrix of the transposed weight copy: src [rows][cols] (elements from
-// the start of the bf16 weights) -> dst [cols][ld] (ld >= rows)
+// the start of the 16-bit weights) -> dst [cols][ld] (ld >= rows)
 struct TransposeJob {
   int64_t src, dst;
   int32_t rows, cols, ld, tile_begin;
 };
-int transpose_bf16_launch(const bf16_t* src, bf16_t* dst, const TransposeJob* jobs, int njobs,
+int transpose_h16_launch(const h16_t* src, h16_t* dst, const TransposeJob* jobs, int njobs,
                           int total_tiles, hipStream_t s);
 
-int attention_fwd_launch(bool bf16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
+int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
                          int C, hipStream_t s);
-// defer (optional): see ColsumJob; honoured by the head-width-64 bf16 path
-int attention_bwd_launch(bool bf16, const void* qkv, const void* out, const float* lse,
+// defer (optional): see ColsumJob; honoured by the head-width-64 16-bit path
+int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
                          float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
                          ColsumJob* defer = nullptr);
 
-int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
+int layernorm_fwd_launch(bool h16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s);
 int layernorm_bwd_part_rows(int M);
-// dy: the mode's activation type (bf16 or fp32) [M][C]
-int layernorm_bwd_launch(bool bf16, const void* dy, const float* x, const float* mean,
+// dy: the mode's activation type (16-bit or fp32) [M][C]
+int layernorm_bwd_launch(bool h16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
                          int beta, int M, int C, hipStream_t s, ColsumJob* defer = nullptr);
@@ -45,16 +47,17 @@ int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, flo
 int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int Tn,
                      int block_size, int C, int Vp, int beta_wpe, hipStream_t s);
 int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s);
-int cross_entropy_launch(bool bf16, void* logits, const int32_t* tgt, float* row_loss,
-                         const int* n_valid, float loss_scale, int N, int V, int ldv,
-                         hipStream_t s);
+// dscale (optional, device): the gradient is further multiplied by *dscale
+int cross_entropy_launch(bool h16, void* logits, const int32_t* tgt, float* row_loss,
+                         const int* n_valid, float loss_scale, const float* dscale, int N, int V,
+                         int ldv, hipStream_t s);
 int loss_finalize_launch(const float* row_loss, int N, const int* n_valid, float* loss,
                          hipStream_t s);
 int colsum_part_rows(int M);
 // out (+)= column sums of part [nrow][ncol] (ncol % 4 == 0)
 int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
                            hipStream_t s);
-int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* out, int beta,
+int colsum_launch(bool h16, const void* a, int M, int N, float* part, float* out, int beta,
                   hipStream_t s);
 // finishes n ColsumJobs (each ncol % 4 == 0) in one launch per
 // COLSUM_GROUP_MAX jobs
@@ -63,21 +66,30 @@ int colsum_finalize_group_launch(const ColsumJob* jobs, int n, int beta, hipStre
 
 // sampling with a key/value cache: cache kv[k|v][b][h][t][hs] of one layer
 // (t < max_len), in the mode's activation type
-int kv_store_launch(bool bf16, const void* qkv, void* kv, int B, int Tn, int H, int hs,
+int kv_store_launch(bool h16, const void* qkv, void* kv, int B, int Tn, int H, int hs,
                     int max_len, int pos0, hipStream_t s);
-int decode_attn_launch(bool bf16, const void* qkv, const void* kv, void* out, int B, int H, int hs,
+int decode_attn_launch(bool h16, const void* qkv, const void* kv, void* out, int B, int H, int hs,
                        int max_len, int len, hipStream_t s);
 int sample_launch(const float* logits, int B, int V, int ldv, float temperature, int top_k,
                   const float* u, int32_t* tok, hipStream_t s);
 // products of the few rows of a decode step: see decode.hip
-bool gemv_fits(bool bf16, bool ln, int M, int K);
-int gemv_launch(bool bf16, int epi, const void* A, const float* ln_w, const float* ln_b,
+bool gemv_fits(bool h16, bool ln, int M, int K);
+int gemv_launch(bool h16, int epi, const void* A, const float* ln_w, const float* ln_b,
                 const void* W, const float* bias, const float* aux, void* out, int M, int N, int K,
                 int ldo, void* kv, int H, int hs, int max_len, int pos, hipStream_t s);
 
 int adamw_norm_blocks();
-int adamw_launch(float* p, const float* g, float* m, float* v, bf16_t* shadow, int64_t n,
+int adamw_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
                  const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
                  float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
                  float max_norm, int t, int skip_nonfinite, hipStream_t s);
-int to_bf16_launch(const float* p, bf16_t* o, int64_t n, hipStream_t s);
+// the same with dynamic loss scaling; scaler: device {scale, growth_tracker,
+// steps, found_inf} (float, int32 x3), read and updated in place
+int adamw_amp_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
+                     const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
+                     float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
+                     float max_norm, float* scaler, float growth, float backoff, int interval,
+                     hipStream_t s);
+int to_h16_launch(const float* p, h16_t* o, int64_t n, hipStream_t s);
+
+}  // namespace HALF_NS

@@ -7,13 +7,15 @@
 //   y = (x - mean) * rstd * w + b,  rstd = 1/sqrt(var + eps)
 //   dx = rstd * (g - mean(g) - xhat * mean(g * xhat)),  g = dy * w
 // The backward also adds dx into the residual-stream gradient, writes its
-// bf16/fp32 copy for the next matrix product, and produces per-block column
+// 16-bit/fp32 copy for the next matrix product, and produces per-block column
 // partial sums of dy*xhat (dw), dy (db) and of the updated residual gradient
 // (the bias gradient of the projection whose output is that residual).
 #include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
+
+namespace HALF_NS {
 
 #define LN_EPS 1e-5f
 #define LN_MAXV_MAX 8  // float4 per lane: C <= 2048
@@ -26,13 +28,13 @@ template <> struct Raw4<float> {
   __device__ __forceinline__ static float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ static float4 f32(float4 v) { return v; }
 };
-template <> struct Raw4<bf16_t> {
+template <> struct Raw4<h16_t> {
   typedef uint2 type;
-  __device__ __forceinline__ static uint2 load(const bf16_t* p) { return *(const uint2*)p; }
+  __device__ __forceinline__ static uint2 load(const h16_t* p) { return *(const uint2*)p; }
   __device__ __forceinline__ static uint2 zero() { return make_uint2(0u, 0u); }
   __device__ __forceinline__ static float4 f32(uint2 u) {
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    return make_float4(h_lo(u.x), h_hi(u.x),
+                       h_lo(u.y), h_hi(u.y));
   }
 };
 template <typename T>
@@ -40,8 +42,8 @@ __device__ __forceinline__ void store4(T* p, float4 v);
 template <>
 __device__ __forceinline__ void store4<float>(float* p, float4 v) { *(float4*)p = v; }
 template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
-  *(uint2*)p = make_uint2(pack2bf(v.x, v.y), pack2bf(v.z, v.w));
+__device__ __forceinline__ void store4<h16_t>(h16_t* p, float4 v) {
+  *(uint2*)p = make_uint2(pack2h(v.x, v.y), pack2h(v.z, v.w));
 }
 
 template <typename T, int LN_MAXV>
@@ -298,13 +300,13 @@ __global__ __launch_bounds__(256) void colsum_finalize_group_kernel(ColsumGroupA
     default: MACRO(8); break;   \
   }
 
-int layernorm_fwd_launch(bool bf16, const float* x, const float* w, const float* b, void* y,
+int layernorm_fwd_launch(bool h16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s) {
   if (C % 4 || C > LN_MAXV_MAX * 256) return -5;
 #define LNF(V)                                                                                  \
-  if (bf16)                                                                                      \
-    hipLaunchKernelGGL((ln_fwd_kernel<bf16_t, V>), dim3(cdiv(M, 4)), dim3(256), 0, s, x, w, b,  \
-                       (bf16_t*)y, mean, rstd, M, C);                                            \
+  if (h16)                                                                                      \
+    hipLaunchKernelGGL((ln_fwd_kernel<h16_t, V>), dim3(cdiv(M, 4)), dim3(256), 0, s, x, w, b,  \
+                       (h16_t*)y, mean, rstd, M, C);                                            \
   else                                                                                           \
     hipLaunchKernelGGL((ln_fwd_kernel<float, V>), dim3(cdiv(M, 4)), dim3(256), 0, s, x, w, b,   \
                        (float*)y, mean, rstd, M, C);
@@ -318,16 +320,16 @@ int layernorm_bwd_part_rows(int M) { return (int)cdiv(M, LN_BWD_ROWS); }
 
 // dres = (accumulate ? dres : 0) + LN'(dy); dres_act = copy; then
 // dw, db (beta-accumulated) and bias_grad (+)= column sum of dres, if non-null.
-int layernorm_bwd_launch(bool bf16, const void* dy, const float* x, const float* mean,
+int layernorm_bwd_launch(bool h16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
                          int beta, int M, int C, hipStream_t s, ColsumJob* defer) {
   if (C % 4 || C > LN_MAXV_MAX * 256) return -5;
   const int nb = (int)cdiv(M, LN_BWD_ROWS);
 #define LNB(V)                                                                                   \
-  if (bf16)                                                                                       \
-    hipLaunchKernelGGL((ln_bwd_kernel<bf16_t, V>), dim3(nb), dim3(256), 0, s, (const bf16_t*)dy, \
-                       x, mean, rstd, w, dres, (bf16_t*)dres_act, accumulate, part, M, C);       \
+  if (h16)                                                                                       \
+    hipLaunchKernelGGL((ln_bwd_kernel<h16_t, V>), dim3(nb), dim3(256), 0, s, (const h16_t*)dy, \
+                       x, mean, rstd, w, dres, (h16_t*)dres_act, accumulate, part, M, C);       \
   else                                                                                            \
     hipLaunchKernelGGL((ln_bwd_kernel<float, V>), dim3(nb), dim3(256), 0, s, (const float*)dy, x, \
                        mean, rstd, w, dres, (float*)dres_act, accumulate, part, M, C);
@@ -376,3 +378,5 @@ int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, in
                      ncol, ncol, out, nullptr, nullptr, beta);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+}  // namespace HALF_NS

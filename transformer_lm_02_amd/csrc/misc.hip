@@ -1,6 +1,8 @@
 // Embedding, fused masked softmax cross-entropy, bias-gradient column sums.
 #include "common.h"
 
+namespace HALF_NS {
+
 // ---------------------------------------------------------------- embedding
 // x[b*T + t] = wte[idx] + wpe[t] ("nanoGPT" (stanleyjacob.dev), Part IV Stage
 // 4: token embeddings plus learned position embeddings).  An id outside
@@ -93,8 +95,8 @@ __global__ __launch_bounds__(RED_THREADS) void count_valid_kernel(const int32_t*
 // written over the logits ("Let's reproduce GPT-2 (124M)", chapter "Cross
 // Entropy Loss"; scale = loss_scale / n_valid, zero for an ignored row).
 #define CE_THREADS 1024    // fp32 kernel
-#define CE_BF_THREADS 512  // bf16 kernel: two rows in flight per compute unit
-#define CE_BF_MAXU 13      // uint4 (8 bf16) per thread: rows up to 53248 columns
+#define CE_BF_THREADS 512  // 16-bit kernel: two rows in flight per compute unit
+#define CE_BF_MAXU 13      // uint4 (8 16-bit) per thread: rows up to 53248 columns
 template <int NT>
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
   v = is_max ? wave_max(v) : wave_sum(v);
@@ -108,27 +110,26 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) 
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // One block per row; the row stays in registers.  Each thread takes the max
 // m_t of its own columns and replaces every cached logit z by
-// p = exp(z - m_t) (bf16), adding the fp32 values into s_t.  The block then
+// p = exp(z - m_t) (16-bit), adding the fp32 values into s_t.  The block then
 // forms lse = M + log(sum_t s_t exp(m_t - M)) with M the row max, and the
 // gradient is p * exp(m_t - lse) * scale; the thread holding the target
 // column rewrites that one element as scale * (exp(z_y - lse) - 1).
 // Columns >= V (padding) are cached as -inf, so every pass is branch-free.
-__global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_bf16_kernel(
-    bf16_t* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
-    const int* __restrict__ n_valid, float loss_scale, int V, int ldv) {
+__global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_h16_kernel(
+    h16_t* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
+    const int* __restrict__ n_valid, float loss_scale, const float* __restrict__ dscale, int V,
+    int ldv) {
   __shared__ float red[CE_BF_THREADS / 64];
   const int64_t row = blockIdx.x;
-  bf16_t* z = logits + row * ldv;
+  h16_t* z = logits + row * ldv;
   const int nvec = ldv >> 3;
   const int y = tgt[row];
   const bool has_y = y >= 0 && y < V;
-  const float zy = has_y ? bf2f(z[y]) : 0.f;
-  const uint32_t NEG2 = 0xff80ff80u;  // two bf16 -inf
+  const float zy = has_y ? h2f(z[y]) : 0.f;
+  const uint32_t NEG2 = H16_NEG_INF * 0x10001u;  // two 16-bit -inf
   // the row through one buffer descriptor (32-bit per-lane offsets, bounds
   // checked against the row length), so no per-slot 64-bit addresses
   const __amdgpu_buffer_rsrc_t rs =
@@ -152,8 +153,8 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int col = 8 * vp + 2 * j;
-          if (col >= V) w[j] = (w[j] & 0xffff0000u) | 0xff80u;
-          if (col + 1 >= V) w[j] = (w[j] & 0x0000ffffu) | 0xff800000u;
+          if (col >= V) w[j] = (w[j] & 0xffff0000u) | H16_NEG_INF;
+          if (col + 1 >= V) w[j] = (w[j] & 0x0000ffffu) | (H16_NEG_INF << 16);
         }
         cache[k] = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -161,9 +162,9 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_bf16_kernel(
   float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < CE_BF_MAXU; ++i) {
-    mt = fmax_fast(fmax_fast(fmax_fast(mt, bf_lo(cache[i].x)), bf_hi(cache[i].x)), bf_lo(cache[i].y));
-    mt = fmax_fast(fmax_fast(fmax_fast(mt, bf_hi(cache[i].y)), bf_lo(cache[i].z)), bf_hi(cache[i].z));
-    mt = fmax_fast(fmax_fast(mt, bf_lo(cache[i].w)), bf_hi(cache[i].w));
+    mt = fmax_fast(fmax_fast(fmax_fast(mt, h_lo(cache[i].x)), h_hi(cache[i].x)), h_lo(cache[i].y));
+    mt = fmax_fast(fmax_fast(fmax_fast(mt, h_hi(cache[i].y)), h_lo(cache[i].z)), h_hi(cache[i].z));
+    mt = fmax_fast(fmax_fast(mt, h_lo(cache[i].w)), h_hi(cache[i].w));
   }
   // a thread without columns keeps mt = -inf and s_t = 0
   const float mref = mt == -INFINITY ? 0.f : mt;
@@ -173,9 +174,9 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_bf16_kernel(
     uint32_t w[4] = {cache[i].x, cache[i].y, cache[i].z, cache[i].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float a = __expf(bf_lo(w[j]) - mref), b = __expf(bf_hi(w[j]) - mref);
+      const float a = __expf(h_lo(w[j]) - mref), b = __expf(h_hi(w[j]) - mref);
       st += a + b;
-      w[j] = pack2bf(a, b);
+      w[j] = pack2h(a, b);
     }
     cache[i] = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -183,29 +184,31 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_bf16_kernel(
   const float S = block_reduce<CE_BF_THREADS>(mt == -INFINITY ? 0.f : st * __expf(mt - M), false, red);
   const float lse = M + __logf(S);
   const int nv = *n_valid;
-  const float scale = (y >= 0 && nv > 0) ? loss_scale / (float)nv : 0.f;
+  const float scale =
+      (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
   const float c = scale * __expf(mref - lse);
 #pragma unroll
   for (int i = 0; i < CE_BF_MAXU; ++i) {
     // slots past the row end lie outside the descriptor: the store is dropped
     const uint32_t w[4] = {cache[i].x, cache[i].y, cache[i].z, cache[i].w};
-    const u32x4_t d = {pack2bf(bf_lo(w[0]) * c, bf_hi(w[0]) * c),
-                       pack2bf(bf_lo(w[1]) * c, bf_hi(w[1]) * c),
-                       pack2bf(bf_lo(w[2]) * c, bf_hi(w[2]) * c),
-                       pack2bf(bf_lo(w[3]) * c, bf_hi(w[3]) * c)};
+    const u32x4_t d = {pack2h(h_lo(w[0]) * c, h_hi(w[0]) * c),
+                       pack2h(h_lo(w[1]) * c, h_hi(w[1]) * c),
+                       pack2h(h_lo(w[2]) * c, h_hi(w[2]) * c),
+                       pack2h(h_lo(w[3]) * c, h_hi(w[3]) * c)};
     __builtin_amdgcn_raw_buffer_store_b128(d, rs, voff + i * CE_BF_THREADS * 16, 0, 0);
   }
   // the same thread wrote the vector holding y just above, so this store
   // lands after it
   if (has_y && (int)threadIdx.x == (y >> 3) % CE_BF_THREADS)
-    z[y] = f2bf(scale * (__expf(zy - lse) - 1.0f));
+    z[y] = f2h(scale * (__expf(zy - lse) - 1.0f));
   if (threadIdx.x == 0) row_loss[row] = has_y ? lse - zy : 0.f;
 }
 
 // fp32 logits (fp32 mode): the same, reading the row from memory per pass.
 __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
     float* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
-    const int* __restrict__ n_valid, float loss_scale, int V, int ldv) {
+    const int* __restrict__ n_valid, float loss_scale, const float* __restrict__ dscale, int V,
+    int ldv) {
   __shared__ float red[CE_THREADS / 64];
   const int64_t row = blockIdx.x;
   float* z = logits + row * ldv;
@@ -218,7 +221,8 @@ __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
   const float lse = mx + logf(s);
   const int y = tgt[row];
   const int nv = *n_valid;
-  const float scale = (y >= 0 && nv > 0) ? loss_scale / (float)nv : 0.f;
+  const float scale =
+      (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
   const float zy = (y >= 0 && y < V) ? z[y] : 0.f;
   __syncthreads();
   for (int c = threadIdx.x; c < ldv; c += CE_THREADS)
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(RED_THREADS) void loss_finalize_kernel(const float*
 // ---------------------------------------------------------------- column sums
 // part[rb][n] = sum of a[row][n] over the CS_ROWS rows of block-row rb
 // (bias gradients: db = sum over tokens of dy).  Each thread owns 8
-// consecutive columns (one 16-byte bf16 load per row); the 4 waves split the
+// consecutive columns (one 16-byte 16-bit load per row); the 4 waves split the
 // rows and combine in LDS in a fixed order.
 #define CS_ROWS 256
 template <typename T>
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256) void colsum_part_kernel(const T* __restrict__ 
         const uint4 v = *(const uint4*)p;
         const uint32_t* w = (const uint32_t*)&v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] += bf2f((bf16_t)(w[e >> 1] >> (16 * (e & 1))));
+        for (int e = 0; e < 8; ++e) s[e] += h2f((h16_t)(w[e >> 1] >> (16 * (e & 1))));
       } else {
         const float4 v0 = *(const float4*)p, v1 = *(const float4*)(p + 4);
         s[0] += v0.x; s[1] += v0.y; s[2] += v0.z; s[3] += v0.w;
@@ -320,16 +324,16 @@ int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int cross_entropy_launch(bool bf16, void* logits, const int32_t* tgt, float* row_loss,
-                         const int* n_valid, float loss_scale, int N, int V, int ldv,
-                         hipStream_t s) {
-  if (bf16) {
+int cross_entropy_launch(bool h16, void* logits, const int32_t* tgt, float* row_loss,
+                         const int* n_valid, float loss_scale, const float* dscale, int N, int V,
+                         int ldv, hipStream_t s) {
+  if (h16) {
     if (ldv % 8 || ldv > CE_BF_MAXU * CE_BF_THREADS * 8) return -5;
-    hipLaunchKernelGGL(ce_bf16_kernel, dim3(N), dim3(CE_BF_THREADS), 0, s, (bf16_t*)logits, tgt,
-                       row_loss, n_valid, loss_scale, V, ldv);
+    hipLaunchKernelGGL(ce_h16_kernel, dim3(N), dim3(CE_BF_THREADS), 0, s, (h16_t*)logits, tgt,
+                       row_loss, n_valid, loss_scale, dscale, V, ldv);
   } else {
     hipLaunchKernelGGL(ce_f32_kernel, dim3(N), dim3(CE_THREADS), 0, s, (float*)logits, tgt,
-                       row_loss, n_valid, loss_scale, V, ldv);
+                       row_loss, n_valid, loss_scale, dscale, V, ldv);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -344,16 +348,18 @@ int colsum_part_rows(int M) { return (int)cdiv(M, CS_ROWS); }
 
 // out (+)= column sums of a [M][N] (N % 8 == 0); part: fp32 scratch
 // [colsum_part_rows(M)][N].
-int colsum_launch(bool bf16, const void* a, int M, int N, float* part, float* out, int beta,
+int colsum_launch(bool h16, const void* a, int M, int N, float* part, float* out, int beta,
                   hipStream_t s) {
   if (N % 8) return -5;
   const int nb = colsum_part_rows(M);
-  if (bf16)
-    hipLaunchKernelGGL(colsum_part_kernel<bf16_t>, dim3(cdiv(N, 512), nb), dim3(256), 0, s,
-                       (const bf16_t*)a, M, N, part);
+  if (h16)
+    hipLaunchKernelGGL(colsum_part_kernel<h16_t>, dim3(cdiv(N, 512), nb), dim3(256), 0, s,
+                       (const h16_t*)a, M, N, part);
   else
     hipLaunchKernelGGL(colsum_part_kernel<float>, dim3(cdiv(N, 512), nb), dim3(256), 0, s,
                        (const float*)a, M, N, part);
   if (hipGetLastError() != hipSuccess) return -4;
   return colsum_finalize_launch(part, nb, N, out, beta, s);
 }
+
+}  // namespace HALF_NS
