@@ -47,7 +47,7 @@ def flops_per_token(dims, T):
 # launches it for the input gradients through the transposed weight copies
 # (fc and qkv per layer, the tied LM head once, the attention projection per
 # layer) and for the forward q|k|v projection.
-DOMINANT_KERNEL = "gemm2_kernel<128, 192, true, true, 0, 2, 64, 2>"
+DOMINANT_KERNEL = "gemm2_kernel<128, 192, true, true, 0, 2, 64, 2>"  # b16:: or f16:: build
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_act_128x192.json")
 TRAFFIC_SOURCES = ["transformer_lm_02_amd/csrc/gemm2.hip", "transformer_lm_02_amd/csrc/gemm.h",
                    "transformer_lm_02_amd/csrc/common.h"]
@@ -122,7 +122,7 @@ def time_dominant_kernel(torch, bd, B, T, dims, reps=5, fp16=False):
     ms_total = e0.elapsed_time(e1) / reps
     flops = sum(2.0 * M * N * K * n for (_, _, _, M, N, K, n) in ops)
     achieved = flops / (ms_total * 1e-3) / 1e12
-    name = DOMINANT_KERNEL + (" in binary16" if fp16 else "")
+    name = ("f16::" if fp16 else "b16::") + DOMINANT_KERNEL
     return {"kernel": name + " (input gradients of fc, qkv, attention projection and LM "
                              "head; forward q|k|v projection)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
