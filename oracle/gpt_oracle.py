@@ -41,6 +41,10 @@ Readings taken where the pages are silent (each repeated where it is used):
   * Sampling: the top-k cutoff keeps values equal to the k-th largest;
     top_k <= 0 keeps all; the multinomial draw is by inverse CDF in token-id
     order with a uniform supplied by the caller.
+  * Dropout: at the embedding sum, on the attention probabilities and on the
+    MLP output (not after the attention's output projection, which neither
+    page names); masks from Philox4x32-10 keyed by a seed, with the counter
+    layout of dropout_mult; a kept value is multiplied by 1/(1-p).
   * Dynamic loss scaling (float16): initial scale 2^16, growth factor 2
     after 2000 consecutive clean steps, backoff factor 0.5 on a step with an
     inf or NaN gradient (the defaults of the GradScaler the pages construct;
@@ -196,11 +200,14 @@ def gelu_bwd(u):
     return 0.5 * (1.0 + t) + 0.5 * u * (1.0 - t * t) * GELU_C * (1.0 + 3.0 * GELU_A * u * u)
 
 
-def causal_attention_fwd(q, k, v):
+def causal_attention_fwd(q, k, v, z=None):
     """The manual attention path of [NG] Deep dive 1 (the semantics of the
     fused flash kernel): scores q k^T / sqrt(hs), entries above the diagonal
-    set to -inf before the softmax ([BK] "Common pitfalls"), row softmax, then
-    the weighted sum of v.  q, k, v: (..., T, hs).  Returns out and P.
+    set to -inf before the softmax ([BK] "Common pitfalls"), row softmax,
+    dropout on the probabilities, then the weighted sum of v.  q, k, v:
+    (..., T, hs); z (optional, (..., T, T)): the dropout multipliers (0 or
+    1/(1-p)) applied to the probabilities.  Returns out and P (before
+    dropout).
     """
     T, hs = q.shape[-2], q.shape[-1]
     s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(hs)
@@ -209,19 +216,23 @@ def causal_attention_fwd(q, k, v):
     s = s - s.max(axis=-1, keepdims=True)
     e = np.exp(s)
     p = e / e.sum(axis=-1, keepdims=True)
-    return p @ v, p
+    return (p if z is None else p * z) @ v, p
 
 
-def causal_attention_bwd(dout, q, k, v, p):
+def causal_attention_bwd(dout, q, k, v, p, z=None):
     """Derivative of causal_attention_fwd: returns dq, dk, dv.
 
-    dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(P * dP)); the masked
-    entries have P = 0 and so get no gradient; dQ = dS K / sqrt(hs),
+    With Pd = P * z (P when there is no dropout): dV = Pd^T dO;
+    dP = (dO V^T) * z; dS = P * (dP - rowsum(P * dP)); the masked entries
+    have P = 0 and so get no gradient; dQ = dS K / sqrt(hs),
     dK = dS^T Q / sqrt(hs).
     """
     hs = q.shape[-1]
-    dv = np.swapaxes(p, -1, -2) @ dout
+    pd = p if z is None else p * z
+    dv = np.swapaxes(pd, -1, -2) @ dout
     dp = dout @ np.swapaxes(v, -1, -2)
+    if z is not None:
+        dp = dp * z
     ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
     dq = ds @ k / math.sqrt(hs)
     dk = np.swapaxes(ds, -1, -2) @ q / math.sqrt(hs)
@@ -258,10 +269,81 @@ def cross_entropy(logits, targets, vocab_size, loss_scale=1.0):
 
 
 # --------------------------------------------------------------------------
+# dropout from a counter-based generator
+# --------------------------------------------------------------------------
+# Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
+# Easy as 1, 2, 3", SC'11): multipliers of the two 32-bit products, and the
+# key increments (the fractional parts of the golden ratio and of sqrt(3),
+# in 32-bit fixed point).
+PHILOX_M32 = (0xD2511F53, 0xCD9E8D57)
+PHILOX_W32 = (0x9E3779B9, 0xBB67AE85)
+
+
+def philox(counter, key, width=32, mults=PHILOX_M32, weyl=PHILOX_W32, rounds=10):
+    """The Philox bijection of four words: each round multiplies words 0 and
+    2 by the two constants, and the new words are (hi(M1 c2) ^ c1 ^ k0,
+    lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key is increased by
+    the Weyl constants between rounds.  counter: four broadcastable integer
+    arrays, key: two integers.  width 32 works on uint64 arrays (a 32 x 32
+    product fits); width 64 on Python integers (the 64-bit variant, used only
+    to check the round structure).  Returns the four output words."""
+    mask = (1 << width) - 1
+    if width == 32:
+        c = [np.asarray(x, dtype=np.uint64) & np.uint64(mask) for x in counter]
+        k0, k1 = np.uint64(key[0] & mask), np.uint64(key[1] & mask)
+        M0, M1 = np.uint64(mults[0]), np.uint64(mults[1])
+        W0, W1, msk, sh = np.uint64(weyl[0]), np.uint64(weyl[1]), np.uint64(mask), np.uint64(32)
+    else:
+        c = [np.asarray(x, dtype=object) for x in counter]
+        k0, k1 = key[0] & mask, key[1] & mask
+        (M0, M1), (W0, W1), msk, sh = mults, weyl, mask, width
+    for r in range(rounds):
+        if r:
+            k0, k1 = (k0 + W0) & msk, (k1 + W1) & msk
+        p0, p1 = M0 * c[0], M1 * c[2]
+        c = [(p1 >> sh) ^ c[1] ^ k0, p1 & msk, (p0 >> sh) ^ c[3] ^ k1, p0 & msk]
+    return c
+
+
+@dataclass(frozen=True)
+class Dropout:
+    """Dropout of probability p ([NG] Part IV Stage 4 and Deep dive 1; [BK]
+    "The model in forty lines"; [NG] Part VIII check 15 gives 0.2 for the
+    character-level model) with masks drawn from Philox4x32-10 keyed by a
+    64-bit seed; step tells calls apart (one per forward)."""
+    p: float
+    seed: int
+    step: int = 0
+
+
+def dropout_threshold(p: float) -> int:
+    """A 32-bit word w keeps its element when w >= this (so w / 2^32 >= p)."""
+    return min((1 << 32) - 1, math.ceil(p * 4294967296.0))
+
+
+def dropout_mult(dr: Dropout, site: int, bh, rows: int, cols: int, dtype=np.float64):
+    """The multipliers (0 or 1/(1-p)) of one site's matrix, shape
+    (len(bh), rows, cols).  Element (r, c) of head bh is kept when word c % 4
+    of Philox4x32-10 with key (seed low 32 bits, seed high 32 bits) and
+    counter (c // 4, r, site * 2^24 + bh, step) is >= dropout_threshold(p).
+    Sites: 0 the embedding sum, 1 + 2l the attention probabilities of layer
+    l (rows queries, columns keys, bh = b * n_head + h), 2 + 2l the MLP
+    output of layer l (rows b * T + t, columns features, bh = 0)."""
+    bh = np.atleast_1d(np.asarray(bh, dtype=np.int64))
+    g = np.arange((cols + 3) // 4, dtype=np.int64)[None, None, :]
+    r = np.arange(rows, dtype=np.int64)[None, :, None]
+    c2 = ((site << 24) + bh)[:, None, None]
+    words = philox((g, r, c2, dr.step), (dr.seed & 0xFFFFFFFF, dr.seed >> 32))
+    w = np.stack(np.broadcast_arrays(*words), axis=-1).reshape(len(bh), rows, -1)[:, :, :cols]
+    keep = w >= np.uint64(dropout_threshold(dr.p))
+    return keep.astype(dtype) * (1.0 / (1.0 - dr.p))
+
+
+# --------------------------------------------------------------------------
 # the model: forward and backward
 # --------------------------------------------------------------------------
 def forward(flat_params, idx, targets, cfg: Config, loss_scale=1.0,
-            dtype=np.float64):
+            dtype=np.float64, dropout: Dropout | None = None):
     """GPT.forward of [NG] Part IV Stage 4 and Deep dive 1.
 
     token rows of wte plus position rows of wpe; per block
@@ -270,13 +352,23 @@ def forward(flat_params, idx, targets, cfg: Config, loss_scale=1.0,
     idx, targets: int arrays (B, T), T <= block_size ([RC] "Implementing the
     forward pass to get logits").  Returns (logits (B,T,Vp), loss, cache);
     loss is None when targets is None.
+    dropout (p > 0): the three places the pages name - the embedding sum
+    ([NG] Part IV Stage 4), the attention probabilities and the MLP output
+    ([NG] Deep dive 1; [BK] "The model in forty lines").  Reading: the
+    attention's output projection is not followed by dropout (neither page
+    puts one there).  Masks from dropout_mult.
     """
     P = unpack(np.asarray(flat_params, dtype=dtype), cfg)
     B, T = idx.shape
     if T > cfg.block_size:
         raise ValueError("sequence longer than block_size")
     d, H, hs = cfg.n_embd, cfg.n_head, cfg.head_dim
+    drop = dropout is not None and dropout.p > 0
     x = P["wte"][idx] + P["wpe"][:T]
+    z_emb = None
+    if drop:
+        z_emb = dropout_mult(dropout, 0, 0, B * T, d, dtype)[0].reshape(B, T, d)
+        x = x * z_emb
     layers = []
     for l in range(cfg.n_layer):
         p = f"h{l}."
@@ -286,15 +378,23 @@ def forward(flat_params, idx, targets, cfg: Config, loss_scale=1.0,
         # split the 3d columns into q | k | v, then d columns into heads
         q, k, v = (qkv[..., i * d:(i + 1) * d].reshape(B, T, H, hs).transpose(0, 2, 1, 3)
                    for i in range(3))
-        o, att_p = causal_attention_fwd(q, k, v)
+        z_att = None
+        if drop:
+            z_att = dropout_mult(dropout, 1 + 2 * l, np.arange(B * H), T, T, dtype).reshape(B, H, T, T)
+        o, att_p = causal_attention_fwd(q, k, v, z_att)
         o = o.transpose(0, 2, 1, 3).reshape(B, T, d)
         x = x + (o @ P[p + "aproj.w"].T + P[p + "aproj.b"])
-        c.update(h1=h1, q=q, k=k, v=v, att_p=att_p, o=o, x_mid=x)
+        c.update(h1=h1, q=q, k=k, v=v, att_p=att_p, z_att=z_att, o=o, x_mid=x)
         h2, c["ln2"] = layernorm_fwd(x, P[p + "ln2.w"], P[p + "ln2.b"])
         u = h2 @ P[p + "fc.w"].T + P[p + "fc.b"]
         g = gelu_fwd(u)
-        x = x + (g @ P[p + "mproj.w"].T + P[p + "mproj.b"])
-        c.update(h2=h2, u=u, g=g)
+        y = g @ P[p + "mproj.w"].T + P[p + "mproj.b"]
+        z_mlp = None
+        if drop:
+            z_mlp = dropout_mult(dropout, 2 + 2 * l, 0, B * T, d, dtype)[0].reshape(B, T, d)
+            y = y * z_mlp
+        x = x + y
+        c.update(h2=h2, u=u, g=g, z_mlp=z_mlp)
         layers.append(c)
     hf, lnf_cache = layernorm_fwd(x, P["lnf.w"], P["lnf.b"])
     logits = hf @ P["wte"].T
@@ -303,7 +403,7 @@ def forward(flat_params, idx, targets, cfg: Config, loss_scale=1.0,
         loss, dlogits = cross_entropy(logits.reshape(B * T, -1), targets.reshape(-1),
                                       cfg.vocab_size, loss_scale)
         dlogits = dlogits.reshape(logits.shape)
-    cache = dict(P=P, idx=idx, layers=layers, hf=hf, lnf=lnf_cache, dlogits=dlogits)
+    cache = dict(P=P, idx=idx, layers=layers, hf=hf, lnf=lnf_cache, dlogits=dlogits, z_emb=z_emb)
     return logits, loss, cache
 
 
@@ -325,10 +425,11 @@ def backward(cache, cfg: Config, dtype=np.float64):
     dx, G["lnf.w"][...], G["lnf.b"][...] = layernorm_bwd(dhf, P["lnf.w"], cache["lnf"])
     for l in reversed(range(cfg.n_layer)):
         p, c = f"h{l}.", cache["layers"][l]
-        # MLP branch: x = x_mid + g Wm^T + bm, g = gelu(u), u = h2 Wfc^T + bfc
-        G[p + "mproj.w"][...] = dx.reshape(-1, d).T @ c["g"].reshape(-1, 4 * d)
-        G[p + "mproj.b"][...] = dx.reshape(-1, d).sum(axis=0)
-        dg = dx @ P[p + "mproj.w"]
+        # MLP branch: x = x_mid + z * (g Wm^T + bm), g = gelu(u), u = h2 Wfc^T + bfc
+        dy = dx if c["z_mlp"] is None else dx * c["z_mlp"]
+        G[p + "mproj.w"][...] = dy.reshape(-1, d).T @ c["g"].reshape(-1, 4 * d)
+        G[p + "mproj.b"][...] = dy.reshape(-1, d).sum(axis=0)
+        dg = dy @ P[p + "mproj.w"]
         du = dg * gelu_bwd(c["u"])
         G[p + "fc.w"][...] = du.reshape(-1, 4 * d).T @ c["h2"].reshape(-1, d)
         G[p + "fc.b"][...] = du.reshape(-1, 4 * d).sum(axis=0)
@@ -339,7 +440,7 @@ def backward(cache, cfg: Config, dtype=np.float64):
         G[p + "aproj.w"][...] = dx.reshape(-1, d).T @ c["o"].reshape(-1, d)
         G[p + "aproj.b"][...] = dx.reshape(-1, d).sum(axis=0)
         do = (dx @ P[p + "aproj.w"]).reshape(B, T, H, hs).transpose(0, 2, 1, 3)
-        dq, dk, dv = causal_attention_bwd(do, c["q"], c["k"], c["v"], c["att_p"])
+        dq, dk, dv = causal_attention_bwd(do, c["q"], c["k"], c["v"], c["att_p"], c["z_att"])
         dqkv = np.concatenate([t.transpose(0, 2, 1, 3).reshape(B, T, d) for t in (dq, dk, dv)],
                               axis=-1)
         G[p + "attn.w"][...] = dqkv.reshape(-1, 3 * d).T @ c["h1"].reshape(-1, d)
@@ -347,16 +448,18 @@ def backward(cache, cfg: Config, dtype=np.float64):
         dh1 = dqkv @ P[p + "attn.w"]
         dln, G[p + "ln1.w"][...], G[p + "ln1.b"][...] = layernorm_bwd(dh1, P[p + "ln1.w"], c["ln1"])
         dx = dx + dln
-    # embeddings: x = wte[idx] + wpe[:T]
+    # embeddings: x = z * (wte[idx] + wpe[:T])
+    if cache["z_emb"] is not None:
+        dx = dx * cache["z_emb"]
     np.add.at(G["wte"], idx.reshape(-1), dx.reshape(-1, d))
     G["wpe"][:T] += dx.sum(axis=0)
     return grads
 
 
 def loss_and_grads(flat_params, idx, targets, cfg: Config, loss_scale=1.0,
-                   dtype=np.float64):
+                   dtype=np.float64, dropout: Dropout | None = None):
     """One forward plus backward: (loss, flat grads, logits)."""
-    logits, loss, cache = forward(flat_params, idx, targets, cfg, loss_scale, dtype)
+    logits, loss, cache = forward(flat_params, idx, targets, cfg, loss_scale, dtype, dropout)
     return loss, backward(cache, cfg, dtype), logits
 
 

@@ -39,16 +39,16 @@ def _gelu_bwd_sign(u):
     return 0.5 * (1.0 + t) - 0.5 * u * (1.0 - t * t) * O.GELU_C * (1.0 + 3.0 * O.GELU_A * u * u)
 
 
-def _attn_no_scale(q, k, v):
+def _attn_no_scale(q, k, v, z=None):
     T = q.shape[-2]
     s = q @ np.swapaxes(k, -1, -2)
     s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
     e = np.exp(s - s.max(-1, keepdims=True))
     p = e / e.sum(-1, keepdims=True)
-    return p @ v, p
+    return (p if z is None else p * z) @ v, p
 
 
-def _attn_mask_inclusive(q, k, v):
+def _attn_mask_inclusive(q, k, v, z=None):
     # masks the diagonal too (off-by-one); row 0 then has no visible key, so
     # give it itself to stay finite
     T, hs = q.shape[-2], q.shape[-1]
@@ -58,13 +58,15 @@ def _attn_mask_inclusive(q, k, v):
     s = np.where(mask, -np.inf, s)
     e = np.exp(s - s.max(-1, keepdims=True))
     p = e / e.sum(-1, keepdims=True)
-    return p @ v, p
+    return (p if z is None else p * z) @ v, p
 
 
-def _attn_bwd_transposed(dout, q, k, v, p):
+def _attn_bwd_transposed(dout, q, k, v, p, z=None):
     hs = q.shape[-1]
     dv = p @ dout
     dp = dout @ np.swapaxes(v, -1, -2)
+    if z is not None:
+        dp = dp * z
     ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
     return ds @ k / math.sqrt(hs), np.swapaxes(ds, -1, -2) @ q / math.sqrt(hs), dv
 
@@ -227,6 +229,44 @@ def _train_amp_unscaled_backward(params, m, v, state, micro_batches, cfg, lr, be
 
 _orig_amp, _orig_update, _orig_train_amp = O.amp_step, O.scaler_update, O.train_step_amp
 
+
+def _attn_drop_renormalised(q, k, v, z=None):
+    # dropout whose kept probabilities are renormalised to sum to one
+    out, p = _orig_attn_fwd(q, k, v)
+    if z is None:
+        return out, p
+    pd = p * z
+    pd = pd / pd.sum(axis=-1, keepdims=True).clip(1e-300)
+    return pd @ v, p
+
+
+def _attn_bwd_mask_only_on_dv(dout, q, k, v, p, z=None):
+    # the mask is applied to dV but forgotten in dP
+    dq, dk, dv = _orig_attn_bwd(dout, q, k, v, p)
+    if z is None:
+        return dq, dk, dv
+    return dq, dk, np.swapaxes(p * z, -1, -2) @ dout
+
+
+def _dropout_unscaled(dr, site, bh, rows, cols, dtype=np.float64):
+    return (_orig_dmult(dr, site, bh, rows, cols, dtype) > 0).astype(dtype)
+
+
+def _philox_bump_first(counter, key, width=32, mults=O.PHILOX_M32, weyl=O.PHILOX_W32, rounds=10):
+    mask = (1 << width) - 1
+    key = ((key[0] + weyl[0]) & mask, (key[1] + weyl[1]) & mask)
+    return _orig_philox(counter, key, width, mults, weyl, rounds)
+
+
+def _philox_hi_lo_swapped(counter, key, width=32, mults=O.PHILOX_M32, weyl=O.PHILOX_W32,
+                          rounds=10):
+    w = _orig_philox(counter, key, width, mults, weyl, rounds)
+    return [w[1], w[0], w[3], w[2]]
+
+
+_orig_attn_fwd, _orig_attn_bwd = O.causal_attention_fwd, O.causal_attention_bwd
+_orig_dmult, _orig_philox = O.dropout_mult, O.philox
+
 MUTANTS = [
     ("layernorm_fwd", _ln_unbiased),
     ("layernorm_bwd", _ln_bwd_no_mean_term),
@@ -254,6 +294,11 @@ MUTANTS = [
     ("scaler_update", _scaler_grows_early),
     ("scaler_update", _scaler_backoff_keeps_count),
     ("train_step_amp", _train_amp_unscaled_backward),
+    ("causal_attention_fwd", _attn_drop_renormalised),
+    ("causal_attention_bwd", _attn_bwd_mask_only_on_dv),
+    ("dropout_mult", _dropout_unscaled),
+    ("philox", _philox_bump_first),
+    ("philox", _philox_hi_lo_swapped),
 ]
 
 # the pins that should catch mistakes in the model and optimizer
@@ -277,6 +322,10 @@ PIN_TESTS = [
     lambda: pins.test_amp_scale_sequence_closed_form(),
     lambda: pins.test_amp_skipped_step_changes_nothing_and_keeps_the_step_count(),
     lambda: pins.test_train_step_amp_equals_unscaled_step(),
+    lambda: pins.test_philox_round_structure_matches_numpy(),
+    lambda: pins.test_dropout_masks_keep_one_minus_p_and_are_independent(),
+    lambda: pins.test_dropout_model_matches_pytorch_autograd(),
+    lambda: pins.test_dropout_finite_differences(),
 ]
 
 

@@ -193,7 +193,11 @@ def test_key_bias_gradient_vanishes():
 
 
 # ---------------------------------------------------------------- model vs PyTorch autograd
-def _torch_model_loss(params, idx, tgt, cfg):
+def _torch_model_loss(params, idx, tgt, cfg, masks=None):
+    """PyTorch autograd through F.* in float64.  masks (optional): dropout
+    multipliers injected where the pages' model applies nn.Dropout - the
+    embedding sum, the attention probabilities (the manual path: softmax,
+    dropout, then v) and the MLP output."""
     import torch
     import torch.nn.functional as F
     P = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
@@ -202,18 +206,26 @@ def _torch_model_loss(params, idx, tgt, cfg):
     d, H = cfg.n_embd, cfg.n_head
     ix = torch.tensor(idx, dtype=torch.long)
     x = F.embedding(ix, P["wte"]) + P["wpe"][:T]
+    if masks is not None:
+        x = x * torch.tensor(masks["emb"])
     for l in range(cfg.n_layer):
         p = f"h{l}."
         h = F.layer_norm(x, (d,), P[p + "ln1.w"], P[p + "ln1.b"], eps=1e-5)
         qkv = F.linear(h, P[p + "attn.w"], P[p + "attn.b"])
         q, k, v = qkv.split(d, dim=2)
         q, k, v = [t.view(B, T, H, d // H).transpose(1, 2) for t in (q, k, v)]
-        y = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+        if masks is None:
+            y = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+        else:
+            att = (q @ k.transpose(-2, -1)) / math.sqrt(d // H)
+            att = att.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+            y = (F.softmax(att, dim=-1) * torch.tensor(masks["att"][l])) @ v
         y = y.transpose(1, 2).reshape(B, T, d)
         x = x + F.linear(y, P[p + "aproj.w"], P[p + "aproj.b"])
         h = F.layer_norm(x, (d,), P[p + "ln2.w"], P[p + "ln2.b"], eps=1e-5)
         u = F.linear(h, P[p + "fc.w"], P[p + "fc.b"])
-        x = x + F.linear(F.gelu(u, approximate="tanh"), P[p + "mproj.w"], P[p + "mproj.b"])
+        m = F.linear(F.gelu(u, approximate="tanh"), P[p + "mproj.w"], P[p + "mproj.b"])
+        x = x + (m if masks is None else m * torch.tensor(masks["mlp"][l]))
     x = F.layer_norm(x, (d,), P["lnf.w"], P["lnf.b"], eps=1e-5)
     logits = F.linear(x, P["wte"])
     loss = F.cross_entropy(logits[..., :cfg.vocab_size].reshape(B * T, -1),
@@ -674,3 +686,133 @@ def test_train_step_amp_equals_unscaled_step():
     assert np.array_equal(amp["grads"], plain["grads"] * 65536.0)
     assert amp["loss"] == plain["loss"] and amp["norm"] == plain["norm"]
     assert np.array_equal(amp["params"], plain["params"])
+
+
+# ---------------------------------------------------------------- dropout and its generator
+# Philox4x64-10 (the same paper's 64-bit variant, which numpy implements):
+# multipliers and Weyl key increments
+_M64 = (0xD2E7470EE14C6C93, 0xCA5A826395121157)
+_W64 = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)
+
+
+def test_philox_round_structure_matches_numpy():
+    """The oracle's Philox rounds (products, word order, key schedule, round
+    count), run at 64-bit width with that variant's constants, reproduce
+    numpy.random.Philox, which draws the block of counter + 1 first."""
+    for key, ctr in [((0, 0), (0, 0, 0, 0)), ((1, 2), (5, 0, 0, 0)),
+                     ((0x0123456789ABCDEF, 0xFEDCBA9876543210), (2**64 - 2, 7, 2**63, 3))]:
+        bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
+                              counter=np.array(ctr, dtype=np.uint64))
+        raw = [int(x) for x in bg.random_raw(8)]
+        for blk in range(2):
+            c = list(ctr)
+            c[0] += blk + 1
+            for i in range(3):  # the counter is a 256-bit little-endian number
+                if c[i] >= 2**64:
+                    c[i] -= 2**64
+                    c[i + 1] += 1
+            got = [int(w) for w in O.philox(c, key, width=64, mults=_M64, weyl=_W64)]
+            assert got == raw[4 * blk:4 * blk + 4], (key, ctr, blk)
+
+
+def test_philox_key_increments_from_their_definitions():
+    """The Weyl increments are the fractional parts of the golden ratio and
+    of sqrt(3) in fixed point, at 32 and 64 bits."""
+    from math import isqrt
+    for bits, (w0, w1) in [(32, O.PHILOX_W32), (64, _W64)]:
+        one = 1 << bits
+        # floor(2^bits (sqrt(5) - 1) / 2) and floor(2^bits (sqrt(3) - 1))
+        assert w0 == (isqrt(5 * one * one) - one) // 2
+        assert w1 == isqrt(3 * one * one) - one
+
+
+def test_philox32_is_a_bijection_sample_and_avalanches():
+    """No two of 2^16 counters collide, and flipping one counter bit flips
+    about half of the 128 output bits."""
+    c = np.arange(1 << 16, dtype=np.uint64)
+    w = O.philox((c, 0, 0, 0), (7, 9))
+    packed = {(int(a), int(b), int(c_), int(d)) for a, b, c_, d in zip(*w)}
+    assert len(packed) == 1 << 16
+    base = O.philox((c, 3, 5, 11), (7, 9))
+    flip = O.philox((c ^ np.uint64(1 << 13), 3, 5, 11), (7, 9))
+    bits = sum(np.unpackbits(np.asarray(a ^ b, dtype=">u4").view(np.uint8)).sum()
+               for a, b in zip(base, flip))
+    frac = bits / (128 * len(c))
+    assert abs(frac - 0.5) < 0.01, frac
+
+
+def test_dropout_masks_keep_one_minus_p_and_are_independent():
+    """Kept fraction within 5 sigma of 1 - p; the multipliers average 1 (the
+    1/(1-p) scale); masks of different steps, sites and heads agree on
+    about p^2 + (1-p)^2 of the elements, as independent draws do."""
+    p = 0.2
+    dr = O.Dropout(p, seed=0x1234_5678_9ABC_DEF0, step=3)
+    z = O.dropout_mult(dr, 2, 0, 1024, 1024)[0]
+    n = z.size
+    keep = (z > 0).mean()
+    assert abs(keep - (1 - p)) < 5 * math.sqrt(p * (1 - p) / n)
+    assert abs(z.mean() - 1.0) < 5 * math.sqrt(p / (1 - p) / n)
+    assert np.all((z == 0) | np.isclose(z, 1.25, rtol=0, atol=1e-15))
+    agree = p * p + (1 - p) ** 2
+    for other in [O.dropout_mult(O.Dropout(p, dr.seed, 4), 2, 0, 1024, 1024)[0],
+                  O.dropout_mult(dr, 3, 0, 1024, 1024)[0],
+                  O.dropout_mult(dr, 2, 1, 1024, 1024)[0],
+                  O.dropout_mult(O.Dropout(p, dr.seed + 1, 3), 2, 0, 1024, 1024)[0]]:
+        a = ((z > 0) == (other > 0)).mean()
+        assert abs(a - agree) < 5 * math.sqrt(agree * (1 - agree) / n), a
+    # p = 0 keeps everything
+    assert np.all(O.dropout_mult(O.Dropout(0.0, 5), 0, 0, 64, 64) == 1.0)
+
+
+def _masks_of(cfg, dr, B, T):
+    d, H = cfg.n_embd, cfg.n_head
+    return dict(emb=O.dropout_mult(dr, 0, 0, B * T, d)[0].reshape(B, T, d),
+                att=[O.dropout_mult(dr, 1 + 2 * l, np.arange(B * H), T, T).reshape(B, H, T, T)
+                     for l in range(cfg.n_layer)],
+                mlp=[O.dropout_mult(dr, 2 + 2 * l, 0, B * T, d)[0].reshape(B, T, d)
+                     for l in range(cfg.n_layer)])
+
+
+def test_dropout_model_matches_pytorch_autograd():
+    """The same masks injected into PyTorch's autograd model at the places
+    the pages' model applies dropout: loss and every gradient agree."""
+    cfg = micro_cfg(n_layer=2, n_head=2, n_embd=16, block_size=8)
+    dims = {k: getattr(cfg, k) for k in synth.MODEL_KEYS}
+    params = synth.perturbed_params(dims, seed=31, scale=0.2).astype(np.float64)
+    rng = np.random.default_rng(32)
+    idx = rng.integers(0, cfg.vocab_size, (3, 8))
+    tgt = rng.integers(0, cfg.vocab_size, (3, 8))
+    dr = O.Dropout(0.3, seed=77, step=1)
+    loss, grads, logits = O.loss_and_grads(params, idx, tgt, cfg, dropout=dr)
+    tloss, tgrads, tlogits = _torch_model_loss(params, idx, tgt, cfg, masks=_masks_of(cfg, dr, 3, 8))
+    assert abs(loss - tloss) <= 1e-12 * abs(tloss)
+    assert np.allclose(logits, tlogits, rtol=1e-11, atol=1e-13)
+    assert np.allclose(grads, tgrads, rtol=1e-9, atol=1e-14 * np.abs(tgrads).max())
+    loss0 = O.loss_and_grads(params, idx, tgt, cfg)[0]
+    assert abs(loss - loss0) > 1e-3  # dropout changed the result
+
+
+def test_dropout_finite_differences():
+    """With the masks fixed by (seed, step), the loss is a smooth function of
+    the parameters: central differences agree with the analytic backward."""
+    cfg = micro_cfg()
+    dims = {k: getattr(cfg, k) for k in synth.MODEL_KEYS}
+    params = synth.perturbed_params(dims, seed=13, scale=0.3).astype(np.float64)
+    rng = np.random.default_rng(14)
+    idx = rng.integers(0, cfg.vocab_size, (2, 8))
+    tgt = rng.integers(0, cfg.vocab_size, (2, 8))
+    dr = O.Dropout(0.25, seed=2024, step=9)
+    _, grads, _ = O.loss_and_grads(params, idx, tgt, cfg, dropout=dr)
+    h, off = 1e-6, 0
+    for name, shape in O.param_shapes(cfg):
+        n = int(np.prod(shape))
+        gmax = np.abs(grads[off:off + n]).max()
+        for j in rng.choice(n, size=min(n, 6), replace=False):
+            e = off + j
+            pp, pm = params.copy(), params.copy()
+            pp[e] += h
+            pm[e] -= h
+            fd = (O.forward(pp, idx, tgt, cfg, dropout=dr)[1] -
+                  O.forward(pm, idx, tgt, cfg, dropout=dr)[1]) / (2 * h)
+            assert abs(fd - grads[e]) <= 1e-5 * (abs(grads[e]) + 1e-3 * gmax + 1e-12), (name, j)
+        off += n
