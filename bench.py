@@ -8,10 +8,13 @@ GPT-2 vocabulary, N(0, 0.02) weights with 0.02/sqrt(24) residual
 projections, all resident in HBM before the timed region.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--fp16]
+                    [--dropout P]
 
 Prints one JSON line.  --fp16 times the same step in IEEE half precision
 with dynamic loss scaling (scaled forward, backward, then unscale, clip,
-AdamW or skip and scale update on the device).
+AdamW or skip and scale update on the device).  --dropout P times it with
+dropout P at the embedding sum, the attention probabilities and the MLP output
+(a fresh Philox counter word per step).
 """
 from __future__ import annotations
 
@@ -243,6 +246,8 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="instead of training, time sampling with the KV cache for B sequences")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="train with dropout P (the pretraining configuration uses 0)")
     ap.add_argument("--fp16", action="store_true",
                     help="IEEE half precision with dynamic loss scaling instead of bf16")
     ap.add_argument("--probe", action="store_true",
@@ -277,16 +282,18 @@ def main():
         batches.append((torch.as_tensor(idx).cuda(), torch.as_tensor(tgt).cuda()))
     torch.cuda.synchronize()
 
+    drop = (lambda i: (args.dropout, 1337, i)) if args.dropout > 0 else (lambda i: None)
+
     def step(i):
         idx, tgt = batches[i % nb]
         lr = min(6e-4 * (i + 1) / 715, 6e-4)
         if args.fp16:
             # scale, backward, unscale, clip, step or skip, update
-            model.forward(idx, tgt, scaled=True)
+            model.forward(idx, tgt, scaled=True, dropout=drop(i))
             model.backward(zero_first=True)
             model.amp_step(lr=lr, max_norm=1.0)
         else:
-            model.forward(idx, tgt)
+            model.forward(idx, tgt, dropout=drop(i))
             model.backward(zero_first=True)
             model.adamw_step(lr=lr, t=i + 1, max_norm=1.0)
 
@@ -330,6 +337,8 @@ def main():
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(dims)
     prec = "fp16 (dynamic loss scaling)" if args.fp16 else "bf16"
+    if args.dropout > 0:
+        prec += f" dropout {args.dropout:g}"
     out = {
         "metric": f"train tokens/sec + ms/step + MFU, GPT-2 124M {prec} B=16 T=1024, 1 MI355X",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -337,7 +346,7 @@ def main():
         "ms_per_step_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "mfu": round(mfu, 4),
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None if args.fp16 else round(value / A100_TOKENS_PER_S, 3),
+        "vs_baseline": None if (args.fp16 or args.dropout > 0) else round(value / A100_TOKENS_PER_S, 3),
         "baseline": "pages' 90 ms/step = ~182,000 tokens/s on one A100 SXM (context)",
         "dtype": "fp16" if args.fp16 else "bf16",
         "data": "synthetic (Zipf(1.1) token ids; random-init weights)",

@@ -184,6 +184,40 @@ int gpt_amp_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
                  float* norm_out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Dropout
+ * ------------------------------------------------------------------------- */
+
+/* Dropout of a training forward ("nanoGPT", Part IV Stage 4 and Part V Deep
+ * dive 1; "Build GPT from scratch", "The model in forty lines"; 0.2 for the
+ * character-level model, "nanoGPT" Part VIII check 15): applied to the
+ * embedding sum, to the attention probabilities (after the softmax, before
+ * the product with v) and to the MLP output; a kept value is multiplied by
+ * 1/(1-p).  Reading: no dropout after the attention's output projection
+ * (neither page puts one there).  Masks come from Philox4x32-10 (Salmon et
+ * al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) with key = seed
+ * (low word first): element (row, col) of a site's matrix is kept when word
+ * col % 4 of philox(counter = {col / 4, row, site * 2^24 + bh, step}) is
+ * >= ceil(p * 2^32).  Sites: 0 the embedding sum (rows b*T + t, columns
+ * features), 1 + 2l the attention probabilities of layer l (rows queries,
+ * columns keys, bh = b * n_head + h), 2 + 2l the MLP output of layer l (as
+ * the embedding); bh = 0 except for attention. */
+typedef struct {
+  float p;       /* probability of dropping an element, in [0, 1); 0: none */
+  uint32_t step; /* counter word telling forward calls apart */
+  uint64_t seed; /* Philox key */
+} gpt_dropout;
+
+/* gpt_forward_loss with optional dynamic loss scaling (scaler: as
+ * gpt_forward_loss_scaled; NULL: none) and optional dropout (NULL or p = 0:
+ * none).  gpt_backward uses the same masks, regenerated from the counter.
+ * Errors: as gpt_forward_loss; GPT_EINVAL for p outside [0, 1);
+ * GPT_EUNSUPPORTED for dropout with more than 127 layers. */
+int gpt_forward_loss_ex(gpt_model* h, const int32_t* idx, const int32_t* targets,
+                        int32_t B, int32_t T, float loss_scale,
+                        const gpt_loss_scaler* scaler, const gpt_dropout* dropout,
+                        float* loss_out, void* logits_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sampling from the model ("nanoGPT", Part IV, one generation: sample.py +
  * model.py, generate), with a cache of keys and values ("Build GPT from
  * scratch", exercise "Add a KV cache") so that a step feeds one new token per
@@ -281,6 +315,13 @@ int gpt_op_attention_bwd(int32_t dtype, const void* qkv, const void* out,
 int gpt_op_layernorm_fwd(int32_t dtype, const float* x, const float* w, const float* b,
                          void* y, float* mean, float* rstd, int32_t M, int32_t C,
                          void* stream);
+
+/* y = x times the dropout multipliers of one site's matrix (see gpt_dropout):
+ * x, y device fp32 [rows][cols] (cols % 4 == 0; y may equal x); site_word =
+ * site * 2^24 + bh.  p = 0 copies.  The masks of every site can be checked
+ * element by element through this call. */
+int gpt_op_dropout(const float* x, float* y, int64_t rows, int32_t cols, float p,
+                   uint64_t seed, uint32_t step, uint32_t site_word, void* stream);
 
 /* Masked softmax cross-entropy, in place: logits act [N][ldv] -> dlogits
  * (loss_scale * (softmax - onehot) / n_valid over columns < V, zero for

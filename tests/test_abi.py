@@ -124,3 +124,15 @@ def test_loss_scaling_and_dtype_arguments_are_checked_without_a_device():
     assert lib.gpt_init(ctypes.byref(h), ctypes.byref(cfg), None, None, None, None, None, None,
                         None) == bd.GPT_EINVAL
     assert not h.value
+
+
+def test_dropout_arguments_are_checked_without_a_device():
+    lib = bd.lib
+    assert lib.gpt_forward_loss_ex(None, None, None, 1, 1, 1.0, None, None, None, None,
+                                   None) == bd.GPT_EINVAL
+    assert lib.gpt_op_dropout(None, None, 4, 4, 0.5, 1, 0, 0, None) == bd.GPT_EINVAL
+    # cols % 4 != 0 and p outside [0, 1) are refused before any HIP call
+    buf = ctypes.c_void_p(16)
+    assert lib.gpt_op_dropout(buf, buf, 4, 6, 0.5, 1, 0, 0, None) == bd.GPT_EINVAL
+    assert lib.gpt_op_dropout(buf, buf, 4, 8, 1.0, 1, 0, 0, None) == bd.GPT_EINVAL
+    assert ctypes.sizeof(bd.gpt_dropout) == 16

@@ -36,12 +36,20 @@ class gpt_config(ctypes.Structure):
         "max_batch")]
 
 
+class gpt_dropout(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_float), ("step", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+
+
 _p, _i32, _i64, _f = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _SIGS = {
     "gpt_query_sizes": [ctypes.POINTER(gpt_config), ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
     "gpt_init": [ctypes.POINTER(_p), ctypes.POINTER(gpt_config), _p, _p, _p, _p, _p, _p, _p],
     "gpt_forward_loss": [_p, _p, _p, _i32, _i32, _f, _p, _p, _p],
     "gpt_forward_loss_scaled": [_p, _p, _p, _i32, _i32, _f, _p, _p, _p, _p],
+    "gpt_forward_loss_ex": [_p, _p, _p, _i32, _i32, _f, _p, ctypes.POINTER(gpt_dropout), _p, _p,
+                            _p],
+    "gpt_op_dropout": [_p, _p, _i64, _i32, _f, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                       _p],
     "gpt_amp_step": [_p, _f, _f, _f, _f, _f, _f, _p, _f, _f, _i32, _p, _p],
     "gpt_backward": [_p, _i32, _p],
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
@@ -135,17 +143,26 @@ class GPT:
         import torch
         return {GPT_BF16: torch.bfloat16, GPT_FP16: torch.float16}.get(self.mode, torch.float32)
 
-    def forward(self, idx, targets=None, loss_scale=1.0, logits=False, scaled=False):
+    def forward(self, idx, targets=None, loss_scale=1.0, logits=False, scaled=False,
+                dropout=None):
         """idx/targets: int32 cuda tensors [B, T].  Returns (loss tensor [1] or
         None, logits tensor [B, T, Vp] or None).  scaled: the logits gradient
-        is further multiplied by the device loss scale (gpt_forward_loss_scaled)."""
+        is further multiplied by the device loss scale (gpt_forward_loss_scaled).
+        dropout: (p, seed, step) for a training forward with dropout
+        (gpt_forward_loss_ex); the next backward uses its masks."""
         import torch
         B, T = idx.shape
         out = None
         if logits:
             out = torch.empty((B, T, self.dims["padded_vocab"]), dtype=self.act_dtype, device=idx.device)
         loss = self.scalars[0:1] if targets is not None else None
-        if scaled:
+        if dropout is not None:
+            p, seed, step = dropout
+            dr = gpt_dropout(p, step, seed)
+            check(lib.gpt_forward_loss_ex(self.handle, _ptr(idx), _ptr(targets), B, T, loss_scale,
+                                          _ptr(self.scaler) if scaled else None, ctypes.byref(dr),
+                                          _ptr(loss), _ptr(out), _stream()), "gpt_forward_loss_ex")
+        elif scaled:
             check(lib.gpt_forward_loss_scaled(self.handle, _ptr(idx), _ptr(targets), B, T,
                                               loss_scale, _ptr(self.scaler), _ptr(loss), _ptr(out),
                                               _stream()), "gpt_forward_loss_scaled")
@@ -346,6 +363,17 @@ def op_layernorm_fwd(x, w, b, bf16=False, fp16=False):
     check(lib.gpt_op_layernorm_fwd(_bf(y), _ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(mean),
                                    _ptr(rstd), M, C, _stream()), "gpt_op_layernorm_fwd")
     return y, mean, rstd
+
+
+def op_dropout(x, p, seed, step, site_word):
+    """y = x times the dropout multipliers of one site (gpt_op_dropout); x fp32
+    cuda [rows, cols]."""
+    import torch
+    rows, cols = x.shape
+    y = torch.empty_like(x)
+    check(lib.gpt_op_dropout(_ptr(x), _ptr(y), rows, cols, p, seed, step, site_word, _stream()),
+          "gpt_op_dropout")
+    return y
 
 
 def op_cross_entropy(logits, targets, V, loss_scale=1.0):

@@ -69,10 +69,8 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, i
                      int32_t T, float loss_scale, float* loss_out, void* logits_out,
                      void* stream) {
   if (!h) return null_handle();
-  return h->fp16 ? f16::gpt_forward_loss((f16::Model*)h->impl, idx, targets, B, T, loss_scale,
-                                         nullptr, loss_out, logits_out, stream)
-                 : b16::gpt_forward_loss((b16::Model*)h->impl, idx, targets, B, T, loss_scale,
-                                         nullptr, loss_out, logits_out, stream);
+  return gpt_forward_loss_ex(h, idx, targets, B, T, loss_scale, nullptr, nullptr, loss_out,
+                             logits_out, stream);
 }
 
 int gpt_forward_loss_scaled(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B,
@@ -83,11 +81,20 @@ int gpt_forward_loss_scaled(gpt_model* h, const int32_t* idx, const int32_t* tar
     gpt_error_text() = "null scaler";
     return GPT_EINVAL;
   }
-  const float* ds = &scaler->scale;
+  return gpt_forward_loss_ex(h, idx, targets, B, T, loss_scale, scaler, nullptr, loss_out,
+                             logits_out, stream);
+}
+
+int gpt_forward_loss_ex(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B,
+                        int32_t T, float loss_scale, const gpt_loss_scaler* scaler,
+                        const gpt_dropout* dropout, float* loss_out, void* logits_out,
+                        void* stream) {
+  if (!h) return null_handle();
+  const float* ds = scaler ? &scaler->scale : nullptr;
   return h->fp16 ? f16::gpt_forward_loss((f16::Model*)h->impl, idx, targets, B, T, loss_scale, ds,
-                                         loss_out, logits_out, stream)
+                                         dropout, loss_out, logits_out, stream)
                  : b16::gpt_forward_loss((b16::Model*)h->impl, idx, targets, B, T, loss_scale, ds,
-                                         loss_out, logits_out, stream);
+                                         dropout, loss_out, logits_out, stream);
 }
 
 int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
@@ -208,6 +215,11 @@ int gpt_op_attention_bwd(int32_t dtype, const void* qkv, const void* out, const 
 int gpt_op_layernorm_fwd(int32_t dtype, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int32_t M, int32_t C, void* stream) {
   return OP(gpt_op_layernorm_fwd, dtype, x, w, b, y, mean, rstd, M, C, stream);
+}
+
+int gpt_op_dropout(const float* x, float* y, int64_t rows, int32_t cols, float p, uint64_t seed,
+                   uint32_t step, uint32_t site_word, void* stream) {
+  return b16::gpt_op_dropout(x, y, rows, cols, p, seed, step, site_word, stream);
 }
 
 int gpt_op_cross_entropy(int32_t dtype, void* logits, const int32_t* targets, float* loss,

@@ -19,8 +19,9 @@ std::string& gpt_error_text();
   int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, float* adam_m,  \
                float* adam_v, void* workspace, const float* init_params, void* stream);         \
   int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t B,         \
-                       int32_t T, float loss_scale, const float* dscale, float* loss_out,       \
-                       void* logits_out, void* stream);                                         \
+                       int32_t T, float loss_scale, const float* dscale,                        \
+                       const gpt_dropout* dropout, float* loss_out, void* logits_out,           \
+                       void* stream);                                                           \
   int gpt_backward(Model* h, int32_t zero_first, void* stream);                                 \
   int gpt_adamw_step(Model* h, float lr, float beta1, float beta2, float eps,                   \
                      float weight_decay, float max_norm, int32_t t, int32_t skip_nonfinite,     \
@@ -53,6 +54,8 @@ std::string& gpt_error_text();
   int gpt_op_layernorm_fwd(int32_t h16, const float* x, const float* w, const float* b,         \
                            void* y, float* mean, float* rstd, int32_t M, int32_t C,             \
                            void* stream);                                                       \
+  int gpt_op_dropout(const float* x, float* y, int64_t rows, int32_t cols, float p,             \
+                     uint64_t seed, uint32_t step, uint32_t site_word, void* stream);           \
   int gpt_op_cross_entropy(int32_t h16, void* logits, const int32_t* targets, float* loss,      \
                            float* row_loss, int32_t* n_valid, float loss_scale, int32_t N,      \
                            int32_t V, int32_t ldv, void* stream);

@@ -28,7 +28,7 @@ namespace HALF_NS {
 // ================================================================ generic (fp32 mode)
 template <typename T>
 __global__ void attn_fwd_generic(const T* __restrict__ qkv, T* __restrict__ out,
-                                 float* __restrict__ lse, int B, int Tn, int H, int C) {
+                                 float* __restrict__ lse, int B, int Tn, int H, int C, Drop dr) {
   const int hs = C / H;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
@@ -47,8 +47,9 @@ __global__ void attn_fwd_generic(const T* __restrict__ qkv, T* __restrict__ out,
     s *= scale;
     const float mn = fmaxf(m, s);
     const float alpha = expf(m - mn), p = expf(s - mn);
-    l = l * alpha + p;
-    for (int c = 0; c < hs; ++c) o[c] = o[c] * alpha + p * ldf(V + c);
+    l = l * alpha + p;  // the normaliser sums the probabilities before dropout
+    const float pz = dr.thresh ? p * drop1(dr, (uint32_t)j, (uint32_t)q, (uint32_t)bh) : p;
+    for (int c = 0; c < hs; ++c) o[c] = o[c] * alpha + pz * ldf(V + c);
     m = mn;
   }
   T* O = out + ((int64_t)b * Tn + q) * C + h * hs;
@@ -82,7 +83,7 @@ __global__ void attn_bwd_dot(const T* __restrict__ out, const T* __restrict__ do
 template <typename T>
 __global__ void attn_bwd_dq_generic(const T* __restrict__ qkv, const float* __restrict__ lse,
                                     const float* __restrict__ D, const T* __restrict__ dout,
-                                    T* __restrict__ dqkv, int B, int Tn, int H, int C) {
+                                    T* __restrict__ dqkv, int B, int Tn, int H, int C, Drop dr) {
   const int hs = C / H;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
@@ -103,6 +104,7 @@ __global__ void attn_bwd_dq_generic(const T* __restrict__ qkv, const float* __re
       dp += ldf(dO + c) * ldf(V + c);
     }
     const float p = expf(s * scale - L);
+    if (dr.thresh) dp *= drop1(dr, (uint32_t)j, (uint32_t)q, (uint32_t)bh);
     const float ds = p * (dp - Dq);
     for (int c = 0; c < hs; ++c) dq[c] += ds * ldf(K + c);
   }
@@ -113,7 +115,7 @@ __global__ void attn_bwd_dq_generic(const T* __restrict__ qkv, const float* __re
 template <typename T>
 __global__ void attn_bwd_dkdv_generic(const T* __restrict__ qkv, const float* __restrict__ lse,
                                       const float* __restrict__ D, const T* __restrict__ dout,
-                                      T* __restrict__ dqkv, int B, int Tn, int H, int C) {
+                                      T* __restrict__ dqkv, int B, int Tn, int H, int C, Drop dr) {
   const int hs = C / H;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
@@ -133,9 +135,10 @@ __global__ void attn_bwd_dkdv_generic(const T* __restrict__ qkv, const float* __
       dp += ldf(dO + c) * ldf(V + c);
     }
     const float p = expf(s * scale - lse[(int64_t)bh * Tn + q]);
-    const float ds = p * (dp - D[(int64_t)bh * Tn + q]);
+    const float z = dr.thresh ? drop1(dr, (uint32_t)j, (uint32_t)q, (uint32_t)bh) : 1.f;
+    const float ds = p * (z * dp - D[(int64_t)bh * Tn + q]);
     for (int c = 0; c < hs; ++c) {
-      dv[c] += p * ldf(dO + c);
+      dv[c] += p * z * ldf(dO + c);
       dk[c] += ds * ldf(Q + c);
     }
   }
@@ -256,7 +259,7 @@ template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restrict__ qkv,
                                                            h16_t* __restrict__ out,
                                                            float* __restrict__ lse, int B, int Tn,
-                                                           int H, int C) {
+                                                           int H, int C, Drop dr) {
   __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
@@ -339,12 +342,25 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
         uint32_t w[4];
+        float pe[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          w[j] = pack2h(fexp2(fmaf(s[t][8 * ss + 2 * j], sc, nm)),
-                         fexp2(fmaf(s[t][8 * ss + 2 * j + 1], sc, nm)));
+          pe[2 * j] = fexp2(fmaf(s[t][8 * ss + 2 * j], sc, nm));
+          pe[2 * j + 1] = fexp2(fmaf(s[t][8 * ss + 2 * j + 1], sc, nm));
+          w[j] = pack2h(pe[2 * j], pe[2 * j + 1]);
           // the row sum adds the probabilities as rounded for the product
+          // (before dropout: the normaliser is the softmax's)
           l = FDOT2(__builtin_bit_cast(h16x2_t, w[j]), ones, l);
+        }
+        if (dr.thresh) {
+          // keys kv0 + 32t + 16ss + 4(lane/32) + 0..3, then + 8
+          const uint32_t g = (uint32_t)(kv0 + 32 * t + 16 * ss + 4 * (lane >> 5)) >> 2;
+          const float4 za = drop4(dr, g, (uint32_t)my_q, (uint32_t)bh);
+          const float4 zb = drop4(dr, g + 2, (uint32_t)my_q, (uint32_t)bh);
+          w[0] = pack2h(pe[0] * za.x, pe[1] * za.y);
+          w[1] = pack2h(pe[2] * za.z, pe[3] * za.w);
+          w[2] = pack2h(pe[4] * zb.x, pe[5] * zb.y);
+          w[3] = pack2h(pe[6] * zb.z, pe[7] * zb.w);
         }
         const uint4 wv = make_uint4(w[0], w[1], w[2], w[3]);
         const h16x8_t pb = __builtin_bit_cast(h16x8_t, wv);
@@ -382,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
 template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     const h16_t* __restrict__ qkv, const float* __restrict__ Dg, const h16_t* __restrict__ dout,
-    h16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C) {
+    h16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C, Drop dr) {
   // per stage: Q tile, dO tile, 4 small slots (wave 0: scaled logsumexp, wave 1: D)
   __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2 * TILE_ELEMS + 4 * 512];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -467,10 +483,22 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
           sa[r] = (unsigned)(c - lo) < span ? sa[r] : 0.f;
         }
       }
+      if (dr.thresh) {
+        // dropout: dS = P (z dP~ - D) and dV += (P z)^T dO; this lane's key
+        // is one column of the mask, so each element takes its own word
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = 32 * t + ACC_ROW(r, lane);
-        dpa[r] = sa[r] * (dpa[r] - sD[qq]);
+        for (int r = 0; r < 16; ++r) {
+          const int qq = 32 * t + ACC_ROW(r, lane);
+          const float z = drop1(dr, (uint32_t)my_kv, (uint32_t)(qs + qq), (uint32_t)bh);
+          dpa[r] = sa[r] * (z * dpa[r] - sD[qq]);
+          sa[r] *= z;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qq = 32 * t + ACC_ROW(r, lane);
+          dpa[r] = sa[r] * (dpa[r] - sD[qq]);
+        }
       }
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
@@ -540,7 +568,7 @@ template <int FLASH_NS>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     const h16_t* __restrict__ qkv, const h16_t* __restrict__ outp, const float* __restrict__ lse,
     float* __restrict__ Dg, const h16_t* __restrict__ dout, h16_t* __restrict__ dqkv,
-    float* __restrict__ cs_part, int B, int Tn, int H, int C) {
+    float* __restrict__ cs_part, int B, int Tn, int H, int C, Drop dr) {
   __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
@@ -628,10 +656,25 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
         for (int r = 0; r < 16; ++r)
           s[t][r] = (32 * t + 8 * (r >> 2) + (r & 3)) > lim ? 0.f : s[t][r];
     }
+    if (dr.thresh) {
+      // dS = P (z dP~ - D); keys kv0 + 32t + 8G + 4(lane/32) + 0..3 share a word group
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[t][r] = s[t][r] * (dp[t][r] - Dq);
+        for (int G = 0; G < 4; ++G) {
+          const uint32_t g = (uint32_t)(kv0 + 32 * t + 8 * G + 4 * (lane >> 5)) >> 2;
+          const float4 z = drop4(dr, g, (uint32_t)my_q, (uint32_t)bh);
+          dp[t][4 * G + 0] = s[t][4 * G + 0] * (z.x * dp[t][4 * G + 0] - Dq);
+          dp[t][4 * G + 1] = s[t][4 * G + 1] * (z.y * dp[t][4 * G + 1] - Dq);
+          dp[t][4 * G + 2] = s[t][4 * G + 2] * (z.z * dp[t][4 * G + 2] - Dq);
+          dp[t][4 * G + 3] = s[t][4 * G + 3] * (z.w * dp[t][4 * G + 3] - Dq);
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[t][r] = s[t][r] * (dp[t][r] - Dq);
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -687,32 +730,34 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
 
 // ================================================================ launchers
 int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
-                         int C, hipStream_t s) {
+                         int C, hipStream_t s, Drop dr) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
   if (h16 && hs == 64) {
     const int nqb = (Tn + 127) / 128;
     hipLaunchKernelGGL(flash_fwd_kernel<FLASH_FWD_NS>, dim3(nqb * B * H), dim3(256), 0, s,
-                       (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C);
+                       (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C, dr);
   } else if (h16) {
     hipLaunchKernelGGL(attn_fwd_generic<h16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                       (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C);
+                       (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C, dr);
   } else {
     hipLaunchKernelGGL(attn_fwd_generic<float>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                       (const float*)qkv, (float*)out, lse, B, Tn, H, C);
+                       (const float*)qkv, (float*)out, lse, B, Tn, H, C, dr);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 // D: fp32 scratch of 2*B*H*T elements (rowsum(dout * out), then the row
-// logsumexp times log2(e) for the 16-bit head-width-64 kernels).
+// logsumexp times log2(e) for the 16-bit head-width-64 kernels).  dr: the
+// forward's dropout of the probabilities (rowsum(dout * out) is still the
+// row's D with dropout: it equals rowsum(P * dP) for dP = z dP~).
 // cs_part / cs_out (optional): cs_out[n] (+)= column sums of dqkv (the bias
 // gradient of the fused q|k|v projection); cs_part is fp32 scratch of at
 // least max(B * cdiv(Tn, 128), colsum_part_rows(B * Tn)) x 3C elements.
 int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
                          float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
-                         ColsumJob* defer) {
+                         ColsumJob* defer, Drop dr) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
   const int64_t rows = (int64_t)B * H * Tn;
@@ -728,9 +773,10 @@ int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float
       float* cp = cs_out ? cs_part : nullptr;
       hipLaunchKernelGGL(flash_bwd_dq_kernel<FLASH_DQ_NS>, dim3(nb * B * H), dim3(256), 0, s,
                          (const h16_t*)qkv, (const h16_t*)out, lse, D, (const h16_t*)dout,
-                         (h16_t*)dqkv, cp, B, Tn, H, C);
+                         (h16_t*)dqkv, cp, B, Tn, H, C, dr);
       hipLaunchKernelGGL(flash_bwd_dkdv_kernel<FLASH_DKDV_NS>, dim3(nb * B * H), dim3(256), 0, s,
-                         (const h16_t*)qkv, D, (const h16_t*)dout, (h16_t*)dqkv, cp, B, Tn, H, C);
+                         (const h16_t*)qkv, D, (const h16_t*)dout, (h16_t*)dqkv, cp, B, Tn, H, C,
+                         dr);
       if (cs_out) {
         if (hipGetLastError() != hipSuccess) return -4;
         if (defer) {
@@ -745,9 +791,11 @@ int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float
       }
     } else {
       hipLaunchKernelGGL(attn_bwd_dq_generic<h16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                         (const h16_t*)qkv, lse, D, (const h16_t*)dout, (h16_t*)dqkv, B, Tn, H, C);
+                         (const h16_t*)qkv, lse, D, (const h16_t*)dout, (h16_t*)dqkv, B, Tn, H, C,
+                         dr);
       hipLaunchKernelGGL(attn_bwd_dkdv_generic<h16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                         (const h16_t*)qkv, lse, D, (const h16_t*)dout, (h16_t*)dqkv, B, Tn, H, C);
+                         (const h16_t*)qkv, lse, D, (const h16_t*)dout, (h16_t*)dqkv, B, Tn, H, C,
+                         dr);
     }
     if (cs_out && !flash) {
       if (hipGetLastError() != hipSuccess) return -4;
@@ -757,9 +805,9 @@ int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float
     hipLaunchKernelGGL(attn_bwd_dot<float>, dim3(cdiv(rows, 4)), dim3(256), 0, s,
                        (const float*)out, (const float*)dout, lse, D, nullptr, B, Tn, H, C);
     hipLaunchKernelGGL(attn_bwd_dq_generic<float>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                       (const float*)qkv, lse, D, (const float*)dout, (float*)dqkv, B, Tn, H, C);
+                       (const float*)qkv, lse, D, (const float*)dout, (float*)dqkv, B, Tn, H, C, dr);
     hipLaunchKernelGGL(attn_bwd_dkdv_generic<float>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
-                       (const float*)qkv, lse, D, (const float*)dout, (float*)dqkv, B, Tn, H, C);
+                       (const float*)qkv, lse, D, (const float*)dout, (float*)dqkv, B, Tn, H, C, dr);
     if (cs_out) {
       if (hipGetLastError() != hipSuccess) return -4;
       return colsum_launch(false, dqkv, B * Tn, 3 * C, cs_part, cs_out, cs_beta, s);

@@ -131,6 +131,55 @@ __device__ __forceinline__ void gelu_both(float u, float& g, float& gp) {
   gp = fmaf(g * (1.0f - s), q, s);
 }
 
+// ---------------------------------------------------------------- dropout
+// Masks from Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC'11): ten rounds of the bijection that
+// multiplies words 0 and 2 by two constants and mixes the halves of the
+// products with words 1 and 3 and the key; the key grows by two Weyl
+// increments between rounds.  Counter-based, so a backward kernel regenerates
+// the forward's mask from the element's coordinates alone.
+//
+// Element (row, col) of a site's matrix (for attention, query row and key
+// column of head bh = b * n_head + h) is kept when word col % 4 of
+// philox(counter = {col / 4, row, site_word + bh, step}, key = seed) is at
+// least thresh; a kept value is multiplied by scale = 1 / (1 - p).
+struct Drop {
+  uint32_t k0 = 0, k1 = 0;  // the 64-bit seed
+  uint32_t step = 0;        // counter word 3: tells forward calls apart
+  uint32_t site = 0;        // counter word 2: site * 2^24 (attention adds bh)
+  uint32_t thresh = 0;      // 0: no dropout
+  float scale = 1.f;
+};
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t h0 = __umulhi(0xD2511F53u, c0), l0 = 0xD2511F53u * c0;
+    const uint32_t h1 = __umulhi(0xCD9E8D57u, c2), l1 = 0xCD9E8D57u * c2;
+    c0 = h1 ^ c1 ^ k0;
+    c1 = l1;
+    c2 = h0 ^ c3 ^ k1;
+    c3 = l0;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+// multipliers (0 or scale) of columns 4g .. 4g+3 of one row
+__device__ __forceinline__ float4 drop4(const Drop& d, uint32_t g, uint32_t row, uint32_t bh) {
+  const uint4 w = philox4x32_10(g, row, d.site + bh, d.step, d.k0, d.k1);
+  return make_float4(w.x >= d.thresh ? d.scale : 0.f, w.y >= d.thresh ? d.scale : 0.f,
+                     w.z >= d.thresh ? d.scale : 0.f, w.w >= d.thresh ? d.scale : 0.f);
+}
+// multiplier of one element
+__device__ __forceinline__ float drop1(const Drop& d, uint32_t col, uint32_t row, uint32_t bh) {
+  const uint4 w = philox4x32_10(col >> 2, row, d.site + bh, d.step, d.k0, d.k1);
+  const uint32_t x = (col & 2) ? ((col & 1) ? w.w : w.z) : ((col & 1) ? w.y : w.x);
+  return x >= d.thresh ? d.scale : 0.f;
+}
+
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace HALF_NS

@@ -11,7 +11,8 @@ namespace HALF_NS {
 enum GemmEpi {
   EPI_ACT = 0,      // out_act[m][n] = acc + bias[n]
   EPI_F32 = 1,      // out_f32[m][n] = acc + bias[n]
-  EPI_RESID = 2,    // out_f32[m][n] = aux_f32[m][n] + acc + bias[n]   (residual add)
+  EPI_RESID = 2,    // out_f32[m][n] = aux_f32[m][n] + z[m][n] (acc + bias[n])  (residual add;
+                    // z the dropout multiplier of GemmEpiArgs::drop, 1 without dropout)
   EPI_GELU = 3,     // u = acc + bias[n]; out_act = gelu'(u); out2_act = gelu(u)
   EPI_GELU_BWD = 4, // out_act[m][n] = acc * aux_act[m][n]  (aux: the stored gelu'(u))
   EPI_ACCUM = 5     // out_f32[m][n] = (beta ? out_f32[m][n] : 0) + acc
@@ -45,6 +46,8 @@ struct GemmEpiArgs {
   // non-null: the pipelined kernel's column sums are left in cs_part and
   // described here instead of finalized (part = nullptr if it finalized)
   ColsumJob* cs_defer = nullptr;
+  // EPI_RESID: dropout of the branch output (element (m, n) of the site)
+  Drop drop;
 };
 
 // A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]; likewise B(n,k).

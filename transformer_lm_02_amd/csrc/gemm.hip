@@ -24,7 +24,9 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& e, int m, int n, fl
   } else if constexpr (EPI == EPI_F32) {
     ((float*)e.out)[i] = acc + (e.bias ? e.bias[n] : 0.f);
   } else if constexpr (EPI == EPI_RESID) {
-    ((float*)e.out)[i] = ((const float*)e.aux)[i] + acc + (e.bias ? e.bias[n] : 0.f);
+    float y = acc + (e.bias ? e.bias[n] : 0.f);
+    if (e.drop.thresh) y *= drop1(e.drop, (uint32_t)n, (uint32_t)m, 0);
+    ((float*)e.out)[i] = ((const float*)e.aux)[i] + y;
   } else if constexpr (EPI == EPI_GELU) {
     float g, gp;
     gelu_both(acc + (e.bias ? e.bias[n] : 0.f), g, gp);

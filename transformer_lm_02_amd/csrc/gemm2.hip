@@ -217,10 +217,19 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
     o[1] = make_float4(v[4] + bias8[4], v[5] + bias8[5], v[6] + bias8[6], v[7] + bias8[7]);
   } else if constexpr (EPI == EPI_RESID) {
     float4* o = (float4*)((float*)e.out + i);
-    o[0] = make_float4(x.a.x + v[0] + bias8[0], x.a.y + v[1] + bias8[1], x.a.z + v[2] + bias8[2],
-                       x.a.w + v[3] + bias8[3]);
-    o[1] = make_float4(x.b.x + v[4] + bias8[4], x.b.y + v[5] + bias8[5], x.b.z + v[6] + bias8[6],
-                       x.b.w + v[7] + bias8[7]);
+    if (e.drop.thresh) {
+      const float4 z0 = drop4(e.drop, (uint32_t)n >> 2, (uint32_t)m, 0);
+      const float4 z1 = drop4(e.drop, ((uint32_t)n >> 2) + 1, (uint32_t)m, 0);
+      o[0] = make_float4(x.a.x + z0.x * (v[0] + bias8[0]), x.a.y + z0.y * (v[1] + bias8[1]),
+                         x.a.z + z0.z * (v[2] + bias8[2]), x.a.w + z0.w * (v[3] + bias8[3]));
+      o[1] = make_float4(x.b.x + z1.x * (v[4] + bias8[4]), x.b.y + z1.y * (v[5] + bias8[5]),
+                         x.b.z + z1.z * (v[6] + bias8[6]), x.b.w + z1.w * (v[7] + bias8[7]));
+    } else {
+      o[0] = make_float4(x.a.x + v[0] + bias8[0], x.a.y + v[1] + bias8[1], x.a.z + v[2] + bias8[2],
+                         x.a.w + v[3] + bias8[3]);
+      o[1] = make_float4(x.b.x + v[4] + bias8[4], x.b.y + v[5] + bias8[5], x.b.z + v[6] + bias8[6],
+                         x.b.w + v[7] + bias8[7]);
+    }
   } else if constexpr (EPI == EPI_ACT) {
     *(uint4*)((h16_t*)e.out + i) =
         make_uint4(pack2h(v[0] + bias8[0], v[1] + bias8[1]), pack2h(v[2] + bias8[2], v[3] + bias8[3]),

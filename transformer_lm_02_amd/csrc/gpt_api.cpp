@@ -236,6 +236,7 @@ struct Model {
   bool have_fwd = false, have_targets = false;
   int B = 0, T = 0;
   const int32_t* idx = nullptr;
+  Drop drop;  // dropout of the last forward (site word 0); thresh 0: none
 
   bool h16() const { return cfg.mode != GPT_FP32; }
   int64_t es() const { return h16() ? 2 : 4; }
@@ -344,12 +345,36 @@ int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, fl
   return GPT_OK;
 }
 
+// Dropout sites of one forward: 0 the embedding sum, 1 + 2l the attention
+// probabilities of layer l, 2 + 2l the MLP output of layer l (counter word 2
+// = site * 2^24, plus b * n_head + h for attention).
+static Drop at_site(Drop d, int site) {
+  if (d.thresh) d.site = (uint32_t)site << 24;
+  return d;
+}
+// thresh = ceil(p 2^32) (a word w keeps its element when w >= thresh, i.e.
+// w / 2^32 >= p), scale = 1 / (1 - p); p = 0 gives no dropout
+static int make_drop(const gpt_dropout* g, int n_layer, Drop* out) {
+  *out = Drop();
+  if (!g || g->p == 0.f) return GPT_OK;
+  if (!(g->p > 0.f && g->p < 1.f)) return fail(GPT_EINVAL, "dropout p must be in [0, 1)");
+  if (2 * n_layer + 1 > 255) return fail(GPT_EUNSUPPORTED, "dropout covers at most 127 layers");
+  const double t = ceil((double)g->p * 4294967296.0);
+  out->thresh = (uint32_t)(t > 4294967295.0 ? 4294967295.0 : t);
+  out->scale = (float)(1.0 / (1.0 - (double)g->p));
+  out->k0 = (uint32_t)g->seed;
+  out->k1 = (uint32_t)(g->seed >> 32);
+  out->step = g->step;
+  return GPT_OK;
+}
+
 // Embedding, the L blocks and the final LayerNorm over B sequences of T
-// tokens ([NG] Part IV Stage 4: GPT.forward up to ln_f).  With kv set, each
-// block's keys and values are also stored in the cache kv (sized for B
-// sequences of max_len positions) at positions [0, T).
+// tokens ([NG] Part IV Stage 4: GPT.forward up to ln_f), with the dropout dr
+// (none for sampling).  With kv set, each block's keys and values are also
+// stored in the cache kv (sized for B sequences of max_len positions) at
+// positions [0, T).
 static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, int max_len,
-                         hipStream_t s) {
+                         hipStream_t s, Drop dr = Drop()) {
   const gpt_config& c = h->cfg;
   const bool bf = h->h16();
   const WsOff& w = h->wo;
@@ -357,7 +382,7 @@ static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, i
   const int M = B * T, d = c.n_embd, H = c.n_head;
   const int64_t kv_layer = 2ll * B * H * max_len * (d / H);
   CK(embed_fwd_launch(idx, h->P(p.wte), h->P(p.wpe), h->at<float>(w.layer.empty() ? w.x_final : w.layer[0].x_in),
-                      M, T, d, c.padded_vocab, h->at<int>(w.flags), s));
+                      M, T, d, c.padded_vocab, h->at<int>(w.flags), s, at_site(dr, 0)));
   for (int l = 0; l < c.n_layer; ++l) {
     const WsLayer& L = w.layer[l];
     const LayerOff& P = p.layer[l];
@@ -373,7 +398,8 @@ static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, i
     if (kv)
       CK(kv_store_launch(bf, h->at(L.qkv), (char*)kv + l * kv_layer * h->es(), B, T, H, d / H,
                          max_len, 0, s));
-    CK(attention_fwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), B, T, H, d, s));
+    CK(attention_fwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), B, T, H, d, s,
+                            at_site(dr, 1 + 2 * l)));
     e = GemmEpiArgs();
     e.out = h->at(L.x_mid);
     e.aux = h->at(L.x_in);
@@ -395,6 +421,7 @@ static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, i
     e.aux = h->at(L.x_mid);
     e.bias = h->P(P.mprojb);
     e.ldc = d;
+    e.drop = at_site(dr, 2 + 2 * l);
     CK(gemm_launch(bf, true, true, EPI_RESID, h->at(L.g), 4 * d, h->W(P.mprojw), 4 * d, M, d, 4 * d,
                    4 * d, 4 * d, e, s));
   }
@@ -404,13 +431,15 @@ static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, i
 }
 
 int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
-                     float loss_scale, const float* dscale, float* loss_out, void* logits_out,
-                     void* stream) {
+                     float loss_scale, const float* dscale, const gpt_dropout* dropout,
+                     float* loss_out, void* logits_out, void* stream) {
   if (!h || !idx) return fail(GPT_EINVAL, "null handle or idx");
   const gpt_config& c = h->cfg;
   if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
   if (T < 1) return fail(GPT_EINVAL, "T < 1");
   if (T > c.block_size) return fail(GPT_ESEQLEN, "T > block_size");
+  Drop dr;
+  if (int rc = make_drop(dropout, c.n_layer, &dr)) return rc;
   hipStream_t s = (hipStream_t)stream;
   const bool bf = h->h16();
   const WsOff& w = h->wo;
@@ -418,7 +447,7 @@ int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32
   const int M = B * T, d = c.n_embd;
   h->have_fwd = false;
 
-  CK(forward_stack(h, idx, B, T, nullptr, 1, s));
+  CK(forward_stack(h, idx, B, T, nullptr, 1, s, dr));
   {
     GemmEpiArgs e;
     e.out = h->at(w.logits);
@@ -442,6 +471,7 @@ int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32
   h->B = B;
   h->T = T;
   h->idx = idx;
+  h->drop = dr;
   return GPT_OK;
 }
 
@@ -653,10 +683,14 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
       CK(gemm_launch(bf, true, false, EPI_ACT, h->at(w.logits), vi, h->W(p.wte), d, M, d, vi, vi,
                      c.padded_vocab, e, s));
   }
+  // with dropout, the LayerNorm backward that yields the gradient at a block's
+  // output also forms the masked copy that the MLP projection's backward reads
+  // (dres itself, the residual's gradient, stays unmasked)
+  const Drop dr = h->drop;
   CK(layernorm_bwd_launch(bf, dln, h->at<float>(w.x_final), h->at<float>(w.lnf_mean),
                           h->at<float>(w.lnf_rstd), h->P(p.lnfw), dres, dres_act, 0, ln_slice(),
                           h->G(p.lnfw), h->G(p.lnfb), h->G(p.layer[c.n_layer - 1].mprojb), beta, M,
-                          d, s, &(job = ColsumJob())));
+                          d, s, &(job = ColsumJob()), at_site(dr, 2 + 2 * (c.n_layer - 1))));
   keep(job);
   for (int l = c.n_layer - 1; l >= 0; --l) {
     const WsLayer& L = w.layer[l];
@@ -719,7 +753,7 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     // formed by the attention backward
     CK(attention_bwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), h->at(w.dO), dbig,
                             h->at<float>(w.Dbuf), B, T, H, d, cs_slice(), h->G(P.attnb), beta, s,
-                            &(job = ColsumJob())));
+                            &(job = ColsumJob()), at_site(dr, 1 + 2 * l)));
     keep(job);
     // fused q|k|v projection: dW (+)= dqkv^T ln1 ; dln1 = dqkv Wqkv
     e = GemmEpiArgs();
@@ -739,10 +773,13 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     CK(layernorm_bwd_launch(bf, dln, h->at<float>(L.x_in), h->at<float>(L.ln1_mean),
                             h->at<float>(L.ln1_rstd), h->P(P.ln1w), dres, dres_act, 1, ln_slice(),
                             h->G(P.ln1w), h->G(P.ln1b), l > 0 ? h->G(p.layer[l - 1].mprojb) : nullptr,
-                            beta, M, d, s, &(job = ColsumJob())));
+                            beta, M, d, s, &(job = ColsumJob()),
+                            l > 0 ? at_site(dr, 2 + 2 * (l - 1)) : Drop()));
     keep(job);
   }
   CK(colsum_finalize_group_launch(jobs.data(), (int)jobs.size(), beta, s));
+  // the embedding sum's dropout: the gradient that reaches wte and wpe
+  CK(dropout_rows_launch(dres, dres, M, d, at_site(dr, 0), s));
   // embeddings: dwte[idx] += dx ; dwpe[t] (+)= sum_b dx
   CK(embed_bwd_launch(h->idx, dres, h->G(p.wte), h->G(p.wpe), B, T, c.block_size, d,
                       c.padded_vocab, beta, s));
@@ -858,6 +895,17 @@ int gpt_op_layernorm_fwd(int32_t h16, const float* x, const float* w, const floa
                          float* mean, float* rstd, int32_t M, int32_t C, void* stream) {
   if (!x || !w || !b || !y || !mean || !rstd || M < 0 || C < 1) return fail(GPT_EINVAL, "bad layernorm arguments");
   CK(layernorm_fwd_launch(h16 != 0, x, w, b, y, mean, rstd, M, C, (hipStream_t)stream));
+  return GPT_OK;
+}
+
+int gpt_op_dropout(const float* x, float* y, int64_t rows, int32_t cols, float p, uint64_t seed,
+                   uint32_t step, uint32_t site_word, void* stream) {
+  if (!x || !y || rows < 0 || cols < 1 || cols % 4) return fail(GPT_EINVAL, "bad dropout arguments");
+  gpt_dropout g{p, step, seed};
+  Drop dr;
+  if (int rc = make_drop(&g, 0, &dr)) return rc;
+  dr.site = site_word;
+  CK(dropout_rows_launch(x, y, rows, cols, dr, (hipStream_t)stream));
   return GPT_OK;
 }
 

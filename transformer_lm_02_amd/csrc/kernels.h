@@ -25,25 +25,33 @@ struct TransposeJob {
 int transpose_h16_launch(const h16_t* src, h16_t* dst, const TransposeJob* jobs, int njobs,
                           int total_tiles, hipStream_t s);
 
+// dr: dropout of the attention probabilities (site word without bh; the
+// kernels add b * H + h)
 int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
-                         int C, hipStream_t s);
+                         int C, hipStream_t s, Drop dr = Drop());
 // defer (optional): see ColsumJob; honoured by the head-width-64 16-bit path
 int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
                          float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
-                         ColsumJob* defer = nullptr);
+                         ColsumJob* defer = nullptr, Drop dr = Drop());
 
 int layernorm_fwd_launch(bool h16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s);
 int layernorm_bwd_part_rows(int M);
 // dy: the mode's activation type (16-bit or fp32) [M][C]
+// dres_act and bias_grad carry the dropout multipliers of dr (see layernorm.hip)
 int layernorm_bwd_launch(bool h16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
-                         int beta, int M, int C, hipStream_t s, ColsumJob* defer = nullptr);
+                         int beta, int M, int C, hipStream_t s, ColsumJob* defer = nullptr,
+                         Drop dr = Drop());
 
+// dr: dropout of the embedding sum (Drop in common.h; default: none)
 int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, float* x, int M,
-                     int Tn, int C, int Vp, int* flags, hipStream_t s);
+                     int Tn, int C, int Vp, int* flags, hipStream_t s, Drop dr = Drop());
+// y [M][C] fp32 = x times the dropout multipliers of dr (a copy when dr is
+// off; y may be x); C % 4 == 0
+int dropout_rows_launch(const float* x, float* y, int64_t M, int C, Drop dr, hipStream_t s);
 int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int Tn,
                      int block_size, int C, int Vp, int beta_wpe, hipStream_t s);
 int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s);

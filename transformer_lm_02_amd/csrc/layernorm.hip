@@ -106,7 +106,7 @@ template <typename T, int LN_MAXV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
     const T* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres,
-    T* __restrict__ dres_act, int accumulate, float* __restrict__ part, int M, int C) {
+    T* __restrict__ dres_act, int accumulate, float* __restrict__ part, int M, int C, Drop dr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nv = C >> 2;
   float4 pw[LN_MAXV], pb[LN_MAXV], pr[LN_MAXV], ww[LN_MAXV];
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
       pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
     }
     const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
-    float4* dr = (float4*)(dres + row * C);
+    float4* dres4 = (float4*)(dres + row * C);
     T* da = dres_act + row * C;
 #pragma unroll
     for (int i = 0; i < LN_MAXV; ++i) {
@@ -171,7 +171,12 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
         o.y = rs * (g[i].y - m1 - xh[i].y * m2) + pc[i].y;
         o.z = rs * (g[i].z - m1 - xh[i].z * m2) + pc[i].z;
         o.w = rs * (g[i].w - m1 - xh[i].w * m2) + pc[i].w;
-        dr[j] = o;
+        dres4[j] = o;
+        if (dr.thresh) {
+          // the gradient reaching the dropped-out branch output
+          const float4 z = drop4(dr, (uint32_t)j, (uint32_t)row, 0);
+          o.x *= z.x; o.y *= z.y; o.z *= z.z; o.w *= z.w;
+        }
         store4<T>(da + 4 * j, o);
         pr[i].x += o.x; pr[i].y += o.y; pr[i].z += o.z; pr[i].w += o.w;
       }
@@ -318,21 +323,23 @@ int layernorm_fwd_launch(bool h16, const float* x, const float* w, const float* 
 // partial rows written by one backward call (one per block)
 int layernorm_bwd_part_rows(int M) { return (int)cdiv(M, LN_BWD_ROWS); }
 
-// dres = (accumulate ? dres : 0) + LN'(dy); dres_act = copy; then
-// dw, db (beta-accumulated) and bias_grad (+)= column sum of dres, if non-null.
+// dres = (accumulate ? dres : 0) + LN'(dy); dres_act = z dres (z the dropout
+// multipliers of dr, 1 without it: the output gradient of the dropped-out
+// branch that feeds the residual); then dw, db (beta-accumulated) and
+// bias_grad (+)= column sum of dres_act, if non-null.
 int layernorm_bwd_launch(bool h16, const void* dy, const float* x, const float* mean,
                          const float* rstd, const float* w, float* dres, void* dres_act,
                          int accumulate, float* part, float* dw, float* db, float* bias_grad,
-                         int beta, int M, int C, hipStream_t s, ColsumJob* defer) {
+                         int beta, int M, int C, hipStream_t s, ColsumJob* defer, Drop dr) {
   if (C % 4 || C > LN_MAXV_MAX * 256) return -5;
   const int nb = (int)cdiv(M, LN_BWD_ROWS);
 #define LNB(V)                                                                                   \
   if (h16)                                                                                       \
     hipLaunchKernelGGL((ln_bwd_kernel<h16_t, V>), dim3(nb), dim3(256), 0, s, (const h16_t*)dy, \
-                       x, mean, rstd, w, dres, (h16_t*)dres_act, accumulate, part, M, C);       \
+                       x, mean, rstd, w, dres, (h16_t*)dres_act, accumulate, part, M, C, dr);   \
   else                                                                                            \
     hipLaunchKernelGGL((ln_bwd_kernel<float, V>), dim3(nb), dim3(256), 0, s, (const float*)dy, x, \
-                       mean, rstd, w, dres, (float*)dres_act, accumulate, part, M, C);
+                       mean, rstd, w, dres, (float*)dres_act, accumulate, part, M, C, dr);
   LN_DISPATCH(LNB)
 #undef LNB
   if (defer) {

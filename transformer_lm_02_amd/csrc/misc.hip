@@ -5,11 +5,12 @@ namespace HALF_NS {
 
 // ---------------------------------------------------------------- embedding
 // x[b*T + t] = wte[idx] + wpe[t] ("nanoGPT" (stanleyjacob.dev), Part IV Stage
-// 4: token embeddings plus learned position embeddings).  An id outside
-// [0, Vp) reads no memory: its token row is taken as zero and flag bit 1 set.
+// 4: token embeddings plus learned position embeddings, then dropout).  An id
+// outside [0, Vp) reads no memory: its token row is taken as zero and flag
+// bit 1 set.
 __global__ void embed_fwd_kernel(const int32_t* __restrict__ idx, const float* __restrict__ wte,
                                  const float* __restrict__ wpe, float* __restrict__ x, int M,
-                                 int Tn, int C, int Vp, int* __restrict__ flags) {
+                                 int Tn, int C, int Vp, int* __restrict__ flags, Drop dr) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
@@ -25,8 +26,27 @@ __global__ void embed_fwd_kernel(const int32_t* __restrict__ idx, const float* _
       const float4 w = a[j];
       v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
     }
+    if (dr.thresh) {
+      const float4 z = drop4(dr, (uint32_t)j, (uint32_t)row, 0);
+      v.x *= z.x; v.y *= z.y; v.z *= z.z; v.w *= z.w;
+    }
     o[j] = v;
   }
+}
+
+// y[m][c] = x[m][c] times the dropout multiplier of element (m, c)
+// (C % 4 == 0; y may be x): for example the gradient that reaches a
+// dropped-out value
+__global__ void dropout_rows_kernel(const float* x, float* y, int64_t M, int C, Drop dr) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nv = C >> 2;
+  if (i >= M * nv) return;
+  const int64_t row = i / nv;
+  const int j = (int)(i % nv);
+  float4 v = ((const float4*)x)[i];
+  const float4 z = drop4(dr, (uint32_t)j, (uint32_t)row, 0);
+  v.x *= z.x; v.y *= z.y; v.z *= z.z; v.w *= z.w;
+  ((float4*)y)[i] = v;
 }
 
 // dwte[idx[m]] += dx[m] (fp32 atomics: rows of frequent ids add up in the
@@ -303,9 +323,22 @@ int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, in
                            hipStream_t s);
 
 int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, float* x, int M,
-                     int Tn, int C, int Vp, int* flags, hipStream_t s) {
+                     int Tn, int C, int Vp, int* flags, hipStream_t s, Drop dr) {
   hipLaunchKernelGGL(embed_fwd_kernel, dim3(cdiv(M, 4)), dim3(256), 0, s, idx, wte, wpe, x, M, Tn,
-                     C, Vp, flags);
+                     C, Vp, flags, dr);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int dropout_rows_launch(const float* x, float* y, int64_t M, int C, Drop dr, hipStream_t s) {
+  if (M <= 0) return 0;
+  if (C % 4) return -5;
+  if (!dr.thresh) {
+    if (x == y) return 0;
+    return hipMemcpyAsync(y, x, (size_t)M * C * 4, hipMemcpyDeviceToDevice, s) == hipSuccess ? 0
+                                                                                           : -4;
+  }
+  hipLaunchKernelGGL(dropout_rows_kernel, dim3(cdiv(M * (C / 4), 256)), dim3(256), 0, s, x, y, M,
+                     C, dr);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
