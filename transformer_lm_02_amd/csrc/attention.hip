@@ -255,11 +255,17 @@ __device__ __forceinline__ void slot_steps(int i, int n, F& f) {
 // the lane's own; P^T in the accumulator registers is directly the B operand
 // of O^T = V^T P^T.  The key loop is unrolled by the ring depth so that every
 // LDS address is a per-lane base plus an immediate offset.
-template <int FLASH_NS>
+// DROP: dropout of the probabilities (Philox words of 4 consecutive keys per
+// call); the kept/dropped bits are written to dmask for the backward, one
+// 32-bit word per (query, 64-key block, lane half): bit 16t + r is register
+// r of accumulator tile t, i.e. key kv0 + 32t + 8(r/4) + 4(lane/32) + r%4,
+// at dmask[((bh * nkb + kb) * 2 + lane/32) * T + query].
+template <int FLASH_NS, bool DROP>
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restrict__ qkv,
                                                            h16_t* __restrict__ out,
                                                            float* __restrict__ lse, int B, int Tn,
-                                                           int H, int C, Drop dr) {
+                                                           int H, int C, Drop dr,
+                                                           uint32_t* __restrict__ dmask) {
   __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
@@ -337,6 +343,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
       m = mn;
     }
     const float nm = -m;
+    uint32_t mw = 0;  // DROP: this block's kept bits
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -352,8 +359,9 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
           // (before dropout: the normaliser is the softmax's)
           l = FDOT2(__builtin_bit_cast(h16x2_t, w[j]), ones, l);
         }
-        if (dr.thresh) {
-          // keys kv0 + 32t + 16ss + 4(lane/32) + 0..3, then + 8
+        if constexpr (DROP) {
+          // keys kv0 + 32t + 16ss + 4(lane/32) + 0..3 (registers 8ss..8ss+3),
+          // then + 8 (registers 8ss+4..8ss+7)
           const uint32_t g = (uint32_t)(kv0 + 32 * t + 16 * ss + 4 * (lane >> 5)) >> 2;
           const float4 za = drop4(dr, g, (uint32_t)my_q, (uint32_t)bh);
           const float4 zb = drop4(dr, g + 2, (uint32_t)my_q, (uint32_t)bh);
@@ -361,6 +369,11 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
           w[1] = pack2h(pe[2] * za.z, pe[3] * za.w);
           w[2] = pack2h(pe[4] * zb.x, pe[5] * zb.y);
           w[3] = pack2h(pe[6] * zb.z, pe[7] * zb.w);
+          const uint32_t bits = (za.x > 0.f ? 1u : 0u) | (za.y > 0.f ? 2u : 0u) |
+                                (za.z > 0.f ? 4u : 0u) | (za.w > 0.f ? 8u : 0u) |
+                                (zb.x > 0.f ? 16u : 0u) | (zb.y > 0.f ? 32u : 0u) |
+                                (zb.z > 0.f ? 64u : 0u) | (zb.w > 0.f ? 128u : 0u);
+          mw |= bits << (16 * t + 8 * ss);
         }
         const uint4 wv = make_uint4(w[0], w[1], w[2], w[3]);
         const h16x8_t pb = __builtin_bit_cast(h16x8_t, wv);
@@ -368,6 +381,12 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
         for (int ht = 0; ht < 2; ++ht)
           o[ht] = MFMA32(frag_rows(tV, 32 * ht, 2 * t + ss, lane), pb, o[ht]);
       }
+    if constexpr (DROP) {
+      if (my_q < Tn) {
+        const int nkb = (Tn + 63) / 64;
+        dmask[((int64_t)(bh * nkb + kb) * 2 + (lane >> 5)) * Tn + my_q] = mw;
+      }
+    }
   };
   for (int kb = 0; kb < nkv; kb += FLASH_NS) slot_steps<0, FLASH_NS>(kb, nkv, step);
   const float lt = l + __shfl_xor(l, 32, 64);
@@ -395,10 +414,14 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
 // operands are transposing reads of the dO and Q tiles.  Dg holds
 // rowsum(dO * O) at [0, B*H*T) and the row logsumexp times log2(e) at
 // [B*H*T, 2*B*H*T).
-template <int FLASH_NS>
+// DROP: each stage also brings the forward's kept bits of its 64 queries for
+// this workgroup's 128 keys (4 runs of 64 words: key block 0/1 x lane half
+// 0/1), one run per wave, into the second quarter of that wave's small slot.
+template <int FLASH_NS, bool DROP>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     const h16_t* __restrict__ qkv, const float* __restrict__ Dg, const h16_t* __restrict__ dout,
-    h16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C, Drop dr) {
+    h16_t* __restrict__ dqkv, float* __restrict__ cs_part, int B, int Tn, int H, int C, Drop dr,
+    const uint32_t* __restrict__ dmask) {
   // per stage: Q tile, dO tile, 4 small slots (wave 0: scaled logsumexp, wave 1: D)
   __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2 * TILE_ELEMS + 4 * 512];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -430,7 +453,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
   f32x16_t dv[2] = {zero16(), zero16()}, dk[2] = {zero16(), zero16()};
   const int qstart = k0;
   const int nq = (Tn - qstart + 63) / 64;
-  // 5 loads per wave per stage: 2 + 2 tile loads and one small load
+  // the kept bits: run (key block k0/64 + wave/2, lane half wave%2) of this head
+  const int nkb = (Tn + 63) / 64;
+  const __amdgpu_buffer_rsrc_t rmk =
+      rsrc_of(dmask, DROP ? (uint32_t)((int64_t)B * H * nkb * 2 * Tn * 4) : 0u);
+  const int64_t mrun = ((int64_t)(bh * nkb + (k0 >> 6) + (wave >> 1)) * 2 + (wave & 1)) * Tn;
+  // 5 loads per wave per stage (6 with DROP): 2 + 2 tile loads, one small load
+  constexpr int LOADS = DROP ? 6 : 5;
   auto stage = [&](h16_t* dst, int qs) {
     tile_dma(rq, dst, qs, ld, h * 64, lane, wave);
     tile_dma(rdo, dst + TILE_ELEMS, qs, C, h * 64, lane, wave);
@@ -440,13 +469,26 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     const uint32_t off = wave < 2 ? (uint32_t)((qs + lane) * 4) : 0xFFFFFF00u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsm, AS3(dst + 2 * TILE_ELEMS + wave * 512), 4, off,
                                              0, 0, 0);
+    if constexpr (DROP) {
+      // words of queries qs + lane; a run's end may read the next run's
+      // words (queries >= T, whose probabilities are zero) or, at the
+      // buffer's end, nothing
+      const int64_t wi = mrun + qs + lane;
+      const uint32_t moff = wi < (int64_t)B * H * nkb * 2 * Tn ? (uint32_t)(wi * 4) : 0xFFFFFF00u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rmk, AS3(dst + 2 * TILE_ELEMS + wave * 512 + 128), 4,
+                                               moff, 0, 0, 0);
+    }
   };
 #pragma unroll
   for (int st = 0; st < FLASH_NS - 1; ++st)
     if (st < nq) stage(ring[st], qstart + 64 * st);
+  // this lane's key in the forward's word layout: run (key block, half) and bit
+  const int kloc = my_kv - k0;  // 0..127
+  const int krun = 2 * (kloc >> 6) + ((kloc >> 2) & 1);
+  const int kbit = 16 * ((kloc >> 5) & 1) + 4 * ((kloc >> 3) & 3) + (kloc & 3);
   auto step = [&](int qi, auto slot) {
     constexpr int SL = decltype(slot)::value;
-    if (qi + FLASH_NS - 2 < nq) vm_wait_barrier<(FLASH_NS - 2) * 5>();
+    if (qi + FLASH_NS - 2 < nq) vm_wait_barrier<(FLASH_NS - 2) * LOADS>();
     else vm_wait_barrier<0>();
     if (qi + FLASH_NS - 1 < nq)
       stage(ring[(SL + FLASH_NS - 1) % FLASH_NS], qstart + 64 * (qi + FLASH_NS - 1));
@@ -454,6 +496,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     const h16_t* tdO = tQ + TILE_ELEMS;
     const float* sL = (const float*)(tQ + 2 * TILE_ELEMS);
     const float* sD = (const float*)(tQ + 2 * TILE_ELEMS + 512);
+    const uint32_t* sM = (const uint32_t*)(tQ + 2 * TILE_ELEMS + krun * 512 + 128);
     const int qs = qstart + 64 * qi;
     if (qs + 63 < kw || kw >= Tn) return;  // no query of this block sees these keys
     // query qs + 32t + ACC_ROW(r) is kept when it lies in [my_kv, Tn);
@@ -483,13 +526,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
           sa[r] = (unsigned)(c - lo) < span ? sa[r] : 0.f;
         }
       }
-      if (dr.thresh) {
-        // dropout: dS = P (z dP~ - D) and dV += (P z)^T dO; this lane's key
-        // is one column of the mask, so each element takes its own word
+      if constexpr (DROP) {
+        // dropout: dS = P (z dP~ - D) and dV += (P z)^T dO, z from the
+        // forward's bit for (query, this lane's key)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qq = 32 * t + ACC_ROW(r, lane);
-          const float z = drop1(dr, (uint32_t)my_kv, (uint32_t)(qs + qq), (uint32_t)bh);
+          const float z = (sM[qq] >> kbit) & 1u ? dr.scale : 0.f;
           dpa[r] = sa[r] * (z * dpa[r] - sD[qq]);
           sa[r] *= z;
         }
@@ -564,11 +607,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
 // grid: (T/128 query blocks, heaviest first) x (B*H); 4 waves x 32 queries.
 // S^T = K Q^T and dP^T = V dO^T put one query per lane; dS^T is the B
 // operand of dQ^T += K^T dS^T, whose A operand is a transposing read of K.
-template <int FLASH_NS>
+// DROP: the forward's kept bits (same lane layout) from dmask.
+template <int FLASH_NS, bool DROP>
 __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     const h16_t* __restrict__ qkv, const h16_t* __restrict__ outp, const float* __restrict__ lse,
     float* __restrict__ Dg, const h16_t* __restrict__ dout, h16_t* __restrict__ dqkv,
-    float* __restrict__ cs_part, int B, int Tn, int H, int C, Drop dr) {
+    float* __restrict__ cs_part, int B, int Tn, int H, int C, Drop dr,
+    const uint32_t* __restrict__ dmask) {
   __shared__ __attribute__((aligned(1024))) h16_t ring[FLASH_NS][2][TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
@@ -636,6 +681,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
     const h16_t* tV = ring[SL][1];
     const int kv0 = kb * 64;
     if (kv0 > qw + 31) return;
+    uint32_t mw = 0;
+    if constexpr (DROP) {
+      if (my_q < Tn) {
+        const int nkb = (Tn + 63) / 64;
+        mw = dmask[((int64_t)(bh * nkb + kb) * 2 + (lane >> 5)) * Tn + my_q];
+      }
+    }
     f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -656,18 +708,14 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
         for (int r = 0; r < 16; ++r)
           s[t][r] = (32 * t + 8 * (r >> 2) + (r & 3)) > lim ? 0.f : s[t][r];
     }
-    if (dr.thresh) {
-      // dS = P (z dP~ - D); keys kv0 + 32t + 8G + 4(lane/32) + 0..3 share a word group
+    if constexpr (DROP) {
+      // dS = P (z dP~ - D), z = scale where the forward kept the element
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int G = 0; G < 4; ++G) {
-          const uint32_t g = (uint32_t)(kv0 + 32 * t + 8 * G + 4 * (lane >> 5)) >> 2;
-          const float4 z = drop4(dr, g, (uint32_t)my_q, (uint32_t)bh);
-          dp[t][4 * G + 0] = s[t][4 * G + 0] * (z.x * dp[t][4 * G + 0] - Dq);
-          dp[t][4 * G + 1] = s[t][4 * G + 1] * (z.y * dp[t][4 * G + 1] - Dq);
-          dp[t][4 * G + 2] = s[t][4 * G + 2] * (z.z * dp[t][4 * G + 2] - Dq);
-          dp[t][4 * G + 3] = s[t][4 * G + 3] * (z.w * dp[t][4 * G + 3] - Dq);
+        for (int r = 0; r < 16; ++r) {
+          const float z = (mw >> (16 * t + r)) & 1u ? dr.scale : 0.f;
+          dp[t][r] = s[t][r] * (z * dp[t][r] - Dq);
         }
     } else {
 #pragma unroll
@@ -730,13 +778,18 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
 
 // ================================================================ launchers
 int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
-                         int C, hipStream_t s, Drop dr) {
+                         int C, hipStream_t s, Drop dr, uint32_t* dmask) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
   if (h16 && hs == 64) {
     const int nqb = (Tn + 127) / 128;
-    hipLaunchKernelGGL(flash_fwd_kernel<FLASH_FWD_NS>, dim3(nqb * B * H), dim3(256), 0, s,
-                       (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C, dr);
+    if (dr.thresh && !dmask) return -5;
+    if (dr.thresh)
+      hipLaunchKernelGGL((flash_fwd_kernel<FLASH_FWD_NS, true>), dim3(nqb * B * H), dim3(256), 0,
+                         s, (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C, dr, dmask);
+    else
+      hipLaunchKernelGGL((flash_fwd_kernel<FLASH_FWD_NS, false>), dim3(nqb * B * H), dim3(256), 0,
+                         s, (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C, dr, dmask);
   } else if (h16) {
     hipLaunchKernelGGL(attn_fwd_generic<h16_t>, dim3(cdiv(Tn, 64), B * H), dim3(64), 0, s,
                        (const h16_t*)qkv, (h16_t*)out, lse, B, Tn, H, C, dr);
@@ -750,14 +803,16 @@ int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B
 // D: fp32 scratch of 2*B*H*T elements (rowsum(dout * out), then the row
 // logsumexp times log2(e) for the 16-bit head-width-64 kernels).  dr: the
 // forward's dropout of the probabilities (rowsum(dout * out) is still the
-// row's D with dropout: it equals rowsum(P * dP) for dP = z dP~).
+// row's D with dropout: it equals rowsum(P * dP) for dP = z dP~); the
+// head-width-64 16-bit kernels read the forward's kept bits from dmask, the
+// others regenerate them.
 // cs_part / cs_out (optional): cs_out[n] (+)= column sums of dqkv (the bias
 // gradient of the fused q|k|v projection); cs_part is fp32 scratch of at
 // least max(B * cdiv(Tn, 128), colsum_part_rows(B * Tn)) x 3C elements.
 int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
                          float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
-                         ColsumJob* defer, Drop dr) {
+                         ColsumJob* defer, Drop dr, const uint32_t* dmask) {
   const int hs = C / H;
   if (hs * H != C || hs > 128) return -5;
   const int64_t rows = (int64_t)B * H * Tn;
@@ -771,12 +826,20 @@ int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float
       // so it runs first
       const int nb = (Tn + 127) / 128;
       float* cp = cs_out ? cs_part : nullptr;
-      hipLaunchKernelGGL(flash_bwd_dq_kernel<FLASH_DQ_NS>, dim3(nb * B * H), dim3(256), 0, s,
-                         (const h16_t*)qkv, (const h16_t*)out, lse, D, (const h16_t*)dout,
-                         (h16_t*)dqkv, cp, B, Tn, H, C, dr);
-      hipLaunchKernelGGL(flash_bwd_dkdv_kernel<FLASH_DKDV_NS>, dim3(nb * B * H), dim3(256), 0, s,
-                         (const h16_t*)qkv, D, (const h16_t*)dout, (h16_t*)dqkv, cp, B, Tn, H, C,
-                         dr);
+      if (dr.thresh && !dmask) return -5;
+#define FLASH_BWD(DROP)                                                                            \
+  hipLaunchKernelGGL((flash_bwd_dq_kernel<FLASH_DQ_NS, DROP>), dim3(nb * B * H), dim3(256), 0, s, \
+                     (const h16_t*)qkv, (const h16_t*)out, lse, D, (const h16_t*)dout,             \
+                     (h16_t*)dqkv, cp, B, Tn, H, C, dr, dmask);                                    \
+  hipLaunchKernelGGL((flash_bwd_dkdv_kernel<FLASH_DKDV_NS, DROP>), dim3(nb * B * H), dim3(256), 0, \
+                     s, (const h16_t*)qkv, D, (const h16_t*)dout, (h16_t*)dqkv, cp, B, Tn, H, C,   \
+                     dr, dmask);
+      if (dr.thresh) {
+        FLASH_BWD(true)
+      } else {
+        FLASH_BWD(false)
+      }
+#undef FLASH_BWD
       if (cs_out) {
         if (hipGetLastError() != hipSuccess) return -4;
         if (defer) {

@@ -100,6 +100,7 @@ ParamOff param_offsets(const gpt_config& c) {
 struct WsLayer {
   int64_t attnT, aprojT, fcT, mprojT;  // element offsets in the transposed copy
   size_t x_in, ln1_mean, ln1_rstd, ln1, qkv, att, lse, x_mid, ln2_mean, ln2_rstd, ln2, dgelu, g;
+  size_t dmask = 0;  // the flash forward's dropout bits for its backward (16-bit, head width 64)
 };
 struct WsOff {
   size_t shadow = 0;
@@ -166,6 +167,9 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
     L.ln2 = take(M * d * es);
     L.dgelu = take(M * 4 * d * es);  // gelu'(u), kept for the backward
     L.g = take(M * 4 * d * es);
+    // one bit per (query, key) of every head, as 32-bit words per 64-key
+    // block and half: [b*H + h][key block][half][query]
+    if (bf && d / H == 64) L.dmask = take(M * H * round_up(c.block_size, 64) / 64 * 2 * 4);
     w.layer.push_back(L);
   }
   w.x_final = take(M * d * 4);
@@ -399,7 +403,7 @@ static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, i
       CK(kv_store_launch(bf, h->at(L.qkv), (char*)kv + l * kv_layer * h->es(), B, T, H, d / H,
                          max_len, 0, s));
     CK(attention_fwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), B, T, H, d, s,
-                            at_site(dr, 1 + 2 * l)));
+                            at_site(dr, 1 + 2 * l), L.dmask ? h->at<uint32_t>(L.dmask) : nullptr));
     e = GemmEpiArgs();
     e.out = h->at(L.x_mid);
     e.aux = h->at(L.x_in);
@@ -753,7 +757,8 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     // formed by the attention backward
     CK(attention_bwd_launch(bf, h->at(L.qkv), h->at(L.att), h->at<float>(L.lse), h->at(w.dO), dbig,
                             h->at<float>(w.Dbuf), B, T, H, d, cs_slice(), h->G(P.attnb), beta, s,
-                            &(job = ColsumJob()), at_site(dr, 1 + 2 * l)));
+                            &(job = ColsumJob()), at_site(dr, 1 + 2 * l),
+                            L.dmask ? h->at<uint32_t>(L.dmask) : nullptr));
     keep(job);
     // fused q|k|v projection: dW (+)= dqkv^T ln1 ; dln1 = dqkv Wqkv
     e = GemmEpiArgs();

@@ -26,14 +26,17 @@ int transpose_h16_launch(const h16_t* src, h16_t* dst, const TransposeJob* jobs,
                           int total_tiles, hipStream_t s);
 
 // dr: dropout of the attention probabilities (site word without bh; the
-// kernels add b * H + h)
+// kernels add b * H + h).  dmask: the kept bits, written by the forward and
+// read by the backward of the head-width-64 16-bit kernels (required there
+// with dropout: B * H * cdiv(T, 64) * 2 * T 32-bit words)
 int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B, int Tn, int H,
-                         int C, hipStream_t s, Drop dr = Drop());
+                         int C, hipStream_t s, Drop dr = Drop(), uint32_t* dmask = nullptr);
 // defer (optional): see ColsumJob; honoured by the head-width-64 16-bit path
 int attention_bwd_launch(bool h16, const void* qkv, const void* out, const float* lse,
                          const void* dout, void* dqkv, float* D, int B, int Tn, int H, int C,
                          float* cs_part, float* cs_out, int cs_beta, hipStream_t s,
-                         ColsumJob* defer = nullptr, Drop dr = Drop());
+                         ColsumJob* defer = nullptr, Drop dr = Drop(),
+                         const uint32_t* dmask = nullptr);
 
 int layernorm_fwd_launch(bool h16, const float* x, const float* w, const float* b, void* y,
                          float* mean, float* rstd, int M, int C, hipStream_t s);
