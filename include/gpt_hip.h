@@ -111,6 +111,15 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets,
                      int32_t B, int32_t T, float loss_scale, float* loss_out,
                      void* logits_out, void* stream);
 
+/* Evaluation ("nanoGPT", Part IV Stage 2, estimate_loss: the model in eval
+ * mode and no gradient): the mean loss over the targets >= 0 of one batch
+ * into loss_out (device float), with no dropout and no gradient written.
+ * The caller averages such losses over its evaluation batches.  A following
+ * gpt_backward fails with GPT_ESTATE.  Errors as gpt_forward_loss; targets
+ * and loss_out must not be NULL. */
+int gpt_eval_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B,
+                  int32_t T, float* loss_out, void* stream);
+
 /* Backward pass of the last forward (which must have had targets).
  * zero_first != 0: grads = new gradient; else grads += new gradient
  * (accumulation until zero_grad, "nanoGPT" Deep dive 2). */

@@ -463,6 +463,14 @@ def loss_and_grads(flat_params, idx, targets, cfg: Config, loss_scale=1.0,
     return loss, backward(cache, cfg, dtype), logits
 
 
+def estimate_loss(flat_params, batches, cfg: Config, dtype=np.float64) -> float:
+    """The eval gate's loss estimate ([NG] Part IV Stage 2): the model in eval
+    mode (no dropout, no gradient), the mean of the per-batch mean losses over
+    the given batches of one split."""
+    return float(np.mean([forward(flat_params, idx, tgt, cfg, dtype=dtype)[1]
+                          for idx, tgt in batches]))
+
+
 # --------------------------------------------------------------------------
 # the optimizer step
 # --------------------------------------------------------------------------

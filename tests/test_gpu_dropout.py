@@ -141,3 +141,39 @@ def test_dropout_arguments_are_checked():
             m.forward(idx, tgt, dropout=(p, 1, 0))
         assert e.value.code == bd.GPT_EINVAL
     m.close()
+
+
+# ---------------------------------------------------------------- evaluation
+@pytest.mark.parametrize("name,mode,tol", [("tiny", 0, 1e-5), ("char", 1, 2e-2)])
+def test_estimate_loss_matches_oracle(name, mode, tol):
+    """gpt_eval_loss per batch, averaged as the pages' eval gate does, against
+    the oracle's estimate_loss; eval mode ignores a dropout the previous
+    training forward used."""
+    dims = synth.WORKLOADS[name]
+    case(f"{name} mode={mode} estimate_loss over 3 batches")
+    params = synth.init_params(dims, seed=23)
+    batches = [synth.tokens(dims, seed=24 + i, batch=2) for i in range(3)]
+    ref = O.estimate_loss(params, batches, ocfg(dims))
+    m = bd.GPT(dims, mode, max_batch=2, init_params=params)
+    dev = [dev_tokens(*b) for b in batches]
+    m.forward(*dev[0], dropout=(0.25, 3, 1))
+    got = m.estimate_loss(dev)
+    assert abs(got - ref) <= tol, (got, ref)
+    m.close()
+
+
+def test_eval_loss_equals_training_loss_and_leaves_no_gradient_state():
+    """The same kernels up to the gradient write: the eval loss is the
+    training forward's loss bit for bit; backward after it is refused."""
+    dims = synth.WORKLOADS["char"]
+    case("char bf16 eval loss vs training loss B=4")
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=4, init_params=synth.init_params(dims, seed=25))
+    idx, tgt = dev_tokens(*synth.tokens(dims, seed=26, batch=4))
+    train = m.forward(idx, tgt)[0].clone()
+    ev = m.eval_loss(idx, tgt).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(train, ev)
+    with pytest.raises(bd.GptError) as e:
+        m.backward()
+    assert e.value.code == bd.GPT_ESTATE
+    m.close()

@@ -816,3 +816,17 @@ def test_dropout_finite_differences():
                   O.forward(pm, idx, tgt, cfg, dropout=dr)[1]) / (2 * h)
             assert abs(fd - grads[e]) <= 1e-5 * (abs(grads[e]) + 1e-3 * gmax + 1e-12), (name, j)
         off += n
+
+
+def test_estimate_loss_mean_of_batches():
+    """Batches with equal counts of valid targets: the mean of the batch
+    losses is the loss of all of them as one batch (mean of equal-size
+    means); a single batch gives that batch's loss."""
+    w = synth.WORKLOADS["tiny"]
+    cfg = cfg_of(w)
+    params = synth.init_params(w, seed=5).astype(np.float64)
+    batches = [synth.tokens(w, seed=60 + i, batch=2) for i in range(3)]
+    whole = (np.concatenate([b[0] for b in batches]), np.concatenate([b[1] for b in batches]))
+    est = O.estimate_loss(params, batches, cfg)
+    assert abs(est - O.forward(params, *whole, cfg)[1]) < 1e-12
+    assert O.estimate_loss(params, batches[:1], cfg) == O.forward(params, *batches[0], cfg)[1]

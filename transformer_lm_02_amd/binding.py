@@ -52,6 +52,7 @@ _SIGS = {
                        _p],
     "gpt_amp_step": [_p, _f, _f, _f, _f, _f, _f, _p, _f, _f, _i32, _p, _p],
     "gpt_backward": [_p, _i32, _p],
+    "gpt_eval_loss": [_p, _p, _p, _i32, _i32, _p, _p],
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
     "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
     "gpt_op_linear": [_i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
@@ -193,6 +194,25 @@ class GPT:
                                _ptr(self.scaler), growth_factor, backoff_factor, growth_interval,
                                _ptr(norm), _stream()), "gpt_amp_step")
         return norm
+
+    def eval_loss(self, idx, targets):
+        """Mean loss of one batch in eval mode, no gradient (gpt_eval_loss);
+        returns a device tensor [1]."""
+        B, T = idx.shape
+        loss = self.scalars[2:3]
+        check(lib.gpt_eval_loss(self.handle, _ptr(idx), _ptr(targets), B, T, _ptr(loss), _stream()),
+              "gpt_eval_loss")
+        return loss
+
+    def estimate_loss(self, batches):
+        """The pages' estimate_loss over one split: the mean of the eval
+        losses of the batches (read back, as the pages' loop does with
+        loss.item())."""
+        import torch
+        out = torch.empty(len(batches), dtype=torch.float32, device=self.params.device)
+        for k, (idx, tgt) in enumerate(batches):
+            out[k:k + 1].copy_(self.eval_loss(idx, tgt))
+        return float(out.cpu().double().mean())
 
     def backward(self, zero_first=True):
         check(lib.gpt_backward(self.handle, 1 if zero_first else 0, _stream()), "gpt_backward")

@@ -97,6 +97,13 @@ int gpt_forward_loss_ex(gpt_model* h, const int32_t* idx, const int32_t* targets
                                          dropout, loss_out, logits_out, stream);
 }
 
+int gpt_eval_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
+                  float* loss_out, void* stream) {
+  if (!h) return null_handle();
+  return h->fp16 ? f16::gpt_eval_loss((f16::Model*)h->impl, idx, targets, B, T, loss_out, stream)
+                 : b16::gpt_eval_loss((b16::Model*)h->impl, idx, targets, B, T, loss_out, stream);
+}
+
 int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
   if (!h) return null_handle();
   return h->fp16 ? f16::gpt_backward((f16::Model*)h->impl, zero_first, stream)

@@ -479,6 +479,35 @@ int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32
   return GPT_OK;
 }
 
+// Evaluation ([NG] Part IV Stage 2, estimate_loss: the model in eval mode, so
+// no dropout, and no gradient): the mean loss over the valid targets, the
+// logits left unmodified.
+int gpt_eval_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
+                  float* loss_out, void* stream) {
+  if (!h || !idx || !targets || !loss_out) return fail(GPT_EINVAL, "null handle or buffer");
+  const gpt_config& c = h->cfg;
+  if (B < 1 || B > c.max_batch) return fail(GPT_EINVAL, "B outside [1, max_batch]");
+  if (T < 1) return fail(GPT_EINVAL, "T < 1");
+  if (T > c.block_size) return fail(GPT_ESEQLEN, "T > block_size");
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = h->h16();
+  const WsOff& w = h->wo;
+  const ParamOff& p = h->po;
+  const int M = B * T, d = c.n_embd;
+  h->have_fwd = false;
+  CK(forward_stack(h, idx, B, T, nullptr, 1, s));
+  GemmEpiArgs e;
+  e.out = h->at(w.logits);
+  e.ldc = (int)w.vi;
+  CK(gemm_launch(bf, true, true, EPI_ACT, h->at(w.lnf), d, h->W(p.wte), d, M, c.padded_vocab, d,
+                 d, d, e, s));
+  CK(count_valid_launch(targets, M, h->at<int>(w.nvalid), s));
+  CK(cross_entropy_launch(bf, h->at(w.logits), targets, h->at<float>(w.row_loss),
+                          h->at<int>(w.nvalid), 1.f, nullptr, M, c.vocab_size, (int)w.vi, s, 0));
+  CK(loss_finalize_launch(h->at<float>(w.row_loss), M, h->at<int>(w.nvalid), loss_out, s));
+  return GPT_OK;
+}
+
 // ---------------------------------------------------------------- sampling
 int64_t gpt_kv_cache_bytes(const gpt_config* c, int32_t B, int32_t max_len) {
   if (validate(c) != GPT_OK || B < 1 || max_len < 1) return -1;

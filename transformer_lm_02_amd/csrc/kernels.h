@@ -58,10 +58,11 @@ int dropout_rows_launch(const float* x, float* y, int64_t M, int C, Drop dr, hip
 int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int Tn,
                      int block_size, int C, int Vp, int beta_wpe, hipStream_t s);
 int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s);
-// dscale (optional, device): the gradient is further multiplied by *dscale
+// dscale (optional, device): the gradient is further multiplied by *dscale;
+// write_grad = 0: only the row losses (the logits are left as they are)
 int cross_entropy_launch(bool h16, void* logits, const int32_t* tgt, float* row_loss,
                          const int* n_valid, float loss_scale, const float* dscale, int N, int V,
-                         int ldv, hipStream_t s);
+                         int ldv, hipStream_t s, int write_grad = 1);
 int loss_finalize_launch(const float* row_loss, int N, const int* n_valid, float* loss,
                          hipStream_t s);
 int colsum_part_rows(int M);

@@ -141,7 +141,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_h16_kernel(
     h16_t* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
     const int* __restrict__ n_valid, float loss_scale, const float* __restrict__ dscale, int V,
-    int ldv) {
+    int ldv, int write_grad) {
   __shared__ float red[CE_BF_THREADS / 64];
   const int64_t row = blockIdx.x;
   h16_t* z = logits + row * ldv;
@@ -206,6 +206,10 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_h16_kernel(
   const int nv = *n_valid;
   const float scale =
       (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
+  if (!write_grad) {  // the loss alone (evaluation): the logits stay as they are
+    if (threadIdx.x == 0) row_loss[row] = has_y ? lse - zy : 0.f;
+    return;
+  }
   const float c = scale * __expf(mref - lse);
 #pragma unroll
   for (int i = 0; i < CE_BF_MAXU; ++i) {
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_h16_kernel(
 __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
     float* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
     const int* __restrict__ n_valid, float loss_scale, const float* __restrict__ dscale, int V,
-    int ldv) {
+    int ldv, int write_grad) {
   __shared__ float red[CE_THREADS / 64];
   const int64_t row = blockIdx.x;
   float* z = logits + row * ldv;
@@ -244,6 +248,10 @@ __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
   const float scale =
       (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
   const float zy = (y >= 0 && y < V) ? z[y] : 0.f;
+  if (!write_grad) {
+    if (threadIdx.x == 0) row_loss[row] = (y >= 0 && y < V) ? lse - zy : 0.f;
+    return;
+  }
   __syncthreads();
   for (int c = threadIdx.x; c < ldv; c += CE_THREADS)
     z[c] = c < V ? scale * (expf(z[c] - lse) - (c == y ? 1.f : 0.f)) : 0.f;
@@ -359,14 +367,14 @@ int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s) {
 
 int cross_entropy_launch(bool h16, void* logits, const int32_t* tgt, float* row_loss,
                          const int* n_valid, float loss_scale, const float* dscale, int N, int V,
-                         int ldv, hipStream_t s) {
+                         int ldv, hipStream_t s, int write_grad) {
   if (h16) {
     if (ldv % 8 || ldv > CE_BF_MAXU * CE_BF_THREADS * 8) return -5;
     hipLaunchKernelGGL(ce_h16_kernel, dim3(N), dim3(CE_BF_THREADS), 0, s, (h16_t*)logits, tgt,
-                       row_loss, n_valid, loss_scale, dscale, V, ldv);
+                       row_loss, n_valid, loss_scale, dscale, V, ldv, write_grad);
   } else {
     hipLaunchKernelGGL(ce_f32_kernel, dim3(N), dim3(CE_THREADS), 0, s, (float*)logits, tgt,
-                       row_loss, n_valid, loss_scale, dscale, V, ldv);
+                       row_loss, n_valid, loss_scale, dscale, V, ldv, write_grad);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
