@@ -177,3 +177,32 @@ def test_eval_loss_equals_training_loss_and_leaves_no_gradient_state():
         m.backward()
     assert e.value.code == bd.GPT_ESTATE
     m.close()
+
+
+def test_bf16_dropout_per_query_attention_kernels():
+    """Head width 32 in bf16: the per-query attention kernels, which
+    regenerate the masks instead of reading stored bits."""
+    dropout_parity("tiny", 1, 2, 64, 0.25, 808, 4, min_cos=0.995, n_embd=128, n_head=4)
+
+
+def test_dropout_with_gradient_accumulation():
+    """Two micro-batches, each forward with its own step word and loss scale
+    1/2, the second backward accumulating: the sum of the oracle's two
+    dropout gradients ("Let's reproduce GPT-2 (124M)", chapter "Gradient
+    Accumulation"; each backward uses its own forward's masks)."""
+    dims = synth.WORKLOADS["tiny"]
+    case("tiny fp32 dropout accumulation 2 x B=2")
+    params = synth.perturbed_params(dims, seed=27)
+    mbs = [synth.tokens(dims, seed=28 + i, batch=2) for i in range(2)]
+    ref = np.zeros(params.size)
+    for i, (idx, tgt) in enumerate(mbs):
+        _, g, _ = O.loss_and_grads(params, idx, tgt, ocfg(dims), loss_scale=0.5,
+                                   dropout=O.Dropout(0.25, 31, i))
+        ref += g
+    m = bd.GPT(dims, bd.GPT_FP32, max_batch=2, init_params=params)
+    for i, (idx, tgt) in enumerate(mbs):
+        m.forward(*dev_tokens(idx, tgt), loss_scale=0.5, dropout=(0.25, 31, i))
+        m.backward(zero_first=(i == 0))
+    torch.cuda.synchronize()
+    check_grads(dims, to_np(m.grads), ref, max_rel_err=1e-4)
+    m.close()
