@@ -286,7 +286,7 @@ def main():
 
     def step(i):
         idx, tgt = batches[i % nb]
-        lr = min(6e-4 * (i + 1) / 715, 6e-4)
+        lr = bd.lr_at(i)  # warmup 715, cosine to 6e-5 at 19073
         if args.fp16:
             # scale, backward, unscale, clip, step or skip, update
             model.forward(idx, tgt, scaled=True, dropout=drop(i))

@@ -140,6 +140,17 @@ int gpt_adamw_step(gpt_model* h, float lr, float beta1, float beta2, float eps,
                    float weight_decay, float max_norm, int32_t t,
                    int32_t skip_nonfinite, float* norm_out, void* stream);
 
+/* Learning rate at optimizer iteration it ("nanoGPT", Part IV Stage 1,
+ * get_lr; "Karpathy's Let's Reproduce GPT-2 in One Read", Section 3):
+ * it < warmup: max_lr * (it + 1) / warmup (linear warmup);
+ * warmup <= it <= decay_end: min_lr + (max_lr - min_lr) * (1 + cos(pi *
+ * (it - warmup) / (decay_end - warmup))) / 2 (cosine decay);
+ * it > decay_end: min_lr.  Host arithmetic in double, no device involved.
+ * NaN for it < 0, warmup < 0 or decay_end <= warmup.  The pages' values:
+ * max 6e-4, min 6e-5, warmup 715, decay_end 19073 (build-nanogpt) or warmup
+ * 2000, decay_end 600000 (nanoGPT). */
+double gpt_lr_at(int64_t it, double max_lr, double min_lr, int64_t warmup, int64_t decay_end);
+
 /* ---------------------------------------------------------------------------
  * Dynamic loss scaling for float16 training ("nanoGPT", Part IV Stages 4-5,
  * Part V Deep dive 2 and Part VIII checks 6-7; "Let's reproduce GPT-2

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "gpt_hip.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(gpt_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|double|void|const char\*)\s+(gpt_\w+)\s*\(", src,
+                                 flags=re.M)))
 
 
 def test_header_declares_the_step_entry_points():
@@ -136,3 +137,30 @@ def test_dropout_arguments_are_checked_without_a_device():
     assert lib.gpt_op_dropout(buf, buf, 4, 6, 0.5, 1, 0, 0, None) == bd.GPT_EINVAL
     assert lib.gpt_op_dropout(buf, buf, 4, 8, 1.0, 1, 0, 0, None) == bd.GPT_EINVAL
     assert ctypes.sizeof(bd.gpt_dropout) == 16
+
+
+def test_declared_entry_points_include_every_return_type():
+    names = declared_functions()
+    for n in ("gpt_kv_cache_bytes", "gpt_lr_at", "gpt_sample", "gpt_eval_loss"):
+        assert n in names
+
+
+def test_lr_schedule_host_function_matches_pages_and_oracle():
+    """gpt_lr_at (host arithmetic in the library) against the learning rates
+    the pages print ([NG] Part VII Lab 4, tests/golden/page_values.json) and
+    against the oracle's get_lr at many iterations of both schedules."""
+    import json
+    import math
+
+    from oracle import gpt_oracle as O
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "page_values.json")))["lr_schedule_nanogpt"]
+    for it, want in g["points"]:
+        got = bd.lr_at(it, g["max_lr"], g["min_lr"], g["warmup"], g["decay_end"])
+        assert abs(got - want) <= g["rel_tol"] * want + 1e-9, (it, got, want)
+    for W, D in [(715, 19073), (2000, 600000), (1, 2)]:
+        for it in list(range(0, 3 * W)) + [D - 1, D, D + 1, 2 * D] + list(range(W, D, max(1, D // 97))):
+            assert bd.lr_at(it, 6e-4, 6e-5, W, D) == pytest.approx(O.get_lr(it, 6e-4, 6e-5, W, D),
+                                                                     rel=1e-14)
+    assert bd.lr_at(0) == pytest.approx(6e-4 / 715)
+    for bad in [(-1, 6e-4, 6e-5, 715, 19073), (5, 6e-4, 6e-5, 100, 100), (5, 6e-4, 6e-5, -1, 10)]:
+        assert math.isnan(bd.lib.gpt_lr_at(*bad))

@@ -74,6 +74,8 @@ lib.gpt_kv_cache_bytes.argtypes = [ctypes.POINTER(gpt_config), _i32, _i32]
 lib.gpt_kv_cache_bytes.restype = ctypes.c_int64
 lib.gpt_destroy.argtypes = [_p]
 lib.gpt_destroy.restype = None
+lib.gpt_lr_at.argtypes = [_i64, ctypes.c_double, ctypes.c_double, _i64, _i64]
+lib.gpt_lr_at.restype = ctypes.c_double
 lib.gpt_strerror.argtypes = [ctypes.c_int]
 lib.gpt_strerror.restype = ctypes.c_char_p
 
@@ -300,6 +302,13 @@ class GPT:
             self.close()
         except Exception:
             pass
+
+
+def lr_at(it, max_lr=6e-4, min_lr=None, warmup=715, decay_end=19073):
+    """Learning rate at iteration it (gpt_lr_at); min_lr defaults to a tenth
+    of max_lr."""
+    return lib.gpt_lr_at(it, max_lr, 0.1 * max_lr if min_lr is None else min_lr, warmup,
+                         decay_end)
 
 
 def sample(logits, vocab_size, temperature, top_k, u):

@@ -4,6 +4,8 @@
 // share no state; a handle records which one created it.
 #include "api_impl.h"
 
+#include <math.h>
+
 #include <string>
 
 std::string& gpt_error_text() {
@@ -173,6 +175,17 @@ void gpt_destroy(gpt_model* h) {
   else
     b16::gpt_destroy((b16::Model*)h->impl);
   delete h;
+}
+
+// Learning rate at iteration it: linear warmup to max_lr, cosine decay to
+// min_lr at decay_end, min_lr afterwards ("nanoGPT", Part IV Stage 1, get_lr)
+double gpt_lr_at(int64_t it, double max_lr, double min_lr, int64_t warmup, int64_t decay_end) {
+  if (it < 0 || warmup < 0 || decay_end <= warmup) return NAN;
+  if (it < warmup) return max_lr * (double)(it + 1) / (double)warmup;
+  if (it > decay_end) return min_lr;
+  const double ratio = (double)(it - warmup) / (double)(decay_end - warmup);
+  const double coeff = 0.5 * (1.0 + cos(M_PI * ratio));  // 1 at warmup, 0 at decay_end
+  return min_lr + coeff * (max_lr - min_lr);
 }
 
 const char* gpt_strerror(int code) {
