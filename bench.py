@@ -8,13 +8,16 @@ GPT-2 vocabulary, N(0, 0.02) weights with 0.02/sqrt(24) residual
 projections, all resident in HBM before the timed region.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--fp16]
-                    [--dropout P]
+                    [--dropout P] [--accum K]
 
 Prints one JSON line.  --fp16 times the same step in IEEE half precision
 with dynamic loss scaling (scaled forward, backward, then unscale, clip,
 AdamW or skip and scale update on the device).  --dropout P times it with
 dropout P at the embedding sum, the attention probabilities and the MLP output
-(a fresh Philox counter word per step).
+(a fresh Philox counter word per step).  --accum K makes a step one optimizer
+iteration over K accumulated micro-batches (loss scaled by 1/K, the first
+backward replacing the gradients, the others adding; K = 32 is the pages'
+524,288-token batch), then clipping and AdamW.
 """
 from __future__ import annotations
 
@@ -246,6 +249,8 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="instead of training, time sampling with the KV cache for B sequences")
+    ap.add_argument("--accum", type=int, default=1, metavar="K",
+                    help="micro-batches accumulated per optimizer step")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="train with dropout P (the pretraining configuration uses 0)")
     ap.add_argument("--fp16", action="store_true",
@@ -284,17 +289,21 @@ def main():
 
     drop = (lambda i: (args.dropout, 1337, i)) if args.dropout > 0 else (lambda i: None)
 
+    K = max(1, args.accum)
+
     def step(i):
-        idx, tgt = batches[i % nb]
         lr = bd.lr_at(i)  # warmup 715, cosine to 6e-5 at 19073
+        for k in range(K):
+            idx, tgt = batches[(i * K + k) % nb]
+            if args.fp16:
+                # scale, backward; after the micro-steps unscale, clip, step or skip, update
+                model.forward(idx, tgt, loss_scale=1.0 / K, scaled=True, dropout=drop(i * K + k))
+            else:
+                model.forward(idx, tgt, loss_scale=1.0 / K, dropout=drop(i * K + k))
+            model.backward(zero_first=(k == 0))
         if args.fp16:
-            # scale, backward, unscale, clip, step or skip, update
-            model.forward(idx, tgt, scaled=True, dropout=drop(i))
-            model.backward(zero_first=True)
             model.amp_step(lr=lr, max_norm=1.0)
         else:
-            model.forward(idx, tgt, dropout=drop(i))
-            model.backward(zero_first=True)
             model.adamw_step(lr=lr, t=i + 1, max_norm=1.0)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -319,7 +328,7 @@ def main():
     pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     loss = float(model.scalars[0].item())
     norm = float(model.scalars[1].item())
-    tokens = B * T
+    tokens = B * T * K
     value = tokens / (ms * 1e-3)
     fpt = flops_per_token(dims, T)
     mfu = fpt * tokens / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
@@ -339,19 +348,22 @@ def main():
     prec = "fp16 (dynamic loss scaling)" if args.fp16 else "bf16"
     if args.dropout > 0:
         prec += f" dropout {args.dropout:g}"
+    shape = f"B=16 T=1024 x {K} micro-batches" if K > 1 else "B=16 T=1024"
     out = {
-        "metric": f"train tokens/sec + ms/step + MFU, GPT-2 124M {prec} B=16 T=1024, 1 MI355X",
+        "metric": f"train tokens/sec + ms/step + MFU, GPT-2 124M {prec} {shape}, 1 MI355X",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "ms_per_step_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "mfu": round(mfu, 4),
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None if (args.fp16 or args.dropout > 0) else round(value / A100_TOKENS_PER_S, 3),
+        "vs_baseline": None if (args.fp16 or args.dropout > 0 or K > 1) else round(value / A100_TOKENS_PER_S, 3),
         "baseline": "pages' 90 ms/step = ~182,000 tokens/s on one A100 SXM (context)",
         "dtype": "fp16" if args.fp16 else "bf16",
         "data": "synthetic (Zipf(1.1) token ids; random-init weights)",
         "config": {"workload": "GPT-2 124M training step (fwd+bwd+clip+AdamW), vocab 50304 "
-                               "(pad masked), B=16, T=1024", "global_batch": B, "seq_len": T,
+                               "(pad masked), B=16, T=1024"
+                               + (f", {K} micro-batches per optimizer step" if K > 1 else ""),
+                   "global_batch": B * K, "seq_len": T,
                    "flops_per_step": fpt * tokens, "loss": round(loss, 4), "grad_norm": round(norm, 4)},
         **({"loss_scaler": dict(zip(("scale", "growth_tracker", "updates", "last_skipped"), scaler)),
             "optimizer_steps_run": args.warmup + args.steps} if scaler else {}),
