@@ -8,7 +8,7 @@ GPT-2 vocabulary, N(0, 0.02) weights with 0.02/sqrt(24) residual
 projections, all resident in HBM before the timed region.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--fp16]
-                    [--dropout P] [--accum K]
+                    [--dropout P] [--accum K] [--workload gpt2|char|gpt2_1p5b]
 
 Prints one JSON line.  --fp16 times the same step in IEEE half precision
 with dynamic loss scaling (scaled forward, backward, then unscale, clip,
@@ -17,7 +17,10 @@ dropout P at the embedding sum, the attention probabilities and the MLP output
 (a fresh Philox counter word per step).  --accum K makes a step one optimizer
 iteration over K accumulated micro-batches (loss scaled by 1/K, the first
 backward replacing the gradients, the others adding; K = 32 is the pages'
-524,288-token batch), then clipping and AdamW.
+524,288-token batch), then clipping and AdamW.  --workload times another model
+of the pages at its own batch: the character-level model (vocab 65, T 256, 6
+layers of width 384, B 64; the pages train it with dropout 0.2) or the 1.5B
+shape (width 1600, 48 layers, B 8).
 """
 from __future__ import annotations
 
@@ -249,6 +252,8 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="instead of training, time sampling with the KV cache for B sequences")
+    ap.add_argument("--workload", default=WORKLOAD, choices=["gpt2", "char", "gpt2_1p5b"],
+                    help="model and batch (default: GPT-2 124M, B=16, T=1024)")
     ap.add_argument("--accum", type=int, default=1, metavar="K",
                     help="micro-batches accumulated per optimizer step")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
@@ -268,15 +273,16 @@ def main():
     from transformer_lm_02_amd import binding as bd
     from transformer_lm_02_amd import synth
 
-    dims = synth.WORKLOADS[WORKLOAD]
+    dims = synth.WORKLOADS[args.workload]
     B, T = dims["batch"], dims["block_size"]
+    headline = args.workload == WORKLOAD
     if args.decode:
         decode_bench(torch, bd, synth, synth.model_dims(dims), args.decode, 64, 448)
         return
     if args.probe:
         probe(torch, bd, B, T, dims)
         return
-    print(f"[bench] building model {WORKLOAD} B={B} T={T}", file=sys.stderr, flush=True)
+    print(f"[bench] building model {args.workload} B={B} T={T}", file=sys.stderr, flush=True)
     params = synth.init_params(dims, seed=1337)
     model = bd.GPT(dims, bd.GPT_FP16 if args.fp16 else bd.GPT_BF16, max_batch=B,
                    init_params=params)
@@ -336,32 +342,36 @@ def main():
           f"norm {norm:.4f}, MFU {mfu:.4f}", file=sys.stderr, flush=True)
     scaler = model.scaler_state() if args.fp16 else None
     roof = None
-    if not args.no_kernel_timing:
+    if not args.no_kernel_timing and headline:
         roof = time_dominant_kernel(torch, bd, B, T, dims, fp16=args.fp16)
     model.close()
     del model
     torch.cuda.empty_cache()
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and headline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(dims)
     prec = "fp16 (dynamic loss scaling)" if args.fp16 else "bf16"
     if args.dropout > 0:
         prec += f" dropout {args.dropout:g}"
-    shape = f"B=16 T=1024 x {K} micro-batches" if K > 1 else "B=16 T=1024"
+    model_name = {"gpt2": "GPT-2 124M", "char": "character-level GPT (6x384)",
+                  "gpt2_1p5b": "GPT-2 1.5B shape"}[args.workload]
+    shape = f"B={B} T={T}" + (f" x {K} micro-batches" if K > 1 else "")
     out = {
-        "metric": f"train tokens/sec + ms/step + MFU, GPT-2 124M {prec} {shape}, 1 MI355X",
+        "metric": f"train tokens/sec + ms/step + MFU, {model_name} {prec} {shape}, 1 MI355X",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "ms_per_step_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "mfu": round(mfu, 4),
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None if (args.fp16 or args.dropout > 0 or K > 1) else round(value / A100_TOKENS_PER_S, 3),
+        "vs_baseline": None if (args.fp16 or args.dropout > 0 or K > 1 or not headline)
+        else round(value / A100_TOKENS_PER_S, 3),
         "baseline": "pages' 90 ms/step = ~182,000 tokens/s on one A100 SXM (context)",
         "dtype": "fp16" if args.fp16 else "bf16",
-        "data": "synthetic (Zipf(1.1) token ids; random-init weights)",
-        "config": {"workload": "GPT-2 124M training step (fwd+bwd+clip+AdamW), vocab 50304 "
-                               "(pad masked), B=16, T=1024"
+        "data": ("synthetic (Zipf(1.1) token ids; random-init weights)" if dims["tokens"] == "zipf"
+                 else "synthetic (uniform token ids; random-init weights)"),
+        "config": {"workload": f"{model_name} training step (fwd+bwd+clip+AdamW), vocab "
+                               f"{dims['padded_vocab']} (pad masked), B={B}, T={T}"
                                + (f", {K} micro-batches per optimizer step" if K > 1 else ""),
                    "global_batch": B * K, "seq_len": T,
                    "flops_per_step": fpt * tokens, "loss": round(loss, 4), "grad_norm": round(norm, 4)},

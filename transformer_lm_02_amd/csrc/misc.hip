@@ -228,6 +228,54 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_h16_kernel(
   if (threadIdx.x == 0) row_loss[row] = has_y ? lse - zy : 0.f;
 }
 
+// Rows of at most 512 columns (the character-level vocabulary): one wave per
+// row, four rows per workgroup, each lane holding 8 consecutive columns in
+// registers; the same loss and gradient as above, the gradient formed
+// directly as scale * (exp(z - lse) - [v == y]).
+#define CE_SMALL_MAXV 512
+__global__ __launch_bounds__(256) void ce_h16_small_kernel(
+    h16_t* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
+    const int* __restrict__ n_valid, float loss_scale, const float* __restrict__ dscale, int N,
+    int V, int ldv, int write_grad) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;  // uniform per wave
+  h16_t* z = logits + row * ldv;
+  const int y = tgt[row];
+  const bool has_y = y >= 0 && y < V;
+  const int c0 = 8 * lane;
+  const bool mine = c0 < ldv;
+  const uint4 raw = mine ? *(const uint4*)(z + c0) : make_uint4(0, 0, 0, 0);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+  float m = -INFINITY, zyl = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float x = (j & 1) ? h_hi(w[j >> 1]) : h_lo(w[j >> 1]);
+    v[j] = (c0 + j < V) ? x : -INFINITY;  // padding and lanes past the row: excluded
+    m = fmax_fast(m, v[j]);
+    zyl = (c0 + j == y) ? x : zyl;
+  }
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += __expf(v[j] - m);
+  s = wave_sum(s);
+  const float lse = m + __logf(s);
+  const float zy = wave_sum(zyl);  // one lane holds z_y, the others add zero
+  if (lane == 0) row_loss[row] = has_y ? lse - zy : 0.f;
+  if (!write_grad || !mine) return;
+  const int nv = *n_valid;
+  const float scale =
+      (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
+  float d[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    d[j] = (c0 + j < V) ? scale * (__expf(v[j] - lse) - (c0 + j == y ? 1.f : 0.f)) : 0.f;
+  *(uint4*)(z + c0) =
+      make_uint4(pack2h(d[0], d[1]), pack2h(d[2], d[3]), pack2h(d[4], d[5]), pack2h(d[6], d[7]));
+}
+
 // fp32 logits (fp32 mode): the same, reading the row from memory per pass.
 __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
     float* __restrict__ logits, const int32_t* __restrict__ tgt, float* __restrict__ row_loss,
@@ -368,7 +416,10 @@ int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s) {
 int cross_entropy_launch(bool h16, void* logits, const int32_t* tgt, float* row_loss,
                          const int* n_valid, float loss_scale, const float* dscale, int N, int V,
                          int ldv, hipStream_t s, int write_grad) {
-  if (h16) {
+  if (h16 && ldv % 8 == 0 && ldv <= CE_SMALL_MAXV) {
+    hipLaunchKernelGGL(ce_h16_small_kernel, dim3(cdiv(N, 4)), dim3(256), 0, s, (h16_t*)logits,
+                       tgt, row_loss, n_valid, loss_scale, dscale, N, V, ldv, write_grad);
+  } else if (h16) {
     if (ldv % 8 || ldv > CE_BF_MAXU * CE_BF_THREADS * 8) return -5;
     hipLaunchKernelGGL(ce_h16_kernel, dim3(N), dim3(CE_BF_THREADS), 0, s, (h16_t*)logits, tgt,
                        row_loss, n_valid, loss_scale, dscale, V, ldv, write_grad);
