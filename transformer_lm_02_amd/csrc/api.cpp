@@ -53,17 +53,20 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
     return GPT_EINVAL;
   }
   *out = nullptr;
-  gpt_model* h = new gpt_model{cfg && cfg->mode == GPT_FP16, nullptr};
-  const int rc =
-      h->fp16 ? f16::gpt_init((f16::Model**)&h->impl, cfg, params, grads, adam_m, adam_v,
-                              workspace, init_params, stream)
-              : b16::gpt_init((b16::Model**)&h->impl, cfg, params, grads, adam_m, adam_v,
-                              workspace, init_params, stream);
-  if (rc != GPT_OK) {
-    delete h;
-    return rc;
+  const bool fp16 = cfg && cfg->mode == GPT_FP16;
+  void* impl = nullptr;
+  int rc;
+  if (fp16) {
+    f16::Model* m = nullptr;
+    rc = f16::gpt_init(&m, cfg, params, grads, adam_m, adam_v, workspace, init_params, stream);
+    impl = m;
+  } else {
+    b16::Model* m = nullptr;
+    rc = b16::gpt_init(&m, cfg, params, grads, adam_m, adam_v, workspace, init_params, stream);
+    impl = m;
   }
-  *out = h;
+  if (rc != GPT_OK) return rc;  // the build's own init released what it made
+  *out = new gpt_model{fp16, impl};
   return GPT_OK;
 }
 
