@@ -249,7 +249,9 @@ int gpt_forward_loss_ex(gpt_model* h, const int32_t* idx, const int32_t* targets
 
 /* Bytes of a cache for B sequences of up to max_len positions:
  * kv[layer][k|v][b][head][t][head_width] in the mode's activation type
- * (bf16 in GPT_BF16 mode, binary16 in GPT_FP16 mode, fp32 in GPT_FP32 mode).  -1 for an invalid config
+ * (bf16 in GPT_BF16 mode, binary16 in GPT_FP16 mode, fp32 in GPT_FP32 mode),
+ * followed by 64 x head_width elements of slack that a decode step may read
+ * (whole chunks of 64 positions) but never uses.  -1 for an invalid config
  * or size.  The caller allocates it on the device and owns it. */
 int64_t gpt_kv_cache_bytes(const gpt_config* cfg, int32_t B, int32_t max_len);
 
@@ -275,7 +277,8 @@ int gpt_decode_step(gpt_model* h, const int32_t* tok, int32_t B, int32_t pos, vo
  * largest z are removed (ids equal to it stay); p = softmax(z); the token is
  * the first id whose cumulative p exceeds u[b] (device fp32 [B], uniforms in
  * [0, 1) that the caller draws).  tok_out: device int32 [B].
- * Errors: GPT_EINVAL (null pointer, B < 1, ldv < V, temperature <= 0). */
+ * Errors: GPT_EINVAL (null pointer, B < 1, ldv < V, temperature <= 0),
+ * GPT_EUNSUPPORTED (V above 57344). */
 int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float temperature,
                int32_t top_k, const float* u, int32_t* tok_out, void* stream);
 

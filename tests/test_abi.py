@@ -164,3 +164,18 @@ def test_lr_schedule_host_function_matches_pages_and_oracle():
     assert bd.lr_at(0) == pytest.approx(6e-4 / 715)
     for bad in [(-1, 6e-4, 6e-5, 715, 19073), (5, 6e-4, 6e-5, 100, 100), (5, 6e-4, 6e-5, -1, 10)]:
         assert math.isnan(bd.lib.gpt_lr_at(*bad))
+
+
+def test_kv_cache_bytes_layout_plus_slack():
+    """kv[layer][k|v][b][head][t][head_width] in the mode's activation type,
+    then 64 positions of one head of slack for the decode step's whole-chunk
+    reads."""
+    for name, mode, es in (("gpt2", bd.GPT_BF16, 2), ("char", bd.GPT_FP32, 4), ("gpt2", bd.GPT_FP16, 2)):
+        c = dims_cfg(name, mode)
+        d = synth.WORKLOADS[name]
+        hs = d["n_embd"] // d["n_head"]
+        for B, L in ((1, 1), (3, 100), (2, d["block_size"])):
+            want = (d["n_layer"] * 2 * B * d["n_embd"] * L + 64 * hs) * es
+            assert bd.lib.gpt_kv_cache_bytes(ctypes.byref(c), B, L) == want
+        assert bd.lib.gpt_kv_cache_bytes(ctypes.byref(c), 0, 8) == -1
+        assert bd.lib.gpt_kv_cache_bytes(ctypes.byref(c), 1, 0) == -1

@@ -91,8 +91,11 @@ def test_decode_agrees_with_prefill_and_with_forward_bf16():
     m.close()
 
 
-@pytest.mark.parametrize("temp,k", [(0.8, 200), (1.3, 5), (0.8, 1), (1.0, 0), (0.8, 50257)])
+@pytest.mark.parametrize("temp,k", [(0.8, 200), (1.3, 5), (0.8, 1), (1.0, 0), (0.8, 50257),
+                                    (0.8, 960), (0.8, 961), (1.0, 3000)])
 def test_sample_kernel_matches_oracle(temp, k):
+    """Rows 0 and 1 draw the first and the last kept id, so a cutoff that
+    keeps one id too many or too few shows."""
     case(f"sample temperature={temp} top_k={k}")
     V, ldv, B = 50257, 50304, 8
     rng = np.random.default_rng(21 + k)
@@ -212,4 +215,31 @@ def test_gpt2_decode_logits_match_oracle():
         assert rel_err(g[:, :V], ref[:, -1, :V]) <= 3e-2, i
         assert np.argmax(g[0, :V]) == np.argmax(ref[0, -1, :V]) or \
             np.sort(ref[0, -1, :V])[-1] - np.sort(ref[0, -1, :V])[-2] < 0.05
+    m.close()
+
+
+def test_bf16_decode_past_one_chunk_per_wave():
+    """Cache lengths 1024..1026 and 1100: the decode attention's waves take
+    chunks of 64 positions in turn, so these lengths give every wave one whole
+    chunk, then a second (partial) chunk to the first waves."""
+    dims = dict(vocab_size=300, padded_vocab=320, block_size=1200, n_layer=1, n_head=2, n_embd=128)
+    case("bf16 decode at cache lengths 1024..1026 and 1100, B=2")
+    params = synth.perturbed_params(dims, seed=43)
+    B, T0 = 2, 1023
+    seq = np.random.default_rng(44).integers(0, dims["vocab_size"], size=(B, 1100)).astype(np.int32)
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=B, init_params=params)
+    kv, L = m.kv_cache(B, dims["block_size"])
+    m.prefill(dev(seq[:, :T0]), kv, L)
+    got = {}
+    for pos in range(T0, T0 + 3):
+        got[pos + 1] = to_np(m.decode_step(dev(seq[:, pos]), pos, kv, L))
+    m.prefill(dev(seq[:, :1099]), kv, L)
+    got[1100] = to_np(m.decode_step(dev(seq[:, 1099]), 1099, kv, L))
+    torch.cuda.synchronize()
+    V = dims["vocab_size"]
+    for n, g in got.items():
+        ref, _, _ = O.forward(params, seq[:, :n], None, ocfg(dims))
+        r = ref[:, -1, :V]
+        assert rel_err(g[:, :V], r) <= 3e-2, (n, rel_err(g[:, :V], r))
+        assert max_rel(g[:, :V], r) <= 9e-2, (n, max_rel(g[:, :V], r))
     m.close()

@@ -512,7 +512,9 @@ int gpt_eval_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t 
 int64_t gpt_kv_cache_bytes(const gpt_config* c, int32_t B, int32_t max_len) {
   if (validate(c) != GPT_OK || B < 1 || max_len < 1) return -1;
   const int64_t es = c->mode != GPT_FP32 ? 2 : 4;
-  return (int64_t)c->n_layer * 2 * B * c->n_embd * (int64_t)max_len * es;
+  // + 64 rows of one head: the decode attention reads whole chunks of 64
+  // value rows, past the last sequence's len up to 63 rows beyond the end
+  return ((int64_t)c->n_layer * 2 * B * c->n_embd * max_len + 64ll * (c->n_embd / c->n_head)) * es;
 }
 
 static int check_decode_args(Model* h, int B, int max_len, const void* kv, const float* logits_out) {
