@@ -45,10 +45,10 @@ Readings taken where the pages are silent (each repeated where it is used):
     MLP output (not after the attention's output projection, which neither
     page names); masks from Philox4x32-10 keyed by a seed, with the counter
     layout of dropout_mult; a kept value is multiplied by 1/(1-p).
-    Parity unpinned: the two 32-bit Philox multipliers (PHILOX_M32) are the
-    published paper's and no installed library computes the 32-bit variant;
-    the round structure and key schedule are pinned through numpy's 64-bit
-    Philox, the key increments through their definitions.
+    The generator is pinned to the known-answer vectors published with its
+    definition (multipliers, key schedule and rounds at 32 bits), its round
+    structure also through numpy's 64-bit Philox, and the key increments
+    through their definitions.
   * Dynamic loss scaling (float16): initial scale 2^16, growth factor 2
     after 2000 consecutive clean steps, backoff factor 0.5 on a step with an
     inf or NaN gradient (the defaults of the GradScaler the pages construct;

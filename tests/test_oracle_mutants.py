@@ -264,6 +264,13 @@ def _philox_hi_lo_swapped(counter, key, width=32, mults=O.PHILOX_M32, weyl=O.PHI
     return [w[1], w[0], w[3], w[2]]
 
 
+def _philox32_multipliers_swapped(counter, key, width=32, mults=O.PHILOX_M32, weyl=O.PHILOX_W32,
+                                  rounds=10):
+    if width == 32:  # the 64-bit variant (checked against numpy) is left alone
+        mults = (mults[1], mults[0])
+    return _orig_philox(counter, key, width, mults, weyl, rounds)
+
+
 _orig_attn_fwd, _orig_attn_bwd = O.causal_attention_fwd, O.causal_attention_bwd
 _orig_dmult, _orig_philox = O.dropout_mult, O.philox
 
@@ -299,6 +306,7 @@ MUTANTS = [
     ("dropout_mult", _dropout_unscaled),
     ("philox", _philox_bump_first),
     ("philox", _philox_hi_lo_swapped),
+    ("philox", _philox32_multipliers_swapped),
 ]
 
 # the pins that should catch mistakes in the model and optimizer
@@ -323,6 +331,7 @@ PIN_TESTS = [
     lambda: pins.test_amp_skipped_step_changes_nothing_and_keeps_the_step_count(),
     lambda: pins.test_train_step_amp_equals_unscaled_step(),
     lambda: pins.test_philox_round_structure_matches_numpy(),
+    lambda: pins.test_philox32_known_answer_vectors(),
     lambda: pins.test_dropout_masks_keep_one_minus_p_and_are_independent(),
     lambda: pins.test_dropout_model_matches_pytorch_autograd(),
     lambda: pins.test_dropout_finite_differences(),

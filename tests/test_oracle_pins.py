@@ -715,6 +715,19 @@ def test_philox_round_structure_matches_numpy():
             assert got == raw[4 * blk:4 * blk + 4], (key, ctr, blk)
 
 
+def test_philox32_known_answer_vectors():
+    """The 32-bit generator itself, multipliers included, against the
+    known-answer vectors published with its definition (the file cites
+    where they come from): three 128-bit outputs, all zeros, all ones and
+    the digits of pi as input."""
+    kat = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")))
+    for v in kat["vectors"]:
+        c = [int(x, 16) for x in v["counter"]]
+        k = [int(x, 16) for x in v["key"]]
+        got = [int(w) for w in O.philox(c, k)]
+        assert got == [int(x, 16) for x in v["out"]], (v, [hex(w) for w in got])
+
+
 def test_philox_key_increments_from_their_definitions():
     """The Weyl increments are the fractional parts of the golden ratio and
     of sqrt(3) in fixed point, at 32 and 64 bits."""
