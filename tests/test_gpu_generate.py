@@ -243,3 +243,28 @@ def test_bf16_decode_past_one_chunk_per_wave():
         assert rel_err(g[:, :V], r) <= 3e-2, (n, rel_err(g[:, :V], r))
         assert max_rel(g[:, :V], r) <= 9e-2, (n, max_rel(g[:, :V], r))
     m.close()
+
+
+def test_bf16_decode_at_gpt2_xl_width_three_sequences():
+    """One layer at GPT-2 1.5B width (n_embd 1600, 25 heads): the few-row
+    products' LayerNorm rows of K = 1600 and the MLP projection's K = 6400
+    run past the chunks of K requested up front (the last one partial), over
+    3 sequences."""
+    dims = dict(vocab_size=300, padded_vocab=320, block_size=16, n_layer=1, n_head=25, n_embd=1600)
+    case("bf16 decode n_embd=1600 B=3 T0=4 +4")
+    params = synth.perturbed_params(dims, seed=45)
+    B, T0, n = 3, 4, 4
+    seq = np.random.default_rng(46).integers(0, dims["vocab_size"], size=(B, T0 + n)).astype(np.int32)
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=B, init_params=params)
+    kv, L = m.kv_cache(B, dims["block_size"])
+    got = [to_np(m.prefill(dev(seq[:, :T0]), kv, L))]
+    for i in range(n):
+        got.append(to_np(m.decode_step(dev(seq[:, T0 + i]), T0 + i, kv, L)))
+    torch.cuda.synchronize()
+    V = dims["vocab_size"]
+    for i, g in enumerate(got):
+        ref, _, _ = O.forward(params, seq[:, :T0 + i], None, ocfg(dims))
+        r = ref[:, -1, :V]
+        assert rel_err(g[:, :V], r) <= 3e-2, (i, rel_err(g[:, :V], r))
+        assert max_rel(g[:, :V], r) <= 9e-2, (i, max_rel(g[:, :V], r))
+    m.close()
