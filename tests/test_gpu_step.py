@@ -111,6 +111,29 @@ def test_tiny_fp32_full_step_parity():
     m.close()
 
 
+@pytest.mark.parametrize("pattern", ["one_id", "two_ids", "cycle"])
+def test_tiny_fp32_embedding_gradient_repeated_ids(pattern):
+    """The embedding backward adds the rows of each id inside a workgroup of
+    256 rows (runs of at most 16 rows per wave) before its atomic adds:
+    three workgroups of one repeated id, of two alternating ids, and of ids
+    cycling through the vocabulary, against the oracle's gradients at 1e-4."""
+    dims = synth.WORKLOADS["tiny"]
+    B, T, V = 12, dims["block_size"], dims["vocab_size"]
+    case(f"tiny fp32 embedding gradient tokens={pattern} B={B} T={T}")
+    params = synth.perturbed_params(dims, seed=51)
+    n = np.arange(B * T).reshape(B, T)
+    idx = {"one_id": np.full((B, T), 7), "two_ids": 3 + 50 * (n % 2), "cycle": n % V}[pattern]
+    idx = idx.astype(np.int32)
+    tgt = np.random.default_rng(52).integers(0, V, size=(B, T)).astype(np.int32)
+    _, ref_g, _ = O.loss_and_grads(params, idx, tgt, ocfg(dims))
+    m = bd.GPT(dims, bd.GPT_FP32, max_batch=B, init_params=params)
+    m.forward(*dev_tokens(idx, tgt))
+    m.backward(zero_first=True)
+    torch.cuda.synchronize()
+    check_grads(dims, to_np(m.grads), ref_g, max_rel_err=1e-4)
+    m.close()
+
+
 def test_tiny_fp32_gradient_accumulation():
     dims = synth.WORKLOADS["tiny"]
     case("tiny fp32 accumulation 4 x B=1")

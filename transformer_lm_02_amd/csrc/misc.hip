@@ -51,8 +51,9 @@ __global__ void dropout_rows_kernel(const float* x, float* y, int64_t M, int C, 
 
 // dwte[idx[m]] += dx[m], rows of one id added inside the workgroup first.
 // A workgroup takes EMB_ROWS consecutive rows and sorts (id, row) in LDS
-// (bitonic), so that equal ids form runs; a wave sums a run's rows in row
-// order and makes one fp32 atomic add per column.  A frequent id (Zipf-like
+// (bitonic), so that equal ids form runs (cut every EMB_SUB sorted
+// positions); a wave sums a run's rows in row order and makes one fp32
+// atomic add per column.  A frequent id (Zipf-like
 // text puts ~10 % of the tokens on one id) then costs one atomic per
 // workgroup per column instead of one per row, which the memory side would
 // serialise.  Runs of different workgroups still add in the order the
@@ -60,6 +61,7 @@ __global__ void dropout_rows_kernel(const float* x, float* y, int64_t M, int C, 
 #define EMB_ROWS 256
 #define EMB_THREADS 1024  // 16 waves share a workgroup's runs (each run costs a load latency)
 #define EMB_CPL 12        // columns a lane holds: C <= 64 * EMB_CPL
+#define EMB_SUB 16        // longest run a wave sums
 __global__ __launch_bounds__(EMB_THREADS) void embed_bwd_wte_runs_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ dx, float* __restrict__ dwte, int M,
     int C, int Vp) {
@@ -90,9 +92,13 @@ __global__ __launch_bounds__(EMB_THREADS) void embed_bwd_wte_runs_kernel(
       }
       __syncthreads();
     }
+  // a run also restarts at every EMB_SUB-th sorted position, so that no wave
+  // sums more than EMB_SUB rows one after another (a batch of one repeated
+  // id would otherwise put all EMB_ROWS rows on one wave)
   if (tid < EMB_ROWS) {
     const uint32_t my = (uint32_t)(key[tid] >> 32);
-    if (my != 0xffffffffu && (tid == 0 || (uint32_t)(key[tid - 1] >> 32) != my))
+    if (my != 0xffffffffu &&
+        (tid % EMB_SUB == 0 || (uint32_t)(key[tid - 1] >> 32) != my))
       runs[atomicAdd(&nruns, 1)] = tid;
   }
   __syncthreads();
@@ -103,7 +109,8 @@ __global__ __launch_bounds__(EMB_THREADS) void embed_bwd_wte_runs_kernel(
     float acc[EMB_CPL];
 #pragma unroll
     for (int i = 0; i < EMB_CPL; ++i) acc[i] = 0.f;
-    for (int p = p0; p < EMB_ROWS && (uint32_t)(key[p] >> 32) == rid; ++p) {
+    for (int p = p0; p < EMB_ROWS && (uint32_t)(key[p] >> 32) == rid && (p == p0 || p % EMB_SUB);
+         ++p) {
       const float* src = dx + (r0 + (int)(key[p] & 0xffffffffu)) * C;
       // every column of the row requested before any is added
       float v[EMB_CPL];
