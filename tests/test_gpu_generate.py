@@ -219,22 +219,27 @@ def test_gpt2_decode_logits_match_oracle():
 
 
 def test_bf16_decode_past_one_chunk_per_wave():
-    """Cache lengths 1024..1026 and 1100: the decode attention's waves take
-    chunks of 64 positions in turn, so these lengths give every wave one whole
-    chunk, then a second (partial) chunk to the first waves."""
+    """The decode attention's 8 waves take chunks of 64 positions in turn.
+    Cache lengths 64 and 65 (one whole chunk; a second chunk holding one
+    row), 512 and 513 (every wave one whole chunk; a second round of one
+    row), 1024..1026 and 1100 (two rounds, the last partial)."""
     dims = dict(vocab_size=300, padded_vocab=320, block_size=1200, n_layer=1, n_head=2, n_embd=128)
-    case("bf16 decode at cache lengths 1024..1026 and 1100, B=2")
+    case("bf16 decode at cache lengths 64..1100 over a NaN-filled cache, B=2")
     params = synth.perturbed_params(dims, seed=43)
     B, T0 = 2, 1023
     seq = np.random.default_rng(44).integers(0, dims["vocab_size"], size=(B, 1100)).astype(np.int32)
     m = bd.GPT(dims, bd.GPT_BF16, max_batch=B, init_params=params)
     kv, L = m.kv_cache(B, dims["block_size"])
+    # every byte 0xff: each position not yet written (and the slack) holds
+    # bf16 NaNs, which would reach the logits if a row past len were used
+    kv.fill_(255)
     m.prefill(dev(seq[:, :T0]), kv, L)
     got = {}
     for pos in range(T0, T0 + 3):
         got[pos + 1] = to_np(m.decode_step(dev(seq[:, pos]), pos, kv, L))
-    m.prefill(dev(seq[:, :1099]), kv, L)
-    got[1100] = to_np(m.decode_step(dev(seq[:, 1099]), 1099, kv, L))
+    for n in (64, 65, 512, 513, 1100):
+        m.prefill(dev(seq[:, :n - 1]), kv, L)
+        got[n] = to_np(m.decode_step(dev(seq[:, n - 1]), n - 1, kv, L))
     torch.cuda.synchronize()
     V = dims["vocab_size"]
     for n, g in got.items():
