@@ -534,7 +534,8 @@ __global__ __launch_bounds__(SAMP_THREADS) void sample_kernel(const float* __res
   __shared__ uint32_t cscan[SAMP_THREADS];
   __shared__ float fred[SAMP_THREADS / 64];
   __shared__ float fsum[SAMP_THREADS / 64];  // apart from fred: no barrier between their uses
-  __shared__ uint32_t sel[2];  // [0]: key prefix found so far, [1]: rank still to find
+  __shared__ uint32_t sel[3];  // [0]: key prefix found so far, [1]: rank still to find,
+                               // [2]: 1 once the prefix's bin holds exactly that rank
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* z = logits + (int64_t)row * ldv;
@@ -578,6 +579,7 @@ __global__ __launch_bounds__(SAMP_THREADS) void sample_kernel(const float* __res
     if (tid == 0) {
       sel[0] = 0u;
       sel[1] = (uint32_t)top_k;
+      sel[2] = 0u;
     }
     for (int pass = 0; pass < 3; ++pass) {
       const int width = pass < 2 ? 12 : 8, shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
@@ -624,8 +626,12 @@ __global__ __launch_bounds__(SAMP_THREADS) void sample_kernel(const float* __res
         }
         sel[0] = prefix | ((uint32_t)dgt << shift);
         sel[1] = rank - acc;
+        // every value of the bin is kept: the prefix with its lower bits 0
+        // keeps exactly them and all above, so the later passes can go
+        sel[2] = rank - acc == hist[dgt];
       }
       __syncthreads();
+      if (sel[2]) break;
     }
     cut_key = sel[0];
   }
