@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 // e = exp(z - max); the token is the first id whose running sum of e exceeds
 // u * sum(e).  Wave w owns the ids [w*SEG, (w+1)*SEG) and lane l the ids
 // w*SEG + 64 j + l (coalesced loads, held in registers), so the search for
-// the token goes by segments (a scan of the 8 wave sums), then by rows of 64
+// the token goes by segments (a scan of the 16 wave sums), then by rows of 64
 // consecutive ids inside the segment, then by lanes (a wave scan).
 #define SAMP_THREADS 1024
 #define SAMP_PER 56                    // rows of 64 ids per wave
