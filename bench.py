@@ -51,22 +51,39 @@ def flops_per_token(dims, T):
     return 6 * N + 12 * dims["n_layer"] * dims["n_head"] * hs * T
 
 
-# The kernel with the largest share of the step: the bf16 GEMM with bf16
-# output on 128x192 tiles (two workgroups per CU, k-tiles of 64).  A step
-# launches it for the input gradients through the transposed weight copies
-# (fc and qkv per layer, the tied LM head once, the attention projection per
-# layer) and for the forward q|k|v projection.
-DOMINANT_KERNEL = "gemm2_kernel<128, 192, true, true, 0, 2, 64, 2>"  # b16:: or f16:: build
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_act_128x192.json")
+# The step's matrix products, grouped by the kernel instantiation the library
+# runs them with at this workload (the template names rocprofv3 reports).
+# Each group is timed through the single-op entry point that runs the same
+# kernel at the same shapes, one step's launches at a time, with events on
+# the stream the launches go to; the group with the largest time per step is
+# the dominant kernel that `roofline` reports.  The attention-projection and
+# MLP-projection forwards (residual epilogue) have no single-op entry point
+# and are not timed here; they are 8 % of the step.
 TRAFFIC_SOURCES = ["transformer_lm_02_amd/csrc/gemm2.hip", "transformer_lm_02_amd/csrc/gemm.h",
                    "transformer_lm_02_amd/csrc/common.h"]
 
 
-def dominant_launches(B, T, dims):
-    """(M, N, K, count) of the launches one step makes of the dominant kernel."""
+def gemm_groups(B, T, dims):
+    """name -> (kernel template, entry point, [(M, N, K, launches per step)]).
+    Shapes are the entry point's: linear C[M][N] = A[M][K] B[N][K]^T;
+    linear_dw dW[N][K] = dY[M][N]^T X[M][K]; gelu / gelu_bwd as linear."""
     M, d, L = B * T, dims["n_embd"], dims["n_layer"]
     vi = -(-dims["padded_vocab"] // 64) * 64
-    return [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, vi, 1), (M, d, d, L), (M, 3 * d, d, L)]
+    return {
+        "weight_gradients": (
+            "gemm2_kernel<128, 128, false, false, 5, 2, 64, 2> + splitk_reduce_kernel",
+            "linear_dw",
+            [(M, d, 4 * d, L), (M, 4 * d, d, L), (M, d, d, L), (M, 3 * d, d, L), (M, vi, d, 1)]),
+        "input_gradients_and_qkv": (
+            "gemm2_kernel<128, 192, true, true, 0, 2, 64, 2>", "linear",
+            [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, vi, 1), (M, d, d, L), (M, 3 * d, d, L)]),
+        "lm_head_forward": ("gemm2_kernel<256, 192, true, true, 0, 2, 32, 2>", "linear",
+                            [(M, dims["padded_vocab"], d, 1)]),
+        "mlp_expansion_gelu": ("gemm2_kernel<256, 192, true, true, 3, 2, 32, 2>", "gelu",
+                               [(M, 4 * d, d, L)]),
+        "mlp_projection_dx_gelu_bwd": ("gemm2_kernel<256, 192, true, true, 4, 2, 32, 2>",
+                                       "gelu_bwd", [(M, 4 * d, d, L)]),
+    }
 
 
 def sources_hash():
@@ -78,11 +95,12 @@ def sources_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
-    runs, or None when the kernel sources changed since they were taken."""
+def measured_traffic(group):
+    """HBM bytes per launch of a group from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs, or None when there are none or the kernel
+    sources changed since they were taken."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", f"traffic_{group}.json")) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -91,92 +109,149 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def dominant_operands(torch, B, T, dims, dt=None):
-    dt = dt or torch.bfloat16
+def group_operands(torch, shapes, entry, dt):
     g = torch.Generator(device="cuda").manual_seed(7)
     ops = []
-    for (M, N, K, n) in dominant_launches(B, T, dims):
-        A = (torch.randn((M, K), device="cuda", generator=g) * 1e-3).to(dt)
-        W = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(dt)
-        C = torch.empty((M, N), dtype=dt, device="cuda")
-        ops.append((A, W, C, M, N, K, n))
+    for (M, N, K, n) in shapes:
+        if entry == "linear_dw":
+            a = (torch.randn((M, N), device="cuda", generator=g) * 1e-3).to(dt)
+            b = (torch.randn((M, K), device="cuda", generator=g)).to(dt)
+            c = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            aux = None
+        else:
+            a = (torch.randn((M, K), device="cuda", generator=g) * 1e-3).to(dt)
+            b = (torch.randn((N, K), device="cuda", generator=g) * 0.02).to(dt)
+            c = torch.empty((M, N), dtype=dt, device="cuda")
+            aux = torch.empty((M, N), dtype=dt, device="cuda") if entry in ("gelu", "gelu_bwd") else None
+        ops.append((a, b, c, aux, M, N, K, n))
     return ops
 
 
-def launch_dominant(bd, ops, stream_ptr, reps=1):
+def launch_group(bd, entry, ops, ws, stream_ptr, reps=1):
     import ctypes
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
     for _ in range(reps):
-        for (A, W, C, M, N, K, n) in ops:
+        for (a, b, c, aux, M, N, K, n) in ops:
+            dt = bd._bf(a)
             for _ in range(n):
-                bd.check(bd.lib.gpt_op_linear(bd._bf(A), ctypes.c_void_p(A.data_ptr()),
-                                              ctypes.c_void_p(W.data_ptr()), None,
-                                              ctypes.c_void_p(C.data_ptr()), 0, M, N, K,
-                                              stream_ptr), "gpt_op_linear")
+                if entry == "linear":
+                    rc = bd.lib.gpt_op_linear(dt, vp(a), vp(b), None, vp(c), 0, M, N, K, stream_ptr)
+                elif entry == "linear_dw":
+                    rc = bd.lib.gpt_op_linear_dw(dt, vp(a), vp(b), vp(c), 0, M, N, K, vp(ws), wsb,
+                                                 stream_ptr)
+                elif entry == "gelu":
+                    rc = bd.lib.gpt_op_linear_gelu(dt, vp(a), vp(b), None, vp(c), vp(aux), M, N, K,
+                                                   stream_ptr)
+                else:  # gelu_bwd with the bias gradient's column sums, as in the step
+                    rc = bd.lib.gpt_op_linear_gelu_bwd(dt, vp(a), vp(b), vp(aux), vp(c), vp(ws[:N]),
+                                                       0, M, N, K, vp(ws[N:]), wsb - 4 * N,
+                                                       stream_ptr)
+                bd.check(rc, entry)
 
 
-def time_dominant_kernel(torch, bd, B, T, dims, reps=5, fp16=False):
-    """The step's launches of the dominant kernel (same shapes, same entry
-    into the library), timed with events on the stream they run on."""
+def time_gemm_groups(torch, bd, B, T, dims, reps=3, fp16=False):
+    """Per group: one step's launches, timed with events on the current
+    stream over `reps` repetitions after one untimed pass."""
     import ctypes
-    ops = dominant_operands(torch, B, T, dims, torch.float16 if fp16 else torch.bfloat16)
+    dt = torch.float16 if fp16 else torch.bfloat16
     s = torch.cuda.current_stream()
     sp = ctypes.c_void_p(s.cuda_stream)
-    launch_dominant(bd, ops, sp, 1)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    launch_dominant(bd, ops, sp, reps)
-    e1.record(s)
-    torch.cuda.synchronize()
-    n_launch = sum(o[-1] for o in ops)
-    ms_total = e0.elapsed_time(e1) / reps
-    flops = sum(2.0 * M * N * K * n for (_, _, _, M, N, K, n) in ops)
-    achieved = flops / (ms_total * 1e-3) / 1e12
-    name = ("f16::" if fp16 else "b16::") + DOMINANT_KERNEL
-    return {"kernel": name + " (input gradients of fc, qkv, attention projection and LM "
-                             "head; forward q|k|v projection)",
-            "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None if fp16 else measured_traffic(), "launches_per_step": n_launch,
-            "ms_per_launch": round(ms_total / n_launch, 4),
-            "flops_per_launch": flops / n_launch}
+    d = dims["n_embd"]
+    # the step's split-K scratch: 16 partial slices of the widest layer matrix
+    ws = torch.empty(16 * 4 * d * d, dtype=torch.float32, device="cuda")
+    out = {}
+    for name, (kern, entry, shapes) in gemm_groups(B, T, dims).items():
+        ops = group_operands(torch, shapes, entry, dt)
+        launch_group(bd, entry, ops, ws, sp, 1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        launch_group(bd, entry, ops, ws, sp, reps)
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / reps
+        n_launch = sum(o[-1] for o in ops)
+        flops = sum(2.0 * M * N * K * n for (M, N, K, n) in shapes)
+        out[name] = {"kernel": ("f16::" if fp16 else "b16::") + kern, "entry": entry,
+                     "ms_per_step": ms_step, "launches_per_step": n_launch,
+                     "flops_per_step": flops}
+        del ops
+    return out
 
 
-def probe(torch, bd, B, T, dims):
-    """For counter runs: one step's launches of the dominant kernel, then a
-    plain 1 GiB device copy (the calibration of FETCH_SIZE / WRITE_SIZE)."""
+def roofline_from_groups(groups, fp16=False):
+    name = max(groups, key=lambda k: groups[k]["ms_per_step"])
+    g = groups[name]
+    n = g["launches_per_step"]
+    ms_launch = g["ms_per_step"] / n
+    achieved = g["flops_per_step"] / (g["ms_per_step"] * 1e-3) / 1e12
+    return {"kernel": g["kernel"], "group": name, "bound": "mfma",
+            "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None if fp16 else measured_traffic(name),
+            "launches_per_step": n, "ms_per_launch": round(ms_launch, 4),
+            "flops_per_launch": g["flops_per_step"] / n,
+            "groups_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in groups.items()}}
+
+
+def probe(torch, bd, B, T, dims, group):
+    """For counter runs: one step's launches of one group, then a plain 1 GiB
+    device copy (the calibration of FETCH_SIZE / WRITE_SIZE)."""
     import ctypes
-    ops = dominant_operands(torch, B, T, dims)
+    kern, entry, shapes = gemm_groups(B, T, dims)[group]
+    ops = group_operands(torch, shapes, entry, torch.bfloat16)
+    ws = torch.empty(16 * 4 * dims["n_embd"] ** 2, dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream()
-    launch_dominant(bd, ops, ctypes.c_void_p(s.cuda_stream), 1)
+    launch_group(bd, entry, ops, ws, ctypes.c_void_p(s.cuda_stream), 1)
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"probe": DOMINANT_KERNEL, "launches": dominant_launches(B, T, dims),
+    print(json.dumps({"probe": group, "kernel": kern, "launches": shapes,
                       "copy_bytes": src.numel() * 4, "sources_hash": sources_hash()}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(dims, seed=1338):
-    """The float64 oracle (as it stands) on a bounded sample of the workload:
-    one full step (forward, backward, clip, AdamW) on two sequences of 1024
-    tokens with the full model; tokens/s scales linearly in the batch."""
+    """The oracle (as it stands, in its float32 mode) on a bounded sample of
+    the workload: one full step (forward, backward, clip, AdamW) on one
+    sequence of 1024 tokens with the full model, once with every BLAS thread
+    of the host and once with one; tokens/s scales linearly in the batch."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle import gpt_oracle as O
     from transformer_lm_02_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        cores = os.cpu_count()
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
     cfg = O.Config(**{k: dims[k] for k in synth.MODEL_KEYS})
-    params = synth.init_params(dims, seed=1337).astype(np.float64)
-    idx, tgt = synth.tokens(dims, seed=seed, batch=2)
+    params = synth.init_params(dims, seed=1337)
+    idx, tgt = synth.tokens(dims, seed=seed, batch=1)
     zeros = np.zeros_like(params)
-    t0 = time.perf_counter()
-    O.train_step(params, zeros, zeros, 1, [(idx, tgt)], cfg, lr=6e-4)
-    dt = time.perf_counter() - t0
+
+    def run():
+        t0 = time.perf_counter()
+        O.train_step(params, zeros, zeros, 1, [(idx, tgt)], cfg, lr=6e-4, dtype=np.float32)
+        return time.perf_counter() - t0
+
+    dt = run()
+    with threadpool_limits(1):
+        dt1 = run()
     return {"value": round(idx.size / dt, 2), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle", "sample": f"2 x 1024 tokens, full 124M model, float64 numpy step "
-                                        f"(fwd+bwd+clip+AdamW) in {dt:.1f} s"}
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": round(idx.size / dt1, 2), "unit": "tokens/s", "cores": 1,
+                              "s_per_step": round(dt1, 2)},
+            "s_per_step": round(dt, 2),
+            "sample": f"1 x 1024 tokens, full 124M model, float32 numpy oracle step "
+                      f"(fwd+bwd+clip+AdamW): {dt:.1f} s on {cores} threads, {dt1:.1f} s on 1"}
 
 
 def decode_bench(torch, bd, synth, dims, B, prompt, n_new, temperature=0.8, top_k=200):
@@ -260,8 +335,9 @@ def main():
                     help="train with dropout P (the pretraining configuration uses 0)")
     ap.add_argument("--fp16", action="store_true",
                     help="IEEE half precision with dynamic loss scaling instead of bf16")
-    ap.add_argument("--probe", action="store_true",
-                    help="only launch the dominant kernel and a calibration copy (counter runs)")
+    ap.add_argument("--probe", default=None, metavar="GROUP",
+                    help="only launch one step's products of GROUP and a calibration copy "
+                         "(counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library "
@@ -280,7 +356,7 @@ def main():
         decode_bench(torch, bd, synth, synth.model_dims(dims), args.decode, 64, 448)
         return
     if args.probe:
-        probe(torch, bd, B, T, dims)
+        probe(torch, bd, B, T, dims, args.probe)
         return
     print(f"[bench] building model {args.workload} B={B} T={T}", file=sys.stderr, flush=True)
     params = synth.init_params(dims, seed=1337)
@@ -342,11 +418,14 @@ def main():
           f"norm {norm:.4f}, MFU {mfu:.4f}", file=sys.stderr, flush=True)
     scaler = model.scaler_state() if args.fp16 else None
     roof = None
-    if not args.no_kernel_timing and headline:
-        roof = time_dominant_kernel(torch, bd, B, T, dims, fp16=args.fp16)
     model.close()
     del model
     torch.cuda.empty_cache()
+    if not args.no_kernel_timing and headline:
+        print("[bench] timing the step's matrix products by kernel", file=sys.stderr, flush=True)
+        roof = roofline_from_groups(time_gemm_groups(torch, bd, B, T, dims, fp16=args.fp16),
+                                    fp16=args.fp16)
+        torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline and headline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -51,8 +51,11 @@ enum { GPT_FP32 = 0, GPT_BF16 = 1, GPT_FP16 = 2 };
 
 /* Device flag bits reported by gpt_read_flags. */
 enum {
-  GPT_FLAG_BAD_TOKEN = 1  /* an input id was outside [0, padded_vocab); its
-                             embedding row was taken as zero */
+  GPT_FLAG_BAD_TOKEN = 1,  /* an input id was outside [0, padded_vocab); its
+                              embedding row was taken as zero */
+  GPT_FLAG_BAD_TARGET = 2  /* a target was outside [-1, vocab_size); it was
+                              treated as ignored (-1): left out of the count of
+                              valid targets, zero loss and zero gradient */
 };
 
 typedef struct {
@@ -87,20 +90,29 @@ typedef struct gpt_model gpt_model;
 int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace_bytes);
 
 /* Bind caller-owned device buffers and create a handle.
- * params, grads, adam_m, adam_v: device fp32 [n_params]; workspace: device
- * memory of workspace_bytes.  init_params: device fp32 [n_params] in the
- * canonical order, copied into params (NULL keeps params as they are).
- * adam_m and adam_v are zeroed.  The 16-bit weight copy (16-bit modes) is written.
- * The buffers must stay valid until gpt_destroy. */
+ * params, grads, adam_m, adam_v: device fp32 [n_params] (params 16-byte
+ * aligned); workspace: device memory of workspace_bytes.
+ * init_params: device fp32 [n_params] in the canonical order, copied into
+ * params; or NULL: params are drawn on the device from `seed` ("Let's
+ * reproduce GPT-2 (124M)", chapter "Model Initialization"; "nanoGPT" Part V
+ * Deep dive 1): every Linear weight and both embedding tables (pad rows
+ * included) N(0, 0.02^2), attn.c_proj and mlp.c_proj weights
+ * N(0, (0.02 / sqrt(2 n_layer))^2), biases 0, LayerNorm gains 1 and shifts
+ * 0.  The normals come from Philox4x32-10 under the 64-bit seed through the
+ * Box-Muller transform; element i's value depends only on i and the seed.
+ * seed is unused when init_params is not NULL.
+ * adam_m, adam_v and grads are zeroed.  The 16-bit weight copy (16-bit
+ * modes) is written.  The buffers must stay valid until gpt_destroy. */
 int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads,
              float* adam_m, float* adam_v, void* workspace, const float* init_params,
-             void* stream);
+             uint64_t seed, void* stream);
 
 /* Forward pass and, when targets != NULL, the loss and its gradient w.r.t.
  * the logits ("nanoGPT", Part IV Stage 4; loss of "Let's reproduce GPT-2
  * (124M)", chapter "Cross Entropy Loss").
  * idx, targets: device int32 [B*T], row-major (b, t).  A target of -1 is
- * ignored (ignore_index=-1); the loss is the mean over the others.
+ * ignored (ignore_index=-1); the loss is the mean over the others.  A target
+ * outside [-1, V) is treated as ignored too and raises GPT_FLAG_BAD_TARGET.
  * loss_scale multiplies the gradient only (1/k under accumulation over k
  * micro-batches, "nanoGPT" Part IV Stage 4).
  * loss_out: device float, receives the unscaled mean loss (may be NULL).
@@ -112,7 +124,7 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets,
                      void* logits_out, void* stream);
 
 /* Evaluation ("nanoGPT", Part IV Stage 2, estimate_loss: the model in eval
- * mode and no gradient): the mean loss over the targets >= 0 of one batch
+ * mode and no gradient): the mean loss over the targets in [0, V) of one batch
  * into loss_out (device float), with no dropout and no gradient written.
  * The caller averages such losses over its evaluation batches.  A following
  * gpt_backward fails with GPT_ESTATE.  Errors as gpt_forward_loss; targets
@@ -276,7 +288,10 @@ int gpt_decode_step(gpt_model* h, const int32_t* tok, int32_t B, int32_t pos, vo
  * z = logits / temperature; when 0 < top_k < V, ids with z below the k-th
  * largest z are removed (ids equal to it stay); p = softmax(z); the token is
  * the first id whose cumulative p exceeds u[b] (device fp32 [B], uniforms in
- * [0, 1) that the caller draws).  tok_out: device int32 [B].
+ * [0, 1) that the caller draws).  tok_out: device int32 [B].  A row with no
+ * distribution to draw from (a NaN or +inf logit, or u[b] negative or NaN)
+ * gets -1, which a following gpt_decode_step reports as GPT_FLAG_BAD_TOKEN;
+ * u[b] >= 1 takes the last kept id.
  * Errors: GPT_EINVAL (null pointer, B < 1, ldv < V, temperature <= 0),
  * GPT_EUNSUPPORTED (V above 57344). */
 int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float temperature,
@@ -304,6 +319,30 @@ const char* gpt_strerror(int code);
  * C: act [M][N] (fp32 when out_f32 != 0).  16-bit dtypes need K % 8 == 0. */
 int gpt_op_linear(int32_t dtype, const void* A, const void* B, const float* bias,
                   void* C, int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* The MLP expansion with its activation ("nanoGPT" Deep dive 1, the MLP:
+ * expand, tanh-GELU; "Let's Reproduce GPT-2 in One Read", the GELU check):
+ * u = A W^T + bias over K; dgelu[m][n] = gelu'(u), g[m][n] = gelu(u), with
+ * gelu(u) = 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).  A: act [M][K],
+ * W: act [N][K], bias: fp32 [N] or NULL, dgelu and g: act [M][N].  The step
+ * keeps gelu'(u) instead of u for its backward.  16-bit dtypes need
+ * K % 8 == 0. */
+int gpt_op_linear_gelu(int32_t dtype, const void* A, const void* W, const float* bias,
+                       void* dgelu, void* g, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* The MLP projection's input gradient through the activation ("nanoGPT"
+ * Part IV Stage 4, the backward of Deep dive 1's MLP):
+ * du[m][n] = (sum_k dY[m][k] Wt[n][k]) * dgelu[m][n], and when dbias is not
+ * NULL, dbias[n] (+)= sum_m du[m][n] (the expansion's bias gradient; added to
+ * dbias when accumulate_bias != 0), summed from the fp32 values before du is
+ * rounded.  dY: act [M][K], Wt: act [N][K] (the projection's weight
+ * transposed), dgelu: act [M][N] as gpt_op_linear_gelu writes it, du: act
+ * [M][N], dbias: fp32 [N].  workspace: device fp32 scratch of workspace_bytes
+ * >= ceil(M/128) * N * 4 (column-sum partials), needed only with dbias;
+ * GPT_EINVAL otherwise.  16-bit dtypes need K % 8 == 0. */
+int gpt_op_linear_gelu_bwd(int32_t dtype, const void* dY, const void* Wt, const void* dgelu,
+                           void* du, float* dbias, int32_t accumulate_bias, int32_t M, int32_t N,
+                           int32_t K, float* workspace, int64_t workspace_bytes, void* stream);
 
 /* dW (+)= dY^T X: dY act [M][N], X act [M][K], dW fp32 [N][K];
  * accumulate != 0 adds to dW.  The weight gradient of a Linear layer.
@@ -348,9 +387,10 @@ int gpt_op_dropout(const float* x, float* y, int64_t rows, int32_t cols, float p
 
 /* Masked softmax cross-entropy, in place: logits act [N][ldv] -> dlogits
  * (loss_scale * (softmax - onehot) / n_valid over columns < V, zero for
- * columns in [V, ldv)); loss: device fp32 scalar = mean over targets >= 0.
+ * columns in [V, ldv)); loss: device fp32 scalar = mean over the targets in
+ * [0, V) (any other target is ignored: zero loss and gradient in its row).
  * row_loss: device fp32 [N] receiving each row's loss (0 if ignored);
- * n_valid: device int32 receiving the count of targets >= 0.
+ * n_valid: device int32 receiving the count of targets in [0, V).
  * 16-bit dtypes need ldv % 8 == 0 and ldv <= 53248. */
 int gpt_op_cross_entropy(int32_t dtype, void* logits, const int32_t* targets,
                          float* loss, float* row_loss, int32_t* n_valid,

@@ -92,7 +92,7 @@ def test_null_arguments_are_rejected_without_a_device():
     h = ctypes.c_void_p()
     cfg = dims_cfg("tiny", bd.GPT_FP32)
     assert lib.gpt_init(ctypes.byref(h), ctypes.byref(cfg), None, None, None, None, None, None,
-                        None) == bd.GPT_EINVAL
+                        0, None) == bd.GPT_EINVAL
     assert b"invalid argument" in lib.gpt_strerror(bd.GPT_EINVAL)
     lib.gpt_destroy(None)
 
@@ -123,7 +123,7 @@ def test_loss_scaling_and_dtype_arguments_are_checked_without_a_device():
     cfg = dims_cfg("tiny", bd.GPT_FP16)
     cfg.n_head = 5
     assert lib.gpt_init(ctypes.byref(h), ctypes.byref(cfg), None, None, None, None, None, None,
-                        None) == bd.GPT_EINVAL
+                        0, None) == bd.GPT_EINVAL
     assert not h.value
 
 

@@ -129,6 +129,28 @@ def test_sample_kernel_keeps_ties_at_the_cutoff():
     assert list(tok) == [7, 100, 500, 999]
 
 
+def test_sample_kernel_writes_minus_one_without_a_distribution():
+    """A row holding a NaN logit (its total is NaN), and a row with a negative
+    uniform, have nothing to draw: the token is -1, never a stale value.  The
+    output starts out filled with a valid id to show that it was written;
+    the clean row beside them draws as the oracle does, and u = 1 takes the
+    last kept id."""
+    case("sample without a distribution: NaN logit, negative uniform")
+    V, B = 5000, 4
+    rng = np.random.default_rng(31)
+    logits = (rng.normal(size=(B, V)) * 2).astype(np.float32)
+    logits[0, 1234] = np.nan
+    u = np.array([0.5, -0.25, 0.3, 1.0], np.float32)
+    tok = torch.full((B,), 17, dtype=torch.int32, device="cuda")
+    bd.check(bd.lib.gpt_sample(bd._ptr(dev(logits)), B, V, V, 1.0, 0, bd._ptr(dev(u)),
+                               bd._ptr(tok), bd._stream()), "gpt_sample")
+    got = to_np(tok).astype(int)
+    assert got[0] == -1 and got[1] == -1
+    t_ref, _ = O.topk_sample(logits[2].astype(np.float64), V, 1.0, 0, float(u[2]))
+    assert got[2] == t_ref
+    assert got[3] == V - 1
+
+
 def identity_params(dims):
     """Blocks that add nothing (projections, biases and wpe zero; LayerNorms
     identity) and orthonormal token rows orthogonal to the ones vector: the

@@ -75,6 +75,56 @@ def test_linear_dx_bf16(M, N, K):
     assert rel_err(got, ref) < 1e-5 and max_rel(got, ref) < 1e-4
 
 
+# The MLP expansion's two epilogues at the step's own shapes: 16384 x 3072 x
+# 768 (GPT-2 124M, B=16 T=1024) and 8192 x 6400 x 1600 (the 1.5B shape, B=8)
+# take the widest tiles; 2048 x 3072 x 768 and a ragged shape take the others.
+GELU_SHAPES = [(16384, 3072, 768), (8192, 6400, 1600), (2048, 3072, 768), (300, 200, 136)]
+
+
+@pytest.mark.parametrize("M,N,K", GELU_SHAPES)
+def test_linear_gelu_forward_bf16(M, N, K):
+    """u = A W^T + b; the kernel stores gelu'(u) and gelu(u) in bf16: every
+    element against the tanh form's definition in float64."""
+    case(f"linear+gelu bf16 M={M} N={N} K={K}")
+    A, W = bf16_round(rnd((M, K), 40)), bf16_round(rnd((N, K), 41, 1.5 / math.sqrt(K)))
+    bias = rnd(N, 42, 0.5)
+    u = A @ W.T + bias
+    dg, g = bd.op_linear_gelu(to_dev(A, torch.bfloat16), to_dev(W, torch.bfloat16),
+                              torch.as_tensor(bias).cuda())
+    torch.cuda.synchronize()
+    for got, ref in ((to_np(g), O.gelu_fwd(u)), (to_np(dg), O.gelu_bwd(u))):
+        # bf16 output: half an ulp of the value, plus the fp32 accumulation
+        err = np.abs(got - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2e-4 * np.abs(ref).max()), float(err.max())
+        assert rel_err(got, ref) < 4e-3
+
+
+@pytest.mark.parametrize("M,N,K", GELU_SHAPES)
+def test_linear_gelu_backward_bf16(M, N, K):
+    """du = (dY Wt^T) * gelu'(u) in bf16 and the bias gradient colsum(du) in
+    fp32, accumulated onto an existing value: every element against float64."""
+    case(f"linear gelu-backward bf16 M={M} N={N} K={K}")
+    dY = bf16_round(rnd((M, K), 43, 0.01))
+    Wt = bf16_round(rnd((N, K), 44, 0.02))
+    dgelu = bf16_round(np.random.default_rng(45).uniform(-0.15, 1.15, (M, N)))
+    du_ref = (dY @ Wt.T) * dgelu
+    db0 = rnd(N, 46)
+    db_ref = db0 + du_ref.sum(axis=0)
+    db = torch.as_tensor(db0).cuda()
+    du = bd.op_linear_gelu_bwd(to_dev(dY, torch.bfloat16), to_dev(Wt, torch.bfloat16),
+                               to_dev(dgelu, torch.bfloat16), dbias=db, accumulate_bias=True)
+    torch.cuda.synchronize()
+    got = to_np(du)
+    err = np.abs(got - du_ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(du_ref) + 2e-4 * np.abs(du_ref).max()), float(err.max())
+    assert rel_err(got, du_ref) < 4e-3
+    assert max_rel(to_np(db) - db0, db_ref - db0) < 1e-4
+    # without the bias gradient no scratch is needed
+    du2 = bd.op_linear_gelu_bwd(to_dev(dY, torch.bfloat16), to_dev(Wt, torch.bfloat16),
+                                to_dev(dgelu, torch.bfloat16))
+    assert torch.equal(du, du2)
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 192, 64), (70, 33, 17)])
 def test_linear_family_fp32(M, N, K):
     case(f"linear family fp32 M={M} N={N} K={K}")

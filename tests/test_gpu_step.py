@@ -260,6 +260,86 @@ def test_gpt2_full_batch_sampled_logits_and_properties():
     m.close()
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,batch,override", [
+    ("gpt2", 16, {}),
+    # the 1.5B shape's width at its batch of 8: every per-layer kernel at that
+    # shape and tile choice; depth only repeats them
+    ("gpt2_1p5b", 8, {"n_layer": 2}),
+])
+def test_full_batch_gradients_match_oracle(name, batch, override):
+    """The benchmark's launch configuration (B sequences of T=1024, so that
+    every product takes the tiles the benchmark times) against the oracle's
+    gradients of the whole batch, built as the sum over sequences of the
+    oracle's per-sequence gradients with loss scale 1/B (run in parallel host
+    processes while the GPU works): loss within 2e-2, per-tensor cosine >=
+    0.995 (key bias aside).  Then the AdamW step on those gradients against
+    the oracle's AdamW on the same gradients, every element."""
+    from tests import oracle_jobs
+    dims = dict(synth.WORKLOADS[name], **override)
+    T = dims["block_size"]
+    case(f"{name} bf16 full batch B={batch} T={T} gradients vs oracle")
+    handle = oracle_jobs.start_batch_grads(dims, batch, 1337, 1338, T)
+    params = synth.init_params(dims, seed=1337)
+    idx, tgt = synth.tokens(dims, seed=1338, batch=batch, T=T)
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=batch, init_params=params)
+    loss, _ = m.forward(*dev_tokens(idx, tgt))
+    m.backward()
+    torch.cuda.synchronize()
+    got_loss = float(loss.item())
+    got_g = to_np(m.grads)
+    lr = 6e-4
+    norm = m.adamw_step(lr=lr, t=1, max_norm=1.0)
+    torch.cuda.synchronize()
+    got_p = to_np(m.params)
+    got_norm = float(norm.item())
+    m.close()
+    # AdamW on identical inputs (the GPU's own gradients)
+    ref_norm = O.grad_norm(got_g)
+    assert abs(got_norm - ref_norm) <= 1e-5 * ref_norm
+    ref_p, _, _ = O.adamw(params.astype(np.float64), got_g, np.zeros_like(got_g),
+                          np.zeros_like(got_g), O.decay_mask(ocfg(dims)), 1, lr,
+                          coef=O.clip_coef(ref_norm, 1.0))
+    p0 = params.astype(np.float64)
+    assert max_rel(got_p - p0, ref_p - p0) <= 1e-3
+    ref_loss, ref_g = oracle_jobs.finish_batch_grads(handle)
+    assert abs(got_loss - ref_loss) <= 2e-2, (got_loss, ref_loss)
+    worst = check_grads(dims, got_g, ref_g, min_cos=0.995)
+    print(f"loss gpu {got_loss:.5f} oracle {ref_loss:.5f}; norm gpu {got_norm:.5f} "
+          f"oracle {O.grad_norm(ref_g):.5f}; lowest cosines {worst}", flush=True)
+
+
+def test_large_finite_gradients_keep_a_finite_norm():
+    """Gradients of magnitude 1e20 are finite in fp32 and their squares are
+    finite in fp64: the norm is finite and exact to fp32 rounding, the step is
+    not skipped, and a loss-scaled step counts it as clean."""
+    dims = synth.WORKLOADS["tiny"]
+    case("norm of finite gradients of magnitude 1e20")
+    params = synth.perturbed_params(dims, seed=21)
+    n = params.size
+    g = synth.synthetic_grads(n, seed=22)
+    g[::1000] = np.float32(1e20)
+    g[7] = np.float32(-3e20)
+    ref = float(np.sqrt(np.sum(g.astype(np.float64) ** 2)))
+    mdl = bd.GPT(dims, bd.GPT_FP32, max_batch=1, init_params=params)
+    mdl.grads.copy_(torch.as_tensor(g))
+    norm = mdl.adamw_step(lr=1e-3, t=1, max_norm=1.0, skip_nonfinite=True)
+    torch.cuda.synchronize()
+    assert math.isfinite(float(norm.item()))
+    assert abs(float(norm.item()) - ref) <= 1e-6 * ref
+    assert not np.array_equal(to_np(mdl.params), params.astype(np.float64))  # not skipped
+    mdl.close()
+    mdl = bd.GPT(dims, bd.GPT_FP16, max_batch=1, init_params=params)
+    mdl.init_scaler(scale=1.0)
+    mdl.grads.copy_(torch.as_tensor(g))
+    norm = mdl.amp_step(lr=1e-3, max_norm=1.0)
+    torch.cuda.synchronize()
+    assert abs(float(norm.item()) - ref) <= 1e-6 * ref
+    scale, _, steps, found_inf = mdl.scaler_state()
+    assert (scale, steps, found_inf) == (1.0, 1, 0)
+    mdl.close()
+
+
 def test_bf16_causal_invariance_bit_identical():
     dims = synth.WORKLOADS["char"]
     case("char bf16 causal bit-identity B=4 T=256")
@@ -351,3 +431,36 @@ def test_error_paths_and_bad_token_flag():
     assert math.isfinite(float(loss.item()))
     assert m.read_flags() == 0
     m.close()
+
+
+def test_out_of_range_targets_are_ignored_and_flagged():
+    """Targets outside [-1, V) name no class: the library leaves them out of
+    the count of valid targets, of the loss and of the gradient, exactly as
+    -1, and raises GPT_FLAG_BAD_TARGET.  Checked against the oracle run with
+    those targets set to -1."""
+    dims = synth.WORKLOADS["tiny"]
+    case("tiny fp32 out-of-range targets")
+    params = synth.perturbed_params(dims, seed=23)
+    idx, tgt = synth.tokens(dims, seed=24, batch=2)
+    bad = tgt.copy()
+    bad[0, 3], bad[1, 10], bad[1, 11] = 65, 9999, -7
+    ign = bad.copy()
+    ign[(ign < 0) | (ign >= 65)] = -1
+    ref_loss, ref_g, _ = O.loss_and_grads(params, idx, ign, ocfg(dims))
+    m = bd.GPT(dims, bd.GPT_FP32, max_batch=2, init_params=params)
+    loss, _ = m.forward(*dev_tokens(idx, bad))
+    m.backward()
+    assert m.read_flags() == bd.GPT_FLAG_BAD_TARGET
+    assert abs(float(loss.item()) - ref_loss) <= 1e-5
+    check_grads(dims, to_np(m.grads), ref_g, max_rel_err=1e-4)
+    m.close()
+    # the single-op cross-entropy counts and ignores them the same way
+    z = np.random.default_rng(25).standard_normal((6, 65)).astype(np.float32)
+    t = np.array([3, 65, -1, 64, -2, 100], np.int32)
+    t_ign = np.where((t < 0) | (t >= 65), -1, t).astype(np.int32)
+    loss_ref, dz_ref = O.cross_entropy(z.astype(np.float64), t_ign, 65)
+    zd = torch.as_tensor(z).cuda()
+    l, _, nv = bd.op_cross_entropy(zd, torch.as_tensor(t).cuda(), 65)
+    assert int(nv.item()) == 2
+    assert abs(float(l.item()) - loss_ref) <= 1e-5
+    assert max_rel(to_np(zd), dz_ref) <= 1e-5

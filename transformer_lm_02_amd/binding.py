@@ -28,6 +28,7 @@ lib = ctypes.CDLL(LIB_PATH)
 GPT_OK, GPT_EINVAL, GPT_ESEQLEN, GPT_ESTATE, GPT_EHIP, GPT_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 GPT_FP32, GPT_BF16, GPT_FP16 = 0, 1, 2
 GPT_FLAG_BAD_TOKEN = 1
+GPT_FLAG_BAD_TARGET = 2
 
 
 class gpt_config(ctypes.Structure):
@@ -43,7 +44,8 @@ class gpt_dropout(ctypes.Structure):
 _p, _i32, _i64, _f = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _SIGS = {
     "gpt_query_sizes": [ctypes.POINTER(gpt_config), ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
-    "gpt_init": [ctypes.POINTER(_p), ctypes.POINTER(gpt_config), _p, _p, _p, _p, _p, _p, _p],
+    "gpt_init": [ctypes.POINTER(_p), ctypes.POINTER(gpt_config), _p, _p, _p, _p, _p, _p,
+                 ctypes.c_uint64, _p],
     "gpt_forward_loss": [_p, _p, _p, _i32, _i32, _f, _p, _p, _p],
     "gpt_forward_loss_scaled": [_p, _p, _p, _i32, _i32, _f, _p, _p, _p, _p],
     "gpt_forward_loss_ex": [_p, _p, _p, _i32, _i32, _f, _p, ctypes.POINTER(gpt_dropout), _p, _p,
@@ -56,6 +58,8 @@ _SIGS = {
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
     "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
     "gpt_op_linear": [_i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
+    "gpt_op_linear_gelu": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p],
+    "gpt_op_linear_gelu_bwd": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
     "gpt_op_linear_dw": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
     "gpt_op_linear_dx": [_i32, _p, _p, _p, _i32, _i32, _i32, _p],
     "gpt_op_attention_fwd": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
@@ -113,7 +117,10 @@ def _ptr(t):
 class GPT:
     """Device buffers (torch tensors) plus the library handle."""
 
-    def __init__(self, dims: dict, mode: int, max_batch: int, init_params=None, device="cuda"):
+    def __init__(self, dims: dict, mode: int, max_batch: int, init_params=None, seed=0,
+                 device="cuda"):
+        """init_params: host array of the initial parameters (canonical order),
+        or None to draw them on the device from `seed` (gpt_init)."""
         import torch
         self.dims = dict(dims)
         self.mode = mode
@@ -137,7 +144,7 @@ class GPT:
         h = ctypes.c_void_p()
         check(lib.gpt_init(ctypes.byref(h), ctypes.byref(self.cfg), _ptr(self.params),
                            _ptr(self.grads), _ptr(self.adam_m), _ptr(self.adam_v),
-                           _ptr(self.workspace), _ptr(init), _stream()), "gpt_init")
+                           _ptr(self.workspace), _ptr(init), seed, _stream()), "gpt_init")
         self.handle = h
         self._init = init
 
@@ -337,6 +344,40 @@ def op_linear(A, B, bias=None, out_f32=False):
     check(lib.gpt_op_linear(_bf(A), _ptr(A), _ptr(B), _ptr(bias), _ptr(C), int(out_f32), M, N, K,
                             _stream()), "gpt_op_linear")
     return C
+
+
+def op_linear_gelu(A, W, bias=None):
+    """(dgelu, g) = (gelu'(u), gelu(u)) with u = A W^T + bias: gpt_op_linear_gelu."""
+    import torch
+    M, K = A.shape
+    N = W.shape[0]
+    dg = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    g = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    check(lib.gpt_op_linear_gelu(_bf(A), _ptr(A), _ptr(W), _ptr(bias), _ptr(dg), _ptr(g), M, N, K,
+                                 _stream()), "gpt_op_linear_gelu")
+    return dg, g
+
+
+def gelu_bwd_scratch_bytes(M, N):
+    """Scratch the column sums of gpt_op_linear_gelu_bwd need: ceil(M/128) N fp32."""
+    return -(-M // 128) * N * 4
+
+
+def op_linear_gelu_bwd(dY, Wt, dgelu, dbias=None, accumulate_bias=False, workspace=None):
+    """du = (dY Wt^T) * dgelu and dbias (+)= colsum(du): gpt_op_linear_gelu_bwd.
+    workspace: fp32 cuda scratch (allocated here when dbias is given and it is None)."""
+    import torch
+    M, K = dY.shape
+    N = Wt.shape[0]
+    du = torch.empty((M, N), dtype=dY.dtype, device=dY.device)
+    if dbias is not None and workspace is None:
+        workspace = torch.empty(gelu_bwd_scratch_bytes(M, N) // 4, dtype=torch.float32,
+                                device=dY.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.gpt_op_linear_gelu_bwd(_bf(dY), _ptr(dY), _ptr(Wt), _ptr(dgelu), _ptr(du), _ptr(dbias),
+                                     int(accumulate_bias), M, N, K, _ptr(workspace), wsb,
+                                     _stream()), "gpt_op_linear_gelu_bwd")
+    return du
 
 
 def op_linear_dw(dY, X, dW=None, workspace=None):

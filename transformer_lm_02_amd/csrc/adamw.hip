@@ -20,7 +20,10 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const float* __restrict__ g,
   const int64_t nv = n >> 2;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += (int64_t)gridDim.x * 256) {
     const float4 v = ((const float4*)g)[i];
-    s += (double)(v.x * v.x) + (double)(v.y * v.y) + (double)(v.z * v.z) + (double)(v.w * v.w);
+    // squared in fp64: a finite fp32 value squares to a finite fp64 one, so
+    // the sum is non-finite exactly when some element is inf or NaN
+    const double x = v.x, y = v.y, z = v.z, w = v.w;
+    s += x * x + y * y + z * z + w * w;
   }
   if (blockIdx.x == 0)
     for (int64_t i = 4 * nv + threadIdx.x; i < n; i += 256) s += (double)g[i] * g[i];

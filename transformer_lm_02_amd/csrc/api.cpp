@@ -47,7 +47,8 @@ int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace
 }
 
 int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads, float* adam_m,
-             float* adam_v, void* workspace, const float* init_params, void* stream) {
+             float* adam_v, void* workspace, const float* init_params, uint64_t seed,
+             void* stream) {
   if (!out) {
     gpt_error_text() = "null output handle";
     return GPT_EINVAL;
@@ -58,11 +59,11 @@ int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads
   int rc;
   if (fp16) {
     f16::Model* m = nullptr;
-    rc = f16::gpt_init(&m, cfg, params, grads, adam_m, adam_v, workspace, init_params, stream);
+    rc = f16::gpt_init(&m, cfg, params, grads, adam_m, adam_v, workspace, init_params, seed, stream);
     impl = m;
   } else {
     b16::Model* m = nullptr;
-    rc = b16::gpt_init(&m, cfg, params, grads, adam_m, adam_v, workspace, init_params, stream);
+    rc = b16::gpt_init(&m, cfg, params, grads, adam_m, adam_v, workspace, init_params, seed, stream);
     impl = m;
   }
   if (rc != GPT_OK) return rc;  // the build's own init released what it made
@@ -210,6 +211,18 @@ const char* gpt_strerror(int code) {
 int gpt_op_linear(int32_t dtype, const void* A, const void* B, const float* bias, void* C,
                   int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream) {
   return OP(gpt_op_linear, dtype, A, B, bias, C, out_f32, M, N, K, stream);
+}
+
+int gpt_op_linear_gelu(int32_t dtype, const void* A, const void* W, const float* bias,
+                       void* dgelu, void* g, int32_t M, int32_t N, int32_t K, void* stream) {
+  return OP(gpt_op_linear_gelu, dtype, A, W, bias, dgelu, g, M, N, K, stream);
+}
+
+int gpt_op_linear_gelu_bwd(int32_t dtype, const void* dY, const void* Wt, const void* dgelu,
+                           void* du, float* dbias, int32_t accumulate_bias, int32_t M, int32_t N,
+                           int32_t K, float* workspace, int64_t workspace_bytes, void* stream) {
+  return OP(gpt_op_linear_gelu_bwd, dtype, dY, Wt, dgelu, du, dbias, accumulate_bias, M, N, K,
+            workspace, workspace_bytes, stream);
 }
 
 int gpt_op_linear_dw(int32_t dtype, const void* dY, const void* X, float* dW, int32_t accumulate,

@@ -17,7 +17,8 @@ std::string& gpt_error_text();
   struct Model;                                                                                 \
   int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace_bytes);      \
   int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, float* adam_m,  \
-               float* adam_v, void* workspace, const float* init_params, void* stream);         \
+               float* adam_v, void* workspace, const float* init_params, uint64_t seed,         \
+               void* stream);                                                                   \
   int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t B,         \
                        int32_t T, float loss_scale, const float* dscale,                        \
                        const gpt_dropout* dropout, float* loss_out, void* logits_out,           \
@@ -43,6 +44,12 @@ std::string& gpt_error_text();
   void gpt_destroy(Model* h);                                                                   \
   int gpt_op_linear(int32_t h16, const void* A, const void* B, const float* bias, void* C,      \
                     int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream);            \
+  int gpt_op_linear_gelu(int32_t h16, const void* A, const void* W, const float* bias,        \
+                         void* dgelu, void* g, int32_t M, int32_t N, int32_t K, void* stream);   \
+  int gpt_op_linear_gelu_bwd(int32_t h16, const void* dY, const void* Wt, const void* dgelu,    \
+                             void* du, float* dbias, int32_t accumulate_bias, int32_t M,        \
+                             int32_t N, int32_t K, float* workspace, int64_t workspace_bytes,   \
+                             void* stream);                                                     \
   int gpt_op_linear_dw(int32_t h16, const void* dY, const void* X, float* dW,                   \
                        int32_t accumulate, int32_t M, int32_t N, int32_t K, float* workspace,   \
                        int64_t workspace_bytes, void* stream);                                  \

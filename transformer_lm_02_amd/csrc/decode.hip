@@ -540,6 +540,10 @@ __global__ __launch_bounds__(SAMP_THREADS) void sample_kernel(const float* __res
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* z = logits + (int64_t)row * ldv;
   const int seg0 = wave * SAMP_SEG;
+  // -1 unless a draw lands below: no kept mass to draw from (a NaN or +inf
+  // logit makes the total NaN), or a uniform that is negative or NaN.  The
+  // barriers of the reductions below order this store before the draw's.
+  if (tid == 0) tok[row] = -1;
   // every load issued before any is used: a clamped index (masked
   // afterwards, so no load sits in a branch of its own) as a 32-bit byte
   // offset from the row (one address register each), and a scheduling

@@ -54,44 +54,49 @@ int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 struct LayerOff {
   int64_t ln1w, ln1b, attnw, attnb, aprojw, aprojb, ln2w, ln2b, fcw, fcb, mprojw, mprojb;
 };
+// initial value of a tensor drawn from a seed: N(0, 0.02^2), N(0, (0.02 /
+// sqrt(2 L))^2) for the projections into the residual stream, or a constant
+enum InitKind { INIT_STD = 0, INIT_RESID = 1, INIT_ONE = 2, INIT_ZERO = 3 };
 struct ParamOff {
   int64_t wte, wpe, lnfw, lnfb, total;
   std::vector<LayerOff> layer;
   std::vector<std::pair<int64_t, int64_t>> tensors;  // (offset, count) in order
   std::vector<int> is2d;
+  std::vector<int> init;  // InitKind per tensor
 };
 
 ParamOff param_offsets(const gpt_config& c) {
   ParamOff p;
   int64_t off = 0;
   const int64_t d = c.n_embd;
-  auto take = [&](int64_t n, bool two_d) {
+  auto take = [&](int64_t n, bool two_d, int init) {
     int64_t o = off;
     p.tensors.push_back({o, n});
     p.is2d.push_back(two_d);
+    p.init.push_back(init);
     off += n;
     return o;
   };
-  p.wte = take((int64_t)c.padded_vocab * d, true);
-  p.wpe = take((int64_t)c.block_size * d, true);
+  p.wte = take((int64_t)c.padded_vocab * d, true, INIT_STD);
+  p.wpe = take((int64_t)c.block_size * d, true, INIT_STD);
   for (int l = 0; l < c.n_layer; ++l) {
     LayerOff L;
-    L.ln1w = take(d, false);
-    L.ln1b = take(d, false);
-    L.attnw = take(3 * d * d, true);
-    L.attnb = take(3 * d, false);
-    L.aprojw = take(d * d, true);
-    L.aprojb = take(d, false);
-    L.ln2w = take(d, false);
-    L.ln2b = take(d, false);
-    L.fcw = take(4 * d * d, true);
-    L.fcb = take(4 * d, false);
-    L.mprojw = take(4 * d * d, true);
-    L.mprojb = take(d, false);
+    L.ln1w = take(d, false, INIT_ONE);
+    L.ln1b = take(d, false, INIT_ZERO);
+    L.attnw = take(3 * d * d, true, INIT_STD);
+    L.attnb = take(3 * d, false, INIT_ZERO);
+    L.aprojw = take(d * d, true, INIT_RESID);
+    L.aprojb = take(d, false, INIT_ZERO);
+    L.ln2w = take(d, false, INIT_ONE);
+    L.ln2b = take(d, false, INIT_ZERO);
+    L.fcw = take(4 * d * d, true, INIT_STD);
+    L.fcb = take(4 * d, false, INIT_ZERO);
+    L.mprojw = take(4 * d * d, true, INIT_RESID);
+    L.mprojb = take(d, false, INIT_ZERO);
     p.layer.push_back(L);
   }
-  p.lnfw = take(d, false);
-  p.lnfb = take(d, false);
+  p.lnfw = take(d, false, INIT_ONE);
+  p.lnfb = take(d, false, INIT_ZERO);
   p.total = off;
   return p;
 }
@@ -109,6 +114,7 @@ struct WsOff {
   size_t dres, dres_act, dln, dbig, dO, Dbuf, ln_part, cs_part, norm_part, chunks, splitk;
   int64_t splitk_bytes;
   int64_t ln_part_elems, cs_part_elems;  // one slice of each (several slices kept)
+  size_t init_tab;  // InitSeg per chunk (initialisation from a seed)
   size_t total;
   int nchunks;
   int64_t vi;  // logits row pitch: padded_vocab rounded up to 64
@@ -204,6 +210,7 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   for (auto& t : p.tensors) nch += (t.second + kChunk - 1) / kChunk;
   w.nchunks = (int)nch;
   w.chunks = take(nch * (int64_t)sizeof(AdamChunk));
+  w.init_tab = take(nch * (int64_t)sizeof(InitSeg));
   w.total = off;
   return w;
 }
@@ -236,6 +243,7 @@ struct Model {
   float *params, *grads, *m, *v;
   char* ws;
   std::vector<AdamChunk> chunks;
+  std::vector<InitSeg> init_segs;
   std::vector<TransposeJob> tjobs;
   bool have_fwd = false, have_targets = false;
   int B = 0, T = 0;
@@ -272,7 +280,8 @@ int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace
 }
 
 int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, float* adam_m,
-             float* adam_v, void* workspace, const float* init_params, void* stream) {
+             float* adam_v, void* workspace, const float* init_params, uint64_t seed,
+             void* stream) {
   if (!out) return fail(GPT_EINVAL, "null output handle");
   *out = nullptr;
   int rc = validate(cfg);
@@ -280,6 +289,7 @@ int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, fl
   if (!params || !grads || !adam_m || !adam_v || !workspace)
     return fail(GPT_EINVAL, "null device buffer");
   if ((uintptr_t)workspace & 255) return fail(GPT_EINVAL, "workspace must be 256-byte aligned");
+  if ((uintptr_t)params & 15) return fail(GPT_EINVAL, "params must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   Model* h = new Model;
   h->cfg = *cfg;
@@ -290,10 +300,17 @@ int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, fl
   h->m = adam_m;
   h->v = adam_v;
   h->ws = (char*)workspace;
+  const float res_std = (float)(0.02 / sqrt(2.0 * cfg->n_layer));
   for (size_t i = 0; i < h->po.tensors.size(); ++i) {
     const int64_t o = h->po.tensors[i].first, n = h->po.tensors[i].second;
-    for (int64_t c = 0; c < n; c += kChunk)
-      h->chunks.push_back({o + c, (int32_t)std::min<int64_t>(kChunk, n - c), h->po.is2d[i]});
+    const int k = h->po.init[i];
+    const float sd = k == INIT_STD ? 0.02f : k == INIT_RESID ? res_std : 0.f;
+    const float val = k == INIT_ONE ? 1.f : 0.f;
+    for (int64_t c = 0; c < n; c += kChunk) {
+      const int32_t cnt = (int32_t)std::min<int64_t>(kChunk, n - c);
+      h->chunks.push_back({o + c, cnt, h->po.is2d[i]});
+      h->init_segs.push_back({o + c, cnt, 0, sd, val});
+    }
   }
   if (h->h16()) {
     const int64_t d = cfg->n_embd;
@@ -324,6 +341,9 @@ int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, fl
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->ws + h->wo.chunks, h->chunks.data(), h->chunks.size() * sizeof(AdamChunk),
                        hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !init_params)
+    e = hipMemcpyAsync(h->ws + h->wo.init_tab, h->init_segs.data(),
+                       h->init_segs.size() * sizeof(InitSeg), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && h->h16()) {
     e = hipMemcpyAsync(h->ws + h->wo.tjobs, h->tjobs.data(), h->tjobs.size() * sizeof(TransposeJob),
                        hipMemcpyHostToDevice, s);
@@ -336,6 +356,14 @@ int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, fl
     gpt_error_text() = hipGetErrorString(e);
     delete h;
     return GPT_EHIP;
+  }
+  if (!init_params) {
+    rc = init_params_launch(params, h->at<InitSeg>(h->wo.init_tab), (int)h->init_segs.size(),
+                            seed, s);
+    if (rc) {
+      delete h;
+      return map_rc(rc);
+    }
   }
   if (h->h16()) {
     rc = to_h16_launch(params, h->at<h16_t>(h->wo.shadow), h->po.total, s);
@@ -464,7 +492,7 @@ int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32
                          (size_t)w.vi * h->es(), (size_t)c.padded_vocab * h->es(), M,
                          hipMemcpyDeviceToDevice, s));
   if (targets) {
-    CK(count_valid_launch(targets, M, h->at<int>(w.nvalid), s));
+    CK(count_valid_launch(targets, M, c.vocab_size, h->at<int>(w.nvalid), h->at<int>(w.flags), s));
     CK(cross_entropy_launch(bf, h->at(w.logits), targets, h->at<float>(w.row_loss),
                             h->at<int>(w.nvalid), loss_scale, dscale, M, c.vocab_size, (int)w.vi,
                             s));
@@ -501,7 +529,7 @@ int gpt_eval_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t 
   e.ldc = (int)w.vi;
   CK(gemm_launch(bf, true, true, EPI_ACT, h->at(w.lnf), d, h->W(p.wte), d, M, c.padded_vocab, d,
                  d, d, e, s));
-  CK(count_valid_launch(targets, M, h->at<int>(w.nvalid), s));
+  CK(count_valid_launch(targets, M, c.vocab_size, h->at<int>(w.nvalid), h->at<int>(w.flags), s));
   CK(cross_entropy_launch(bf, h->at(w.logits), targets, h->at<float>(w.row_loss),
                           h->at<int>(w.nvalid), 1.f, nullptr, M, c.vocab_size, (int)w.vi, s, 0));
   CK(loss_finalize_launch(h->at<float>(w.row_loss), M, h->at<int>(w.nvalid), loss_out, s));
@@ -886,6 +914,48 @@ int gpt_op_linear(int32_t h16, const void* A, const void* B, const float* bias, 
   return GPT_OK;
 }
 
+// MLP expansion forward (fc + bias + tanh-GELU): u = A W^T + bias;
+// dgelu = gelu'(u), g = gelu(u), both in the activation type
+int gpt_op_linear_gelu(int32_t h16, const void* A, const void* W, const float* bias, void* dgelu,
+                       void* g, int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!A || !W || !dgelu || !g || M < 0 || N < 0 || K < 1)
+    return fail(GPT_EINVAL, "bad linear_gelu arguments");
+  GemmEpiArgs e;
+  e.out = dgelu;
+  e.out2 = g;
+  e.bias = bias;
+  e.ldc = N;
+  CK(gemm_launch(h16 != 0, true, true, EPI_GELU, A, K, W, K, M, N, K, K, K, e,
+                 (hipStream_t)stream));
+  return GPT_OK;
+}
+
+// Column-sum scratch of the GELU-derivative product: one fp32 row per 128 rows
+int64_t op_gelu_bwd_scratch_bytes(int64_t M, int64_t N) { return cdiv(M, 128) * N * 4; }
+
+// MLP projection backward into the expansion: du = (dY Wt^T) * dgelu and,
+// when dbias is set, dbias (+)= colsum(du) through the fp32 scratch
+int gpt_op_linear_gelu_bwd(int32_t h16, const void* dY, const void* Wt, const void* dgelu,
+                           void* du, float* dbias, int32_t accumulate_bias, int32_t M, int32_t N,
+                           int32_t K, float* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dY || !Wt || !dgelu || !du || M < 0 || N < 1 || K < 1)
+    return fail(GPT_EINVAL, "bad linear_gelu_bwd arguments");
+  if (dbias && (!workspace || workspace_bytes < op_gelu_bwd_scratch_bytes(M, N)))
+    return fail(GPT_EINVAL, "linear_gelu_bwd: workspace below ceil(M/128)*N*4 bytes");
+  GemmEpiArgs e;
+  e.out = du;
+  e.aux = dgelu;
+  e.ldc = N;
+  if (dbias) {
+    e.cs_part = workspace;
+    e.cs_out = dbias;
+    e.cs_beta = accumulate_bias ? 1 : 0;
+  }
+  CK(gemm_launch(h16 != 0, true, true, EPI_GELU_BWD, dY, K, Wt, K, M, N, K, K, K, e,
+                 (hipStream_t)stream));
+  return GPT_OK;
+}
+
 int gpt_op_linear_dw(int32_t h16, const void* dY, const void* X, float* dW, int32_t accumulate,
                      int32_t M, int32_t N, int32_t K, float* workspace, int64_t workspace_bytes,
                      void* stream) {
@@ -951,7 +1021,7 @@ int gpt_op_cross_entropy(int32_t h16, void* logits, const int32_t* targets, floa
   if (!logits || !targets || !loss || !row_loss || !n_valid || N < 1 || V < 1 || ldv < V)
     return fail(GPT_EINVAL, "bad cross-entropy arguments");
   hipStream_t s = (hipStream_t)stream;
-  CK(count_valid_launch(targets, N, n_valid, s));
+  CK(count_valid_launch(targets, N, V, n_valid, nullptr, s));
   CK(cross_entropy_launch(h16 != 0, logits, targets, row_loss, n_valid, loss_scale, nullptr, N, V,
                           ldv, s));
   CK(loss_finalize_launch(row_loss, N, n_valid, loss, s));

@@ -18,6 +18,19 @@ struct AdamChunk {
 
 // one matrix of the transposed weight copy: src [rows][cols] (elements from
 // the start of the 16-bit weights) -> dst [cols][ld] (ld >= rows)
+// One piece (at most 8192 elements, a multiple of 4, starting at a multiple
+// of 4) of one parameter tensor for the initialisation from a seed:
+// std > 0 draws N(0, std^2), otherwise every element is `value`.
+struct InitSeg {
+  int64_t offset;
+  int32_t count;
+  int32_t pad;
+  float std;
+  float value;
+};
+int init_params_launch(float* params, const InitSeg* segs, int nsegs, uint64_t seed,
+                       hipStream_t s);
+
 struct TransposeJob {
   int64_t src, dst;
   int32_t rows, cols, ld, tile_begin;
@@ -57,7 +70,9 @@ int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, flo
 int dropout_rows_launch(const float* x, float* y, int64_t M, int C, Drop dr, hipStream_t s);
 int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int Tn,
                      int block_size, int C, int Vp, int beta_wpe, hipStream_t s);
-int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s);
+// n_valid = count of targets in [0, V); a target outside [-1, V) sets bit 2
+// of *flags (when flags is not null) and counts as ignored
+int count_valid_launch(const int32_t* tgt, int N, int V, int* out, int* flags, hipStream_t s);
 // dscale (optional, device): the gradient is further multiplied by *dscale;
 // write_grad = 0: only the row losses (the logits are left as they are)
 int cross_entropy_launch(bool h16, void* logits, const int32_t* tgt, float* row_loss,

@@ -1,5 +1,7 @@
-// Embedding, fused masked softmax cross-entropy, bias-gradient column sums.
+// Embedding, fused masked softmax cross-entropy, bias-gradient column sums,
+// parameter initialisation from a seed.
 #include "common.h"
+#include "kernels.h"
 
 namespace HALF_NS {
 
@@ -154,28 +156,38 @@ __global__ void embed_bwd_wpe_kernel(const float* __restrict__ dx, float* __rest
 }
 
 // ---------------------------------------------------------------- cross-entropy
-// count of targets >= 0 (ignore_index = -1, "nanoGPT" Part IV Stage 4)
+// count of targets in [0, V) (ignore_index = -1, "nanoGPT" Part IV Stage 4).
+// A target outside [-1, V) names no class: it is counted as ignored (the
+// cross-entropy kernels give its row zero loss and zero gradient too) and
+// raises bit 2 of flags.
 // One workgroup of 1024 threads: 16-byte loads where the targets are 16-byte
 // aligned, so each thread has only a few loads in flight instead of a long
 // chain of dependent round trips.
 #define RED_THREADS 1024
+__device__ __forceinline__ int valid_target(int y, int V, int& bad) {
+  bad |= (y < -1) | (y >= V);
+  return (y >= 0) & (y < V);
+}
 __global__ __launch_bounds__(RED_THREADS) void count_valid_kernel(const int32_t* __restrict__ tgt, int N,
-                                                                  int* __restrict__ out) {
+                                                                  int V, int* __restrict__ out,
+                                                                  int* __restrict__ flags) {
   __shared__ int red[RED_THREADS / 64];
-  int c = 0;
+  int c = 0, bad = 0;
   int done = 0;
   if (((uintptr_t)tgt & 15) == 0) {
     const int n4 = N >> 2;
 #pragma unroll 4
     for (int i = threadIdx.x; i < n4; i += RED_THREADS) {
       const int4 v = ((const int4*)tgt)[i];
-      c += (v.x >= 0) + (v.y >= 0) + (v.z >= 0) + (v.w >= 0);
+      c += valid_target(v.x, V, bad) + valid_target(v.y, V, bad) + valid_target(v.z, V, bad) +
+           valid_target(v.w, V, bad);
     }
     done = n4 << 2;
   }
-  for (int i = done + threadIdx.x; i < N; i += RED_THREADS) c += tgt[i] >= 0;
+  for (int i = done + threadIdx.x; i < N; i += RED_THREADS) c += valid_target(tgt[i], V, bad);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if (bad && flags) atomicOr(flags, 2);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -282,7 +294,7 @@ __global__ __launch_bounds__(CE_BF_THREADS, 4) void ce_h16_kernel(
   const float lse = M + __logf(S);
   const int nv = *n_valid;
   const float scale =
-      (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
+      (has_y && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
   if (!write_grad) {  // the loss alone (evaluation): the logits stay as they are
     if (threadIdx.x == 0) row_loss[row] = has_y ? lse - zy : 0.f;
     return;
@@ -344,7 +356,7 @@ __global__ __launch_bounds__(256) void ce_h16_small_kernel(
   if (!write_grad || !mine) return;
   const int nv = *n_valid;
   const float scale =
-      (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
+      (has_y && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
   float d[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -370,17 +382,18 @@ __global__ __launch_bounds__(CE_THREADS) void ce_f32_kernel(
   const float lse = mx + logf(s);
   const int y = tgt[row];
   const int nv = *n_valid;
+  const bool has_y = y >= 0 && y < V;
   const float scale =
-      (y >= 0 && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
-  const float zy = (y >= 0 && y < V) ? z[y] : 0.f;
+      (has_y && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
+  const float zy = has_y ? z[y] : 0.f;
   if (!write_grad) {
-    if (threadIdx.x == 0) row_loss[row] = (y >= 0 && y < V) ? lse - zy : 0.f;
+    if (threadIdx.x == 0) row_loss[row] = has_y ? lse - zy : 0.f;
     return;
   }
   __syncthreads();
   for (int c = threadIdx.x; c < ldv; c += CE_THREADS)
     z[c] = c < V ? scale * (expf(z[c] - lse) - (c == y ? 1.f : 0.f)) : 0.f;
-  if (threadIdx.x == 0) row_loss[row] = (y >= 0 && y < V) ? lse - zy : 0.f;
+  if (threadIdx.x == 0) row_loss[row] = has_y ? lse - zy : 0.f;
 }
 
 // loss = sum(row_loss) / n_valid, single workgroup, fixed order.
@@ -451,9 +464,61 @@ __global__ __launch_bounds__(256) void colsum_part_kernel(const T* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- initialisation
+// Parameters drawn on the device from a seed ("Let's reproduce GPT-2 (124M)",
+// chapter "Model Initialization"; "nanoGPT" Part V Deep dive 1): every
+// Linear weight and both embedding tables N(0, 0.02^2), the two projections
+// per block that write into the residual stream N(0, (0.02 / sqrt(2 L))^2),
+// biases 0, LayerNorm gains 1 and shifts 0.  The table of pieces carries the
+// standard deviation or the constant of each piece.
+// Element i takes normal number i % 4 of Philox4x32-10 at counter
+// {i / 4 (low, high words), 'INIT', 0} under the 64-bit seed: the two pairs of
+// 32-bit words become two pairs of normals by the Box-Muller transform
+// (Box and Muller, 1958): r = sqrt(-2 ln u1), (r cos 2 pi u2, r sin 2 pi u2)
+// with u1 in (0, 1), u2 in [0, 1).  The values depend only on the element's
+// position and the seed, not on how the table cuts the tensors.
+__device__ __forceinline__ void box_muller(uint32_t a, uint32_t b, float& n0, float& n1) {
+  const float u1 = ((float)(a >> 8) + 0.5f) * (1.0f / 16777216.0f);  // (0, 1)
+  const float u2 = (float)(b >> 8) * (1.0f / 16777216.0f);           // [0, 1)
+  const float r = sqrtf(-2.0f * logf(u1));
+  float sn, cs;
+  sincosf(6.283185307179586f * u2, &sn, &cs);
+  n0 = r * cs;
+  n1 = r * sn;
+}
+
+__global__ __launch_bounds__(256) void init_params_kernel(float* __restrict__ p,
+                                                          const InitSeg* __restrict__ segs,
+                                                          uint32_t k0, uint32_t k1) {
+  const InitSeg sg = segs[blockIdx.x];
+  for (int j = 4 * (int)threadIdx.x; j < sg.count; j += 4 * 256) {
+    const int64_t i = sg.offset + j;
+    float4 o;
+    if (sg.std > 0.f) {
+      const uint64_t q = (uint64_t)i >> 2;
+      const uint4 w = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), 0x494E4954u, 0u, k0, k1);
+      float n0, n1, n2, n3;
+      box_muller(w.x, w.y, n0, n1);
+      box_muller(w.z, w.w, n2, n3);
+      o = make_float4(n0 * sg.std, n1 * sg.std, n2 * sg.std, n3 * sg.std);
+    } else {
+      o = make_float4(sg.value, sg.value, sg.value, sg.value);
+    }
+    *(float4*)(p + i) = o;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
                            hipStream_t s);
+
+int init_params_launch(float* params, const InitSeg* segs, int nsegs, uint64_t seed,
+                       hipStream_t s) {
+  if (nsegs <= 0) return 0;
+  hipLaunchKernelGGL(init_params_kernel, dim3(nsegs), dim3(256), 0, s, params, segs,
+                     (uint32_t)seed, (uint32_t)(seed >> 32));
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 int embed_fwd_launch(const int32_t* idx, const float* wte, const float* wpe, float* x, int M,
                      int Tn, int C, int Vp, int* flags, hipStream_t s, Drop dr) {
@@ -489,8 +554,8 @@ int embed_bwd_launch(const int32_t* idx, const float* dx, float* dwte, float* dw
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int count_valid_launch(const int32_t* tgt, int N, int* out, hipStream_t s) {
-  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(RED_THREADS), 0, s, tgt, N, out);
+int count_valid_launch(const int32_t* tgt, int N, int V, int* out, int* flags, hipStream_t s) {
+  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(RED_THREADS), 0, s, tgt, N, V, out, flags);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
