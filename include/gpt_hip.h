@@ -344,6 +344,21 @@ int gpt_op_linear_gelu_bwd(int32_t dtype, const void* dY, const void* Wt, const 
                            void* du, float* dbias, int32_t accumulate_bias, int32_t M, int32_t N,
                            int32_t K, float* workspace, int64_t workspace_bytes, void* stream);
 
+/* gpt_op_linear_gelu_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the column-sum scratch taken
+ * from a 4 MiB device array the library holds per device until the process
+ * ends, so the call allocates nothing and needs no workspace.  The array of
+ * the calling thread's current device is used (the device of `stream`).
+ * With dbias set, ceil(M/128) * N * 4 must not exceed 4 MiB (GPT_EINVAL,
+ * nothing enqueued).  Calls that overlap on one device share the array and
+ * race: serialise them (one stream, or events).  Nothing in the array needs
+ * to start at zero; it keeps the last call's partials. */
+int gpt_op_linear_gelu_bwd_noalloc(int32_t dtype, const void* dY, const void* Wt,
+                                   const void* dgelu, void* du, float* dbias,
+                                   int32_t accumulate_bias, int32_t M, int32_t N, int32_t K,
+                                   void* stream);
+
 /* dW (+)= dY^T X: dY act [M][N], X act [M][K], dW fp32 [N][K];
  * accumulate != 0 adds to dW.  The weight gradient of a Linear layer.
  * workspace: optional device fp32 scratch of workspace_bytes (NULL: none);

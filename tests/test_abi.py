@@ -179,3 +179,16 @@ def test_kv_cache_bytes_layout_plus_slack():
             assert bd.lib.gpt_kv_cache_bytes(ctypes.byref(c), B, L) == want
         assert bd.lib.gpt_kv_cache_bytes(ctypes.byref(c), 0, 8) == -1
         assert bd.lib.gpt_kv_cache_bytes(ctypes.byref(c), 1, 0) == -1
+
+
+def test_noalloc_entry_point_refuses_sizes_beyond_its_scratch_without_a_device():
+    """ceil(M/128) * N * 4 bytes of column sums above the 4 MiB scratch are
+    refused on the host before any HIP call; the pointers are never read."""
+    lib = bd.lib
+    fake = ctypes.c_void_p(1 << 20)
+    rc = lib.gpt_op_linear_gelu_bwd_noalloc(bd.GPT_BF16, fake, fake, fake, fake, fake, 0,
+                                            128 * 1025, 1024, 64, None)
+    assert rc == bd.GPT_EINVAL
+    assert b"4 MiB" in lib.gpt_strerror(rc)
+    assert lib.gpt_op_linear_gelu_bwd_noalloc(9, fake, fake, fake, fake, fake, 0, 128, 8, 8,
+                                              None) == bd.GPT_EINVAL

@@ -60,6 +60,7 @@ _SIGS = {
     "gpt_op_linear": [_i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
     "gpt_op_linear_gelu": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p],
     "gpt_op_linear_gelu_bwd": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
+    "gpt_op_linear_gelu_bwd_noalloc": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
     "gpt_op_linear_dw": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
     "gpt_op_linear_dx": [_i32, _p, _p, _p, _i32, _i32, _i32, _p],
     "gpt_op_attention_fwd": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
@@ -377,6 +378,19 @@ def op_linear_gelu_bwd(dY, Wt, dgelu, dbias=None, accumulate_bias=False, workspa
     check(lib.gpt_op_linear_gelu_bwd(_bf(dY), _ptr(dY), _ptr(Wt), _ptr(dgelu), _ptr(du), _ptr(dbias),
                                      int(accumulate_bias), M, N, K, _ptr(workspace), wsb,
                                      _stream()), "gpt_op_linear_gelu_bwd")
+    return du
+
+
+def op_linear_gelu_bwd_noalloc(dY, Wt, dgelu, dbias=None, accumulate_bias=False):
+    """gpt_op_linear_gelu_bwd_noalloc: as op_linear_gelu_bwd, with the library's
+    own device scratch in place of a workspace."""
+    import torch
+    M, K = dY.shape
+    N = Wt.shape[0]
+    du = torch.empty((M, N), dtype=dY.dtype, device=dY.device)
+    check(lib.gpt_op_linear_gelu_bwd_noalloc(_bf(dY), _ptr(dY), _ptr(Wt), _ptr(dgelu), _ptr(du),
+                                             _ptr(dbias), int(accumulate_bias), M, N, K,
+                                             _stream()), "gpt_op_linear_gelu_bwd_noalloc")
     return du
 
 

@@ -4,9 +4,19 @@
 // share no state; a handle records which one created it.
 #include "api_impl.h"
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
 #include <string>
+
+// Device scratch of gpt_op_linear_gelu_bwd_noalloc: the column-sum partials
+// of its bias gradient, for callers that cannot allocate.  Each device holds
+// its own copy until the process ends; its address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is handed to kernels.
+static constexpr int64_t kNoAllocScratchBytes = 4 << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / 4];
 
 std::string& gpt_error_text() {
   static thread_local std::string msg;
@@ -32,6 +42,36 @@ int bad_dtype() {
   return GPT_EINVAL;
 }
 bool dtype_ok(int32_t dtype) { return dtype == GPT_FP32 || dtype == GPT_BF16 || dtype == GPT_FP16; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch's device address on the calling thread's current device
+int current_device_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    gpt_error_text() = hipGetErrorString(e);
+    return GPT_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    gpt_error_text() = "device ordinal beyond the scratch table";
+    return GPT_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      gpt_error_text() = e != hipSuccess ? hipGetErrorString(e) : "null scratch address";
+      return GPT_EHIP;
+    }
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPT_OK;
+}
 }  // namespace
 
 #define OP(name, dtype, ...)                                                            \
@@ -223,6 +263,25 @@ int gpt_op_linear_gelu_bwd(int32_t dtype, const void* dY, const void* Wt, const 
                            int32_t K, float* workspace, int64_t workspace_bytes, void* stream) {
   return OP(gpt_op_linear_gelu_bwd, dtype, dY, Wt, dgelu, du, dbias, accumulate_bias, M, N, K,
             workspace, workspace_bytes, stream);
+}
+
+int gpt_op_linear_gelu_bwd_noalloc(int32_t dtype, const void* dY, const void* Wt,
+                                   const void* dgelu, void* du, float* dbias,
+                                   int32_t accumulate_bias, int32_t M, int32_t N, int32_t K,
+                                   void* stream) {
+  if (!dtype_ok(dtype)) return bad_dtype();
+  float* ws = nullptr;
+  if (dbias && M > 0 && N > 0) {
+    if (((int64_t)M + 127) / 128 * (int64_t)N * 4 > kNoAllocScratchBytes) {
+      gpt_error_text() =
+          "linear_gelu_bwd_noalloc: ceil(M/128) * N * 4 bytes of column sums exceed its 4 MiB "
+          "scratch";
+      return GPT_EINVAL;
+    }
+    if (int rc = current_device_scratch(&ws)) return rc;
+  }
+  return OP(gpt_op_linear_gelu_bwd, dtype, dY, Wt, dgelu, du, dbias, accumulate_bias, M, N, K, ws,
+            ws ? kNoAllocScratchBytes : 0, stream);
 }
 
 int gpt_op_linear_dw(int32_t dtype, const void* dY, const void* X, float* dW, int32_t accumulate,
