@@ -335,6 +335,9 @@ def main():
                     help="train with dropout P (the pretraining configuration uses 0)")
     ap.add_argument("--fp16", action="store_true",
                     help="IEEE half precision with dynamic loss scaling instead of bf16")
+    ap.add_argument("--fused-ce", type=int, default=None, choices=[0, 1], metavar="0|1",
+                    help="GPT_OPT_FUSED_HEAD_CE: the cross-entropy fused into the tied head "
+                         "(default: the library's default)")
     ap.add_argument("--probe", default=None, metavar="GROUP",
                     help="only launch one step's products of GROUP and a calibration copy "
                          "(counter runs)")
@@ -362,6 +365,9 @@ def main():
     params = synth.init_params(dims, seed=1337)
     model = bd.GPT(dims, bd.GPT_FP16 if args.fp16 else bd.GPT_BF16, max_batch=B,
                    init_params=params)
+    if args.fused_ce is not None:
+        model.set_option(bd.GPT_OPT_FUSED_HEAD_CE, args.fused_ce)
+    model_fused = model.get_option(bd.GPT_OPT_FUSED_HEAD_CE) and not args.fp16
     nb = 4
     batches = []
     for i in range(nb):
@@ -453,6 +459,7 @@ def main():
                                f"{dims['padded_vocab']} (pad masked), B={B}, T={T}"
                                + (f", {K} micro-batches per optimizer step" if K > 1 else ""),
                    "global_batch": B * K, "seq_len": T,
+                   "fused_head_ce": bool(model_fused),
                    "flops_per_step": fpt * tokens, "loss": round(loss, 4), "grad_norm": round(norm, 4)},
         **({"loss_scaler": dict(zip(("scale", "growth_tracker", "updates", "last_skipped"), scaler)),
             "optimizer_steps_run": args.warmup + args.steps} if scaler else {}),

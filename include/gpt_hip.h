@@ -53,9 +53,14 @@ enum { GPT_FP32 = 0, GPT_BF16 = 1, GPT_FP16 = 2 };
 enum {
   GPT_FLAG_BAD_TOKEN = 1,  /* an input id was outside [0, padded_vocab); its
                               embedding row was taken as zero */
-  GPT_FLAG_BAD_TARGET = 2  /* a target was outside [-1, vocab_size); it was
+  GPT_FLAG_BAD_TARGET = 2, /* a target was outside [-1, vocab_size); it was
                               treated as ignored (-1): left out of the count of
                               valid targets, zero loss and zero gradient */
+  GPT_FLAG_HEAD_RANGE = 4  /* fused head + cross-entropy (GPT_OPT_FUSED_HEAD_CE):
+                              a row's sum of exp(logit) left [1e-28, 1e28], the
+                              range its 16-bit exp(logit) values carry exactly
+                              (logits beyond about +-64); that step's loss and
+                              gradients are not valid */
 };
 
 typedef struct {
@@ -296,6 +301,27 @@ int gpt_decode_step(gpt_model* h, const int32_t* tok, int32_t B, int32_t pos, vo
  * GPT_EUNSUPPORTED (V above 57344). */
 int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float temperature,
                int32_t top_k, const float* u, int32_t* tok_out, void* stream);
+
+/* Options of a handle (gpt_set_option).
+ * GPT_OPT_FUSED_HEAD_CE (value 0 or 1, default 1): fuse the cross-entropy into the tied
+ * LM head, so that no pass over the logits follows the head's product
+ * ("Let's reproduce GPT-2 (124M)", chapters "Cross Entropy Loss" and "Flash
+ * Attention": do not make extra passes over a large tensor).  The head's
+ * product stores p = exp(z) in place of the logits z and, in its epilogue,
+ * each row's sums of p; one small pass per row takes S = sum of p, the loss
+ * log S - z_y, the factor r = loss_scale / (n_valid S), r times the final
+ * LayerNorm's output, and writes p_y - S at the target's column.  The logit
+ * gradient is then r times a stored row: the head's weight-gradient product
+ * takes the scaled LayerNorm output as its other operand, and its
+ * input-gradient product multiplies its rows by r in the epilogue.
+ * Applies to gpt_forward_loss with targets and without logits_out in
+ * GPT_BF16 mode (other modes and calls keep the separate pass).  It carries
+ * logits within about +-64 (GPT_FLAG_HEAD_RANGE otherwise).
+ * Errors: GPT_EINVAL (null handle, unknown option or value). */
+enum { GPT_OPT_FUSED_HEAD_CE = 1 };
+int gpt_set_option(gpt_model* h, int32_t option, int32_t value);
+/* The current value of an option into *value.  Errors: GPT_EINVAL. */
+int gpt_get_option(gpt_model* h, int32_t option, int32_t* value);
 
 /* Synchronise `stream`, return the device flags (GPT_FLAG_*) raised since the
  * last call in *flags, and clear them. */

@@ -192,3 +192,10 @@ def test_noalloc_entry_point_refuses_sizes_beyond_its_scratch_without_a_device()
     assert b"4 MiB" in lib.gpt_strerror(rc)
     assert lib.gpt_op_linear_gelu_bwd_noalloc(9, fake, fake, fake, fake, fake, 0, 128, 8, 8,
                                               None) == bd.GPT_EINVAL
+
+
+def test_set_option_checks_its_arguments_without_a_device():
+    lib = bd.lib
+    assert lib.gpt_set_option(None, bd.GPT_OPT_FUSED_HEAD_CE, 1) == bd.GPT_EINVAL
+    v = ctypes.c_int32(7)
+    assert lib.gpt_get_option(None, bd.GPT_OPT_FUSED_HEAD_CE, ctypes.byref(v)) == bd.GPT_EINVAL

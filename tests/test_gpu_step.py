@@ -283,6 +283,14 @@ def test_full_batch_gradients_match_oracle(name, batch, override):
     params = synth.init_params(dims, seed=1337)
     idx, tgt = synth.tokens(dims, seed=1338, batch=batch, T=T)
     m = bd.GPT(dims, bd.GPT_BF16, max_batch=batch, init_params=params)
+    # the fused head + cross-entropy first (compared after the oracle is in)
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, 1)
+    loss_f, _ = m.forward(*dev_tokens(idx, tgt))
+    m.backward()
+    torch.cuda.synchronize()
+    fused_loss, fused_g = float(loss_f.item()), to_np(m.grads)
+    assert m.read_flags() == 0
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, 0)
     loss, _ = m.forward(*dev_tokens(idx, tgt))
     m.backward()
     torch.cuda.synchronize()
@@ -304,9 +312,74 @@ def test_full_batch_gradients_match_oracle(name, batch, override):
     assert max_rel(got_p - p0, ref_p - p0) <= 1e-3
     ref_loss, ref_g = oracle_jobs.finish_batch_grads(handle)
     assert abs(got_loss - ref_loss) <= 2e-2, (got_loss, ref_loss)
+    assert abs(fused_loss - ref_loss) <= 2e-2, (fused_loss, ref_loss)
+    worst_f = check_grads(dims, fused_g, ref_g, min_cos=0.995)
+    print(f"fused head+CE: loss {fused_loss:.5f}; lowest cosines {worst_f}", flush=True)
     worst = check_grads(dims, got_g, ref_g, min_cos=0.995)
     print(f"loss gpu {got_loss:.5f} oracle {ref_loss:.5f}; norm gpu {got_norm:.5f} "
           f"oracle {O.grad_norm(ref_g):.5f}; lowest cosines {worst}", flush=True)
+
+
+@pytest.mark.parametrize("batch,T,seed,mask", [(2, 1024, 21, False), (3, 200, 22, True)])
+def test_fused_head_cross_entropy_step_parity(batch, T, seed, mask):
+    """The tied head with the cross-entropy fused (GPT_OPT_FUSED_HEAD_CE:
+    exp(z) and row sums in the head's epilogue, the softmax factor and the
+    one-hot term folded into the backward products) against the oracle: loss
+    within 2e-2, per-tensor cosine >= 0.995; and against the separate
+    cross-entropy pass on the same inputs.  The ragged case has ignored and
+    out-of-range targets."""
+    dims = synth.WORKLOADS["gpt2"]
+    case(f"gpt2 bf16 fused head+CE B={batch} T={T} ignored targets={mask}")
+    params = synth.init_params(dims, seed=1337 + seed)
+    idx, tgt = synth.tokens(dims, seed=1338 + seed, batch=batch, T=T)
+    if mask:
+        tgt[0, :7] = -1
+        tgt[2, 100] = -1
+        tgt[1, 50] = 50300  # in [V, Vp): ignored, flagged
+    ref_tgt = np.where(tgt >= dims["vocab_size"], -1, tgt)
+    ref_loss, ref_g, _ = O.loss_and_grads(params, idx, ref_tgt, ocfg(dims))
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=batch, init_params=params)
+    di, dt = dev_tokens(idx, tgt)
+    loss, _ = m.forward(di, dt)
+    m.backward()
+    torch.cuda.synchronize()
+    sep_loss, sep_g = float(loss.item()), to_np(m.grads)
+    m.read_flags()
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, 1)
+    loss, _ = m.forward(di, dt)
+    m.backward()
+    torch.cuda.synchronize()
+    got_loss, got_g = float(loss.item()), to_np(m.grads)
+    assert m.read_flags() == (bd.GPT_FLAG_BAD_TARGET if mask else 0)
+    assert abs(got_loss - ref_loss) <= 2e-2, (got_loss, ref_loss)
+    worst = check_grads(dims, got_g, ref_g, min_cos=0.995)
+    assert abs(got_loss - sep_loss) <= 2e-3, (got_loss, sep_loss)
+    check_grads(dims, got_g, sep_g, min_cos=0.999)
+    print(f"fused loss {got_loss:.5f} separate {sep_loss:.5f} oracle {ref_loss:.5f}; "
+          f"lowest cosines {worst}", flush=True)
+    m.close()
+
+
+def test_fused_head_cross_entropy_flags_logits_out_of_range():
+    """Logits far beyond +-64 (a final LayerNorm gain of 400) leave the range
+    the fused head's 16-bit exp(z) carries: the flag is raised (and nothing
+    faults); the separate pass has no such limit."""
+    dims = synth.WORKLOADS["gpt2"]
+    case("gpt2 bf16 fused head+CE out-of-range logits flag")
+    params = synth.init_params(dims, seed=1361)
+    off, shape = synth.tensor_offsets(dims)["lnf.w"]
+    params[off:off + int(np.prod(shape))] = 400.0
+    idx, tgt = synth.tokens(dims, seed=1362, batch=1, T=64)
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=1, init_params=params)
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, 1)
+    m.forward(*dev_tokens(idx, tgt))
+    assert m.read_flags() & bd.GPT_FLAG_HEAD_RANGE
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, 0)
+    loss, _ = m.forward(*dev_tokens(idx, tgt))
+    torch.cuda.synchronize()
+    assert math.isfinite(float(loss.item()))
+    assert m.read_flags() == 0
+    m.close()
 
 
 def test_large_finite_gradients_keep_a_finite_norm():

@@ -29,6 +29,8 @@ GPT_OK, GPT_EINVAL, GPT_ESEQLEN, GPT_ESTATE, GPT_EHIP, GPT_EUNSUPPORTED = 0, -1,
 GPT_FP32, GPT_BF16, GPT_FP16 = 0, 1, 2
 GPT_FLAG_BAD_TOKEN = 1
 GPT_FLAG_BAD_TARGET = 2
+GPT_FLAG_HEAD_RANGE = 4
+GPT_OPT_FUSED_HEAD_CE = 1
 
 
 class gpt_config(ctypes.Structure):
@@ -57,6 +59,8 @@ _SIGS = {
     "gpt_eval_loss": [_p, _p, _p, _i32, _i32, _p, _p],
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
     "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
+    "gpt_set_option": [_p, _i32, _i32],
+    "gpt_get_option": [_p, _i32, ctypes.POINTER(_i32)],
     "gpt_op_linear": [_i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
     "gpt_op_linear_gelu": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p],
     "gpt_op_linear_gelu_bwd": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
@@ -294,6 +298,14 @@ class GPT:
             else:
                 logits = self.prefill(seq[:, -bs:].contiguous(), kv, max_len, logits)
         return seq, kept
+
+    def set_option(self, option: int, value: int) -> None:
+        check(lib.gpt_set_option(self.handle, option, value), "gpt_set_option")
+
+    def get_option(self, option: int) -> int:
+        v = _i32()
+        check(lib.gpt_get_option(self.handle, option, ctypes.byref(v)), "gpt_get_option")
+        return v.value
 
     def read_flags(self) -> int:
         f = _i32()

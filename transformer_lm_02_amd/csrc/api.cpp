@@ -206,6 +206,18 @@ int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float tem
   return b16::gpt_sample(logits, B, V, ldv, temperature, top_k, u, tok_out, stream);
 }
 
+int gpt_set_option(gpt_model* h, int32_t option, int32_t value) {
+  if (!h) return null_handle();
+  return h->fp16 ? f16::gpt_set_option((f16::Model*)h->impl, option, value)
+                 : b16::gpt_set_option((b16::Model*)h->impl, option, value);
+}
+
+int gpt_get_option(gpt_model* h, int32_t option, int32_t* value) {
+  if (!h) return null_handle();
+  return h->fp16 ? f16::gpt_get_option((f16::Model*)h->impl, option, value)
+                 : b16::gpt_get_option((b16::Model*)h->impl, option, value);
+}
+
 int gpt_read_flags(gpt_model* h, int32_t* flags, void* stream) {
   if (!h) return null_handle();
   return h->fp16 ? f16::gpt_read_flags((f16::Model*)h->impl, flags, stream)

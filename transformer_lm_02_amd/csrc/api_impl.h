@@ -41,6 +41,8 @@ std::string& gpt_error_text();
   int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float temperature,     \
                  int32_t top_k, const float* u, int32_t* tok_out, void* stream);                \
   int gpt_read_flags(Model* h, int32_t* flags, void* stream);                                   \
+  int gpt_set_option(Model* h, int32_t option, int32_t value);                                  \
+  int gpt_get_option(Model* h, int32_t option, int32_t* value);                                 \
   void gpt_destroy(Model* h);                                                                   \
   int gpt_op_linear(int32_t h16, const void* A, const void* B, const float* bias, void* C,      \
                     int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream);            \

@@ -15,7 +15,27 @@ enum GemmEpi {
                     // z the dropout multiplier of GemmEpiArgs::drop, 1 without dropout)
   EPI_GELU = 3,     // u = acc + bias[n]; out_act = gelu'(u); out2_act = gelu(u)
   EPI_GELU_BWD = 4, // out_act[m][n] = acc * aux_act[m][n]  (aux: the stored gelu'(u))
-  EPI_ACCUM = 5     // out_f32[m][n] = (beta ? out_f32[m][n] : 0) + acc
+  EPI_ACCUM = 5,    // out_f32[m][n] = (beta ? out_f32[m][n] : 0) + acc
+  EPI_HEAD = 6,     // tied head with the cross-entropy fused (see HeadEpi): out_act[m][n] =
+                    // exp(acc) for n < V, 0 for n >= V; plus row sums and the target logit
+  EPI_HEAD_DX = 7   // out_act[m][n] = r[m] acc  (see HeadEpi)
+};
+
+// Operands of the fused head + cross-entropy epilogues.  The forward stores
+// p~ = exp(z) (shift 0) instead of the logits z, part[m][n / 96] = sum of p~
+// over each block of 96 columns below V (fixed order, from the fp32 values)
+// and zy[m] = z at n = tgt[m] (when 0 <= tgt[m] < V).  A later pass takes the
+// row sum S, stores p~ - S at the target column and r[m] = sc[m] / S (sc the
+// row's loss scale, zero for an ignored row): the logit gradient
+// sc (softmax - onehot) is then r[m] times the stored row, which the
+// input-gradient product applies in its epilogue.
+struct HeadEpi {
+  const int32_t* tgt = nullptr;
+  float* part = nullptr;
+  float* zy = nullptr;
+  int V = 0;
+  int npart = 0;  // blocks of 96 columns per row: ceil(N / 96)
+  const float* r = nullptr;
 };
 
 // A column-sum finalize left for later: out[k][i] = (beta ? out[k][i] : 0)
@@ -48,6 +68,8 @@ struct GemmEpiArgs {
   ColsumJob* cs_defer = nullptr;
   // EPI_RESID: dropout of the branch output (element (m, n) of the site)
   Drop drop;
+  // EPI_HEAD, EPI_HEAD_DX
+  HeadEpi head;
 };
 
 // A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]; likewise B(n,k).

@@ -187,12 +187,14 @@ __device__ __forceinline__ Aux8 aux8(const GemmEpiArgs& e, int splitk, int m, in
       x.a = s[0];
       x.b = s[1];
     }
+  } else if constexpr (EPI == EPI_HEAD_DX) {
+    x.a.x = e.head.r[m];  // the row's softmax factor
   }
   return x;
 }
 template <int EPI>
 constexpr bool epi_reads_aux() {
-  return EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_ACCUM;
+  return EPI == EPI_RESID || EPI == EPI_GELU_BWD || EPI == EPI_ACCUM || EPI == EPI_HEAD_DX;
 }
 
 // 8 consecutive outputs of one row: epilogue and 16/32-byte stores
@@ -243,6 +245,10 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
                                                pack2h(gp[4], gp[5]), pack2h(gp[6], gp[7]));
     *(uint4*)((h16_t*)e.out2 + i) =
         make_uint4(pack2h(g[0], g[1]), pack2h(g[2], g[3]), pack2h(g[4], g[5]), pack2h(g[6], g[7]));
+  } else if constexpr (EPI == EPI_HEAD_DX) {
+    const float r = x.a.x;
+    *(uint4*)((h16_t*)e.out + i) = make_uint4(pack2h(r * v[0], r * v[1]), pack2h(r * v[2], r * v[3]),
+                                              pack2h(r * v[4], r * v[5]), pack2h(r * v[6], r * v[7]));
   } else {  // EPI_GELU_BWD: the 16-bit gelu'(u) values travel in x.a's bits
     const uint32_t w[4] = {__float_as_uint(x.a.x), __float_as_uint(x.a.y), __float_as_uint(x.a.z),
                            __float_as_uint(x.a.w)};
@@ -453,7 +459,43 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
         if (grow < p.M && gcol < p.N) epi8<EPI>(p.e, part, splitk, grow, gcol, v, bias8, x, csum);
       }
     };
-    if constexpr (epi_reads_aux<EPI>()) {
+    if constexpr (EPI == EPI_HEAD) {
+      // p~ = exp(z) below V (0 above), the target's z, and the sum of p~ over
+      // this wave's 96 columns of each row: the LPR lanes of a row add their
+      // sums in lane order
+      const int blk = (n0 + wn * WC) / 96;
+#pragma unroll 1
+      for (int it = 0; it < NIT; ++it) {
+        const int lr = it * RPI + my_r;
+        const int grow = grow0 + it * RPI;
+        float sum = 0.f;
+        if (lane_on && lr < 32 && grow < p.M && gcol < p.N) {
+          const float4 v0 = *(const float4*)(ep + lr * EP_PITCH + my_c);
+          const float4 v1 = *(const float4*)(ep + lr * EP_PITCH + my_c + 4);
+          const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          const int y = p.e.head.tgt[grow];
+          float e8[8], zy = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            e8[j] = gcol + j < p.e.head.V ? __expf(v[j]) : 0.f;
+            sum += e8[j];
+            zy = (gcol + j == y) ? v[j] : zy;
+          }
+          *(uint4*)((h16_t*)p.e.out + (int64_t)grow * p.e.ldc + gcol) =
+              make_uint4(pack2h(e8[0], e8[1]), pack2h(e8[2], e8[3]), pack2h(e8[4], e8[5]),
+                         pack2h(e8[6], e8[7]));
+          if (y >= gcol && y < gcol + 8 && y < p.e.head.V) p.e.head.zy[grow] = zy;
+        }
+        // the LPR = 12 lanes of a row (lanes b..b+11, b = 12 my_r) in a fixed
+        // tree: +6, +3, then +1 and +2 into lane b
+        static_assert(LPR == 12, "row sums assume 12 lanes a row");
+        float tot = sum + __shfl_down(sum, 6, 64);
+        tot += __shfl_down(tot, 3, 64);
+        tot = tot + __shfl_down(tot, 1, 64) + __shfl_down(tot, 2, 64);
+        if (lane_on && lr < 32 && grow < p.M && my_c == 0 && n0 + wn * WC < p.N)
+          p.e.head.part[(int64_t)grow * p.e.head.npart + blk] = tot;
+      }
+    } else if constexpr (epi_reads_aux<EPI>()) {
       // the auxiliary operands of PG row passes are loaded together, then
       // those passes run (PG = the whole slab where registers allow)
 #pragma unroll
@@ -588,8 +630,11 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
     return 0;
   } else {
     const int64_t t256 = cdiv(p.M, 256) * cdiv(p.N, 256);
-    if (t256 < 64) {  // small problem: smaller tiles keep more CUs busy
-      return run2<128, 128, AK, BKC, EPI, 4, 64>(p, s);
+    // the fused head's row sums are kept per 96 columns: tiles 192 wide
+    if constexpr (EPI != EPI_HEAD) {
+      if (t256 < 64) {  // small problem: smaller tiles keep more CUs busy
+        return run2<128, 128, AK, BKC, EPI, 4, 64>(p, s);
+      }
     }
     if constexpr (BKC) {
       if (cdiv(p.M, 256) * cdiv(p.N, 192) >= 1024) return run2<256, 192, AK, BKC, EPI, 2, BK, 2>(p, s);
@@ -610,6 +655,10 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
                  float* ws, int64_t ws_bytes, hipStream_t s) {
   if (K % 8 || lda % 8 || ldb % 8 || N % 8 || e.ldc % 8) return -5;
   if (e.cs_out && (epi != EPI_GELU_BWD || e.ldc != N || N % 4)) return -5;
+  if (epi == EPI_HEAD &&
+      (!e.head.tgt || !e.head.part || !e.head.zy || e.head.npart != (int)cdiv(N, 96)))
+    return -5;
+  if (epi == EPI_HEAD_DX && !e.head.r) return -5;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)e.out) & 15) return -5;
   if ((e.aux && ((uintptr_t)e.aux & 15)) || (e.out2 && ((uintptr_t)e.out2 & 15))) return -5;
   if (e.bias && ((uintptr_t)e.bias & 15)) return -5;
@@ -625,6 +674,8 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
   G2(true, true, EPI_RESID)
   G2(true, true, EPI_GELU)
   G2(true, true, EPI_GELU_BWD)
+  G2(true, true, EPI_HEAD)
+  G2(true, true, EPI_HEAD_DX)
   G2(true, false, EPI_ACT)
   G2(true, false, EPI_F32)
   G2(true, false, EPI_GELU_BWD)

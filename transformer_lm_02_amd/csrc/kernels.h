@@ -16,8 +16,6 @@ struct AdamChunk {
   int32_t decay;
 };
 
-// one matrix of the transposed weight copy: src [rows][cols] (elements from
-// the start of the 16-bit weights) -> dst [cols][ld] (ld >= rows)
 // One piece (at most 8192 elements, a multiple of 4, starting at a multiple
 // of 4) of one parameter tensor for the initialisation from a seed:
 // std > 0 draws N(0, std^2), otherwise every element is `value`.
@@ -28,9 +26,19 @@ struct InitSeg {
   float std;
   float value;
 };
+// The fused head + cross-entropy (see HeadEpi in gemm.h): per row the loss,
+// the gradient factor r, h2 = r * h and the target column of the stored
+// exp(z) minus the row's sum; flag bit 4 when a row's exp-sum leaves the
+// range the 16-bit exp(z) can carry
+int head_combine_launch(const float* part, int npart, const float* zy, const int32_t* tgt, int V,
+                        const int* n_valid, float loss_scale, const float* dscale, const h16_t* h,
+                        int C, float* row_loss, float* r, h16_t* h2, h16_t* logits, int ldv, int M,
+                        int* flags, hipStream_t s);
 int init_params_launch(float* params, const InitSeg* segs, int nsegs, uint64_t seed,
                        hipStream_t s);
 
+// one matrix of the transposed weight copy: src [rows][cols] (elements from
+// the start of the 16-bit weights) -> dst [cols][ld] (ld >= rows)
 struct TransposeJob {
   int64_t src, dst;
   int32_t rows, cols, ld, tile_begin;

@@ -508,9 +508,68 @@ __global__ __launch_bounds__(256) void init_params_kernel(float* __restrict__ p,
   }
 }
 
+// ---------------------------------------------------------------- fused head + cross-entropy
+// The head's forward epilogue left p~ = exp(z) in the logits buffer,
+// part[m][0..npart) (sums of p~ over blocks of 96 columns below V) and zy[m]
+// (the target's logit).  Per row: S = sum of the parts (lane-strided, then a
+// fixed-order wave sum), so log S = logsumexp_{v<V} z_v ("Let's reproduce
+// GPT-2 (124M)", chapter "Cross Entropy Loss"); row_loss = log S - zy for a
+// target in [0, V) (0 otherwise); sc = loss_scale * dscale / n_valid for such
+// a row (0 otherwise) and r = sc / S.  The target's column of the buffer
+// becomes exp(zy) - S, so that the logit gradient sc (softmax - onehot) is r
+// times the stored row; h2[m] = r * h[m] in 16 bits (the weight gradient's
+// token-side operand).  p~ overflows or vanishes for logits beyond about
+// +-80: a valid row with S outside [1e-28, 1e28] raises flag bit 4.
+__global__ __launch_bounds__(256) void head_combine_kernel(
+    const float* __restrict__ part, int npart, const float* __restrict__ zy,
+    const int32_t* __restrict__ tgt, int V, const int* __restrict__ n_valid, float loss_scale,
+    const float* __restrict__ dscale, const h16_t* __restrict__ h, int C,
+    float* __restrict__ row_loss, float* __restrict__ r_out, h16_t* __restrict__ h2,
+    h16_t* __restrict__ logits, int ldv, int M, int* __restrict__ flags) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;  // uniform per wave
+  const float* pr = part + row * npart;
+  float acc = 0.f;
+  for (int j = lane; j < npart; j += 64) acc += pr[j];
+  const float S = wave_sum(acc);
+  const int y = tgt[row];
+  const bool valid = y >= 0 && y < V;
+  const int nv = *n_valid;
+  const float sc = (valid && nv > 0) ? loss_scale * (dscale ? *dscale : 1.f) / (float)nv : 0.f;
+  const float r = sc / S;
+  if (lane == 0) {
+    const float z = valid ? zy[row] : 0.f;
+    row_loss[row] = valid ? __logf(S) - z : 0.f;
+    r_out[row] = r;
+    if (valid) logits[row * ldv + y] = f2h(__expf(z) - S);
+    if (valid && !(S >= 1e-28f && S <= 1e28f)) atomicOr(flags, 4);
+  }
+  const h16_t* hr = h + row * C;
+  h16_t* o = h2 + row * C;
+  for (int j = lane; j < C / 8; j += 64) {
+    const uint4 w = *(const uint4*)(hr + 8 * j);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    uint32_t q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = pack2h(r * h_lo(u[k]), r * h_hi(u[k]));
+    *(uint4*)(o + 8 * j) = make_uint4(q[0], q[1], q[2], q[3]);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 int colsum_finalize_launch(const float* part, int nrow, int ncol, float* out, int beta,
                            hipStream_t s);
+
+int head_combine_launch(const float* part, int npart, const float* zy, const int32_t* tgt, int V,
+                        const int* n_valid, float loss_scale, const float* dscale, const h16_t* h,
+                        int C, float* row_loss, float* r, h16_t* h2, h16_t* logits, int ldv, int M,
+                        int* flags, hipStream_t s) {
+  if (C % 8) return -5;
+  hipLaunchKernelGGL(head_combine_kernel, dim3(cdiv(M, 4)), dim3(256), 0, s, part, npart, zy, tgt, V,
+                     n_valid, loss_scale, dscale, h, C, row_loss, r, h2, logits, ldv, M, flags);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 int init_params_launch(float* params, const InitSeg* segs, int nsegs, uint64_t seed,
                        hipStream_t s) {
