@@ -56,9 +56,10 @@ def flops_per_token(dims, T):
 # Each group is timed through the single-op entry point that runs the same
 # kernel at the same shapes, one step's launches at a time, with events on
 # the stream the launches go to; the group with the largest time per step is
-# the dominant kernel that `roofline` reports.  The attention-projection and
-# MLP-projection forwards (residual epilogue) have no single-op entry point
-# and are not timed here; they are 8 % of the step.
+# the dominant kernel that `roofline` reports.  Not timed here (no single-op
+# entry point): the attention- and MLP-projection forwards (residual
+# epilogue, 8 % of the step) and the two products of the fused head with the
+# cross-entropy (one launch each, 14 % of the step).
 TRAFFIC_SOURCES = ["transformer_lm_02_amd/csrc/gemm2.hip", "transformer_lm_02_amd/csrc/gemm.h",
                    "transformer_lm_02_amd/csrc/common.h"]
 
@@ -76,9 +77,7 @@ def gemm_groups(B, T, dims):
             [(M, d, 4 * d, L), (M, 4 * d, d, L), (M, d, d, L), (M, 3 * d, d, L), (M, vi, d, 1)]),
         "input_gradients_and_qkv": (
             "gemm2_kernel<128, 192, true, true, 0, 2, 64, 2>", "linear",
-            [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, vi, 1), (M, d, d, L), (M, 3 * d, d, L)]),
-        "lm_head_forward": ("gemm2_kernel<256, 192, true, true, 0, 2, 32, 2>", "linear",
-                            [(M, dims["padded_vocab"], d, 1)]),
+            [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, d, L), (M, 3 * d, d, L)]),
         "mlp_expansion_gelu": ("gemm2_kernel<256, 192, true, true, 3, 2, 32, 2>", "gelu",
                                [(M, 4 * d, d, L)]),
         "mlp_projection_dx_gelu_bwd": ("gemm2_kernel<256, 192, true, true, 4, 2, 32, 2>",
