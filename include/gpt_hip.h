@@ -131,11 +131,19 @@ int gpt_forward_loss(gpt_model* h, const int32_t* idx, const int32_t* targets,
 /* Evaluation ("nanoGPT", Part IV Stage 2, estimate_loss: the model in eval
  * mode and no gradient): the mean loss over the targets in [0, V) of one batch
  * into loss_out (device float), with no dropout and no gradient written.
- * The caller averages such losses over its evaluation batches.  A following
+ * gpt_estimate_loss averages such losses over evaluation batches.  A following
  * gpt_backward fails with GPT_ESTATE.  Errors as gpt_forward_loss; targets
  * and loss_out must not be NULL. */
 int gpt_eval_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t B,
                   int32_t T, float* loss_out, void* stream);
+
+/* The pages' estimate_loss over one split ("nanoGPT", Part IV Stage 2): the
+ * eval loss (as gpt_eval_loss) of each of n_batches batches, then the mean of
+ * those losses (fp64 sum in a fixed order) into loss_out (device float).
+ * idx, targets: device int32 [n_batches][B][T].  Errors as gpt_eval_loss;
+ * GPT_EINVAL for n_batches outside [1, 1024]. */
+int gpt_estimate_loss(gpt_model* h, const int32_t* idx, const int32_t* targets,
+                      int32_t n_batches, int32_t B, int32_t T, float* loss_out, void* stream);
 
 /* Backward pass of the last forward (which must have had targets).
  * zero_first != 0: grads = new gradient; else grads += new gradient

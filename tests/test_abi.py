@@ -197,5 +197,6 @@ def test_noalloc_entry_point_refuses_sizes_beyond_its_scratch_without_a_device()
 def test_set_option_checks_its_arguments_without_a_device():
     lib = bd.lib
     assert lib.gpt_set_option(None, bd.GPT_OPT_FUSED_HEAD_CE, 1) == bd.GPT_EINVAL
+    assert lib.gpt_estimate_loss(None, None, None, 1, 1, 1, None, None) == bd.GPT_EINVAL
     v = ctypes.c_int32(7)
     assert lib.gpt_get_option(None, bd.GPT_OPT_FUSED_HEAD_CE, ctypes.byref(v)) == bd.GPT_EINVAL

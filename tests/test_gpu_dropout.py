@@ -146,9 +146,10 @@ def test_dropout_arguments_are_checked():
 # ---------------------------------------------------------------- evaluation
 @pytest.mark.parametrize("name,mode,tol", [("tiny", 0, 1e-5), ("char", 1, 2e-2)])
 def test_estimate_loss_matches_oracle(name, mode, tol):
-    """gpt_eval_loss per batch, averaged as the pages' eval gate does, against
-    the oracle's estimate_loss; eval mode ignores a dropout the previous
-    training forward used."""
+    """gpt_estimate_loss (each batch's eval loss and their mean on the
+    device, as the pages' eval gate averages them) against the oracle's
+    estimate_loss; eval mode ignores a dropout the previous training forward
+    used."""
     dims = synth.WORKLOADS[name]
     case(f"{name} mode={mode} estimate_loss over 3 batches")
     params = synth.init_params(dims, seed=23)
@@ -159,6 +160,29 @@ def test_estimate_loss_matches_oracle(name, mode, tol):
     m.forward(*dev[0], dropout=(0.25, 3, 1))
     got = m.estimate_loss(dev)
     assert abs(got - ref) <= tol, (got, ref)
+    m.close()
+
+
+def test_gpt2_eval_loss_with_the_fused_head():
+    """GPT-2 shapes take the fused head + cross-entropy in bf16 mode, in
+    training and in evaluation alike: the eval loss is the training forward's
+    loss bit for bit, and gpt_estimate_loss over two batches matches the
+    oracle's estimate_loss."""
+    dims = synth.WORKLOADS["gpt2"]
+    case("gpt2 bf16 eval loss with the fused head B=2 T=256")
+    params = synth.init_params(dims, seed=27)
+    batches = [synth.tokens(dims, seed=28 + i, batch=2, T=256) for i in range(2)]
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=2, init_params=params)
+    assert m.get_option(bd.GPT_OPT_FUSED_HEAD_CE) == 1
+    dev = [dev_tokens(*b) for b in batches]
+    train_loss, _ = m.forward(*dev[0])
+    a = train_loss.clone()
+    b = m.eval_loss(*dev[0]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = O.estimate_loss(params, batches, ocfg(dims))
+    got = m.estimate_loss(dev)
+    assert abs(got - ref) <= 2e-2, (got, ref)
     m.close()
 
 

@@ -57,6 +57,7 @@ _SIGS = {
     "gpt_amp_step": [_p, _f, _f, _f, _f, _f, _f, _p, _f, _f, _i32, _p, _p],
     "gpt_backward": [_p, _i32, _p],
     "gpt_eval_loss": [_p, _p, _p, _i32, _i32, _p, _p],
+    "gpt_estimate_loss": [_p, _p, _p, _i32, _i32, _i32, _p, _p],
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
     "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
     "gpt_set_option": [_p, _i32, _i32],
@@ -219,14 +220,18 @@ class GPT:
         return loss
 
     def estimate_loss(self, batches):
-        """The pages' estimate_loss over one split: the mean of the eval
-        losses of the batches (read back, as the pages' loop does with
-        loss.item())."""
+        """The pages' estimate_loss over one split (gpt_estimate_loss: every
+        batch's eval loss and their mean on the device); batches: list of
+        (idx, targets) int32 cuda tensors [B, T] of one shape.  Returns the
+        mean as a float (read back, as the pages' loop does with loss.item())."""
         import torch
-        out = torch.empty(len(batches), dtype=torch.float32, device=self.params.device)
-        for k, (idx, tgt) in enumerate(batches):
-            out[k:k + 1].copy_(self.eval_loss(idx, tgt))
-        return float(out.cpu().double().mean())
+        idx = torch.stack([b[0] for b in batches]).contiguous()
+        tgt = torch.stack([b[1] for b in batches]).contiguous()
+        n, B, T = idx.shape
+        loss = self.scalars[3:4]
+        check(lib.gpt_estimate_loss(self.handle, _ptr(idx), _ptr(tgt), n, B, T, _ptr(loss),
+                                    _stream()), "gpt_estimate_loss")
+        return float(loss.item())
 
     def backward(self, zero_first=True):
         check(lib.gpt_backward(self.handle, 1 if zero_first else 0, _stream()), "gpt_backward")

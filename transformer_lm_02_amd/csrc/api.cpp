@@ -150,6 +150,15 @@ int gpt_eval_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int3
                  : b16::gpt_eval_loss((b16::Model*)h->impl, idx, targets, B, T, loss_out, stream);
 }
 
+int gpt_estimate_loss(gpt_model* h, const int32_t* idx, const int32_t* targets, int32_t n_batches,
+                      int32_t B, int32_t T, float* loss_out, void* stream) {
+  if (!h) return null_handle();
+  return h->fp16 ? f16::gpt_estimate_loss((f16::Model*)h->impl, idx, targets, n_batches, B, T,
+                                          loss_out, stream)
+                 : b16::gpt_estimate_loss((b16::Model*)h->impl, idx, targets, n_batches, B, T,
+                                          loss_out, stream);
+}
+
 int gpt_backward(gpt_model* h, int32_t zero_first, void* stream) {
   if (!h) return null_handle();
   return h->fp16 ? f16::gpt_backward((f16::Model*)h->impl, zero_first, stream)

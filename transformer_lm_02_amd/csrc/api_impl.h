@@ -26,6 +26,8 @@ std::string& gpt_error_text();
   int gpt_backward(Model* h, int32_t zero_first, void* stream);                                 \
   int gpt_eval_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T, \
                     float* loss_out, void* stream);                                             \
+  int gpt_estimate_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t n_batches, \
+                        int32_t B, int32_t T, float* loss_out, void* stream);                   \
   int gpt_adamw_step(Model* h, float lr, float beta1, float beta2, float eps,                   \
                      float weight_decay, float max_norm, int32_t t, int32_t skip_nonfinite,     \
                      float* norm_out, void* stream);                                            \

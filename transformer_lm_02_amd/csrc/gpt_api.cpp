@@ -119,6 +119,7 @@ struct WsOff {
   int64_t splitk_bytes;
   int64_t ln_part_elems, cs_part_elems;  // one slice of each (several slices kept)
   size_t init_tab;  // InitSeg per chunk (initialisation from a seed)
+  size_t eval_losses = 0;  // per-batch losses of gpt_estimate_loss
   size_t total;
   int nchunks;
   int64_t vi;  // logits row pitch: padded_vocab rounded up to 64
@@ -128,6 +129,7 @@ struct WsOff {
 };
 
 constexpr int64_t kChunk = 8192;
+constexpr int kEvalBatches = 1024;  // batches one gpt_estimate_loss call averages
 
 WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   WsOff w;
@@ -222,6 +224,7 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   w.nchunks = (int)nch;
   w.chunks = take(nch * (int64_t)sizeof(AdamChunk));
   w.init_tab = take(nch * (int64_t)sizeof(InitSeg));
+  w.eval_losses = take(kEvalBatches * 4);
   w.total = off;
   return w;
 }
@@ -487,6 +490,33 @@ static int forward_stack(Model* h, const int32_t* idx, int B, int T, void* kv, i
   return GPT_OK;
 }
 
+// The tied head with the cross-entropy fused (after forward_stack and the
+// count of valid targets): the product's epilogue stores exp(z) and each
+// row's sums, one small pass takes each row's loss, the gradient factor r,
+// r * lnf and the target columns; no pass over the logits follows.
+static int fused_head_loss(Model* h, const int32_t* targets, int M, float loss_scale,
+                           const float* dscale, hipStream_t s) {
+  const gpt_config& c = h->cfg;
+  const WsOff& w = h->wo;
+  const int d = c.n_embd;
+  GemmEpiArgs e;
+  e.out = h->at(w.logits);
+  e.ldc = (int)w.vi;
+  e.head.tgt = targets;
+  e.head.part = h->at<float>(w.head_part);
+  e.head.zy = h->at<float>(w.head_zy);
+  e.head.V = c.vocab_size;
+  e.head.npart = w.head_npart;
+  CK(gemm_launch(true, true, true, EPI_HEAD, h->at(w.lnf), d, h->W(h->po.wte), d, M,
+                 c.padded_vocab, d, d, d, e, s));
+  CK(head_combine_launch(h->at<float>(w.head_part), w.head_npart, h->at<float>(w.head_zy), targets,
+                         c.vocab_size, h->at<int>(w.nvalid), loss_scale, dscale,
+                         h->at<h16_t>(w.lnf), d, h->at<float>(w.row_loss), h->at<float>(w.head_r),
+                         h->at<h16_t>(w.head_h2), h->at<h16_t>(w.logits), (int)w.vi, M,
+                         h->at<int>(w.flags), s));
+  return GPT_OK;
+}
+
 int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
                      float loss_scale, const float* dscale, const gpt_dropout* dropout,
                      float* loss_out, void* logits_out, void* stream) {
@@ -507,25 +537,8 @@ int gpt_forward_loss(Model* h, const int32_t* idx, const int32_t* targets, int32
   CK(forward_stack(h, idx, B, T, nullptr, 1, s, dr));
   const bool fused = targets && !logits_out && h->fused_ok();
   if (fused) {
-    // the tied head with the cross-entropy fused: the product's epilogue
-    // stores exp(z) and each row's sums, one small pass takes the loss and the
-    // gradient factors; no pass over the logits follows
     CK(count_valid_launch(targets, M, c.vocab_size, h->at<int>(w.nvalid), h->at<int>(w.flags), s));
-    GemmEpiArgs e;
-    e.out = h->at(w.logits);
-    e.ldc = (int)w.vi;
-    e.head.tgt = targets;
-    e.head.part = h->at<float>(w.head_part);
-    e.head.zy = h->at<float>(w.head_zy);
-    e.head.V = c.vocab_size;
-    e.head.npart = w.head_npart;
-    CK(gemm_launch(bf, true, true, EPI_HEAD, h->at(w.lnf), d, h->W(p.wte), d, M, c.padded_vocab, d,
-                   d, d, e, s));
-    CK(head_combine_launch(h->at<float>(w.head_part), w.head_npart, h->at<float>(w.head_zy), targets,
-                           c.vocab_size, h->at<int>(w.nvalid), loss_scale, dscale,
-                           h->at<h16_t>(w.lnf), d, h->at<float>(w.row_loss),
-                           h->at<float>(w.head_r), h->at<h16_t>(w.head_h2), h->at<h16_t>(w.logits),
-                           (int)w.vi, M, h->at<int>(w.flags), s));
+    CK(fused_head_loss(h, targets, M, loss_scale, dscale, s));
     if (loss_out) CK(loss_finalize_launch(h->at<float>(w.row_loss), M, h->at<int>(w.nvalid), loss_out, s));
   } else {
     GemmEpiArgs e;
@@ -572,15 +585,37 @@ int gpt_eval_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t 
   const int M = B * T, d = c.n_embd;
   h->have_fwd = false;
   CK(forward_stack(h, idx, B, T, nullptr, 1, s));
-  GemmEpiArgs e;
-  e.out = h->at(w.logits);
-  e.ldc = (int)w.vi;
-  CK(gemm_launch(bf, true, true, EPI_ACT, h->at(w.lnf), d, h->W(p.wte), d, M, c.padded_vocab, d,
-                 d, d, e, s));
   CK(count_valid_launch(targets, M, c.vocab_size, h->at<int>(w.nvalid), h->at<int>(w.flags), s));
-  CK(cross_entropy_launch(bf, h->at(w.logits), targets, h->at<float>(w.row_loss),
-                          h->at<int>(w.nvalid), 1.f, nullptr, M, c.vocab_size, (int)w.vi, s, 0));
+  if (h->fused_ok()) {
+    // the same fused head as training, so the eval loss is the training
+    // forward's loss bit for bit (the factors it leaves go unused)
+    CK(fused_head_loss(h, targets, M, 1.f, nullptr, s));
+  } else {
+    GemmEpiArgs e;
+    e.out = h->at(w.logits);
+    e.ldc = (int)w.vi;
+    CK(gemm_launch(bf, true, true, EPI_ACT, h->at(w.lnf), d, h->W(p.wte), d, M, c.padded_vocab, d,
+                   d, d, e, s));
+    CK(cross_entropy_launch(bf, h->at(w.logits), targets, h->at<float>(w.row_loss),
+                            h->at<int>(w.nvalid), 1.f, nullptr, M, c.vocab_size, (int)w.vi, s, 0));
+  }
   CK(loss_finalize_launch(h->at<float>(w.row_loss), M, h->at<int>(w.nvalid), loss_out, s));
+  return GPT_OK;
+}
+
+// The pages' estimate_loss over one split ([NG] Part IV Stage 2): the eval
+// loss of each of n_batches batches (idx, targets: [n_batches][B][T]), then
+// their mean in a fixed order (fp64) into loss_out, all on the device.
+int gpt_estimate_loss(Model* h, const int32_t* idx, const int32_t* targets, int32_t n_batches,
+                      int32_t B, int32_t T, float* loss_out, void* stream) {
+  if (!h || !idx || !targets || !loss_out) return fail(GPT_EINVAL, "null handle or buffer");
+  if (n_batches < 1 || n_batches > kEvalBatches)
+    return fail(GPT_EINVAL, "n_batches outside [1, 1024]");
+  float* losses = h->at<float>(h->wo.eval_losses);
+  const int64_t n = (int64_t)B * T;
+  for (int k = 0; k < n_batches; ++k)
+    if (int rc = gpt_eval_loss(h, idx + k * n, targets + k * n, B, T, losses + k, stream)) return rc;
+  CK(mean_launch(losses, n_batches, loss_out, (hipStream_t)stream));
   return GPT_OK;
 }
 

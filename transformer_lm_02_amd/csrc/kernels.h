@@ -34,6 +34,8 @@ int head_combine_launch(const float* part, int npart, const float* zy, const int
                         const int* n_valid, float loss_scale, const float* dscale, const h16_t* h,
                         int C, float* row_loss, float* r, h16_t* h2, h16_t* logits, int ldv, int M,
                         int* flags, hipStream_t s);
+// out = mean of x[0..n) (fp64 sum in a fixed order)
+int mean_launch(const float* x, int n, float* out, hipStream_t s);
 int init_params_launch(float* params, const InitSeg* segs, int nsegs, uint64_t seed,
                        hipStream_t s);
 

@@ -426,6 +426,19 @@ __global__ __launch_bounds__(RED_THREADS) void loss_finalize_kernel(const float*
   }
 }
 
+// out = mean of x[0..n), summed in fp64 in a fixed order (thread strides,
+// then waves in order): the mean of evaluation batches' losses
+__global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int n,
+                                                   float* __restrict__ out) {
+  __shared__ double red[4];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) s += x[i];
+  s = wave_sum_d(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = (float)((red[0] + red[1] + red[2] + red[3]) / n);
+}
+
 // ---------------------------------------------------------------- column sums
 // part[rb][n] = sum of a[row][n] over the CS_ROWS rows of block-row rb
 // (bias gradients: db = sum over tokens of dy).  Each thread owns 8
@@ -568,6 +581,12 @@ int head_combine_launch(const float* part, int npart, const float* zy, const int
   if (C % 8) return -5;
   hipLaunchKernelGGL(head_combine_kernel, dim3(cdiv(M, 4)), dim3(256), 0, s, part, npart, zy, tgt, V,
                      n_valid, loss_scale, dscale, h, C, row_loss, r, h2, logits, ldv, M, flags);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int mean_launch(const float* x, int n, float* out, hipStream_t s) {
+  if (n < 1) return -5;
+  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, x, n, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
