@@ -146,11 +146,20 @@ struct Gemm2Args {
   GemmEpiArgs e;
 };
 
-__device__ __forceinline__ void tile_coords2(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int n = tiles_m * tiles_n;
+// Workgroup -> (output tile, k split).  Workgroups go to the 8 XCDs in
+// turn (workgroup w to XCD w % 8), so the linear work index (split-major,
+// then tiles in groups of 8 row tiles) is cut into 8 contiguous chunks, one
+// per XCD: the workgroups resident on one XCD then share a split's k range
+// and neighbouring tiles' operand rows in that XCD's L2.
+__device__ __forceinline__ void tile_split_coords(int wg, int tiles_m, int tiles_n, int ksplit,
+                                                  int& tm, int& tn, int& split) {
+  const int tiles = tiles_m * tiles_n;
+  const int n = tiles * ksplit;
   const int xcd = wg & 7, local = wg >> 3;
   const int base = n >> 3, rem = n & 7;
-  const int tile = xcd * base + min(xcd, rem) + local;
+  const int w = xcd * base + min(xcd, rem) + local;
+  split = w / tiles;
+  const int tile = w - split * tiles;
   constexpr int GROUP_M = 8;
   const int per_group = GROUP_M * tiles_n;
   const int g = tile / per_group;
@@ -274,18 +283,25 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   constexpr int LDS_ELEMS_RING = NS * STAGE_ELEMS;
   constexpr int LDS_ELEMS_EPI = 4 * 32 * EP_PITCH * 2;  // in 16-bit units
   constexpr int LDS_ELEMS = LDS_ELEMS_RING > LDS_ELEMS_EPI ? LDS_ELEMS_RING : LDS_ELEMS_EPI;
-  __shared__ __attribute__((aligned(1024))) h16_t lds[LDS_ELEMS];
+  // EPI_HEAD: the tile's target ids, in LDS past the ring and the staging area
+  constexpr int LDS_ELEMS_Y = EPI == EPI_HEAD ? 2 * BM : 0;
+  __shared__ __attribute__((aligned(1024))) h16_t lds[LDS_ELEMS + LDS_ELEMS_Y];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int tm, tn;
-  tile_coords2(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  int tm, tn, split;
+  tile_split_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.ksplit, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm = wave >> 1, wn = wave & 1;
-  const int split = blockIdx.y;
   const int nk_total = (p.K + BK - 1) / BK;
   const int kt0 = split * p.k_tiles_per_split;
   const int nk = min(nk_total - kt0, p.k_tiles_per_split);
+  // EPI_HEAD: thread t fetches the target id of row m0 + t now, so the load's
+  // latency is spent under the main loop rather than in the epilogue
+  int y_pref = -1;
+  if constexpr (EPI == EPI_HEAD) {
+    if (tid < BM && m0 + tid < p.M) y_pref = p.e.head.tgt[m0 + tid];
+  }
 
   const uint32_t a_bytes = (uint32_t)((int64_t)(AK ? p.M : p.ka_rows) * p.lda * 2);
   const uint32_t b_bytes = (uint32_t)((int64_t)(BKC ? p.N : p.kb_rows) * p.ldb * 2);
@@ -411,7 +427,13 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
     for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::true_type());
     if (nk > 0) tile(nk - 1, std::false_type());
   }
+  int* ys = (int*)(lds + LDS_ELEMS);
+  if constexpr (EPI == EPI_HEAD) {
+    if (tid < BM) ys[tid] = y_pref;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0: the store lands before the barrier
+  }
   // every wave is done with the ring before it is reused for the epilogue
+  // (and the target ids are in LDS)
   wait_vm_barrier<0>();
 
   // epilogue: per 32-row slab of the wave tile, stage fp32 in LDS, then each
@@ -473,7 +495,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
           const float4 v0 = *(const float4*)(ep + lr * EP_PITCH + my_c);
           const float4 v1 = *(const float4*)(ep + lr * EP_PITCH + my_c + 4);
           const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-          const int y = p.e.head.tgt[grow];
+          const int y = ys[grow - m0];
           float e8[8], zy = 0.f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -566,7 +588,7 @@ int run2(Gemm2Args p, hipStream_t s) {
   p.tiles_m = (int)cdiv(p.M, BM);
   p.tiles_n = (int)cdiv(p.N, BN);
   hipLaunchKernelGGL((gemm2_kernel<BM, BN, AK, BKC, EPI, NS, BK, OCC>),
-                     dim3(p.tiles_m * p.tiles_n, p.ksplit), dim3(256), 0, s, p);
+                     dim3(p.tiles_m * p.tiles_n * p.ksplit), dim3(256), 0, s, p);
   if (p.e.cs_part) {
     if (ColsumJob* d = p.e.cs_defer) {
       *d = ColsumJob();
