@@ -327,7 +327,12 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
     float mb = fmax_fast(s[0][0], s[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mb = fmax_fast(fmax_fast(mb, s[0][r]), s[1][r]);
-    mb = fmax_fast(mb, __shfl_xor(mb, 32, 64)) * sc;
+    {
+      // the other half-wave's value: lanes l and l^32 hold one query's two
+      // halves of the keys; the swap leaves lane l's pair in both results
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
+      mb = fmax_fast(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sc;
+    }
     // The reference point m of the exponentials moves only when some
     // query's block maximum exceeds it by more than 8 (log2 units): the
     // probabilities then stay below 2^8 and the accumulator is rescaled

@@ -282,10 +282,12 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   constexpr int EP_PITCH = WC + 8;          // fp32 staging pitch: rows r, r+4 32 banks apart
   constexpr int LDS_ELEMS_RING = NS * STAGE_ELEMS;
   constexpr int LDS_ELEMS_EPI = 4 * 32 * EP_PITCH * 2;  // in 16-bit units
-  constexpr int LDS_ELEMS = LDS_ELEMS_RING > LDS_ELEMS_EPI ? LDS_ELEMS_RING : LDS_ELEMS_EPI;
-  // EPI_HEAD: the tile's target ids, in LDS past the ring and the staging area
-  constexpr int LDS_ELEMS_Y = EPI == EPI_HEAD ? 2 * BM : 0;
-  __shared__ __attribute__((aligned(1024))) h16_t lds[LDS_ELEMS + LDS_ELEMS_Y];
+  // EPI_HEAD: after the main loop, the tile's target ids and each wave's
+  // per-lane row sums of a 32-row slab ([32][12] fp32) follow the staging area
+  constexpr int LDS_ELEMS_HEAD = EPI == EPI_HEAD ? LDS_ELEMS_EPI + 2 * BM + 4 * 32 * 12 * 2 : 0;
+  constexpr int LDS_ELEMS_0 = LDS_ELEMS_RING > LDS_ELEMS_EPI ? LDS_ELEMS_RING : LDS_ELEMS_EPI;
+  constexpr int LDS_ELEMS = LDS_ELEMS_0 > LDS_ELEMS_HEAD ? LDS_ELEMS_0 : LDS_ELEMS_HEAD;
+  __shared__ __attribute__((aligned(1024))) h16_t lds[LDS_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -427,14 +429,13 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
     for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::true_type());
     if (nk > 0) tile(nk - 1, std::false_type());
   }
-  int* ys = (int*)(lds + LDS_ELEMS);
+  // every wave is done with the ring before it is reused for the epilogue
+  wait_vm_barrier<0>();
+  int* ys = (int*)(lds + LDS_ELEMS_EPI);
   if constexpr (EPI == EPI_HEAD) {
     if (tid < BM) ys[tid] = y_pref;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0: the store lands before the barrier
+    __syncthreads();
   }
-  // every wave is done with the ring before it is reused for the epilogue
-  // (and the target ids are in LDS)
-  wait_vm_barrier<0>();
 
   // epilogue: per 32-row slab of the wave tile, stage fp32 in LDS, then each
   // lane handles 8 consecutive columns of one row
@@ -485,7 +486,9 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
       // p~ = exp(z) below V (0 above), the target's z, and the sum of p~ over
       // this wave's 96 columns of each row: the LPR lanes of a row add their
       // sums in lane order
+      static_assert(LPR == 12, "row sums assume 12 lanes a row");
       const int blk = (n0 + wn * WC) / 96;
+      float* ps = (float*)(ys + BM) + wave * 32 * 12;
 #pragma unroll 1
       for (int it = 0; it < NIT; ++it) {
         const int lr = it * RPI + my_r;
@@ -508,14 +511,19 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
                          pack2h(e8[6], e8[7]));
           if (y >= gcol && y < gcol + 8 && y < p.e.head.V) p.e.head.zy[grow] = zy;
         }
-        // the LPR = 12 lanes of a row (lanes b..b+11, b = 12 my_r) in a fixed
-        // tree: +6, +3, then +1 and +2 into lane b
-        static_assert(LPR == 12, "row sums assume 12 lanes a row");
-        float tot = sum + __shfl_down(sum, 6, 64);
-        tot += __shfl_down(tot, 3, 64);
-        tot = tot + __shfl_down(tot, 1, 64) + __shfl_down(tot, 2, 64);
-        if (lane_on && lr < 32 && grow < p.M && my_c == 0 && n0 + wn * WC < p.N)
-          p.e.head.part[(int64_t)grow * p.e.head.npart + blk] = tot;
+        if (lane_on && lr < 32) ps[lr * 12 + my_c / 8] = sum;
+      }
+      // lane r adds the 12 lane sums of slab row r in a fixed order (the
+      // wave's own LDS writes above, so no barrier)
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int grow = grow0 - my_r + lane;
+      if (lane < 32 && grow < p.M && n0 + wn * WC < p.N) {
+        const float4 a = *(const float4*)(ps + lane * 12);
+        const float4 b4 = *(const float4*)(ps + lane * 12 + 4);
+        const float4 c = *(const float4*)(ps + lane * 12 + 8);
+        const float tot = ((a.x + a.y) + (a.z + a.w)) + ((b4.x + b4.y) + (b4.z + b4.w)) +
+                          ((c.x + c.y) + (c.z + c.w));
+        p.e.head.part[(int64_t)grow * p.e.head.npart + blk] = tot;
       }
     } else if constexpr (epi_reads_aux<EPI>()) {
       // the auxiliary operands of PG row passes are loaded together, then
