@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
     v[i] = j < nv ? xr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
     s += v[i].x + v[i].y + v[i].z + v[i].w;
   }
-  const float mean = wave_sum(s) / C;
+  const float mean = wave_sum_dpp(s) / C;
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < LN_MAXV; ++i) {
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const float* __restrict__ x
       q += a * a + bb * bb + c * c + d * d;
     }
   }
-  const float var = wave_sum(q) / C;
+  const float var = wave_sum_dpp(q) / C;
   const float rstd = 1.0f / sqrtf(var + LN_EPS);
   T* yr = y + row * C;
 #pragma unroll
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
       pw[i].z += d.z * xh[i].z; pw[i].w += d.w * xh[i].w;
       pb[i].x += d.x; pb[i].y += d.y; pb[i].z += d.z; pb[i].w += d.w;
     }
-    const float m1 = wave_sum(s1) / C, m2 = wave_sum(s2) / C;
+    const float m1 = wave_sum_dpp(s1) / C, m2 = wave_sum_dpp(s2) / C;
     float4* dres4 = (float4*)(dres + row * C);
     T* da = dres_act + row * C;
 #pragma unroll
