@@ -481,6 +481,90 @@ def test_adamw_skips_nonfinite_gradients():
     mdl.close()
 
 
+def _adam_inputs(n, seed):
+    rng = np.random.default_rng(seed)
+    m0 = rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)
+    v0 = (rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)) ** 2
+    return m0, v0
+
+
+@pytest.mark.parametrize("name", ["char", "gpt2_narrow"])
+def test_adamw_tiles_equal_the_flat_update_bit_for_bit(name):
+    """In the 16-bit modes the weight matrices are updated by 64x64 tiles that
+    also write the transposed copies; fp32 mode updates every tensor in flat
+    chunks.  The per-element arithmetic is the same, so params, m and v agree
+    bit for bit (char: a 65-row embedding, so partial tiles too)."""
+    dims = dict(synth.WORKLOADS["char" if name == "char" else "gpt2"])
+    if name == "gpt2_narrow":
+        dims.update(n_layer=2)
+    case(f"adamw tiles vs flat chunks, {name}")
+    n = synth.n_params(dims)
+    params = synth.perturbed_params(dims, seed=21)
+    g = synth.synthetic_grads(n, seed=22, scale=1e-2)
+    m0, v0 = _adam_inputs(n, 23)
+    out = []
+    for mode in (bd.GPT_FP32, bd.GPT_BF16, bd.GPT_FP16):
+        mdl = bd.GPT(dims, mode, max_batch=1, init_params=params)
+        mdl.grads.copy_(torch.as_tensor(g))
+        mdl.adam_m.copy_(torch.as_tensor(m0))
+        mdl.adam_v.copy_(torch.as_tensor(v0))
+        mdl.adamw_step(lr=6e-4, t=5, max_norm=1.0)
+        torch.cuda.synchronize()
+        out.append((mdl.params.cpu().numpy(), mdl.adam_m.cpu().numpy(), mdl.adam_v.cpu().numpy()))
+        mdl.close()
+    names = per_tensor(dims, np.arange(n))
+    for k in (1, 2):
+        for what, a, b in zip(("params", "m", "v"), out[0], out[k]):
+            bad = np.flatnonzero(a != b)
+            where = sorted({t for t, ix in names.items() if np.isin(ix, bad).any()})
+            worst = float(np.max(np.abs(a[bad] - b[bad]) / np.maximum(np.abs(a[bad]), 1e-30))) if bad.size else 0.0
+            assert bad.size == 0, (what, k, bad.size, where[:6], worst, bad[:8].tolist())
+
+
+@pytest.mark.parametrize("mode_name", ["bf16", "fp16"])
+def test_weight_copies_after_a_step_equal_fresh_copies(mode_name):
+    """The 16-bit weight copy and its transposes written by the optimizer step
+    equal those that gpt_init derives from the same updated parameters: a
+    model stepped once and a model initialised with its updated parameters
+    give the same loss and the same gradients, bit for bit (the forward reads
+    the copy, the input-gradient products its transposes) except for the
+    order of the embedding backward's atomic additions into wte."""
+    dims = dict(synth.WORKLOADS["char"])
+    mode = bd.GPT_BF16 if mode_name == "bf16" else bd.GPT_FP16
+    case(f"weight copies after a step, char {mode_name}")
+    params = synth.perturbed_params(dims, seed=31)
+    idx, tgt = synth.tokens(dims, seed=32, batch=4)
+    idx2, tgt2 = synth.tokens(dims, seed=33, batch=4)
+    a = bd.GPT(dims, mode, max_batch=4, init_params=params)
+    a.forward(*dev_tokens(idx, tgt), scaled=mode == bd.GPT_FP16)
+    a.backward()
+    if mode == bd.GPT_FP16:
+        a.amp_step(lr=3e-3)
+    else:
+        a.adamw_step(lr=3e-3, t=1)
+    torch.cuda.synchronize()
+    updated = a.params.cpu().numpy()
+    assert not np.array_equal(updated, params)
+    b = bd.GPT(dims, mode, max_batch=4, init_params=updated)
+    res = []
+    for mdl in (a, b):
+        loss, _ = mdl.forward(*dev_tokens(idx2, tgt2))
+        mdl.backward()
+        torch.cuda.synchronize()
+        res.append((float(loss.item()), mdl.grads.cpu().numpy()))
+    assert res[0][0] == res[1][0]
+    ga, gb = per_tensor(dims, res[0][1]), per_tensor(dims, res[1][1])
+    for name in ga:
+        if name == "wte":
+            # the embedding backward adds token rows into wte with atomics,
+            # whose order varies from run to run
+            assert rel_err(ga[name], gb[name]) <= 1e-6, name
+        else:
+            assert np.array_equal(ga[name], gb[name]), name
+    a.close()
+    b.close()
+
+
 # ---------------------------------------------------------------- error paths
 def test_error_paths_and_bad_token_flag():
     dims = synth.WORKLOADS["tiny"]

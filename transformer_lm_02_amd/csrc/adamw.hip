@@ -108,6 +108,23 @@ __global__ void amp_finalize_kernel(const double* __restrict__ part, int nblk, f
   }
 }
 
+// The AdamW update of one element ("Let's reproduce GPT-2 (124M)", chapter
+// "AdamW, Gradient Clipping"; PyTorch's order: decoupled decay first, then
+// the bias-corrected step with eps outside the square root).  coef: the clip
+// (and unscale) factor; decay = 1 - lr * wd for decayed tensors, else 1.
+__device__ __forceinline__ void adamw_elem(float& pk, float gk_raw, float& mk, float& vk,
+                                           float coef, float beta1, float beta2, float eps,
+                                           float decay, float step, float rbc2) {
+  // no multiply-add contraction: every kernel that applies the update (flat
+  // chunks or matrix tiles, vector or scalar code) rounds the same way
+#pragma clang fp contract(off)
+  const float gk = gk_raw * coef;
+  mk = beta1 * mk + (1.0f - beta1) * gk;
+  vk = beta2 * vk + (1.0f - beta2) * gk * gk;
+  const float denom = sqrtf(vk) * rbc2 + eps;  // sqrt(v / bc2) + eps
+  pk = pk * decay - step * mk / denom;
+}
+
 // One chunk per workgroup.  16-bit copy of the updated weights written when
 // shadow != nullptr.  bc_in_scal: the bias corrections come from scal[2..3]
 // (the loss-scaled step, whose step count lives on the device).
@@ -135,17 +152,99 @@ __global__ __launch_bounds__(256) void adamw_kernel(
     float* ma = &mm.x;
     float* va = &vv.x;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float gk = ga[k] * coef;
-      ma[k] = beta1 * ma[k] + (1.0f - beta1) * gk;
-      va[k] = beta2 * va[k] + (1.0f - beta2) * gk * gk;
-      const float denom = sqrtf(va[k]) * rbc2 + eps;  // sqrt(v / bc2) + eps
-      pa[k] = pa[k] * decay - step * ma[k] / denom;
-    }
+    for (int k = 0; k < 4; ++k)
+      adamw_elem(pa[k], ga[k], ma[k], va[k], coef, beta1, beta2, eps, decay, step, rbc2);
     ((float4*)p)[e] = pp;
     ((float4*)m)[e] = mm;
     ((float4*)v)[e] = vv;
     if (shadow) *(uint2*)(shadow + 4 * e) = make_uint2(pack2h(pp.x, pp.y), pack2h(pp.z, pp.w));
+  }
+}
+
+// AdamW over the weight matrices that have transposed 16-bit copies (every
+// one of them 2-D, so decayed), one 64 x 64 tile per workgroup: the update of
+// adamw_kernel, the 16-bit copy in the parameters' layout, and the same
+// 16-bit values transposed through LDS into the copy that the input-gradient
+// products read, so no separate transpose pass follows the step.  A job is a
+// matrix [rows][cols] at element offset src of the parameters (and of the
+// copy), transposed to dstT + dst with leading dimension ld.
+__global__ __launch_bounds__(256) void adamw_tile_kernel(
+    float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
+    float* __restrict__ v, h16_t* __restrict__ shadow, h16_t* __restrict__ dstT,
+    const TransposeJob* __restrict__ jobs, int njobs, const float* __restrict__ scal, float lr,
+    float beta1, float beta2, float eps, float wd, float bc1, float bc2, int skip_nonfinite,
+    int bc_in_scal) {
+  if (skip_nonfinite && scal[1] != 0.f) return;
+  if (bc_in_scal) {
+    bc1 = scal[2];
+    bc2 = scal[3];
+  }
+  __shared__ __attribute__((aligned(16))) h16_t tile[64][72];
+  int j = 0;
+  while (j + 1 < njobs && (int)blockIdx.x >= jobs[j + 1].tile_begin) ++j;
+  const TransposeJob job = jobs[j];
+  const int t = blockIdx.x - job.tile_begin;
+  const int tiles_c = (job.cols + 63) / 64;
+  const int r0 = (t / tiles_c) * 64, c0 = (t % tiles_c) * 64;
+  const float coef = scal[0];
+  const float decay = 1.0f - lr * wd;
+  const float step = lr / bc1;
+  const float rbc2 = 1.0f / sqrtf(bc2);
+  h16_t* D = dstT + job.dst;
+  const bool full = r0 + 64 <= job.rows && c0 + 64 <= job.cols && job.cols % 8 == 0 &&
+                    job.ld % 8 == 0 && job.src % 8 == 0 && job.dst % 8 == 0;
+  if (full) {
+    // 16 threads x 4 values cover a 64-value tile row: four passes of 16 rows
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int r = (threadIdx.x >> 4) + 16 * pass, c4 = 4 * (threadIdx.x & 15);
+      const int64_t e = (job.src + (int64_t)(r0 + r) * job.cols + c0 + c4) / 4;
+      float4 pp = ((float4*)p)[e], gg = ((const float4*)g)[e];
+      float4 mm = ((float4*)m)[e], vv = ((float4*)v)[e];
+      float* pa = &pp.x;
+      const float* ga = &gg.x;
+      float* ma = &mm.x;
+      float* va = &vv.x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        adamw_elem(pa[k], ga[k], ma[k], va[k], coef, beta1, beta2, eps, decay, step, rbc2);
+      ((float4*)p)[e] = pp;
+      ((float4*)m)[e] = mm;
+      ((float4*)v)[e] = vv;
+      const uint2 w = make_uint2(pack2h(pp.x, pp.y), pack2h(pp.z, pp.w));
+      *(uint2*)(shadow + 4 * e) = w;
+      *(uint2*)&tile[r][c4] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int oc = (threadIdx.x >> 3) + 32 * pass, r8 = 8 * (threadIdx.x & 7);
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)tile[r8 + 2 * k][oc] | ((uint32_t)tile[r8 + 2 * k + 1][oc] << 16);
+      *(uint4*)(D + (int64_t)(c0 + oc) * job.ld + r0 + r8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int r = i / 64, c = i % 64;
+      if (r0 + r < job.rows && c0 + c < job.cols) {
+        const int64_t e = job.src + (int64_t)(r0 + r) * job.cols + c0 + c;
+        float pk = p[e], mk = m[e], vk = v[e];
+        adamw_elem(pk, g[e], mk, vk, coef, beta1, beta2, eps, decay, step, rbc2);
+        p[e] = pk;
+        m[e] = mk;
+        v[e] = vk;
+        const h16_t hv = f2h(pk);
+        shadow[e] = hv;
+        tile[r][c] = hv;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int c = i / 64, r = i % 64;  // output row c, column r
+      if (r0 + r < job.rows && c0 + c < job.cols) D[(int64_t)(c0 + c) * job.ld + r0 + r] = tile[r][c];
+    }
   }
 }
 
@@ -159,21 +258,27 @@ __global__ void to_h16_kernel(const float* __restrict__ p, h16_t* __restrict__ o
 int adamw_norm_blocks() { return NORM_BLOCKS; }
 
 int adamw_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
-                 const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
-                 float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
-                 float max_norm, int t, int skip_nonfinite, hipStream_t s) {
+                 const AdamChunk* chunks, int nchunks, const TileJobs& tj, double* norm_part,
+                 float* scal, float* norm_out, float lr, float beta1, float beta2, float eps,
+                 float wd, float max_norm, int t, int skip_nonfinite, hipStream_t s) {
   hipLaunchKernelGGL(sumsq_kernel, dim3(NORM_BLOCKS), dim3(256), 0, s, g, n, norm_part);
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(256), 0, s, norm_part, NORM_BLOCKS,
                      max_norm, norm_out, scal);
   const float bc1 = (float)(1.0 - pow((double)beta1, (double)t));
   const float bc2 = (float)(1.0 - pow((double)beta2, (double)t));
-  hipLaunchKernelGGL(adamw_kernel, dim3(nchunks), dim3(256), 0, s, p, g, m, v, shadow, chunks,
-                     scal, lr, beta1, beta2, eps, wd, bc1, bc2, skip_nonfinite, 0);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(adamw_kernel, dim3(nchunks), dim3(256), 0, s, p, g, m, v, shadow, chunks,
+                       scal, lr, beta1, beta2, eps, wd, bc1, bc2, skip_nonfinite, 0);
+  if (tj.ntiles > 0)
+    hipLaunchKernelGGL(adamw_tile_kernel, dim3(tj.ntiles), dim3(256), 0, s, p, g, m, v, shadow,
+                       tj.dstT, tj.jobs, tj.njobs, scal, lr, beta1, beta2, eps, wd, bc1, bc2,
+                       skip_nonfinite, 0);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int adamw_amp_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
-                     const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
+                     const AdamChunk* chunks, int nchunks, const TileJobs& tj,
+                     double* norm_part, float* scal,
                      float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
                      float max_norm, float* scaler, float growth, float backoff, int interval,
                      hipStream_t s) {
@@ -181,8 +286,12 @@ int adamw_amp_launch(float* p, const float* g, float* m, float* v, h16_t* shadow
   hipLaunchKernelGGL(amp_finalize_kernel, dim3(1), dim3(256), 0, s, norm_part, NORM_BLOCKS,
                      max_norm, beta1, beta2, (ScalerState*)scaler, growth, backoff, interval,
                      norm_out, scal);
-  hipLaunchKernelGGL(adamw_kernel, dim3(nchunks), dim3(256), 0, s, p, g, m, v, shadow, chunks,
-                     scal, lr, beta1, beta2, eps, wd, 1.f, 1.f, 1, 1);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(adamw_kernel, dim3(nchunks), dim3(256), 0, s, p, g, m, v, shadow, chunks,
+                       scal, lr, beta1, beta2, eps, wd, 1.f, 1.f, 1, 1);
+  if (tj.ntiles > 0)
+    hipLaunchKernelGGL(adamw_tile_kernel, dim3(tj.ntiles), dim3(256), 0, s, p, g, m, v, shadow,
+                       tj.dstT, tj.jobs, tj.njobs, scal, lr, beta1, beta2, eps, wd, 1.f, 1.f, 1, 1);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -283,6 +283,16 @@ struct Model {
     return h16() ? (const void*)(at<h16_t>(wo.shadow) + off) : (const void*)(params + off);
   }
   const h16_t* WT(int64_t off) const { return at<h16_t>(wo.wT) + off; }
+  // AdamW's tiles: the weight matrices with transposed copies (16-bit modes)
+  TileJobs tiles() const {
+    TileJobs t;
+    if (!h16()) return t;
+    t.dstT = at<h16_t>(wo.wT);
+    t.jobs = at<TransposeJob>(wo.tjobs);
+    t.njobs = wo.njobs;
+    t.ntiles = wo.ttiles;
+    return t;
+  }
   int refresh_transposes(hipStream_t s) const {
     if (!h16()) return 0;
     return transpose_h16_launch(at<h16_t>(wo.shadow), at<h16_t>(wo.wT),
@@ -322,18 +332,6 @@ int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, fl
   h->m = adam_m;
   h->v = adam_v;
   h->ws = (char*)workspace;
-  const float res_std = (float)(0.02 / sqrt(2.0 * cfg->n_layer));
-  for (size_t i = 0; i < h->po.tensors.size(); ++i) {
-    const int64_t o = h->po.tensors[i].first, n = h->po.tensors[i].second;
-    const int k = h->po.init[i];
-    const float sd = k == INIT_STD ? 0.02f : k == INIT_RESID ? res_std : 0.f;
-    const float val = k == INIT_ONE ? 1.f : 0.f;
-    for (int64_t c = 0; c < n; c += kChunk) {
-      const int32_t cnt = (int32_t)std::min<int64_t>(kChunk, n - c);
-      h->chunks.push_back({o + c, cnt, h->po.is2d[i]});
-      h->init_segs.push_back({o + c, cnt, 0, sd, val});
-    }
-  }
   if (h->h16()) {
     const int64_t d = cfg->n_embd;
     int tiles = 0;
@@ -351,6 +349,25 @@ int gpt_init(Model** out, const gpt_config* cfg, float* params, float* grads, fl
       job(P.mprojw, L.mprojT, d, 4 * d, d);
     }
     h->wo.ttiles = tiles;
+  }
+  const float res_std = (float)(0.02 / sqrt(2.0 * cfg->n_layer));
+  for (size_t i = 0; i < h->po.tensors.size(); ++i) {
+    const int64_t o = h->po.tensors[i].first, n = h->po.tensors[i].second;
+    const int k = h->po.init[i];
+    const float sd = k == INIT_STD ? 0.02f : k == INIT_RESID ? res_std : 0.f;
+    const float val = k == INIT_ONE ? 1.f : 0.f;
+    // a matrix with a transposed copy is updated by AdamW tiles, not chunks
+    bool tiled = false;
+    for (const TransposeJob& j : h->tjobs) tiled = tiled || j.src == o;
+    if (tiled && !h->po.is2d[i]) {
+      delete h;
+      return fail(GPT_EINVAL, "internal: a transposed weight is not 2-D");
+    }
+    for (int64_t c = 0; c < n; c += kChunk) {
+      const int32_t cnt = (int32_t)std::min<int64_t>(kChunk, n - c);
+      if (!tiled) h->chunks.push_back({o + c, cnt, h->po.is2d[i]});
+      h->init_segs.push_back({o + c, cnt, 0, sd, val});
+    }
   }
   const int64_t nb = h->po.total * 4;
   hipError_t e = hipSuccess;
@@ -958,10 +975,9 @@ int gpt_adamw_step(Model* h, float lr, float beta1, float beta2, float eps, floa
   const WsOff& w = h->wo;
   CK(adamw_launch(h->params, h->grads, h->m, h->v,
                   h->h16() ? h->at<h16_t>(w.shadow) : nullptr, h->po.total,
-                  h->at<AdamChunk>(w.chunks), w.nchunks, h->at<double>(w.norm_part),
-                  h->at<float>(w.scal), norm_out, lr, beta1, beta2, eps, weight_decay, max_norm, t,
-                  skip_nonfinite, s));
-  CK(h->refresh_transposes(s));
+                  h->at<AdamChunk>(w.chunks), (int)h->chunks.size(), h->tiles(),
+                  h->at<double>(w.norm_part), h->at<float>(w.scal), norm_out, lr, beta1, beta2, eps,
+                  weight_decay, max_norm, t, skip_nonfinite, s));
   return GPT_OK;
 }
 
@@ -978,11 +994,10 @@ int gpt_amp_step(Model* h, float lr, float beta1, float beta2, float eps, float 
   hipStream_t s = (hipStream_t)stream;
   const WsOff& w = h->wo;
   CK(adamw_amp_launch(h->params, h->grads, h->m, h->v, h->h16() ? h->at<h16_t>(w.shadow) : nullptr,
-                      h->po.total, h->at<AdamChunk>(w.chunks), w.nchunks,
+                      h->po.total, h->at<AdamChunk>(w.chunks), (int)h->chunks.size(), h->tiles(),
                       h->at<double>(w.norm_part), h->at<float>(w.scal), norm_out, lr, beta1, beta2,
                       eps, weight_decay, max_norm, (float*)scaler, growth_factor, backoff_factor,
                       growth_interval, s));
-  CK(h->refresh_transposes(s));
   return GPT_OK;
 }
 

@@ -116,14 +116,23 @@ int gemv_launch(bool h16, int epi, const void* A, const float* ln_w, const float
                 int ldo, void* kv, int H, int hs, int max_len, int pos, hipStream_t s);
 
 int adamw_norm_blocks();
+// Weight matrices updated by 64 x 64 tiles, each also writing its transposed
+// 16-bit copy (jobs as for transpose_h16_launch, dstT its destination base);
+// ntiles = 0: none (every tensor in the flat chunks).
+struct TileJobs {
+  h16_t* dstT = nullptr;
+  const TransposeJob* jobs = nullptr;
+  int njobs = 0, ntiles = 0;
+};
 int adamw_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
-                 const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
-                 float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
-                 float max_norm, int t, int skip_nonfinite, hipStream_t s);
+                 const AdamChunk* chunks, int nchunks, const TileJobs& tj, double* norm_part,
+                 float* scal, float* norm_out, float lr, float beta1, float beta2, float eps,
+                 float wd, float max_norm, int t, int skip_nonfinite, hipStream_t s);
 // the same with dynamic loss scaling; scaler: device {scale, growth_tracker,
 // steps, found_inf} (float, int32 x3), read and updated in place
 int adamw_amp_launch(float* p, const float* g, float* m, float* v, h16_t* shadow, int64_t n,
-                     const AdamChunk* chunks, int nchunks, double* norm_part, float* scal,
+                     const AdamChunk* chunks, int nchunks, const TileJobs& tj,
+                     double* norm_part, float* scal,
                      float* norm_out, float lr, float beta1, float beta2, float eps, float wd,
                      float max_norm, float* scaler, float growth, float backoff, int interval,
                      hipStream_t s);
