@@ -459,6 +459,68 @@ def test_tokens_per_iter_and_flops_formula():
     assert O.flops_per_token(cfg, 1024) == 6 * N + 12 * 12 * 12 * 64 * 1024 == 855_383_040
 
 
+class _FlopCounter(np.ndarray):
+    """An ndarray that adds 2*m*n*k to a class counter for every matrix
+    product it takes part in (broadcast batch included) and keeps the type
+    through every ufunc, so a whole oracle pass can be counted."""
+    flops = 0
+
+    def __array_ufunc__(self, ufunc, method, *inputs, out=None, **kw):
+        args = [a.view(np.ndarray) if isinstance(a, _FlopCounter) else a for a in inputs]
+        if out is not None:
+            kw["out"] = tuple(o.view(np.ndarray) if isinstance(o, _FlopCounter) else o for o in out)
+        if ufunc is np.matmul and method == "__call__":
+            a, b = np.asarray(args[0]), np.asarray(args[1])
+            m = a.shape[-2] if a.ndim > 1 else 1
+            n = b.shape[-1] if b.ndim > 1 else 1
+            batch = np.broadcast_shapes(a.shape[:-2], b.shape[:-2])
+            _FlopCounter.flops += 2 * m * n * a.shape[-1] * int(np.prod(batch, dtype=np.int64))
+        res = getattr(ufunc, method)(*args, **kw)
+        if out is not None:
+            return out[0] if len(out) == 1 else out
+        if isinstance(res, np.ndarray):
+            return res.view(_FlopCounter)
+        if isinstance(res, tuple):
+            return tuple(r.view(_FlopCounter) if isinstance(r, np.ndarray) else r for r in res)
+        return res
+
+
+class _CountingNumpy:
+    """The numpy module as the oracle sees it, except that asarray hands back
+    counting arrays."""
+
+    def __getattr__(self, name):
+        return getattr(np, name)
+
+    @staticmethod
+    def asarray(a, dtype=None):
+        return np.asarray(a, dtype=dtype).view(_FlopCounter)
+
+
+def test_flops_formula_against_the_oracles_counted_products(monkeypatch):
+    """The model FLOPs per token of "nanoGPT" Part IV Stage 6 (6N + 12 L H Q
+    T) against the multiply-adds the oracle actually performs in one forward
+    and backward: every product counted as it runs.  The oracle's products
+    are the weight matrices' (forward, input gradient and weight gradient:
+    6 per matrix weight per token) and the dense T x T attention (Q K^T and
+    P V forward, four products backward: 12 L H Q T per token); the formula's
+    N also counts the biases and LayerNorm parameters, which take no product,
+    so the two differ by exactly 6 (13 L d + 2 d) per token."""
+    w = dict(synth.WORKLOADS["tiny"])
+    cfg = cfg_of(w)
+    params = synth.init_params(w, seed=1337)
+    idx, tgt = synth.tokens(w, seed=1338)
+    B, T = idx.shape
+    monkeypatch.setattr(O, "np", _CountingNumpy())
+    _FlopCounter.flops = 0
+    O.loss_and_grads(params, idx, tgt, cfg)
+    counted = _FlopCounter.flops
+    monkeypatch.undo()
+    L, d, H, hs, Vp = cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.head_dim, cfg.padded_vocab
+    assert counted == B * T * (6 * (12 * L * d * d + Vp * d) + 12 * L * H * hs * T)
+    assert counted // (B * T) + 6 * (13 * L * d + 2 * d) == O.flops_per_token(cfg, T)
+
+
 def test_zipf_generator_law():
     idx, _ = synth.zipf_tokens(64, 1024, 50257, seed=3)
     counts = np.bincount(idx.reshape(-1), minlength=50257)
