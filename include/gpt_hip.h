@@ -106,8 +106,11 @@ int gpt_query_sizes(const gpt_config* cfg, int64_t* n_params, int64_t* workspace
  * 0.  The normals come from Philox4x32-10 under the 64-bit seed through the
  * Box-Muller transform; element i's value depends only on i and the seed.
  * seed is unused when init_params is not NULL.
- * adam_m, adam_v and grads are zeroed.  The 16-bit weight copy (16-bit
- * modes) is written.  The buffers must stay valid until gpt_destroy. */
+ * adam_m, adam_v and grads are zeroed.  In the 16-bit modes the 16-bit
+ * copy of the weights and the transposed copies of the weight matrices (in
+ * the workspace) are written here and, after that, by gpt_adamw_step and
+ * gpt_amp_step: a caller that writes params itself must create a new handle
+ * for the copies to follow.  The buffers must stay valid until gpt_destroy. */
 int gpt_init(gpt_model** out, const gpt_config* cfg, float* params, float* grads,
              float* adam_m, float* adam_v, void* workspace, const float* init_params,
              uint64_t seed, void* stream);
