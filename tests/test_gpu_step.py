@@ -340,6 +340,7 @@ def test_fused_head_cross_entropy_step_parity(batch, T, seed, mask):
     ref_loss, ref_g, _ = O.loss_and_grads(params, idx, ref_tgt, ocfg(dims))
     m = bd.GPT(dims, bd.GPT_BF16, max_batch=batch, init_params=params)
     di, dt = dev_tokens(idx, tgt)
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, 0)
     loss, _ = m.forward(di, dt)
     m.backward()
     torch.cuda.synchronize()
@@ -357,6 +358,38 @@ def test_fused_head_cross_entropy_step_parity(batch, T, seed, mask):
     check_grads(dims, got_g, sep_g, min_cos=0.999)
     print(f"fused loss {got_loss:.5f} separate {sep_loss:.5f} oracle {ref_loss:.5f}; "
           f"lowest cosines {worst}", flush=True)
+    m.close()
+
+
+@pytest.mark.parametrize("fused", [1, 0])
+def test_single_position_and_no_valid_target(fused):
+    """Degenerate inputs of the loss, both head paths: sequences of one
+    position (T = 1) against the oracle; and a batch whose every target is
+    ignored, where the mean over no targets is 0 (the oracle's reading) and
+    every gradient is exactly zero, the evaluation loss too."""
+    dims = dict(synth.WORKLOADS["gpt2"], n_layer=2)
+    case(f"gpt2 bf16 2 layers T=1 and all targets ignored, fused head {fused}")
+    params = synth.init_params(dims, seed=1401)
+    idx, tgt = synth.tokens(dims, seed=1402, batch=4, T=1)
+    ref_loss, ref_g, _ = O.loss_and_grads(params, idx, tgt, ocfg(dims))
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=4, init_params=params)
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, fused)
+    loss, _ = m.forward(*dev_tokens(idx, tgt))
+    m.backward()
+    torch.cuda.synchronize()
+    assert abs(float(loss.item()) - ref_loss) <= 2e-2, (float(loss.item()), ref_loss)
+    check_grads(dims, to_np(m.grads), ref_g, min_cos=0.995)
+    idx2, tgt2 = synth.tokens(dims, seed=1403, batch=4, T=37)
+    tgt2[:] = -1
+    ref_loss2, ref_g2, _ = O.loss_and_grads(params, idx2, tgt2, ocfg(dims))
+    assert ref_loss2 == 0.0 and not ref_g2.any()
+    loss, _ = m.forward(*dev_tokens(idx2, tgt2))
+    m.backward()
+    torch.cuda.synchronize()
+    assert float(loss.item()) == 0.0
+    assert float(m.grads.abs().max().item()) == 0.0
+    assert float(m.eval_loss(*dev_tokens(idx2, tgt2)).item()) == 0.0
+    assert m.read_flags() == 0
     m.close()
 
 
