@@ -86,11 +86,17 @@ def gemm_groups(B, T, dims):
 
 
 def sources_hash():
+    """Hash of the product kernels' sources with comments and blank space
+    removed, so that an edit of a comment does not void measured counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
     return h.hexdigest()[:16]
 
 

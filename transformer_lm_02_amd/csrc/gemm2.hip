@@ -484,8 +484,9 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
     };
     if constexpr (EPI == EPI_HEAD) {
       // p~ = exp(z) below V (0 above), the target's z, and the sum of p~ over
-      // this wave's 96 columns of each row: the LPR lanes of a row add their
-      // sums in lane order
+      // this wave's 96 columns of each row: each of the LPR lanes of a row
+      // sums its 8 columns, and after the slab one lane per row adds the 12
+      // sums in a fixed order
       static_assert(LPR == 12, "row sums assume 12 lanes a row");
       const int blk = (n0 + wn * WC) / 96;
       float* ps = (float*)(ys + BM) + wave * 32 * 12;
