@@ -465,6 +465,39 @@ def test_bf16_causal_invariance_bit_identical():
     m.close()
 
 
+# ---------------------------------------------------------------- the largest supported shapes
+WIDEST = dict(vocab_size=500, padded_vocab=512, block_size=64, n_layer=1, n_head=32,
+              n_embd=2048, batch=2, tokens="uniform")
+LONGEST_ROW = dict(vocab_size=53200, padded_vocab=53248, block_size=64, n_layer=1, n_head=1,
+                   n_embd=64, batch=2, tokens="zipf")
+
+
+@pytest.mark.parametrize("name,dims,fused", [("widest", WIDEST, 1),
+                                             ("longest row, fused head", LONGEST_ROW, 1),
+                                             ("longest row, separate pass", LONGEST_ROW, 0)])
+def test_largest_supported_shapes_match_oracle(name, dims, fused):
+    """The limits the boundary accepts in bf16 mode: a width of 2048 (the
+    LayerNorm kernels' longest row, 32 heads of 64) and a padded vocabulary of
+    53248 columns (the separate cross-entropy pass's longest row, also run
+    through the fused head), against the oracle: loss within 2e-2, per-tensor
+    gradient cosine >= 0.995."""
+    case(f"bf16 {name}")
+    params = synth.init_params(dims, seed=1501)
+    idx, tgt = synth.tokens(dims, seed=1502, batch=2, T=64)
+    ref_loss, ref_g, _ = O.loss_and_grads(params, idx, tgt, ocfg(dims))
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=2, init_params=params)
+    m.set_option(bd.GPT_OPT_FUSED_HEAD_CE, fused)
+    loss, _ = m.forward(*dev_tokens(idx, tgt))
+    m.backward()
+    torch.cuda.synchronize()
+    got = float(loss.item())
+    assert abs(got - ref_loss) <= 2e-2, (got, ref_loss)
+    worst = check_grads(dims, to_np(m.grads), ref_g, min_cos=0.995)
+    print(f"loss gpu {got:.5f} oracle {ref_loss:.5f}; lowest cosines {worst}", flush=True)
+    assert m.read_flags() == 0
+    m.close()
+
+
 # ---------------------------------------------------------------- AdamW on identical inputs
 @pytest.mark.parametrize("max_norm,scale", [(1.0, 1e-3), (1.0, 1.0), (0.0, 1e-2)])
 def test_adamw_kernel_matches_oracle(max_norm, scale):
