@@ -533,6 +533,8 @@ __global__ __launch_bounds__(256) void init_params_kernel(float* __restrict__ p,
 // times the stored row; h2[m] = r * h[m] in 16 bits (the weight gradient's
 // token-side operand).  p~ overflows or vanishes for logits beyond about
 // +-80: a valid row with S outside [1e-28, 1e28] raises flag bit 4.
+#define HEAD_MAXP 9  // row-sum blocks per lane: npart <= 576 (rows of up to 55296 columns)
+#define HEAD_MAXH 4  // 16-byte chunks of x per lane: C <= 2048
 __global__ __launch_bounds__(256) void head_combine_kernel(
     const float* __restrict__ part, int npart, const float* __restrict__ zy,
     const int32_t* __restrict__ tgt, int V, const int* __restrict__ n_valid, float loss_scale,
@@ -543,8 +545,14 @@ __global__ __launch_bounds__(256) void head_combine_kernel(
   const int lane = threadIdx.x & 63;
   if (row >= M) return;  // uniform per wave
   const float* pr = part + row * npart;
+  // every load issued before any is used (indices clamped into the row, the
+  // extra values masked to zero): the same per-lane order as a strided loop
+  float pv[HEAD_MAXP];
+#pragma unroll
+  for (int i = 0; i < HEAD_MAXP; ++i) pv[i] = pr[min(lane + 64 * i, npart - 1)];
   float acc = 0.f;
-  for (int j = lane; j < npart; j += 64) acc += pr[j];
+#pragma unroll
+  for (int i = 0; i < HEAD_MAXP; ++i) acc += lane + 64 * i < npart ? pv[i] : 0.f;
   const float S = wave_sum(acc);
   const int y = tgt[row];
   const bool valid = y >= 0 && y < V;
@@ -560,13 +568,19 @@ __global__ __launch_bounds__(256) void head_combine_kernel(
   }
   const h16_t* hr = h + row * C;
   h16_t* o = h2 + row * C;
-  for (int j = lane; j < C / 8; j += 64) {
-    const uint4 w = *(const uint4*)(hr + 8 * j);
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-    uint32_t q[4];
+  uint4 hv[HEAD_MAXH];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = pack2h(r * h_lo(u[k]), r * h_hi(u[k]));
-    *(uint4*)(o + 8 * j) = make_uint4(q[0], q[1], q[2], q[3]);
+  for (int i = 0; i < HEAD_MAXH; ++i) hv[i] = *(const uint4*)(hr + 8 * min(lane + 64 * i, C / 8 - 1));
+#pragma unroll
+  for (int i = 0; i < HEAD_MAXH; ++i) {
+    const int j = lane + 64 * i;
+    if (j < C / 8) {
+      const uint32_t u[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+      uint32_t q[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[k] = pack2h(r * h_lo(u[k]), r * h_hi(u[k]));
+      *(uint4*)(o + 8 * j) = make_uint4(q[0], q[1], q[2], q[3]);
+    }
   }
 }
 
@@ -578,7 +592,7 @@ int head_combine_launch(const float* part, int npart, const float* zy, const int
                         const int* n_valid, float loss_scale, const float* dscale, const h16_t* h,
                         int C, float* row_loss, float* r, h16_t* h2, h16_t* logits, int ldv, int M,
                         int* flags, hipStream_t s) {
-  if (C % 8) return -5;
+  if (C % 8 || C > 8 * 64 * HEAD_MAXH || npart < 1 || npart > 64 * HEAD_MAXP) return -5;
   hipLaunchKernelGGL(head_combine_kernel, dim3(cdiv(M, 4)), dim3(256), 0, s, part, npart, zy, tgt, V,
                      n_valid, loss_scale, dscale, h, C, row_loss, r, h2, logits, ldv, M, flags);
   return hipGetLastError() == hipSuccess ? 0 : -4;
