@@ -418,8 +418,9 @@ int gpt_op_attention_fwd(int32_t dtype, const void* qkv, void* out, float* lse,
                          int32_t B, int32_t T, int32_t H, int32_t C, void* stream);
 
 /* Its backward: dout act [B*T][C] -> dqkv act [B*T][3*C] (every element
- * written).  D: fp32 scratch [2][B][H][T]; D[0] receives rowsum(dout * out),
- * D[1] the row logsumexp times log2(e). */
+ * written).  D: fp32 scratch [2][B][H][T]; D[0] receives rowsum(dout * out)
+ * (negated in 16-bit modes at head width 64), D[1] the row logsumexp times
+ * log2(e). */
 int gpt_op_attention_bwd(int32_t dtype, const void* qkv, const void* out,
                          const float* lse, const void* dout, void* dqkv, float* D,
                          int32_t B, int32_t T, int32_t H, int32_t C, void* stream);

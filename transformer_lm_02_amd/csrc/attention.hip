@@ -417,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(const h16_t* __restri
 // the diagonal on.  S = Q K^T and dP = dO V^T put one key per lane; P^T and
 // dS^T are then the A operands of dV += P^T dO and dK += dS^T Q, whose B
 // operands are transposing reads of the dO and Q tiles.  Dg holds
-// rowsum(dO * O) at [0, B*H*T) and the row logsumexp times log2(e) at
+// -rowsum(dO * O) at [0, B*H*T) and the row logsumexp times log2(e) at
 // [B*H*T, 2*B*H*T).
 // DROP: each stage also brings the forward's kept bits of its 64 queries for
 // this workgroup's 128 keys (4 runs of 64 words: key block 0/1 x lane half
@@ -513,7 +513,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
     // live accumulators (S, dP, dK, dV) within 256 registers
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      // dP starts from -D of its query rows (read from LDS into the
+      // accumulator), so the products leave dP - D
       f32x16_t sa = zero16(), dpa = zero16();
+      if constexpr (!DROP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dpa[r] = sD[32 * t + ACC_ROW(r, lane)];
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         sa = MFMA32(frag_hd(tQ, 32 * t, ks, lane), fk[ks], sa);
@@ -538,14 +544,13 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dkdv_kernel(
         for (int r = 0; r < 16; ++r) {
           const int qq = 32 * t + ACC_ROW(r, lane);
           const float z = (sM[qq] >> kbit) & 1u ? dr.scale : 0.f;
-          dpa[r] = sa[r] * (z * dpa[r] - sD[qq]);
+          dpa[r] = sa[r] * (z * dpa[r] + sD[qq]);
           sa[r] *= z;
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qq = 32 * t + ACC_ROW(r, lane);
-          dpa[r] = sa[r] * (dpa[r] - sD[qq]);
+          dpa[r] = sa[r] * dpa[r];
         }
       }
 #pragma unroll
@@ -658,13 +663,20 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
   const float sc = LOG2E * 0.125f;
   const float L2q = my_q < Tn ? lse[(int64_t)bh * Tn + my_q] * LOG2E : 0.f;
   const float nL2 = -L2q;
-  // D and the scaled logsumexp of every query row, for the key-side kernel
+  // -D and the scaled logsumexp of every query row, for the key-side kernel
   // that runs next
   if (lane < 32 && my_q < Tn) {
-    Dg[(int64_t)bh * Tn + my_q] = Dq;
+    Dg[(int64_t)bh * Tn + my_q] = -Dq;
     Dg[bht + (int64_t)bh * Tn + my_q] = L2q;
   }
   f32x16_t dq[2] = {zero16(), zero16()};
+  // without dropout every dP accumulation starts from -D of the lane's query
+  // (a loop-invariant accumulator input), so the products leave dP - D
+  f32x16_t dp0 = zero16();
+  if constexpr (!DROP) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp0[r] = -Dq;
+  }
   const int nkv = (min(Tn, q0 + 128) + 63) / 64;
 #pragma unroll
   for (int st = 0; st < FLASH_NS - 1; ++st)
@@ -693,7 +705,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
         mw = dmask[((int64_t)(bh * nkb + kb) * 2 + (lane >> 5)) * Tn + my_q];
       }
     }
-    f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+    f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {dp0, dp0};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -726,7 +738,7 @@ __global__ __launch_bounds__(256, 2) void flash_bwd_dq_kernel(
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[t][r] = s[t][r] * (dp[t][r] - Dq);
+        for (int r = 0; r < 16; ++r) dp[t][r] = s[t][r] * dp[t][r];
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -805,12 +817,12 @@ int attention_fwd_launch(bool h16, const void* qkv, void* out, float* lse, int B
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// D: fp32 scratch of 2*B*H*T elements (rowsum(dout * out), then the row
-// logsumexp times log2(e) for the 16-bit head-width-64 kernels).  dr: the
-// forward's dropout of the probabilities (rowsum(dout * out) is still the
-// row's D with dropout: it equals rowsum(P * dP) for dP = z dP~); the
-// head-width-64 16-bit kernels read the forward's kept bits from dmask, the
-// others regenerate them.
+// D: fp32 scratch of 2*B*H*T elements (rowsum(dout * out), negated by the
+// 16-bit head-width-64 kernels, then the row logsumexp times log2(e) for
+// those kernels).  dr: the forward's dropout of the probabilities
+// (rowsum(dout * out) is still the row's D with dropout: it equals
+// rowsum(P * dP) for dP = z dP~); the head-width-64 16-bit kernels read the
+// forward's kept bits from dmask, the others regenerate them.
 // cs_part / cs_out (optional): cs_out[n] (+)= column sums of dqkv (the bias
 // gradient of the fused q|k|v projection); cs_part is fp32 scratch of at
 // least max(B * cdiv(Tn, 128), colsum_part_rows(B * Tn)) x 3C elements.
