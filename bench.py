@@ -67,14 +67,17 @@ TRAFFIC_SOURCES = ["transformer_lm_02_amd/csrc/gemm2.hip", "transformer_lm_02_am
 def gemm_groups(B, T, dims):
     """name -> (kernel template, entry point, [(M, N, K, launches per step)]).
     Shapes are the entry point's: linear C[M][N] = A[M][K] B[N][K]^T;
-    linear_dw dW[N][K] = dY[M][N]^T X[M][K]; gelu / gelu_bwd as linear."""
+    linear_dw_seq dW[N][K] = dY[M][N]^T X[M][K], launched in the backward's
+    order (the head, then per layer the first four shapes in turn);
+    gelu / gelu_bwd as linear."""
     M, d, L = B * T, dims["n_embd"], dims["n_layer"]
     vi = -(-dims["padded_vocab"] // 64) * 64
     return {
         "weight_gradients": (
-            "gemm2_kernel<128, 128, false, false, 5, 2, 64, 2> + splitk_reduce_kernel",
-            "linear_dw",
-            [(M, d, 4 * d, L), (M, 4 * d, d, L), (M, d, d, L), (M, 3 * d, d, L), (M, vi, d, 1)]),
+            "gemm2_kernel<128, 128, false, false, 5, 2, 64, 2> (split-K reductions inside the "
+            "next launch) + splitk_reduce_kernel",
+            "linear_dw_seq",
+            [(M, vi, d, 1), (M, d, 4 * d, L), (M, 4 * d, d, L), (M, d, d, L), (M, 3 * d, d, L)]),
         "input_gradients_and_qkv": (
             "gemm2_kernel<128, 192, true, true, 0, 2, 64, 2>", "linear",
             [(M, d, 4 * d, L), (M, d, 3 * d, L), (M, d, d, L), (M, 3 * d, d, L)]),
@@ -118,7 +121,7 @@ def group_operands(torch, shapes, entry, dt):
     g = torch.Generator(device="cuda").manual_seed(7)
     ops = []
     for (M, N, K, n) in shapes:
-        if entry == "linear_dw":
+        if entry == "linear_dw_seq":
             a = (torch.randn((M, N), device="cuda", generator=g) * 1e-3).to(dt)
             b = (torch.randn((M, K), device="cuda", generator=g)).to(dt)
             c = torch.empty((N, K), dtype=torch.float32, device="cuda")
@@ -136,15 +139,22 @@ def launch_group(bd, entry, ops, ws, stream_ptr, reps=1):
     import ctypes
     vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    if entry == "linear_dw_seq":
+        # the backward's order: shapes with one launch first (the head), then
+        # one launch of every other shape per layer
+        once = [o for o in ops if o[-1] == 1]
+        per = [o for o in ops if o[-1] > 1]
+        seq = once + [o for _ in range(max([o[-1] for o in per] or [0])) for o in per]
+        items = [(o[0], o[1], o[2], False) for o in seq]
+        for _ in range(reps):
+            bd.op_linear_dw_seq(items, ws)
+        return
     for _ in range(reps):
         for (a, b, c, aux, M, N, K, n) in ops:
             dt = bd._bf(a)
             for _ in range(n):
                 if entry == "linear":
                     rc = bd.lib.gpt_op_linear(dt, vp(a), vp(b), None, vp(c), 0, M, N, K, stream_ptr)
-                elif entry == "linear_dw":
-                    rc = bd.lib.gpt_op_linear_dw(dt, vp(a), vp(b), vp(c), 0, M, N, K, vp(ws), wsb,
-                                                 stream_ptr)
                 elif entry == "gelu":
                     rc = bd.lib.gpt_op_linear_gelu(dt, vp(a), vp(b), None, vp(c), vp(aux), M, N, K,
                                                    stream_ptr)
@@ -184,7 +194,17 @@ def time_gemm_groups(torch, bd, B, T, dims, reps=3, fp16=False):
     return out
 
 
-def roofline_from_groups(groups, fp16=False):
+def roofline_from_groups(groups, fp16=False, instep=None):
+    """The group with the largest time per step.  instep: the weight-gradient
+    group timed inside training steps (events around its launches), which
+    then replaces that group's replay through the single-op entry point."""
+    replay = {k: round(v["ms_per_step"], 4) for k, v in groups.items()}
+    if instep and "weight_gradients" in groups:
+        g = dict(groups["weight_gradients"])
+        assert round(instep["launches_per_step"]) == g["launches_per_step"], instep
+        g["ms_per_step"] = instep["ms_per_step"]
+        g["timing"] = f"in-step HIP events over {instep['steps']} steps"
+        groups = dict(groups, weight_gradients=g)
     name = max(groups, key=lambda k: groups[k]["ms_per_step"])
     g = groups[name]
     n = g["launches_per_step"]
@@ -196,7 +216,9 @@ def roofline_from_groups(groups, fp16=False):
             "traffic": None if fp16 else measured_traffic(name),
             "launches_per_step": n, "ms_per_launch": round(ms_launch, 4),
             "flops_per_launch": g["flops_per_step"] / n,
-            "groups_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in groups.items()}}
+            "timing": g.get("timing", "replay of the step's launches through the single-op entry "
+                                      "point"),
+            "groups_ms_per_step_replayed": replay}
 
 
 def probe(torch, bd, B, T, dims, group):
@@ -428,6 +450,20 @@ def main():
     print(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), loss {loss:.4f}, "
           f"norm {norm:.4f}, MFU {mfu:.4f}", file=sys.stderr, flush=True)
     scaler = model.scaler_state() if args.fp16 else None
+    instep = None
+    if not args.no_kernel_timing and headline:
+        # the weight-gradient launches timed inside the step: HIP events the
+        # library records on its stream around each of them.  The events cost
+        # ~0.3 ms per step, so they run on further steps of the same workload
+        # right after the timed ones, not inside them.
+        n_ev = 10
+        model.set_option(bd.GPT_OPT_TIME_WEIGHT_GRADIENTS, 1)
+        for i in range(n_ev):
+            step(args.warmup + args.steps + i)
+        torch.cuda.synchronize()
+        ev_ms, ev_n = model.read_timing()
+        model.set_option(bd.GPT_OPT_TIME_WEIGHT_GRADIENTS, 0)
+        instep = {"ms_per_step": ev_ms / n_ev, "launches_per_step": ev_n / n_ev, "steps": n_ev}
     roof = None
     model.close()
     del model
@@ -435,7 +471,7 @@ def main():
     if not args.no_kernel_timing and headline:
         print("[bench] timing the step's matrix products by kernel", file=sys.stderr, flush=True)
         roof = roofline_from_groups(time_gemm_groups(torch, bd, B, T, dims, fp16=args.fp16),
-                                    fp16=args.fp16)
+                                    fp16=args.fp16, instep=instep)
         torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline and headline:

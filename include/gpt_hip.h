@@ -328,11 +328,23 @@ int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float tem
  * Applies to gpt_forward_loss with targets and without logits_out in
  * GPT_BF16 mode (other modes and calls keep the separate pass).  It carries
  * logits within about +-64 (GPT_FLAG_HEAD_RANGE otherwise).
+ * GPT_OPT_TIME_WEIGHT_GRADIENTS (value 0 or 1, default 0): gpt_backward
+ * records a HIP event on its stream before and after each weight-gradient
+ * launch ("Let's reproduce GPT-2 (124M)", "Speed Stack": time what the step
+ * spends where), for gpt_read_timing.  Only the time between the events is
+ * measured; the results of the step do not change.
  * Errors: GPT_EINVAL (null handle, unknown option or value). */
-enum { GPT_OPT_FUSED_HEAD_CE = 1 };
+enum { GPT_OPT_FUSED_HEAD_CE = 1, GPT_OPT_TIME_WEIGHT_GRADIENTS = 2 };
 int gpt_set_option(gpt_model* h, int32_t option, int32_t value);
 /* The current value of an option into *value.  Errors: GPT_EINVAL. */
 int gpt_get_option(gpt_model* h, int32_t option, int32_t* value);
+
+/* With GPT_OPT_TIME_WEIGHT_GRADIENTS on: waits for the events recorded since
+ * the last call, puts the summed time of the weight-gradient launches they
+ * bracket in *ms (milliseconds) and their number in *launches (the final
+ * split-K reduction of a backward is counted with the last launch), and
+ * starts over.  Errors: GPT_EINVAL (null pointer), GPT_EHIP. */
+int gpt_read_timing(gpt_model* h, double* ms, int64_t* launches);
 
 /* Synchronise `stream`, return the device flags (GPT_FLAG_*) raised since the
  * last call in *flags, and clear them. */
@@ -404,6 +416,22 @@ int gpt_op_linear_gelu_bwd_noalloc(int32_t dtype, const void* dY, const void* Wt
 int gpt_op_linear_dw(int32_t dtype, const void* dY, const void* X, float* dW,
                      int32_t accumulate, int32_t M, int32_t N, int32_t K,
                      float* workspace, int64_t workspace_bytes, void* stream);
+
+/* count weight gradients in the order given, as the training backward
+ * launches its own: product i is gpt_op_linear_dw(dtype, dY[i], X[i], dW[i],
+ * accumulate[i], M[i], N[i], K[i], ...), with the same results bit for bit.
+ * dY, X, dW: host arrays of device pointers; accumulate, M, N, K: host arrays
+ * of count values.  A product whose reduction over M is split leaves its
+ * partial sums to the next product's launch, which adds them (in the same
+ * fixed order) with workgroups beside its own tiles; the last product's are
+ * added after the sequence.  workspace: optional device fp32 scratch
+ * (NULL: no split), used as two halves.  The dW of consecutive products must
+ * not overlap unless they are the same pointer (the earlier reduction then
+ * runs first).  On error the dW are unspecified. */
+int gpt_op_linear_dw_seq(int32_t dtype, int32_t count, const void* const* dY,
+                         const void* const* X, float* const* dW, const int32_t* accumulate,
+                         const int32_t* M, const int32_t* N, const int32_t* K,
+                         float* workspace, int64_t workspace_bytes, void* stream);
 
 /* dX = dY W: dY act [M][N], W act [N][K], dX fp32 [M][K].  The input
  * gradient of a Linear layer. */

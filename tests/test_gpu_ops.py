@@ -65,6 +65,49 @@ def test_linear_dw_bf16(M, N, K, split):
     assert rel_err(got2, ref + 1.0) < 1e-5
 
 
+def test_linear_dw_seq_equals_one_at_a_time():
+    """gpt_op_linear_dw_seq, where each product's split-K reduction runs
+    inside the next product's launch, against gpt_op_linear_dw called once
+    per product in the same order: equal bit for bit.  The sequence holds
+    split products (4096 tokens, 16 splits), one with enough tiles not to
+    split, two in a row adding into one gradient, one on the plain kernel
+    (300 tokens) after a pending reduction, and accumulation."""
+    case("linear_dw_seq vs linear_dw, 7 products")
+    seq = [  # (M tokens, N, K, accumulate, gradient index)
+        (4096, 768, 256, 0, 0),
+        (4096, 256, 768, 1, 1),
+        (1024, 3072, 2304, 0, 2),
+        (4096, 384, 384, 0, 3),
+        (4096, 384, 384, 1, 3),
+        (300, 104, 136, 1, 4),
+        (4096, 768, 256, 1, 0),
+    ]
+    shapes = {0: (768, 256), 1: (256, 768), 2: (3072, 2304), 3: (384, 384), 4: (104, 136)}
+    inputs = [(to_dev(bf16_round(rnd((M, N), 40 + i, 0.01)), torch.bfloat16),
+               to_dev(bf16_round(rnd((M, K), 50 + i)), torch.bfloat16))
+              for i, (M, N, K, _, _) in enumerate(seq)]
+    init = {g: rnd(s, 60 + g) for g, s in shapes.items()}
+    ws = torch.empty(3 * 16 * 768 * 256, dtype=torch.float32, device="cuda")
+    one = {g: torch.as_tensor(v).cuda() for g, v in init.items()}
+    for (M, N, K, acc, g), (dY, X) in zip(seq, inputs):
+        if acc:
+            bd.op_linear_dw(dY, X, one[g], workspace=ws)
+        else:
+            one[g].copy_(bd.op_linear_dw(dY, X, workspace=ws))
+    chained = {g: torch.as_tensor(v).cuda() for g, v in init.items()}
+    bd.op_linear_dw_seq([(dY, X, chained[g], acc)
+                         for (M, N, K, acc, g), (dY, X) in zip(seq, inputs)], ws)
+    torch.cuda.synchronize()
+    for g in shapes:
+        a, b = to_np(one[g]), to_np(chained[g])
+        assert np.array_equal(a, b), (g, float(np.abs(a - b).max()))
+    # and the values themselves: gradient 3 is the sum of its two products
+    M, N, K, _, _ = seq[3]
+    ref = sum(to_np(dY).astype(np.float64).T @ to_np(X).astype(np.float64)
+              for dY, X in inputs[3:5])
+    assert rel_err(to_np(chained[3]), ref) < 1e-5
+
+
 @pytest.mark.parametrize("M,N,K", [(16384, 768, 768), (300, 200, 136), (512, 50304, 768),
                                    (1000, 3072, 768), (257, 4800, 1600), (4100, 768, 6400)])
 def test_linear_dx_bf16(M, N, K):

@@ -631,6 +631,39 @@ def test_weight_copies_after_a_step_equal_fresh_copies(mode_name):
     b.close()
 
 
+def test_weight_gradient_timing_leaves_the_step_unchanged():
+    """GPT_OPT_TIME_WEIGHT_GRADIENTS records events around the backward's
+    weight-gradient launches: the gradients are those of a backward without
+    them (up to the order of the embedding backward's atomic additions into
+    wte), and gpt_read_timing counts 4 n_layer + 1 launches per backward
+    (the head's, then four per block) with a positive time, then starts over."""
+    dims = dict(synth.WORKLOADS["char"])
+    case("weight-gradient timing events, char bf16")
+    m = bd.GPT(dims, bd.GPT_BF16, max_batch=8, init_params=synth.perturbed_params(dims, seed=41))
+    toks = dev_tokens(*synth.tokens(dims, seed=42, batch=8))
+    assert m.get_option(bd.GPT_OPT_TIME_WEIGHT_GRADIENTS) == 0
+    grads = []
+    for on in (0, 1, 1):
+        m.set_option(bd.GPT_OPT_TIME_WEIGHT_GRADIENTS, on)
+        m.forward(*toks)
+        m.backward()
+        torch.cuda.synchronize()
+        grads.append(m.grads.cpu().numpy())
+    ms, n = m.read_timing()
+    assert n == 2 * (4 * dims["n_layer"] + 1) and ms > 0.0, (ms, n)
+    assert m.read_timing() == (0.0, 0)
+    for g in grads[1:]:
+        for name, a in per_tensor(dims, g).items():
+            b = per_tensor(dims, grads[0])[name]
+            if name == "wte":
+                assert rel_err(a, b) <= 1e-6, name
+            else:
+                assert np.array_equal(a, b), name
+    with pytest.raises(bd.GptError):
+        m.set_option(bd.GPT_OPT_TIME_WEIGHT_GRADIENTS, 2)
+    m.close()
+
+
 # ---------------------------------------------------------------- error paths
 def test_error_paths_and_bad_token_flag():
     dims = synth.WORKLOADS["tiny"]

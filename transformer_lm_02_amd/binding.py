@@ -31,6 +31,7 @@ GPT_FLAG_BAD_TOKEN = 1
 GPT_FLAG_BAD_TARGET = 2
 GPT_FLAG_HEAD_RANGE = 4
 GPT_OPT_FUSED_HEAD_CE = 1
+GPT_OPT_TIME_WEIGHT_GRADIENTS = 2
 
 
 class gpt_config(ctypes.Structure):
@@ -60,6 +61,7 @@ _SIGS = {
     "gpt_estimate_loss": [_p, _p, _p, _i32, _i32, _i32, _p, _p],
     "gpt_adamw_step": [_p, _f, _f, _f, _f, _f, _f, _i32, _i32, _p, _p],
     "gpt_read_flags": [_p, ctypes.POINTER(_i32), _p],
+    "gpt_read_timing": [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)],
     "gpt_set_option": [_p, _i32, _i32],
     "gpt_get_option": [_p, _i32, ctypes.POINTER(_i32)],
     "gpt_op_linear": [_i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
@@ -67,6 +69,7 @@ _SIGS = {
     "gpt_op_linear_gelu_bwd": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
     "gpt_op_linear_gelu_bwd_noalloc": [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
     "gpt_op_linear_dw": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i64, _p],
+    "gpt_op_linear_dw_seq": [_i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p],
     "gpt_op_linear_dx": [_i32, _p, _p, _p, _i32, _i32, _i32, _p],
     "gpt_op_attention_fwd": [_i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
     "gpt_op_attention_bwd": [_i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p],
@@ -317,6 +320,14 @@ class GPT:
         check(lib.gpt_read_flags(self.handle, ctypes.byref(f), _stream()), "gpt_read_flags")
         return f.value
 
+    def read_timing(self):
+        """(milliseconds, launches) of the weight-gradient launches timed since
+        the last call (GPT_OPT_TIME_WEIGHT_GRADIENTS)."""
+        ms, n = ctypes.c_double(), _i64()
+        check(lib.gpt_read_timing(self.handle, ctypes.byref(ms), ctypes.byref(n)),
+              "gpt_read_timing")
+        return ms.value, n.value
+
     def close(self):
         if getattr(self, "handle", None):
             lib.gpt_destroy(self.handle)
@@ -422,6 +433,22 @@ def op_linear_dw(dY, X, dW=None, workspace=None):
     check(lib.gpt_op_linear_dw(_bf(dY), _ptr(dY), _ptr(X), _ptr(dW), int(acc), M, N, K,
                                _ptr(workspace), wsb, _stream()), "gpt_op_linear_dw")
     return dW
+
+
+def op_linear_dw_seq(items, workspace=None):
+    """gpt_op_linear_dw_seq over items = [(dY, X, dW, accumulate), ...]
+    (dW fp32 [N][K], written or added to)."""
+    n = len(items)
+    ptrs = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
+    ints = lambda vs: (ctypes.c_int32 * n)(*vs)
+    dt = _bf(items[0][0]) if n else GPT_BF16
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.gpt_op_linear_dw_seq(
+        dt, n, ptrs([it[0] for it in items]), ptrs([it[1] for it in items]),
+        ptrs([it[2] for it in items]), ints([int(bool(it[3])) for it in items]),
+        ints([it[0].shape[0] for it in items]), ints([it[0].shape[1] for it in items]),
+        ints([it[1].shape[1] for it in items]), _ptr(workspace), wsb, _stream()),
+        "gpt_op_linear_dw_seq")
 
 
 def op_linear_dx(dY, W):

@@ -227,6 +227,12 @@ int gpt_get_option(gpt_model* h, int32_t option, int32_t* value) {
                  : b16::gpt_get_option((b16::Model*)h->impl, option, value);
 }
 
+int gpt_read_timing(gpt_model* h, double* ms, int64_t* launches) {
+  if (!h) return null_handle();
+  return h->fp16 ? f16::gpt_read_timing((f16::Model*)h->impl, ms, launches)
+                 : b16::gpt_read_timing((b16::Model*)h->impl, ms, launches);
+}
+
 int gpt_read_flags(gpt_model* h, int32_t* flags, void* stream) {
   if (!h) return null_handle();
   return h->fp16 ? f16::gpt_read_flags((f16::Model*)h->impl, flags, stream)
@@ -310,6 +316,14 @@ int gpt_op_linear_dw(int32_t dtype, const void* dY, const void* X, float* dW, in
                      void* stream) {
   return OP(gpt_op_linear_dw, dtype, dY, X, dW, accumulate, M, N, K, workspace, workspace_bytes,
             stream);
+}
+
+int gpt_op_linear_dw_seq(int32_t dtype, int32_t count, const void* const* dY, const void* const* X,
+                         float* const* dW, const int32_t* accumulate, const int32_t* M,
+                         const int32_t* N, const int32_t* K, float* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  return OP(gpt_op_linear_dw_seq, dtype, count, dY, X, dW, accumulate, M, N, K, workspace,
+            workspace_bytes, stream);
 }
 
 int gpt_op_linear_dx(int32_t dtype, const void* dY, const void* W, float* dX, int32_t M, int32_t N,

@@ -45,6 +45,7 @@ std::string& gpt_error_text();
   int gpt_read_flags(Model* h, int32_t* flags, void* stream);                                   \
   int gpt_set_option(Model* h, int32_t option, int32_t value);                                  \
   int gpt_get_option(Model* h, int32_t option, int32_t* value);                                 \
+  int gpt_read_timing(Model* h, double* ms, int64_t* launches);                                 \
   void gpt_destroy(Model* h);                                                                   \
   int gpt_op_linear(int32_t h16, const void* A, const void* B, const float* bias, void* C,      \
                     int32_t out_f32, int32_t M, int32_t N, int32_t K, void* stream);            \
@@ -57,6 +58,10 @@ std::string& gpt_error_text();
   int gpt_op_linear_dw(int32_t h16, const void* dY, const void* X, float* dW,                   \
                        int32_t accumulate, int32_t M, int32_t N, int32_t K, float* workspace,   \
                        int64_t workspace_bytes, void* stream);                                  \
+  int gpt_op_linear_dw_seq(int32_t h16, int32_t count, const void* const* dY,                  \
+                           const void* const* X, float* const* dW, const int32_t* accumulate,   \
+                           const int32_t* M, const int32_t* N, const int32_t* K,                \
+                           float* workspace, int64_t workspace_bytes, void* stream);            \
   int gpt_op_linear_dx(int32_t h16, const void* dY, const void* W, float* dX, int32_t M,        \
                        int32_t N, int32_t K, void* stream);                                     \
   int gpt_op_attention_fwd(int32_t h16, const void* qkv, void* out, float* lse, int32_t B,      \

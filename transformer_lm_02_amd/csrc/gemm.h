@@ -48,6 +48,26 @@ struct ColsumJob {
   int nrow = 0, ncol = 0, seg = 0;
 };
 
+// Weight gradients launched one after another can pass their split-K
+// reductions along: a launch handed a chain writes its partials into one
+// half of the chain's scratch and leaves the reduction pending, and the next
+// such launch runs the pending reduction in workgroups of its own beside its
+// tiles (they use slots the tiles leave free) while its tiles write into the
+// other half.  The reduction adds the partials in split order to the gradient
+// (or to zero), as the standalone reduction does, so results are the same.
+// splitk_chain_flush runs whatever is still pending.
+struct SplitKChain {
+  float* ws[2] = {nullptr, nullptr};  // the two halves of the scratch
+  int64_t ws_bytes = 0;               // bytes of each half
+  int next = 0;                       // the half the next launch writes
+  // the pending reduction, if part is non-null: out[i] = (beta ? out[i] : 0)
+  // + sum over k < ks of part[k * n + i]
+  const float* part = nullptr;
+  float* out = nullptr;
+  int64_t n = 0;
+  int ks = 0, beta = 0;
+};
+
 struct GemmEpiArgs {
   void* out = nullptr;
   void* out2 = nullptr;
@@ -70,6 +90,9 @@ struct GemmEpiArgs {
   Drop drop;
   // EPI_HEAD, EPI_HEAD_DX
   HeadEpi head;
+  // EPI_ACCUM: non-null to take part in a chain of split-K reductions (host
+  // side; the scratch then comes from the chain)
+  SplitKChain* chain = nullptr;
 };
 
 // A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]; likewise B(n,k).
@@ -85,5 +108,8 @@ int gemm_launch(bool h16, bool a_kcontig, bool b_kcontig, int epi,
 
 // split-K scratch the launcher may use for an M x N weight gradient
 inline int64_t gemm_splitk_bytes(int64_t M, int64_t N) { return 16 * M * N * 4; }
+
+// runs the chain's pending reduction, if any, as a launch of its own
+int splitk_chain_flush(SplitKChain* ch, hipStream_t stream);
 
 }  // namespace HALF_NS

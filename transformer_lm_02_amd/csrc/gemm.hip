@@ -348,6 +348,9 @@ int gemm_launch(bool h16, bool a_kcontig, bool b_kcontig, int epi, const void* A
                                 kb_rows, e, ws, ws_bytes, stream);
     if (rc != -5) return rc == 0 ? (hipGetLastError() == hipSuccess ? 0 : -4) : rc;
   }
+  // the plain kernel may use the scratch: a pending chained reduction first
+  if (e.chain)
+    if (const int rc = splitk_chain_flush(e.chain, stream)) return rc;
   const int rc = gemm_launch_plain(h16, a_kcontig, b_kcontig, epi, A, lda, B, ldb, M, N, K,
                                    ka_rows, kb_rows, e, stream, ws, ws_bytes);
   if (rc != 0 || !e.cs_out) return rc;

@@ -137,6 +137,15 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// A previous launch's split-K reduction run by workgroups past the tiles:
+// out[i] = (beta ? out[i] : 0) + sum over k < ks of part[k * 4 n4 + i]
+struct SplitKRed {
+  const float* part = nullptr;
+  float* out = nullptr;
+  int64_t n4 = 0;  // float4 groups
+  int ks = 0, beta = 0, wgs = 0;
+};
+
 struct Gemm2Args {
   const h16_t* A;
   const h16_t* B;
@@ -144,7 +153,46 @@ struct Gemm2Args {
   int ksplit, k_tiles_per_split;
   float* part;  // split-K partials [ksplit][M][N] (EPI_ACCUM with ksplit > 1)
   GemmEpiArgs e;
+  SplitKRed red;  // EPI_ACCUM: wgs workgroups after the tiles
 };
+
+// Workgroup w of the reducers: float4 groups w * 256 * U + t + 256 j, then
+// every wgs * 256 * U further; each thread keeps U groups in flight.  The
+// partials are added in split order, as splitk_reduce_kernel adds them.
+__device__ __forceinline__ void splitk_reduce_wg(const SplitKRed& r, int w) {
+  constexpr int U = 8;
+  const float4* part = (const float4*)r.part;
+  float4* out = (float4*)r.out;
+  const int64_t stride = (int64_t)r.wgs * 256 * U;
+  for (int64_t i0 = (int64_t)w * 256 * U + threadIdx.x; i0 < r.n4; i0 += stride) {
+    float4 s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + 256 * u;
+      s[u] = r.beta && i < r.n4 ? out[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int k = 0; k < r.ks; ++k) {
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + 256 * u;
+        v[u] = i < r.n4 ? part[(int64_t)k * r.n4 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        s[u].x += v[u].x;
+        s[u].y += v[u].y;
+        s[u].z += v[u].z;
+        s[u].w += v[u].w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + 256 * u;
+      if (i < r.n4) out[i] = s[u];
+    }
+  }
+}
 
 // Workgroup -> (output tile, k split).  Workgroups go to the 8 XCDs in
 // turn (workgroup w to XCD w % 8), so the linear work index (split-major,
@@ -289,6 +337,14 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   constexpr int LDS_ELEMS = LDS_ELEMS_0 > LDS_ELEMS_HEAD ? LDS_ELEMS_0 : LDS_ELEMS_HEAD;
   __shared__ __attribute__((aligned(1024))) h16_t lds[LDS_ELEMS];
 
+  if constexpr (EPI == EPI_ACCUM) {
+    // workgroups past the tiles run a previous launch's split-K reduction
+    const int nwork = p.tiles_m * p.tiles_n * p.ksplit;
+    if ((int)blockIdx.x >= nwork) {
+      splitk_reduce_wg(p.red, (int)blockIdx.x - nwork);
+      return;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn, split;
@@ -597,7 +653,7 @@ int run2(Gemm2Args p, hipStream_t s) {
   p.tiles_m = (int)cdiv(p.M, BM);
   p.tiles_n = (int)cdiv(p.N, BN);
   hipLaunchKernelGGL((gemm2_kernel<BM, BN, AK, BKC, EPI, NS, BK, OCC>),
-                     dim3(p.tiles_m * p.tiles_n * p.ksplit), dim3(256), 0, s, p);
+                     dim3(p.tiles_m * p.tiles_n * p.ksplit + p.red.wgs), dim3(256), 0, s, p);
   if (p.e.cs_part) {
     if (ColsumJob* d = p.e.cs_defer) {
       *d = ColsumJob();
@@ -640,6 +696,11 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
     const int nk = (int)cdiv(p.K, BKW);
     p.k_tiles_per_split = nk;
     const int64_t tiles = cdiv(p.M, 128) * cdiv(p.N, 128);
+    SplitKChain* ch = p.e.chain;
+    if (ch) {
+      ws = ch->ws[ch->next];
+      ws_bytes = ch->ws_bytes;
+    }
     int ks = 1;
     if (ws != nullptr && nk >= 8) {
       ks = (int)std::max<int64_t>(1, std::min<int64_t>(16, (400 + tiles / 2) / tiles));
@@ -652,11 +713,31 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
       p.ksplit = ks;
       p.part = ws;
     }
+    if (ch && ch->part) {
+      // the pending reduction in the slots the tiles leave free (two
+      // workgroups per CU on 256 CUs), at least 64 workgroups
+      p.red.part = ch->part;
+      p.red.out = ch->out;
+      p.red.n4 = ch->n / 4;
+      p.red.ks = ch->ks;
+      p.red.beta = ch->beta;
+      p.red.wgs = (int)std::max<int64_t>(64, std::min<int64_t>(256, 512 - tiles * p.ksplit));
+      ch->part = nullptr;
+    }
     if (const int rc = run2<128, 128, AK, BKC, EPI, 2, BKW, 2>(p, s)) return rc;
     if (p.ksplit > 1) {
       const int64_t n = (int64_t)p.M * p.N;
-      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, ws, p.ksplit,
-                         n, (float*)p.e.out, p.e.beta);
+      if (ch) {
+        ch->part = ws;
+        ch->out = (float*)p.e.out;
+        ch->n = n;
+        ch->ks = p.ksplit;
+        ch->beta = p.e.beta;
+        ch->next ^= 1;
+      } else {
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(n / 4, 256)), dim3(256), 0, s, ws,
+                           p.ksplit, n, (float*)p.e.out, p.e.beta);
+      }
     }
     return 0;
   } else {
@@ -677,6 +758,14 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
 }
 
 }  // namespace
+
+int splitk_chain_flush(SplitKChain* ch, hipStream_t s) {
+  if (!ch || !ch->part) return 0;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(cdiv(ch->n / 4, 256)), dim3(256), 0, s, ch->part,
+                     ch->ks, ch->n, ch->out, ch->beta);
+  ch->part = nullptr;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 // The pipelined kernel covers 16-bit with k-contiguous K % 8 == 0, every
 // leading dimension % 8 == 0, N % 8 == 0, ldc % 8 == 0 and operands below

@@ -271,6 +271,23 @@ struct Model {
     return fused_ce && cfg.mode == GPT_BF16 && cfg.padded_vocab % 8 == 0 && cfg.n_embd % 8 == 0;
   }
   Drop drop;  // dropout of the last forward (site word 0); thresh 0: none
+  // GPT_OPT_TIME_WEIGHT_GRADIENTS: gpt_backward records an event before and
+  // after each weight-gradient launch, taking tev in order; gpt_read_timing
+  // sums the intervals and starts the list over
+  bool time_dw = false;
+  std::vector<hipEvent_t> tev;
+  size_t tev_used = 0;
+  int mark(hipStream_t s) {
+    if (tev_used == tev.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return -4;
+      tev.push_back(e);
+    }
+    return hipEventRecord(tev[tev_used++], s) == hipSuccess ? 0 : -4;
+  }
+  ~Model() {
+    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
+  }
 
   bool h16() const { return cfg.mode != GPT_FP32; }
   int64_t es() const { return h16() ? 2 : 4; }
@@ -824,6 +841,15 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
   ColsumJob job;
   float* sk = w.splitk_bytes ? h->at<float>(w.splitk) : nullptr;
   const int64_t skb = w.splitk_bytes;
+  // the weight gradients pass their split-K reductions along (each runs
+  // inside the next weight-gradient launch), over the two halves of the
+  // split-K scratch
+  SplitKChain chain;
+  if (sk) {
+    chain.ws_bytes = (skb / 2) & ~(int64_t)255;
+    chain.ws[0] = sk;
+    chain.ws[1] = (float*)((char*)sk + chain.ws_bytes);
+  }
 
   // LM head: dwte (+)= dlogits^T lnf ; dlnf = dlogits wte.  The input
   // gradients of the LayerNorms (dlnf, dln2, dln1) are stored in the
@@ -837,8 +863,11 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.out = h->G(p.wte);
     e.ldc = d;
     e.beta = beta;
+    e.chain = &chain;
+    if (h->time_dw) CK(h->mark(s));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, h->at(w.logits), vi, h->at(w.head_h2), d,
                    c.padded_vocab, d, M, M, M, e, s, sk, skb));
+    if (h->time_dw) CK(h->mark(s));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -850,8 +879,11 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.out = h->G(p.wte);
     e.ldc = d;
     e.beta = beta;
+    e.chain = &chain;
+    if (h->time_dw) CK(h->mark(s));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, h->at(w.logits), vi, h->at(w.lnf), d,
                    c.padded_vocab, d, M, M, M, e, s, sk, skb));
+    if (h->time_dw) CK(h->mark(s));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -879,7 +911,10 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.mprojw);
     e.ldc = 4 * d;
     e.beta = beta;
+    e.chain = &chain;
+    if (h->time_dw) CK(h->mark(s));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.g), 4 * d, d, 4 * d, M, M, M, e, s, sk, skb));
+    if (h->time_dw) CK(h->mark(s));
     e = GemmEpiArgs();
     e.out = dbig;
     e.aux = h->at(L.dgelu);
@@ -900,7 +935,10 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.fcw);
     e.ldc = d;
     e.beta = beta;
+    e.chain = &chain;
+    if (h->time_dw) CK(h->mark(s));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 4 * d, h->at(L.ln2), d, 4 * d, d, M, M, M, e, s, sk, skb));
+    if (h->time_dw) CK(h->mark(s));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -920,7 +958,10 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.aprojw);
     e.ldc = d;
     e.beta = beta;
+    e.chain = &chain;
+    if (h->time_dw) CK(h->mark(s));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.att), d, d, d, M, M, M, e, s, sk, skb));
+    if (h->time_dw) CK(h->mark(s));
     e = GemmEpiArgs();
     e.out = h->at(w.dO);
     e.ldc = d;
@@ -940,7 +981,11 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.out = h->G(P.attnw);
     e.ldc = d;
     e.beta = beta;
+    e.chain = &chain;
+    if (h->time_dw) CK(h->mark(s));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 3 * d, h->at(L.ln1), d, 3 * d, d, M, M, M, e, s, sk, skb));
+    if (l == 0) CK(splitk_chain_flush(&chain, s));  // the last weight gradient's reduction
+    if (h->time_dw) CK(h->mark(s));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -957,6 +1002,7 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
                             l > 0 ? at_site(dr, 2 + 2 * (l - 1)) : Drop()));
     keep(job);
   }
+  CK(splitk_chain_flush(&chain, s));  // nothing pending unless the layer loop was empty
   CK(colsum_finalize_group_launch(jobs.data(), (int)jobs.size(), beta, s));
   // the embedding sum's dropout: the gradient that reaches wte and wpe
   CK(dropout_rows_launch(dres, dres, M, d, at_site(dr, 0), s));
@@ -1003,12 +1049,12 @@ int gpt_amp_step(Model* h, float lr, float beta1, float beta2, float eps, float 
 
 int gpt_set_option(Model* h, int32_t option, int32_t value) {
   if (!h) return fail(GPT_EINVAL, "null handle");
-  if (option == GPT_OPT_FUSED_HEAD_CE) {
-    if (value != 0 && value != 1) return fail(GPT_EINVAL, "option value must be 0 or 1");
-    h->fused_ce = value != 0;
-    return GPT_OK;
-  }
-  return fail(GPT_EINVAL, "unknown option");
+  if (option != GPT_OPT_FUSED_HEAD_CE && option != GPT_OPT_TIME_WEIGHT_GRADIENTS)
+    return fail(GPT_EINVAL, "unknown option");
+  if (value != 0 && value != 1) return fail(GPT_EINVAL, "option value must be 0 or 1");
+  if (option == GPT_OPT_FUSED_HEAD_CE) h->fused_ce = value != 0;
+  else h->time_dw = value != 0;
+  return GPT_OK;
 }
 
 int gpt_get_option(Model* h, int32_t option, int32_t* value) {
@@ -1017,7 +1063,26 @@ int gpt_get_option(Model* h, int32_t option, int32_t* value) {
     *value = h->fused_ce ? 1 : 0;
     return GPT_OK;
   }
+  if (option == GPT_OPT_TIME_WEIGHT_GRADIENTS) {
+    *value = h->time_dw ? 1 : 0;
+    return GPT_OK;
+  }
   return fail(GPT_EINVAL, "unknown option");
+}
+
+int gpt_read_timing(Model* h, double* ms, int64_t* launches) {
+  if (!h || !ms || !launches) return fail(GPT_EINVAL, "null handle or output");
+  double total = 0.0;
+  for (size_t i = 0; i + 1 < h->tev_used; i += 2) {
+    CKH(hipEventSynchronize(h->tev[i + 1]));
+    float t = 0.f;
+    CKH(hipEventElapsedTime(&t, h->tev[i], h->tev[i + 1]));
+    total += t;
+  }
+  *ms = total;
+  *launches = (int64_t)(h->tev_used / 2);
+  h->tev_used = 0;
+  return GPT_OK;
 }
 
 int gpt_read_flags(Model* h, int32_t* flags, void* stream) {
@@ -1099,6 +1164,38 @@ int gpt_op_linear_dw(int32_t h16, const void* dY, const void* X, float* dW, int3
   e.beta = accumulate ? 1 : 0;
   CK(gemm_launch(h16 != 0, false, false, EPI_ACCUM, dY, N, X, K, N, K, M, M, M, e,
                  (hipStream_t)stream, workspace, workspace ? workspace_bytes : 0));
+  return GPT_OK;
+}
+
+int gpt_op_linear_dw_seq(int32_t h16, int32_t count, const void* const* dY, const void* const* X,
+                         float* const* dW, const int32_t* accumulate, const int32_t* M,
+                         const int32_t* N, const int32_t* K, float* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  if (count < 0 || (count > 0 && (!dY || !X || !dW || !accumulate || !M || !N || !K)))
+    return fail(GPT_EINVAL, "bad linear_dw_seq arguments");
+  for (int i = 0; i < count; ++i)
+    if (!dY[i] || !X[i] || !dW[i] || M[i] < 1 || N[i] < 0 || K[i] < 0)
+      return fail(GPT_EINVAL, "bad linear_dw_seq arguments");
+  hipStream_t s = (hipStream_t)stream;
+  SplitKChain chain;
+  if (workspace && workspace_bytes > 0) {
+    chain.ws_bytes = (workspace_bytes / 2) & ~(int64_t)255;
+    chain.ws[0] = workspace;
+    chain.ws[1] = (float*)((char*)workspace + chain.ws_bytes);
+  }
+  for (int i = 0; i < count; ++i) {
+    // a product that adds into the previous product's gradient waits for
+    // that product's reduction
+    if (i > 0 && dW[i] == dW[i - 1]) CK(splitk_chain_flush(&chain, s));
+    GemmEpiArgs e;
+    e.out = dW[i];
+    e.ldc = K[i];
+    e.beta = accumulate[i] ? 1 : 0;
+    e.chain = &chain;
+    CK(gemm_launch(h16 != 0, false, false, EPI_ACCUM, dY[i], N[i], X[i], K[i], N[i], K[i], M[i],
+                   M[i], M[i], e, s, workspace, workspace ? workspace_bytes : 0));
+  }
+  CK(splitk_chain_flush(&chain, s));
   return GPT_OK;
 }
 
