@@ -217,7 +217,8 @@ WsOff ws_offsets(const gpt_config& c, const ParamOff& p) {
   w.cs_part_elems = std::max<int64_t>(cdiv(M, 128), colsum_part_rows((int)M)) * 4 * d;
   w.cs_part = take(2 * c.n_layer * w.cs_part_elems * 4);
   w.norm_part = take((int64_t)adamw_norm_blocks() * 8);
-  w.splitk_bytes = bf ? gemm_splitk_bytes(4 * d, d) : 0;
+  // two halves, one per weight gradient in flight (SplitKChain)
+  w.splitk_bytes = bf ? 2 * gemm_splitk_bytes(4 * d, d) : 0;
   w.splitk = take(w.splitk_bytes);
   int64_t nch = 0;
   for (auto& t : p.tensors) nch += (t.second + kChunk - 1) / kChunk;
