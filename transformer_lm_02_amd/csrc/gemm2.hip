@@ -137,6 +137,23 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Non-temporal 16-byte stores, for outputs no kernel reads soon: the head's
+// exp(z) (read by the backward), the weight gradients and their split-K
+// partials, the stored GELU derivative.  Written through L2 without keeping
+// the lines, they leave it to the operands the products re-read (the head's
+// forward reads its activation rows from L2 across all 262 column tiles).
+// Outputs the next kernel reads keep ordinary stores.
+typedef unsigned int ntu4_t __attribute__((ext_vector_type(4)));
+typedef float ntf4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+  const ntu4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (ntu4_t*)p);
+}
+__device__ __forceinline__ void st_nt(float4* p, float4 v) {
+  const ntf4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (ntf4_t*)p);
+}
+
 // A previous launch's split-K reduction run by workgroups past the tiles:
 // out[i] = (beta ? out[i] : 0) + sum over k < ks of part[k * 4 n4 + i]
 struct SplitKRed {
@@ -189,7 +206,7 @@ __device__ __forceinline__ void splitk_reduce_wg(const SplitKRed& r, int w) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = i0 + 256 * u;
-      if (i < r.n4) out[i] = s[u];
+      if (i < r.n4) st_nt(&out[i], s[u]);
     }
   }
 }
@@ -263,12 +280,12 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
   if constexpr (EPI == EPI_ACCUM) {
     if (splitk) {
       float4* o = (float4*)(part + i);
-      o[0] = make_float4(v[0], v[1], v[2], v[3]);
-      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      st_nt(&o[0], make_float4(v[0], v[1], v[2], v[3]));
+      st_nt(&o[1], make_float4(v[4], v[5], v[6], v[7]));
     } else {
       float4* o = (float4*)((float*)e.out + i);
-      o[0] = make_float4(x.a.x + v[0], x.a.y + v[1], x.a.z + v[2], x.a.w + v[3]);
-      o[1] = make_float4(x.b.x + v[4], x.b.y + v[5], x.b.z + v[6], x.b.w + v[7]);
+      st_nt(&o[0], make_float4(x.a.x + v[0], x.a.y + v[1], x.a.z + v[2], x.a.w + v[3]));
+      st_nt(&o[1], make_float4(x.b.x + v[4], x.b.y + v[5], x.b.z + v[6], x.b.w + v[7]));
     }
   } else if constexpr (EPI == EPI_F32) {
     float4* o = (float4*)((float*)e.out + i);
@@ -298,8 +315,8 @@ __device__ __forceinline__ void epi8(const GemmEpiArgs& e, float* part, int spli
     float g[8], gp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) gelu_both(v[j] + bias8[j], g[j], gp[j]);
-    *(uint4*)((h16_t*)e.out + i) = make_uint4(pack2h(gp[0], gp[1]), pack2h(gp[2], gp[3]),
-                                               pack2h(gp[4], gp[5]), pack2h(gp[6], gp[7]));
+    st_nt((h16_t*)e.out + i, make_uint4(pack2h(gp[0], gp[1]), pack2h(gp[2], gp[3]),
+                                        pack2h(gp[4], gp[5]), pack2h(gp[6], gp[7])));
     *(uint4*)((h16_t*)e.out2 + i) =
         make_uint4(pack2h(g[0], g[1]), pack2h(g[2], g[3]), pack2h(g[4], g[5]), pack2h(g[6], g[7]));
   } else if constexpr (EPI == EPI_HEAD_DX) {
@@ -563,9 +580,9 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
             sum += e8[j];
             zy = (gcol + j == y) ? v[j] : zy;
           }
-          *(uint4*)((h16_t*)p.e.out + (int64_t)grow * p.e.ldc + gcol) =
-              make_uint4(pack2h(e8[0], e8[1]), pack2h(e8[2], e8[3]), pack2h(e8[4], e8[5]),
-                         pack2h(e8[6], e8[7]));
+          st_nt((h16_t*)p.e.out + (int64_t)grow * p.e.ldc + gcol,
+                make_uint4(pack2h(e8[0], e8[1]), pack2h(e8[2], e8[3]), pack2h(e8[4], e8[5]),
+                           pack2h(e8[6], e8[7])));
           if (y >= gcol && y < gcol + 8 && y < p.e.head.V) p.e.head.zy[grow] = zy;
         }
         if (lane_on && lr < 32) ps[lr * 12 + my_c / 8] = sum;
@@ -643,7 +660,7 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
     const float4 v = ((const float4*)(part + (int64_t)k * n))[i4];
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
-  ((float4*)out)[i4] = s;
+  st_nt((float4*)out + i4, s);
 }
 
 // launches one configuration; then, when column sums were asked for, adds
