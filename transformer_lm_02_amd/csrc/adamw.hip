@@ -194,13 +194,26 @@ __global__ __launch_bounds__(256) void adamw_tile_kernel(
   const bool full = r0 + 64 <= job.rows && c0 + 64 <= job.cols && job.cols % 8 == 0 &&
                     job.ld % 8 == 0 && job.src % 8 == 0 && job.dst % 8 == 0;
   if (full) {
-    // 16 threads x 4 values cover a 64-value tile row: four passes of 16 rows
+    // 16 threads x 4 values cover a 64-value tile row: four passes of 16
+    // rows, every load of the four issued before any is used.  The outputs
+    // are read again only by the next step: non-temporal stores.
+    float4 P4[4], G4[4], M4[4], V4[4];
+    int64_t E4[4];
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int r = (threadIdx.x >> 4) + 16 * pass, c4 = 4 * (threadIdx.x & 15);
-      const int64_t e = (job.src + (int64_t)(r0 + r) * job.cols + c0 + c4) / 4;
-      float4 pp = ((float4*)p)[e], gg = ((const float4*)g)[e];
-      float4 mm = ((float4*)m)[e], vv = ((float4*)v)[e];
+      E4[pass] = (job.src + (int64_t)(r0 + r) * job.cols + c0 + c4) / 4;
+      P4[pass] = ((float4*)p)[E4[pass]];
+      G4[pass] = ((const float4*)g)[E4[pass]];
+      M4[pass] = ((float4*)m)[E4[pass]];
+      V4[pass] = ((float4*)v)[E4[pass]];
+    }
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int r = (threadIdx.x >> 4) + 16 * pass, c4 = 4 * (threadIdx.x & 15);
+      const int64_t e = E4[pass];
+      float4 pp = P4[pass], gg = G4[pass];
+      float4 mm = M4[pass], vv = V4[pass];
       float* pa = &pp.x;
       const float* ga = &gg.x;
       float* ma = &mm.x;
@@ -208,11 +221,11 @@ __global__ __launch_bounds__(256) void adamw_tile_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         adamw_elem(pa[k], ga[k], ma[k], va[k], coef, beta1, beta2, eps, decay, step, rbc2);
-      ((float4*)p)[e] = pp;
-      ((float4*)m)[e] = mm;
-      ((float4*)v)[e] = vv;
+      st_nt((float4*)p + e, pp);
+      st_nt((float4*)m + e, mm);
+      st_nt((float4*)v + e, vv);
       const uint2 w = make_uint2(pack2h(pp.x, pp.y), pack2h(pp.z, pp.w));
-      *(uint2*)(shadow + 4 * e) = w;
+      st_nt(shadow + 4 * e, w);
       *(uint2*)&tile[r][c4] = w;
     }
     __syncthreads();
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(256) void adamw_tile_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         w[k] = (uint32_t)tile[r8 + 2 * k][oc] | ((uint32_t)tile[r8 + 2 * k + 1][oc] << 16);
-      *(uint4*)(D + (int64_t)(c0 + oc) * job.ld + r0 + r8) = make_uint4(w[0], w[1], w[2], w[3]);
+      st_nt(D + (int64_t)(c0 + oc) * job.ld + r0 + r8, make_uint4(w[0], w[1], w[2], w[3]));
     }
   } else {
     for (int i = threadIdx.x; i < 64 * 64; i += 256) {

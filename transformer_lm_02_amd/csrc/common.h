@@ -202,4 +202,22 @@ __device__ __forceinline__ float drop1(const Drop& d, uint32_t col, uint32_t row
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Non-temporal stores, for outputs no kernel reads soon: written through L2
+// without keeping the lines, they leave L2 to data that is read again.
+typedef unsigned int ntu4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int ntu2_t __attribute__((ext_vector_type(2)));
+typedef float ntf4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+  const ntu4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (ntu4_t*)p);
+}
+__device__ __forceinline__ void st_nt(void* p, uint2 v) {
+  const ntu2_t w = {v.x, v.y};
+  __builtin_nontemporal_store(w, (ntu2_t*)p);
+}
+__device__ __forceinline__ void st_nt(float4* p, float4 v) {
+  const ntf4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (ntf4_t*)p);
+}
+
 }  // namespace HALF_NS

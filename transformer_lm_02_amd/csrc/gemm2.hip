@@ -137,22 +137,12 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Non-temporal 16-byte stores, for outputs no kernel reads soon: the head's
-// exp(z) (read by the backward), the weight gradients and their split-K
-// partials, the stored GELU derivative.  Written through L2 without keeping
-// the lines, they leave it to the operands the products re-read (the head's
-// forward reads its activation rows from L2 across all 262 column tiles).
-// Outputs the next kernel reads keep ordinary stores.
-typedef unsigned int ntu4_t __attribute__((ext_vector_type(4)));
-typedef float ntf4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_nt(void* p, uint4 v) {
-  const ntu4_t w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, (ntu4_t*)p);
-}
-__device__ __forceinline__ void st_nt(float4* p, float4 v) {
-  const ntf4_t w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, (ntf4_t*)p);
-}
+// Outputs no kernel reads soon go out with non-temporal stores (st_nt): the
+// head's exp(z) (read by the backward), the weight gradients and their
+// split-K partials, the stored GELU derivative.  They leave L2 to the
+// operands the products re-read (the head's forward reads its activation
+// rows from L2 across all 262 column tiles).  Outputs the next kernel reads
+// keep ordinary stores.
 
 // A previous launch's split-K reduction run by workgroups past the tiles:
 // out[i] = (beta ? out[i] : 0) + sum over k < ks of part[k * 4 n4 + i]
