@@ -199,9 +199,9 @@ def roofline_from_groups(groups, fp16=False, instep=None):
     group timed inside training steps (events around its launches), which
     then replaces that group's replay through the single-op entry point."""
     replay = {k: round(v["ms_per_step"], 4) for k, v in groups.items()}
-    if instep and "weight_gradients" in groups:
+    if (instep and "weight_gradients" in groups
+            and round(instep["launches_per_step"]) == groups["weight_gradients"]["launches_per_step"]):
         g = dict(groups["weight_gradients"])
-        assert round(instep["launches_per_step"]) == g["launches_per_step"], instep
         g["ms_per_step"] = instep["ms_per_step"]
         g["timing"] = f"in-step HIP events over {instep['steps']} steps"
         groups = dict(groups, weight_gradients=g)
@@ -463,7 +463,9 @@ def main():
         torch.cuda.synchronize()
         ev_ms, ev_n = model.read_timing()
         model.set_option(bd.GPT_OPT_TIME_WEIGHT_GRADIENTS, 0)
-        instep = {"ms_per_step": ev_ms / n_ev, "launches_per_step": ev_n / n_ev, "steps": n_ev}
+        # per backward (one micro-batch), as the groups are counted
+        instep = {"ms_per_step": ev_ms / (n_ev * K), "launches_per_step": ev_n / (n_ev * K),
+                  "steps": n_ev}
     roof = None
     model.close()
     del model
