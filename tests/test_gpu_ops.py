@@ -65,14 +65,16 @@ def test_linear_dw_bf16(M, N, K, split):
     assert rel_err(got2, ref + 1.0) < 1e-5
 
 
-def test_linear_dw_seq_equals_one_at_a_time():
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_linear_dw_seq_equals_one_at_a_time(dtype):
     """gpt_op_linear_dw_seq, where each product's split-K reduction runs
     inside the next product's launch, against gpt_op_linear_dw called once
     per product in the same order: equal bit for bit.  The sequence holds
     split products (4096 tokens, 16 splits), one with enough tiles not to
     split, two in a row adding into one gradient, one on the plain kernel
     (300 tokens) after a pending reduction, and accumulation."""
-    case("linear_dw_seq vs linear_dw, 7 products")
+    case(f"linear_dw_seq vs linear_dw, 7 products, {dtype}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float16
     seq = [  # (M tokens, N, K, accumulate, gradient index)
         (4096, 768, 256, 0, 0),
         (4096, 256, 768, 1, 1),
@@ -83,8 +85,8 @@ def test_linear_dw_seq_equals_one_at_a_time():
         (4096, 768, 256, 1, 0),
     ]
     shapes = {0: (768, 256), 1: (256, 768), 2: (3072, 2304), 3: (384, 384), 4: (104, 136)}
-    inputs = [(to_dev(bf16_round(rnd((M, N), 40 + i, 0.01)), torch.bfloat16),
-               to_dev(bf16_round(rnd((M, K), 50 + i)), torch.bfloat16))
+    inputs = [(to_dev(bf16_round(rnd((M, N), 40 + i, 0.01)), dt),
+               to_dev(bf16_round(rnd((M, K), 50 + i)), dt))
               for i, (M, N, K, _, _) in enumerate(seq)]
     init = {g: rnd(s, 60 + g) for g, s in shapes.items()}
     ws = torch.empty(3 * 16 * 768 * 256, dtype=torch.float32, device="cuda")
