@@ -53,10 +53,12 @@ def flops_per_token(dims, T):
 
 # The step's matrix products, grouped by the kernel instantiation the library
 # runs them with at this workload (the template names rocprofv3 reports).
-# Each group is timed through the single-op entry point that runs the same
+# Each group is replayed through the single-op entry point that runs the same
 # kernel at the same shapes, one step's launches at a time, with events on
-# the stream the launches go to; the group with the largest time per step is
-# the dominant kernel that `roofline` reports.  Not timed here (no single-op
+# the stream the launches go to; the weight-gradient group is also timed
+# inside training steps (events the library records around its launches),
+# which replaces its replay.  The group with the largest time per step is the
+# dominant kernel that `roofline` reports.  Not timed here (no single-op
 # entry point): the attention- and MLP-projection forwards (residual
 # epilogue, 8 % of the step) and the two products of the fused head with the
 # cross-entropy (one launch each, 14 % of the step).
