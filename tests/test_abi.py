@@ -200,3 +200,18 @@ def test_set_option_checks_its_arguments_without_a_device():
     assert lib.gpt_estimate_loss(None, None, None, 1, 1, 1, None, None) == bd.GPT_EINVAL
     v = ctypes.c_int32(7)
     assert lib.gpt_get_option(None, bd.GPT_OPT_FUSED_HEAD_CE, ctypes.byref(v)) == bd.GPT_EINVAL
+
+
+def test_weight_gradient_sequence_and_timing_check_their_arguments_without_a_device():
+    """gpt_op_linear_dw_seq rejects a negative count and null arrays, and
+    accepts an empty sequence; the timing calls reject a null handle."""
+    lib = bd.lib
+    assert lib.gpt_op_linear_dw_seq(bd.GPT_BF16, -1, None, None, None, None, None, None, None,
+                                    None, 0, None) == bd.GPT_EINVAL
+    assert lib.gpt_op_linear_dw_seq(bd.GPT_BF16, 2, None, None, None, None, None, None, None,
+                                    None, 0, None) == bd.GPT_EINVAL
+    assert lib.gpt_op_linear_dw_seq(bd.GPT_BF16, 0, None, None, None, None, None, None, None,
+                                    None, 0, None) == bd.GPT_OK
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.gpt_read_timing(None, ctypes.byref(ms), ctypes.byref(n)) == bd.GPT_EINVAL
+    assert lib.gpt_set_option(None, bd.GPT_OPT_TIME_WEIGHT_GRADIENTS, 1) == bd.GPT_EINVAL
