@@ -71,12 +71,15 @@ def test_linear_dw_seq_equals_one_at_a_time(dtype):
     inside the next product's launch, against gpt_op_linear_dw called once
     per product in the same order: equal bit for bit.  The sequence holds
     split products (4096 tokens, 16 splits), one with enough tiles not to
-    split, two in a row adding into one gradient, one on the plain kernel
-    (300 tokens) after a pending reduction, and accumulation."""
-    case(f"linear_dw_seq vs linear_dw, 7 products, {dtype}")
+    split, one with the 1024 tiles or more that take the wide tiles (after a
+    pending reduction, which it hosts), two in a row adding into one
+    gradient, one on the plain kernel (300 tokens) after a pending
+    reduction, and accumulation."""
+    case(f"linear_dw_seq vs linear_dw, 8 products, {dtype}")
     dt = torch.bfloat16 if dtype == "bf16" else torch.float16
     seq = [  # (M tokens, N, K, accumulate, gradient index)
         (4096, 768, 256, 0, 0),
+        (1024, 4096, 4096, 0, 5),
         (4096, 256, 768, 1, 1),
         (1024, 3072, 2304, 0, 2),
         (4096, 384, 384, 0, 3),
@@ -84,7 +87,8 @@ def test_linear_dw_seq_equals_one_at_a_time(dtype):
         (300, 104, 136, 1, 4),
         (4096, 768, 256, 1, 0),
     ]
-    shapes = {0: (768, 256), 1: (256, 768), 2: (3072, 2304), 3: (384, 384), 4: (104, 136)}
+    shapes = {0: (768, 256), 1: (256, 768), 2: (3072, 2304), 3: (384, 384), 4: (104, 136),
+              5: (4096, 4096)}
     inputs = [(to_dev(bf16_round(rnd((M, N), 40 + i, 0.01)), dt),
                to_dev(bf16_round(rnd((M, K), 50 + i)), dt))
               for i, (M, N, K, _, _) in enumerate(seq)]
@@ -104,10 +108,12 @@ def test_linear_dw_seq_equals_one_at_a_time(dtype):
         a, b = to_np(one[g]), to_np(chained[g])
         assert np.array_equal(a, b), (g, float(np.abs(a - b).max()))
     # and the values themselves: gradient 3 is the sum of its two products
-    M, N, K, _, _ = seq[3]
     ref = sum(to_np(dY).astype(np.float64).T @ to_np(X).astype(np.float64)
-              for dY, X in inputs[3:5])
+              for dY, X in inputs[4:6])
     assert rel_err(to_np(chained[3]), ref) < 1e-5
+    dY, X = inputs[1]
+    ref = to_np(dY).astype(np.float64).T @ to_np(X).astype(np.float64)
+    assert rel_err(to_np(chained[5]), ref) < 1e-5
 
 
 @pytest.mark.parametrize("M,N,K", [(16384, 768, 768), (300, 200, 136), (512, 50304, 768),

@@ -684,7 +684,9 @@ inline int64_t tile_cost(int64_t M, int64_t N, int BM, int BN) {
 // Tile choice (measured on MI355X for the step's shapes):
 //  * weight gradients (both operands m/n-contiguous): 128x128 tiles with
 //    k-tiles of 64, two workgroups per CU, the token reduction split so that
-//    about 400 workgroups run (partials summed in order afterwards);
+//    about 400 workgroups run (partials summed in order afterwards); with
+//    1024 such tiles or more (the head's gradient, never split) 128x256
+//    tiles with k-tiles of 48 instead;
 //  * k-contiguous products, two workgroups per CU (one's epilogue and waits
 //    hide behind the other's MFMAs): with at least 1024 tiles of 256x192,
 //    those tiles with 2 stages of 32 k; otherwise 128x192 tiles with 2 stages
@@ -697,6 +699,23 @@ int dispatch2(Gemm2Args p, float* ws, int64_t ws_bytes, hipStream_t s) {
   p.k_tiles_per_split = (int)cdiv(p.K, BK);
   p.part = nullptr;
   if constexpr (EPI == EPI_ACCUM && !AK && !BKC) {
+    // The head's product (a 50304-row gradient: thousands of tiles, no
+    // split): 128x256 tiles with k-tiles of 48, so that two workgroups still
+    // fit a CU, read a quarter fewer operand bytes per flop
+    if (cdiv(p.M, 128) * cdiv(p.N, 128) >= 1024) {
+      p.k_tiles_per_split = (int)cdiv(p.K, 48);
+      SplitKChain* ch = p.e.chain;
+      if (ch && ch->part) {
+        p.red.part = ch->part;
+        p.red.out = ch->out;
+        p.red.n4 = ch->n / 4;
+        p.red.ks = ch->ks;
+        p.red.beta = ch->beta;
+        p.red.wgs = 64;
+        ch->part = nullptr;
+      }
+      return run2<128, 256, AK, BKC, EPI, 2, 48, 2>(p, s);
+    }
     // 128x128 tiles, k-tiles of 64, two workgroups per CU; the token
     // reduction split so that about 400 workgroups run
     constexpr int BKW = 64;
