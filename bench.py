@@ -76,8 +76,9 @@ def gemm_groups(B, T, dims):
     vi = -(-dims["padded_vocab"] // 64) * 64
     return {
         "weight_gradients": (
-            "gemm2_kernel<128, 128, false, false, 5, 2, 64, 2> (split-K reductions inside the "
-            "next launch) + splitk_reduce_kernel",
+            "gemm2_kernel<128, 128, false, false, 5, 2, 64, 2> (layers; split-K reductions "
+            "inside the next launch) + gemm2_kernel<128, 256, false, false, 5, 2, 48, 2> (head) "
+            "+ splitk_reduce_kernel",
             "linear_dw_seq",
             [(M, vi, d, 1), (M, d, 4 * d, L), (M, 4 * d, d, L), (M, d, d, L), (M, 3 * d, d, L)]),
         "input_gradients_and_qkv": (
