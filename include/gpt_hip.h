@@ -332,7 +332,11 @@ int gpt_sample(const float* logits, int32_t B, int32_t V, int32_t ldv, float tem
  * records a HIP event on its stream before and after each weight-gradient
  * launch ("Let's reproduce GPT-2 (124M)", "Speed Stack": time what the step
  * spends where), for gpt_read_timing.  Only the time between the events is
- * measured; the results of the step do not change.
+ * measured; the results of the step do not change.  The library keeps the
+ * events until gpt_read_timing takes them (two per launch, 98 per GPT-2
+ * backward), so a caller that turns the option on reads them now and then.
+ * A launch that fails leaves its opening event unmatched; the next launch's
+ * pair replaces it.
  * Errors: GPT_EINVAL (null handle, unknown option or value). */
 enum { GPT_OPT_FUSED_HEAD_CE = 1, GPT_OPT_TIME_WEIGHT_GRADIENTS = 2 };
 int gpt_set_option(gpt_model* h, int32_t option, int32_t value);

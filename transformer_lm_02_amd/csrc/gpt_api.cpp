@@ -278,13 +278,20 @@ struct Model {
   bool time_dw = false;
   std::vector<hipEvent_t> tev;
   size_t tev_used = 0;
-  int mark(hipStream_t s) {
+  // begin: the event before a launch, which always takes an even index (a
+  // begin left unmatched by a failed launch is dropped), so that the pairs
+  // gpt_read_timing sums stay aligned; the count grows only once the event
+  // is recorded
+  int mark(hipStream_t s, bool begin) {
+    if (begin && (tev_used & 1)) --tev_used;
     if (tev_used == tev.size()) {
       hipEvent_t e;
       if (hipEventCreate(&e) != hipSuccess) return -4;
       tev.push_back(e);
     }
-    return hipEventRecord(tev[tev_used++], s) == hipSuccess ? 0 : -4;
+    if (hipEventRecord(tev[tev_used], s) != hipSuccess) return -4;
+    ++tev_used;
+    return 0;
   }
   ~Model() {
     for (hipEvent_t e : tev) (void)hipEventDestroy(e);
@@ -865,10 +872,10 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.ldc = d;
     e.beta = beta;
     e.chain = &chain;
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, true));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, h->at(w.logits), vi, h->at(w.head_h2), d,
                    c.padded_vocab, d, M, M, M, e, s, sk, skb));
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, false));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -881,10 +888,10 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.ldc = d;
     e.beta = beta;
     e.chain = &chain;
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, true));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, h->at(w.logits), vi, h->at(w.lnf), d,
                    c.padded_vocab, d, M, M, M, e, s, sk, skb));
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, false));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -913,9 +920,9 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.ldc = 4 * d;
     e.beta = beta;
     e.chain = &chain;
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, true));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.g), 4 * d, d, 4 * d, M, M, M, e, s, sk, skb));
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, false));
     e = GemmEpiArgs();
     e.out = dbig;
     e.aux = h->at(L.dgelu);
@@ -937,9 +944,9 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.ldc = d;
     e.beta = beta;
     e.chain = &chain;
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, true));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 4 * d, h->at(L.ln2), d, 4 * d, d, M, M, M, e, s, sk, skb));
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, false));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
@@ -960,9 +967,9 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.ldc = d;
     e.beta = beta;
     e.chain = &chain;
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, true));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dres_act, d, h->at(L.att), d, d, d, M, M, M, e, s, sk, skb));
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, false));
     e = GemmEpiArgs();
     e.out = h->at(w.dO);
     e.ldc = d;
@@ -983,10 +990,10 @@ int gpt_backward(Model* h, int32_t zero_first, void* stream) {
     e.ldc = d;
     e.beta = beta;
     e.chain = &chain;
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, true));
     CK(gemm_launch(bf, false, false, EPI_ACCUM, dbig, 3 * d, h->at(L.ln1), d, 3 * d, d, M, M, M, e, s, sk, skb));
     if (l == 0) CK(splitk_chain_flush(&chain, s));  // the last weight gradient's reduction
-    if (h->time_dw) CK(h->mark(s));
+    if (h->time_dw) CK(h->mark(s, false));
     e = GemmEpiArgs();
     e.out = dln;
     e.ldc = d;
