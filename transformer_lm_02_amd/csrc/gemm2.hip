@@ -17,6 +17,7 @@
 //  * weight gradients with few output tiles split K over workgroups into an
 //    fp32 partial buffer that a second kernel sums in a fixed order.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "gemm.h"
@@ -130,6 +131,19 @@ struct Stage {
     }
   }
 };
+
+// f(std::integral_constant<int, i>()) for i = 0 .. N-1
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_from<0, N>(f);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
@@ -388,6 +402,41 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   constexpr int L = SA::LOADS + SB::LOADS;  // loads per wave per stage
   constexpr int NF = (TM + TN) * (AK ? 1 : 2) / 1;  // LDS reads per k-step (tr reads count 2)
   (void)NF;
+  // Epilogue lane layout: per 32-row slab of the wave tile, each lane takes 8
+  // consecutive columns of one row, RPI rows per pass, NIT passes.
+  constexpr int LPR = WC / 8;                // lanes per row
+  constexpr int RPI = 64 / LPR;              // rows per pass (lanes >= RPI*LPR idle)
+  constexpr int NIT = (32 + RPI - 1) / RPI;  // row passes per 32-row slab
+  const int my_c = 8 * (lane % LPR), my_r = lane / LPR;
+  const bool lane_on = my_r < RPI;
+  const int gcol = n0 + wn * WC + my_c;
+  // The residual epilogue on 128x192 tiles reads the residual of the wave's
+  // first slab during the main loop: pass q's two 16-byte loads follow k-tile
+  // q's operand loads, so those HBM reads overlap the products rather than
+  // the epilogue's stores (the second slab is read as before; registers allow
+  // one).  Buffer loads with out-of-range offsets (reading zero) for lanes
+  // without a row keep every wave's load count, and so its waits, fixed.
+  constexpr bool RPRE = EPI == EPI_RESID && OCC > 1 && BM == 128 && BN == 192;
+  static_assert(!RPRE || NS == 2, "the waits below assume one k-tile in flight");
+  // (taken when the main loop has a k-tile for every pass)
+  const bool rpre_on = RPRE && nk >= NIT;
+  Aux8 rpre[RPRE ? NIT : 1];
+  __amdgpu_buffer_rsrc_t rres;
+  if constexpr (RPRE) rres = make_rsrc(p.e.aux, (uint32_t)((int64_t)p.M * p.e.ldc * 4));
+  // pass q's loads (q a compile-time index, so rpre stays in registers)
+  auto res_issue = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    if constexpr (RPRE && q < NIT) {
+      const int lr = q * RPI + my_r, grow = m0 + wm * WR + lr;
+      const uint32_t off = lane_on && lr < 32 && grow < p.M && gcol < p.N
+                               ? (uint32_t)(((int64_t)grow * p.e.ldc + gcol) * 4)
+                               : kOOB;
+      // after this k-tile's operand loads, in issue order: the waits count on it
+      asm volatile("" ::: "memory");
+      rpre[q].a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off, 0, 0));
+      rpre[q].b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rres, (int)(off + 16), 0, 0));
+    }
+  };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
     if (s < nk) {
@@ -399,9 +448,15 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
     // Two workgroups share the CU: the other one's MFMAs hide this one's
     // latencies, so fragments are single-buffered (registers stay within the
     // 256 per wave that two waves per SIMD allow).
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + NS - 2 < nk) wait_vm_barrier<(NS - 2) * L>();
-      else wait_vm_barrier<0>();
+    // One k-tile; res_prev: the previous k-tile issued two residual loads
+    // after its operand loads, which may stay in flight
+    auto ktile = [&](int kt, bool res_prev) __attribute__((always_inline)) {
+      if (kt + NS - 2 < nk) {
+        if (RPRE && res_prev) wait_vm_barrier<(NS - 2) * L + 2>();
+        else wait_vm_barrier<(NS - 2) * L>();
+      } else {
+        wait_vm_barrier<0>();
+      }
       if (kt + NS - 1 < nk) {
         const int s = (kt + NS - 1) % NS;
         sa.issue(ra, lds + s * STAGE_ELEMS, kt0 + kt + NS - 1, p.lda, p.K, wave);
@@ -409,6 +464,9 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
       }
       const h16_t* la = lds + (kt % NS) * STAGE_ELEMS;
       const h16_t* lb = la + SA::ELEMS;
+      return std::make_pair(la, lb);
+    };
+    auto kmath = [&](const h16_t* la, const h16_t* lb) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         h16x8_t fa[TM], fb[TN];
@@ -422,6 +480,23 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
           for (int j = 0; j < TN; ++j)
             acc[i][j] = MFMA_32X32X16(fa[i], fb[j], acc[i][j]);
       }
+    };
+    int kt = 0;
+    if constexpr (RPRE) {
+      // the first NIT k-tiles unrolled, each followed by one pass's residual loads
+      if (rpre_on) {
+        static_for<NIT>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          const auto ab = ktile(q, q >= 1);
+          res_issue(qc);
+          kmath(ab.first, ab.second);
+        });
+        kt = NIT;
+      }
+    }
+    for (; kt < nk; ++kt) {
+      const auto ab = ktile(kt, rpre_on && kt == NIT);
+      kmath(ab.first, ab.second);
     }
   } else {
     // Software pipeline.  Stage kt is known resident after a wait (own DMA
@@ -503,11 +578,6 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   // epilogue: per 32-row slab of the wave tile, stage fp32 in LDS, then each
   // lane handles 8 consecutive columns of one row
   float* ep = (float*)lds + wave * 32 * EP_PITCH;
-  constexpr int LPR = WC / 8;        // lanes per row
-  constexpr int RPI = 64 / LPR;      // rows per pass (lanes >= RPI*LPR idle)
-  const int my_c = 8 * (lane % LPR), my_r = lane / LPR;
-  const bool lane_on = my_r < RPI;
-  const int gcol = n0 + wn * WC + my_c;
   float bias8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (EPI != EPI_ACCUM && EPI != EPI_GELU_BWD && p.e.bias != nullptr && gcol < p.N) {
     const float4 b0 = *(const float4*)(p.e.bias + gcol), b1 = *(const float4*)(p.e.bias + gcol + 4);
@@ -519,12 +589,12 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
   // column sums of this lane's 8 columns over its rows (GELU-derivative
   // epilogue with cs_part set); zeros otherwise
   float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int NIT = (32 + RPI - 1) / RPI;  // row passes per 32-row slab
   // prefetch group (register budget): a whole slab when the accumulators
   // leave room (or the operand is 16 bytes per pass), else two passes
   constexpr int PG =
       ((EPI == EPI_GELU_BWD && TM * TN <= 12) || TM * TN <= 6 || (OCC == 1 && TN <= 3)) ? NIT : 2;
-#pragma unroll
+  // unrolled in full: a runtime slab index would put the accumulators in scratch
+#pragma clang loop unroll(full)
   for (int i = 0; i < TM; ++i) {
     const int grow0 = m0 + wm * WR + 32 * i + my_r;
     // accumulator layout of a 32x32 tile: lane l, register r -> row
@@ -591,7 +661,12 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
       }
     } else if constexpr (epi_reads_aux<EPI>()) {
       // the auxiliary operands of PG row passes are loaded together, then
-      // those passes run (PG = the whole slab where registers allow)
+      // those passes run (PG = the whole slab where registers allow); the
+      // first slab's residual may already be in registers
+      if (rpre_on && i == 0) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) row_pass(it, rpre[it]);
+      } else {
 #pragma unroll
       for (int g0 = 0; g0 < NIT; g0 += PG) {
         Aux8 ax[PG];
@@ -605,6 +680,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_kernel(Gemm2Args p) {
 #pragma unroll
         for (int k = 0; k < PG; ++k)
           if (g0 + k < NIT) row_pass(g0 + k, ax[k]);
+      }
       }
     } else {
       // nothing to prefetch: a rolled loop keeps the code (and registers) small
@@ -805,6 +881,7 @@ int gemm2_launch(bool a_kcontig, bool b_kcontig, int epi, const void* A, int lda
       (!e.head.tgt || !e.head.part || !e.head.zy || e.head.npart != (int)cdiv(N, 96)))
     return -5;
   if (epi == EPI_HEAD_DX && !e.head.r) return -5;
+  if (epi == EPI_RESID && (int64_t)M * e.ldc * 4 >= (1ll << 32) - 4096) return -5;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)e.out) & 15) return -5;
   if ((e.aux && ((uintptr_t)e.aux & 15)) || (e.out2 && ((uintptr_t)e.out2 & 15))) return -5;
   if (e.bias && ((uintptr_t)e.bias & 15)) return -5;
