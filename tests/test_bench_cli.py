@@ -1,7 +1,8 @@
 """bench.py without a GPU: its refusal of more than one GPU, its FLOP count
 per token against the per-token figures derived from the pages' MFU
 estimator ("nanoGPT" Part IV Stage 6: 6 N + 12 L H Q T, N without the
-position table), and the weight-gradient group it times."""
+position table), the weight-gradient group it times, and the committed counter
+record its traffic figure comes from."""
 import os
 import subprocess
 import sys
@@ -47,3 +48,22 @@ def test_weight_gradient_group():
     ops = [(i, i, i, None, M, N, K, n) for i, (M, N, K, n) in enumerate(shapes)]
     once = [o for o in ops if o[-1] == 1]
     assert len(once) == 1 and once[0][5] == vi
+
+
+def test_committed_traffic_counters_match_the_kernel_sources():
+    """The HBM bytes bench.py reports as roofline.traffic come from the
+    committed counter record of the weight-gradient group, which holds the
+    hash of the matrix-product sources it was taken on.  A change to those
+    sources without new counter runs would report traffic as null; this
+    fails first.  The record's per-launch figure is the sum of its read and
+    write parts and lies above the algorithmic bytes."""
+    import json
+    with open(os.path.join(ROOT, "profiles", "traffic_weight_gradients.json")) as fh:
+        rec = json.load(fh)
+    assert rec["sources_hash"] == bench.sources_hash()
+    assert bench.measured_traffic("weight_gradients") == rec["bytes_per_launch"]
+    # each of the three is rounded to a byte on its own
+    assert abs(rec["bytes_per_launch"] - rec["read_bytes_per_launch"]
+               - rec["write_bytes_per_launch"]) <= 1
+    assert rec["algorithmic_bytes_per_launch"] < rec["bytes_per_launch"]
+    assert rec["launches_per_step"] == 49
