@@ -402,9 +402,9 @@ int gpt_op_linear_gelu_bwd(int32_t dtype, const void* dY, const void* Wt, const 
  * hipMalloc): the same kernels and results, with the column-sum scratch taken
  * from a 4 MiB device array the library holds per device until the process
  * ends, so the call allocates nothing and needs no workspace.  The array of
- * the calling thread's current device is used (the device of `stream`).
- * With dbias set, ceil(M/128) * N * 4 must not exceed 4 MiB (GPT_EINVAL,
- * nothing enqueued).  Calls that overlap on one device share the array and
+ * the calling thread's current device is used, and `stream` must belong to
+ * that device (GPT_EINVAL otherwise, nothing enqueued).  With dbias set,
+ * ceil(M/128) * N * 4 must not exceed 4 MiB (GPT_EINVAL, nothing enqueued).  Calls that overlap on one device share the array and
  * race: serialise them (one stream, or events).  Nothing in the array needs
  * to start at zero; it keeps the last call's partials. */
 int gpt_op_linear_gelu_bwd_noalloc(int32_t dtype, const void* dY, const void* Wt,

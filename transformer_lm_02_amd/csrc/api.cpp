@@ -47,13 +47,27 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 float* g_scratch_ptr[kMaxDevices] = {};
 
-// the scratch's device address on the calling thread's current device
-int current_device_scratch(float** out) {
+// the scratch's device address on the calling thread's current device, which
+// must be the device of `stream` (a null stream is the current device's)
+int current_device_scratch(hipStream_t stream, float** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
     gpt_error_text() = hipGetErrorString(e);
     return GPT_EHIP;
+  }
+  if (stream) {
+    hipDevice_t sdev = dev;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) {
+      gpt_error_text() = hipGetErrorString(e);
+      return GPT_EHIP;
+    }
+    if ((int)sdev != dev) {
+      gpt_error_text() = "linear_gelu_bwd_noalloc: the stream belongs to another device than the "
+                         "current one (make the stream's device current)";
+      return GPT_EINVAL;
+    }
   }
   if (dev < 0 || dev >= kMaxDevices) {
     gpt_error_text() = "device ordinal beyond the scratch table";
@@ -305,7 +319,7 @@ int gpt_op_linear_gelu_bwd_noalloc(int32_t dtype, const void* dY, const void* Wt
           "scratch";
       return GPT_EINVAL;
     }
-    if (int rc = current_device_scratch(&ws)) return rc;
+    if (int rc = current_device_scratch((hipStream_t)stream, &ws)) return rc;
   }
   return OP(gpt_op_linear_gelu_bwd, dtype, dY, Wt, dgelu, du, dbias, accumulate_bias, M, N, K, ws,
             ws ? kNoAllocScratchBytes : 0, stream);
