@@ -199,6 +199,15 @@ def test_gpt2_bf16_ragged_short_batch():
     bf16_step_parity("gpt2", batch=3, T=200, seed=4)
 
 
+def test_gpt2_width_ragged_rows_on_the_large_tiles():
+    """6000 rows (B=6, T=1000) at the GPT-2 width with two layers: enough rows
+    for the residual products to take the 128x192 tiles that read their first
+    slab's residual during the main loop, with a last row tile 112 rows deep
+    (lanes past the last row read zero).  The character-level full batch
+    covers the same tiles with a main loop too short for that (K = 384)."""
+    bf16_step_parity("gpt2", batch=6, T=1000, seed=7, n_layer=2)
+
+
 def test_gpt2_1p5b_width_two_layers_bf16_parity():
     """The 1.5B shape's layer width (d 1600, 25 heads of 64, MLP 6400, padded
     vocabulary) with two layers: every per-layer kernel at that shape; depth
